@@ -1,0 +1,331 @@
+/*
+ * qlora_oracle.c -- plain, slow CPU oracle for the NF4-quantized linear with a
+ * LoRA branch.  TEST INFRASTRUCTURE ONLY: the product path never links, loads
+ * or calls this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg do.  It shares no code, header, table or constant generator
+ * with the HIP library.
+ *
+ * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC
+ * (no fused multiply-add contraction, no flush-to-zero: every float operation
+ * below is one IEEE-754 binary32 or binary64 operation rounded to nearest-even).
+ *
+ * Sources, cited by page title and section:
+ *  [NF4]  "What does QLoRA change compared with plain LoRA when fine-tuning
+ *         Llama?" (katajob), section "NF4: 4-bit NormalFloat": sixteen levels
+ *         tuned to a zero-centred normal; per-block scaling over contiguous
+ *         groups of (commonly) 64 weights, one constant per block; at run time
+ *         a block is expanded to the compute dtype (bfloat16) for the matmul.
+ *  [DQ]   same page, section "Double quantization": the per-block constants are
+ *         themselves quantized to 8 bits with a second-level scale per group.
+ *  [LORA] "QLoRA: fine-tuning a large model on one GPU" (pranaymahendrakar),
+ *         Researcher level, "LoRA, stated once": h = W0 x + (alpha/r) B A x with
+ *         B in R^{d x r}, A in R^{r x k}.
+ *  [BWD]  same page, "What QLoRA adds", and the katajob page, "What stays in
+ *         full precision": gradients reach A and B through the dequantized
+ *         base weight; the base weight gets no gradient and no update.
+ *  [STEPS] "qlora" glossary (chipfoundryservices), table "How QLoRA Works":
+ *         quantize at load (4-bit), forward dequantizes then computes, backward
+ *         in bfloat16, only the adapter is updated.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *  - level construction: normal quantiles at equally spaced probabilities
+ *    between 1/2 and p_hi = 1 - (1/30 + 1/32)/2, eight on the positive side and
+ *    seven on the negative side, plus an exact zero, all divided by the largest
+ *    quantile so that the extremes are exactly -1 and +1; rounded to binary32
+ *    once.  (The value of p_hi is not on the pages; it is a declared choice.)
+ *  - code i is the i-th smallest level; element 2j of the row-major weight goes
+ *    into the low nibble of byte j, element 2j+1 into the high nibble;
+ *  - encode: x = fl32(w / c_b); nearest level, ties to the lower code; c_b = 0
+ *    gives code 7 (the zero level) for the whole block;
+ *  - double quantization: unsigned 8-bit linear codes over groups of 256
+ *    consecutive block constants, step d = fl32(max / 255), q = round-half-even
+ *    of fl32(c / d) clamped to [0, 255]; decoding uses c' = fl32(q * d);
+ *  - dequant: w' = bf16_rne(fl32(level[code] * c'));
+ *  - scale s = fl32(alpha / r); no bias; no dropout.
+ *
+ * The forward and backward contractions are written out in binary64 from their
+ * definitions; inputs arrive as binary64 arrays (the bf16 activations and
+ * adapters widen exactly), the dequantized weight as bf16 bit patterns.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* ---------------------------------------------------------------- codebook */
+
+/* Standard normal CDF written with the complementary error function. */
+static double std_normal_cdf(double x) { return 0.5 * erfc(-x / sqrt(2.0)); }
+
+/* Standard normal quantile by bisection on the CDF, run until the bracket
+ * cannot shrink any further in binary64. */
+static double std_normal_quantile(double p) {
+  double lo = -40.0, hi = 40.0;
+  for (;;) {
+    double mid = 0.5 * (lo + hi);
+    if (mid <= lo || mid >= hi) break;
+    if (std_normal_cdf(mid) < p) lo = mid; else hi = mid;
+  }
+  /* pick whichever end of the final bracket has the closer CDF value */
+  return (fabs(std_normal_cdf(lo) - p) <= fabs(std_normal_cdf(hi) - p)) ? lo : hi;
+}
+
+/* The 16 NF4 levels, ascending, in binary64 before rounding (see the reading
+ * above).  Exposed so the tests can check the unrounded values too. */
+void oracle_nf4_levels_f64(double out[16]) {
+  const double p_hi = 1.0 - 0.5 * (1.0 / 30.0 + 1.0 / 32.0);
+  const double qmax = std_normal_quantile(p_hi);
+  double v[16];
+  int n = 0;
+  /* seven negative levels: -Phi^-1(1/2 + j (p_hi - 1/2) / 7), j = 7..1 */
+  for (int j = 7; j >= 1; --j) v[n++] = -std_normal_quantile(0.5 + j * (p_hi - 0.5) / 7.0) / qmax;
+  v[n++] = 0.0;
+  /* eight positive levels: Phi^-1(1/2 + i (p_hi - 1/2) / 8), i = 1..8 */
+  for (int i = 1; i <= 8; ++i) v[n++] = std_normal_quantile(0.5 + i * (p_hi - 0.5) / 8.0) / qmax;
+  /* already ascending by construction; keep an explicit sort for clarity */
+  for (int i = 1; i < 16; ++i)
+    for (int j = i; j > 0 && v[j - 1] > v[j]; --j) { double t = v[j]; v[j] = v[j - 1]; v[j - 1] = t; }
+  memcpy(out, v, sizeof v);
+}
+
+void oracle_nf4_levels(float out[16]) {
+  double v[16];
+  oracle_nf4_levels_f64(v);
+  for (int i = 0; i < 16; ++i) out[i] = (float)v[i]; /* one rounding to binary32 */
+}
+
+/* ------------------------------------------------------------- bf16 helper */
+
+/* binary32 -> bfloat16 bit pattern, round to nearest, ties to even. */
+static uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40); /* NaN stays NaN */
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7fffu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+/* --------------------------------------------------------------- quantize */
+
+/* Nearest level to x, ties to the lower code.  Distances are taken in binary64:
+ * for |x| >= 2^-29 both operands are binary32 values in [-1, 1] whose ulps are
+ * at least 2^-52, so every difference is exact; for smaller |x| the zero level
+ * is nearer than any other by a wide margin.  Hence this is the exact argmin. */
+static int nearest_code(float x, const float lv[16]) {
+  int best = 0;
+  double bd = fabs((double)x - (double)lv[0]);
+  for (int i = 1; i < 16; ++i) {
+    double d = fabs((double)x - (double)lv[i]);
+    if (d < bd) { bd = d; best = i; } /* strict: an equal distance keeps the lower code */
+  }
+  return best;
+}
+
+/*
+ * Block-wise NF4 quantization with double quantization of the constants.
+ *   W          [n_out * n_in] binary32, row-major; n_in % 64 == 0
+ *   codes      [n_out * n_in / 2]
+ *   absmax_q   [n_out * n_in / 64]          8-bit block constants
+ *   absmax_step[ceil(n_out * n_in / 64 / 256)] binary32 second-level steps
+ *   absmax_f32 [n_out * n_in / 64] or NULL: the un-quantized block absmax
+ * Returns 0, or -1 when n_in is not a multiple of 64.
+ */
+int oracle_quantize_nf4(const float *W, int64_t n_out, int64_t n_in, uint8_t *codes, uint8_t *absmax_q,
+                        float *absmax_step, float *absmax_f32) {
+  if (n_in % 64 != 0 || n_out < 0) return -1;
+  float lv[16];
+  oracle_nf4_levels(lv);
+  const int64_t nblk = n_out * n_in / 64;
+  float *c = (float *)malloc(sizeof(float) * (size_t)(nblk > 0 ? nblk : 1));
+  /* [NF4] one absmax per 64 contiguous weights; encode with the exact binary32 constant */
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < nblk; ++b) {
+    const float *w = W + b * 64;
+    float m = 0.0f;
+    for (int e = 0; e < 64; ++e) { float a = fabsf(w[e]); if (a > m) m = a; }
+    c[b] = m;
+    int q[64];
+    for (int e = 0; e < 64; ++e) q[e] = (m == 0.0f) ? 7 : nearest_code(w[e] / m, lv);
+    for (int j = 0; j < 32; ++j) codes[b * 32 + j] = (uint8_t)(q[2 * j] | (q[2 * j + 1] << 4));
+  }
+  /* [DQ] groups of 256 consecutive constants, unsigned 8-bit, step = group max / 255 */
+  const int64_t ngrp = (nblk + 255) / 256;
+#pragma omp parallel for schedule(static)
+  for (int64_t g = 0; g < ngrp; ++g) {
+    const int64_t b0 = g * 256, b1 = (b0 + 256 < nblk) ? b0 + 256 : nblk;
+    float s = 0.0f;
+    for (int64_t b = b0; b < b1; ++b) if (c[b] > s) s = c[b];
+    const float d = s / 255.0f;
+    absmax_step[g] = (s == 0.0f) ? 0.0f : d;
+    for (int64_t b = b0; b < b1; ++b) {
+      int qb = 0;
+      if (s != 0.0f) {
+        float t = c[b] / d;
+        float r = rintf(t); /* default rounding mode: nearest, ties to even */
+        qb = (r < 0.0f) ? 0 : (r > 255.0f) ? 255 : (int)r;
+      }
+      absmax_q[b] = (uint8_t)qb;
+    }
+  }
+  if (absmax_f32) memcpy(absmax_f32, c, sizeof(float) * (size_t)nblk);
+  free(c);
+  return 0;
+}
+
+/* Dequantize to bf16 bit patterns: w' = bf16_rne(fl32(level[code] * fl32(q * d))). */
+int oracle_dequant(const uint8_t *codes, const uint8_t *absmax_q, const float *absmax_step, int64_t n_out,
+                   int64_t n_in, uint16_t *W_out) {
+  if (n_in % 64 != 0 || n_out < 0) return -1;
+  float lv[16];
+  oracle_nf4_levels(lv);
+  const int64_t n = n_out * n_in;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t b = i / 64, g = b / 256;
+    const float cq = (float)absmax_q[b] * absmax_step[g];
+    const int code = (i & 1) ? (codes[i >> 1] >> 4) : (codes[i >> 1] & 15);
+    W_out[i] = f32_to_bf16_rne(lv[code] * cq);
+  }
+  return 0;
+}
+
+static inline double bf16_to_f64(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* ---------------------------------------------------------------- forward */
+
+/*
+ * [LORA] forward for selected token rows:
+ *   U[t, j] = sum_k X[t, k] A[j, k]
+ *   Y[t, n] = sum_k X[t, k] W'[n, k] + s * sum_j U[t, j] B[n, j],   s = fl32(alpha / r)
+ * X [T, K], A [r, K], B [N, r] binary64; Wdq [N, K] bf16 bits.
+ * rows: n_rows indices into [0, T) (or NULL for all rows, then n_rows = T).
+ * Y [n_rows, N], U [n_rows, r] binary64 (U may be NULL).
+ */
+void oracle_linear_fwd(const double *X, int64_t T, const uint16_t *Wdq, int64_t N, int64_t K, const double *A,
+                       const double *B, int32_t r, float alpha, const int64_t *rows, int64_t n_rows, double *Y,
+                       double *U) {
+  const double s = (double)(alpha / (float)r);
+  if (!rows) n_rows = T;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < n_rows; ++i) {
+    const int64_t t = rows ? rows[i] : i;
+    const double *x = X + t * K;
+    double *u = (double *)malloc(sizeof(double) * (size_t)(r > 0 ? r : 1));
+    for (int32_t j = 0; j < r; ++j) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k) acc += x[k] * A[(int64_t)j * K + k];
+      u[j] = acc;
+      if (U) U[i * r + j] = acc;
+    }
+    for (int64_t n = 0; n < N; ++n) {
+      const uint16_t *w = Wdq + n * K;
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k) acc += x[k] * bf16_to_f64(w[k]);
+      double lora = 0.0;
+      for (int32_t j = 0; j < r; ++j) lora += u[j] * B[n * r + j];
+      Y[i * N + n] = acc + s * lora;
+    }
+    free(u);
+  }
+}
+
+/* --------------------------------------------------------------- backward */
+
+/*
+ * [BWD] backward of the layer above with respect to X, A and B (W gets none):
+ *   U  = X A^T                      [T, r]
+ *   dU = s * dY B                   [T, r]
+ *   dA = dU^T X                     [r, K]
+ *   dB = s * dY^T U                 [N, r]
+ *   dX = dY W' + dU A               [T, K]   (only for the selected rows)
+ * dX [n_rows, K] (may be NULL), dA [r, K], dB [N, r] binary64.
+ */
+void oracle_linear_bwd(const double *X, const double *dY, int64_t T, const uint16_t *Wdq, int64_t N, int64_t K,
+                       const double *A, const double *B, int32_t r, float alpha, const int64_t *rows,
+                       int64_t n_rows, double *dX, double *dA, double *dB) {
+  const double s = (double)(alpha / (float)r);
+  double *U = (double *)calloc((size_t)(T * r > 0 ? T * r : 1), sizeof(double));
+  double *dU = (double *)calloc((size_t)(T * r > 0 ? T * r : 1), sizeof(double));
+  /* U[t, j] = sum_k X[t, k] A[j, k];  dU[t, j] = s * sum_n dY[t, n] B[n, j] */
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    for (int32_t j = 0; j < r; ++j) {
+      double a = 0.0;
+      for (int64_t k = 0; k < K; ++k) a += X[t * K + k] * A[(int64_t)j * K + k];
+      U[t * r + j] = a;
+    }
+    double *g = dU + t * r;
+    for (int64_t n = 0; n < N; ++n) {
+      const double y = dY[t * N + n];
+      for (int32_t j = 0; j < r; ++j) g[j] += y * B[n * r + j];
+    }
+    for (int32_t j = 0; j < r; ++j) g[j] *= s;
+  }
+  /* dA[j, :] = sum_t dU[t, j] X[t, :] */
+#pragma omp parallel for schedule(static)
+  for (int32_t j = 0; j < r; ++j) {
+    double *out = dA + (int64_t)j * K;
+    for (int64_t k = 0; k < K; ++k) out[k] = 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+      const double a = dU[t * r + j];
+      for (int64_t k = 0; k < K; ++k) out[k] += a * X[t * K + k];
+    }
+  }
+  /* dB[n, :] = s * sum_t dY[t, n] U[t, :]   (each thread owns a range of rows n) */
+#pragma omp parallel
+  {
+#ifdef _OPENMP
+    const int64_t nth = omp_get_num_threads(), me = omp_get_thread_num();
+#else
+    const int64_t nth = 1, me = 0;
+#endif
+    const int64_t n0 = N * me / nth, n1 = N * (me + 1) / nth;
+    for (int64_t n = n0; n < n1; ++n)
+      for (int32_t j = 0; j < r; ++j) dB[n * r + j] = 0.0;
+    for (int64_t t = 0; t < T; ++t)
+      for (int64_t n = n0; n < n1; ++n) {
+        const double y = dY[t * N + n];
+        for (int32_t j = 0; j < r; ++j) dB[n * r + j] += y * U[t * r + j];
+      }
+    for (int64_t n = n0; n < n1; ++n)
+      for (int32_t j = 0; j < r; ++j) dB[n * r + j] *= s;
+  }
+  /* dX[t, k] = sum_n dY[t, n] W'[n, k] + sum_j dU[t, j] A[j, k] */
+  if (dX) {
+    if (!rows) n_rows = T;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n_rows; ++i) {
+      const int64_t t = rows ? rows[i] : i;
+      double *out = dX + i * K;
+      for (int64_t k = 0; k < K; ++k) out[k] = 0.0;
+      for (int64_t n = 0; n < N; ++n) {
+        const double g = dY[t * N + n];
+        const uint16_t *w = Wdq + n * K;
+        for (int64_t k = 0; k < K; ++k) out[k] += g * bf16_to_f64(w[k]);
+      }
+      for (int32_t j = 0; j < r; ++j) {
+        const double g = dU[t * r + j];
+        for (int64_t k = 0; k < K; ++k) out[k] += g * A[(int64_t)j * K + k];
+      }
+    }
+  }
+  free(U);
+  free(dU);
+}
