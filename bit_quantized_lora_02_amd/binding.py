@@ -1,0 +1,260 @@
+"""Thin ctypes binding over ``libqlora.so`` (the C ABI of ``include/qlora.h``).
+
+This module only marshals arguments: torch tensors supply device memory
+(``data_ptr()``) and the current HIP stream; every step of the computation runs
+in the library's gfx950 kernels.  There is no CPU or PyTorch fallback: if the
+library is missing or the device is not gfx950, calls raise.
+
+Names follow the C ABI: ``quantize_nf4``, ``dequant``, ``linear_fwd``,
+``linear_bwd``, plus ``QLoRALinearFn`` (a torch.autograd.Function whose backward
+returns gradients for X, A and B and none for the frozen NF4 weight).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqlora.so")
+
+QLORA_OK = 0
+QLORA_EINVAL = -1
+QLORA_EWORKSPACE = -2
+QLORA_ENODEV = -3
+QLORA_EHIP = -4
+OP_FWD = 0
+OP_BWD = 1
+MAX_RANK = 128
+
+EXPORTED = (
+    "qlora_nf4_storage",
+    "qlora_nf4_codebook",
+    "qlora_workspace_bytes",
+    "qlora_quantize_nf4",
+    "qlora_dequant",
+    "qlora_linear_fwd",
+    "qlora_linear_bwd",
+    "qlora_strerror",
+    "qlora_last_error",
+    "qlora_timing_enable",
+    "qlora_timing_read",
+)
+
+
+class QLoRAError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{msg} (code {code})")
+        self.code = code
+
+
+class _NF4(ctypes.Structure):
+    _fields_ = [
+        ("n_out", ctypes.c_int64),
+        ("n_in", ctypes.c_int64),
+        ("codes", ctypes.c_void_p),
+        ("absmax_q", ctypes.c_void_p),
+        ("absmax_step", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libqlora.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first (python -m bit_quantized_lora_02_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    pnf4 = ctypes.POINTER(_NF4)
+    sig = {
+        "qlora_nf4_storage": ([i64, i64, ctypes.POINTER(sz), ctypes.POINTER(sz), ctypes.POINTER(sz)], ctypes.c_int),
+        "qlora_nf4_codebook": ([P], ctypes.c_int),
+        "qlora_workspace_bytes": ([ctypes.c_int, i64, i64, i64, i32, ctypes.POINTER(sz)], ctypes.c_int),
+        "qlora_quantize_nf4": ([P, pnf4, P], ctypes.c_int),
+        "qlora_dequant": ([pnf4, P, P], ctypes.c_int),
+        "qlora_linear_fwd": ([P, i64, pnf4, P, P, i32, ctypes.c_float, P, P, P, sz, P], ctypes.c_int),
+        "qlora_linear_bwd": ([P, P, i64, pnf4, P, P, i32, ctypes.c_float, P, P, P, P, P, sz, P], ctypes.c_int),
+        "qlora_strerror": ([ctypes.c_int], ctypes.c_char_p),
+        "qlora_last_error": ([], ctypes.c_char_p),
+        "qlora_timing_enable": ([ctypes.c_char_p, ctypes.c_int], ctypes.c_int),
+        "qlora_timing_read": ([ctypes.c_char_p, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str):
+    if rc != QLORA_OK:
+        lib = load_library()
+        raise QLoRAError(rc, f"{what}: {lib.qlora_strerror(rc).decode()}: {lib.qlora_last_error().decode()}")
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _bits(t: torch.Tensor) -> torch.Tensor:
+    """bf16 tensor -> contiguous view used for the uint16 ABI arguments."""
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"expected a bfloat16 tensor, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError("expected a GPU tensor")
+    return t.contiguous()
+
+
+def storage_bytes(n_out: int, n_in: int) -> tuple[int, int, int]:
+    c, q, s = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load_library().qlora_nf4_storage(n_out, n_in, ctypes.byref(c), ctypes.byref(q), ctypes.byref(s)),
+           "qlora_nf4_storage")
+    return c.value, q.value, s.value
+
+
+def codebook() -> list[float]:
+    arr = (ctypes.c_float * 16)()
+    _check(load_library().qlora_nf4_codebook(arr), "qlora_nf4_codebook")
+    return list(arr)
+
+
+def workspace_bytes(op: int, T: int, n_out: int, n_in: int, r: int) -> int:
+    b = ctypes.c_size_t()
+    _check(load_library().qlora_workspace_bytes(op, T, n_out, n_in, r, ctypes.byref(b)), "qlora_workspace_bytes")
+    return b.value
+
+
+@dataclass
+class NF4Weight:
+    """A frozen NF4 weight: the three device arrays of the layout plus its shape."""
+    n_out: int
+    n_in: int
+    codes: torch.Tensor  # uint8 [n_out*n_in/2]
+    absmax_q: torch.Tensor  # uint8 [n_out*n_in/64]
+    absmax_step: torch.Tensor  # float32 [ceil(n_out*n_in/16384)]
+
+    def struct(self) -> _NF4:
+        return _NF4(self.n_out, self.n_in, self.codes.data_ptr(), self.absmax_q.data_ptr(), self.absmax_step.data_ptr())
+
+    @property
+    def device(self):
+        return self.codes.device
+
+    @staticmethod
+    def empty(n_out: int, n_in: int, device) -> "NF4Weight":
+        cb, qb, sb = storage_bytes(n_out, n_in)
+        return NF4Weight(n_out, n_in, torch.empty(cb, dtype=torch.uint8, device=device),
+                         torch.empty(qb, dtype=torch.uint8, device=device),
+                         torch.empty(sb // 4, dtype=torch.float32, device=device))
+
+
+def quantize_nf4(W: torch.Tensor) -> NF4Weight:
+    """Quantize a float32 [n_out, n_in] GPU tensor to NF4 with double-quantized constants."""
+    if W.dtype != torch.float32 or not W.is_cuda or W.dim() != 2:
+        raise TypeError("W must be a 2-D float32 GPU tensor")
+    W = W.contiguous()
+    w = NF4Weight.empty(W.shape[0], W.shape[1], W.device)
+    st = w.struct()
+    _check(load_library().qlora_quantize_nf4(_ptr(W), ctypes.byref(st), _stream(W.device)), "qlora_quantize_nf4")
+    return w
+
+
+def dequant(w: NF4Weight) -> torch.Tensor:
+    """bf16 [n_out, n_in] expansion of an NF4 weight (tests and export only)."""
+    out = torch.empty((w.n_out, w.n_in), dtype=torch.bfloat16, device=w.device)
+    st = w.struct()
+    _check(load_library().qlora_dequant(ctypes.byref(st), _ptr(out), _stream(w.device)), "qlora_dequant")
+    return out
+
+
+def _workspace(op, T, w: NF4Weight, r) -> tuple[torch.Tensor | None, int]:
+    nb = workspace_bytes(op, T, w.n_out, w.n_in, r)
+    if nb == 0:
+        return None, 0
+    return torch.empty(nb, dtype=torch.uint8, device=w.device), nb
+
+
+def linear_fwd(X: torch.Tensor, w: NF4Weight, A: torch.Tensor, B: torch.Tensor, alpha: float,
+               save_u: bool = True, ws: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """Y = X . deq(W)^T + (alpha/r) (X A^T) B^T; returns (Y, U or None)."""
+    X, A, B = _bits(X), _bits(A), _bits(B)
+    T, r = X.shape[0], A.shape[0]
+    if X.shape[1] != w.n_in or A.shape != (r, w.n_in) or B.shape != (w.n_out, r):
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, A {tuple(A.shape)}, B {tuple(B.shape)}, "
+                         f"W [{w.n_out}, {w.n_in}]")
+    Y = out if out is not None else torch.empty((T, w.n_out), dtype=torch.bfloat16, device=X.device)
+    U = torch.empty((T, r), dtype=torch.bfloat16, device=X.device) if save_u else None
+    if ws is None:
+        ws, nb = _workspace(OP_FWD, T, w, r)
+    else:
+        nb = ws.numel()
+    st = w.struct()
+    _check(load_library().qlora_linear_fwd(_ptr(X), T, ctypes.byref(st), _ptr(A), _ptr(B), r, float(alpha), _ptr(Y),
+                                           _ptr(U), _ptr(ws), nb, _stream(X.device)), "qlora_linear_fwd")
+    return Y, U
+
+
+def linear_bwd(X: torch.Tensor, dY: torch.Tensor, w: NF4Weight, A: torch.Tensor, B: torch.Tensor, alpha: float,
+               U: torch.Tensor | None = None, need_dx: bool = True, ws: torch.Tensor | None = None,
+               outs: tuple | None = None):
+    """Gradients (dX or None, dA, dB) of the forward above; W gets none."""
+    X, dY, A, B = _bits(X), _bits(dY), _bits(A), _bits(B)
+    if U is not None:
+        U = _bits(U)
+    T, r = X.shape[0], A.shape[0]
+    if dY.shape != (T, w.n_out) or A.shape != (r, w.n_in) or B.shape != (w.n_out, r):
+        raise ValueError("shape mismatch in linear_bwd")
+    if outs is not None:
+        dX, dA, dB = outs
+    else:
+        dX = torch.empty_like(X) if need_dx else None
+        dA = torch.empty_like(A)
+        dB = torch.empty_like(B)
+    if ws is None:
+        ws, nb = _workspace(OP_BWD, T, w, r)
+    else:
+        nb = ws.numel()
+    st = w.struct()
+    _check(load_library().qlora_linear_bwd(_ptr(X), _ptr(dY), T, ctypes.byref(st), _ptr(A), _ptr(B), r, float(alpha),
+                                           _ptr(U), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws), nb, _stream(X.device)),
+           "qlora_linear_bwd")
+    return dX, dA, dB
+
+
+class QLoRALinearFn(torch.autograd.Function):
+    """Autograd wrapper: forward(X, w, A, B, alpha) -> Y; gradients for X, A, B only."""
+
+    @staticmethod
+    def forward(ctx, X, w: NF4Weight, A, B, alpha: float):
+        Y, U = linear_fwd(X, w, A, B, alpha, save_u=True)
+        ctx.save_for_backward(X, A, B, U)
+        ctx.w, ctx.alpha = w, alpha
+        return Y
+
+    @staticmethod
+    def backward(ctx, dY):
+        X, A, B, U = ctx.saved_tensors
+        dX, dA, dB = linear_bwd(X, dY.contiguous(), ctx.w, A, B, ctx.alpha, U=U, need_dx=ctx.needs_input_grad[0])
+        return dX, None, dA, dB, None
+
+
+def timing_enable(kernel: str, enable: bool = True):
+    _check(load_library().qlora_timing_enable(kernel.encode(), 1 if enable else 0), "qlora_timing_enable")
+
+
+def timing_read(kernel: str) -> tuple[int, float]:
+    n, ms = ctypes.c_int64(), ctypes.c_double()
+    _check(load_library().qlora_timing_read(kernel.encode(), ctypes.byref(n), ctypes.byref(ms)), "qlora_timing_read")
+    return n.value, ms.value

@@ -1,0 +1,450 @@
+// abi.hip -- the C ABI declared in include/qlora.h: argument checks, workspace
+// planning, the NF4 codebook, kernel sequencing and measurement hooks.
+//
+// Every entry point validates all of its arguments before its first HIP call,
+// returns a QLORA_E* code instead of aborting, and enqueues its kernels on the
+// caller's stream without synchronizing or allocating device memory.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "device.h"
+#include "launch.h"
+#include "qlora.h"
+
+using namespace qlora;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+// ------------------------------------------------------------------ codebook
+// Standard-normal quantile by Newton's method on the CDF written with erfc,
+// started from the logistic approximation of the normal CDF.
+double normal_quantile(double p) {
+  double x = log(p / (1.0 - p)) / 1.702;
+  for (int it = 0; it < 64; ++it) {
+    const double f = 0.5 * erfc(-x / sqrt(2.0)) - p;
+    const double dens = exp(-0.5 * x * x) / sqrt(2.0 * M_PI);
+    const double dx = f / dens;
+    x -= dx;
+    if (fabs(dx) <= 1e-17 * (1.0 + fabs(x))) break;
+  }
+  return x;
+}
+
+struct Codebook {
+  Levels lv;
+  Thresholds thr;
+};
+
+// Levels: quantiles at probabilities equally spaced between 1/2 and
+// p_hi = 1 - (1/30 + 1/32)/2 (seven negative, eight positive, plus zero),
+// divided by the largest, rounded to binary32 once.  Thresholds: for each pair
+// of neighbouring levels, the largest binary32 value not above their exact
+// midpoint, so that x > thr_i  <=>  x is strictly above the midpoint, and a
+// value exactly on a midpoint keeps the lower code.
+const Codebook &codebook() {
+  static Codebook cb;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    const double p_hi = 1.0 - 0.5 * (1.0 / 30.0 + 1.0 / 32.0);
+    const double top = normal_quantile(p_hi);
+    double v[16];
+    for (int j = 7; j >= 1; --j) v[7 - j] = -normal_quantile(0.5 + j * (p_hi - 0.5) / 7.0) / top;
+    v[7] = 0.0;
+    for (int i = 1; i <= 8; ++i) v[7 + i] = normal_quantile(0.5 + i * (p_hi - 0.5) / 8.0) / top;
+    v[15] = 1.0;  // top / top
+    v[0] = -1.0;
+    for (int i = 0; i < 16; ++i) cb.lv.v[i] = (float)v[i];
+    for (int i = 0; i < 15; ++i) {
+      const double mid = ((double)cb.lv.v[i] + (double)cb.lv.v[i + 1]) * 0.5;  // exact in binary64
+      float t = (float)mid;
+      if ((double)t > mid) t = nextafterf(t, -INFINITY);
+      cb.thr.v[i] = t;
+    }
+  });
+  return cb;
+}
+
+// ------------------------------------------------------------ device check
+std::atomic<int> g_dev_ok[64];
+
+int check_device(int *dev_out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(QLORA_ENODEV, "no HIP device available");
+  }
+  if (dev < 64) {
+    int st = g_dev_ok[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+      hipDeviceProp_t prop;
+      if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(QLORA_ENODEV, "hipGetDeviceProperties failed for device %d", dev);
+      }
+      st = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+      g_dev_ok[dev].store(st, std::memory_order_relaxed);
+    }
+    if (st < 0) return fail(QLORA_ENODEV, "device %d is not gfx950 (this library holds gfx950 code only)", dev);
+  }
+  if (dev_out) *dev_out = dev;
+  return QLORA_OK;
+}
+
+bool debug_sync() {
+  static int v = -1;
+  if (v < 0) {
+    const char *e = getenv("QLORA_DEBUG_SYNC");
+    v = (e && e[0] == '1') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+// --------------------------------------------------------------- timing
+std::mutex g_tmu;
+std::string g_timed;  // "" = off, "*" = all
+std::map<std::string, std::vector<std::pair<hipEvent_t, hipEvent_t>>> g_events;
+
+struct Timed {
+  hipEvent_t a = nullptr, b = nullptr;
+  std::string name;
+  hipStream_t s;
+  Timed(const char *kname, hipStream_t st) : s(st) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (g_timed.empty() || (g_timed != "*" && g_timed != kname)) return;
+    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+      (void)hipGetLastError();
+      a = b = nullptr;
+      return;
+    }
+    name = kname;
+    (void)hipEventRecord(a, s);
+  }
+  ~Timed() {
+    if (!a) return;
+    (void)hipEventRecord(b, s);
+    std::lock_guard<std::mutex> lk(g_tmu);
+    g_events[name].push_back({a, b});
+  }
+};
+
+int launched(hipError_t e, const char *what, hipStream_t s) {
+  if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(QLORA_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return QLORA_OK;
+}
+
+#define LAUNCH(name, call)                             \
+  do {                                                 \
+    hipError_t e_;                                     \
+    {                                                  \
+      Timed t_(name, s);                               \
+      e_ = (call);                                     \
+    }                                                  \
+    int rc_ = launched(e_, name, s);                   \
+    if (rc_ != QLORA_OK) return rc_;                   \
+  } while (0)
+
+// ------------------------------------------------------------- validation
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+constexpr int64_t kMaxDim = (int64_t)1 << 22;
+
+int check_nf4(const qlora_nf4 *q, bool for_gemm) {
+  if (!q) return fail(QLORA_EINVAL, "q is NULL");
+  if (!q->codes || !q->absmax_q || !q->absmax_step) return fail(QLORA_EINVAL, "q has a NULL array");
+  if (!aligned16(q->codes) || !aligned16(q->absmax_q) || !aligned16(q->absmax_step))
+    return fail(QLORA_EINVAL, "q arrays must be 16-byte aligned");
+  if (q->n_out < 1 || q->n_in < 64 || q->n_in % 64 != 0)
+    return fail(QLORA_EINVAL, "need n_out >= 1 and n_in a positive multiple of 64 (got %lld x %lld)",
+                (long long)q->n_out, (long long)q->n_in);
+  if (q->n_out > kMaxDim || q->n_in > kMaxDim || q->n_out * q->n_in > ((int64_t)1 << 40))
+    return fail(QLORA_EINVAL, "weight too large (%lld x %lld)", (long long)q->n_out, (long long)q->n_in);
+  if (for_gemm && q->n_out % 8 != 0) return fail(QLORA_EINVAL, "n_out must be a multiple of 8 (got %lld)", (long long)q->n_out);
+  return QLORA_OK;
+}
+
+// --------------------------------------------------------------- planning
+constexpr size_t kAlign = 256;
+size_t up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Split {
+  int n = 0;
+  int64_t kchunk = 0;
+};
+
+// Split a reduction of length Kred for an M x N output so that ~1024
+// workgroups run (four per CU), each split at least 256 deep.
+Split plan_split(int64_t M, int64_t N, int64_t Kred) {
+  Split sp;
+  if (Kred <= 0 || M <= 0 || N <= 0) return sp;
+  const int64_t tiles = ceil_div(M, 64) * ceil_div(N, 64);
+  int64_t want = ceil_div(1024, tiles);
+  int64_t maxs = Kred / 256;
+  if (maxs < 1) maxs = 1;
+  int64_t ns = want < maxs ? want : maxs;
+  if (ns > 64) ns = 64;
+  if (ns < 1) ns = 1;
+  sp.kchunk = up((size_t)ceil_div(Kred, ns), 32);
+  sp.n = (int)ceil_div(Kred, sp.kchunk);
+  return sp;
+}
+
+struct Plan {
+  int64_t rp = 0;
+  size_t off_bp = 0, off_v = 0, off_du = 0, off_part = 0, total = 0;
+  Split su, sdu, sdb, sda;
+};
+
+Plan make_plan(int op, int64_t T, int64_t N, int64_t K, int32_t r) {
+  Plan p;
+  p.rp = (int64_t)up((size_t)r, 64);
+  size_t off = 0;
+  p.off_bp = off;
+  off = up(off + (size_t)(N * p.rp * 2), kAlign);
+  p.off_v = off;  // fwd: V = bf16(s U) padded; bwd: U padded
+  off = up(off + (size_t)(T * p.rp * 2), kAlign);
+  size_t part = 0;
+  if (op == QLORA_OP_FWD) {
+    p.su = plan_split(T, r, K);
+    part = (size_t)p.su.n * T * r * 4;
+  } else {
+    p.off_du = off;
+    off = up(off + (size_t)(T * p.rp * 2), kAlign);
+    p.su = plan_split(T, r, K);
+    p.sdu = plan_split(T, r, N);
+    p.sdb = plan_split(N, r, T);
+    p.sda = plan_split(r, K, T);
+    const size_t cands[4] = {(size_t)p.su.n * T * r * 4, (size_t)p.sdu.n * T * r * 4, (size_t)p.sdb.n * N * r * 4,
+                             (size_t)p.sda.n * r * K * 4};
+    for (size_t c : cands) part = c > part ? c : part;
+  }
+  p.off_part = off;
+  off = up(off + part, kAlign);
+  p.total = off;
+  return p;
+}
+
+int check_lora_args(int64_t T, const qlora_nf4 *q, const void *A, const void *B, int32_t r, float alpha) {
+  int rc = check_nf4(q, true);
+  if (rc) return rc;
+  if (T < 0 || T > kMaxDim) return fail(QLORA_EINVAL, "T must be in [0, 2^22] (got %lld)", (long long)T);
+  if (r < 1 || r > QLORA_MAX_RANK) return fail(QLORA_EINVAL, "r must be in [1, %d] (got %d)", QLORA_MAX_RANK, (int)r);
+  if (!isfinite(alpha)) return fail(QLORA_EINVAL, "alpha must be finite");
+  if (!A || !B) return fail(QLORA_EINVAL, "A and B must not be NULL");
+  if (!aligned16(A) || !aligned16(B)) return fail(QLORA_EINVAL, "A and B must be 16-byte aligned");
+  return QLORA_OK;
+}
+
+int check_ws(int op, int64_t T, int64_t N, int64_t K, int32_t r, const void *ws, size_t ws_bytes, Plan *p) {
+  *p = make_plan(op, T, N, K, r);
+  if (ws_bytes < p->total)
+    return fail(QLORA_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, p->total);
+  if (p->total > 0 && (!ws || ((uintptr_t)ws & (kAlign - 1))))
+    return fail(QLORA_EINVAL, "workspace must be non-NULL and 256-byte aligned");
+  return QLORA_OK;
+}
+
+}  // namespace
+
+// =========================================================== C ABI
+extern "C" {
+
+const char *qlora_strerror(int code) {
+  switch (code) {
+    case QLORA_OK: return "ok";
+    case QLORA_EINVAL: return "invalid argument";
+    case QLORA_EWORKSPACE: return "workspace too small";
+    case QLORA_ENODEV: return "no gfx950 device";
+    case QLORA_EHIP: return "HIP error";
+    default: return "unknown error";
+  }
+}
+
+const char *qlora_last_error(void) { return g_err; }
+
+int qlora_nf4_storage(int64_t n_out, int64_t n_in, size_t *codes_bytes, size_t *absmax_q_bytes,
+                      size_t *absmax_step_bytes) {
+  if (!codes_bytes || !absmax_q_bytes || !absmax_step_bytes) return fail(QLORA_EINVAL, "NULL output pointer");
+  if (n_out < 1 || n_in < 64 || n_in % 64 != 0 || n_out > kMaxDim || n_in > kMaxDim)
+    return fail(QLORA_EINVAL, "need n_out >= 1 and n_in a positive multiple of 64 (got %lld x %lld)",
+                (long long)n_out, (long long)n_in);
+  const int64_t n = n_out * n_in, nblk = n / 64;
+  *codes_bytes = (size_t)(n / 2);
+  *absmax_q_bytes = (size_t)nblk;
+  *absmax_step_bytes = (size_t)(4 * ceil_div(nblk, 256));
+  return QLORA_OK;
+}
+
+int qlora_nf4_codebook(float levels[16]) {
+  if (!levels) return fail(QLORA_EINVAL, "levels is NULL");
+  memcpy(levels, codebook().lv.v, sizeof(float) * 16);
+  return QLORA_OK;
+}
+
+int qlora_workspace_bytes(int op, int64_t T, int64_t n_out, int64_t n_in, int32_t r, size_t *bytes) {
+  if (!bytes) return fail(QLORA_EINVAL, "bytes is NULL");
+  if (op != QLORA_OP_FWD && op != QLORA_OP_BWD) return fail(QLORA_EINVAL, "unknown op %d", op);
+  if (T < 0 || T > kMaxDim || n_out < 8 || n_out % 8 != 0 || n_out > kMaxDim || n_in < 64 || n_in % 64 != 0 ||
+      n_in > kMaxDim || r < 1 || r > QLORA_MAX_RANK)
+    return fail(QLORA_EINVAL, "bad sizes T=%lld n_out=%lld n_in=%lld r=%d", (long long)T, (long long)n_out,
+                (long long)n_in, (int)r);
+  *bytes = make_plan(op, T, n_out, n_in, r).total;
+  return QLORA_OK;
+}
+
+int qlora_quantize_nf4(const float *W, const qlora_nf4 *q, void *stream) {
+  int rc = check_nf4(q, false);
+  if (rc) return rc;
+  if (!W || !aligned16(W)) return fail(QLORA_EINVAL, "W must be non-NULL and 16-byte aligned");
+  if ((rc = check_device(nullptr))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  LAUNCH("quantize_nf4",
+         launch_quantize_nf4(W, q->n_out, q->n_in, q->codes, q->absmax_q, q->absmax_step, codebook().thr, s));
+  return QLORA_OK;
+}
+
+int qlora_dequant(const qlora_nf4 *q, qlora_bf16 *W_out, void *stream) {
+  int rc = check_nf4(q, false);
+  if (rc) return rc;
+  if (!W_out || !aligned16(W_out)) return fail(QLORA_EINVAL, "W_out must be non-NULL and 16-byte aligned");
+  if ((rc = check_device(nullptr))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  LAUNCH("dequant", launch_dequant(q->codes, q->absmax_q, q->absmax_step, q->n_out, q->n_in, W_out, codebook().lv, s));
+  return QLORA_OK;
+}
+
+int qlora_linear_fwd(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const qlora_bf16 *A, const qlora_bf16 *B,
+                     int32_t r, float alpha, qlora_bf16 *Y, qlora_bf16 *U_out, void *ws, size_t ws_bytes,
+                     void *stream) {
+  int rc = check_lora_args(T, q, A, B, r, alpha);
+  if (rc) return rc;
+  if (T > 0 && (!X || !Y)) return fail(QLORA_EINVAL, "X and Y must not be NULL");
+  if ((X && !aligned16(X)) || (Y && !aligned16(Y)) || (U_out && !aligned16(U_out)))
+    return fail(QLORA_EINVAL, "X, Y and U_out must be 16-byte aligned");
+  const int64_t N = q->n_out, K = q->n_in;
+  Plan p;
+  if ((rc = check_ws(QLORA_OP_FWD, T, N, K, r, ws, ws_bytes, &p))) return rc;
+  if ((rc = check_device(nullptr))) return rc;
+  if (T == 0) return QLORA_OK;
+  hipStream_t s = (hipStream_t)stream;
+  char *w = (char *)ws;
+  bf16_t *Bp = (bf16_t *)(w + p.off_bp);
+  bf16_t *V = (bf16_t *)(w + p.off_v);
+  float *part = (float *)(w + p.off_part);
+  const float sc = alpha / (float)r;
+  const Levels &lv = codebook().lv;
+  LAUNCH("pad_b", launch_pad_copy(B, r, r, N, Bp, p.rp, s));
+  LAUNCH("lora_u", launch_gemm_splitk(0, 0, X, K, A, K, T, r, K, p.su.kchunk, p.su.n, part, s));
+  LAUNCH("lora_u_finalize", launch_finalize(part, p.su.n, T, r, U_out, r, U_out ? r : 0, 1.0f, V, p.rp, p.rp, r, sc, s));
+  LAUNCH("nf4_gemm_fwd", launch_nf4_gemm_fwd(X, T, K, q->codes, q->absmax_q, q->absmax_step, N, V, Bp, p.rp, Y, lv, s));
+  return QLORA_OK;
+}
+
+int qlora_linear_bwd(const qlora_bf16 *X, const qlora_bf16 *dY, int64_t T, const qlora_nf4 *q, const qlora_bf16 *A,
+                     const qlora_bf16 *B, int32_t r, float alpha, const qlora_bf16 *U, qlora_bf16 *dX,
+                     qlora_bf16 *dA, qlora_bf16 *dB, void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_lora_args(T, q, A, B, r, alpha);
+  if (rc) return rc;
+  if (!dA || !dB) return fail(QLORA_EINVAL, "dA and dB must not be NULL");
+  if (T > 0 && (!X || !dY)) return fail(QLORA_EINVAL, "X and dY must not be NULL");
+  if ((X && !aligned16(X)) || (dY && !aligned16(dY)) || (U && !aligned16(U)) || (dX && !aligned16(dX)) ||
+      !aligned16(dA) || !aligned16(dB))
+    return fail(QLORA_EINVAL, "X, dY, U, dX, dA and dB must be 16-byte aligned");
+  const int64_t N = q->n_out, K = q->n_in;
+  Plan p;
+  if ((rc = check_ws(QLORA_OP_BWD, T, N, K, r, ws, ws_bytes, &p))) return rc;
+  if ((rc = check_device(nullptr))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  char *w = (char *)ws;
+  bf16_t *Bp = (bf16_t *)(w + p.off_bp);
+  bf16_t *Up = (bf16_t *)(w + p.off_v);
+  bf16_t *dUp = (bf16_t *)(w + p.off_du);
+  float *part = (float *)(w + p.off_part);
+  const float sc = alpha / (float)r;
+  const Levels &lv = codebook().lv;
+  if (T == 0) {  // empty batch: the gradients of A and B are sums over no tokens
+    LAUNCH("zero_da", launch_finalize(part, 0, r, K, dA, K, K, 1.0f, nullptr, 0, 0, 0, 0.f, s));
+    LAUNCH("zero_db", launch_finalize(part, 0, N, r, dB, r, r, 1.0f, nullptr, 0, 0, 0, 0.f, s));
+    return QLORA_OK;
+  }
+  LAUNCH("pad_b", launch_pad_copy(B, r, r, N, Bp, p.rp, s));
+  if (U) {
+    LAUNCH("pad_u", launch_pad_copy(U, r, r, T, Up, p.rp, s));
+  } else {
+    LAUNCH("lora_u", launch_gemm_splitk(0, 0, X, K, A, K, T, r, K, p.su.kchunk, p.su.n, part, s));
+    LAUNCH("lora_u_finalize", launch_finalize(part, p.su.n, T, r, nullptr, 0, 0, 0.f, Up, p.rp, p.rp, r, 1.0f, s));
+  }
+  // dU = s dY B  -> dUp [T, rp]
+  LAUNCH("lora_du", launch_gemm_splitk(0, 1, dY, N, Bp, p.rp, T, r, N, p.sdu.kchunk, p.sdu.n, part, s));
+  LAUNCH("lora_du_finalize", launch_finalize(part, p.sdu.n, T, r, nullptr, 0, 0, 0.f, dUp, p.rp, p.rp, r, sc, s));
+  // dB = s dY^T U  -> [N, r]
+  LAUNCH("lora_db", launch_gemm_splitk(1, 1, dY, N, Up, p.rp, N, r, T, p.sdb.kchunk, p.sdb.n, part, s));
+  LAUNCH("lora_db_finalize", launch_finalize(part, p.sdb.n, N, r, dB, r, r, sc, nullptr, 0, 0, 0, 0.f, s));
+  // dA = dU^T X  -> [r, K]
+  LAUNCH("lora_da", launch_gemm_splitk(1, 1, dUp, p.rp, X, K, r, K, T, p.sda.kchunk, p.sda.n, part, s));
+  LAUNCH("lora_da_finalize", launch_finalize(part, p.sda.n, r, K, dA, K, K, 1.0f, nullptr, 0, 0, 0, 0.f, s));
+  // dX = dY W' + dU A
+  if (dX)
+    LAUNCH("nf4_gemm_dx",
+           launch_nf4_gemm_dx(dY, T, N, q->codes, q->absmax_q, q->absmax_step, K, dUp, A, r, p.rp, dX, lv, s));
+  return QLORA_OK;
+}
+
+int qlora_timing_enable(const char *kernel, int enable) {
+  if (!kernel) return fail(QLORA_EINVAL, "kernel name is NULL");
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (enable)
+    g_timed = kernel;
+  else if (g_timed == kernel || !strcmp(kernel, "*"))
+    g_timed.clear();
+  return QLORA_OK;
+}
+
+int qlora_timing_read(const char *kernel, int64_t *launches, double *total_ms) {
+  if (!kernel || !launches || !total_ms) return fail(QLORA_EINVAL, "NULL argument");
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    auto it = g_events.find(kernel);
+    if (it != g_events.end()) {
+      ev.swap(it->second);
+      g_events.erase(it);
+    }
+  }
+  double tot = 0.0;
+  int rc = QLORA_OK;
+  for (auto &pr : ev) {
+    float ms = 0.f;
+    if (hipEventSynchronize(pr.second) != hipSuccess || hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess) {
+      (void)hipGetLastError();
+      rc = fail(QLORA_EHIP, "reading timing events failed");
+    }
+    tot += ms;
+    (void)hipEventDestroy(pr.first);
+    (void)hipEventDestroy(pr.second);
+  }
+  *launches = (int64_t)ev.size();
+  *total_ms = tot;
+  return rc;
+}
+
+}  // extern "C"

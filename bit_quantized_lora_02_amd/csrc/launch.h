@@ -1,0 +1,32 @@
+// launch.h -- host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlora {
+
+typedef uint16_t bf16_t;
+struct Levels;
+struct Thresholds;
+
+hipError_t launch_quantize_nf4(const float *W, int64_t n_out, int64_t n_in, uint8_t *codes, uint8_t *absmax_q,
+                               float *absmax_step, const Thresholds &thr, hipStream_t s);
+hipError_t launch_dequant(const uint8_t *codes, const uint8_t *absmax_q, const float *absmax_step, int64_t n_out,
+                          int64_t n_in, bf16_t *out, const Levels &lv, hipStream_t s);
+
+hipError_t launch_nf4_gemm_fwd(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
+                               const float *step, int64_t N, const bf16_t *V, const bf16_t *Bp, int64_t rp, bf16_t *Y,
+                               const Levels &lv, hipStream_t s);
+hipError_t launch_nf4_gemm_dx(const bf16_t *dY, int64_t T, int64_t N, const uint8_t *codes, const uint8_t *absmax_q,
+                              const float *step, int64_t K, const bf16_t *dUp, const bf16_t *A, int64_t r, int64_t rp,
+                              bf16_t *dX, const Levels &lv, hipStream_t s);
+
+hipError_t launch_gemm_splitk(int la, int lb, const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb, int64_t M,
+                              int64_t N, int64_t Kred, int64_t kchunk, int nsplit, float *C, hipStream_t s);
+hipError_t launch_finalize(const float *part, int nsplit, int64_t M, int64_t N, bf16_t *out1, int64_t ld1, int64_t n1,
+                           float scale1, bf16_t *out2, int64_t ld2, int64_t n2, int64_t nvalid2, float scale2,
+                           hipStream_t s);
+hipError_t launch_pad_copy(const bf16_t *in, int64_t ldi, int64_t ncols, int64_t M, bf16_t *out, int64_t ldo,
+                           hipStream_t s);
+
+}  // namespace qlora

@@ -1,0 +1,166 @@
+/*
+ * qlora.h -- C ABI of the MI355X (gfx950) NF4-quantized linear with a LoRA branch.
+ *
+ * The layer:  Y = X . deq(W)^T + s . (X . A^T) . B^T,   s = fl32(alpha / r),  no bias.
+ *
+ * Sources (page title, section):
+ *  - "What does QLoRA change compared with plain LoRA when fine-tuning Llama?"
+ *    (katajob.com), "NF4: 4-bit NormalFloat": 16 levels for a zero-centred
+ *    normal, per-block scaling over 64 contiguous weights, blocks expanded to
+ *    bf16 inside the matmul and discarded.  "Double quantization": the block
+ *    constants are stored in 8 bits with a second-level scale per group.
+ *    "What stays in full precision": A and B are bf16, gradients flow through
+ *    the dequantized weight, W is never written.
+ *  - "QLoRA: fine-tuning a large model on one GPU" (learn.pranaymahendrakar.com),
+ *    Researcher level, "LoRA, stated once": h = W0 x + (alpha/r) B A x, with
+ *    B of shape d x r and A of shape r x k; Developer level, the printed
+ *    adapter shapes lora_A (r, in) and lora_B (out, r).
+ *  - "qlora" (chipfoundryservices.com glossary), table "How QLoRA Works": quantize
+ *    at load, forward dequantizes then computes, backward in bf16, only the
+ *    adapter is trained.
+ *
+ * Conventions shared by every entry point
+ *  - Plain C types only.  bf16 tensors are passed as uint16_t bit patterns.
+ *  - Device pointers point to memory of the current HIP device; host pointers
+ *    are marked "host".  All tensors are dense and row-major.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    work is enqueued asynchronously on it; no entry point synchronizes the
+ *    host, allocates device memory or keeps a pointer after it returns.  The
+ *    caller keeps every buffer alive until the stream work is done.
+ *  - Argument checks run before any HIP call.  Failures return a negative
+ *    QLORA_E* code and leave a message for qlora_last_error(); nothing aborts
+ *    and no C++ exception crosses the ABI.  A device fault inside a kernel
+ *    surfaces at the caller's next synchronization, as usual for HIP.
+ *  - Inputs must be finite (a precondition, not checked).
+ *  - Device pointers must be 16-byte aligned.
+ */
+#ifndef QLORA_H
+#define QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t qlora_bf16; /* bf16 bit pattern */
+
+#define QLORA_OK 0
+#define QLORA_EINVAL (-1)     /* bad pointer, shape, rank, alignment or op          */
+#define QLORA_EWORKSPACE (-2) /* workspace smaller than qlora_workspace_bytes says  */
+#define QLORA_ENODEV (-3)     /* no HIP device, or the current device is not gfx950 */
+#define QLORA_EHIP (-4)       /* a HIP launch or runtime call failed                */
+
+#define QLORA_OP_FWD 0
+#define QLORA_OP_BWD 1
+
+#define QLORA_MAX_RANK 128
+
+/*
+ * An NF4 weight of logical shape [n_out, n_in] (katajob, "NF4" and "Double
+ * quantization").  Layout in device memory:
+ *   codes       [n_out * n_in / 2]  byte j holds element 2j (low nibble) and
+ *                                   element 2j+1 (high nibble) of the row-major
+ *                                   flattened weight; code i = i-th smallest level
+ *   absmax_q    [n_out * n_in / 64] 8-bit constant of each 64-element block
+ *   absmax_step [ceil(n_out * n_in / 16384)] binary32 step of each group of
+ *                                   256 consecutive block constants
+ * Decoding: w' = bf16_rne(fl32(level[code] * fl32(absmax_q[b] * absmax_step[b / 256]))).
+ * Requirements: n_in % 64 == 0 (a block never straddles a row), n_out % 8 == 0,
+ * n_out >= 8.  The struct itself is host memory; the three arrays are device
+ * memory owned by the caller.  qlora_linear_fwd/bwd never write them.
+ */
+typedef struct qlora_nf4 {
+  int64_t n_out;
+  int64_t n_in;
+  uint8_t *codes;
+  uint8_t *absmax_q;
+  float *absmax_step;
+} qlora_nf4;
+
+/* Byte sizes of the three NF4 arrays for [n_out, n_in] (host only, no HIP call).
+ * 4 + 8/64 + 32/16384 = 4.127 bits per weight (katajob, "Double quantization":
+ * 0.5 bit/weight of binary32 constants, of which double quantization saves
+ * roughly 0.37).  Returns QLORA_EINVAL on a shape the layout does not allow. */
+int qlora_nf4_storage(int64_t n_out, int64_t n_in, size_t *codes_bytes, size_t *absmax_q_bytes,
+                      size_t *absmax_step_bytes);
+
+/* The 16 NF4 levels, ascending, binary32, into host memory `levels` (no HIP
+ * call).  Construction: standard-normal quantiles at probabilities equally
+ * spaced between 1/2 and 1 - (1/30 + 1/32)/2, seven below zero and eight above,
+ * plus an exact zero, divided by the largest so the extremes are -1 and +1
+ * (katajob, "NF4": levels placed for a zero-centred normal). */
+int qlora_nf4_codebook(float levels[16]);
+
+/* Workspace bytes needed by `op` (QLORA_OP_FWD or QLORA_OP_BWD) for these
+ * sizes, into host *bytes (no HIP call).  The forward workspace is O(T*r + n_out*r),
+ * never O(n_out*n_in): the dequantized weight is never stored. */
+int qlora_workspace_bytes(int op, int64_t T, int64_t n_out, int64_t n_in, int32_t r, size_t *bytes);
+
+/* Quantize a binary32 weight W [n_out, n_in] (device) into q's arrays (device,
+ * caller-allocated with qlora_nf4_storage sizes).  Block absmax c_b over 64
+ * contiguous elements; code = nearest level to fl32(w / c_b), ties to the lower
+ * code, c_b = 0 gives code 7; per group of 256 constants, step d = fl32(max/255)
+ * and absmax_q = clamp(round_half_even(fl32(c_b / d)), 0, 255).  Codes use the
+ * exact binary32 c_b (katajob, "NF4" and "Double quantization"). */
+int qlora_quantize_nf4(const float *W, const qlora_nf4 *q, void *stream);
+
+/* Expand q to bf16 W_out [n_out, n_in] (device).  For tests and export only:
+ * the forward and backward never materialize the dequantized weight. */
+int qlora_dequant(const qlora_nf4 *q, qlora_bf16 *W_out, void *stream);
+
+/*
+ * Forward (pranaymahendrakar, "LoRA, stated once"; glossary, step 3):
+ *   U = X . A^T                               [T, r]
+ *   Y = X . deq(W)^T + s . U . B^T            [T, n_out],  s = fl32(alpha / r)
+ * X [T, n_in], A [r, n_in], B [n_out, r], Y [T, n_out] bf16, device.
+ * U_out [T, r] bf16 (device) receives U for the backward, or NULL.
+ * T >= 0 (T = 0 does nothing), 1 <= r <= QLORA_MAX_RANK.
+ * ws: device workspace of at least qlora_workspace_bytes(QLORA_OP_FWD, ...).
+ * Accumulation is binary32; Y is rounded to bf16 once.
+ */
+int qlora_linear_fwd(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const qlora_bf16 *A, const qlora_bf16 *B,
+                     int32_t r, float alpha, qlora_bf16 *Y, qlora_bf16 *U_out, void *ws, size_t ws_bytes,
+                     void *stream);
+
+/*
+ * Backward of the forward above with respect to X, A and B; W gets no gradient
+ * (katajob, "What stays in full precision"; glossary, step 4):
+ *   dU = s . dY . B                 [T, r]
+ *   dA = dU^T . X                   [r, n_in]
+ *   dB = s . dY^T . U               [n_out, r]
+ *   dX = dY . deq(W) + dU . A       [T, n_in]
+ * dY [T, n_out] bf16 device.  U [T, r] as saved by the forward, or NULL to
+ * recompute it from X and A.  dX may be NULL to skip it.  dA, dB, dX are
+ * overwritten (never accumulated); with T = 0, dA and dB are set to zero.
+ * ws: at least qlora_workspace_bytes(QLORA_OP_BWD, ...).  The reductions over
+ * T and n_out run in a fixed order, so results are bitwise repeatable.
+ */
+int qlora_linear_bwd(const qlora_bf16 *X, const qlora_bf16 *dY, int64_t T, const qlora_nf4 *q, const qlora_bf16 *A,
+                     const qlora_bf16 *B, int32_t r, float alpha, const qlora_bf16 *U, qlora_bf16 *dX,
+                     qlora_bf16 *dA, qlora_bf16 *dB, void *ws, size_t ws_bytes, void *stream);
+
+/* Static text for a QLORA_E* code. */
+const char *qlora_strerror(int code);
+
+/* Detail of the last failing call on this host thread ("" if none). */
+const char *qlora_last_error(void);
+
+/*
+ * Kernel timing for measurement (host).  While enabled, the library records a
+ * pair of HIP events on the launch stream around every launch of the kernel
+ * named `kernel` ("nf4_gemm_fwd", "nf4_gemm_dx", or "*" for all kernels).
+ * qlora_timing_read() waits for the recorded events, then returns the number
+ * of timed launches of `kernel` and their summed milliseconds, and clears the
+ * record.  Disabled by default; enabling it adds two event records per timed
+ * launch and nothing else.
+ */
+int qlora_timing_enable(const char *kernel, int enable);
+int qlora_timing_read(const char *kernel, int64_t *launches, double *total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_H */

@@ -1,0 +1,174 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+They load libqlora.so, check that it exports every function include/qlora.h
+declares, exercise the host-only entry points, and drive every argument-error
+path, all of which return before the library's first HIP call.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from bit_quantized_lora_02_amd import binding as B
+from conftest import gpu_available
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from bit_quantized_lora_02_amd import build as _build
+        _build.build()
+    return B.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert declared, "no declarations found"
+    assert sorted(B.EXPORTED) == declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_storage_sizes(lib, oracle):
+    for n_out, n_in in [(256, 256), (4096, 4096), (5, 4160), (28672, 8192), (1, 64)]:
+        assert B.storage_bytes(n_out, n_in) == oracle.storage_bytes(n_out, n_in)
+    cb, qb, sb = B.storage_bytes(4096, 4096)
+    assert 8.0 * (cb + qb + sb) / 4096 ** 2 == 4.126953125
+
+
+def test_codebook_matches_oracle_bitwise(lib, oracle):
+    got = np.array(B.codebook(), np.float32)
+    assert np.array_equal(got.view(np.uint32), oracle.nf4_levels().view(np.uint32))
+
+
+def test_workspace_never_scales_with_weight(lib):
+    T, r = 2048, 16
+    small = B.workspace_bytes(B.OP_FWD, T, 4096, 4096, r)
+    big = B.workspace_bytes(B.OP_FWD, T, 4096, 16 * 4096, r)
+    # forward workspace is O(T*r + n_out*r): 16x more input features adds no weight-sized buffer
+    assert big <= small * 4
+    deq_bytes = 2 * 4096 * 16 * 4096  # what a stored bf16 W' would take
+    assert big < deq_bytes // 100
+
+
+def _nf4(n_out, n_in, p=0x1000):
+    return B._NF4(n_out, n_in, p, p, p)
+
+
+def _err(fn, *args):
+    rc = fn(*args)
+    return rc, B.load_library().qlora_last_error().decode()
+
+
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: every check below fails first
+MIS = ctypes.c_void_p(0x10008)
+
+
+def test_error_paths_storage_and_workspace(lib):
+    c = ctypes.c_size_t()
+    assert lib.qlora_nf4_storage(4, 100, ctypes.byref(c), ctypes.byref(c), ctypes.byref(c)) == B.QLORA_EINVAL
+    assert lib.qlora_nf4_storage(0, 64, ctypes.byref(c), ctypes.byref(c), ctypes.byref(c)) == B.QLORA_EINVAL
+    assert lib.qlora_nf4_storage(4, 64, None, ctypes.byref(c), ctypes.byref(c)) == B.QLORA_EINVAL
+    assert lib.qlora_workspace_bytes(7, 1, 64, 64, 8, ctypes.byref(c)) == B.QLORA_EINVAL
+    assert lib.qlora_workspace_bytes(0, 1, 64, 64, 0, ctypes.byref(c)) == B.QLORA_EINVAL
+    assert lib.qlora_workspace_bytes(0, 1, 64, 64, 129, ctypes.byref(c)) == B.QLORA_EINVAL
+    assert lib.qlora_workspace_bytes(0, 1, 60, 64, 8, ctypes.byref(c)) == B.QLORA_EINVAL
+    assert lib.qlora_workspace_bytes(0, -1, 64, 64, 8, ctypes.byref(c)) == B.QLORA_EINVAL
+    assert lib.qlora_nf4_codebook(None) == B.QLORA_EINVAL
+    assert B.codebook()  # still fine afterwards
+
+
+def test_error_paths_quantize_dequant(lib):
+    q = _nf4(64, 64)
+    rc, msg = _err(lib.qlora_quantize_nf4, None, ctypes.byref(q), None)
+    assert rc == B.QLORA_EINVAL and "W" in msg
+    rc, _ = _err(lib.qlora_quantize_nf4, MIS, ctypes.byref(q), None)
+    assert rc == B.QLORA_EINVAL
+    bad = _nf4(64, 96)
+    rc, msg = _err(lib.qlora_quantize_nf4, FAKE, ctypes.byref(bad), None)
+    assert rc == B.QLORA_EINVAL and "64" in msg
+    nul = B._NF4(64, 64, 0x1000, None, 0x1000)
+    assert lib.qlora_quantize_nf4(FAKE, ctypes.byref(nul), None) == B.QLORA_EINVAL
+    mis = B._NF4(64, 64, 0x1004, 0x1000, 0x1000)
+    assert lib.qlora_quantize_nf4(FAKE, ctypes.byref(mis), None) == B.QLORA_EINVAL
+    assert lib.qlora_quantize_nf4(FAKE, None, None) == B.QLORA_EINVAL
+    assert lib.qlora_dequant(ctypes.byref(q), None, None) == B.QLORA_EINVAL
+    assert lib.qlora_dequant(ctypes.byref(q), MIS, None) == B.QLORA_EINVAL
+
+
+def _fwd(lib, X=FAKE, T=4, q=None, A=FAKE, Bm=FAKE, r=8, alpha=16.0, Y=FAKE, U=None, ws=FAKE, nb=1 << 30):
+    q = q if q is not None else _nf4(64, 64)
+    return lib.qlora_linear_fwd(X, T, ctypes.byref(q), A, Bm, r, alpha, Y, U, ws, nb, None)
+
+
+def _bwd(lib, X=FAKE, dY=FAKE, T=4, q=None, A=FAKE, Bm=FAKE, r=8, alpha=16.0, U=None, dX=FAKE, dA=FAKE, dB=FAKE,
+         ws=FAKE, nb=1 << 30):
+    q = q if q is not None else _nf4(64, 64)
+    return lib.qlora_linear_bwd(X, dY, T, ctypes.byref(q), A, Bm, r, alpha, U, dX, dA, dB, ws, nb, None)
+
+
+def test_error_paths_forward(lib):
+    E = B.QLORA_EINVAL
+    assert _fwd(lib, X=None) == E
+    assert _fwd(lib, Y=None) == E
+    assert _fwd(lib, A=None) == E
+    assert _fwd(lib, Bm=None) == E
+    assert _fwd(lib, r=0) == E
+    assert _fwd(lib, r=129) == E
+    assert _fwd(lib, T=-1) == E
+    assert _fwd(lib, alpha=float("inf")) == E
+    assert _fwd(lib, X=MIS) == E
+    assert _fwd(lib, U=MIS) == E
+    assert _fwd(lib, q=_nf4(64, 100)) == E
+    assert _fwd(lib, q=_nf4(60, 64)) == E  # n_out must be a multiple of 8 for the GEMMs
+    assert _fwd(lib, ws=MIS) == E
+    need = B.workspace_bytes(B.OP_FWD, 4, 64, 64, 8)
+    assert _fwd(lib, nb=need - 1) == B.QLORA_EWORKSPACE
+    assert "workspace" in lib.qlora_last_error().decode()
+
+
+def test_error_paths_backward(lib):
+    E = B.QLORA_EINVAL
+    assert _bwd(lib, dA=None) == E
+    assert _bwd(lib, dB=None) == E
+    assert _bwd(lib, dY=None) == E
+    assert _bwd(lib, X=None) == E
+    assert _bwd(lib, dX=MIS) == E
+    assert _bwd(lib, U=MIS) == E
+    assert _bwd(lib, r=200) == E
+    need = B.workspace_bytes(B.OP_BWD, 4, 64, 64, 8)
+    assert _bwd(lib, nb=need - 1) == B.QLORA_EWORKSPACE
+
+
+def test_strerror(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert lib.qlora_strerror(code)
+    assert lib.qlora_strerror(-99) == b"unknown error"
+
+
+@pytest.mark.skipif(gpu_available(), reason="checks the no-device path")
+def test_no_device_is_reported(lib):
+    """With valid-looking arguments and no GPU, the device check fails cleanly (no launch)."""
+    q = _nf4(64, 64)
+    assert lib.qlora_quantize_nf4(FAKE, ctypes.byref(q), None) == B.QLORA_ENODEV
+    assert _fwd(lib) == B.QLORA_ENODEV
+    assert _bwd(lib) == B.QLORA_ENODEV
+
+
+def test_timing_api_host_only(lib):
+    n, ms = B.timing_read("nf4_gemm_fwd")
+    assert n == 0 and ms == 0.0
+    B.timing_enable("nf4_gemm_fwd", True)
+    B.timing_enable("nf4_gemm_fwd", False)
+    assert lib.qlora_timing_enable(None, 1) == B.QLORA_EINVAL
