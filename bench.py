@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of the NF4 + LoRA linear on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config attn_4096]
+
+A step is one training pass of the layer over one batch: forward (U = X A^T,
+Y = X W'^T + s U B^T) and backward (dU, dB, dA, dX) through the C ABI, with
+every input already in HBM.  Quantization happens once before timing (the
+method quantizes at load time) and is reported separately as quantize_ms.
+The default workload is the attention-projection linear: NF4 W 4096 x 4096,
+T = 2048 tokens, r = 16, alpha = 32.  ``--config small_token`` times the
+forward alone, as that workload is defined.
+
+Prints one JSON line: throughput in TFLOP/s of algorithmic work
+(fwd 2TNK + 2Tr(K+N), bwd 2TNK + 4Tr(K+N)), the 4-bit weight-stream GB/s, a
+roofline entry for the dominant kernel timed live with HIP events recorded
+around its launches, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NF4+LoRA linear fwd+bwd TFLOP/s and 4-bit weight GB/s, % of MI355X roofline"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
+WORKLOAD_TEXT = {
+    "attn_4096": "attention projection: NF4 W 4096x4096 (block 64, double-quant groups of 256), T=2048, r=16, alpha=32",
+    "mlp_8b": "8B-class MLP: gate/up 14336x4096, down 4096x14336, NF4 with 1% outliers, T=4096, r=64, alpha=16",
+    "layer_70b": "70B-class layer: q,o 8192x8192, k,v 1024x8192, gate/up 28672x8192, down 8192x28672, T=4096, r=64",
+    "small_token": "small-token forward: NF4 W {n}x8192, T={t}, r=16, alpha=32",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="attn_4096", choices=["attn_4096", "mlp_8b", "layer_70b", "small_token"])
+    ap.add_argument("--tokens", type=int, default=1, help="T for --config small_token")
+    ap.add_argument("--wide", action="store_true", help="28672x8192 instead of 8192x8192 for small_token")
+    ap.add_argument("--copies", type=int, default=4, help="rotating input/weight copies (defeats the 256 MB MALL)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 256 MiB (scales rocprofv3 FETCH_SIZE/WRITE_SIZE)")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for name in ("nf4_gemm.hip", "device.h"):
+        with open(os.path.join(ROOT, "bit_quantized_lora_02_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch from a committed counter summary, if it matches the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_digest") != source_digest():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def linears_for(args):
+    from bit_quantized_lora_02_amd.synth import CONFIGS
+    c = CONFIGS[args.config]
+    if args.config == "small_token":
+        name, n_out, n_in = c["linears"][1 if args.wide else 0]
+        return [(name, n_out, n_in)], args.tokens, c["r"], c["alpha"], c["outliers"], False
+    return c["linears"], c["T"], c["r"], c["alpha"], c["outliers"], True
+
+
+def cpu_baseline(inp, train: bool, target_s: float):
+    """The oracle as it is, on the first linear, for a token slice sized to ~target_s seconds."""
+    import numpy as np
+
+    import oracle
+    n_out, n_in = inp.W.shape
+    r = inp.A.shape[0]
+    T = inp.X.shape[0]
+    oc, oq, od = oracle.quantize_nf4(inp.W)
+    Wd = oracle.dequant(oc, oq, od, n_out, n_in)
+
+    def run(ts):
+        X = inp.X[:ts]
+        t0 = time.perf_counter()
+        oracle.linear_fwd(X, Wd, inp.A, inp.B, inp.alpha)
+        if train:
+            oracle.linear_bwd(X, inp.dY[:ts], Wd, inp.A, inp.B, inp.alpha)
+        return time.perf_counter() - t0
+
+    ts = min(T, 8)
+    dt = run(ts)
+    ts = int(max(1, min(T, ts * target_s / max(dt, 1e-3))))
+    dt = run(ts)
+    fl = flops_linear(ts, n_out, n_in, r, train)
+    kind = "fwd+bwd" if train else "fwd"
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{kind} of the {n_out}x{n_in} linear on the first {ts} of {T} tokens "
+                      f"({dt:.1f} s, binary64 C oracle, OpenMP)", "seconds": dt, "tokens": ts}
+
+
+def flops_linear(T, N, K, r, train):
+    f = 2 * T * N * K + 2 * T * r * (K + N)
+    if train:
+        f += 2 * T * N * K + 4 * T * r * (K + N)
+    return f
+
+
+def weight_bytes(N, K):
+    nblk = N * K // 64
+    return N * K // 2 + nblk + 4 * ((nblk + 255) // 256)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this NF4 + LoRA linear runs on a single MI355X "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from bit_quantized_lora_02_amd import binding as B
+    from bit_quantized_lora_02_amd.synth import linear_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.calibrate_copy:
+        nbytes = 256 << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": nbytes, "bytes_written": nbytes, "launches": 5}))
+        return
+
+    lins, T, r, alpha, outliers, train = linears_for(args)
+    layers = []
+    first_inp = None
+    t_quant = 0.0
+    for li, (name, n_out, n_in) in enumerate(lins):
+        inp = linear_inputs(n_out, n_in, T, r, alpha, seed=li, outlier_frac=outliers, make_dy=train)
+        if first_inp is None:
+            first_inp = inp
+        Wg = torch.from_numpy(inp.W).to(dev)
+        g = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        w = B.quantize_nf4(Wg)
+        torch.cuda.synchronize()
+        t_quant += time.perf_counter() - t0
+        del Wg
+        X, A, Bm = g(inp.X), g(inp.A), g(inp.B)
+        dY = g(inp.dY) if train else None
+        copies = []
+        for c in range(max(1, args.copies)):
+            wc = w if c == 0 else B.NF4Weight(w.n_out, w.n_in, w.codes.clone(), w.absmax_q.clone(),
+                                              w.absmax_step.clone())
+            copies.append(dict(w=wc, X=X if c == 0 else X.clone(), dY=(dY if c == 0 else dY.clone()) if train else None,
+                               Y=torch.empty((T, n_out), dtype=torch.bfloat16, device=dev),
+                               U=torch.empty((T, r), dtype=torch.bfloat16, device=dev),
+                               dX=torch.empty((T, n_in), dtype=torch.bfloat16, device=dev) if train else None))
+        layers.append(dict(name=name, n_out=n_out, n_in=n_in, A=A, B=Bm, copies=copies,
+                           dA=torch.empty_like(A), dB=torch.empty_like(Bm),
+                           ws_f=torch.empty(max(1, B.workspace_bytes(B.OP_FWD, T, n_out, n_in, r)), dtype=torch.uint8,
+                                            device=dev),
+                           ws_b=torch.empty(max(1, B.workspace_bytes(B.OP_BWD, T, n_out, n_in, r)), dtype=torch.uint8,
+                                            device=dev) if train else None))
+
+    def step(i):
+        for L in layers:
+            c = L["copies"][i % len(L["copies"])]
+            B.linear_fwd(c["X"], c["w"], L["A"], L["B"], alpha, ws=L["ws_f"], out=c["Y"], u_out=c["U"])
+            if train:
+                B.linear_bwd(c["X"], c["dY"], c["w"], L["A"], L["B"], alpha, U=c["U"], ws=L["ws_b"],
+                             outs=(c["dX"], L["dA"], L["dB"]))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    timed = ["nf4_gemm_fwd", "nf4_gemm_dx"] if train else ["nf4_gemm_fwd"]
+    for k in timed:
+        B.timing_read(k)  # clear
+        B.timing_enable(k, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    for k in timed:
+        B.timing_enable(k, False)
+    ktimes = {k: B.timing_read(k) for k in timed}
+
+    ms_step = elapsed / args.steps * 1e3
+    fl_step = sum(flops_linear(T, L["n_out"], L["n_in"], r, train) for L in layers)
+    wb_step = sum(weight_bytes(L["n_out"], L["n_in"]) for L in layers) * (2 if train else 1)
+    tflops = fl_step / (elapsed / args.steps) / 1e12
+    wgbps = wb_step / (elapsed / args.steps) / 1e9
+
+    # per-kernel algorithmic work per launch, summed over the layers of one step
+    kflops = {
+        "nf4_gemm_fwd": sum(2 * T * L["n_out"] * (L["n_in"] + r) for L in layers),
+        "nf4_gemm_dx": sum(2 * T * L["n_in"] * (L["n_out"] + r) for L in layers),
+    }
+    kbytes = {  # compulsory HBM bytes of one launch: weight stream + activations in and out + LoRA operands
+        "nf4_gemm_fwd": sum(weight_bytes(L["n_out"], L["n_in"]) + 2 * T * (L["n_in"] + L["n_out"]) +
+                            2 * (T + L["n_out"]) * r for L in layers),
+        "nf4_gemm_dx": sum(weight_bytes(L["n_out"], L["n_in"]) + 2 * T * (L["n_in"] + L["n_out"]) +
+                           2 * (T + L["n_in"]) * r for L in layers),
+    }
+    kernels = {}
+    for k, (n, ms) in ktimes.items():
+        per_step_launches = n / args.steps if args.steps else 0
+        avg_ms = ms / n if n else float("nan")
+        kernels[k] = {"launches": n, "avg_ms_per_launch": avg_ms,
+                      "ms_per_step": ms / args.steps,
+                      "tflops": kflops[k] / (ms / args.steps * 1e-3) / 1e12 if ms else None,
+                      "gbps": kbytes[k] / (ms / args.steps * 1e-3) / 1e9 if ms else None,
+                      "launches_per_step": per_step_launches}
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    kd = kernels[dom]
+    wl = args.config if args.config != "small_token" else f"small_token_{lins[0][1]}x8192_T{T}"
+    traffic = traffic_from_profiles(dom, wl)
+    if train or T > 80:
+        roof = {"bound": "mfma", "achieved": kd["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": kd["tflops"] / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": dom,
+                "avg_ms_per_launch": kd["avg_ms_per_launch"]}
+    else:
+        roof = {"bound": "hbm", "achieved": kd["gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": kd["gbps"] / PEAK_HBM_GBPS, "traffic": traffic, "kernel": dom,
+                "avg_ms_per_launch": kd["avg_ms_per_launch"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(first_inp, train, args.cpu_seconds)
+
+    text = WORKLOAD_TEXT[args.config].format(n=lins[0][1], t=T)
+    line = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": text, "name": wl, "tokens": T, "rank": r, "alpha": alpha,
+                   "pass": "fwd+bwd" if train else "fwd",
+                   "linears": [[L["name"], L["n_out"], L["n_in"]] for L in layers],
+                   "parallelism": "single GPU"},
+        "weight_stream_GBps": wgbps,
+        "weight_stream_frac_hbm": wgbps / PEAK_HBM_GBPS,
+        "quantize_ms": t_quant * 1e3,
+        "roofline": roof,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

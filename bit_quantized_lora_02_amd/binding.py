@@ -187,15 +187,18 @@ def _workspace(op, T, w: NF4Weight, r) -> tuple[torch.Tensor | None, int]:
 
 
 def linear_fwd(X: torch.Tensor, w: NF4Weight, A: torch.Tensor, B: torch.Tensor, alpha: float,
-               save_u: bool = True, ws: torch.Tensor | None = None, out: torch.Tensor | None = None):
-    """Y = X . deq(W)^T + (alpha/r) (X A^T) B^T; returns (Y, U or None)."""
+               save_u: bool = True, ws: torch.Tensor | None = None, out: torch.Tensor | None = None,
+               u_out: torch.Tensor | None = None):
+    """Y = X . deq(W)^T + (alpha/r) (X A^T) B^T; returns (Y, U or None).
+
+    ``out``/``u_out`` are optional preallocated [T, n_out] / [T, r] bf16 buffers."""
     X, A, B = _bits(X), _bits(A), _bits(B)
     T, r = X.shape[0], A.shape[0]
     if X.shape[1] != w.n_in or A.shape != (r, w.n_in) or B.shape != (w.n_out, r):
         raise ValueError(f"shape mismatch: X {tuple(X.shape)}, A {tuple(A.shape)}, B {tuple(B.shape)}, "
                          f"W [{w.n_out}, {w.n_in}]")
     Y = out if out is not None else torch.empty((T, w.n_out), dtype=torch.bfloat16, device=X.device)
-    U = torch.empty((T, r), dtype=torch.bfloat16, device=X.device) if save_u else None
+    U = u_out if u_out is not None else (torch.empty((T, r), dtype=torch.bfloat16, device=X.device) if save_u else None)
     if ws is None:
         ws, nb = _workspace(OP_FWD, T, w, r)
     else:

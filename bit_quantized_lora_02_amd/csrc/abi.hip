@@ -120,8 +120,14 @@ bool debug_sync() {
 
 // --------------------------------------------------------------- timing
 std::mutex g_tmu;
-std::string g_timed;  // "" = off, "*" = all
+std::vector<std::string> g_timed;  // kernel names being timed; "*" = all
 std::map<std::string, std::vector<std::pair<hipEvent_t, hipEvent_t>>> g_events;
+
+bool is_timed(const char *kname) {
+  for (const auto &n : g_timed)
+    if (n == "*" || n == kname) return true;
+  return false;
+}
 
 struct Timed {
   hipEvent_t a = nullptr, b = nullptr;
@@ -129,7 +135,7 @@ struct Timed {
   hipStream_t s;
   Timed(const char *kname, hipStream_t st) : s(st) {
     std::lock_guard<std::mutex> lk(g_tmu);
-    if (g_timed.empty() || (g_timed != "*" && g_timed != kname)) return;
+    if (!is_timed(kname)) return;
     if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
       (void)hipGetLastError();
       a = b = nullptr;
@@ -412,10 +418,16 @@ int qlora_linear_bwd(const qlora_bf16 *X, const qlora_bf16 *dY, int64_t T, const
 int qlora_timing_enable(const char *kernel, int enable) {
   if (!kernel) return fail(QLORA_EINVAL, "kernel name is NULL");
   std::lock_guard<std::mutex> lk(g_tmu);
-  if (enable)
-    g_timed = kernel;
-  else if (g_timed == kernel || !strcmp(kernel, "*"))
+  if (!strcmp(kernel, "*") && !enable) {
     g_timed.clear();
+    return QLORA_OK;
+  }
+  for (auto it = g_timed.begin(); it != g_timed.end(); ++it)
+    if (*it == kernel) {
+      g_timed.erase(it);
+      break;
+    }
+  if (enable) g_timed.push_back(kernel);
   return QLORA_OK;
 }
 

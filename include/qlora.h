@@ -67,8 +67,9 @@ typedef uint16_t qlora_bf16; /* bf16 bit pattern */
  *   absmax_step [ceil(n_out * n_in / 16384)] binary32 step of each group of
  *                                   256 consecutive block constants
  * Decoding: w' = bf16_rne(fl32(level[code] * fl32(absmax_q[b] * absmax_step[b / 256]))).
- * Requirements: n_in % 64 == 0 (a block never straddles a row), n_out % 8 == 0,
- * n_out >= 8.  The struct itself is host memory; the three arrays are device
+ * Requirements: n_in % 64 == 0 (a block never straddles a row) and n_out >= 1;
+ * qlora_linear_fwd/bwd also need n_out % 8 == 0 (16-byte rows of dY and Y).
+ * Both sizes are at most 2^22.  The struct itself is host memory; the three arrays are device
  * memory owned by the caller.  qlora_linear_fwd/bwd never write them.
  */
 typedef struct qlora_nf4 {
@@ -150,7 +151,8 @@ const char *qlora_last_error(void);
 /*
  * Kernel timing for measurement (host).  While enabled, the library records a
  * pair of HIP events on the launch stream around every launch of the kernel
- * named `kernel` ("nf4_gemm_fwd", "nf4_gemm_dx", or "*" for all kernels).
+ * named `kernel` ("nf4_gemm_fwd", "nf4_gemm_dx", ..., or "*" for all kernels).
+ * Several names can be enabled at once; disabling "*" disables every name.
  * qlora_timing_read() waits for the recorded events, then returns the number
  * of timed launches of `kernel` and their summed milliseconds, and clears the
  * record.  Disabled by default; enabling it adds two event records per timed
