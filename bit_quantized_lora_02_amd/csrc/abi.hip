@@ -361,7 +361,8 @@ int qlora_linear_fwd(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const q
   LAUNCH("pad_b", launch_pad_copy(B, r, r, N, Bp, p.rp, s));
   LAUNCH("lora_u", launch_gemm_splitk(0, 0, X, K, A, K, T, r, K, p.su.kchunk, p.su.n, part, s));
   LAUNCH("lora_u_finalize", launch_finalize(part, p.su.n, T, r, U_out, r, U_out ? r : 0, 1.0f, V, p.rp, p.rp, r, sc, s));
-  LAUNCH("nf4_gemm_fwd", launch_nf4_gemm_fwd(X, T, K, q->codes, q->absmax_q, q->absmax_step, N, V, Bp, p.rp, Y, lv, s));
+  LAUNCH("nf4_gemm_fwd", launch_nf4_gemm_fwd(nf4_gemm_pick_tile(T, N), X, T, K, q->codes, q->absmax_q,
+                                             q->absmax_step, N, V, Bp, p.rp, Y, lv, s));
   return QLORA_OK;
 }
 
@@ -411,7 +412,8 @@ int qlora_linear_bwd(const qlora_bf16 *X, const qlora_bf16 *dY, int64_t T, const
   // dX = dY W' + dU A
   if (dX)
     LAUNCH("nf4_gemm_dx",
-           launch_nf4_gemm_dx(dY, T, N, q->codes, q->absmax_q, q->absmax_step, K, dUp, A, r, p.rp, dX, lv, s));
+           launch_nf4_gemm_dx(nf4_gemm_pick_tile(T, K), dY, T, N, q->codes, q->absmax_q, q->absmax_step, K, dUp, A,
+                              r, p.rp, dX, lv, s));
   return QLORA_OK;
 }
 

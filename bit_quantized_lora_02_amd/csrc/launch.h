@@ -14,12 +14,16 @@ hipError_t launch_quantize_nf4(const float *W, int64_t n_out, int64_t n_in, uint
 hipError_t launch_dequant(const uint8_t *codes, const uint8_t *absmax_q, const float *absmax_step, int64_t n_out,
                           int64_t n_in, bf16_t *out, const Levels &lv, hipStream_t s);
 
-hipError_t launch_nf4_gemm_fwd(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
-                               const float *step, int64_t N, const bf16_t *V, const bf16_t *Bp, int64_t rp, bf16_t *Y,
-                               const Levels &lv, hipStream_t s);
-hipError_t launch_nf4_gemm_dx(const bf16_t *dY, int64_t T, int64_t N, const uint8_t *codes, const uint8_t *absmax_q,
-                              const float *step, int64_t K, const bf16_t *dUp, const bf16_t *A, int64_t r, int64_t rp,
-                              bf16_t *dX, const Levels &lv, hipStream_t s);
+// Output-tile shapes of the fused NF4 GEMMs (rows x columns of the output).
+enum { NF4_TILE_128x128 = 0, NF4_TILE_256x256_W8 = 3 };
+int nf4_gemm_pick_tile(int64_t M, int64_t N);
+
+hipError_t launch_nf4_gemm_fwd(int tile, const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes,
+                               const uint8_t *absmax_q, const float *step, int64_t N, const bf16_t *V,
+                               const bf16_t *Bp, int64_t rp, bf16_t *Y, const Levels &lv, hipStream_t s);
+hipError_t launch_nf4_gemm_dx(int tile, const bf16_t *dY, int64_t T, int64_t N, const uint8_t *codes,
+                              const uint8_t *absmax_q, const float *step, int64_t K, const bf16_t *dUp, const bf16_t *A,
+                              int64_t r, int64_t rp, bf16_t *dX, const Levels &lv, hipStream_t s);
 
 hipError_t launch_gemm_splitk(int la, int lb, const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb, int64_t M,
                               int64_t N, int64_t Kred, int64_t kchunk, int nsplit, float *C, hipStream_t s);

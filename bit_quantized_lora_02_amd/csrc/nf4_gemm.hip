@@ -8,17 +8,19 @@
 //   forward   Y  = X . W'^T + V . Bp^T      V = bf16(s . X . A^T), Bp = B (padded)
 //   backward  dX = dY . W'  + dUp . A       dUp = bf16(s . dY . B) (padded)
 //
-// Each workgroup computes a 128x128 output tile with 4 waves (2x2, 64x64 per
-// wave, 2x2 tiles of v_mfma_f32_32x32x16_bf16).  The reduction runs in steps
-// of 64: the A operand (activations) is copied global -> registers -> LDS, the
-// B operand is decoded from nibbles in registers and written to LDS as bf16,
-// so the dequantized weight exists only as one 128x64 tile in LDS.  The LoRA
-// term is appended as extra reduction steps over the padded rank, so it lands
-// in the same binary32 accumulators.  LDS is double buffered: the global loads
-// for step s+1 are issued before the MFMAs of step s.
+// A workgroup of WAVES_M x WAVES_N waves computes a BM x BN output tile; each
+// wave owns WM x WN tiles of v_mfma_f32_32x32x16_bf16 (32x32 outputs each).
+// The reduction runs in steps of 64 (one NF4 block per weight row): the A
+// operand (activations) goes global -> registers -> LDS; the B operand is
+// decoded from nibbles in registers and written to LDS as bf16, so the
+// dequantized weight exists only as one BN x 64 tile in LDS.  LDS is double
+// buffered and the global loads of step s+1 are issued before the MFMAs of
+// step s, so one barrier per step separates the two.  The LoRA term follows as
+// a few unpipelined extra reduction steps over the padded rank, landing in the
+// same binary32 accumulators.
 //
 // LDS tiles are [row][64] bf16 (128-byte rows) with the 16-byte chunk index
-// XOR-swizzled by (row & 7), so the 32 rows a wave reads per MFMA operand fall
+// XOR-swizzled by (row & 7), so the 8 rows that 8 consecutive lanes read fall
 // on distinct banks.
 #include "device.h"
 #include "launch.h"
@@ -26,287 +28,385 @@
 namespace qlora {
 
 namespace {
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int NT = 256;
+
+constexpr int BK = 64;
+
+template <int WAVES_M_, int WAVES_N_, int WM_, int WN_>
+struct TileCfg {
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, WM = WM_, WN = WN_;
+  static constexpr int NT = 64 * WAVES_M * WAVES_N;
+  static constexpr int BM = WAVES_M * WM * 32;
+  static constexpr int BN = WAVES_N * WN * 32;
+  static constexpr int A_CH = BM * 8 / NT;   // 16-byte chunks of the A tile per thread and step
+  static constexpr int C_CH = BN * 2 / NT;   // 16-byte chunks of codes (32 nibbles) per thread (forward)
+  static constexpr int L_CH = BN * 8 / NT;   // 16-byte bf16 chunks of the LoRA B tile per thread (forward)
+  static_assert(A_CH >= 1 && C_CH >= 1 && L_CH >= 1, "unsupported tile");
+};
 
 __device__ __forceinline__ int lds_off(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
 
-// Copy a [128 x 64] bf16 tile of a row-major matrix (row stride ld elements)
-// into registers: thread t takes rows (t>>3) + 32i, 16-byte chunk (t&7).  Rows
-// at or past `rows` and columns at or past `cols` read as zero (cols % 8 == 0).
-__device__ __forceinline__ void load_act_tile(const bf16_t *__restrict__ src, int64_t ld, int64_t row0, int64_t rows,
-                                              int64_t col0, int64_t cols, int tid, u32x4_t r[4]) {
-  const int chunk = tid & 7;
+template <class C>
+__device__ __forceinline__ void zero_acc(f32x16_t acc[C::WM][C::WN]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t row = row0 + (tid >> 3) + 32 * i;
-    const int64_t col = col0 + chunk * 8;
-    if (row < rows && col < cols)
-      r[i] = *reinterpret_cast<const u32x4_t *>(src + row * ld + col);
-    else
-      r[i] = u32x4_t{0u, 0u, 0u, 0u};
+  for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+}
+
+// Rows [row0, row0+BM) x columns [col0, col0+64) of a row-major bf16 matrix
+// into registers: chunk c = tid + NT*i covers row c>>3, 16-byte chunk c&7.
+// Rows >= rows or columns >= cols read as zero (cols % 8 == 0).
+template <class C>
+__device__ __forceinline__ void load_a(const bf16_t *__restrict__ src, int64_t ld, int64_t row0, int64_t rows,
+                                       int64_t col0, int64_t cols, int tid, u32x4_t r[C::A_CH]) {
+#pragma unroll
+  for (int i = 0; i < C::A_CH; ++i) {
+    const int c = tid + C::NT * i;
+    const int64_t row = row0 + (c >> 3), col = col0 + (c & 7) * 8;
+    r[i] = (row < rows && col < cols) ? *reinterpret_cast<const u32x4_t *>(src + row * ld + col)
+                                      : u32x4_t{0u, 0u, 0u, 0u};
   }
 }
 
-__device__ __forceinline__ void store_act_tile(bf16_t *s, int tid, const u32x4_t r[4]) {
-  const int chunk = tid & 7;
+template <class C>
+__device__ __forceinline__ void store_a(bf16_t *s, int tid, const u32x4_t r[C::A_CH]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (tid >> 3) + 32 * i;
-    *reinterpret_cast<u32x4_t *>(s + lds_off(row, chunk)) = r[i];
+  for (int i = 0; i < C::A_CH; ++i) {
+    const int c = tid + C::NT * i;
+    *reinterpret_cast<u32x4_t *>(s + lds_off(c >> 3, c & 7)) = r[i];
   }
 }
 
-// 2x2 wave grid, 64x64 per wave: one 64-deep reduction step out of LDS.
+// One 64-deep reduction step out of LDS for this wave's WM x WN MFMA tiles.
+template <class C>
 __device__ __forceinline__ void mma_step(const bf16_t *sA, const bf16_t *sB, int wm, int wn, int lane,
-                                         f32x16_t acc[2][2]) {
+                                         f32x16_t acc[C::WM][C::WN]) {
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     const int chunk = kk * 2 + (lane >> 5);
-    u32x4_t a[2], b[2];
+    u32x4_t a[C::WM], b[C::WN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ra = wm * 64 + i * 32 + (lane & 31);
+    for (int i = 0; i < C::WM; ++i) {
+      const int ra = (wm * C::WM + i) * 32 + (lane & 31);
       a[i] = *reinterpret_cast<const u32x4_t *>(sA + lds_off(ra, chunk));
-      const int rb = wn * 64 + i * 32 + (lane & 31);
-      b[i] = *reinterpret_cast<const u32x4_t *>(sB + lds_off(rb, chunk));
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < C::WN; ++j) {
+      const int rb = (wn * C::WN + j) * 32 + (lane & 31);
+      b[j] = *reinterpret_cast<const u32x4_t *>(sB + lds_off(rb, chunk));
+    }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16(a[i], b[j], acc[i][j]);
+    for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::WN; ++j) acc[i][j] = mfma_32x32x16(a[i], b[j], acc[i][j]);
   }
 }
 
-__device__ __forceinline__ void store_tile_out(bf16_t *__restrict__ out, int64_t ld, int64_t m0, int64_t rows,
-                                               int64_t n0, int64_t cols, int wm, int wn, int lane,
-                                               const f32x16_t acc[2][2]) {
+template <class C>
+__device__ __forceinline__ void store_out(bf16_t *__restrict__ out, int64_t ld, int64_t m0, int64_t rows, int64_t n0,
+                                          int64_t cols, int wm, int wn, int lane, const f32x16_t acc[C::WM][C::WN]) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < C::WM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < C::WN; ++j) {
+      const int64_t col = n0 + (wn * C::WN + j) * 32 + (lane & 31);
       if (col >= cols) continue;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * 64 + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+        const int64_t row = m0 + (wm * C::WM + i) * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
         if (row < rows) out[row * ld + col] = f32_to_bf16(acc[i][j][e]);
       }
     }
 }
+
 }  // namespace
 
 // ---------------------------------------------------------------- forward
 // Y[T, N] = X[T, K] . W'[N, K]^T + V[T, rp] . Bp[N, rp]^T
-__global__ __launch_bounds__(NT) void k_nf4_gemm_fwd(const bf16_t *__restrict__ X, int64_t T, int64_t K,
-                                                     const uint8_t *__restrict__ codes,
-                                                     const uint8_t *__restrict__ absmax_q,
-                                                     const float *__restrict__ step, int64_t N,
-                                                     const bf16_t *__restrict__ V, const bf16_t *__restrict__ Bp,
-                                                     int64_t rp, bf16_t *__restrict__ Y, Levels lv) {
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * BK];
+template <class C>
+__global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict__ X, int64_t T, int64_t K,
+                                                        const uint8_t *__restrict__ codes,
+                                                        const uint8_t *__restrict__ absmax_q,
+                                                        const float *__restrict__ step, int64_t N,
+                                                        const bf16_t *__restrict__ V, const bf16_t *__restrict__ Bp,
+                                                        int64_t rp, bf16_t *__restrict__ Y, Levels lv) {
+  __shared__ __attribute__((aligned(16))) bf16_t sA[2][C::BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t sB[2][C::BN * BK];
   __shared__ float s_lv[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int64_t m0 = (int64_t)blockIdx.y * C::BM, n0 = (int64_t)blockIdx.x * C::BN;
   levels_to_lds(lv, s_lv, tid);
 
-  const int nk = (int)(K / BK), nsteps = nk + (int)(rp / BK);
-  // B-operand loader: row (tid >> 1) of the tile, 32 consecutive k from (tid & 1) * 32
-  const int brow = tid >> 1, bhalf = tid & 1;
-  const int64_t wrow = n0 + brow;
-  const bool wrow_ok = wrow < N;
+  const int nk = (int)(K / BK);
+  u32x4_t ra[C::A_CH];
+  u32x4_t rc[C::C_CH];
+  float rcq[C::C_CH];
 
-  u32x4_t ra[4], rb[4];
-  uint32_t rc[4];
-  float rcq = 0.f;
-
-  auto load_step = [&](int s) {
-    if (s < nk) {
-      const int64_t k0 = (int64_t)s * BK;
-      load_act_tile(X, K, m0, T, k0, K, tid, ra);
-      if (wrow_ok) {
-        u32x4_t c = *reinterpret_cast<const u32x4_t *>(codes + wrow * (K / 2) + k0 / 2 + bhalf * 16);
-        rc[0] = c.x; rc[1] = c.y; rc[2] = c.z; rc[3] = c.w;
-        rcq = block_scale(absmax_q, step, wrow * (K / BK) + s);
-      } else {
-        rc[0] = rc[1] = rc[2] = rc[3] = 0x77777777u;
-        rcq = 0.f;
-      }
-    } else {
-      const int64_t k0 = (int64_t)(s - nk) * BK;
-      load_act_tile(V, rp, m0, T, k0, rp, tid, ra);
+  auto load_main = [&](int s) {
+    const int64_t k0 = (int64_t)s * BK;
+    load_a<C>(X, K, m0, T, k0, K, tid, ra);
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        rb[c] = wrow_ok ? *reinterpret_cast<const u32x4_t *>(Bp + wrow * rp + k0 + bhalf * 32 + c * 8)
-                        : u32x4_t{0u, 0u, 0u, 0u};
+    for (int i = 0; i < C::C_CH; ++i) {
+      const int c = tid + C::NT * i;
+      const int64_t wrow = n0 + (c >> 1);
+      if (wrow < N) {
+        rc[i] = *reinterpret_cast<const u32x4_t *>(codes + wrow * (K / 2) + k0 / 2 + (c & 1) * 16);
+        rcq[i] = block_scale(absmax_q, step, wrow * (K / BK) + s);
+      } else {
+        rc[i] = u32x4_t{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
+        rcq[i] = 0.f;
+      }
     }
   };
-  auto store_step = [&](int s, int buf) {
-    store_act_tile(sA[buf], tid, ra);
-    if (s < nk) {
+  auto store_main = [&](int buf) {
+    store_a<C>(sA[buf], tid, ra);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+    for (int i = 0; i < C::C_CH; ++i) {
+      const int c = tid + C::NT * i;
+      const int row = c >> 1, half = c & 1;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
         float v[8];
-        decode8(rc[c], rcq, s_lv, v);
+        decode8(rc[i][w], rcq[i], s_lv, v);
         u32x4_t o;
         o.x = pack_bf16x2(v[0], v[1]);
         o.y = pack_bf16x2(v[2], v[3]);
         o.z = pack_bf16x2(v[4], v[5]);
         o.w = pack_bf16x2(v[6], v[7]);
-        *reinterpret_cast<u32x4_t *>(sB[buf] + lds_off(brow, bhalf * 4 + c)) = o;
+        *reinterpret_cast<u32x4_t *>(sB[buf] + lds_off(row, half * 4 + w)) = o;
       }
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4_t *>(sB[buf] + lds_off(brow, bhalf * 4 + c)) = rb[c];
     }
   };
 
-  f32x16_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  f32x16_t acc[C::WM][C::WN];
+  zero_acc<C>(acc);
 
-  load_step(0);
+  load_main(0);
   __syncthreads();  // level table visible
-  store_step(0, 0);
+  store_main(0);
   __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
+  for (int s = 0; s < nk; ++s) {
     const int buf = s & 1;
-    if (s + 1 < nsteps) load_step(s + 1);
-    mma_step(sA[buf], sB[buf], wm, wn, lane, acc);
-    if (s + 1 < nsteps) store_step(s + 1, buf ^ 1);
+    if (s + 1 < nk) load_main(s + 1);
+    mma_step<C>(sA[buf], sB[buf], wm, wn, lane, acc);
+    if (s + 1 < nk) store_main(buf ^ 1);
     __syncthreads();
   }
-  store_tile_out(Y, N, m0, T, n0, N, wm, wn, lane, acc);
+  // LoRA up-projection: V [T, rp] . Bp [N, rp]^T, one 64-deep step at a time
+  for (int64_t k0 = 0; k0 < rp; k0 += BK) {
+    {
+      u32x4_t rv[C::A_CH], rb[C::L_CH];
+      load_a<C>(V, rp, m0, T, k0, rp, tid, rv);
+#pragma unroll
+      for (int i = 0; i < C::L_CH; ++i) {
+        const int c = tid + C::NT * i;
+        const int64_t wrow = n0 + (c >> 3);
+        rb[i] = (wrow < N) ? *reinterpret_cast<const u32x4_t *>(Bp + wrow * rp + k0 + (c & 7) * 8)
+                           : u32x4_t{0u, 0u, 0u, 0u};
+      }
+      store_a<C>(sA[0], tid, rv);
+#pragma unroll
+      for (int i = 0; i < C::L_CH; ++i) {
+        const int c = tid + C::NT * i;
+        *reinterpret_cast<u32x4_t *>(sB[0] + lds_off(c >> 3, c & 7)) = rb[i];
+      }
+    }
+    __syncthreads();
+    mma_step<C>(sA[0], sB[0], wm, wn, lane, acc);
+    __syncthreads();
+  }
+  store_out<C>(Y, N, m0, T, n0, N, wm, wn, lane, acc);
 }
 
 // --------------------------------------------------------------- backward
 // dX[T, K] = dY[T, N] . W'[N, K] + dUp[T, rp] . A[r, K]   (rows of A past r read as 0)
-// The reduction index is the weight row n, so the B operand is decoded in
-// 4-row x 8-column micro-tiles and packed across rows: the transposition to
-// [k_out][n] happens in the bf16 pack, at no extra cost.
-__global__ __launch_bounds__(NT) void k_nf4_gemm_dx(const bf16_t *__restrict__ dY, int64_t T, int64_t N,
-                                                    const uint8_t *__restrict__ codes,
-                                                    const uint8_t *__restrict__ absmax_q,
-                                                    const float *__restrict__ step, int64_t K,
-                                                    const bf16_t *__restrict__ dUp, const bf16_t *__restrict__ A,
-                                                    int64_t r, int64_t rp, bf16_t *__restrict__ dX, Levels lv) {
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * BK];
+// The reduction index is the weight row n.  The B operand is decoded exactly as
+// in the forward (16 bytes of codes = 32 consecutive columns of one weight
+// row, one block constant) and stored in its natural [n][k_out] layout, rows
+// padded by 32 bytes so that four consecutive rows start 32 bytes apart in
+// the bank space.  The MFMA operand, which needs 8 consecutive n for one
+// k_out, is read with ds_read_b64_tr_b16: in each 16-lane group, lane i gets
+// element (i & 3) of the 8 bytes addressed by lane 4m + (i >> 2), m = 0..3, so
+// lane a points at row base + (a >> 2), columns 4 (a & 3) .. +3, and two such
+// reads (rows +0..3 and +4..7) give the 8 reduction values of the operand.
+template <class C>
+__global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict__ dY, int64_t T, int64_t N,
+                                                       const uint8_t *__restrict__ codes,
+                                                       const uint8_t *__restrict__ absmax_q,
+                                                       const float *__restrict__ step, int64_t K,
+                                                       const bf16_t *__restrict__ dUp, const bf16_t *__restrict__ A,
+                                                       int64_t r, int64_t rp, bf16_t *__restrict__ dX, Levels lv) {
+  constexpr int LDB = C::BN + 16;  // padded row length (elements) of the [64][BN] B tile
+  constexpr int PIECES = C::BN / 32;  // 32-column pieces per B-tile row
+  __shared__ __attribute__((aligned(16))) bf16_t sA[2][C::BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t sB[2][BK * LDB];
   __shared__ float s_lv[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;  // n0 indexes k_out (columns of W)
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int64_t m0 = (int64_t)blockIdx.y * C::BM, n0 = (int64_t)blockIdx.x * C::BN;  // n0 indexes k_out
   levels_to_lds(lv, s_lv, tid);
 
-  const int nk = (int)((N + BK - 1) / BK), nsteps = nk + (int)(rp / BK);
-  // B loader: column chunk cc = tid & 15 (8 output columns), row group g = tid >> 4 (4 reduction rows)
-  const int cc = tid & 15, g = tid >> 4;
-  const int64_t kcol = n0 + cc * 8;
-  const bool kcol_ok = kcol < K;
+  const int nk = (int)((N + BK - 1) / BK);
+  u32x4_t ra[C::A_CH];
+  u32x4_t rc[C::C_CH];
+  float rcq[C::C_CH];
 
-  u32x4_t ra[4];
-  uint32_t rw[4];  // one 32-bit word (8 nibbles) per reduction row
-  float rcq[4];
-  u32x4_t rl[4];   // LoRA phase: 8 bf16 of A per row
-
-  auto load_step = [&](int s) {
-    if (s < nk) {
-      const int64_t k0 = (int64_t)s * BK;
-      load_act_tile(dY, N, m0, T, k0, N, tid, ra);
+  auto load_main = [&](int s) {
+    const int64_t k0 = (int64_t)s * BK;
+    load_a<C>(dY, N, m0, T, k0, N, tid, ra);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int64_t n = k0 + g * 4 + p;
-        if (n < N && kcol_ok) {
-          rw[p] = *reinterpret_cast<const uint32_t *>(codes + n * (K / 2) + kcol / 2);
-          rcq[p] = block_scale(absmax_q, step, n * (K / BK) + kcol / BK);
-        } else {
-          rw[p] = 0x77777777u;
-          rcq[p] = 0.f;
-        }
-      }
-    } else {
-      const int64_t k0 = (int64_t)(s - nk) * BK;
-      load_act_tile(dUp, rp, m0, T, k0, rp, tid, ra);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int64_t j = k0 + g * 4 + p;
-        rl[p] = (j < r && kcol_ok) ? *reinterpret_cast<const u32x4_t *>(A + j * K + kcol) : u32x4_t{0u, 0u, 0u, 0u};
+    for (int i = 0; i < C::C_CH; ++i) {
+      const int c = tid + C::NT * i;
+      const int64_t n = k0 + c / PIECES, kc = n0 + (c % PIECES) * 32;
+      if (n < N && kc < K) {
+        rc[i] = *reinterpret_cast<const u32x4_t *>(codes + n * (K / 2) + kc / 2);
+        rcq[i] = block_scale(absmax_q, step, n * (K / BK) + kc / BK);
+      } else {
+        rc[i] = u32x4_t{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
+        rcq[i] = 0.f;
       }
     }
   };
-  auto store_step = [&](int s, int buf) {
-    store_act_tile(sA[buf], tid, ra);
-    // destination: LDS row (k_out) = cc*8 + e, reduction columns g*4 .. g*4+3 (8 bytes)
-    if (s < nk) {
-      float v[4][8];
+  auto store_main = [&](int buf) {
+    store_a<C>(sA[buf], tid, ra);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) decode8(rw[p], rcq[p], s_lv, v[p]);
+    for (int i = 0; i < C::C_CH; ++i) {
+      const int c = tid + C::NT * i;
+      bf16_t *dst = sB[buf] + (c / PIECES) * LDB + (c % PIECES) * 32;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int row = cc * 8 + e;
-        u32x2_t o;
-        o.x = pack_bf16x2(v[0][e], v[1][e]);
-        o.y = pack_bf16x2(v[2][e], v[3][e]);
-        *reinterpret_cast<u32x2_t *>(sB[buf] + lds_off(row, g >> 1) + (g & 1) * 4) = o;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int row = cc * 8 + e;
-        const int w = e >> 1;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low bf16 of each word
-        u32x2_t o;
-        o.x = __builtin_amdgcn_perm(rl[1][w], rl[0][w], sel);
-        o.y = __builtin_amdgcn_perm(rl[3][w], rl[2][w], sel);
-        *reinterpret_cast<u32x2_t *>(sB[buf] + lds_off(row, g >> 1) + (g & 1) * 4) = o;
+      for (int w = 0; w < 4; ++w) {
+        float v[8];
+        decode8(rc[i][w], rcq[i], s_lv, v);
+        u32x4_t o;
+        o.x = pack_bf16x2(v[0], v[1]);
+        o.y = pack_bf16x2(v[2], v[3]);
+        o.z = pack_bf16x2(v[4], v[5]);
+        o.w = pack_bf16x2(v[6], v[7]);
+        *reinterpret_cast<u32x4_t *>(dst + w * 8) = o;
       }
     }
   };
+  // this wave's B operands for one 16-deep substep, via two transposing reads each
+  const int grp = lane >> 4, ai = lane & 15;
+  auto mma = [&](const bf16_t *sa, const bf16_t *sb, f32x16_t (&acc)[C::WM][C::WN]) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int chunk = kk * 2 + (lane >> 5);
+      u32x4_t a[C::WM], b[C::WN];
+#pragma unroll
+      for (int i = 0; i < C::WM; ++i) {
+        const int ra_ = (wm * C::WM + i) * 32 + (lane & 31);
+        a[i] = *reinterpret_cast<const u32x4_t *>(sa + lds_off(ra_, chunk));
+      }
+#pragma unroll
+      for (int j = 0; j < C::WN; ++j) {
+        const int row = kk * 16 + 8 * (grp >> 1) + (ai >> 2);
+        const int col = (wn * C::WN + j) * 32 + 16 * (grp & 1) + 4 * (ai & 3);
+        typedef short s4_t __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s4_t lds_s4;
+        const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(sb + row * LDB + col));
+        const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(sb + (row + 4) * LDB + col));
+        const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+        b[j] = u32x4_t{l2.x, l2.y, h2.x, h2.y};
+      }
+#pragma unroll
+      for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::WN; ++j) acc[i][j] = mfma_32x32x16(a[i], b[j], acc[i][j]);
+    }
+  };
 
-  f32x16_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  f32x16_t acc[C::WM][C::WN];
+  zero_acc<C>(acc);
 
-  load_step(0);
+  load_main(0);
   __syncthreads();
-  store_step(0, 0);
+  store_main(0);
   __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
+  for (int s = 0; s < nk; ++s) {
     const int buf = s & 1;
-    if (s + 1 < nsteps) load_step(s + 1);
-    mma_step(sA[buf], sB[buf], wm, wn, lane, acc);
-    if (s + 1 < nsteps) store_step(s + 1, buf ^ 1);
+    if (s + 1 < nk) load_main(s + 1);
+    mma(sA[buf], sB[buf], acc);
+    if (s + 1 < nk) store_main(buf ^ 1);
     __syncthreads();
   }
-  store_tile_out(dX, K, m0, T, n0, K, wm, wn, lane, acc);
+  // LoRA term: dUp [T, rp] . A [r, K], reduction over the rank (rows j of A)
+  for (int64_t k0 = 0; k0 < rp; k0 += BK) {
+    {
+      constexpr int LCH = BK * C::BN / 8 / C::NT;  // 16-byte chunks of A per thread
+      u32x4_t rv[C::A_CH], rl[LCH];
+      load_a<C>(dUp, rp, m0, T, k0, rp, tid, rv);
+#pragma unroll
+      for (int i = 0; i < LCH; ++i) {
+        const int c = tid + C::NT * i;
+        const int64_t j = k0 + c / (C::BN / 8), kc = n0 + (c % (C::BN / 8)) * 8;
+        rl[i] = (j < r && kc < K) ? *reinterpret_cast<const u32x4_t *>(A + j * K + kc) : u32x4_t{0u, 0u, 0u, 0u};
+      }
+      store_a<C>(sA[0], tid, rv);
+#pragma unroll
+      for (int i = 0; i < LCH; ++i) {
+        const int c = tid + C::NT * i;
+        *reinterpret_cast<u32x4_t *>(sB[0] + (c / (C::BN / 8)) * LDB + (c % (C::BN / 8)) * 8) = rl[i];
+      }
+    }
+    __syncthreads();
+    mma(sA[0], sB[0], acc);
+    __syncthreads();
+  }
+  store_out<C>(dX, K, m0, T, n0, K, wm, wn, lane, acc);
 }
 
-hipError_t launch_nf4_gemm_fwd(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
-                               const float *step, int64_t N, const bf16_t *V, const bf16_t *Bp, int64_t rp, bf16_t *Y,
-                               const Levels &lv, hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((T + BM - 1) / BM));
-  hipLaunchKernelGGL(k_nf4_gemm_fwd, grid, dim3(NT), 0, s, X, T, K, codes, absmax_q, step, N, V, Bp, rp, Y, lv);
+// ---------------------------------------------------------------- dispatch
+namespace {
+using T128x128 = TileCfg<2, 2, 2, 2>;    // 4 waves, 64x64 per wave, two workgroups per CU
+using T256x256w8 = TileCfg<2, 4, 4, 2>;  // 8 waves, 128x64 per wave, one workgroup per CU
+
+template <class C>
+hipError_t fwd_with(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
+                    const float *step, int64_t N, const bf16_t *V, const bf16_t *Bp, int64_t rp, bf16_t *Y,
+                    const Levels &lv, hipStream_t s) {
+  dim3 grid((unsigned)((N + C::BN - 1) / C::BN), (unsigned)((T + C::BM - 1) / C::BM));
+  hipLaunchKernelGGL(k_nf4_gemm_fwd<C>, grid, dim3(C::NT), 0, s, X, T, K, codes, absmax_q, step, N, V, Bp, rp, Y, lv);
   return hipGetLastError();
 }
 
-hipError_t launch_nf4_gemm_dx(const bf16_t *dY, int64_t T, int64_t N, const uint8_t *codes, const uint8_t *absmax_q,
-                              const float *step, int64_t K, const bf16_t *dUp, const bf16_t *A, int64_t r, int64_t rp,
-                              bf16_t *dX, const Levels &lv, hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  dim3 grid((unsigned)((K + BN - 1) / BN), (unsigned)((T + BM - 1) / BM));
-  hipLaunchKernelGGL(k_nf4_gemm_dx, grid, dim3(NT), 0, s, dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv);
+template <class C>
+hipError_t dx_with(const bf16_t *dY, int64_t T, int64_t N, const uint8_t *codes, const uint8_t *absmax_q,
+                   const float *step, int64_t K, const bf16_t *dUp, const bf16_t *A, int64_t r, int64_t rp,
+                   bf16_t *dX, const Levels &lv, hipStream_t s) {
+  dim3 grid((unsigned)((K + C::BN - 1) / C::BN), (unsigned)((T + C::BM - 1) / C::BM));
+  hipLaunchKernelGGL(k_nf4_gemm_dx<C>, grid, dim3(C::NT), 0, s, dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp,
+                     dX, lv);
   return hipGetLastError();
+}
+}  // namespace
+
+// Tile choice for an M x N output.  Measured on MI355X (both GEMMs, seven
+// workload shapes): the 8-wave 256x256 tile is fastest whenever it yields at
+// least one workgroup per CU (256 tiles); below that the 128x128 tile, which
+// keeps every CU busy, wins.
+int nf4_gemm_pick_tile(int64_t M, int64_t N) {
+  const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+  return big >= 256 ? NF4_TILE_256x256_W8 : NF4_TILE_128x128;
+}
+
+hipError_t launch_nf4_gemm_fwd(int tile, const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes,
+                               const uint8_t *absmax_q, const float *step, int64_t N, const bf16_t *V,
+                               const bf16_t *Bp, int64_t rp, bf16_t *Y, const Levels &lv, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (tile == NF4_TILE_256x256_W8) return fwd_with<T256x256w8>(X, T, K, codes, absmax_q, step, N, V, Bp, rp, Y, lv, s);
+  return fwd_with<T128x128>(X, T, K, codes, absmax_q, step, N, V, Bp, rp, Y, lv, s);
+}
+
+hipError_t launch_nf4_gemm_dx(int tile, const bf16_t *dY, int64_t T, int64_t N, const uint8_t *codes,
+                              const uint8_t *absmax_q, const float *step, int64_t K, const bf16_t *dUp, const bf16_t *A,
+                              int64_t r, int64_t rp, bf16_t *dX, const Levels &lv, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (tile == NF4_TILE_256x256_W8) return dx_with<T256x256w8>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s);
+  return dx_with<T128x128>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s);
 }
 
 }  // namespace qlora

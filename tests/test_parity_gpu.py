@@ -289,6 +289,21 @@ def test_full_size_sampled(cfg, name, n_out, n_in, T, r, alpha, outliers):
     assert abs(la - lb) <= 1e-2 * max(abs(la), abs(lb))
 
 
+@pytest.mark.parametrize("n_out,n_in,T,r", [(4104, 4096, 4133, 16), (1032, 2048, 8200, 40)])
+def test_large_ragged_sampled(n_out, n_in, T, r):
+    """Shapes large enough for the 256-row tiles, with partial tiles in T and n_out."""
+    print(f"large ragged {n_out}x{n_in} T={T} r={r}", flush=True)
+    inp = linear_inputs(n_out, n_in, T, r, 2.0 * r, seed=3)
+    _, g = run_gpu(inp)
+    rows = np.unique(np.concatenate([[0, T - 1, T - 2], np.random.default_rng(2).choice(T, 40, replace=False)]))
+    ref = run_oracle(inp, rows=rows)
+    idx = torch.from_numpy(rows).to(dev())
+    for k in ("Y", "U", "dX"):
+        assert_close(k, gpu_f64(g[k][idx]), ref[k])
+    assert_close("dA", gpu_f64(g["dA"]), ref["dA"])
+    assert_close("dB", gpu_f64(g["dB"]), ref["dB"])
+
+
 @pytest.mark.parametrize("n_out", [8192, 28672])
 @pytest.mark.parametrize("T", [1, 8, 32, 128])
 def test_small_token_forward(n_out, T):
