@@ -202,7 +202,7 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    timed = ["nf4_gemm_fwd", "nf4_gemm_dx"] if train else ["nf4_gemm_fwd"]
+    timed = ["nf4_gemm_fwd", "nf4_gemm_dx"] if train else ["nf4_gemm_fwd", "nf4_gemv"]
     for k in timed:
         B.timing_read(k)  # clear
         B.timing_enable(k, True)
@@ -226,15 +226,20 @@ def main():
     kflops = {
         "nf4_gemm_fwd": sum(2 * T * L["n_out"] * (L["n_in"] + r) for L in layers),
         "nf4_gemm_dx": sum(2 * T * L["n_in"] * (L["n_out"] + r) for L in layers),
+        "nf4_gemv": sum(2 * T * L["n_out"] * L["n_in"] for L in layers),
     }
     kbytes = {  # compulsory HBM bytes of one launch: weight stream + activations in and out + LoRA operands
         "nf4_gemm_fwd": sum(weight_bytes(L["n_out"], L["n_in"]) + 2 * T * (L["n_in"] + L["n_out"]) +
                             2 * (T + L["n_out"]) * r for L in layers),
         "nf4_gemm_dx": sum(weight_bytes(L["n_out"], L["n_in"]) + 2 * T * (L["n_in"] + L["n_out"]) +
                            2 * (T + L["n_in"]) * r for L in layers),
+        # the small-token kernel reads the weight stream and X; its binary32 partials are not algorithmic
+        "nf4_gemv": sum(weight_bytes(L["n_out"], L["n_in"]) + 2 * T * L["n_in"] for L in layers),
     }
     kernels = {}
     for k, (n, ms) in ktimes.items():
+        if n == 0:
+            continue
         per_step_launches = n / args.steps if args.steps else 0
         avg_ms = ms / n if n else float("nan")
         kernels[k] = {"launches": n, "avg_ms_per_launch": avg_ms,

@@ -218,7 +218,12 @@ struct Plan {
   int64_t rp = 0;
   size_t off_bp = 0, off_v = 0, off_du = 0, off_part = 0, total = 0;
   Split su, sdu, sdb, sda;
+  bool gemv = false;  // forward through the small-token kernel
+  int gemv_split = 0;
+  int64_t gemv_kchunk = 0;
 };
+
+bool use_gemv(int64_t T, int64_t K) { return T >= 1 && T <= kGemvMaxT && K % 128 == 0; }
 
 Plan make_plan(int op, int64_t T, int64_t N, int64_t K, int32_t r) {
   Plan p;
@@ -232,6 +237,12 @@ Plan make_plan(int op, int64_t T, int64_t N, int64_t K, int32_t r) {
   if (op == QLORA_OP_FWD) {
     p.su = plan_split(T, r, K);
     part = (size_t)p.su.n * T * r * 4;
+    if (use_gemv(T, K)) {
+      p.gemv = true;
+      nf4_gemv_plan(T, N, K, &p.gemv_split, &p.gemv_kchunk);
+      const size_t gp = (size_t)p.gemv_split * T * N * 4;
+      part = gp > part ? gp : part;
+    }
   } else {
     p.off_du = off;
     off = up(off + (size_t)(T * p.rp * 2), kAlign);
@@ -358,9 +369,15 @@ int qlora_linear_fwd(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const q
   float *part = (float *)(w + p.off_part);
   const float sc = alpha / (float)r;
   const Levels &lv = codebook().lv;
-  LAUNCH("pad_b", launch_pad_copy(B, r, r, N, Bp, p.rp, s));
   LAUNCH("lora_u", launch_gemm_splitk(0, 0, X, K, A, K, T, r, K, p.su.kchunk, p.su.n, part, s));
   LAUNCH("lora_u_finalize", launch_finalize(part, p.su.n, T, r, U_out, r, U_out ? r : 0, 1.0f, V, p.rp, p.rp, r, sc, s));
+  if (p.gemv) {  // few tokens: bound by the weight stream
+    LAUNCH("nf4_gemv", launch_nf4_gemv(X, T, K, q->codes, q->absmax_q, q->absmax_step, N, p.gemv_split, p.gemv_kchunk,
+                                       part, lv, s));
+    LAUNCH("gemv_reduce", launch_gemv_reduce(part, p.gemv_split, T, N, V, p.rp, B, r, Y, s));
+    return QLORA_OK;
+  }
+  LAUNCH("pad_b", launch_pad_copy(B, r, r, N, Bp, p.rp, s));
   LAUNCH("nf4_gemm_fwd", launch_nf4_gemm_fwd(nf4_gemm_pick_tile(T, N), X, T, K, q->codes, q->absmax_q,
                                              q->absmax_step, N, V, Bp, p.rp, Y, lv, s));
   return QLORA_OK;

@@ -57,6 +57,18 @@ __device__ __forceinline__ float block_scale(const uint8_t *__restrict__ absmax_
   return __fmul_rn((float)absmax_q[b], step[b >> 8]);
 }
 
+// The two loads behind a block constant, kept raw so that a prefetch does not
+// make the wave wait for them: the product is formed where it is used.
+struct RawScale {
+  uint32_t q;
+  float d;
+};
+__device__ __forceinline__ RawScale load_scale(const uint8_t *__restrict__ absmax_q, const float *__restrict__ step,
+                                               int64_t b) {
+  return RawScale{(uint32_t)absmax_q[b], step[b >> 8]};
+}
+__device__ __forceinline__ float scale_of(const RawScale &r) { return __fmul_rn((float)r.q, r.d); }
+
 // Decode the 8 nibbles of `codes` (element e in bits 4e..4e+3) into binary32
 // products level * cq; each product is rounded once (no contraction).
 __device__ __forceinline__ void decode8(uint32_t codes, float cq, const float *s_lv, float out[8]) {

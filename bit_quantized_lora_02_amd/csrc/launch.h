@@ -25,6 +25,16 @@ hipError_t launch_nf4_gemm_dx(int tile, const bf16_t *dY, int64_t T, int64_t N, 
                               const uint8_t *absmax_q, const float *step, int64_t K, const bf16_t *dUp, const bf16_t *A,
                               int64_t r, int64_t rp, bf16_t *dX, const Levels &lv, hipStream_t s);
 
+// Small-token forward (T <= 64, n_in % 128 == 0): split-K partial sums, then a
+// fixed-order reduce that adds the LoRA term and rounds to bf16.
+constexpr int64_t kGemvMaxT = 64;
+void nf4_gemv_plan(int64_t T, int64_t N, int64_t K, int *nsplit, int64_t *kchunk);
+hipError_t launch_nf4_gemv(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
+                           const float *step, int64_t N, int nsplit, int64_t kchunk, float *part, const Levels &lv,
+                           hipStream_t s);
+hipError_t launch_gemv_reduce(const float *part, int nsplit, int64_t T, int64_t N, const bf16_t *V, int64_t rp,
+                              const bf16_t *B, int64_t r, bf16_t *Y, hipStream_t s);
+
 hipError_t launch_gemm_splitk(int la, int lb, const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb, int64_t M,
                               int64_t N, int64_t Kred, int64_t kchunk, int nsplit, float *C, hipStream_t s);
 hipError_t launch_finalize(const float *part, int nsplit, int64_t M, int64_t N, bf16_t *out1, int64_t ld1, int64_t n1,

@@ -143,7 +143,7 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
   const int nk = (int)(K / BK);
   u32x4_t ra[C::A_CH];
   u32x4_t rc[C::C_CH];
-  float rcq[C::C_CH];
+  RawScale rcq[C::C_CH];
 
   auto load_main = [&](int s) {
     const int64_t k0 = (int64_t)s * BK;
@@ -154,10 +154,10 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
       const int64_t wrow = n0 + (c >> 1);
       if (wrow < N) {
         rc[i] = *reinterpret_cast<const u32x4_t *>(codes + wrow * (K / 2) + k0 / 2 + (c & 1) * 16);
-        rcq[i] = block_scale(absmax_q, step, wrow * (K / BK) + s);
+        rcq[i] = load_scale(absmax_q, step, wrow * (K / BK) + s);
       } else {
         rc[i] = u32x4_t{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
-        rcq[i] = 0.f;
+        rcq[i] = RawScale{0u, 0.f};
       }
     }
   };
@@ -167,10 +167,11 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
     for (int i = 0; i < C::C_CH; ++i) {
       const int c = tid + C::NT * i;
       const int row = c >> 1, half = c & 1;
+      const float cq = scale_of(rcq[i]);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         float v[8];
-        decode8(rc[i][w], rcq[i], s_lv, v);
+        decode8(rc[i][w], cq, s_lv, v);
         u32x4_t o;
         o.x = pack_bf16x2(v[0], v[1]);
         o.y = pack_bf16x2(v[2], v[3]);
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
   const int nk = (int)((N + BK - 1) / BK);
   u32x4_t ra[C::A_CH];
   u32x4_t rc[C::C_CH];
-  float rcq[C::C_CH];
+  RawScale rcq[C::C_CH];
 
   auto load_main = [&](int s) {
     const int64_t k0 = (int64_t)s * BK;
@@ -263,10 +264,10 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
       const int64_t n = k0 + c / PIECES, kc = n0 + (c % PIECES) * 32;
       if (n < N && kc < K) {
         rc[i] = *reinterpret_cast<const u32x4_t *>(codes + n * (K / 2) + kc / 2);
-        rcq[i] = block_scale(absmax_q, step, n * (K / BK) + kc / BK);
+        rcq[i] = load_scale(absmax_q, step, n * (K / BK) + kc / BK);
       } else {
         rc[i] = u32x4_t{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
-        rcq[i] = 0.f;
+        rcq[i] = RawScale{0u, 0.f};
       }
     }
   };
@@ -276,10 +277,11 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
     for (int i = 0; i < C::C_CH; ++i) {
       const int c = tid + C::NT * i;
       bf16_t *dst = sB[buf] + (c / PIECES) * LDB + (c % PIECES) * 32;
+      const float cq = scale_of(rcq[i]);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         float v[8];
-        decode8(rc[i][w], rcq[i], s_lv, v);
+        decode8(rc[i][w], cq, s_lv, v);
         u32x4_t o;
         o.x = pack_bf16x2(v[0], v[1]);
         o.y = pack_bf16x2(v[2], v[3]);

@@ -143,6 +143,8 @@ SMALL = [
     (512, 192, 257, 64, 16.0),   # n_in with a half tile in dX
     (64, 128, 1, 128, 256.0),    # one token, maximum rank
     (1032, 256, 33, 12, 24.0),
+    (72, 384, 20, 4, 8.0),       # 17..32 tokens through the small-token kernel, n_out not a multiple of 64
+    (520, 192, 40, 8, 16.0),     # few tokens but n_in % 128 != 0: the tiled kernel
 ]
 
 
@@ -241,14 +243,15 @@ def test_autograd_function():
     assert_close("dB", gpu_f64(B.grad), ref["dB"])
 
 
-def test_timing_hook_counts_launches():
-    inp = linear_inputs(256, 256, 64, 8, 16.0, seed=13)
+@pytest.mark.parametrize("T,kernel", [(200, "nf4_gemm_fwd"), (8, "nf4_gemv")])
+def test_timing_hook_counts_launches(T, kernel):
+    inp = linear_inputs(256, 256, T, 8, 16.0, seed=13)
     w = Bd.quantize_nf4(torch.from_numpy(inp.W).to(dev()))
-    Bd.timing_enable("nf4_gemm_fwd", True)
+    Bd.timing_enable(kernel, True)
     for _ in range(3):
         run_gpu(inp, w=w)
-    Bd.timing_enable("nf4_gemm_fwd", False)
-    n, ms = Bd.timing_read("nf4_gemm_fwd")
+    Bd.timing_enable(kernel, False)
+    n, ms = Bd.timing_read(kernel)
     assert n == 3 and ms > 0
 
 
