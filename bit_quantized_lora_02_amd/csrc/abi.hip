@@ -240,8 +240,7 @@ Plan make_plan(int op, int64_t T, int64_t N, int64_t K, int32_t r) {
     if (use_gemv(T, K)) {
       p.gemv = true;
       nf4_gemv_plan(T, N, K, &p.gemv_split, &p.gemv_kchunk);
-      const size_t gp = (size_t)p.gemv_split * T * N * 4;
-      part = gp > part ? gp : part;
+      part = (size_t)p.gemv_split * T * N * 4;
     }
   } else {
     p.off_du = off;
@@ -369,17 +368,21 @@ int qlora_linear_fwd(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const q
   float *part = (float *)(w + p.off_part);
   const float sc = alpha / (float)r;
   const Levels &lv = codebook().lv;
-  LAUNCH("lora_u", launch_gemm_splitk(0, 0, X, K, A, K, T, r, K, p.su.kchunk, p.su.n, part, s));
-  LAUNCH("lora_u_finalize", launch_finalize(part, p.su.n, T, r, U_out, r, U_out ? r : 0, 1.0f, V, p.rp, p.rp, r, sc, s));
   if (p.gemv) {  // few tokens: bound by the weight stream
+    LAUNCH("lora_u_small", launch_lora_u_small(X, T, K, A, r, sc, U_out, V, p.rp, s));
     LAUNCH("nf4_gemv", launch_nf4_gemv(X, T, K, q->codes, q->absmax_q, q->absmax_step, N, p.gemv_split, p.gemv_kchunk,
-                                       part, lv, s));
-    LAUNCH("gemv_reduce", launch_gemv_reduce(part, p.gemv_split, T, N, V, p.rp, B, r, Y, s));
+                                       V, p.rp, B, r, part, Y, lv, s));
+    LAUNCH("gemv_reduce", launch_gemv_reduce(part, p.gemv_split, T, N, Y, s));
     return QLORA_OK;
   }
-  LAUNCH("pad_b", launch_pad_copy(B, r, r, N, Bp, p.rp, s));
+  LAUNCH("lora_u", launch_gemm_splitk(0, 0, X, K, A, K, T, r, K, p.su.kchunk, p.su.n, part, s));
+  LAUNCH("lora_u_finalize", launch_finalize(part, p.su.n, T, r, U_out, r, U_out ? r : 0, 1.0f, V, p.rp, p.rp, r, sc, s));
+  // B is read in place when its rows are 16-byte multiples, else from a zero-padded copy
+  const bool b_direct = (r % 8) == 0;
+  if (!b_direct) LAUNCH("pad_b", launch_pad_copy(B, r, r, N, Bp, p.rp, s));
   LAUNCH("nf4_gemm_fwd", launch_nf4_gemm_fwd(nf4_gemm_pick_tile(T, N), X, T, K, q->codes, q->absmax_q,
-                                             q->absmax_step, N, V, Bp, p.rp, Y, lv, s));
+                                             q->absmax_step, N, V, b_direct ? B : Bp, b_direct ? r : p.rp, r, p.rp,
+                                             Y, lv, s));
   return QLORA_OK;
 }
 
@@ -410,18 +413,30 @@ int qlora_linear_bwd(const qlora_bf16 *X, const qlora_bf16 *dY, int64_t T, const
     LAUNCH("zero_db", launch_finalize(part, 0, N, r, dB, r, r, 1.0f, nullptr, 0, 0, 0, 0.f, s));
     return QLORA_OK;
   }
-  LAUNCH("pad_b", launch_pad_copy(B, r, r, N, Bp, p.rp, s));
-  if (U) {
+  // B and U are read in place when their rows are 16-byte multiples, else from zero-padded copies
+  const bool direct = (r % 8) == 0;
+  const bf16_t *Bsrc = B, *Usrc = U;
+  int64_t ldb = r, ldu = r;
+  if (!direct) {
+    LAUNCH("pad_b", launch_pad_copy(B, r, r, N, Bp, p.rp, s));
+    Bsrc = Bp;
+    ldb = p.rp;
+  }
+  if (U && !direct) {
     LAUNCH("pad_u", launch_pad_copy(U, r, r, T, Up, p.rp, s));
-  } else {
+    Usrc = Up;
+    ldu = p.rp;
+  } else if (!U) {
     LAUNCH("lora_u", launch_gemm_splitk(0, 0, X, K, A, K, T, r, K, p.su.kchunk, p.su.n, part, s));
     LAUNCH("lora_u_finalize", launch_finalize(part, p.su.n, T, r, nullptr, 0, 0, 0.f, Up, p.rp, p.rp, r, 1.0f, s));
+    Usrc = Up;
+    ldu = p.rp;
   }
   // dU = s dY B  -> dUp [T, rp]
-  LAUNCH("lora_du", launch_gemm_splitk(0, 1, dY, N, Bp, p.rp, T, r, N, p.sdu.kchunk, p.sdu.n, part, s));
+  LAUNCH("lora_du", launch_gemm_splitk(0, 1, dY, N, Bsrc, ldb, T, r, N, p.sdu.kchunk, p.sdu.n, part, s));
   LAUNCH("lora_du_finalize", launch_finalize(part, p.sdu.n, T, r, nullptr, 0, 0, 0.f, dUp, p.rp, p.rp, r, sc, s));
   // dB = s dY^T U  -> [N, r]
-  LAUNCH("lora_db", launch_gemm_splitk(1, 1, dY, N, Up, p.rp, N, r, T, p.sdb.kchunk, p.sdb.n, part, s));
+  LAUNCH("lora_db", launch_gemm_splitk(1, 1, dY, N, Usrc, ldu, N, r, T, p.sdb.kchunk, p.sdb.n, part, s));
   LAUNCH("lora_db_finalize", launch_finalize(part, p.sdb.n, N, r, dB, r, r, sc, nullptr, 0, 0, 0, 0.f, s));
   // dA = dU^T X  -> [r, K]
   LAUNCH("lora_da", launch_gemm_splitk(1, 1, dUp, p.rp, X, K, r, K, T, p.sda.kchunk, p.sda.n, part, s));

@@ -15,25 +15,35 @@ hipError_t launch_dequant(const uint8_t *codes, const uint8_t *absmax_q, const f
                           int64_t n_in, bf16_t *out, const Levels &lv, hipStream_t s);
 
 // Output-tile shapes of the fused NF4 GEMMs (rows x columns of the output).
-enum { NF4_TILE_128x128 = 0, NF4_TILE_256x256_W8 = 3 };
+enum {
+  NF4_TILE_128x128 = 0,
+  NF4_TILE_256x256_W8 = 3,
+  NF4_TILE_256x128_W8 = 4,
+  NF4_TILE_128x256_W8 = 5,
+  NF4_TILE_128x128_W8 = 6
+};
 int nf4_gemm_pick_tile(int64_t M, int64_t N);
 
 hipError_t launch_nf4_gemm_fwd(int tile, const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes,
                                const uint8_t *absmax_q, const float *step, int64_t N, const bf16_t *V,
-                               const bf16_t *Bp, int64_t rp, bf16_t *Y, const Levels &lv, hipStream_t s);
+                               const bf16_t *Bp, int64_t ldb, int64_t r, int64_t rp, bf16_t *Y, const Levels &lv,
+                               hipStream_t s);
 hipError_t launch_nf4_gemm_dx(int tile, const bf16_t *dY, int64_t T, int64_t N, const uint8_t *codes,
                               const uint8_t *absmax_q, const float *step, int64_t K, const bf16_t *dUp, const bf16_t *A,
                               int64_t r, int64_t rp, bf16_t *dX, const Levels &lv, hipStream_t s);
 
-// Small-token forward (T <= 64, n_in % 128 == 0): split-K partial sums, then a
-// fixed-order reduce that adds the LoRA term and rounds to bf16.
+// Small-token forward (T <= 64, n_in % 128 == 0): U and V for few tokens, then
+// the split-K GEMV (binary32 partials, LoRA term in the first split) followed
+// by a fixed-order reduce of the partials into Y (with one split the GEMV
+// stores Y itself and the reduce does nothing).
 constexpr int64_t kGemvMaxT = 64;
 void nf4_gemv_plan(int64_t T, int64_t N, int64_t K, int *nsplit, int64_t *kchunk);
+hipError_t launch_lora_u_small(const bf16_t *X, int64_t T, int64_t K, const bf16_t *A, int64_t r, float s,
+                               bf16_t *U_out, bf16_t *V, int64_t rp, hipStream_t st);
 hipError_t launch_nf4_gemv(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
-                           const float *step, int64_t N, int nsplit, int64_t kchunk, float *part, const Levels &lv,
-                           hipStream_t s);
-hipError_t launch_gemv_reduce(const float *part, int nsplit, int64_t T, int64_t N, const bf16_t *V, int64_t rp,
-                              const bf16_t *B, int64_t r, bf16_t *Y, hipStream_t s);
+                           const float *step, int64_t N, int nsplit, int64_t kchunk, const bf16_t *V, int64_t rp,
+                           const bf16_t *B, int64_t r, float *part, bf16_t *Y, const Levels &lv, hipStream_t s);
+hipError_t launch_gemv_reduce(const float *part, int nsplit, int64_t T, int64_t N, bf16_t *Y, hipStream_t s);
 
 hipError_t launch_gemm_splitk(int la, int lb, const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb, int64_t M,
                               int64_t N, int64_t Kred, int64_t kchunk, int nsplit, float *C, hipStream_t s);

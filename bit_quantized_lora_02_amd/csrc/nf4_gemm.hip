@@ -38,7 +38,10 @@ struct TileCfg {
   static constexpr int BM = WAVES_M * WM * 32;
   static constexpr int BN = WAVES_N * WN * 32;
   static constexpr int A_CH = BM * 8 / NT;   // 16-byte chunks of the A tile per thread and step
-  static constexpr int C_CH = BN * 2 / NT;   // 16-byte chunks of codes (32 nibbles) per thread (forward)
+  // 16-byte chunks of codes (32 nibbles) per thread; with fewer chunks than
+  // threads (C_SPARSE) only the first 2*BN threads load and decode
+  static constexpr bool C_SPARSE = BN * 2 < NT;
+  static constexpr int C_CH = C_SPARSE ? 1 : BN * 2 / NT;
   static constexpr int L_CH = BN * 8 / NT;   // 16-byte bf16 chunks of the LoRA B tile per thread (forward)
   static_assert(A_CH >= 1 && C_CH >= 1 && L_CH >= 1, "unsupported tile");
 };
@@ -124,14 +127,15 @@ __device__ __forceinline__ void store_out(bf16_t *__restrict__ out, int64_t ld, 
 }  // namespace
 
 // ---------------------------------------------------------------- forward
-// Y[T, N] = X[T, K] . W'[N, K]^T + V[T, rp] . Bp[N, rp]^T
+// Y[T, N] = X[T, K] . W'[N, K]^T + V[T, rp] . B[N, :r]^T   (B row stride ldb, columns >= r read as 0)
 template <class C>
 __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict__ X, int64_t T, int64_t K,
                                                         const uint8_t *__restrict__ codes,
                                                         const uint8_t *__restrict__ absmax_q,
                                                         const float *__restrict__ step, int64_t N,
                                                         const bf16_t *__restrict__ V, const bf16_t *__restrict__ Bp,
-                                                        int64_t rp, bf16_t *__restrict__ Y, Levels lv) {
+                                                        int64_t ldb, int64_t r, int64_t rp, bf16_t *__restrict__ Y,
+                                                        Levels lv) {
   __shared__ __attribute__((aligned(16))) bf16_t sA[2][C::BM * BK];
   __shared__ __attribute__((aligned(16))) bf16_t sB[2][C::BN * BK];
   __shared__ float s_lv[16];
@@ -152,7 +156,7 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
     for (int i = 0; i < C::C_CH; ++i) {
       const int c = tid + C::NT * i;
       const int64_t wrow = n0 + (c >> 1);
-      if (wrow < N) {
+      if (wrow < N && (!C::C_SPARSE || c < 2 * C::BN)) {
         rc[i] = *reinterpret_cast<const u32x4_t *>(codes + wrow * (K / 2) + k0 / 2 + (c & 1) * 16);
         rcq[i] = load_scale(absmax_q, step, wrow * (K / BK) + s);
       } else {
@@ -166,6 +170,7 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
 #pragma unroll
     for (int i = 0; i < C::C_CH; ++i) {
       const int c = tid + C::NT * i;
+      if (C::C_SPARSE && c >= 2 * C::BN) break;
       const int row = c >> 1, half = c & 1;
       const float cq = scale_of(rcq[i]);
 #pragma unroll
@@ -204,9 +209,9 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
 #pragma unroll
       for (int i = 0; i < C::L_CH; ++i) {
         const int c = tid + C::NT * i;
-        const int64_t wrow = n0 + (c >> 3);
-        rb[i] = (wrow < N) ? *reinterpret_cast<const u32x4_t *>(Bp + wrow * rp + k0 + (c & 7) * 8)
-                           : u32x4_t{0u, 0u, 0u, 0u};
+        const int64_t wrow = n0 + (c >> 3), col = k0 + (c & 7) * 8;  // r % 8 == 0 or B padded to ldb
+        rb[i] = (wrow < N && col < r) ? *reinterpret_cast<const u32x4_t *>(Bp + wrow * ldb + col)
+                                      : u32x4_t{0u, 0u, 0u, 0u};
       }
       store_a<C>(sA[0], tid, rv);
 #pragma unroll
@@ -262,7 +267,7 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
     for (int i = 0; i < C::C_CH; ++i) {
       const int c = tid + C::NT * i;
       const int64_t n = k0 + c / PIECES, kc = n0 + (c % PIECES) * 32;
-      if (n < N && kc < K) {
+      if (n < N && kc < K && (!C::C_SPARSE || c < 2 * C::BN)) {
         rc[i] = *reinterpret_cast<const u32x4_t *>(codes + n * (K / 2) + kc / 2);
         rcq[i] = load_scale(absmax_q, step, n * (K / BK) + kc / BK);
       } else {
@@ -276,6 +281,7 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
 #pragma unroll
     for (int i = 0; i < C::C_CH; ++i) {
       const int c = tid + C::NT * i;
+      if (C::C_SPARSE && c >= 2 * C::BN) break;
       bf16_t *dst = sB[buf] + (c / PIECES) * LDB + (c % PIECES) * 32;
       const float cq = scale_of(rcq[i]);
 #pragma unroll
@@ -365,13 +371,17 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
 namespace {
 using T128x128 = TileCfg<2, 2, 2, 2>;    // 4 waves, 64x64 per wave, two workgroups per CU
 using T256x256w8 = TileCfg<2, 4, 4, 2>;  // 8 waves, 128x64 per wave, one workgroup per CU
+using T256x128w8 = TileCfg<4, 2, 2, 2>;  // 8 waves, 64x64 per wave
+using T128x256w8 = TileCfg<2, 4, 2, 2>;  // 8 waves, 64x64 per wave
+using T128x128w8 = TileCfg<2, 4, 2, 1>;  // 8 waves, 64x32 per wave
 
 template <class C>
 hipError_t fwd_with(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
-                    const float *step, int64_t N, const bf16_t *V, const bf16_t *Bp, int64_t rp, bf16_t *Y,
-                    const Levels &lv, hipStream_t s) {
+                    const float *step, int64_t N, const bf16_t *V, const bf16_t *Bp, int64_t ldb, int64_t r,
+                    int64_t rp, bf16_t *Y, const Levels &lv, hipStream_t s) {
   dim3 grid((unsigned)((N + C::BN - 1) / C::BN), (unsigned)((T + C::BM - 1) / C::BM));
-  hipLaunchKernelGGL(k_nf4_gemm_fwd<C>, grid, dim3(C::NT), 0, s, X, T, K, codes, absmax_q, step, N, V, Bp, rp, Y, lv);
+  hipLaunchKernelGGL(k_nf4_gemm_fwd<C>, grid, dim3(C::NT), 0, s, X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp,
+                     Y, lv);
   return hipGetLastError();
 }
 
@@ -387,28 +397,41 @@ hipError_t dx_with(const bf16_t *dY, int64_t T, int64_t N, const uint8_t *codes,
 }  // namespace
 
 // Tile choice for an M x N output.  Measured on MI355X (both GEMMs, seven
-// workload shapes): the 8-wave 256x256 tile is fastest whenever it yields at
-// least one workgroup per CU (256 tiles); below that the 128x128 tile, which
-// keeps every CU busy, wins.
+// workload shapes): the largest 8-wave tile that still yields at least one
+// workgroup per CU (256 tiles) is fastest -- 256x256, else 256x128; below that
+// the 128x128 tile, two workgroups per CU, wins.
 int nf4_gemm_pick_tile(int64_t M, int64_t N) {
-  const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
-  return big >= 256 ? NF4_TILE_256x256_W8 : NF4_TILE_128x128;
+  auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  if (tiles(256, 256) >= 256) return NF4_TILE_256x256_W8;
+  if (tiles(256, 128) >= 256) return NF4_TILE_256x128_W8;
+  return NF4_TILE_128x128;
 }
 
 hipError_t launch_nf4_gemm_fwd(int tile, const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes,
                                const uint8_t *absmax_q, const float *step, int64_t N, const bf16_t *V,
-                               const bf16_t *Bp, int64_t rp, bf16_t *Y, const Levels &lv, hipStream_t s) {
+                               const bf16_t *Bp, int64_t ldb, int64_t r, int64_t rp, bf16_t *Y, const Levels &lv,
+                               hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (tile == NF4_TILE_256x256_W8) return fwd_with<T256x256w8>(X, T, K, codes, absmax_q, step, N, V, Bp, rp, Y, lv, s);
-  return fwd_with<T128x128>(X, T, K, codes, absmax_q, step, N, V, Bp, rp, Y, lv, s);
+  switch (tile) {
+    case NF4_TILE_256x256_W8: return fwd_with<T256x256w8>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s);
+    case NF4_TILE_256x128_W8: return fwd_with<T256x128w8>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s);
+    case NF4_TILE_128x256_W8: return fwd_with<T128x256w8>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s);
+    case NF4_TILE_128x128_W8: return fwd_with<T128x128w8>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s);
+    default: return fwd_with<T128x128>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s);
+  }
 }
 
 hipError_t launch_nf4_gemm_dx(int tile, const bf16_t *dY, int64_t T, int64_t N, const uint8_t *codes,
                               const uint8_t *absmax_q, const float *step, int64_t K, const bf16_t *dUp, const bf16_t *A,
                               int64_t r, int64_t rp, bf16_t *dX, const Levels &lv, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (tile == NF4_TILE_256x256_W8) return dx_with<T256x256w8>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s);
-  return dx_with<T128x128>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s);
+  switch (tile) {
+    case NF4_TILE_256x256_W8: return dx_with<T256x256w8>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s);
+    case NF4_TILE_256x128_W8: return dx_with<T256x128w8>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s);
+    case NF4_TILE_128x256_W8: return dx_with<T128x256w8>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s);
+    case NF4_TILE_128x128_W8: return dx_with<T128x128w8>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s);
+    default: return dx_with<T128x128>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s);
+  }
 }
 
 }  // namespace qlora
