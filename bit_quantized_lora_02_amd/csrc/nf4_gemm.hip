@@ -48,6 +48,24 @@ struct TileCfg {
 
 __device__ __forceinline__ int lds_off(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
 
+// Output tile of this workgroup.  Workgroups are dispatched round-robin over
+// the 8 XCDs (linear id i runs on XCD i % 8), each with its own L2.  With
+// xb_m, xb_n > 0 the tile grid (tiles_m x tiles_n) is cut into 8 blocks of
+// xb_m x xb_n tiles and XCD j computes block j, so the activation rows and
+// weight columns one XCD reads are shared by all its workgroups.  With 0 the
+// tiles are taken in row-major order.
+struct TileCoord {
+  int64_t m, n;
+};
+__device__ __forceinline__ TileCoord tile_of(int64_t tiles_n, int xb_m, int xb_n) {
+  const int64_t lin = blockIdx.x;
+  if (xb_m <= 0) return TileCoord{lin / tiles_n, lin % tiles_n};
+  const int64_t xcd = lin & 7, local = lin >> 3;
+  const int64_t blocks_n = tiles_n / xb_n;
+  const int64_t bm = xcd / blocks_n, bn = xcd % blocks_n;
+  return TileCoord{bm * xb_m + local / xb_n, bn * xb_n + local % xb_n};
+}
+
 template <class C>
 __device__ __forceinline__ void zero_acc(f32x16_t acc[C::WM][C::WN]) {
 #pragma unroll
@@ -135,13 +153,14 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
                                                         const float *__restrict__ step, int64_t N,
                                                         const bf16_t *__restrict__ V, const bf16_t *__restrict__ Bp,
                                                         int64_t ldb, int64_t r, int64_t rp, bf16_t *__restrict__ Y,
-                                                        Levels lv) {
+                                                        Levels lv, int xb_m, int xb_n) {
   __shared__ __attribute__((aligned(16))) bf16_t sA[2][C::BM * BK];
   __shared__ __attribute__((aligned(16))) bf16_t sB[2][C::BN * BK];
   __shared__ float s_lv[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-  const int64_t m0 = (int64_t)blockIdx.y * C::BM, n0 = (int64_t)blockIdx.x * C::BN;
+  const TileCoord tc = tile_of((N + C::BN - 1) / C::BN, xb_m, xb_n);
+  const int64_t m0 = tc.m * C::BM, n0 = tc.n * C::BN;
   levels_to_lds(lv, s_lv, tid);
 
   const int nk = (int)(K / BK);
@@ -244,7 +263,8 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
                                                        const uint8_t *__restrict__ absmax_q,
                                                        const float *__restrict__ step, int64_t K,
                                                        const bf16_t *__restrict__ dUp, const bf16_t *__restrict__ A,
-                                                       int64_t r, int64_t rp, bf16_t *__restrict__ dX, Levels lv) {
+                                                       int64_t r, int64_t rp, bf16_t *__restrict__ dX, Levels lv,
+                                                       int xb_m, int xb_n) {
   constexpr int LDB = C::BN + 16;  // padded row length (elements) of the [64][BN] B tile
   constexpr int PIECES = C::BN / 32;  // 32-column pieces per B-tile row
   __shared__ __attribute__((aligned(16))) bf16_t sA[2][C::BM * BK];
@@ -252,7 +272,8 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
   __shared__ float s_lv[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-  const int64_t m0 = (int64_t)blockIdx.y * C::BM, n0 = (int64_t)blockIdx.x * C::BN;  // n0 indexes k_out
+  const TileCoord tc = tile_of((K + C::BN - 1) / C::BN, xb_m, xb_n);
+  const int64_t m0 = tc.m * C::BM, n0 = tc.n * C::BN;  // n0 indexes k_out
   levels_to_lds(lv, s_lv, tid);
 
   const int nk = (int)((N + BK - 1) / BK);
@@ -375,13 +396,39 @@ using T256x128w8 = TileCfg<4, 2, 2, 2>;  // 8 waves, 64x64 per wave
 using T128x256w8 = TileCfg<2, 4, 2, 2>;  // 8 waves, 64x64 per wave
 using T128x128w8 = TileCfg<2, 4, 2, 1>;  // 8 waves, 64x32 per wave
 
+// XCD blocking of a tiles_m x tiles_n grid: the 8-way split (xb_m x xb_n
+// tiles per XCD) that minimises the modelled L2-miss traffic
+//   8 * (xb_m / tiles_m * a_bytes + xb_n / tiles_n * b_bytes),
+// where a_bytes is the activation operand and b_bytes the weight stream.
+// Returns 0 x 0 (row-major order) when the grid does not split into 8 blocks.
+void xcd_blocking(int64_t tiles_m, int64_t tiles_n, double a_bytes, double b_bytes, int *xb_m, int *xb_n) {
+  *xb_m = *xb_n = 0;
+  double best = 0.0;
+  for (int64_t bm = 1; bm <= tiles_m; ++bm) {
+    if (tiles_m % bm) continue;
+    const int64_t blocks_m = tiles_m / bm;
+    if (8 % blocks_m) continue;
+    const int64_t blocks_n = 8 / blocks_m;
+    if (tiles_n % blocks_n) continue;
+    const int64_t bn = tiles_n / blocks_n;
+    const double cost = 8.0 * ((double)bm / tiles_m * a_bytes + (double)bn / tiles_n * b_bytes);
+    if (*xb_m == 0 || cost < best) {
+      best = cost;
+      *xb_m = (int)bm;
+      *xb_n = (int)bn;
+    }
+  }
+}
+
 template <class C>
 hipError_t fwd_with(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
                     const float *step, int64_t N, const bf16_t *V, const bf16_t *Bp, int64_t ldb, int64_t r,
                     int64_t rp, bf16_t *Y, const Levels &lv, hipStream_t s) {
-  dim3 grid((unsigned)((N + C::BN - 1) / C::BN), (unsigned)((T + C::BM - 1) / C::BM));
-  hipLaunchKernelGGL(k_nf4_gemm_fwd<C>, grid, dim3(C::NT), 0, s, X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp,
-                     Y, lv);
+  const int64_t tm = (T + C::BM - 1) / C::BM, tn = (N + C::BN - 1) / C::BN;
+  int xb_m, xb_n;
+  xcd_blocking(tm, tn, 2.0 * T * K, 0.516 * N * K, &xb_m, &xb_n);
+  hipLaunchKernelGGL(k_nf4_gemm_fwd<C>, dim3((unsigned)(tm * tn)), dim3(C::NT), 0, s, X, T, K, codes, absmax_q, step,
+                     N, V, Bp, ldb, r, rp, Y, lv, xb_m, xb_n);
   return hipGetLastError();
 }
 
@@ -389,9 +436,11 @@ template <class C>
 hipError_t dx_with(const bf16_t *dY, int64_t T, int64_t N, const uint8_t *codes, const uint8_t *absmax_q,
                    const float *step, int64_t K, const bf16_t *dUp, const bf16_t *A, int64_t r, int64_t rp,
                    bf16_t *dX, const Levels &lv, hipStream_t s) {
-  dim3 grid((unsigned)((K + C::BN - 1) / C::BN), (unsigned)((T + C::BM - 1) / C::BM));
-  hipLaunchKernelGGL(k_nf4_gemm_dx<C>, grid, dim3(C::NT), 0, s, dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp,
-                     dX, lv);
+  const int64_t tm = (T + C::BM - 1) / C::BM, tn = (K + C::BN - 1) / C::BN;
+  int xb_m, xb_n;
+  xcd_blocking(tm, tn, 2.0 * T * N, 0.516 * N * K, &xb_m, &xb_n);
+  hipLaunchKernelGGL(k_nf4_gemm_dx<C>, dim3((unsigned)(tm * tn)), dim3(C::NT), 0, s, dY, T, N, codes, absmax_q, step,
+                     K, dUp, A, r, rp, dX, lv, xb_m, xb_n);
   return hipGetLastError();
 }
 }  // namespace
