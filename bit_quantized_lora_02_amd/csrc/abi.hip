@@ -197,25 +197,18 @@ struct Split {
   int64_t kchunk = 0;
 };
 
-// Split a reduction of length Kred for an M x N output so that ~1024
-// workgroups run (four per CU), each split at least 256 deep.
-Split plan_split(int64_t M, int64_t N, int64_t Kred) {
+// Reduction split of a skinny LoRA GEMM with M output rows.
+Split plan_skinny(int64_t M, int64_t Kred) {
   Split sp;
-  if (Kred <= 0 || M <= 0 || N <= 0) return sp;
-  const int64_t tiles = ceil_div(M, 64) * ceil_div(N, 64);
-  int64_t want = ceil_div(1024, tiles);
-  int64_t maxs = Kred / 256;
-  if (maxs < 1) maxs = 1;
-  int64_t ns = want < maxs ? want : maxs;
-  if (ns > 64) ns = 64;
-  if (ns < 1) ns = 1;
-  sp.kchunk = up((size_t)ceil_div(Kred, ns), 32);
-  sp.n = (int)ceil_div(Kred, sp.kchunk);
+  if (Kred <= 0 || M <= 0) return sp;
+  skinny_plan(M, Kred, &sp.n, &sp.kchunk);
   return sp;
 }
 
 struct Plan {
-  int64_t rp = 0;
+  int64_t rp = 0;  // row length of the padded rank-wide copies (r rounded up to 64)
+  int rn = 0;      // rank columns of the skinny GEMMs' partial sums
+  int64_t rv = 0;  // r rounded up to 8: rank columns read from padded copies
   size_t off_bp = 0, off_v = 0, off_du = 0, off_part = 0, total = 0;
   Split su, sdu, sdb, sda;
   bool gemv = false;  // forward through the small-token kernel
@@ -228,6 +221,8 @@ bool use_gemv(int64_t T, int64_t K) { return T >= 1 && T <= kGemvMaxT && K % 128
 Plan make_plan(int op, int64_t T, int64_t N, int64_t K, int32_t r) {
   Plan p;
   p.rp = (int64_t)up((size_t)r, 64);
+  p.rn = skinny_rn(r);
+  p.rv = (int64_t)up((size_t)r, 8);
   size_t off = 0;
   p.off_bp = off;
   off = up(off + (size_t)(N * p.rp * 2), kAlign);
@@ -235,8 +230,8 @@ Plan make_plan(int op, int64_t T, int64_t N, int64_t K, int32_t r) {
   off = up(off + (size_t)(T * p.rp * 2), kAlign);
   size_t part = 0;
   if (op == QLORA_OP_FWD) {
-    p.su = plan_split(T, r, K);
-    part = (size_t)p.su.n * T * r * 4;
+    p.su = plan_skinny(T, K);
+    part = (size_t)p.su.n * T * p.rn * 4;
     if (use_gemv(T, K)) {
       p.gemv = true;
       nf4_gemv_plan(T, N, K, &p.gemv_split, &p.gemv_kchunk);
@@ -245,12 +240,12 @@ Plan make_plan(int op, int64_t T, int64_t N, int64_t K, int32_t r) {
   } else {
     p.off_du = off;
     off = up(off + (size_t)(T * p.rp * 2), kAlign);
-    p.su = plan_split(T, r, K);
-    p.sdu = plan_split(T, r, N);
-    p.sdb = plan_split(N, r, T);
-    p.sda = plan_split(r, K, T);
-    const size_t cands[4] = {(size_t)p.su.n * T * r * 4, (size_t)p.sdu.n * T * r * 4, (size_t)p.sdb.n * N * r * 4,
-                             (size_t)p.sda.n * r * K * 4};
+    p.su = plan_skinny(T, K);
+    p.sdu = plan_skinny(T, N);
+    p.sdb = plan_skinny(N, T);
+    p.sda = plan_skinny(K, T);
+    const size_t cands[4] = {(size_t)p.su.n * T * p.rn * 4, (size_t)p.sdu.n * T * p.rn * 4,
+                             (size_t)p.sdb.n * N * p.rn * 4, (size_t)p.sda.n * K * p.rn * 4};
     for (size_t c : cands) part = c > part ? c : part;
   }
   p.off_part = off;
@@ -375,8 +370,9 @@ int qlora_linear_fwd(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const q
     LAUNCH("gemv_reduce", launch_gemv_reduce(part, p.gemv_split, T, N, Y, s));
     return QLORA_OK;
   }
-  LAUNCH("lora_u", launch_gemm_splitk(0, 0, X, K, A, K, T, r, K, p.su.kchunk, p.su.n, part, s));
-  LAUNCH("lora_u_finalize", launch_finalize(part, p.su.n, T, r, U_out, r, U_out ? r : 0, 1.0f, V, p.rp, p.rp, r, sc, s));
+  LAUNCH("lora_u", launch_skinny(false, false, p.rn, X, K, T, A, K, r, K, p.su.kchunk, p.su.n, part, s));
+  LAUNCH("lora_u_finalize",
+         launch_finalize(part, p.su.n, T, p.rn, U_out, r, U_out ? r : 0, 1.0f, V, p.rp, p.rp, r, sc, s));
   // B is read in place when its rows are 16-byte multiples, else from a zero-padded copy
   const bool b_direct = (r % 8) == 0;
   if (!b_direct) LAUNCH("pad_b", launch_pad_copy(B, r, r, N, Bp, p.rp, s));
@@ -415,32 +411,39 @@ int qlora_linear_bwd(const qlora_bf16 *X, const qlora_bf16 *dY, int64_t T, const
   }
   // B and U are read in place when their rows are 16-byte multiples, else from zero-padded copies
   const bool direct = (r % 8) == 0;
+  // (the copies are zero past column r, so r rounded up to 8 columns of them are read)
   const bf16_t *Bsrc = B, *Usrc = U;
-  int64_t ldb = r, ldu = r;
+  int64_t ldb = r, ldu = r, rvb = r, rvu = r;
   if (!direct) {
     LAUNCH("pad_b", launch_pad_copy(B, r, r, N, Bp, p.rp, s));
     Bsrc = Bp;
     ldb = p.rp;
+    rvb = p.rv;
   }
   if (U && !direct) {
     LAUNCH("pad_u", launch_pad_copy(U, r, r, T, Up, p.rp, s));
     Usrc = Up;
     ldu = p.rp;
+    rvu = p.rv;
   } else if (!U) {
-    LAUNCH("lora_u", launch_gemm_splitk(0, 0, X, K, A, K, T, r, K, p.su.kchunk, p.su.n, part, s));
-    LAUNCH("lora_u_finalize", launch_finalize(part, p.su.n, T, r, nullptr, 0, 0, 0.f, Up, p.rp, p.rp, r, 1.0f, s));
+    LAUNCH("lora_u", launch_skinny(false, false, p.rn, X, K, T, A, K, r, K, p.su.kchunk, p.su.n, part, s));
+    LAUNCH("lora_u_finalize",
+           launch_finalize(part, p.su.n, T, p.rn, nullptr, 0, 0, 0.f, Up, p.rp, p.rp, r, 1.0f, s));
     Usrc = Up;
     ldu = p.rp;
+    rvu = p.rv;
   }
   // dU = s dY B  -> dUp [T, rp]
-  LAUNCH("lora_du", launch_gemm_splitk(0, 1, dY, N, Bsrc, ldb, T, r, N, p.sdu.kchunk, p.sdu.n, part, s));
-  LAUNCH("lora_du_finalize", launch_finalize(part, p.sdu.n, T, r, nullptr, 0, 0, 0.f, dUp, p.rp, p.rp, r, sc, s));
+  LAUNCH("lora_du", launch_skinny(false, true, p.rn, dY, N, T, Bsrc, ldb, rvb, N, p.sdu.kchunk, p.sdu.n, part, s));
+  LAUNCH("lora_du_finalize",
+         launch_finalize(part, p.sdu.n, T, p.rn, nullptr, 0, 0, 0.f, dUp, p.rp, p.rp, r, sc, s));
   // dB = s dY^T U  -> [N, r]
-  LAUNCH("lora_db", launch_gemm_splitk(1, 1, dY, N, Usrc, ldu, N, r, T, p.sdb.kchunk, p.sdb.n, part, s));
-  LAUNCH("lora_db_finalize", launch_finalize(part, p.sdb.n, N, r, dB, r, r, sc, nullptr, 0, 0, 0, 0.f, s));
-  // dA = dU^T X  -> [r, K]
-  LAUNCH("lora_da", launch_gemm_splitk(1, 1, dUp, p.rp, X, K, r, K, T, p.sda.kchunk, p.sda.n, part, s));
-  LAUNCH("lora_da_finalize", launch_finalize(part, p.sda.n, r, K, dA, K, K, 1.0f, nullptr, 0, 0, 0, 0.f, s));
+  LAUNCH("lora_db", launch_skinny(true, true, p.rn, dY, N, N, Usrc, ldu, rvu, T, p.sdb.kchunk, p.sdb.n, part, s));
+  LAUNCH("lora_db_finalize", launch_finalize(part, p.sdb.n, N, p.rn, dB, r, r, sc, nullptr, 0, 0, 0, 0.f, s));
+  // dA^T = X^T dU  -> [K, r], stored transposed as dA [r, K]
+  LAUNCH("lora_da", launch_skinny(true, true, p.rn, X, K, K, dUp, p.rp, p.rv, T, p.sda.kchunk, p.sda.n, part, s));
+  LAUNCH("lora_da_finalize",
+         launch_finalize(part, p.sda.n, K, p.rn, dA, K, r, 1.0f, nullptr, 0, 0, 0, 0.f, s, true));
   // dX = dY W' + dU A
   if (dX)
     LAUNCH("nf4_gemm_dx",

@@ -45,11 +45,16 @@ hipError_t launch_nf4_gemv(const bf16_t *X, int64_t T, int64_t K, const uint8_t 
                            const bf16_t *B, int64_t r, float *part, bf16_t *Y, const Levels &lv, hipStream_t s);
 hipError_t launch_gemv_reduce(const float *part, int nsplit, int64_t T, int64_t N, bf16_t *Y, hipStream_t s);
 
-hipError_t launch_gemm_splitk(int la, int lb, const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb, int64_t M,
-                              int64_t N, int64_t Kred, int64_t kchunk, int nsplit, float *C, hipStream_t s);
+// Skinny GEMM of the LoRA branch: C[split][m][j] (j < rn) over one reduction
+// chunk; pt / qt select the storage of the long operand P and the rank-wide
+// operand Q (see lora_gemm.hip).
+int skinny_rn(int64_t r);
+void skinny_plan(int64_t M, int64_t Kred, int *nsplit, int64_t *kchunk);
+hipError_t launch_skinny(bool pt, bool qt, int rn, const bf16_t *P, int64_t ldp, int64_t M, const bf16_t *Q,
+                         int64_t ldq, int64_t Rv, int64_t Kred, int64_t kchunk, int nsplit, float *C, hipStream_t s);
 hipError_t launch_finalize(const float *part, int nsplit, int64_t M, int64_t N, bf16_t *out1, int64_t ld1, int64_t n1,
                            float scale1, bf16_t *out2, int64_t ld2, int64_t n2, int64_t nvalid2, float scale2,
-                           hipStream_t s);
+                           hipStream_t s, bool trans1 = false);
 hipError_t launch_pad_copy(const bf16_t *in, int64_t ldi, int64_t ncols, int64_t M, bf16_t *out, int64_t ldo,
                            hipStream_t s);
 

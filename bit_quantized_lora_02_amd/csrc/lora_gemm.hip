@@ -5,131 +5,207 @@
 // B of shape d x r and A of shape r x k.  Its gradients (same page, "What
 // QLoRA adds"; katajob.com, "What stays in full precision") are
 //   U = X A^T,  dU = s dY B,  dA = dU^T X,  dB = s dY^T U.
-// Every one of them has one long reduction (over n_in, n_out or the T tokens)
-// and a narrow output (r <= 128 on one side), so each is a split-K bf16 MFMA
-// GEMM that writes binary32 partial sums; a finalize kernel then adds the
-// splits in a fixed order (bitwise repeatable, no atomics), scales, and rounds
-// to bf16 once.
-//
-// C[M, N] = sum_k A(m, k) B(k, n), 64x64 tile, reduction step 32, 4 waves in
-// a 2x2 grid, one v_mfma_f32_32x32x16_bf16 tile per wave.  Operand storage:
-//   LA = 0: A(m, k) at A[m*lda + k]   (reduction contiguous)
-//   LA = 1: A(m, k) at A[k*lda + m]   (output index contiguous: transposed into LDS)
-//   LB = 0: B(k, n) at B[n*ldb + k];   LB = 1: B(k, n) at B[k*ldb + n]
-// lda and ldb are multiples of 8 and the bases 16-byte aligned.
+// Every one of them has one long dimension (tokens, n_out or n_in) and a
+// narrow one (the rank, r <= 128), so each is a skinny bf16 MFMA GEMM, split
+// along its reduction, that writes binary32 partial sums; a finalize kernel
+// then adds the splits in a fixed order (bitwise repeatable, no atomics),
+// scales, and rounds to bf16 once.
 #include "device.h"
 #include "launch.h"
 
 namespace qlora {
 
+// ------------------------------------------------------------- skinny GEMM
+// A workgroup owns 128 rows of the long output dimension M and every rank
+// column (RN = r rounded up to 16, 32, 64 or 128), and streams the large
+// operand P once.  C[split][m][j] = sum over its reduction range of
+// P(m, k) Q(k, j), with
+//   PT = 0: P(m, k) = P[m*ldp + k]   PT = 1: P(m, k) = P[k*ldp + m]
+//   QT = 0: Q(k, j) = Q[j*ldq + k]   QT = 1: Q(k, j) = Q[k*ldq + j]
+// Tiles are copied global -> registers -> LDS in their natural layout
+// (16-byte chunks, prefetched one 64-deep step ahead, double-buffered LDS);
+// operands whose reduction index is the row are read with ds_read_b64_tr_b16
+// (lane i of a 16-lane group gets element i & 3 of the 8 bytes addressed by
+// lane 4m + (i >> 2), m = 0..3).  4 waves x 32 rows, v_mfma_f32_16x16x32_bf16.
+// Requirements: ldp, ldq, M (when PT = 1) and the valid Q columns Rv (when
+// QT = 1) are multiples of 8; reduction extents past Kred and rows past M
+// read as zero.
 namespace {
-constexpr int TM = 64, TN = 64, TK = 32;
+typedef float f32x4s_t __attribute__((ext_vector_type(4)));
+typedef short s4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s4_t lds_s4_t;
 
-// LDS tiles are [64 rows][32] bf16, 64-byte rows; 16-byte chunks swizzled so
-// that the 8 rows read by 8 consecutive lanes hit distinct banks.
-__device__ __forceinline__ int soff(int row, int chunk) { return row * TK + ((chunk ^ ((row >> 1) & 3)) << 3); }
-
-// Stage one operand tile into LDS as [row = output index][k].
-template <int L>
-__device__ __forceinline__ void stage_tile(const bf16_t *__restrict__ P, int64_t ld, int64_t r0, int64_t R,
-                                           int64_t k0, int64_t kend, int tid, bf16_t *s) {
-  if (L == 0) {
-    // 64 rows x 4 chunks of 8 k: one chunk per thread
-    const int row = tid >> 2, ch = tid & 3;
-    const int64_t gr = r0 + row, gk = k0 + ch * 8;
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (gr < R) {
-      if (gk + 8 <= kend) {
-        v = *reinterpret_cast<const u32x4_t *>(P + gr * ld + gk);
-      } else {
-        uint16_t e[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) e[i] = (gk + i < kend) ? P[gr * ld + gk + i] : (uint16_t)0;
-        v.x = e[0] | ((uint32_t)e[1] << 16);
-        v.y = e[2] | ((uint32_t)e[3] << 16);
-        v.z = e[4] | ((uint32_t)e[5] << 16);
-        v.w = e[6] | ((uint32_t)e[7] << 16);
-      }
-    }
-    *reinterpret_cast<u32x4_t *>(s + soff(row, ch)) = v;
-  } else {
-    // 32 k x 8 chunks of 8 output indices: one chunk per thread, scattered into [row][k]
-    const int kk = tid >> 3, ch = tid & 7;
-    const int64_t gk = k0 + kk, gr = r0 + ch * 8;
-    uint16_t e[8];
-    if (gk < kend && gr + 8 <= R) {
-      u32x4_t v = *reinterpret_cast<const u32x4_t *>(P + gk * ld + gr);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        e[2 * i] = (uint16_t)(v[i] & 0xffffu);
-        e[2 * i + 1] = (uint16_t)(v[i] >> 16);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) e[i] = (gk < kend && gr + i < R) ? P[gk * ld + gr + i] : (uint16_t)0;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = ch * 8 + i;
-      s[soff(row, kk >> 3) + (kk & 7)] = e[i];
-    }
-  }
+__device__ __forceinline__ f32x4s_t mfma16(const u32x4_t &a, const u32x4_t &b, const f32x4s_t &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
 }
+// Transposing read of an 8-deep reduction run: rows row0..row0+7 of column col..
+__device__ __forceinline__ u32x4_t tr_read8(const bf16_t *base, int ld, int row0, int col) {
+  const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t *)(base + row0 * ld + col));
+  const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t *)(base + (row0 + 4) * ld + col));
+  const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+  return u32x4_t{l2.x, l2.y, h2.x, h2.y};
+}
+constexpr int SK = 64;    // reduction step
+constexpr int SBM = 128;  // rows of M per workgroup
 }  // namespace
 
-template <int LA, int LB>
-__global__ __launch_bounds__(256) void k_gemm_splitk(const bf16_t *__restrict__ A, int64_t lda,
-                                                     const bf16_t *__restrict__ B, int64_t ldb, int64_t M, int64_t N,
-                                                     int64_t Kred, int64_t kchunk, float *__restrict__ C) {
-  __shared__ __attribute__((aligned(16))) bf16_t sA[TM * TK];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[TN * TK];
+template <bool PT, bool QT, int RN>
+__global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, int64_t ldp, int64_t M,
+                                                const bf16_t *__restrict__ Q, int64_t ldq, int64_t Rv, int64_t Kred,
+                                                int64_t kchunk, float *__restrict__ C) {
+  constexpr int LDP = PT ? SBM + 16 : SK;             // LDS row length of the P tile (elements)
+  constexpr int LDQ = QT ? RN + (RN >= 32 ? 16 : 0) : SK;
+  constexpr int P_ROWS = PT ? SK : SBM;
+  constexpr int Q_ROWS = QT ? SK : RN;
+  constexpr int P_CH = SBM * SK / 8 / 256;            // 16-byte chunks of P per thread (4)
+  constexpr int Q_CHUNKS = RN * SK / 8;               // 16-byte chunks of the Q tile
+  constexpr int Q_CH = (Q_CHUNKS + 255) / 256;
+  constexpr int NT_ = RN / 16;
+  __shared__ __attribute__((aligned(16))) bf16_t sP[2][P_ROWS * LDP];
+  __shared__ __attribute__((aligned(16))) bf16_t sQ[2][Q_ROWS * LDQ];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * TM, n0 = (int64_t)blockIdx.x * TN;
-  const int64_t kb = (int64_t)blockIdx.z * kchunk;
+  const int64_t m0 = (int64_t)blockIdx.x * SBM;
+  const int64_t kb = (int64_t)blockIdx.y * kchunk;
   const int64_t ke = (kb + kchunk < Kred) ? kb + kchunk : Kred;
-  f32x16_t acc;
+  const int nsteps = (int)((ke - kb + SK - 1) / SK);
+
+  auto p_off = [&](int c, int &row, int &col) {  // chunk c of the P tile -> LDS (row, col)
+    if (PT) { row = c >> 4; col = (c & 15) * 8; }
+    else { row = c >> 3; col = (((c & 7) ^ (row & 7)) << 3); }  // swizzled 16-byte chunks
+  };
+  u32x4_t rp_[P_CH], rq_[Q_CH];
+  auto load = [&](int s) {
+    const int64_t k0 = kb + (int64_t)s * SK;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-  for (int64_t k0 = kb; k0 < ke; k0 += TK) {
-    stage_tile<LA>(A, lda, m0, M, k0, ke, tid, sA);
-    stage_tile<LB>(B, ldb, n0, N, k0, ke, tid, sB);
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int ch = kk * 2 + (lane >> 5);
-      const u32x4_t a = *reinterpret_cast<const u32x4_t *>(sA + soff(wm * 32 + (lane & 31), ch));
-      const u32x4_t b = *reinterpret_cast<const u32x4_t *>(sB + soff(wn * 32 + (lane & 31), ch));
-      acc = mfma_32x32x16(a, b, acc);
+    for (int i = 0; i < P_CH; ++i) {
+      const int c = tid + 256 * i;
+      bool ok;
+      const bf16_t *src;
+      if (PT) {
+        const int64_t k = k0 + (c >> 4), m = m0 + (c & 15) * 8;
+        ok = k < ke && m < M;
+        src = P + k * ldp + m;
+      } else {
+        const int64_t m = m0 + (c >> 3), k = k0 + (c & 7) * 8;
+        ok = m < M && k < ke;
+        src = P + m * ldp + k;
+      }
+      rp_[i] = ok ? *reinterpret_cast<const u32x4_t *>(src) : u32x4_t{0u, 0u, 0u, 0u};
     }
-    __syncthreads();
-  }
-  float *Cs = C + (int64_t)blockIdx.z * M * N;
-  const int64_t col = n0 + wn * 32 + (lane & 31);
-  if (col < N) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int64_t row = m0 + wm * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-      if (row < M) Cs[row * N + col] = acc[e];
+    for (int i = 0; i < Q_CH; ++i) {
+      const int c = tid + 256 * i;
+      bool ok = c < Q_CHUNKS;
+      const bf16_t *src = Q;
+      if (QT) {
+        const int64_t k = k0 + c / (RN / 8), j = (c % (RN / 8)) * 8;
+        ok = ok && k < ke && j < Rv;
+        src = Q + k * ldq + j;
+      } else {
+        const int64_t j = c >> 3, k = k0 + (c & 7) * 8;
+        ok = ok && j < Rv && k < ke;
+        src = Q + j * ldq + k;
+      }
+      rq_[i] = ok ? *reinterpret_cast<const u32x4_t *>(src) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < P_CH; ++i) {
+      int row, col;
+      p_off(tid + 256 * i, row, col);
+      *reinterpret_cast<u32x4_t *>(&sP[buf][row * LDP + col]) = rp_[i];
+    }
+#pragma unroll
+    for (int i = 0; i < Q_CH; ++i) {
+      const int c = tid + 256 * i;
+      if (c >= Q_CHUNKS) break;
+      int row, col;
+      if (QT) { row = c / (RN / 8); col = (c % (RN / 8)) * 8; }
+      else { row = c >> 3; col = (((c & 7) ^ (row & 7)) << 3); }
+      *reinterpret_cast<u32x4_t *>(&sQ[buf][row * LDQ + col]) = rq_[i];
+    }
+  };
+
+  f32x4s_t acc[2][NT_];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NT_; ++j) acc[i][j] = f32x4s_t{0.f, 0.f, 0.f, 0.f};
+
+  const int g = lane >> 4, a = lane & 15;
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int kk = 0; kk < SK / 32; ++kk) {
+      u32x4_t pa[2], qb[NT_];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int mrow = wave * 32 + i * 16;
+        if (PT) {
+          pa[i] = tr_read8(sP[buf], LDP, kk * 32 + 8 * g + (a >> 2), mrow + 4 * (a & 3));
+        } else {
+          const int row = mrow + a, chunk = kk * 4 + g;
+          pa[i] = *reinterpret_cast<const u32x4_t *>(&sP[buf][row * LDP + ((chunk ^ (row & 7)) << 3)]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NT_; ++j) {
+        if (QT) {
+          qb[j] = tr_read8(sQ[buf], LDQ, kk * 32 + 8 * g + (a >> 2), j * 16 + 4 * (a & 3));
+        } else {
+          const int row = j * 16 + a, chunk = kk * 4 + g;
+          qb[j] = *reinterpret_cast<const u32x4_t *>(&sQ[buf][row * LDQ + ((chunk ^ (row & 7)) << 3)]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < NT_; ++j) acc[i][j] = mfma16(pa[i], qb[j], acc[i][j]);
+    }
+  };
+
+  if (nsteps > 0) {
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int s = 0; s < nsteps; ++s) {
+      const int buf = s & 1;
+      if (s + 1 < nsteps) load(s + 1);
+      mma(buf);
+      if (s + 1 < nsteps) store(buf ^ 1);
+      __syncthreads();
     }
   }
+  // element i of lane l of tile (mt, nt): row 16 mt + 4 (l >> 4) + i, column 16 nt + (l & 15)
+  float *Cs = C + (int64_t)blockIdx.y * M * RN;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NT_; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t m = m0 + wave * 32 + i * 16 + 4 * g + e;
+        if (m < M) Cs[m * RN + j * 16 + a] = acc[i][j][e];
+      }
 }
 
-// out1[m*ld1 + n] = bf16(scale1 * S) for n < n1;
+// out1[m*ld1 + n] (or out1[n*ld1 + m] with trans1) = bf16(scale1 * S) for n < n1;
 // out2[m*ld2 + n] = n < nvalid2 ? bf16(scale2 * S) : 0 for n < n2;
 // S = sum over splits p = 0 .. nsplit-1 (in that order) of part[p][m][n] (ld = N).
 __global__ __launch_bounds__(256) void k_finalize(const float *__restrict__ part, int nsplit, int64_t M, int64_t N,
                                                   bf16_t *__restrict__ out1, int64_t ld1, int64_t n1, float scale1,
-                                                  bf16_t *__restrict__ out2, int64_t ld2, int64_t n2, int64_t nvalid2,
-                                                  float scale2) {
+                                                  int trans1, bf16_t *__restrict__ out2, int64_t ld2, int64_t n2,
+                                                  int64_t nvalid2, float scale2) {
   const int64_t ncol = (n1 > n2) ? n1 : n2;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= M * ncol) return;
-  const int64_t m = i / ncol, n = i - m * ncol;
+  // transposed first output: consecutive threads take consecutive m so its stores coalesce
+  const int64_t m = trans1 ? i % M : i / ncol, n = trans1 ? i / M : i - m * ncol;
   float sum = 0.f;
   if (n < N)
     for (int p = 0; p < nsplit; ++p) sum += part[((int64_t)p * M + m) * N + n];
-  if (out1 && n < n1) out1[m * ld1 + n] = f32_to_bf16(scale1 * sum);
+  if (out1 && n < n1) out1[trans1 ? n * ld1 + m : m * ld1 + n] = f32_to_bf16(scale1 * sum);
   if (out2 && n < n2) out2[m * ld2 + n] = (n < nvalid2) ? f32_to_bf16(scale2 * sum) : (bf16_t)0;
 }
 
@@ -142,30 +218,55 @@ __global__ __launch_bounds__(256) void k_pad_copy(const bf16_t *__restrict__ in,
   out[i] = (n < ncols) ? in[m * ldi + n] : (bf16_t)0;
 }
 
-hipError_t launch_gemm_splitk(int la, int lb, const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb, int64_t M,
-                              int64_t N, int64_t Kred, int64_t kchunk, int nsplit, float *C, hipStream_t s) {
-  if (M == 0 || N == 0 || nsplit == 0) return hipSuccess;
-  dim3 grid((unsigned)((N + TN - 1) / TN), (unsigned)((M + TM - 1) / TM), (unsigned)nsplit);
-  if (la == 0 && lb == 0)
-    hipLaunchKernelGGL((k_gemm_splitk<0, 0>), grid, dim3(256), 0, s, A, lda, B, ldb, M, N, Kred, kchunk, C);
-  else if (la == 0 && lb == 1)
-    hipLaunchKernelGGL((k_gemm_splitk<0, 1>), grid, dim3(256), 0, s, A, lda, B, ldb, M, N, Kred, kchunk, C);
-  else if (la == 1 && lb == 0)
-    hipLaunchKernelGGL((k_gemm_splitk<1, 0>), grid, dim3(256), 0, s, A, lda, B, ldb, M, N, Kred, kchunk, C);
-  else
-    hipLaunchKernelGGL((k_gemm_splitk<1, 1>), grid, dim3(256), 0, s, A, lda, B, ldb, M, N, Kred, kchunk, C);
-  return hipGetLastError();
-}
-
 hipError_t launch_finalize(const float *part, int nsplit, int64_t M, int64_t N, bf16_t *out1, int64_t ld1, int64_t n1,
                            float scale1, bf16_t *out2, int64_t ld2, int64_t n2, int64_t nvalid2, float scale2,
-                           hipStream_t s) {
+                           hipStream_t s, bool trans1) {
   const int64_t ncol = (n1 > n2) ? n1 : n2;
   const int64_t total = M * ncol;
   if (total == 0) return hipSuccess;
   hipLaunchKernelGGL(k_finalize, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, nsplit, M, N, out1, ld1,
-                     n1, scale1, out2, ld2, n2, nvalid2, scale2);
+                     n1, scale1, trans1 ? 1 : 0, out2, ld2, n2, nvalid2, scale2);
   return hipGetLastError();
+}
+
+// Rank columns held by a skinny-GEMM workgroup for rank r.
+int skinny_rn(int64_t r) { return r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : 128; }
+
+// Split of the reduction for a skinny GEMM with M output rows: aim at ~512
+// workgroups with at least four 64-deep steps each.
+void skinny_plan(int64_t M, int64_t Kred, int *nsplit, int64_t *kchunk) {
+  const int64_t tiles = (M + SBM - 1) / SBM;
+  int64_t ns = (512 + tiles - 1) / tiles;
+  const int64_t by_depth = Kred / 256 > 0 ? Kred / 256 : 1;
+  if (ns > by_depth) ns = by_depth;
+  if (ns > 64) ns = 64;
+  if (ns < 1) ns = 1;
+  int64_t kc = (Kred + ns - 1) / ns;
+  kc = (kc + SK - 1) / SK * SK;
+  *kchunk = kc > 0 ? kc : SK;
+  *nsplit = Kred > 0 ? (int)((Kred + *kchunk - 1) / *kchunk) : 0;
+}
+
+template <bool PT, bool QT>
+static hipError_t skinny_dispatch(int rn, dim3 grid, hipStream_t s, const bf16_t *P, int64_t ldp, int64_t M,
+                            const bf16_t *Q, int64_t ldq, int64_t Rv, int64_t Kred, int64_t kchunk, float *C) {
+  switch (rn) {
+    case 16: hipLaunchKernelGGL((k_skinny<PT, QT, 16>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C); break;
+    case 32: hipLaunchKernelGGL((k_skinny<PT, QT, 32>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C); break;
+    case 64: hipLaunchKernelGGL((k_skinny<PT, QT, 64>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C); break;
+    default: hipLaunchKernelGGL((k_skinny<PT, QT, 128>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_skinny(bool pt, bool qt, int rn, const bf16_t *P, int64_t ldp, int64_t M, const bf16_t *Q,
+                         int64_t ldq, int64_t Rv, int64_t Kred, int64_t kchunk, int nsplit, float *C, hipStream_t s) {
+  if (M == 0 || nsplit == 0) return hipSuccess;
+  dim3 grid((unsigned)((M + SBM - 1) / SBM), (unsigned)nsplit);
+  if (!pt && !qt) return skinny_dispatch<false, false>(rn, grid, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C);
+  if (!pt && qt) return skinny_dispatch<false, true>(rn, grid, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C);
+  if (pt && !qt) return skinny_dispatch<true, false>(rn, grid, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C);
+  return skinny_dispatch<true, true>(rn, grid, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C);
 }
 
 hipError_t launch_pad_copy(const bf16_t *in, int64_t ldi, int64_t ncols, int64_t M, bf16_t *out, int64_t ldo,
