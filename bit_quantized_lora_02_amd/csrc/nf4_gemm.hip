@@ -10,18 +10,24 @@
 //
 // A workgroup of WAVES_M x WAVES_N waves computes a BM x BN output tile; each
 // wave owns WM x WN tiles of v_mfma_f32_32x32x16_bf16 (32x32 outputs each).
-// The reduction runs in steps of 64 (one NF4 block per weight row): the A
-// operand (activations) goes global -> registers -> LDS; the B operand is
-// decoded from nibbles in registers and written to LDS as bf16, so the
-// dequantized weight exists only as one BN x 64 tile in LDS.  LDS is double
-// buffered and the global loads of step s+1 are issued before the MFMAs of
-// step s, so one barrier per step separates the two.  The LoRA term follows as
-// a few unpipelined extra reduction steps over the padded rank, landing in the
-// same binary32 accumulators.
+// The reduction runs in steps of 64 (one NF4 block per weight row):
+//  - the activation tile of step s+1 is loaded into registers at the start of
+//    step s and written to the other LDS buffer at its end;
+//  - the codes and block constants of step s+2 are loaded into one of two
+//    register slots;
+//  - the MFMAs of step s are interleaved with the decode of step s+1 (level
+//    lookup, one binary32 multiply per weight, bf16 pack, LDS store), so the
+//    decode's VALU and LDS work runs while the matrix unit is busy;
+//  - one barrier per step.
+// The dequantized weight therefore exists only as one 64-deep tile in LDS.
+// The LoRA term follows as a few extra reduction steps over the padded rank,
+// landing in the same binary32 accumulators.
 //
-// LDS tiles are [row][64] bf16 (128-byte rows) with the 16-byte chunk index
-// XOR-swizzled by (row & 7), so the 8 rows that 8 consecutive lanes read fall
-// on distinct banks.
+// LDS tiles of the A operand (and the forward B operand) are [row][64] bf16
+// (128-byte rows) with the 16-byte chunk index XOR-swizzled by (row / 2) % 8:
+// a 16-lane phase of ds_read_b128 then covers all 64 banks once.
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -34,19 +40,25 @@ constexpr int BK = 64;
 template <int WAVES_M_, int WAVES_N_, int WM_, int WN_>
 struct TileCfg {
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, WM = WM_, WN = WN_;
-  static constexpr int NT = 64 * WAVES_M * WAVES_N;
+  static constexpr int NW = WAVES_M * WAVES_N;
+  static constexpr int NT = 64 * NW;
   static constexpr int BM = WAVES_M * WM * 32;
   static constexpr int BN = WAVES_N * WN * 32;
-  static constexpr int A_CH = BM * 8 / NT;   // 16-byte chunks of the A tile per thread and step
-  // 16-byte chunks of codes (32 nibbles) per thread; with fewer chunks than
-  // threads (C_SPARSE) only the first 2*BN threads load and decode
-  static constexpr bool C_SPARSE = BN * 2 < NT;
-  static constexpr int C_CH = C_SPARSE ? 1 : BN * 2 / NT;
-  static constexpr int L_CH = BN * 8 / NT;   // 16-byte bf16 chunks of the LoRA B tile per thread (forward)
-  static_assert(A_CH >= 1 && C_CH >= 1 && L_CH >= 1, "unsupported tile");
+  static constexpr int A_LD = BM * 8 / NT;  // direct 16-byte loads of the A tile per thread and step
+  // weights decoded per decoding thread and step (at least 16); the first DEC threads decode
+  static constexpr int E = (BN * BK / NT > 16) ? BN * BK / NT : 16;
+  static constexpr int DEC = BN * BK / E;
+  static constexpr int NWD = E / 8;         // code words (8 nibbles each) per thread and step
+  static constexpr int L_CH = BN * 8 / NT;  // 16-byte chunks of the LoRA B tile per thread (forward)
+  static_assert(BM * 8 % NT == 0 && A_LD >= 1, "unsupported tile");
+  static_assert((E == 16 || E == 32) && DEC % 64 == 0 && DEC <= NT, "unsupported tile");
+  static_assert(WM % 2 == 0, "the MFMA rows are issued in two halves");
 };
 
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3); }
+
+// Keep the instruction order written in the source at this point.
+__device__ __forceinline__ void fence_sched() { __builtin_amdgcn_sched_barrier(0); }
 
 // Output tile of this workgroup.  Workgroups are dispatched round-robin over
 // the 8 XCDs (linear id i runs on XCD i % 8), each with its own L2.  With
@@ -76,52 +88,128 @@ __device__ __forceinline__ void zero_acc(f32x16_t acc[C::WM][C::WN]) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 }
 
-// Rows [row0, row0+BM) x columns [col0, col0+64) of a row-major bf16 matrix
-// into registers: chunk c = tid + NT*i covers row c>>3, 16-byte chunk c&7.
-// Rows >= rows or columns >= cols read as zero (cols % 8 == 0).
+// Per-lane source rows of the activation tile: load i of this thread covers
+// chunk c = tid + NT*i, i.e. tile row c / 8 and 16-byte chunk c % 8.  Rows
+// past `rows` re-read the last row (their outputs are never stored).
 template <class C>
-__device__ __forceinline__ void load_a(const bf16_t *__restrict__ src, int64_t ld, int64_t row0, int64_t rows,
-                                       int64_t col0, int64_t cols, int tid, u32x4_t r[C::A_CH]) {
+struct ALoads {
+  const bf16_t *src[C::A_LD];
+  int col[C::A_LD], off[C::A_LD];
+  __device__ __forceinline__ void init(const bf16_t *__restrict__ base, int64_t ld, int64_t m0, int64_t rows, int tid) {
 #pragma unroll
-  for (int i = 0; i < C::A_CH; ++i) {
+    for (int i = 0; i < C::A_LD; ++i) {
+      const int c = tid + C::NT * i, row = c >> 3;
+      const int64_t grow = (m0 + row < rows) ? m0 + row : rows - 1;
+      src[i] = base + grow * ld;
+      col[i] = 8 * (c & 7);
+      off[i] = lds_off(row, c & 7);
+    }
+  }
+  // Reduction columns k0 .. k0+63 into registers; a chunk starting at or past
+  // kmax re-reads the last chunk (the matching weight rows decode to 0).
+  __device__ __forceinline__ void load(int64_t k0, int64_t kmax, u32x4_t (&r)[C::A_LD]) const {
+#pragma unroll
+    for (int i = 0; i < C::A_LD; ++i) {
+      int64_t c = k0 + col[i];
+      c = c < kmax ? c : kmax - 8;
+      r[i] = *reinterpret_cast<const u32x4_t *>(src[i] + c);
+    }
+  }
+  __device__ __forceinline__ void store(const u32x4_t (&r)[C::A_LD], bf16_t *sa) const {
+#pragma unroll
+    for (int i = 0; i < C::A_LD; ++i) *reinterpret_cast<u32x4_t *>(sa + off[i]) = r[i];
+  }
+};
+
+// Code words of one thread and step (E/2 bytes, one block constant).
+template <int NWD>
+__device__ __forceinline__ void load_words(const uint8_t *__restrict__ p, uint32_t (&w)[NWD]) {
+  if constexpr (NWD == 4) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(p);
+    w[0] = v.x, w[1] = v.y, w[2] = v.z, w[3] = v.w;
+  } else {
+    const u32x2_t v = *reinterpret_cast<const u32x2_t *>(p);
+    w[0] = v.x, w[1] = v.y;
+  }
+}
+
+// The two halves of decoding one code word: the level lookups, then the
+// binary32 products with the block constant packed to bf16.
+__device__ __forceinline__ void lookup8(uint32_t w, const float *s_lv, float (&v)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = s_lv[(w >> (4 * e)) & 15u];
+}
+__device__ __forceinline__ u32x4_t scale_pack8(const float (&v)[8], float cq) {
+  return u32x4_t{pack_bf16x2(__fmul_rn(v[0], cq), __fmul_rn(v[1], cq)),
+                 pack_bf16x2(__fmul_rn(v[2], cq), __fmul_rn(v[3], cq)),
+                 pack_bf16x2(__fmul_rn(v[4], cq), __fmul_rn(v[5], cq)),
+                 pack_bf16x2(__fmul_rn(v[6], cq), __fmul_rn(v[7], cq))};
+}
+
+// A operand of substep kk (16 reduction columns) for this wave's WM tiles.
+template <class C>
+__device__ __forceinline__ void read_a(const bf16_t *sa, int wm, int lane, int kk, u32x4_t (&a)[C::WM]) {
+  const int chunk = kk * 2 + (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < C::WM; ++i)
+    a[i] = *reinterpret_cast<const u32x4_t *>(sa + lds_off((wm * C::WM + i) * 32 + (lane & 31), chunk));
+}
+// B operand from a [n][64] tile (forward)
+template <class C>
+__device__ __forceinline__ void read_b_rows(const bf16_t *sb, int wn, int lane, int kk, u32x4_t (&b)[C::WN]) {
+  const int chunk = kk * 2 + (lane >> 5);
+#pragma unroll
+  for (int j = 0; j < C::WN; ++j)
+    b[j] = *reinterpret_cast<const u32x4_t *>(sb + lds_off((wn * C::WN + j) * 32 + (lane & 31), chunk));
+}
+// B operand from a natural [k][LDB] tile with two transposing reads per tile:
+// in each 16-lane group, lane i gets element (i & 3) of the 8 bytes addressed
+// by lane 4m + (i >> 2), so lane a points at row base + (a >> 2), columns
+// 4 (a & 3) .. +3, and reads of rows +0..3 and +4..7 give its 8 reduction values.
+template <class C, int LDB>
+__device__ __forceinline__ void read_b_tr(const bf16_t *sb, int wn, int lane, int kk, u32x4_t (&b)[C::WN]) {
+  typedef short s4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s4_t lds_s4;
+  const int grp = lane >> 4, ai = lane & 15;
+  const int row = kk * 16 + 8 * (grp >> 1) + (ai >> 2);
+#pragma unroll
+  for (int j = 0; j < C::WN; ++j) {
+    const int col = (wn * C::WN + j) * 32 + 16 * (grp & 1) + 4 * (ai & 3);
+    const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(sb + row * LDB + col));
+    const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(sb + (row + 4) * LDB + col));
+    const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+    b[j] = u32x4_t{l2.x, l2.y, h2.x, h2.y};
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void mma_rows(int i0, int i1, const u32x4_t (&a)[C::WM], const u32x4_t (&b)[C::WN],
+                                         f32x16_t (&acc)[C::WM][C::WN]) {
+#pragma unroll
+  for (int i = i0; i < i1; ++i)
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) acc[i][j] = mfma_32x32x16(a[i], b[j], acc[i][j]);
+}
+
+// Rows [row0, row0+BM) x columns [col0, col0+64) of a row-major bf16 matrix
+// into registers and LDS (the unpipelined LoRA steps): chunk c = tid + NT*i
+// covers row c>>3, 16-byte chunk c&7.  Rows >= rows or columns >= cols read
+// as zero (cols % 8 == 0).
+template <class C>
+__device__ __forceinline__ void copy_a_tile(const bf16_t *__restrict__ src, int64_t ld, int64_t row0, int64_t rows,
+                                            int64_t col0, int64_t cols, int tid, bf16_t *s) {
+  u32x4_t r[C::A_LD];
+#pragma unroll
+  for (int i = 0; i < C::A_LD; ++i) {
     const int c = tid + C::NT * i;
     const int64_t row = row0 + (c >> 3), col = col0 + (c & 7) * 8;
     r[i] = (row < rows && col < cols) ? *reinterpret_cast<const u32x4_t *>(src + row * ld + col)
                                       : u32x4_t{0u, 0u, 0u, 0u};
   }
-}
-
-template <class C>
-__device__ __forceinline__ void store_a(bf16_t *s, int tid, const u32x4_t r[C::A_CH]) {
 #pragma unroll
-  for (int i = 0; i < C::A_CH; ++i) {
+  for (int i = 0; i < C::A_LD; ++i) {
     const int c = tid + C::NT * i;
     *reinterpret_cast<u32x4_t *>(s + lds_off(c >> 3, c & 7)) = r[i];
-  }
-}
-
-// One 64-deep reduction step out of LDS for this wave's WM x WN MFMA tiles.
-template <class C>
-__device__ __forceinline__ void mma_step(const bf16_t *sA, const bf16_t *sB, int wm, int wn, int lane,
-                                         f32x16_t acc[C::WM][C::WN]) {
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int chunk = kk * 2 + (lane >> 5);
-    u32x4_t a[C::WM], b[C::WN];
-#pragma unroll
-    for (int i = 0; i < C::WM; ++i) {
-      const int ra = (wm * C::WM + i) * 32 + (lane & 31);
-      a[i] = *reinterpret_cast<const u32x4_t *>(sA + lds_off(ra, chunk));
-    }
-#pragma unroll
-    for (int j = 0; j < C::WN; ++j) {
-      const int rb = (wn * C::WN + j) * 32 + (lane & 31);
-      b[j] = *reinterpret_cast<const u32x4_t *>(sB + lds_off(rb, chunk));
-    }
-#pragma unroll
-    for (int i = 0; i < C::WM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::WN; ++j) acc[i][j] = mfma_32x32x16(a[i], b[j], acc[i][j]);
   }
 }
 
@@ -140,6 +228,52 @@ __device__ __forceinline__ void store_out(bf16_t *__restrict__ out, int64_t ld, 
         if (row < rows) out[row * ld + col] = f32_to_bf16(acc[i][j][e]);
       }
     }
+}
+
+// One pipelined reduction step (see the file comment).  P = s % 2 selects the
+// LDS buffers and register slots: step s is multiplied out of buffer P while
+// the words in slot P^1 (step s+1) are decoded into buffer P^1, the
+// activation tile of step s+1 goes through registers into buffer P^1, and
+// step s+2's words are loaded into slot P.  The caller's lambdas carry the
+// layout differences between the forward and dX: `load_next(ra)` issues the
+// global loads, `store_word(w, bf16x8)` writes word w of the decoded slot,
+// `store_a(ra)` writes the activation tile.
+template <class C, class ReadB, class LoadNext, class StoreWord, class StoreA>
+__device__ __forceinline__ void pipelined_step(const bf16_t *sa, const bf16_t *sb, int wm, int wn, int lane,
+                                               const uint32_t (&words)[C::NWD], const RawScale &scale,
+                                               const float *s_lv, f32x16_t (&acc)[C::WM][C::WN], ReadB read_b,
+                                               LoadNext load_next, StoreWord store_word, StoreA store_a,
+                                               bool decoder) {
+  u32x4_t ra[C::A_LD];
+  load_next(ra);  // activation tile of step s+1, then the words of step s+2
+  fence_sched();
+  const float cq = scale_of(scale);
+  constexpr int EVERY = 4 / C::NWD;  // substeps per decoded word
+  {
+    u32x4_t a[2][C::WM], b[2][C::WN];
+    float v[8];
+    read_a<C>(sa, wm, lane, 0, a[0]);
+    read_b(sb, 0, b[0]);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int cur = kk & 1;
+      const bool dec = decoder && (kk % EVERY) == 0;
+      if (dec) lookup8(words[kk / EVERY], s_lv, v);
+      fence_sched();
+      mma_rows<C>(0, C::WM / 2, a[cur], b[cur], acc);
+      fence_sched();
+      if (dec) store_word(kk / EVERY, scale_pack8(v, cq));
+      if (kk == 3) store_a(ra);
+      if (kk < 3) {
+        read_a<C>(sa, wm, lane, kk + 1, a[cur ^ 1]);
+        read_b(sb, kk + 1, b[cur ^ 1]);
+      }
+      fence_sched();
+      mma_rows<C>(C::WM / 2, C::WM, a[cur], b[cur], acc);
+      fence_sched();
+    }
+  }
+  __syncthreads();
 }
 
 }  // namespace
@@ -164,83 +298,87 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
   levels_to_lds(lv, s_lv, tid);
 
   const int nk = (int)(K / BK);
-  u32x4_t ra[C::A_CH];
-  u32x4_t rc[C::C_CH];
-  RawScale rcq[C::C_CH];
-
-  auto load_main = [&](int s) {
-    const int64_t k0 = (int64_t)s * BK;
-    load_a<C>(X, K, m0, T, k0, K, tid, ra);
-#pragma unroll
-    for (int i = 0; i < C::C_CH; ++i) {
-      const int c = tid + C::NT * i;
-      const int64_t wrow = n0 + (c >> 1);
-      if (wrow < N && (!C::C_SPARSE || c < 2 * C::BN)) {
-        rc[i] = *reinterpret_cast<const u32x4_t *>(codes + wrow * (K / 2) + k0 / 2 + (c & 1) * 16);
-        rcq[i] = load_scale(absmax_q, step, wrow * (K / BK) + s);
-      } else {
-        rc[i] = u32x4_t{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
-        rcq[i] = RawScale{0u, 0.f};
-      }
-    }
+  ALoads<C> al;
+  al.init(X, K, m0, T, tid);
+  // this thread decodes weights part*E .. part*E+E-1 of tile row brow
+  constexpr int PARTS = BK / C::E;
+  const bool decoder = tid < C::DEC;  // wave-uniform
+  const int brow = decoder ? tid / PARTS : 0, part = tid % PARTS;
+  const int64_t wrow = (n0 + brow < N) ? n0 + brow : N - 1;  // rows past N feed columns that are never stored
+  const uint8_t *crow = codes + wrow * (K / 2) + part * (C::E / 2);
+  const int64_t blk0 = wrow * (K / BK);
+  uint32_t rc[2][C::NWD];
+  RawScale rs[2];
+  auto load_words_of = [&](int s, uint32_t(&w)[C::NWD], RawScale &sc) {
+    load_words<C::NWD>(crow + (int64_t)s * (BK / 2), w);
+    sc = load_scale(absmax_q, step, blk0 + s);
   };
-  auto store_main = [&](int buf) {
-    store_a<C>(sA[buf], tid, ra);
-#pragma unroll
-    for (int i = 0; i < C::C_CH; ++i) {
-      const int c = tid + C::NT * i;
-      if (C::C_SPARSE && c >= 2 * C::BN) break;
-      const int row = c >> 1, half = c & 1;
-      const float cq = scale_of(rcq[i]);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        float v[8];
-        decode8(rc[i][w], cq, s_lv, v);
-        u32x4_t o;
-        o.x = pack_bf16x2(v[0], v[1]);
-        o.y = pack_bf16x2(v[2], v[3]);
-        o.z = pack_bf16x2(v[4], v[5]);
-        o.w = pack_bf16x2(v[6], v[7]);
-        *reinterpret_cast<u32x4_t *>(sB[buf] + lds_off(row, half * 4 + w)) = o;
-      }
-    }
-  };
+  auto read_b = [&](const bf16_t *sb, int kk, u32x4_t(&b)[C::WN]) { read_b_rows<C>(sb, wn, lane, kk, b); };
 
   f32x16_t acc[C::WM][C::WN];
   zero_acc<C>(acc);
 
-  load_main(0);
-  __syncthreads();  // level table visible
-  store_main(0);
-  __syncthreads();
-  for (int s = 0; s < nk; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nk) load_main(s + 1);
-    mma_step<C>(sA[buf], sB[buf], wm, wn, lane, acc);
-    if (s + 1 < nk) store_main(buf ^ 1);
-    __syncthreads();
+  // prologue: tile 0 of A, words of steps 0 and 1, decode step 0
+  {
+    u32x4_t ra[C::A_LD];
+    al.load(0, K, ra);
+    al.store(ra, sA[0]);
   }
+  load_words_of(0, rc[0], rs[0]);
+  load_words_of(nk > 1 ? 1 : 0, rc[1], rs[1]);
+  __syncthreads();  // level table visible
+  {
+    const float cq = scale_of(rs[0]);
+    if (decoder)
+      for (int w = 0; w < C::NWD; ++w) {
+        float v[8];
+        lookup8(rc[0][w], s_lv, v);
+        *reinterpret_cast<u32x4_t *>(sB[0] + lds_off(brow, part * C::NWD + w)) = scale_pack8(v, cq);
+      }
+  }
+  __syncthreads();
+
+  auto step_p = [&](auto pc, int s) {
+    constexpr int P = decltype(pc)::value;
+    const int sa = (s + 1 < nk) ? s + 1 : nk - 1, sc = (s + 2 < nk) ? s + 2 : nk - 1;
+    auto load_next = [&](u32x4_t(&ra)[C::A_LD]) {
+      al.load((int64_t)sa * BK, K, ra);
+      fence_sched();  // activation loads first: waiting for them leaves the words in flight
+      load_words_of(sc, rc[P], rs[P]);
+    };
+    auto store_word = [&](int w, const u32x4_t &o) {
+      *reinterpret_cast<u32x4_t *>(sB[P ^ 1] + lds_off(brow, part * C::NWD + w)) = o;
+    };
+    auto store_a = [&](const u32x4_t(&ra)[C::A_LD]) { al.store(ra, sA[P ^ 1]); };
+    pipelined_step<C>(sA[P], sB[P], wm, wn, lane, rc[P ^ 1], rs[P ^ 1], s_lv, acc, read_b, load_next,
+                            store_word, store_a, decoder);
+  };
+  int s = 0;
+  for (; s + 1 < nk; s += 2) {
+    step_p(std::integral_constant<int, 0>(), s);
+    step_p(std::integral_constant<int, 1>(), s + 1);
+  }
+  if (s < nk) step_p(std::integral_constant<int, 0>(), s);
+
   // LoRA up-projection: V [T, rp] . Bp [N, rp]^T, one 64-deep step at a time
   for (int64_t k0 = 0; k0 < rp; k0 += BK) {
-    {
-      u32x4_t rv[C::A_CH], rb[C::L_CH];
-      load_a<C>(V, rp, m0, T, k0, rp, tid, rv);
+    copy_a_tile<C>(V, rp, m0, T, k0, rp, tid, sA[0]);
 #pragma unroll
-      for (int i = 0; i < C::L_CH; ++i) {
-        const int c = tid + C::NT * i;
-        const int64_t wrow = n0 + (c >> 3), col = k0 + (c & 7) * 8;  // r % 8 == 0 or B padded to ldb
-        rb[i] = (wrow < N && col < r) ? *reinterpret_cast<const u32x4_t *>(Bp + wrow * ldb + col)
-                                      : u32x4_t{0u, 0u, 0u, 0u};
-      }
-      store_a<C>(sA[0], tid, rv);
-#pragma unroll
-      for (int i = 0; i < C::L_CH; ++i) {
-        const int c = tid + C::NT * i;
-        *reinterpret_cast<u32x4_t *>(sB[0] + lds_off(c >> 3, c & 7)) = rb[i];
-      }
+    for (int i = 0; i < C::L_CH; ++i) {
+      const int c = tid + C::NT * i;
+      const int64_t brw = n0 + (c >> 3), col = k0 + (c & 7) * 8;  // r % 8 == 0 or B padded to ldb
+      const u32x4_t v = (brw < N && col < r) ? *reinterpret_cast<const u32x4_t *>(Bp + brw * ldb + col)
+                                             : u32x4_t{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4_t *>(sB[0] + lds_off(c >> 3, c & 7)) = v;
     }
     __syncthreads();
-    mma_step<C>(sA[0], sB[0], wm, wn, lane, acc);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4_t a[C::WM], b[C::WN];
+      read_a<C>(sA[0], wm, lane, kk, a);
+      read_b_rows<C>(sB[0], wn, lane, kk, b);
+      mma_rows<C>(0, C::WM, a, b, acc);
+    }
     __syncthreads();
   }
   store_out<C>(Y, N, m0, T, n0, N, wm, wn, lane, acc);
@@ -249,14 +387,12 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
 // --------------------------------------------------------------- backward
 // dX[T, K] = dY[T, N] . W'[N, K] + dUp[T, rp] . A[r, K]   (rows of A past r read as 0)
 // The reduction index is the weight row n.  The B operand is decoded exactly as
-// in the forward (16 bytes of codes = 32 consecutive columns of one weight
-// row, one block constant) and stored in its natural [n][k_out] layout, rows
-// padded by 32 bytes so that four consecutive rows start 32 bytes apart in
-// the bank space.  The MFMA operand, which needs 8 consecutive n for one
-// k_out, is read with ds_read_b64_tr_b16: in each 16-lane group, lane i gets
-// element (i & 3) of the 8 bytes addressed by lane 4m + (i >> 2), m = 0..3, so
-// lane a points at row base + (a >> 2), columns 4 (a & 3) .. +3, and two such
-// reads (rows +0..3 and +4..7) give the 8 reduction values of the operand.
+// in the forward (code words of consecutive columns of one weight row, one
+// block constant) and stored in its natural [n][k_out] layout, rows padded so
+// that the four rows one transposing read touches cover all 64 banks; the MFMA
+// operand, which needs 8 consecutive n for one k_out, is read transposed.
+// Weight rows past N decode to zero, so the clamped activation columns they
+// meet contribute nothing.
 template <class C>
 __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict__ dY, int64_t T, int64_t N,
                                                        const uint8_t *__restrict__ codes,
@@ -265,8 +401,7 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
                                                        const bf16_t *__restrict__ dUp, const bf16_t *__restrict__ A,
                                                        int64_t r, int64_t rp, bf16_t *__restrict__ dX, Levels lv,
                                                        int xb_m, int xb_n) {
-  constexpr int LDB = C::BN + 16;  // padded row length (elements) of the [64][BN] B tile
-  constexpr int PIECES = C::BN / 32;  // 32-column pieces per B-tile row
+  constexpr int LDB = C::BN + 32;  // row length (elements) of the [64][BN] B tile: 16 banks mod 64 per row
   __shared__ __attribute__((aligned(16))) bf16_t sA[2][C::BM * BK];
   __shared__ __attribute__((aligned(16))) bf16_t sB[2][BK * LDB];
   __shared__ float s_lv[16];
@@ -277,112 +412,88 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
   levels_to_lds(lv, s_lv, tid);
 
   const int nk = (int)((N + BK - 1) / BK);
-  u32x4_t ra[C::A_CH];
-  u32x4_t rc[C::C_CH];
-  RawScale rcq[C::C_CH];
-
-  auto load_main = [&](int s) {
-    const int64_t k0 = (int64_t)s * BK;
-    load_a<C>(dY, N, m0, T, k0, N, tid, ra);
-#pragma unroll
-    for (int i = 0; i < C::C_CH; ++i) {
-      const int c = tid + C::NT * i;
-      const int64_t n = k0 + c / PIECES, kc = n0 + (c % PIECES) * 32;
-      if (n < N && kc < K && (!C::C_SPARSE || c < 2 * C::BN)) {
-        rc[i] = *reinterpret_cast<const u32x4_t *>(codes + n * (K / 2) + kc / 2);
-        rcq[i] = load_scale(absmax_q, step, n * (K / BK) + kc / BK);
-      } else {
-        rc[i] = u32x4_t{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
-        rcq[i] = RawScale{0u, 0.f};
-      }
-    }
+  ALoads<C> al;
+  al.init(dY, N, m0, T, tid);
+  // this thread decodes columns piece*E .. piece*E+E-1 of tile row bn (weight row k0 + bn)
+  constexpr int PIECES = C::BN / C::E;
+  const bool decoder = tid < C::DEC;  // wave-uniform
+  const int bn = decoder ? tid / PIECES : 0, piece = tid % PIECES;
+  const int64_t kc = (n0 + piece * C::E + C::E <= K) ? n0 + piece * C::E : K - C::E;  // columns past K: never stored
+  uint32_t rc[2][C::NWD];
+  RawScale rs[2];
+  auto load_words_of = [&](int s, uint32_t(&w)[C::NWD], RawScale &sc) {
+    const int64_t n = (int64_t)s * BK + bn;
+    const int64_t nn = n < N ? n : N - 1;
+    load_words<C::NWD>(codes + nn * (K / 2) + kc / 2, w);
+    sc = load_scale(absmax_q, step, nn * (K / BK) + kc / BK);
+    if (n >= N) sc.d = 0.f;  // weight rows past N decode to (signed) zero
   };
-  auto store_main = [&](int buf) {
-    store_a<C>(sA[buf], tid, ra);
-#pragma unroll
-    for (int i = 0; i < C::C_CH; ++i) {
-      const int c = tid + C::NT * i;
-      if (C::C_SPARSE && c >= 2 * C::BN) break;
-      bf16_t *dst = sB[buf] + (c / PIECES) * LDB + (c % PIECES) * 32;
-      const float cq = scale_of(rcq[i]);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        float v[8];
-        decode8(rc[i][w], cq, s_lv, v);
-        u32x4_t o;
-        o.x = pack_bf16x2(v[0], v[1]);
-        o.y = pack_bf16x2(v[2], v[3]);
-        o.z = pack_bf16x2(v[4], v[5]);
-        o.w = pack_bf16x2(v[6], v[7]);
-        *reinterpret_cast<u32x4_t *>(dst + w * 8) = o;
-      }
-    }
-  };
-  // this wave's B operands for one 16-deep substep, via two transposing reads each
-  const int grp = lane >> 4, ai = lane & 15;
-  auto mma = [&](const bf16_t *sa, const bf16_t *sb, f32x16_t (&acc)[C::WM][C::WN]) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int chunk = kk * 2 + (lane >> 5);
-      u32x4_t a[C::WM], b[C::WN];
-#pragma unroll
-      for (int i = 0; i < C::WM; ++i) {
-        const int ra_ = (wm * C::WM + i) * 32 + (lane & 31);
-        a[i] = *reinterpret_cast<const u32x4_t *>(sa + lds_off(ra_, chunk));
-      }
-#pragma unroll
-      for (int j = 0; j < C::WN; ++j) {
-        const int row = kk * 16 + 8 * (grp >> 1) + (ai >> 2);
-        const int col = (wn * C::WN + j) * 32 + 16 * (grp & 1) + 4 * (ai & 3);
-        typedef short s4_t __attribute__((ext_vector_type(4)));
-        typedef __attribute__((address_space(3))) s4_t lds_s4;
-        const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(sb + row * LDB + col));
-        const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(sb + (row + 4) * LDB + col));
-        const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
-        b[j] = u32x4_t{l2.x, l2.y, h2.x, h2.y};
-      }
-#pragma unroll
-      for (int i = 0; i < C::WM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::WN; ++j) acc[i][j] = mfma_32x32x16(a[i], b[j], acc[i][j]);
-    }
-  };
+  auto read_b = [&](const bf16_t *sb, int kk, u32x4_t(&b)[C::WN]) { read_b_tr<C, LDB>(sb, wn, lane, kk, b); };
 
   f32x16_t acc[C::WM][C::WN];
   zero_acc<C>(acc);
 
-  load_main(0);
-  __syncthreads();
-  store_main(0);
-  __syncthreads();
-  for (int s = 0; s < nk; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nk) load_main(s + 1);
-    mma(sA[buf], sB[buf], acc);
-    if (s + 1 < nk) store_main(buf ^ 1);
-    __syncthreads();
+  {
+    u32x4_t ra[C::A_LD];
+    al.load(0, N, ra);
+    al.store(ra, sA[0]);
   }
+  load_words_of(0, rc[0], rs[0]);
+  load_words_of(nk > 1 ? 1 : 0, rc[1], rs[1]);
+  __syncthreads();
+  {
+    const float cq = scale_of(rs[0]);
+    if (decoder)
+      for (int w = 0; w < C::NWD; ++w) {
+        float v[8];
+        lookup8(rc[0][w], s_lv, v);
+        *reinterpret_cast<u32x4_t *>(sB[0] + bn * LDB + piece * C::E + 8 * w) = scale_pack8(v, cq);
+      }
+  }
+  __syncthreads();
+
+  auto step_p = [&](auto pc, int s) {
+    constexpr int P = decltype(pc)::value;
+    const int sa = (s + 1 < nk) ? s + 1 : nk - 1, sc = (s + 2 < nk) ? s + 2 : nk - 1;
+    auto load_next = [&](u32x4_t(&ra)[C::A_LD]) {
+      al.load((int64_t)sa * BK, N, ra);
+      fence_sched();  // activation loads first: waiting for them leaves the words in flight
+      load_words_of(sc, rc[P], rs[P]);
+    };
+    auto store_word = [&](int w, const u32x4_t &o) {
+      *reinterpret_cast<u32x4_t *>(sB[P ^ 1] + bn * LDB + piece * C::E + 8 * w) = o;
+    };
+    auto store_a = [&](const u32x4_t(&ra)[C::A_LD]) { al.store(ra, sA[P ^ 1]); };
+    pipelined_step<C>(sA[P], sB[P], wm, wn, lane, rc[P ^ 1], rs[P ^ 1], s_lv, acc, read_b,
+                                           load_next, store_word, store_a, decoder);
+  };
+  int s = 0;
+  for (; s + 1 < nk; s += 2) {
+    step_p(std::integral_constant<int, 0>(), s);
+    step_p(std::integral_constant<int, 1>(), s + 1);
+  }
+  if (s < nk) step_p(std::integral_constant<int, 0>(), s);
+
   // LoRA term: dUp [T, rp] . A [r, K], reduction over the rank (rows j of A)
   for (int64_t k0 = 0; k0 < rp; k0 += BK) {
-    {
-      constexpr int LCH = BK * C::BN / 8 / C::NT;  // 16-byte chunks of A per thread
-      u32x4_t rv[C::A_CH], rl[LCH];
-      load_a<C>(dUp, rp, m0, T, k0, rp, tid, rv);
+    copy_a_tile<C>(dUp, rp, m0, T, k0, rp, tid, sA[0]);
+    constexpr int LCH = BK * C::BN / 8 / C::NT;  // 16-byte chunks of A per thread
 #pragma unroll
-      for (int i = 0; i < LCH; ++i) {
-        const int c = tid + C::NT * i;
-        const int64_t j = k0 + c / (C::BN / 8), kc = n0 + (c % (C::BN / 8)) * 8;
-        rl[i] = (j < r && kc < K) ? *reinterpret_cast<const u32x4_t *>(A + j * K + kc) : u32x4_t{0u, 0u, 0u, 0u};
-      }
-      store_a<C>(sA[0], tid, rv);
-#pragma unroll
-      for (int i = 0; i < LCH; ++i) {
-        const int c = tid + C::NT * i;
-        *reinterpret_cast<u32x4_t *>(sB[0] + (c / (C::BN / 8)) * LDB + (c % (C::BN / 8)) * 8) = rl[i];
-      }
+    for (int i = 0; i < LCH; ++i) {
+      const int c = tid + C::NT * i;
+      const int64_t j = k0 + c / (C::BN / 8), kcol = n0 + (c % (C::BN / 8)) * 8;
+      const u32x4_t v =
+          (j < r && kcol < K) ? *reinterpret_cast<const u32x4_t *>(A + j * K + kcol) : u32x4_t{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4_t *>(sB[0] + (c / (C::BN / 8)) * LDB + (c % (C::BN / 8)) * 8) = v;
     }
     __syncthreads();
-    mma(sA[0], sB[0], acc);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4_t a[C::WM], b[C::WN];
+      read_a<C>(sA[0], wm, lane, kk, a);
+      read_b_tr<C, LDB>(sB[0], wn, lane, kk, b);
+      mma_rows<C>(0, C::WM, a, b, acc);
+    }
     __syncthreads();
   }
   store_out<C>(dX, K, m0, T, n0, K, wm, wn, lane, acc);
@@ -448,12 +559,12 @@ hipError_t dx_with(const bf16_t *dY, int64_t T, int64_t N, const uint8_t *codes,
 // Tile choice for an M x N output.  Measured on MI355X (both GEMMs, seven
 // workload shapes): the largest 8-wave tile that still yields at least one
 // workgroup per CU (256 tiles) is fastest -- 256x256, else 256x128; below that
-// the 128x128 tile, two workgroups per CU, wins.
+// the 8-wave 128x128 tile (two workgroups per CU) wins.
 int nf4_gemm_pick_tile(int64_t M, int64_t N) {
   auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   if (tiles(256, 256) >= 256) return NF4_TILE_256x256_W8;
   if (tiles(256, 128) >= 256) return NF4_TILE_256x128_W8;
-  return NF4_TILE_128x128;
+  return NF4_TILE_128x128_W8;
 }
 
 hipError_t launch_nf4_gemm_fwd(int tile, const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes,
