@@ -52,6 +52,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 256 MiB (scales rocprofv3 FETCH_SIZE/WRITE_SIZE)")
+    ap.add_argument("--traffic-from", metavar="DIR",
+                    help="write profiles/traffic_<kernel>_<workload>.json from rocprofv3 --pmc outputs under DIR "
+                         "(subdirectories fetch/, write/ of this bench command and calib_fetch/, calib_write/ of "
+                         "--calibrate-copy) and exit")
+    ap.add_argument("--traffic-kernel", default=None, help="kernel for --traffic-from (default: the timed GEMMs)")
+    ap.add_argument("--traffic-command", default="", help="the profiled command, recorded in the JSON")
     return ap.parse_args()
 
 
@@ -59,24 +65,92 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_digest() -> str:
+KERNEL_SOURCES = {"nf4_gemm_fwd": "nf4_gemm.hip", "nf4_gemm_dx": "nf4_gemm.hip", "nf4_gemv": "nf4_gemv.hip"}
+
+
+def source_digest(kernel: str) -> str:
+    """Digest of the sources a kernel is built from (a counter summary is valid only for these)."""
     h = hashlib.sha256()
-    for name in ("nf4_gemm.hip", "device.h"):
+    for name in (KERNEL_SOURCES[kernel], "device.h"):
         with open(os.path.join(ROOT, "bit_quantized_lora_02_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
+def traffic_path(kernel: str, workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+
+
 def traffic_from_profiles(kernel: str, workload: str):
     """HBM bytes per launch from a committed counter summary, if it matches the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    path = traffic_path(kernel, workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("source_digest") != source_digest():
+    if d.get("source_digest") != source_digest(kernel):
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+def _pmc_rows(directory: str):
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no rocprofv3 counter_collection.csv under {directory}")
+    return rows
+
+
+def _per_dispatch_kib(rows, counter: str, match) -> list:
+    """Counter value (KiB) of every dispatch whose kernel name satisfies `match`."""
+    per = {}
+    for r in rows:
+        if r["Counter_Name"] != counter or not match(r["Kernel_Name"]):
+            continue
+        key = (r.get("Dispatch_Id") or r.get("Correlation_Id") or len(per))
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    return list(per.values())
+
+
+def write_traffic(args, workload: str, kernels):
+    """HBM traffic per launch from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by what the
+    same counter reads for a plain device copy of known size."""
+    d = args.traffic_from
+    calib_bytes = 256 << 20
+    cf = _per_dispatch_kib(_pmc_rows(os.path.join(d, "calib_fetch")), "FETCH_SIZE", lambda n: "opy" in n)
+    cw = _per_dispatch_kib(_pmc_rows(os.path.join(d, "calib_write")), "WRITE_SIZE", lambda n: "opy" in n)
+    cf = [v for v in cf if v > calib_bytes / 1024 / 8]
+    cw = [v for v in cw if v > calib_bytes / 1024 / 8]
+    if not cf or not cw:
+        raise SystemExit("calibration copy dispatches not found")
+    f_fac = calib_bytes / (sum(cf) / len(cf) * 1024)
+    w_fac = calib_bytes / (sum(cw) / len(cw) * 1024)
+    fetch_rows = _pmc_rows(os.path.join(d, "fetch"))
+    write_rows = _pmc_rows(os.path.join(d, "write"))
+    for k in kernels:
+        symbol = "k_" + k
+        fk = _per_dispatch_kib(fetch_rows, "FETCH_SIZE", lambda n: symbol + "<" in n or symbol + "(" in n)
+        wk = _per_dispatch_kib(write_rows, "WRITE_SIZE", lambda n: symbol + "<" in n or symbol + "(" in n)
+        if not fk or not wk:
+            log(f"no dispatches of {symbol} in the counter runs")
+            continue
+        fetch_b = sum(fk) / len(fk) * 1024 * f_fac
+        write_b = sum(wk) / len(wk) * 1024 * w_fac
+        out = {"kernel": k, "workload": workload, "source_digest": source_digest(k),
+               "hbm_bytes_per_launch": fetch_b + write_b, "fetch_bytes_per_launch": fetch_b,
+               "write_bytes_per_launch": write_b, "fetch_kib_per_dispatch": sum(fk) / len(fk),
+               "write_kib_per_dispatch": sum(wk) / len(wk), "dispatches": [len(fk), len(wk)],
+               "fetch_scale": f_fac, "write_scale": w_fac,
+               "calibration": "torch device copy of 256 MiB (python bench.py --calibrate-copy)",
+               "command": args.traffic_command}
+        with open(traffic_path(k, workload), "w") as f:
+            json.dump(out, f, indent=1)
+            f.write("\n")
+        print(json.dumps(out))
 
 
 def linears_for(args):
@@ -137,6 +211,13 @@ def main():
         print(f"bench.py measures one GPU only: this NF4 + LoRA linear runs on a single MI355X "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.traffic_from:  # post-processing of counter runs: no GPU needed
+        lins, T, r, alpha, outliers, train = linears_for(args)
+        wl = args.config if args.config != "small_token" else f"small_token_{lins[0][1]}x8192_T{T}"
+        ks = [args.traffic_kernel] if args.traffic_kernel else (
+            ["nf4_gemm_fwd", "nf4_gemm_dx"] if train else ["nf4_gemm_fwd", "nf4_gemv"])
+        write_traffic(args, wl, ks)
+        return
 
     import numpy as np
     import torch

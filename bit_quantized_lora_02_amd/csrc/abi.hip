@@ -22,6 +22,11 @@
 
 using namespace qlora;
 
+LaunchEvents &qlora::launch_events() {
+  static thread_local LaunchEvents ev;
+  return ev;
+}
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -129,11 +134,11 @@ bool is_timed(const char *kname) {
   return false;
 }
 
+// A timed launch gets a pair of events stamped by its own dispatch packet.
 struct Timed {
   hipEvent_t a = nullptr, b = nullptr;
   std::string name;
-  hipStream_t s;
-  Timed(const char *kname, hipStream_t st) : s(st) {
+  Timed(const char *kname) {
     std::lock_guard<std::mutex> lk(g_tmu);
     if (!is_timed(kname)) return;
     if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
@@ -142,11 +147,11 @@ struct Timed {
       return;
     }
     name = kname;
-    (void)hipEventRecord(a, s);
+    launch_events() = LaunchEvents{a, b};
   }
   ~Timed() {
     if (!a) return;
-    (void)hipEventRecord(b, s);
+    launch_events() = LaunchEvents{};
     std::lock_guard<std::mutex> lk(g_tmu);
     g_events[name].push_back({a, b});
   }
@@ -162,7 +167,7 @@ int launched(hipError_t e, const char *what, hipStream_t s) {
   do {                                                 \
     hipError_t e_;                                     \
     {                                                  \
-      Timed t_(name, s);                               \
+      Timed t_(name);                                  \
       e_ = (call);                                     \
     }                                                  \
     int rc_ = launched(e_, name, s);                   \

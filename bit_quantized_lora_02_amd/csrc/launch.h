@@ -1,9 +1,24 @@
 // launch.h -- host-side launchers of the gfx950 kernels (internal to the library).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace qlora {
+
+// Start/stop events of the launch being timed (set by the C ABI around a timed
+// kernel, null otherwise).  hipExtLaunchKernel writes them as part of the
+// kernel's own dispatch, so their difference is the kernel's execution time.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents &launch_events();  // per host thread
+
+template <typename F, typename... Args>
+inline void launch(F kernel, dim3 grid, dim3 block, uint32_t shm, hipStream_t s, Args... args) {
+  const LaunchEvents &ev = launch_events();
+  hipExtLaunchKernelGGL(kernel, grid, block, shm, s, ev.start, ev.stop, 0u, args...);
+}
 
 typedef uint16_t bf16_t;
 struct Levels;

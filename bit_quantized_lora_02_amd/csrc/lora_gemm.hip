@@ -224,7 +224,7 @@ hipError_t launch_finalize(const float *part, int nsplit, int64_t M, int64_t N, 
   const int64_t ncol = (n1 > n2) ? n1 : n2;
   const int64_t total = M * ncol;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_finalize, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, nsplit, M, N, out1, ld1,
+  launch(k_finalize, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, nsplit, M, N, out1, ld1,
                      n1, scale1, trans1 ? 1 : 0, out2, ld2, n2, nvalid2, scale2);
   return hipGetLastError();
 }
@@ -251,10 +251,10 @@ template <bool PT, bool QT>
 static hipError_t skinny_dispatch(int rn, dim3 grid, hipStream_t s, const bf16_t *P, int64_t ldp, int64_t M,
                             const bf16_t *Q, int64_t ldq, int64_t Rv, int64_t Kred, int64_t kchunk, float *C) {
   switch (rn) {
-    case 16: hipLaunchKernelGGL((k_skinny<PT, QT, 16>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C); break;
-    case 32: hipLaunchKernelGGL((k_skinny<PT, QT, 32>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C); break;
-    case 64: hipLaunchKernelGGL((k_skinny<PT, QT, 64>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C); break;
-    default: hipLaunchKernelGGL((k_skinny<PT, QT, 128>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C); break;
+    case 16: launch((k_skinny<PT, QT, 16>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C); break;
+    case 32: launch((k_skinny<PT, QT, 32>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C); break;
+    case 64: launch((k_skinny<PT, QT, 64>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C); break;
+    default: launch((k_skinny<PT, QT, 128>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C); break;
   }
   return hipGetLastError();
 }
@@ -273,7 +273,7 @@ hipError_t launch_pad_copy(const bf16_t *in, int64_t ldi, int64_t ncols, int64_t
                            hipStream_t s) {
   const int64_t total = M * ldo;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_pad_copy, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, in, ldi, ncols, M, out, ldo);
+  launch(k_pad_copy, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, in, ldi, ncols, M, out, ldo);
   return hipGetLastError();
 }
 

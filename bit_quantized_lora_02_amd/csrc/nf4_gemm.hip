@@ -538,7 +538,7 @@ hipError_t fwd_with(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes,
   const int64_t tm = (T + C::BM - 1) / C::BM, tn = (N + C::BN - 1) / C::BN;
   int xb_m, xb_n;
   xcd_blocking(tm, tn, 2.0 * T * K, 0.516 * N * K, &xb_m, &xb_n);
-  hipLaunchKernelGGL(k_nf4_gemm_fwd<C>, dim3((unsigned)(tm * tn)), dim3(C::NT), 0, s, X, T, K, codes, absmax_q, step,
+  launch(k_nf4_gemm_fwd<C>, dim3((unsigned)(tm * tn)), dim3(C::NT), 0, s, X, T, K, codes, absmax_q, step,
                      N, V, Bp, ldb, r, rp, Y, lv, xb_m, xb_n);
   return hipGetLastError();
 }
@@ -550,7 +550,7 @@ hipError_t dx_with(const bf16_t *dY, int64_t T, int64_t N, const uint8_t *codes,
   const int64_t tm = (T + C::BM - 1) / C::BM, tn = (K + C::BN - 1) / C::BN;
   int xb_m, xb_n;
   xcd_blocking(tm, tn, 2.0 * T * N, 0.516 * N * K, &xb_m, &xb_n);
-  hipLaunchKernelGGL(k_nf4_gemm_dx<C>, dim3((unsigned)(tm * tn)), dim3(C::NT), 0, s, dY, T, N, codes, absmax_q, step,
+  launch(k_nf4_gemm_dx<C>, dim3((unsigned)(tm * tn)), dim3(C::NT), 0, s, dY, T, N, codes, absmax_q, step,
                      K, dUp, A, r, rp, dX, lv, xb_m, xb_n);
   return hipGetLastError();
 }

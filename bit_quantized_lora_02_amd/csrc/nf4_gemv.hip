@@ -258,7 +258,7 @@ hipError_t launch_lora_u_small(const bf16_t *X, int64_t T, int64_t K, const bf16
                                bf16_t *U_out, bf16_t *V, int64_t rp, hipStream_t st) {
   if (T == 0) return hipSuccess;
   dim3 grid((unsigned)((T + 15) / 16), (unsigned)((rp + 15) / 16));
-  hipLaunchKernelGGL(k_lora_u_small, grid, dim3(256), 0, st, X, T, K, A, r, s, U_out, V, rp);
+  launch(k_lora_u_small, grid, dim3(256), 0, st, X, T, K, A, r, s, U_out, V, rp);
   return hipGetLastError();
 }
 
@@ -268,13 +268,13 @@ hipError_t launch_nf4_gemv(const bf16_t *X, int64_t T, int64_t K, const uint8_t 
   if (T == 0) return hipSuccess;
   dim3 grid((unsigned)((N + 63) / 64), (unsigned)nsplit);
   if (T <= 16)
-    hipLaunchKernelGGL(k_nf4_gemv<1>, grid, dim3(256), 0, s, X, T, K, codes, absmax_q, step, N, kchunk, V, rp, B, r,
+    launch(k_nf4_gemv<1>, grid, dim3(256), 0, s, X, T, K, codes, absmax_q, step, N, kchunk, V, rp, B, r,
                        part, Y, lv);
   else if (T <= 32)
-    hipLaunchKernelGGL(k_nf4_gemv<2>, grid, dim3(256), 0, s, X, T, K, codes, absmax_q, step, N, kchunk, V, rp, B, r,
+    launch(k_nf4_gemv<2>, grid, dim3(256), 0, s, X, T, K, codes, absmax_q, step, N, kchunk, V, rp, B, r,
                        part, Y, lv);
   else
-    hipLaunchKernelGGL(k_nf4_gemv<4>, grid, dim3(256), 0, s, X, T, K, codes, absmax_q, step, N, kchunk, V, rp, B, r,
+    launch(k_nf4_gemv<4>, grid, dim3(256), 0, s, X, T, K, codes, absmax_q, step, N, kchunk, V, rp, B, r,
                        part, Y, lv);
   return hipGetLastError();
 }
@@ -282,7 +282,7 @@ hipError_t launch_nf4_gemv(const bf16_t *X, int64_t T, int64_t K, const uint8_t 
 hipError_t launch_gemv_reduce(const float *part, int nsplit, int64_t T, int64_t N, bf16_t *Y, hipStream_t s) {
   const int64_t total = T * N;
   if (total == 0 || nsplit <= 1) return hipSuccess;
-  hipLaunchKernelGGL(k_gemv_reduce, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, nsplit, total, Y);
+  launch(k_gemv_reduce, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, nsplit, total, Y);
   return hipGetLastError();
 }
 

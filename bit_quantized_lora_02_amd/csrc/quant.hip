@@ -112,7 +112,7 @@ hipError_t launch_quantize_nf4(const float *W, int64_t n_out, int64_t n_in, uint
   const int64_t nblk = n_out * n_in / 64;
   const int64_t ngrp = (nblk + 255) / 256;
   if (ngrp == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_quantize_nf4, dim3((unsigned)ngrp), dim3(256), 0, s, W, nblk, codes, absmax_q, absmax_step, thr);
+  launch(k_quantize_nf4, dim3((unsigned)ngrp), dim3(256), 0, s, W, nblk, codes, absmax_q, absmax_step, thr);
   return hipGetLastError();
 }
 
@@ -121,7 +121,7 @@ hipError_t launch_dequant(const uint8_t *codes, const uint8_t *absmax_q, const f
   const int64_t n8 = n_out * n_in / 8;
   if (n8 == 0) return hipSuccess;
   const int64_t grid = (n8 + 255) / 256;
-  hipLaunchKernelGGL(k_dequant, dim3((unsigned)grid), dim3(256), 0, s, reinterpret_cast<const uint32_t *>(codes),
+  launch(k_dequant, dim3((unsigned)grid), dim3(256), 0, s, reinterpret_cast<const uint32_t *>(codes),
                      absmax_q, absmax_step, n8, reinterpret_cast<u32x4_t *>(out), lv);
   return hipGetLastError();
 }
