@@ -216,9 +216,9 @@ struct Plan {
   int64_t rv = 0;  // r rounded up to 8: rank columns read from padded copies
   size_t off_bp = 0, off_v = 0, off_du = 0, off_part = 0, total = 0;
   Split su, sdu, sdb, sda;
-  bool gemv = false;  // forward through the small-token kernel
-  int gemv_split = 0;
-  int64_t gemv_kchunk = 0;
+  bool gemv = false;  // forward through the small-token kernels
+  int gemv_rg = 0, gemv_w = 0, gemv_split = 0, gemv_main = 0;
+  size_t off_upart = 0;
 };
 
 bool use_gemv(int64_t T, int64_t K) { return T >= 1 && T <= kGemvMaxT && K % 128 == 0; }
@@ -239,8 +239,10 @@ Plan make_plan(int op, int64_t T, int64_t N, int64_t K, int32_t r) {
     part = (size_t)p.su.n * T * p.rn * 4;
     if (use_gemv(T, K)) {
       p.gemv = true;
-      nf4_gemv_plan(T, N, K, &p.gemv_split, &p.gemv_kchunk);
-      part = (size_t)p.gemv_split * T * N * 4;
+      nf4_gemv_plan(T, N, K, &p.gemv_rg, &p.gemv_w, &p.gemv_split, &p.gemv_main);
+      part = up((size_t)p.gemv_split * T * N * 4, kAlign);
+      p.off_upart = part;  // relative to off_part
+      part += (size_t)4 * p.gemv_split * T * r * 4;
     }
   } else {
     p.off_du = off;
@@ -369,10 +371,10 @@ int qlora_linear_fwd(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const q
   const float sc = alpha / (float)r;
   const Levels &lv = codebook().lv;
   if (p.gemv) {  // few tokens: bound by the weight stream
-    LAUNCH("lora_u_small", launch_lora_u_small(X, T, K, A, r, sc, U_out, V, p.rp, s));
-    LAUNCH("nf4_gemv", launch_nf4_gemv(X, T, K, q->codes, q->absmax_q, q->absmax_step, N, p.gemv_split, p.gemv_kchunk,
-                                       V, p.rp, B, r, part, Y, lv, s));
-    LAUNCH("gemv_reduce", launch_gemv_reduce(part, p.gemv_split, T, N, Y, s));
+    float *upart = (float *)(w + p.off_part + p.off_upart);
+    LAUNCH("nf4_gemv", launch_nf4_gemv(X, T, K, q->codes, q->absmax_q, q->absmax_step, N, p.gemv_rg, p.gemv_w,
+                                       p.gemv_split, p.gemv_main, A, r, part, upart, lv, s));
+    LAUNCH("gemv_finish", launch_gemv_finish(part, upart, p.gemv_split, T, N, B, r, sc, Y, U_out, s));
     return QLORA_OK;
   }
   LAUNCH("lora_u", launch_skinny(false, false, p.rn, X, K, T, A, K, r, K, p.su.kchunk, p.su.n, part, s));

@@ -47,18 +47,17 @@ hipError_t launch_nf4_gemm_dx(int tile, const bf16_t *dY, int64_t T, int64_t N, 
                               const uint8_t *absmax_q, const float *step, int64_t K, const bf16_t *dUp, const bf16_t *A,
                               int64_t r, int64_t rp, bf16_t *dX, const Levels &lv, hipStream_t s);
 
-// Small-token forward (T <= 64, n_in % 128 == 0): U and V for few tokens, then
-// the split-K GEMV (binary32 partials, LoRA term in the first split) followed
-// by a fixed-order reduce of the partials into Y (with one split the GEMV
-// stores Y itself and the reduce does nothing).
+// Small-token forward (T <= 64, n_in % 128 == 0): the split-K GEMV over the
+// weight (binary32 partials per K range, plus the partials of U = X A^T from
+// one extra workgroup per range), then one finishing launch that adds the
+// partials in range order, forms V = bf16(s U), adds V B^T and rounds Y.
 constexpr int64_t kGemvMaxT = 64;
-void nf4_gemv_plan(int64_t T, int64_t N, int64_t K, int *nsplit, int64_t *kchunk);
-hipError_t launch_lora_u_small(const bf16_t *X, int64_t T, int64_t K, const bf16_t *A, int64_t r, float s,
-                               bf16_t *U_out, bf16_t *V, int64_t rp, hipStream_t st);
+void nf4_gemv_plan(int64_t T, int64_t N, int64_t K, int *rg, int *w, int *nsplit, int *gmain);
 hipError_t launch_nf4_gemv(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
-                           const float *step, int64_t N, int nsplit, int64_t kchunk, const bf16_t *V, int64_t rp,
-                           const bf16_t *B, int64_t r, float *part, bf16_t *Y, const Levels &lv, hipStream_t s);
-hipError_t launch_gemv_reduce(const float *part, int nsplit, int64_t T, int64_t N, bf16_t *Y, hipStream_t s);
+                           const float *step, int64_t N, int rg, int w, int nsplit, int gmain, const bf16_t *A,
+                           int64_t r, float *part, float *upart, const Levels &lv, hipStream_t s);
+hipError_t launch_gemv_finish(const float *part, const float *upart, int nsplit, int64_t T, int64_t N,
+                              const bf16_t *B, int64_t r, float s, bf16_t *Y, bf16_t *U_out, hipStream_t st);
 
 // Skinny GEMM of the LoRA branch: C[split][m][j] (j < rn) over one reduction
 // chunk; pt / qt select the storage of the long operand P and the rank-wide

@@ -5,29 +5,32 @@
 // plain LoRA when fine-tuning Llama?", katajob.com, "NF4: 4-bit NormalFloat":
 // blocks expanded to bf16 inside the matmul; "QLoRA: fine-tuning a large model
 // on one GPU", learn.pranaymahendrakar.com, "LoRA, stated once": the adapter
-// adds (alpha/r) B A x), organised for bandwidth in three launches:
+// adds (alpha/r) B A x), organised for bandwidth in two launches:
 //
-// 1. k_lora_u_small: U = X A^T for all T rows (one workgroup per 16 tokens x
-//    16 ranks, the four waves split n_in and reduce through LDS); writes U and
-//    V = bf16(s U).
-// 2. k_nf4_gemv: a workgroup (4 waves) owns 64 weight rows and one K range;
-//    each wave owns 16 rows and issues v_mfma_f32_16x16x32_bf16 with the tokens
-//    as the M dimension.  Each lane streams 16 bytes of codes (32 consecutive
-//    weights of one row, one block constant) per 128-deep step and decodes them
+// 1. k_nf4_gemv: the reduction over n_in is split into K ranges.  A workgroup
+//    (4 waves) owns 64 RG weight rows and one K range; each wave owns RG
+//    groups of 16 rows and issues v_mfma_f32_16x16x32_bf16 with the tokens as
+//    the M dimension, so one load of the activations serves RG row groups.
+//    Each lane streams 16 bytes of codes per row group and 128-deep step (32
+//    consecutive weights of one row, one block constant) and decodes them
 //    straight into its four B operands, so the weight never touches LDS.  The
-//    decode looks up both levels of a code byte at once in a 256-entry LDS table
-//    of level pairs (two copies, one per half-wave, to spread bank traffic):
-//    per byte one shift, one and-or (table offset), one 8-byte LDS read, two
-//    binary32 multiplies by the block constant and one bf16 pack.
-//    Codes are prefetched three steps ahead.  Each K range writes binary32
-//    partial sums; the first also carries the LoRA term V B^T.  (A single
-//    launch with a last-arriving-workgroup reduction needs device-scope
-//    fences, which on this chip write back and invalidate the L2 in every
-//    workgroup and cost far more than a third launch.)
-// 3. k_gemv_reduce: Y = bf16(sum of the partials in split order), so the
+//    decode looks up both levels of a code byte at once in a 256-entry LDS
+//    table of level pairs (two copies, one per half-wave): per byte one shift,
+//    one and-or (table offset), one 8-byte LDS read, two binary32 multiplies
+//    by the block constant and one bf16 pack.  Codes are prefetched two steps
+//    ahead.  Each K range writes binary32 partial sums.  One extra workgroup
+//    per K range computes the partial sums of U = X A^T over that range (one
+//    per quarter range and wave).
+// 2. k_gemv_finish: per token, U = the partials of U added in K-range order,
+//    V = bf16(s U) (and U_out = bf16(U)); then
+//    Y = bf16(sum of the weight partials in K-range order + V B^T), so the
 //    result does not depend on the order in which workgroups finish.
+//    (A single launch with a last-arriving-workgroup reduction needs
+//    device-scope fences, which on this chip write back and invalidate the L2
+//    in every workgroup and cost far more than a second launch.)
 #include "device.h"
 #include "launch.h"
+#include "qlora.h"
 
 namespace qlora {
 
@@ -66,223 +69,277 @@ __device__ __forceinline__ u32x4_t decode8_pairs(uint32_t w, float cq, const cha
   }
   return o;
 }
-}  // namespace
 
-// ------------------------------------------------------------- U for few tokens
-// U[t, j] = sum_k X[t, k] A[j, k]; U_out (nullable, [T, r]) and V = bf16(s U) ([T, rp], zero past r).
-// Workgroup (bx, by) covers tokens 16 bx .. +15 and ranks 16 by .. +15; wave w
-// takes the k range [w K/4, (w+1) K/4) in 32-deep MFMA steps.
-__global__ __launch_bounds__(256) void k_lora_u_small(const bf16_t *__restrict__ X, int64_t T, int64_t K,
-                                                      const bf16_t *__restrict__ A, int64_t r, float s,
-                                                      bf16_t *__restrict__ U_out, bf16_t *__restrict__ V, int64_t rp) {
-  __shared__ f32x4_t red[4][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t0 = (int64_t)blockIdx.x * 16, j0 = (int64_t)blockIdx.y * 16;
-  int64_t t = t0 + (lane & 15);
-  t = t < T ? t : T - 1;  // rows past T feed outputs that are not stored
-  const int64_t j = j0 + (lane & 15);
-  const bool jok = j < r;
-  const int64_t kq = K / 4, kb = wave * kq;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t k = kb + 8 * (lane >> 4); k < kb + kq; k += 32) {
-    const u32x4_t a = *reinterpret_cast<const u32x4_t *>(X + t * K + k);
-    const u32x4_t b = jok ? *reinterpret_cast<const u32x4_t *>(A + j * K + k) : u32x4_t{0u, 0u, 0u, 0u};
-    acc = mfma_16x16x32(a, b, acc);
-  }
-  red[wave][lane] = acc;
-  __syncthreads();
-  if (wave == 0) {
-    const f32x4_t sum = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
-    // element i of lane l: token 16 bx + 4 (l >> 4) + i, rank 16 by + (l & 15)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t tt = t0 + 4 * (lane >> 4) + i;
-      if (tt >= T) continue;
-      if (jok) {
-        if (U_out) U_out[tt * r + j] = f32_to_bf16(sum[i]);
-        V[tt * rp + j] = f32_to_bf16(s * sum[i]);
-      } else if (j < rp) {
-        V[tt * rp + j] = (bf16_t)0;
-      }
-    }
-  }
-}
-
-// ------------------------------------------------------------------ the GEMV
+// Partial U over a quarter of one K range: wave w of the workgroup takes
+// k in [kb + w q, kb + (w+1) q), q = (ke - kb) / 4, and writes
+// upart[t, j] = sum over its k of X[t, k] A[j, k] for all ranks j < r.
 template <int MT>
-__global__ __launch_bounds__(256) void k_nf4_gemv(const bf16_t *__restrict__ X, int64_t T, int64_t K,
-                                                  const uint8_t *__restrict__ codes,
-                                                  const uint8_t *__restrict__ absmax_q,
-                                                  const float *__restrict__ step, int64_t N, int64_t kchunk,
-                                                  const bf16_t *__restrict__ V, int64_t rp,
-                                                  const bf16_t *__restrict__ B, int64_t r, float *__restrict__ part,
-                                                  bf16_t *__restrict__ Y, Levels lv) {
-  __shared__ __attribute__((aligned(16))) float2 s_tab[512];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  pair_table_to_lds(lv, s_tab, tid);
-  __syncthreads();
-  const char *tab = reinterpret_cast<const char *>(s_tab);
-  const uint32_t copy = (lane >> 5) ? kPairTableBytes : 0u;
-  const int g = lane >> 4;  // 32-wide slice of each 128-deep step
-  const int64_t n = (int64_t)blockIdx.x * 64 + wave * 16 + (lane & 15);
-  const bool nok = n < N;
-  const int64_t kb = (int64_t)blockIdx.y * kchunk;
-  const int64_t ke = (kb + kchunk < K) ? kb + kchunk : K;
-  const int nsteps = (int)((ke - kb) / 128);
-  const uint8_t *cptr = codes + (nok ? n : 0) * (K / 2) + (kb + 32 * g) / 2;
-  const int64_t bidx = (nok ? n : 0) * (K / 64) + (kb + 32 * g) / 64;
-
-  auto load_codes = [&](int s, u32x4_t &c, RawScale &cq) {
-    if (nok && s < nsteps) {
-      c = *reinterpret_cast<const u32x4_t *>(cptr + (int64_t)s * 64);
-      cq = load_scale(absmax_q, step, bidx + 2 * s);
-    } else {
-      c = u32x4_t{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
-      cq = RawScale{0u, 0.f};
-    }
-  };
-  const bf16_t *xrow[MT];
+__device__ void lora_u_partial(const bf16_t *__restrict__ X, int64_t T, int64_t K, const bf16_t *__restrict__ A,
+                               int64_t r, int64_t kb, int64_t ke, float *__restrict__ upart, int wave, int lane) {
+  const int g = lane >> 4;
+  const int64_t q = (ke - kb) / 4, k0 = kb + wave * q, k1 = k0 + q;
+  for (int jt = 0; jt * 16 < r; ++jt) {
+    const int64_t j = jt * 16 + (lane & 15);
+    const bool jok = j < r;
+    f32x4_t acc[MT];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    int64_t t = m * 16 + (lane & 15);
-    t = t < T ? t : T - 1;  // rows past T read row T-1 and feed outputs that are never stored
-    xrow[m] = X + t * K + kb + 32 * g;
-  }
-
-  f32x4_t acc[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // three fixed prefetch slots, unrolled so that no register holding a load in
-  // flight is ever copied (a copy would make the wave wait for that load)
-  u32x4_t c0, c1, c2;
-  RawScale q0, q1, q2;
-  load_codes(0, c0, q0);
-  load_codes(1, c1, q1);
-  load_codes(2, c2, q2);
-  auto do_step = [&](int s, u32x4_t &c, RawScale &cq_raw) {
-    u32x4_t a[MT][4];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) a[m][q] = *reinterpret_cast<const u32x4_t *>(xrow[m] + (int64_t)s * 128 + 8 * q);
-    const float cq = scale_of(cq_raw);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const u32x4_t b = decode8_pairs(c[q], cq, tab, copy);
-#pragma unroll
-      for (int m = 0; m < MT; ++m) acc[m] = mfma_16x16x32(a[m][q], b, acc[m]);
-    }
-    load_codes(s + 3, c, cq_raw);  // refill this slot three steps ahead
-  };
-  for (int s = 0; s < nsteps; s += 3) {
-    do_step(s, c0, q0);
-    if (s + 1 < nsteps) do_step(s + 1, c1, q1);
-    if (s + 2 < nsteps) do_step(s + 2, c2, q2);
-  }
-
-  // the first K range also carries the LoRA term V[T, rp] . B[n, :r]^T
-  if (blockIdx.y == 0) {
-    for (int64_t j = 8 * g; j < rp; j += 32) {
-      u32x4_t a[MT];
+    for (int m = 0; m < MT; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int64_t k = k0 + 8 * g; k < k1; k += 32) {
+      const u32x4_t b = jok ? *reinterpret_cast<const u32x4_t *>(A + j * K + k) : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        int64_t t = m * 16 + (lane & 15);
-        t = t < T ? t : T - 1;
-        a[m] = *reinterpret_cast<const u32x4_t *>(V + t * rp + j);
+        const int64_t t = m * 16 + (lane & 15);
+        const u32x4_t a = t < T ? *reinterpret_cast<const u32x4_t *>(X + t * K + k) : u32x4_t{0u, 0u, 0u, 0u};
+        acc[m] = mfma_16x16x32(a, b, acc[m]);
       }
-      uint32_t h[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) h[e] = (nok && j + e < r) ? (uint32_t)B[n * r + j + e] : 0u;
-      const u32x4_t b = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-#pragma unroll
-      for (int m = 0; m < MT; ++m) acc[m] = mfma_16x16x32(a[m], b, acc[m]);
     }
-  }
-
-  // accumulator element i of lane l holds token 16 m + 4 (l >> 4) + i, row n
-  const int nsplit = (int)gridDim.y;
-  if (nsplit == 1) {
-    if (nok)
+    // element i of lane l: token 16 m + 4 (l >> 4) + i, rank 16 jt + (l & 15)
+    if (jok)
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int64_t t = m * 16 + 4 * g + i;
-          if (t < T) Y[t * N + n] = f32_to_bf16(acc[m][i]);
+          if (t < T) upart[t * r + j] = acc[m][i];
         }
+  }
+}
+}  // namespace
+
+// ------------------------------------------------------------------ the GEMV
+// Work item i = (tile, split) = (i / nsplit, i % nsplit): weight rows
+// 64 RG tile .. +64 RG - 1 over the K range [split kchunk, (split+1) kchunk).
+// The first gmain workgroups are persistent: workgroup x takes items
+// x, x + gmain, ..., and its waves stream the steps of all its items as one
+// sequence, so the prefetch runs on across item boundaries.  Workgroup
+// gmain + p computes the U partials of K range p (four, one per wave).
+// A step is D = 128 W deep: lane group g = lane / 16 reads 16 W bytes of codes
+// (32 W consecutive weights) of its row.  part: [nsplit][T][N] binary32,
+// upart: [4 nsplit][T][r] binary32.  K must be a multiple of nsplit * D.
+template <int MT, int RG, int W>
+__global__ __launch_bounds__(256) void k_nf4_gemv(const bf16_t *__restrict__ X, int64_t T, int64_t K,
+                                                  const uint8_t *__restrict__ codes,
+                                                  const uint8_t *__restrict__ absmax_q,
+                                                  const float *__restrict__ step, int64_t N, int nsplit,
+                                                  int gmain, const bf16_t *__restrict__ A, int64_t r,
+                                                  float *__restrict__ part, float *__restrict__ upart, Levels lv) {
+  constexpr int D = 128 * W;              // reduction depth of one step
+  constexpr int NB = W >= 2 ? W / 2 : 1;  // NF4 blocks a lane touches per step
+  __shared__ __attribute__((aligned(16))) float2 s_tab[512];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t kchunk = K / nsplit;
+  if ((int)blockIdx.x >= gmain) {
+    const int64_t kb = (int64_t)(blockIdx.x - gmain) * kchunk;
+    lora_u_partial<MT>(X, T, K, A, r, kb, kb + kchunk, upart + ((int64_t)(blockIdx.x - gmain) * 4 + wave) * T * r,
+                       wave, lane);
     return;
   }
-  if (nok) {
-    float *dst = part + (int64_t)blockIdx.y * T * N;
+  pair_table_to_lds(lv, s_tab, tid);
+  __syncthreads();
+  const char *tab = reinterpret_cast<const char *>(s_tab);
+  const uint32_t copy = (lane >> 5) ? kPairTableBytes : 0u;
+  const int g = lane >> 4;  // which 32 W-wide slice of each step
+  const int nsteps = (int)(kchunk / D);
+  const int64_t tiles = (N + 64 * RG - 1) / (64 * RG);
+  const int64_t nitems = tiles * nsplit;
+  const int64_t my_items = (nitems - blockIdx.x + gmain - 1) / gmain;
+  const int64_t total = my_items * nsteps;  // steps of this workgroup
+  if (total == 0) return;
+
+  // activations: token 16 m + (lane & 15); tokens past T are zero and not loaded
+  const bf16_t *xrow[MT];
+  bool tok[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int64_t t = m * 16 + (lane & 15);
+    tok[m] = t < T;
+    xrow[m] = X + (tok[m] ? t : 0) * K + 32 * W * g;
+  }
+  // row of row group q in tile `tile`: 64 RG tile + 64 q + 16 wave + (lane & 15)
+  auto row_of = [&](int64_t tile, int q) { return tile * 64 * RG + 64 * q + 16 * wave + (lane & 15); };
+
+  f32x4_t acc[RG][MT];
+#pragma unroll
+  for (int q = 0; q < RG; ++q)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[q][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  struct Slot {
+    u32x4_t c[RG][W];
+    RawScale cq[RG][NB];
+  };
+  // load stream position: item li of this workgroup, step ls
+  int64_t li = 0;
+  int ls = 0;
+  auto load_slot = [&](Slot &sl) {
+    const bool past = li >= my_items;  // past the end: re-read the last step (unused)
+    const int64_t item = blockIdx.x + (past ? my_items - 1 : li) * gmain;
+    const int sidx = past ? nsteps - 1 : ls;
+    const int64_t tile = item / nsplit, split = item - tile * nsplit;
+    const int64_t koff = split * kchunk + (int64_t)sidx * D + 32 * W * g;
+#pragma unroll
+    for (int q = 0; q < RG; ++q) {
+      int64_t n = row_of(tile, q);
+      n = n < N ? n : N - 1;  // rows past N re-read the last row; they are never stored
+      const uint8_t *cp = codes + n * (K / 2) + koff / 2;
+#pragma unroll
+      for (int i = 0; i < W; ++i) sl.c[q][i] = *reinterpret_cast<const u32x4_t *>(cp + 16 * i);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) sl.cq[q][b] = load_scale(absmax_q, step, n * (K / 64) + koff / 64 + b);
+    }
+    if (++ls == nsteps) {
+      ls = 0;
+      ++li;
+    }
+  };
+  // compute stream position: item ci, step cs
+  int64_t ci = 0;
+  int cs = 0;
+  auto do_step = [&](Slot &cur, Slot &refill) {
+    load_slot(refill);
+    const int64_t item = blockIdx.x + ci * gmain;
+    const int64_t tile = item / nsplit, split = item - tile * nsplit;
+    const int64_t koff = split * kchunk + (int64_t)cs * D;
+    u32x4_t a[MT][4 * W];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t t = m * 16 + 4 * g + i;
-        if (t < T) dst[t * N + n] = acc[m][i];
+      for (int j = 0; j < 4 * W; ++j)
+        a[m][j] = tok[m] ? *reinterpret_cast<const u32x4_t *>(xrow[m] + koff + 8 * j) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < RG; ++q) {
+#pragma unroll
+      for (int i = 0; i < W; ++i) {
+        const float cq = scale_of(cur.cq[q][W >= 2 ? i / 2 : 0]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4_t b = decode8_pairs(cur.c[q][i][j], cq, tab, copy);
+#pragma unroll
+          for (int m = 0; m < MT; ++m) acc[q][m] = mfma_16x16x32(a[m][4 * i + j], b, acc[q][m]);
+        }
       }
+    }
+    if (++cs == nsteps) {  // item done: store its partial sums and start the next
+      // accumulator element e of lane l holds token 16 m + 4 (l >> 4) + e, row n
+      float *dst = part + split * T * N;
+#pragma unroll
+      for (int q = 0; q < RG; ++q) {
+        const int64_t n = row_of(tile, q);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t t = m * 16 + 4 * g + e;
+            if (n < N && t < T) dst[t * N + n] = acc[q][m][e];
+          }
+          acc[q][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      cs = 0;
+      ++ci;
+    }
+  };
+  // three fixed slots, unrolled so that no register holding a load in flight
+  // is ever copied (a copy would make the wave wait for that load)
+  Slot s0, s1, s2;
+  load_slot(s0);
+  load_slot(s1);
+  for (int64_t f = 0; f < total; f += 3) {
+    do_step(s0, s2);
+    if (f + 1 < total) do_step(s1, s0);
+    if (f + 2 < total) do_step(s2, s1);
   }
 }
 
-// Y[i] = bf16(sum over p = 0 .. nsplit-1, in that order, of part[p][i]), i over T * N
-__global__ __launch_bounds__(256) void k_gemv_reduce(const float *__restrict__ part, int nsplit, int64_t total,
-                                                     bf16_t *__restrict__ Y) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= total) return;
-  float sum = 0.f;
-  for (int p = 0; p < nsplit; ++p) sum += part[(int64_t)p * total + i];
-  Y[i] = f32_to_bf16(sum);
+// Workgroup (x, t): U[t, :] = sum over the nup U partials p (in order) of upart[p][t][:],
+// V = bf16(s U) in LDS (U_out[t, :] = bf16(U) from x == 0), then for its 256
+// outputs n: Y[t, n] = bf16(sum over p (in order) of part[p][t][n] + V . B[n, :r]).
+__global__ __launch_bounds__(256) void k_gemv_finish(const float *__restrict__ part, const float *__restrict__ upart,
+                                                     int nsplit, int nup, int64_t T, int64_t N,
+                                                     const bf16_t *__restrict__ B,
+                                                     int64_t r, float s, bf16_t *__restrict__ Y,
+                                                     bf16_t *__restrict__ U_out) {
+  __shared__ float s_v[QLORA_MAX_RANK];
+  const int tid = threadIdx.x;
+  const int64_t t = blockIdx.y;
+  if (tid < r) {
+    float u = 0.f;
+    for (int p = 0; p < nup; ++p) u += upart[((int64_t)p * T + t) * r + tid];
+    s_v[tid] = bf16_lo_to_f32(f32_to_bf16(s * u));
+    if (U_out && blockIdx.x == 0) U_out[t * r + tid] = f32_to_bf16(u);
+  }
+  __syncthreads();
+  const int64_t n = (int64_t)blockIdx.x * 256 + tid;
+  if (n >= N) return;
+  float y = 0.f;
+  for (int p = 0; p < nsplit; ++p) y += part[((int64_t)p * T + t) * N + n];
+  float l = 0.f;
+  const bf16_t *brow = B + n * r;
+  for (int64_t j = 0; j < r; ++j) l = fmaf(s_v[j], bf16_lo_to_f32(brow[j]), l);
+  Y[t * N + n] = f32_to_bf16(y + l);
 }
 
-// Split of K for the small-token forward: aim at ~8 workgroups per CU, each
-// K range a multiple of 128 and at least 512 deep, and keep the binary32
-// partial sums (written and read once) below ~1/8 of the weight stream:
-// 8 ns T N bytes <= 0.516 N K / 8  <=>  ns <= K / (128 T).
-void nf4_gemv_plan(int64_t T, int64_t N, int64_t K, int *nsplit, int64_t *kchunk) {
-  const int64_t tiles = (N + 63) / 64;
-  int64_t ns = (2048 + tiles - 1) / tiles;
-  const int64_t by_depth = K / 512 > 0 ? K / 512 : 1;
-  const int64_t tt = T > 0 ? T : 1;
-  const int64_t by_traffic = K / (128 * tt) > 0 ? K / (128 * tt) : 1;
-  if (ns > by_depth) ns = by_depth;
-  if (ns > by_traffic) ns = by_traffic;
-  if (ns < 1) ns = 1;
-  int64_t kc = (K + ns - 1) / ns;
-  kc = (kc + 127) / 128 * 128;
-  *kchunk = kc;
-  *nsplit = (int)((K + kc - 1) / kc);
+// Plan of the small-token forward: step depth (W), RG row groups per wave,
+// the K split (nsplit equal ranges of whole steps) and the number of
+// persistent workgroups.  Chosen from a sweep on MI355X over 8192 x 8192 and
+// 28672 x 8192 weights with 1, 8 and 32 tokens: 256-deep steps up to 16
+// tokens, one row group per wave for very few tokens (more waves in flight),
+// up to ~4096 work items of at most 16 K ranges.
+void nf4_gemv_plan(int64_t T, int64_t N, int64_t K, int *rg, int *w, int *nsplit, int *gmain) {
+  int ww = T <= 16 ? 2 : 1;
+  while (ww > 1 && K % (128 * ww) != 0) ww /= 2;
+  const int rr = T <= 4 ? 1 : (T <= 16 ? 2 : 4);
+  const int64_t steps = K / (128 * ww);
+  const int64_t tiles = (N + 64 * rr - 1) / (64 * rr);
+  int64_t ns = 1;
+  for (int64_t d = 1; d <= steps && d <= 16; ++d)
+    if (steps % d == 0 && tiles * d <= 4096) ns = d;
+  const int64_t items = tiles * ns;
+  const int64_t gm = T <= 4 ? 1024 : 512;
+  *rg = rr;
+  *w = ww;
+  *nsplit = (int)ns;
+  *gmain = (int)(items < gm ? items : gm);
 }
 
-hipError_t launch_lora_u_small(const bf16_t *X, int64_t T, int64_t K, const bf16_t *A, int64_t r, float s,
-                               bf16_t *U_out, bf16_t *V, int64_t rp, hipStream_t st) {
-  if (T == 0) return hipSuccess;
-  dim3 grid((unsigned)((T + 15) / 16), (unsigned)((rp + 15) / 16));
-  launch(k_lora_u_small, grid, dim3(256), 0, st, X, T, K, A, r, s, U_out, V, rp);
-  return hipGetLastError();
+template <int MT, int RG, int W>
+static void gemv_with(hipStream_t s, const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes,
+                      const uint8_t *absmax_q, const float *step, int64_t N, int nsplit, int gmain, const bf16_t *A,
+                      int64_t r, float *part, float *upart, const Levels &lv) {
+  launch(k_nf4_gemv<MT, RG, W>, dim3((unsigned)(gmain + nsplit)), dim3(256), 0, s, X, T, K, codes, absmax_q, step, N,
+         nsplit, gmain, A, r, part, upart, lv);
+}
+
+template <int MT, int W>
+static void gemv_rg(int rg, hipStream_t s, const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes,
+                    const uint8_t *absmax_q, const float *step, int64_t N, int nsplit, int gmain, const bf16_t *A,
+                    int64_t r, float *part, float *upart, const Levels &lv) {
+  if (rg == 4) gemv_with<MT, 4, W>(s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv);
+  else if (rg == 2) gemv_with<MT, 2, W>(s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv);
+  else gemv_with<MT, 1, W>(s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv);
 }
 
 hipError_t launch_nf4_gemv(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
-                           const float *step, int64_t N, int nsplit, int64_t kchunk, const bf16_t *V, int64_t rp,
-                           const bf16_t *B, int64_t r, float *part, bf16_t *Y, const Levels &lv, hipStream_t s) {
+                           const float *step, int64_t N, int rg, int w, int nsplit, int gmain, const bf16_t *A,
+                           int64_t r, float *part, float *upart, const Levels &lv, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  dim3 grid((unsigned)((N + 63) / 64), (unsigned)nsplit);
-  if (T <= 16)
-    launch(k_nf4_gemv<1>, grid, dim3(256), 0, s, X, T, K, codes, absmax_q, step, N, kchunk, V, rp, B, r,
-                       part, Y, lv);
-  else if (T <= 32)
-    launch(k_nf4_gemv<2>, grid, dim3(256), 0, s, X, T, K, codes, absmax_q, step, N, kchunk, V, rp, B, r,
-                       part, Y, lv);
-  else
-    launch(k_nf4_gemv<4>, grid, dim3(256), 0, s, X, T, K, codes, absmax_q, step, N, kchunk, V, rp, B, r,
-                       part, Y, lv);
+  if (T <= 16) {
+    if (w == 2) gemv_rg<1, 2>(rg, s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv);
+    else gemv_rg<1, 1>(rg, s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv);
+  } else if (T <= 32) {
+    gemv_rg<2, 1>(rg, s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv);
+  } else {
+    gemv_rg<4, 1>(rg, s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_reduce(const float *part, int nsplit, int64_t T, int64_t N, bf16_t *Y, hipStream_t s) {
-  const int64_t total = T * N;
-  if (total == 0 || nsplit <= 1) return hipSuccess;
-  launch(k_gemv_reduce, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, nsplit, total, Y);
+hipError_t launch_gemv_finish(const float *part, const float *upart, int nsplit, int64_t T, int64_t N,
+                              const bf16_t *B, int64_t r, float s, bf16_t *Y, bf16_t *U_out, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  dim3 grid((unsigned)((N + 255) / 256), (unsigned)T);
+  launch(k_gemv_finish, grid, dim3(256), 0, st, part, upart, nsplit, 4 * nsplit, T, N, B, r, s, Y, U_out);
   return hipGetLastError();
 }
 
