@@ -11,8 +11,8 @@
 // A workgroup of WAVES_M x WAVES_N waves computes a BM x BN output tile; each
 // wave owns WM x WN tiles of v_mfma_f32_32x32x16_bf16 (32x32 outputs each).
 // The reduction runs in steps of 64 (one NF4 block per weight row):
-//  - the activation tile of step s+1 is loaded into registers at the start of
-//    step s and written to the other LDS buffer at its end;
+//  - the activation tile of step s+1 is copied global -> LDS by the load unit
+//    itself (global_load_lds_dwordx4), so it never occupies registers;
 //  - the codes and block constants of step s+2 are loaded into one of two
 //    register slots;
 //  - the MFMAs of step s are interleaved with the decode of step s+1 (level
@@ -88,36 +88,38 @@ __device__ __forceinline__ void zero_acc(f32x16_t acc[C::WM][C::WN]) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 }
 
-// Per-lane source rows of the activation tile: load i of this thread covers
-// chunk c = tid + NT*i, i.e. tile row c / 8 and 16-byte chunk c % 8.  Rows
-// past `rows` re-read the last row (their outputs are never stored).
+// Direct activation loads (global_load_lds_dwordx4: lane l's 16 bytes land
+// at the wave-uniform LDS base + 16 l).  Load i of wave w fills tile rows
+// 8g .. 8g+7 (g = i NW + w), one 1 KB run; lane l fills row 8g + l/8 at
+// swizzled chunk slot l % 8, i.e. logical chunk (l % 8) ^ ((row / 2) % 8).
+// Rows past `rows` re-read the last row (their outputs are never stored).
 template <class C>
 struct ALoads {
   const bf16_t *src[C::A_LD];
-  int col[C::A_LD], off[C::A_LD];
-  __device__ __forceinline__ void init(const bf16_t *__restrict__ base, int64_t ld, int64_t m0, int64_t rows, int tid) {
+  int col[C::A_LD];
+  int wave;
+  __device__ __forceinline__ void init(const bf16_t *__restrict__ base, int64_t ld, int64_t m0, int64_t rows, int w,
+                                       int lane) {
+    wave = w;
 #pragma unroll
     for (int i = 0; i < C::A_LD; ++i) {
-      const int c = tid + C::NT * i, row = c >> 3;
+      const int row = 8 * (i * C::NW + w) + (lane >> 3);
       const int64_t grow = (m0 + row < rows) ? m0 + row : rows - 1;
       src[i] = base + grow * ld;
-      col[i] = 8 * (c & 7);
-      off[i] = lds_off(row, c & 7);
+      col[i] = 8 * ((lane & 7) ^ ((row >> 1) & 7));
     }
   }
-  // Reduction columns k0 .. k0+63 into registers; a chunk starting at or past
-  // kmax re-reads the last chunk (the matching weight rows decode to 0).
-  __device__ __forceinline__ void load(int64_t k0, int64_t kmax, u32x4_t (&r)[C::A_LD]) const {
+  // Reduction columns k0 .. k0+63 into the tile at sa; a chunk starting at or
+  // past kmax re-reads the last chunk (the matching weight rows decode to 0).
+  __device__ __forceinline__ void issue(int64_t k0, int64_t kmax, bf16_t *sa) const {
 #pragma unroll
     for (int i = 0; i < C::A_LD; ++i) {
       int64_t c = k0 + col[i];
       c = c < kmax ? c : kmax - 8;
-      r[i] = *reinterpret_cast<const u32x4_t *>(src[i] + c);
+      __builtin_amdgcn_global_load_lds((const void *)(src[i] + c),
+                                       (__attribute__((address_space(3))) void *)(sa + (i * C::NW + wave) * 512), 16,
+                                       0, 0);
     }
-  }
-  __device__ __forceinline__ void store(const u32x4_t (&r)[C::A_LD], bf16_t *sa) const {
-#pragma unroll
-    for (int i = 0; i < C::A_LD; ++i) *reinterpret_cast<u32x4_t *>(sa + off[i]) = r[i];
   }
 };
 
@@ -230,22 +232,27 @@ __device__ __forceinline__ void store_out(bf16_t *__restrict__ out, int64_t ld, 
     }
 }
 
+// Wait for all but the last three vector-memory loads (the code words and the
+// block constant issued after the activation tile) and for all LDS operations.
+// s_waitcnt fields: vmcnt[3:0], expcnt[6:4] (7 = no wait), lgkmcnt[11:8].
+__device__ __forceinline__ void wait_tile_keep3() { __builtin_amdgcn_s_waitcnt(0x0073); }
+
 // One pipelined reduction step (see the file comment).  P = s % 2 selects the
 // LDS buffers and register slots: step s is multiplied out of buffer P while
 // the words in slot P^1 (step s+1) are decoded into buffer P^1, the
-// activation tile of step s+1 goes through registers into buffer P^1, and
+// activation tile of step s+1 is copied into buffer P^1 by the load unit, and
 // step s+2's words are loaded into slot P.  The caller's lambdas carry the
-// layout differences between the forward and dX: `load_next(ra)` issues the
-// global loads, `store_word(w, bf16x8)` writes word w of the decoded slot,
-// `store_a(ra)` writes the activation tile.
-template <class C, class ReadB, class LoadNext, class StoreWord, class StoreA>
+// layout differences between the forward and dX: `load_next()` issues the
+// global loads (the activation tile first, then exactly three loads for the
+// words), `store_word(w, bf16x8)` writes word w of the decoded slot.  The
+// LDS buffers are distinct variables, so the compiler can tell the reads of
+// buffer P from the direct loads into buffer P^1.
+template <class C, class ReadB, class LoadNext, class StoreWord>
 __device__ __forceinline__ void pipelined_step(const bf16_t *sa, const bf16_t *sb, int wm, int wn, int lane,
                                                const uint32_t (&words)[C::NWD], const RawScale &scale,
                                                const float *s_lv, f32x16_t (&acc)[C::WM][C::WN], ReadB read_b,
-                                               LoadNext load_next, StoreWord store_word, StoreA store_a,
-                                               bool decoder) {
-  u32x4_t ra[C::A_LD];
-  load_next(ra);  // activation tile of step s+1, then the words of step s+2
+                                               LoadNext load_next, StoreWord store_word, bool decoder) {
+  load_next();  // activation tile of step s+1, then the words of step s+2
   fence_sched();
   const float cq = scale_of(scale);
   constexpr int EVERY = 4 / C::NWD;  // substeps per decoded word
@@ -263,7 +270,6 @@ __device__ __forceinline__ void pipelined_step(const bf16_t *sa, const bf16_t *s
       mma_rows<C>(0, C::WM / 2, a[cur], b[cur], acc);
       fence_sched();
       if (dec) store_word(kk / EVERY, scale_pack8(v, cq));
-      if (kk == 3) store_a(ra);
       if (kk < 3) {
         read_a<C>(sa, wm, lane, kk + 1, a[cur ^ 1]);
         read_b(sb, kk + 1, b[cur ^ 1]);
@@ -273,6 +279,7 @@ __device__ __forceinline__ void pipelined_step(const bf16_t *sa, const bf16_t *s
       fence_sched();
     }
   }
+  wait_tile_keep3();
   __syncthreads();
 }
 
@@ -288,9 +295,13 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
                                                         const bf16_t *__restrict__ V, const bf16_t *__restrict__ Bp,
                                                         int64_t ldb, int64_t r, int64_t rp, bf16_t *__restrict__ Y,
                                                         Levels lv, int xb_m, int xb_n) {
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][C::BM * BK];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][C::BN * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t sA0[C::BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t sA1[C::BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t sB0[C::BN * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t sB1[C::BN * BK];
   __shared__ float s_lv[16];
+  bf16_t *const sA[2] = {sA0, sA1};
+  bf16_t *const sB[2] = {sB0, sB1};
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const TileCoord tc = tile_of((N + C::BN - 1) / C::BN, xb_m, xb_n);
@@ -299,7 +310,7 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
 
   const int nk = (int)(K / BK);
   ALoads<C> al;
-  al.init(X, K, m0, T, tid);
+  al.init(X, K, m0, T, wave, lane);
   // this thread decodes weights part*E .. part*E+E-1 of tile row brow
   constexpr int PARTS = BK / C::E;
   const bool decoder = tid < C::DEC;  // wave-uniform
@@ -319,11 +330,7 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
   zero_acc<C>(acc);
 
   // prologue: tile 0 of A, words of steps 0 and 1, decode step 0
-  {
-    u32x4_t ra[C::A_LD];
-    al.load(0, K, ra);
-    al.store(ra, sA[0]);
-  }
+  al.issue(0, K, sA[0]);
   load_words_of(0, rc[0], rs[0]);
   load_words_of(nk > 1 ? 1 : 0, rc[1], rs[1]);
   __syncthreads();  // level table visible
@@ -336,22 +343,22 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
         *reinterpret_cast<u32x4_t *>(sB[0] + lds_off(brow, part * C::NWD + w)) = scale_pack8(v, cq);
       }
   }
+  __builtin_amdgcn_s_waitcnt(0);  // the direct loads of tile 0 have landed
   __syncthreads();
 
   auto step_p = [&](auto pc, int s) {
     constexpr int P = decltype(pc)::value;
     const int sa = (s + 1 < nk) ? s + 1 : nk - 1, sc = (s + 2 < nk) ? s + 2 : nk - 1;
-    auto load_next = [&](u32x4_t(&ra)[C::A_LD]) {
-      al.load((int64_t)sa * BK, K, ra);
+    auto load_next = [&]() {
+      al.issue((int64_t)sa * BK, K, sA[P ^ 1]);
       fence_sched();  // activation loads first: waiting for them leaves the words in flight
       load_words_of(sc, rc[P], rs[P]);
     };
     auto store_word = [&](int w, const u32x4_t &o) {
       *reinterpret_cast<u32x4_t *>(sB[P ^ 1] + lds_off(brow, part * C::NWD + w)) = o;
     };
-    auto store_a = [&](const u32x4_t(&ra)[C::A_LD]) { al.store(ra, sA[P ^ 1]); };
     pipelined_step<C>(sA[P], sB[P], wm, wn, lane, rc[P ^ 1], rs[P ^ 1], s_lv, acc, read_b, load_next,
-                            store_word, store_a, decoder);
+                      store_word, decoder);
   };
   int s = 0;
   for (; s + 1 < nk; s += 2) {
@@ -402,9 +409,13 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
                                                        int64_t r, int64_t rp, bf16_t *__restrict__ dX, Levels lv,
                                                        int xb_m, int xb_n) {
   constexpr int LDB = C::BN + 32;  // row length (elements) of the [64][BN] B tile: 16 banks mod 64 per row
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][C::BM * BK];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][BK * LDB];
+  __shared__ __attribute__((aligned(16))) bf16_t sA0[C::BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t sA1[C::BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t sB0[BK * LDB];
+  __shared__ __attribute__((aligned(16))) bf16_t sB1[BK * LDB];
   __shared__ float s_lv[16];
+  bf16_t *const sA[2] = {sA0, sA1};
+  bf16_t *const sB[2] = {sB0, sB1};
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const TileCoord tc = tile_of((K + C::BN - 1) / C::BN, xb_m, xb_n);
@@ -413,7 +424,7 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
 
   const int nk = (int)((N + BK - 1) / BK);
   ALoads<C> al;
-  al.init(dY, N, m0, T, tid);
+  al.init(dY, N, m0, T, wave, lane);
   // this thread decodes columns piece*E .. piece*E+E-1 of tile row bn (weight row k0 + bn)
   constexpr int PIECES = C::BN / C::E;
   const bool decoder = tid < C::DEC;  // wave-uniform
@@ -433,11 +444,7 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
   f32x16_t acc[C::WM][C::WN];
   zero_acc<C>(acc);
 
-  {
-    u32x4_t ra[C::A_LD];
-    al.load(0, N, ra);
-    al.store(ra, sA[0]);
-  }
+  al.issue(0, N, sA[0]);
   load_words_of(0, rc[0], rs[0]);
   load_words_of(nk > 1 ? 1 : 0, rc[1], rs[1]);
   __syncthreads();
@@ -450,22 +457,22 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
         *reinterpret_cast<u32x4_t *>(sB[0] + bn * LDB + piece * C::E + 8 * w) = scale_pack8(v, cq);
       }
   }
+  __builtin_amdgcn_s_waitcnt(0);  // the direct loads of tile 0 have landed
   __syncthreads();
 
   auto step_p = [&](auto pc, int s) {
     constexpr int P = decltype(pc)::value;
     const int sa = (s + 1 < nk) ? s + 1 : nk - 1, sc = (s + 2 < nk) ? s + 2 : nk - 1;
-    auto load_next = [&](u32x4_t(&ra)[C::A_LD]) {
-      al.load((int64_t)sa * BK, N, ra);
+    auto load_next = [&]() {
+      al.issue((int64_t)sa * BK, N, sA[P ^ 1]);
       fence_sched();  // activation loads first: waiting for them leaves the words in flight
       load_words_of(sc, rc[P], rs[P]);
     };
     auto store_word = [&](int w, const u32x4_t &o) {
       *reinterpret_cast<u32x4_t *>(sB[P ^ 1] + bn * LDB + piece * C::E + 8 * w) = o;
     };
-    auto store_a = [&](const u32x4_t(&ra)[C::A_LD]) { al.store(ra, sA[P ^ 1]); };
-    pipelined_step<C>(sA[P], sB[P], wm, wn, lane, rc[P ^ 1], rs[P ^ 1], s_lv, acc, read_b,
-                                           load_next, store_word, store_a, decoder);
+    pipelined_step<C>(sA[P], sB[P], wm, wn, lane, rc[P ^ 1], rs[P ^ 1], s_lv, acc, read_b, load_next,
+                      store_word, decoder);
   };
   int s = 0;
   for (; s + 1 < nk; s += 2) {
