@@ -214,7 +214,7 @@ struct Plan {
   int64_t rp = 0;  // row length of the padded rank-wide copies (r rounded up to 64)
   int rn = 0;      // rank columns of the skinny GEMMs' partial sums
   int64_t rv = 0;  // r rounded up to 8: rank columns read from padded copies
-  size_t off_bp = 0, off_v = 0, off_du = 0, off_part = 0, total = 0;
+  size_t off_bp = 0, off_v = 0, off_du = 0, off_part = 0, off_part2 = 0, total = 0;
   Split su, sdu, sdb, sda;
   bool gemv = false;  // forward through the small-token kernels
   int gemv_rg = 0, gemv_w = 0, gemv_split = 0, gemv_main = 0;
@@ -251,9 +251,12 @@ Plan make_plan(int op, int64_t T, int64_t N, int64_t K, int32_t r) {
     p.sdu = plan_skinny(T, N);
     p.sdb = plan_skinny(N, T);
     p.sda = plan_skinny(K, T);
-    const size_t cands[4] = {(size_t)p.su.n * T * p.rn * 4, (size_t)p.sdu.n * T * p.rn * 4,
-                             (size_t)p.sdb.n * N * p.rn * 4, (size_t)p.sda.n * K * p.rn * 4};
+    // dA's partial sums get a region of their own, so that dB and dA are finalized in one launch
+    const size_t cands[3] = {(size_t)p.su.n * T * p.rn * 4, (size_t)p.sdu.n * T * p.rn * 4,
+                             (size_t)p.sdb.n * N * p.rn * 4};
     for (size_t c : cands) part = c > part ? c : part;
+    p.off_part2 = up(off + part, kAlign);
+    part = p.off_part2 - off + (size_t)p.sda.n * K * p.rn * 4;
   }
   p.off_part = off;
   off = up(off + part, kAlign);
@@ -446,11 +449,12 @@ int qlora_linear_bwd(const qlora_bf16 *X, const qlora_bf16 *dY, int64_t T, const
          launch_finalize(part, p.sdu.n, T, p.rn, nullptr, 0, 0, 0.f, dUp, p.rp, p.rp, r, sc, s));
   // dB = s dY^T U  -> [N, r]
   LAUNCH("lora_db", launch_skinny(true, true, p.rn, dY, N, N, Usrc, ldu, rvu, T, p.sdb.kchunk, p.sdb.n, part, s));
-  LAUNCH("lora_db_finalize", launch_finalize(part, p.sdb.n, N, p.rn, dB, r, r, sc, nullptr, 0, 0, 0, 0.f, s));
   // dA^T = X^T dU  -> [K, r], stored transposed as dA [r, K]
-  LAUNCH("lora_da", launch_skinny(true, true, p.rn, X, K, K, dUp, p.rp, p.rv, T, p.sda.kchunk, p.sda.n, part, s));
-  LAUNCH("lora_da_finalize",
-         launch_finalize(part, p.sda.n, K, p.rn, dA, K, r, 1.0f, nullptr, 0, 0, 0, 0.f, s, true));
+  float *part2 = (float *)(w + p.off_part2);
+  LAUNCH("lora_da", launch_skinny(true, true, p.rn, X, K, K, dUp, p.rp, p.rv, T, p.sda.kchunk, p.sda.n, part2, s));
+  // dB = s (sum of dB's partials), dA = (sum of dA's partials)^T, one launch
+  LAUNCH("lora_dadb_finalize", launch_finalize_pair(part, p.sdb.n, N, p.rn, dB, r, r, sc, false, part2, p.sda.n, K,
+                                                    p.rn, dA, K, r, 1.0f, true, s));
   // dX = dY W' + dU A
   if (dX)
     LAUNCH("nf4_gemm_dx",

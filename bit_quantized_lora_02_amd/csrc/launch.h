@@ -69,6 +69,11 @@ hipError_t launch_skinny(bool pt, bool qt, int rn, const bf16_t *P, int64_t ldp,
 hipError_t launch_finalize(const float *part, int nsplit, int64_t M, int64_t N, bf16_t *out1, int64_t ld1, int64_t n1,
                            float scale1, bf16_t *out2, int64_t ld2, int64_t n2, int64_t nvalid2, float scale2,
                            hipStream_t s, bool trans1 = false);
+// Two finalize jobs with one output each, in one launch.
+hipError_t launch_finalize_pair(const float *part_a, int nsplit_a, int64_t M_a, int64_t N_a, bf16_t *out_a,
+                                int64_t ld_a, int64_t n_a, float scale_a, bool trans_a, const float *part_b,
+                                int nsplit_b, int64_t M_b, int64_t N_b, bf16_t *out_b, int64_t ld_b, int64_t n_b,
+                                float scale_b, bool trans_b, hipStream_t s);
 hipError_t launch_pad_copy(const bf16_t *in, int64_t ldi, int64_t ncols, int64_t M, bf16_t *out, int64_t ldo,
                            hipStream_t s);
 

@@ -23,7 +23,7 @@ namespace qlora {
 //   PT = 0: P(m, k) = P[m*ldp + k]   PT = 1: P(m, k) = P[k*ldp + m]
 //   QT = 0: Q(k, j) = Q[j*ldq + k]   QT = 1: Q(k, j) = Q[k*ldq + j]
 // Tiles are copied global -> registers -> LDS in their natural layout
-// (16-byte chunks, prefetched one 64-deep step ahead, double-buffered LDS);
+// (16-byte chunks, prefetched two 64-deep steps ahead, double-buffered LDS);
 // operands whose reduction index is the row are read with ds_read_b64_tr_b16
 // (lane i of a 16-lane group gets element i & 3 of the 8 bytes addressed by
 // lane 4m + (i >> 2), m = 0..3).  4 waves x 32 rows, v_mfma_f32_16x16x32_bf16.
@@ -74,8 +74,9 @@ __global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, in
     if (PT) { row = c >> 4; col = (c & 15) * 8; }
     else { row = c >> 3; col = (((c & 7) ^ (row & 7)) << 3); }  // swizzled 16-byte chunks
   };
-  u32x4_t rp_[P_CH], rq_[Q_CH];
-  auto load = [&](int s) {
+  // two register slots (steps of even and odd index): the loads run two steps ahead
+  u32x4_t rpA[P_CH], rqA[Q_CH], rpB[P_CH], rqB[Q_CH];
+  auto load = [&](int s, u32x4_t(&rp_)[P_CH], u32x4_t(&rq_)[Q_CH]) {
     const int64_t k0 = kb + (int64_t)s * SK;
 #pragma unroll
     for (int i = 0; i < P_CH; ++i) {
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, in
       rq_[i] = ok ? *reinterpret_cast<const u32x4_t *>(src) : u32x4_t{0u, 0u, 0u, 0u};
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf, const u32x4_t(&rp_)[P_CH], const u32x4_t(&rq_)[Q_CH]) {
 #pragma unroll
     for (int i = 0; i < P_CH; ++i) {
       int row, col;
@@ -166,14 +167,19 @@ __global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, in
   };
 
   if (nsteps > 0) {
-    load(0);
-    store(0);
+    load(0, rpA, rqA);
+    if (nsteps > 1) load(1, rpB, rqB);
+    store(0, rpA, rqA);
     __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
-      const int buf = s & 1;
-      if (s + 1 < nsteps) load(s + 1);
-      mma(buf);
-      if (s + 1 < nsteps) store(buf ^ 1);
+    for (int s = 0; s < nsteps; s += 2) {
+      if (s + 2 < nsteps) load(s + 2, rpA, rqA);
+      mma(0);
+      if (s + 1 < nsteps) store(1, rpB, rqB);
+      __syncthreads();
+      if (s + 1 >= nsteps) break;
+      if (s + 3 < nsteps) load(s + 3, rpB, rqB);
+      mma(1);
+      if (s + 2 < nsteps) store(0, rpA, rqA);
       __syncthreads();
     }
   }
@@ -190,23 +196,51 @@ __global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, in
       }
 }
 
-// out1[m*ld1 + n] (or out1[n*ld1 + m] with trans1) = bf16(scale1 * S) for n < n1;
-// out2[m*ld2 + n] = n < nvalid2 ? bf16(scale2 * S) : 0 for n < n2;
-// S = sum over splits p = 0 .. nsplit-1 (in that order) of part[p][m][n] (ld = N).
-__global__ __launch_bounds__(256) void k_finalize(const float *__restrict__ part, int nsplit, int64_t M, int64_t N,
-                                                  bf16_t *__restrict__ out1, int64_t ld1, int64_t n1, float scale1,
-                                                  int trans1, bf16_t *__restrict__ out2, int64_t ld2, int64_t n2,
-                                                  int64_t nvalid2, float scale2) {
-  const int64_t ncol = (n1 > n2) ? n1 : n2;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= M * ncol) return;
+// One finalize job: S = sum over splits p = 0 .. nsplit-1 (in that order) of
+// part[p][m][n] (ld = N), then
+//   out1[m*ld1 + n] (or out1[n*ld1 + m] with trans1) = bf16(scale1 * S) for n < n1,
+//   out2[m*ld2 + n] = n < nvalid2 ? bf16(scale2 * S) : 0 for n < n2.
+struct FinJob {
+  const float *part;
+  int nsplit, trans1;
+  int64_t M, N;
+  bf16_t *out1;
+  int64_t ld1, n1;
+  float scale1, scale2;
+  bf16_t *out2;
+  int64_t ld2, n2, nvalid2;
+  int64_t nblocks;  // 256-thread blocks of this job
+};
+
+__device__ __forceinline__ void finalize_one(const FinJob &j, int64_t i) {
+  const int64_t ncol = (j.n1 > j.n2) ? j.n1 : j.n2;
+  if (i >= j.M * ncol) return;
   // transposed first output: consecutive threads take consecutive m so its stores coalesce
-  const int64_t m = trans1 ? i % M : i / ncol, n = trans1 ? i / M : i - m * ncol;
+  const int64_t m = j.trans1 ? i % j.M : i / ncol, n = j.trans1 ? i / j.M : i - m * ncol;
   float sum = 0.f;
-  if (n < N)
-    for (int p = 0; p < nsplit; ++p) sum += part[((int64_t)p * M + m) * N + n];
-  if (out1 && n < n1) out1[trans1 ? n * ld1 + m : m * ld1 + n] = f32_to_bf16(scale1 * sum);
-  if (out2 && n < n2) out2[m * ld2 + n] = (n < nvalid2) ? f32_to_bf16(scale2 * sum) : (bf16_t)0;
+  if (n < j.N) {
+    // all loads first, then the additions in split order
+    const float *src = j.part + m * j.N + n;
+    const int64_t stride = j.M * j.N;
+    int p = 0;
+    for (; p + 8 <= j.nsplit; p += 8) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = src[(int64_t)(p + q) * stride];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) sum += v[q];
+    }
+    for (; p < j.nsplit; ++p) sum += src[(int64_t)p * stride];
+  }
+  if (j.out1 && n < j.n1) j.out1[j.trans1 ? n * j.ld1 + m : m * j.ld1 + n] = f32_to_bf16(j.scale1 * sum);
+  if (j.out2 && n < j.n2) j.out2[m * j.ld2 + n] = (n < j.nvalid2) ? f32_to_bf16(j.scale2 * sum) : (bf16_t)0;
+}
+
+// Blocks [0, a.nblocks) run job a, the rest job b (two independent outputs in one launch).
+__global__ __launch_bounds__(256) void k_finalize(FinJob a, FinJob b) {
+  const int64_t blk = blockIdx.x;
+  if (blk < a.nblocks) finalize_one(a, blk * 256 + threadIdx.x);
+  else finalize_one(b, (blk - a.nblocks) * 256 + threadIdx.x);
 }
 
 // out[m*ldo + n] = n < ncols ? in[m*ldi + n] : 0, for n < ldo (zero-padded copy).
@@ -218,28 +252,64 @@ __global__ __launch_bounds__(256) void k_pad_copy(const bf16_t *__restrict__ in,
   out[i] = (n < ncols) ? in[m * ldi + n] : (bf16_t)0;
 }
 
+namespace {
+FinJob fin_job(const float *part, int nsplit, int64_t M, int64_t N, bf16_t *out1, int64_t ld1, int64_t n1,
+               float scale1, bf16_t *out2, int64_t ld2, int64_t n2, int64_t nvalid2, float scale2, bool trans1) {
+  FinJob j;
+  j.part = part;
+  j.nsplit = nsplit;
+  j.trans1 = trans1 ? 1 : 0;
+  j.M = M;
+  j.N = N;
+  j.out1 = out1;
+  j.ld1 = ld1;
+  j.n1 = n1;
+  j.scale1 = scale1;
+  j.out2 = out2;
+  j.ld2 = ld2;
+  j.n2 = n2;
+  j.nvalid2 = nvalid2;
+  j.scale2 = scale2;
+  const int64_t ncol = (n1 > n2) ? n1 : n2;
+  j.nblocks = (M * ncol + 255) / 256;
+  return j;
+}
+}  // namespace
+
 hipError_t launch_finalize(const float *part, int nsplit, int64_t M, int64_t N, bf16_t *out1, int64_t ld1, int64_t n1,
                            float scale1, bf16_t *out2, int64_t ld2, int64_t n2, int64_t nvalid2, float scale2,
                            hipStream_t s, bool trans1) {
-  const int64_t ncol = (n1 > n2) ? n1 : n2;
-  const int64_t total = M * ncol;
-  if (total == 0) return hipSuccess;
-  launch(k_finalize, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, nsplit, M, N, out1, ld1,
-                     n1, scale1, trans1 ? 1 : 0, out2, ld2, n2, nvalid2, scale2);
+  const FinJob a = fin_job(part, nsplit, M, N, out1, ld1, n1, scale1, out2, ld2, n2, nvalid2, scale2, trans1);
+  if (a.nblocks == 0) return hipSuccess;
+  FinJob none = a;
+  none.nblocks = 0;
+  launch(k_finalize, dim3((unsigned)a.nblocks), dim3(256), 0, s, a, none);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize_pair(const float *part_a, int nsplit_a, int64_t M_a, int64_t N_a, bf16_t *out_a,
+                                int64_t ld_a, int64_t n_a, float scale_a, bool trans_a, const float *part_b,
+                                int nsplit_b, int64_t M_b, int64_t N_b, bf16_t *out_b, int64_t ld_b, int64_t n_b,
+                                float scale_b, bool trans_b, hipStream_t s) {
+  const FinJob a = fin_job(part_a, nsplit_a, M_a, N_a, out_a, ld_a, n_a, scale_a, nullptr, 0, 0, 0, 0.f, trans_a);
+  const FinJob b = fin_job(part_b, nsplit_b, M_b, N_b, out_b, ld_b, n_b, scale_b, nullptr, 0, 0, 0, 0.f, trans_b);
+  if (a.nblocks + b.nblocks == 0) return hipSuccess;
+  launch(k_finalize, dim3((unsigned)(a.nblocks + b.nblocks)), dim3(256), 0, s, a, b);
   return hipGetLastError();
 }
 
 // Rank columns held by a skinny-GEMM workgroup for rank r.
 int skinny_rn(int64_t r) { return r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : 128; }
 
-// Split of the reduction for a skinny GEMM with M output rows: aim at ~512
-// workgroups with at least four 64-deep steps each.
+// Split of the reduction for a skinny GEMM with M output rows: aim at ~1024
+// workgroups (four per CU, so that enough loads are in flight) with at least
+// two 64-deep steps each.
 void skinny_plan(int64_t M, int64_t Kred, int *nsplit, int64_t *kchunk) {
   const int64_t tiles = (M + SBM - 1) / SBM;
-  int64_t ns = (512 + tiles - 1) / tiles;
-  const int64_t by_depth = Kred / 256 > 0 ? Kred / 256 : 1;
+  int64_t ns = (1024 + tiles - 1) / tiles;
+  const int64_t by_depth = Kred / 128 > 0 ? Kred / 128 : 1;
   if (ns > by_depth) ns = by_depth;
-  if (ns > 64) ns = 64;
+  if (ns > 32) ns = 32;  // bounds the binary32 partials (workspace) at 32 T r
   if (ns < 1) ns = 1;
   int64_t kc = (Kred + ns - 1) / ns;
   kc = (kc + SK - 1) / SK * SK;

@@ -273,7 +273,19 @@ __global__ __launch_bounds__(256) void k_gemv_finish(const float *__restrict__ p
   const int64_t n = (int64_t)blockIdx.x * 256 + tid;
   if (n >= N) return;
   float y = 0.f;
-  for (int p = 0; p < nsplit; ++p) y += part[((int64_t)p * T + t) * N + n];
+  {  // all loads first, then the additions in split order
+    const float *src = part + t * N + n;
+    const int64_t stride = T * N;
+    int p = 0;
+    for (; p + 8 <= nsplit; p += 8) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = src[(int64_t)(p + q) * stride];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) y += v[q];
+    }
+    for (; p < nsplit; ++p) y += src[(int64_t)p * stride];
+  }
   float l = 0.f;
   const bf16_t *brow = B + n * r;
   for (int64_t j = 0; j < r; ++j) l = fmaf(s_v[j], bf16_lo_to_f32(brow[j]), l);
