@@ -47,7 +47,8 @@ def parse():
     ap.add_argument("--config", default="attn_4096", choices=["attn_4096", "mlp_8b", "layer_70b", "small_token"])
     ap.add_argument("--tokens", type=int, default=1, help="T for --config small_token")
     ap.add_argument("--wide", action="store_true", help="28672x8192 instead of 8192x8192 for small_token")
-    ap.add_argument("--copies", type=int, default=4, help="rotating input/weight copies (defeats the 256 MB MALL)")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="rotating input/weight copies; default: enough for 512 MB, twice the 256 MB MALL")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -239,6 +240,9 @@ def main():
         return
 
     lins, T, r, alpha, outliers, train = linears_for(args)
+    if args.copies <= 0:  # rotate through >= 512 MB so that a step does not find the previous one's lines cached
+        per_copy = sum(weight_bytes(n, k) + 2 * T * (n + k) * (2 if train else 1) for _, n, k in lins)
+        args.copies = int(min(32, max(2, -(-(512 << 20) // per_copy))))
     layers = []
     first_inp = None
     t_quant = 0.0
@@ -367,6 +371,7 @@ def main():
         "weight_stream_GBps": wgbps,
         "weight_stream_frac_hbm": wgbps / PEAK_HBM_GBPS,
         "quantize_ms": t_quant * 1e3,
+        "rotating_copies": args.copies,
         "roofline": roof,
         "kernels": kernels,
         "cpu_baseline": cpu,

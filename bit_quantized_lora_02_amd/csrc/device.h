@@ -51,6 +51,21 @@ __device__ __forceinline__ void levels_to_lds(const Levels &lv, float *s_lv, int
   }
 }
 
+// Level-pair table for byte-wise decode: entry b = (level[b & 15], level[b >> 4]),
+// i.e. the levels of the low and the high nibble of code byte b.  Threads
+// 0..255 write one entry each.
+__device__ __forceinline__ void pair_levels_to_lds(const Levels &lv, float2 *tab, int tid) {
+  if (tid < 256) {
+    float lo = 0.f, hi = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      lo = ((tid & 15) == i) ? lv.v[i] : lo;
+      hi = ((tid >> 4) == i) ? lv.v[i] : hi;
+    }
+    tab[tid] = make_float2(lo, hi);
+  }
+}
+
 // Block constant of NF4 block b: fl32(q_b * d_{b/256}).
 __device__ __forceinline__ float block_scale(const uint8_t *__restrict__ absmax_q, const float *__restrict__ step,
                                              int64_t b) {

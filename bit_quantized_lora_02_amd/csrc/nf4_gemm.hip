@@ -137,9 +137,15 @@ __device__ __forceinline__ void load_words(const uint8_t *__restrict__ p, uint32
 
 // The two halves of decoding one code word: the level lookups, then the
 // binary32 products with the block constant packed to bf16.
-__device__ __forceinline__ void lookup8(uint32_t w, const float *s_lv, float (&v)[8]) {
+// (the lookups read the level-pair table one code byte at a time: the address
+// is the byte times 8, one v_lshlrev_b32 with a byte select)
+__device__ __forceinline__ void lookup8(uint32_t w, const float2 *s_lv, float (&v)[8]) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = s_lv[(w >> (4 * e)) & 15u];
+  for (int b = 0; b < 4; ++b) {
+    const float2 l = s_lv[(w >> (8 * b)) & 0xffu];
+    v[2 * b] = l.x;
+    v[2 * b + 1] = l.y;
+  }
 }
 __device__ __forceinline__ u32x4_t scale_pack8(const float (&v)[8], float cq) {
   return u32x4_t{pack_bf16x2(__fmul_rn(v[0], cq), __fmul_rn(v[1], cq)),
@@ -250,7 +256,7 @@ __device__ __forceinline__ void wait_tile_keep3() { __builtin_amdgcn_s_waitcnt(0
 template <class C, class ReadB, class LoadNext, class StoreWord>
 __device__ __forceinline__ void pipelined_step(const bf16_t *sa, const bf16_t *sb, int wm, int wn, int lane,
                                                const uint32_t (&words)[C::NWD], const RawScale &scale,
-                                               const float *s_lv, f32x16_t (&acc)[C::WM][C::WN], ReadB read_b,
+                                               const float2 *s_lv, f32x16_t (&acc)[C::WM][C::WN], ReadB read_b,
                                                LoadNext load_next, StoreWord store_word, bool decoder) {
   load_next();  // activation tile of step s+1, then the words of step s+2
   fence_sched();
@@ -299,14 +305,14 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
   __shared__ __attribute__((aligned(16))) bf16_t sA1[C::BM * BK];
   __shared__ __attribute__((aligned(16))) bf16_t sB0[C::BN * BK];
   __shared__ __attribute__((aligned(16))) bf16_t sB1[C::BN * BK];
-  __shared__ float s_lv[16];
+  __shared__ float2 s_lv[256];  // level pairs by code byte
   bf16_t *const sA[2] = {sA0, sA1};
   bf16_t *const sB[2] = {sB0, sB1};
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const TileCoord tc = tile_of((N + C::BN - 1) / C::BN, xb_m, xb_n);
   const int64_t m0 = tc.m * C::BM, n0 = tc.n * C::BN;
-  levels_to_lds(lv, s_lv, tid);
+  pair_levels_to_lds(lv, s_lv, tid);
 
   const int nk = (int)(K / BK);
   ALoads<C> al;
@@ -413,14 +419,14 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
   __shared__ __attribute__((aligned(16))) bf16_t sA1[C::BM * BK];
   __shared__ __attribute__((aligned(16))) bf16_t sB0[BK * LDB];
   __shared__ __attribute__((aligned(16))) bf16_t sB1[BK * LDB];
-  __shared__ float s_lv[16];
+  __shared__ float2 s_lv[256];  // level pairs by code byte
   bf16_t *const sA[2] = {sA0, sA1};
   bf16_t *const sB[2] = {sB0, sB1};
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const TileCoord tc = tile_of((K + C::BN - 1) / C::BN, xb_m, xb_n);
   const int64_t m0 = tc.m * C::BM, n0 = tc.n * C::BN;  // n0 indexes k_out
-  levels_to_lds(lv, s_lv, tid);
+  pair_levels_to_lds(lv, s_lv, tid);
 
   const int nk = (int)((N + BK - 1) / BK);
   ALoads<C> al;

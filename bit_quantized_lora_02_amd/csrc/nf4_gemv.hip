@@ -15,9 +15,9 @@
 //    consecutive weights of one row, one block constant) and decodes them
 //    straight into its four B operands, so the weight never touches LDS.  The
 //    decode looks up both levels of a code byte at once in a 256-entry LDS
-//    table of level pairs (two copies, one per half-wave): per byte one shift,
-//    one and-or (table offset), one 8-byte LDS read, two binary32 multiplies
-//    by the block constant and one bf16 pack.  Codes are prefetched two steps
+//    table of level pairs: per byte one shift with a byte select (the table
+//    offset), one 8-byte LDS read, two binary32 multiplies by the block
+//    constant and one bf16 pack.  Codes are prefetched two steps
 //    ahead.  Each K range writes binary32 partial sums.  One extra workgroup
 //    per K range computes the partial sums of U = X A^T over that range (one
 //    per quarter range and wave).
@@ -42,29 +42,14 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(const u32x4_t &a, const u32x4_t
                                                  0, 0, 0);
 }
 
-// Two copies of the level-pair table: entry b = (level[b & 15], level[b >> 4]).
-constexpr uint32_t kPairTableBytes = 256 * 8;
-
-__device__ __forceinline__ void pair_table_to_lds(const Levels &lv, float2 *tab, int tid) {
-  // 256 threads: thread t writes entry t of both copies
-  float lo = 0.f, hi = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    lo = ((tid & 15) == i) ? lv.v[i] : lo;
-    hi = ((tid >> 4) == i) ? lv.v[i] : hi;
-  }
-  tab[tid] = make_float2(lo, hi);
-  tab[256 + tid] = make_float2(lo, hi);
-}
-
-// 8 codes of one 32-bit word -> 4 packed bf16 pairs of fl32(level * cq).
-// `copy` is the byte offset of this lane's table copy.
-__device__ __forceinline__ u32x4_t decode8_pairs(uint32_t w, float cq, const char *tab, uint32_t copy) {
+// 8 codes of one 32-bit word -> 4 packed bf16 pairs of fl32(level * cq), from
+// the level-pair table (entry b = levels of the low and high nibble of byte b;
+// the address is the byte times 8, one v_lshlrev_b32 with a byte select).
+__device__ __forceinline__ u32x4_t decode8_pairs(uint32_t w, float cq, const float2 *tab) {
   u32x4_t o;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    const uint32_t sh = (b == 0) ? (w << 3) : (w >> (8 * b - 3));
-    const float2 l = *reinterpret_cast<const float2 *>(tab + ((sh & 0x7f8u) | copy));
+    const float2 l = tab[(w >> (8 * b)) & 0xffu];
     o[b] = pack_bf16x2(__fmul_rn(l.x, cq), __fmul_rn(l.y, cq));
   }
   return o;
@@ -126,7 +111,7 @@ __global__ __launch_bounds__(256) void k_nf4_gemv(const bf16_t *__restrict__ X, 
                                                   float *__restrict__ part, float *__restrict__ upart, Levels lv) {
   constexpr int D = 128 * W;              // reduction depth of one step
   constexpr int NB = W >= 2 ? W / 2 : 1;  // NF4 blocks a lane touches per step
-  __shared__ __attribute__((aligned(16))) float2 s_tab[512];
+  __shared__ __attribute__((aligned(16))) float2 s_tab[256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t kchunk = K / nsplit;
   if ((int)blockIdx.x >= gmain) {
@@ -135,10 +120,8 @@ __global__ __launch_bounds__(256) void k_nf4_gemv(const bf16_t *__restrict__ X, 
                        wave, lane);
     return;
   }
-  pair_table_to_lds(lv, s_tab, tid);
+  pair_levels_to_lds(lv, s_tab, tid);
   __syncthreads();
-  const char *tab = reinterpret_cast<const char *>(s_tab);
-  const uint32_t copy = (lane >> 5) ? kPairTableBytes : 0u;
   const int g = lane >> 4;  // which 32 W-wide slice of each step
   const int nsteps = (int)(kchunk / D);
   const int64_t tiles = (N + 64 * RG - 1) / (64 * RG);
@@ -214,7 +197,7 @@ __global__ __launch_bounds__(256) void k_nf4_gemv(const bf16_t *__restrict__ X, 
         const float cq = scale_of(cur.cq[q][W >= 2 ? i / 2 : 0]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const u32x4_t b = decode8_pairs(cur.c[q][i][j], cq, tab, copy);
+          const u32x4_t b = decode8_pairs(cur.c[q][i][j], cq, s_tab);
 #pragma unroll
           for (int m = 0; m < MT; ++m) acc[q][m] = mfma_16x16x32(a[m][4 * i + j], b, acc[q][m]);
         }
@@ -252,20 +235,30 @@ __global__ __launch_bounds__(256) void k_nf4_gemv(const bf16_t *__restrict__ X, 
   }
 }
 
-// Workgroup (x, t): U[t, :] = sum over the nup U partials p (in order) of upart[p][t][:],
-// V = bf16(s U) in LDS (U_out[t, :] = bf16(U) from x == 0), then for its 256
-// outputs n: Y[t, n] = bf16(sum over p (in order) of part[p][t][n] + V . B[n, :r]).
+// Workgroup (x, t): U[t, :] = sum of the nup U partials upart[p][t][:] (thread
+// (j, q) adds the partials p = q, q + 8, ... in order, then the eight subtotals
+// are added in q order), V = bf16(s U) in LDS (U_out[t, :] = bf16(U) from
+// x == 0); then for its 256 outputs n:
+// Y[t, n] = bf16(sum over p (in order) of part[p][t][n] + V . B[n, :r]).
 __global__ __launch_bounds__(256) void k_gemv_finish(const float *__restrict__ part, const float *__restrict__ upart,
                                                      int nsplit, int nup, int64_t T, int64_t N,
-                                                     const bf16_t *__restrict__ B,
-                                                     int64_t r, float s, bf16_t *__restrict__ Y,
-                                                     bf16_t *__restrict__ U_out) {
+                                                     const bf16_t *__restrict__ B, int64_t r, float s,
+                                                     bf16_t *__restrict__ Y, bf16_t *__restrict__ U_out) {
+  __shared__ float s_sub[8][QLORA_MAX_RANK];
   __shared__ float s_v[QLORA_MAX_RANK];
   const int tid = threadIdx.x;
   const int64_t t = blockIdx.y;
+  for (int i = tid; i < 8 * r; i += 256) {
+    const int j = i % r, q = i / r;
+    float u = 0.f;
+    for (int p = q; p < nup; p += 8) u += upart[((int64_t)p * T + t) * r + j];
+    s_sub[q][j] = u;
+  }
+  __syncthreads();
   if (tid < r) {
     float u = 0.f;
-    for (int p = 0; p < nup; ++p) u += upart[((int64_t)p * T + t) * r + tid];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) u += s_sub[q][tid];
     s_v[tid] = bf16_lo_to_f32(f32_to_bf16(s * u));
     if (U_out && blockIdx.x == 0) U_out[t * r + tid] = f32_to_bf16(u);
   }
@@ -288,7 +281,17 @@ __global__ __launch_bounds__(256) void k_gemv_finish(const float *__restrict__ p
   }
   float l = 0.f;
   const bf16_t *brow = B + n * r;
-  for (int64_t j = 0; j < r; ++j) l = fmaf(s_v[j], bf16_lo_to_f32(brow[j]), l);
+  int64_t j = 0;
+  if ((r & 7) == 0)  // rows of B are 16-byte multiples: 8 ranks per load
+    for (; j < r; j += 8) {
+      const u32x4_t w = *reinterpret_cast<const u32x4_t *>(brow + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        l = fmaf(s_v[j + 2 * e], bf16_lo_to_f32(w[e]), l);
+        l = fmaf(s_v[j + 2 * e + 1], bf16_hi_to_f32(w[e]), l);
+      }
+    }
+  for (; j < r; ++j) l = fmaf(s_v[j], bf16_lo_to_f32(brow[j]), l);
   Y[t * N + n] = f32_to_bf16(y + l);
 }
 
