@@ -37,9 +37,10 @@ namespace {
 
 constexpr int BK = 64;
 
-template <int WAVES_M_, int WAVES_N_, int WM_, int WN_>
+template <int WAVES_M_, int WAVES_N_, int WM_, int WN_, int AHEAD_ = 1>
 struct TileCfg {
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, WM = WM_, WN = WN_;
+  static constexpr int AHEAD = AHEAD_;  // substeps by which the MFMA operand reads run ahead (1 or 2)
   static constexpr int NW = WAVES_M * WAVES_N;
   static constexpr int NT = 64 * NW;
   static constexpr int BM = WAVES_M * WM * 32;
@@ -262,7 +263,7 @@ __device__ __forceinline__ void pipelined_step(const bf16_t *sa, const bf16_t *s
   fence_sched();
   const float cq = scale_of(scale);
   constexpr int EVERY = 4 / C::NWD;  // substeps per decoded word
-  {
+  if constexpr (C::AHEAD == 1) {
     u32x4_t a[2][C::WM], b[2][C::WN];
     float v[8];
     read_a<C>(sa, wm, lane, 0, a[0]);
@@ -280,6 +281,31 @@ __device__ __forceinline__ void pipelined_step(const bf16_t *sa, const bf16_t *s
         read_a<C>(sa, wm, lane, kk + 1, a[cur ^ 1]);
         read_b(sb, kk + 1, b[cur ^ 1]);
       }
+      fence_sched();
+      mma_rows<C>(C::WM / 2, C::WM, a[cur], b[cur], acc);
+      fence_sched();
+    }
+  } else {
+    // operand reads two substeps ahead of the MFMAs (three register sets)
+    u32x4_t a[3][C::WM], b[3][C::WN];
+    float v[8];
+    read_a<C>(sa, wm, lane, 0, a[0]);
+    read_b(sb, 0, b[0]);
+    read_a<C>(sa, wm, lane, 1, a[1]);
+    read_b(sb, 1, b[1]);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int cur = kk % 3;
+      const bool dec = decoder && (kk % EVERY) == 0;
+      if (dec) lookup8(words[kk / EVERY], s_lv, v);
+      if (kk + 2 < 4) {
+        read_a<C>(sa, wm, lane, kk + 2, a[(kk + 2) % 3]);
+        read_b(sb, kk + 2, b[(kk + 2) % 3]);
+      }
+      fence_sched();
+      mma_rows<C>(0, C::WM / 2, a[cur], b[cur], acc);
+      fence_sched();
+      if (dec) store_word(kk / EVERY, scale_pack8(v, cq));
       fence_sched();
       mma_rows<C>(C::WM / 2, C::WM, a[cur], b[cur], acc);
       fence_sched();
@@ -516,7 +542,7 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
 namespace {
 using T128x128 = TileCfg<2, 2, 2, 2>;    // 4 waves, 64x64 per wave, two workgroups per CU
 using T256x256w8 = TileCfg<2, 4, 4, 2>;  // 8 waves, 128x64 per wave, one workgroup per CU
-using T256x128w8 = TileCfg<4, 2, 2, 2>;  // 8 waves, 64x64 per wave
+using T256x128w8 = TileCfg<4, 2, 2, 2, 2>;  // 8 waves, 64x64 per wave, operand reads two substeps ahead
 using T128x256w8 = TileCfg<2, 4, 2, 2>;  // 8 waves, 64x64 per wave
 using T128x128w8 = TileCfg<2, 4, 2, 1>;  // 8 waves, 64x32 per wave
 
