@@ -59,6 +59,19 @@ def _load():
     lib.oracle_linear_fwd.restype = None
     lib.oracle_linear_bwd.argtypes = [P, P, i64, P, i64, i64, P, P, ctypes.c_int32, ctypes.c_float, P, i64, P, P, P]
     lib.oracle_linear_bwd.restype = None
+    lib.oracle_linear_fwd_xa.argtypes = [P, P, i64, P, i64, i64, P, P, ctypes.c_int32, ctypes.c_float, P, i64, P, P]
+    lib.oracle_linear_fwd_xa.restype = None
+    lib.oracle_linear_bwd_xa.argtypes = [P, P, P, P, i64, P, i64, i64, P, P, ctypes.c_int32, ctypes.c_float, P, i64,
+                                         P, P, P]
+    lib.oracle_linear_bwd_xa.restype = None
+    lib.oracle_philox4x32_10.argtypes = [P, P, P]
+    lib.oracle_philox4x32_10.restype = None
+    lib.oracle_dropout_threshold.argtypes = [ctypes.c_double]
+    lib.oracle_dropout_threshold.restype = ctypes.c_uint32
+    lib.oracle_dropout_mask.argtypes = [i64, ctypes.c_double, ctypes.c_uint64, ctypes.c_uint64, P]
+    lib.oracle_dropout_mask.restype = None
+    lib.oracle_dropout_apply.argtypes = [P, i64, P, ctypes.c_double, P, P]
+    lib.oracle_dropout_apply.restype = None
     _lib = lib
     return lib
 
@@ -183,3 +196,92 @@ def linear_bwd(X, dY, Wdq: np.ndarray, A, B, alpha: float, rows=None, want_dx: b
     _load().oracle_linear_bwd(_ptr(X), _ptr(dY), T, _ptr(Wdq), N, K, _ptr(A), _ptr(B), r, float(alpha),
                               _ptr(rows), n, _ptr(dX), _ptr(dA), _ptr(dB))
     return dX, dA, dB
+
+
+# ------------------------------------------------------------- LoRA dropout
+
+def linear_fwd_xa(X, Xa, Wdq: np.ndarray, A, B, alpha: float, rows=None):
+    """Forward with the adapter reading Xa instead of X: U = Xa A^T, Y = X W'^T + s U B^T (binary64)."""
+    X, Xa, A, B = _f64(X), _f64(Xa), _f64(A), _f64(B)
+    Wdq = np.ascontiguousarray(Wdq, np.uint16)
+    T, K = X.shape
+    N = Wdq.shape[0]
+    r = A.shape[0]
+    assert Xa.shape == X.shape and Wdq.shape == (N, K) and A.shape == (r, K) and B.shape == (N, r)
+    rows, n = _rows(rows, T)
+    Y = np.zeros((n, N), np.float64)
+    U = np.zeros((n, r), np.float64)
+    _load().oracle_linear_fwd_xa(_ptr(X), _ptr(Xa), T, _ptr(Wdq), N, K, _ptr(A), _ptr(B), r, float(alpha),
+                                 _ptr(rows), n, _ptr(Y), _ptr(U))
+    return Y, U
+
+
+def linear_bwd_xa(X, Xa, G, dY, Wdq: np.ndarray, A, B, alpha: float, rows=None, want_dx: bool = True):
+    """Backward of ``linear_fwd_xa`` where G = dXa/dX elementwise (None: Xa = X).
+
+    Returns (dX [n_rows, K] or None, dA [r, K], dB [N, r]) in binary64.
+    """
+    X, Xa, dY, A, B = _f64(X), _f64(Xa), _f64(dY), _f64(A), _f64(B)
+    G = None if G is None else _f64(G)
+    Wdq = np.ascontiguousarray(Wdq, np.uint16)
+    T, K = X.shape
+    N = Wdq.shape[0]
+    r = A.shape[0]
+    assert Xa.shape == X.shape and dY.shape == (T, N) and A.shape == (r, K) and B.shape == (N, r)
+    assert G is None or G.shape == X.shape
+    rows, n = _rows(rows, T)
+    dX = np.zeros((n, K), np.float64) if want_dx else None
+    dA = np.zeros((r, K), np.float64)
+    dB = np.zeros((N, r), np.float64)
+    _load().oracle_linear_bwd_xa(_ptr(X), _ptr(Xa), _ptr(G), _ptr(dY), T, _ptr(Wdq), N, K, _ptr(A), _ptr(B), r,
+                                 float(alpha), _ptr(rows), n, _ptr(dX), _ptr(dA), _ptr(dB))
+    return dX, dA, dB
+
+
+def philox4x32_10(counter, key) -> np.ndarray:
+    """One Philox4x32-10 block: four uint32 counter words and two key words -> four output words."""
+    c = np.ascontiguousarray(counter, np.uint32)
+    k = np.ascontiguousarray(key, np.uint32)
+    assert c.shape == (4,) and k.shape == (2,)
+    out = np.zeros(4, np.uint32)
+    _load().oracle_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def dropout_threshold(p: float) -> int:
+    """16-bit drop threshold D = round_half_even(p * 65536): an element is dropped iff its draw is < D."""
+    return int(_load().oracle_dropout_threshold(float(p)))
+
+
+def dropout_mask(T: int, K: int, p: float, seed: int, offset: int) -> np.ndarray:
+    """Keep bits of a [T, K] adapter input (K % 8 == 0): uint8 [T, K / 8], bit k % 8 of byte (t, k / 8)."""
+    if K % 8 or not 0.0 <= p < 1.0:
+        raise ValueError("need K % 8 == 0 and 0 <= p < 1")
+    mask = np.zeros((T, K // 8), np.uint8)
+    _load().oracle_dropout_mask(T * K // 8, float(p), int(seed) & (2**64 - 1), int(offset) & (2**64 - 1),
+                                _ptr(mask))
+    return mask
+
+
+def dropout_apply(X_bits: np.ndarray, mask: np.ndarray, p: float):
+    """(Xa as bf16 bits, G = keep * q in binary64) for X [T, K] given as bf16 bits."""
+    X_bits = np.ascontiguousarray(X_bits, np.uint16)
+    mask = np.ascontiguousarray(mask, np.uint8)
+    T, K = X_bits.shape
+    assert mask.shape == (T, K // 8)
+    Xa = np.zeros((T, K), np.uint16)
+    G = np.zeros((T, K), np.float64)
+    _load().oracle_dropout_apply(_ptr(X_bits), T * K, _ptr(mask), float(p), _ptr(Xa), _ptr(G))
+    return Xa, G
+
+
+def linear_fwd_dropout(X_bits, Wdq, A, B, alpha: float, mask, p: float, rows=None):
+    """Forward with inverted dropout on the adapter input (keep bits ``mask``): (Y, U) in binary64."""
+    Xa, _ = dropout_apply(X_bits, mask, p)
+    return linear_fwd_xa(np.ascontiguousarray(X_bits, np.uint16), Xa, Wdq, A, B, alpha, rows)
+
+
+def linear_bwd_dropout(X_bits, dY, Wdq, A, B, alpha: float, mask, p: float, rows=None, want_dx: bool = True):
+    """Backward of ``linear_fwd_dropout``: (dX or None, dA, dB) in binary64."""
+    Xa, G = dropout_apply(X_bits, mask, p)
+    return linear_bwd_xa(np.ascontiguousarray(X_bits, np.uint16), Xa, G, dY, Wdq, A, B, alpha, rows, want_dx)

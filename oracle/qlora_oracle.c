@@ -26,6 +26,9 @@
  *  [STEPS] "qlora" glossary (chipfoundryservices), table "How QLoRA Works":
  *         quantize at load (4-bit), forward dequantizes then computes, backward
  *         in bfloat16, only the adapter is updated.
+ *  [DROP] "Module 08 - QLoRA & Quantization" (ainiketan), "4. QLoRA in code":
+ *         the adapter config sets lora_dropout = 0.05 (so does the Developer
+ *         level of the pranaymahendrakar page).
  *
  * Readings where the pages are silent (each is listed in the design notes):
  *  - level construction: normal quantiles at equally spaced probabilities
@@ -41,7 +44,8 @@
  *    consecutive block constants, step d = fl32(max / 255), q = round-half-even
  *    of fl32(c / d) clamped to [0, 255]; decoding uses c' = fl32(q * d);
  *  - dequant: w' = bf16_rne(fl32(level[code] * c'));
- *  - scale s = fl32(alpha / r); no bias; no dropout.
+ *  - scale s = fl32(alpha / r); no bias; dropout on the adapter input only
+ *    where a caller asks for it (the [DROP] functions at the end).
  *
  * The forward and backward contractions are written out in binary64 from their
  * definitions; inputs arrive as binary64 arrays (the bf16 activations and
@@ -211,26 +215,27 @@ static inline double bf16_to_f64(uint16_t h) {
 /* ---------------------------------------------------------------- forward */
 
 /*
- * [LORA] forward for selected token rows:
- *   U[t, j] = sum_k X[t, k] A[j, k]
+ * [LORA] forward for selected token rows, with the adapter reading Xa (the
+ * layer input itself, or its dropped-out copy, see [DROP] below):
+ *   U[t, j] = sum_k Xa[t, k] A[j, k]
  *   Y[t, n] = sum_k X[t, k] W'[n, k] + s * sum_j U[t, j] B[n, j],   s = fl32(alpha / r)
- * X [T, K], A [r, K], B [N, r] binary64; Wdq [N, K] bf16 bits.
+ * X, Xa [T, K], A [r, K], B [N, r] binary64; Wdq [N, K] bf16 bits.
  * rows: n_rows indices into [0, T) (or NULL for all rows, then n_rows = T).
  * Y [n_rows, N], U [n_rows, r] binary64 (U may be NULL).
  */
-void oracle_linear_fwd(const double *X, int64_t T, const uint16_t *Wdq, int64_t N, int64_t K, const double *A,
-                       const double *B, int32_t r, float alpha, const int64_t *rows, int64_t n_rows, double *Y,
-                       double *U) {
+void oracle_linear_fwd_xa(const double *X, const double *Xa, int64_t T, const uint16_t *Wdq, int64_t N, int64_t K,
+                          const double *A, const double *B, int32_t r, float alpha, const int64_t *rows,
+                          int64_t n_rows, double *Y, double *U) {
   const double s = (double)(alpha / (float)r);
   if (!rows) n_rows = T;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t i = 0; i < n_rows; ++i) {
     const int64_t t = rows ? rows[i] : i;
-    const double *x = X + t * K;
+    const double *x = X + t * K, *xa = Xa + t * K;
     double *u = (double *)malloc(sizeof(double) * (size_t)(r > 0 ? r : 1));
     for (int32_t j = 0; j < r; ++j) {
       double acc = 0.0;
-      for (int64_t k = 0; k < K; ++k) acc += x[k] * A[(int64_t)j * K + k];
+      for (int64_t k = 0; k < K; ++k) acc += xa[k] * A[(int64_t)j * K + k];
       u[j] = acc;
       if (U) U[i * r + j] = acc;
     }
@@ -246,29 +251,38 @@ void oracle_linear_fwd(const double *X, int64_t T, const uint16_t *Wdq, int64_t 
   }
 }
 
+/* The layer without dropout: the adapter reads X itself. */
+void oracle_linear_fwd(const double *X, int64_t T, const uint16_t *Wdq, int64_t N, int64_t K, const double *A,
+                       const double *B, int32_t r, float alpha, const int64_t *rows, int64_t n_rows, double *Y,
+                       double *U) {
+  oracle_linear_fwd_xa(X, X, T, Wdq, N, K, A, B, r, alpha, rows, n_rows, Y, U);
+}
+
 /* --------------------------------------------------------------- backward */
 
 /*
  * [BWD] backward of the layer above with respect to X, A and B (W gets none):
- *   U  = X A^T                      [T, r]
+ *   U  = Xa A^T                     [T, r]
  *   dU = s * dY B                   [T, r]
- *   dA = dU^T X                     [r, K]
+ *   dA = dU^T Xa                    [r, K]
  *   dB = s * dY^T U                 [N, r]
- *   dX = dY W' + dU A               [T, K]   (only for the selected rows)
+ *   dX = dY W' + G o (dU A)         [T, K]   (only for the selected rows)
+ * G [T, K] is the elementwise derivative of Xa with respect to X (NULL: Xa = X,
+ * G = 1); "o" is the elementwise product.
  * dX [n_rows, K] (may be NULL), dA [r, K], dB [N, r] binary64.
  */
-void oracle_linear_bwd(const double *X, const double *dY, int64_t T, const uint16_t *Wdq, int64_t N, int64_t K,
-                       const double *A, const double *B, int32_t r, float alpha, const int64_t *rows,
-                       int64_t n_rows, double *dX, double *dA, double *dB) {
+void oracle_linear_bwd_xa(const double *X, const double *Xa, const double *G, const double *dY, int64_t T,
+                          const uint16_t *Wdq, int64_t N, int64_t K, const double *A, const double *B, int32_t r,
+                          float alpha, const int64_t *rows, int64_t n_rows, double *dX, double *dA, double *dB) {
   const double s = (double)(alpha / (float)r);
   double *U = (double *)calloc((size_t)(T * r > 0 ? T * r : 1), sizeof(double));
   double *dU = (double *)calloc((size_t)(T * r > 0 ? T * r : 1), sizeof(double));
-  /* U[t, j] = sum_k X[t, k] A[j, k];  dU[t, j] = s * sum_n dY[t, n] B[n, j] */
+  /* U[t, j] = sum_k Xa[t, k] A[j, k];  dU[t, j] = s * sum_n dY[t, n] B[n, j] */
 #pragma omp parallel for schedule(static)
   for (int64_t t = 0; t < T; ++t) {
     for (int32_t j = 0; j < r; ++j) {
       double a = 0.0;
-      for (int64_t k = 0; k < K; ++k) a += X[t * K + k] * A[(int64_t)j * K + k];
+      for (int64_t k = 0; k < K; ++k) a += Xa[t * K + k] * A[(int64_t)j * K + k];
       U[t * r + j] = a;
     }
     double *g = dU + t * r;
@@ -278,14 +292,14 @@ void oracle_linear_bwd(const double *X, const double *dY, int64_t T, const uint1
     }
     for (int32_t j = 0; j < r; ++j) g[j] *= s;
   }
-  /* dA[j, :] = sum_t dU[t, j] X[t, :] */
+  /* dA[j, :] = sum_t dU[t, j] Xa[t, :] */
 #pragma omp parallel for schedule(static)
   for (int32_t j = 0; j < r; ++j) {
     double *out = dA + (int64_t)j * K;
     for (int64_t k = 0; k < K; ++k) out[k] = 0.0;
     for (int64_t t = 0; t < T; ++t) {
       const double a = dU[t * r + j];
-      for (int64_t k = 0; k < K; ++k) out[k] += a * X[t * K + k];
+      for (int64_t k = 0; k < K; ++k) out[k] += a * Xa[t * K + k];
     }
   }
   /* dB[n, :] = s * sum_t dY[t, n] U[t, :]   (each thread owns a range of rows n) */
@@ -307,7 +321,7 @@ void oracle_linear_bwd(const double *X, const double *dY, int64_t T, const uint1
     for (int64_t n = n0; n < n1; ++n)
       for (int32_t j = 0; j < r; ++j) dB[n * r + j] *= s;
   }
-  /* dX[t, k] = sum_n dY[t, n] W'[n, k] + sum_j dU[t, j] A[j, k] */
+  /* dX[t, k] = sum_n dY[t, n] W'[n, k] + G[t, k] * sum_j dU[t, j] A[j, k] */
   if (dX) {
     if (!rows) n_rows = T;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -320,12 +334,111 @@ void oracle_linear_bwd(const double *X, const double *dY, int64_t T, const uint1
         const uint16_t *w = Wdq + n * K;
         for (int64_t k = 0; k < K; ++k) out[k] += g * bf16_to_f64(w[k]);
       }
-      for (int32_t j = 0; j < r; ++j) {
-        const double g = dU[t * r + j];
-        for (int64_t k = 0; k < K; ++k) out[k] += g * A[(int64_t)j * K + k];
+      if (!G) {
+        for (int32_t j = 0; j < r; ++j) {
+          const double g = dU[t * r + j];
+          for (int64_t k = 0; k < K; ++k) out[k] += g * A[(int64_t)j * K + k];
+        }
+      } else {
+        for (int64_t k = 0; k < K; ++k) {
+          double lora = 0.0;
+          for (int32_t j = 0; j < r; ++j) lora += dU[t * r + j] * A[(int64_t)j * K + k];
+          out[k] += G[t * K + k] * lora;
+        }
       }
     }
   }
   free(U);
   free(dU);
+}
+
+/* The layer without dropout. */
+void oracle_linear_bwd(const double *X, const double *dY, int64_t T, const uint16_t *Wdq, int64_t N, int64_t K,
+                       const double *A, const double *B, int32_t r, float alpha, const int64_t *rows,
+                       int64_t n_rows, double *dX, double *dA, double *dB) {
+  oracle_linear_bwd_xa(X, X, NULL, dY, T, Wdq, N, K, A, B, r, alpha, rows, n_rows, dX, dA, dB);
+}
+
+/* ------------------------------------------------------------ LoRA dropout */
+
+/*
+ * [DROP] "Module 08 - QLoRA & Quantization" (ainiketan.in), section "4. QLoRA in
+ * code", and the Developer level of the pranaymahendrakar page: the adapter is
+ * configured with lora_dropout = 0.05.  The pages give only the probability;
+ * the readings taken here (each listed in the design notes):
+ *  - inverted dropout on the adapter's input only: Xa = keep ? bf16_rne(fl32(x q)) : 0,
+ *    q = fl32(1 / (1 - p)) (one binary64 division, rounded once); the base
+ *    product reads the undropped X;
+ *  - its derivative is the straight-through keep * q (the rounding to bf16 is
+ *    not differentiated), so dX gets G = keep * q on the adapter term;
+ *  - keep decisions come from the counter-based generator Philox4x32-10
+ *    (J. K. Salmon, M. A. Moraes, R. O. Dror, D. E. Shaw, "Parallel random
+ *    numbers: as easy as 1, 2, 3", SC 2011).  X is viewed as a flat row-major
+ *    array; its 8-element chunk c = (t K + k) / 8 is one generator call with
+ *    counter (c mod 2^32, c div 2^32, offset mod 2^32, offset div 2^32) and key
+ *    (seed mod 2^32, seed div 2^32).  Element i of the chunk takes the 16-bit
+ *    draw h_i = bits 16 (i mod 2) .. +15 of output word i div 2 and is kept
+ *    iff h_i >= D, D = round_half_even(p 65536);
+ *  - the keep flags are stored as bits: bit i of byte c.
+ */
+
+/* Philox4x32 with 10 rounds: each round multiplies words 0 and 2 by the two
+ * round constants, keeping both halves of the 64-bit products, mixes the high
+ * halves with words 1 and 3 and the key by exclusive or, and swaps the
+ * pairs; the key is advanced by the two Weyl constants between rounds. */
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  uint32_t x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3];
+  uint32_t k0 = key[0], k1 = key[1];
+  for (int round = 0; round < 10; ++round) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * x0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * x2;
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    const uint32_t y0 = hi1 ^ x1 ^ k0, y1 = lo1, y2 = hi0 ^ x3 ^ k1, y3 = lo0;
+    x0 = y0;
+    x1 = y1;
+    x2 = y2;
+    x3 = y3;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  out[0] = x0;
+  out[1] = x1;
+  out[2] = x2;
+  out[3] = x3;
+}
+
+/* Drop threshold D for probability p (0 <= p < 1). */
+uint32_t oracle_dropout_threshold(double p) { return (uint32_t)nearbyint(p * 65536.0); }
+
+/* Keep bits of n_chunks 8-element chunks (n_chunks = T K / 8). */
+void oracle_dropout_mask(int64_t n_chunks, double p, uint64_t seed, uint64_t offset, uint8_t *mask) {
+  const uint32_t D = oracle_dropout_threshold(p);
+  const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+#pragma omp parallel for schedule(static)
+  for (int64_t c = 0; c < n_chunks; ++c) {
+    const uint32_t ctr[4] = {(uint32_t)c, (uint32_t)((uint64_t)c >> 32), (uint32_t)offset, (uint32_t)(offset >> 32)};
+    uint32_t o[4];
+    oracle_philox4x32_10(ctr, key, o);
+    uint8_t byte = 0;
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t h = (o[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      if (h >= D) byte |= (uint8_t)(1u << i);
+    }
+    mask[c] = byte;
+  }
+}
+
+/* Xa as bf16 bits and G = keep * q in binary64, from X (bf16 bits) and the keep bits. */
+void oracle_dropout_apply(const uint16_t *X, int64_t n, const uint8_t *mask, double p, uint16_t *Xa, double *G) {
+  const float q = (float)(1.0 / (1.0 - p));
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    const int keep = (mask[i >> 3] >> (i & 7)) & 1;
+    uint32_t u = (uint32_t)X[i] << 16;
+    float x;
+    memcpy(&x, &u, 4);
+    if (Xa) Xa[i] = keep ? f32_to_bf16_rne(x * q) : 0;
+    if (G) G[i] = keep ? (double)q : 0.0;
+  }
 }
