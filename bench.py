@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--wide", action="store_true", help="28672x8192 instead of 8192x8192 for small_token")
     ap.add_argument("--copies", type=int, default=0,
                     help="rotating input/weight copies; default: enough for 512 MB, twice the 256 MB MALL")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="LoRA dropout probability on the adapter input (training configs; default 0: none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -186,11 +188,15 @@ def cpu_baseline(inp, train: bool, target_s: float):
     dt = run(ts)
     ts = int(max(1, min(T, ts * target_s / max(dt, 1e-3))))
     dt = run(ts)
-    fl = flops_linear(ts, n_out, n_in, r, train)
+    reps = 1
+    while dt < 0.5 * target_s and ts == T:  # the whole batch is quicker than the target: repeat the pass
+        dt += run(ts)
+        reps += 1
+    fl = reps * flops_linear(ts, n_out, n_in, r, train)
     kind = "fwd+bwd" if train else "fwd"
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{kind} of the {n_out}x{n_in} linear on the first {ts} of {T} tokens "
-                      f"({dt:.1f} s, binary64 C oracle, OpenMP)", "seconds": dt, "tokens": ts}
+            "sample": f"{reps} x {kind} of the {n_out}x{n_in} linear on the first {ts} of {T} tokens "
+                      f"({dt:.1f} s, binary64 C oracle, OpenMP)", "seconds": dt, "tokens": ts, "passes": reps}
 
 
 def flops_linear(T, N, K, r, train):
@@ -240,6 +246,10 @@ def main():
         return
 
     lins, T, r, alpha, outliers, train = linears_for(args)
+    drop = args.dropout
+    if drop and (not train or not 0.0 < drop < 1.0):
+        print("--dropout needs a training config and 0 < p < 1", file=sys.stderr)
+        sys.exit(2)
     if args.copies <= 0:  # rotate through >= 512 MB so that a step does not find the previous one's lines cached
         per_copy = sum(weight_bytes(n, k) + 2 * T * (n + k) * (2 if train else 1) for _, n, k in lins)
         args.copies = int(min(32, max(2, -(-(512 << 20) // per_copy))))
@@ -267,17 +277,24 @@ def main():
             copies.append(dict(w=wc, X=X if c == 0 else X.clone(), dY=(dY if c == 0 else dY.clone()) if train else None,
                                Y=torch.empty((T, n_out), dtype=torch.bfloat16, device=dev),
                                U=torch.empty((T, r), dtype=torch.bfloat16, device=dev),
-                               dX=torch.empty((T, n_in), dtype=torch.bfloat16, device=dev) if train else None))
+                               dX=torch.empty((T, n_in), dtype=torch.bfloat16, device=dev) if train else None,
+                               mask=torch.empty((T, n_in // 8), dtype=torch.uint8, device=dev) if drop else None))
         layers.append(dict(name=name, n_out=n_out, n_in=n_in, A=A, B=Bm, copies=copies,
                            dA=torch.empty_like(A), dB=torch.empty_like(Bm),
-                           ws_f=torch.empty(max(1, B.workspace_bytes(B.OP_FWD, T, n_out, n_in, r)), dtype=torch.uint8,
-                                            device=dev),
+                           ws_f=torch.empty(max(1, B.workspace_bytes(B.OP_FWD_DROPOUT if drop else B.OP_FWD, T,
+                                                                     n_out, n_in, r)), dtype=torch.uint8, device=dev),
                            ws_b=torch.empty(max(1, B.workspace_bytes(B.OP_BWD, T, n_out, n_in, r)), dtype=torch.uint8,
                                             device=dev) if train else None))
 
     def step(i):
         for L in layers:
             c = L["copies"][i % len(L["copies"])]
+            if drop:  # a fresh mask per step: the step index is the generator offset
+                B.linear_fwd_dropout(c["X"], c["w"], L["A"], L["B"], alpha, drop, seed=2024, offset=i, ws=L["ws_f"],
+                                     out=c["Y"], u_out=c["U"], mask_out=c["mask"])
+                B.linear_bwd_dropout(c["X"], c["dY"], c["w"], L["A"], L["B"], alpha, drop, c["mask"], U=c["U"],
+                                     ws=L["ws_b"], outs=(c["dX"], L["dA"], L["dB"]))
+                continue
             B.linear_fwd(c["X"], c["w"], L["A"], L["B"], alpha, ws=L["ws_f"], out=c["Y"], u_out=c["U"])
             if train:
                 B.linear_bwd(c["X"], c["dY"], c["w"], L["A"], L["B"], alpha, U=c["U"], ws=L["ws_b"],
@@ -335,6 +352,8 @@ def main():
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     kd = kernels[dom]
     wl = args.config if args.config != "small_token" else f"small_token_{lins[0][1]}x8192_T{T}"
+    if drop:
+        wl += f"_dropout{drop:g}"
     traffic = traffic_from_profiles(dom, wl)
     if train or T > 80:
         roof = {"bound": "mfma", "achieved": kd["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -351,6 +370,8 @@ def main():
         cpu = cpu_baseline(first_inp, train, args.cpu_seconds)
 
     text = WORKLOAD_TEXT[args.config].format(n=lins[0][1], t=T)
+    if drop:
+        text += f", LoRA dropout p={drop:g}"
     line = {
         "metric": METRIC,
         "value": tflops,
@@ -365,7 +386,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": text, "name": wl, "tokens": T, "rank": r, "alpha": alpha,
-                   "pass": "fwd+bwd" if train else "fwd",
+                   "pass": "fwd+bwd" if train else "fwd", "lora_dropout": drop,
                    "linears": [[L["name"], L["n_out"], L["n_in"]] for L in layers],
                    "parallelism": "single GPU"},
         "weight_stream_GBps": wgbps,

@@ -6,7 +6,7 @@ in the library's gfx950 kernels.  There is no CPU or PyTorch fallback: if the
 library is missing or the device is not gfx950, calls raise.
 
 Names follow the C ABI: ``quantize_nf4``, ``dequant``, ``linear_fwd``,
-``linear_bwd``, plus ``QLoRALinearFn`` (a torch.autograd.Function whose backward
+``linear_bwd``, ``linear_fwd_dropout``, ``linear_bwd_dropout``, plus ``QLoRALinearFn`` (a torch.autograd.Function whose backward
 returns gradients for X, A and B and none for the frozen NF4 weight).
 """
 from __future__ import annotations
@@ -27,6 +27,7 @@ QLORA_ENODEV = -3
 QLORA_EHIP = -4
 OP_FWD = 0
 OP_BWD = 1
+OP_FWD_DROPOUT = 2
 MAX_RANK = 128
 
 EXPORTED = (
@@ -37,6 +38,8 @@ EXPORTED = (
     "qlora_dequant",
     "qlora_linear_fwd",
     "qlora_linear_bwd",
+    "qlora_linear_fwd_dropout",
+    "qlora_linear_bwd_dropout",
     "qlora_strerror",
     "qlora_last_error",
     "qlora_timing_enable",
@@ -81,6 +84,10 @@ def load_library() -> ctypes.CDLL:
         "qlora_dequant": ([pnf4, P, P], ctypes.c_int),
         "qlora_linear_fwd": ([P, i64, pnf4, P, P, i32, ctypes.c_float, P, P, P, sz, P], ctypes.c_int),
         "qlora_linear_bwd": ([P, P, i64, pnf4, P, P, i32, ctypes.c_float, P, P, P, P, P, sz, P], ctypes.c_int),
+        "qlora_linear_fwd_dropout": ([P, i64, pnf4, P, P, i32, ctypes.c_float, ctypes.c_float, ctypes.c_uint64,
+                                      ctypes.c_uint64, P, P, P, P, sz, P], ctypes.c_int),
+        "qlora_linear_bwd_dropout": ([P, P, i64, pnf4, P, P, i32, ctypes.c_float, ctypes.c_float, P, P, P, P, P, P,
+                                      sz, P], ctypes.c_int),
         "qlora_strerror": ([ctypes.c_int], ctypes.c_char_p),
         "qlora_last_error": ([], ctypes.c_char_p),
         "qlora_timing_enable": ([ctypes.c_char_p, ctypes.c_int], ctypes.c_int),
@@ -233,6 +240,61 @@ def linear_bwd(X: torch.Tensor, dY: torch.Tensor, w: NF4Weight, A: torch.Tensor,
     _check(load_library().qlora_linear_bwd(_ptr(X), _ptr(dY), T, ctypes.byref(st), _ptr(A), _ptr(B), r, float(alpha),
                                            _ptr(U), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws), nb, _stream(X.device)),
            "qlora_linear_bwd")
+    return dX, dA, dB
+
+
+def linear_fwd_dropout(X: torch.Tensor, w: NF4Weight, A: torch.Tensor, B: torch.Tensor, alpha: float, p: float,
+                       seed: int, offset: int = 0, save_u: bool = True, ws: torch.Tensor | None = None,
+                       out: torch.Tensor | None = None, u_out: torch.Tensor | None = None,
+                       mask_out: torch.Tensor | None = None):
+    """Forward with LoRA dropout on the adapter input; returns (Y, U or None, keep-bit mask uint8 [T, n_in/8])."""
+    X, A, B = _bits(X), _bits(A), _bits(B)
+    T, r = X.shape[0], A.shape[0]
+    if X.shape[1] != w.n_in or A.shape != (r, w.n_in) or B.shape != (w.n_out, r):
+        raise ValueError("shape mismatch in linear_fwd_dropout")
+    Y = out if out is not None else torch.empty((T, w.n_out), dtype=torch.bfloat16, device=X.device)
+    U = u_out if u_out is not None else (torch.empty((T, r), dtype=torch.bfloat16, device=X.device) if save_u else None)
+    mask = mask_out if mask_out is not None else torch.empty((T, w.n_in // 8), dtype=torch.uint8, device=X.device)
+    if ws is None:
+        ws, nb = _workspace(OP_FWD_DROPOUT, T, w, r)
+    else:
+        nb = ws.numel()
+    st = w.struct()
+    _check(load_library().qlora_linear_fwd_dropout(_ptr(X), T, ctypes.byref(st), _ptr(A), _ptr(B), r, float(alpha),
+                                                   float(p), int(seed) & (2**64 - 1), int(offset) & (2**64 - 1),
+                                                   _ptr(mask), _ptr(Y), _ptr(U), _ptr(ws), nb, _stream(X.device)),
+           "qlora_linear_fwd_dropout")
+    return Y, U, mask
+
+
+def linear_bwd_dropout(X: torch.Tensor, dY: torch.Tensor, w: NF4Weight, A: torch.Tensor, B: torch.Tensor,
+                       alpha: float, p: float, mask: torch.Tensor, U: torch.Tensor | None = None,
+                       need_dx: bool = True, ws: torch.Tensor | None = None, outs: tuple | None = None):
+    """Gradients (dX or None, dA, dB) of ``linear_fwd_dropout`` given its keep-bit mask."""
+    X, dY, A, B = _bits(X), _bits(dY), _bits(A), _bits(B)
+    if U is not None:
+        U = _bits(U)
+    T, r = X.shape[0], A.shape[0]
+    if dY.shape != (T, w.n_out) or A.shape != (r, w.n_in) or B.shape != (w.n_out, r):
+        raise ValueError("shape mismatch in linear_bwd_dropout")
+    if mask.dtype != torch.uint8 or not mask.is_cuda or mask.numel() != T * w.n_in // 8:
+        raise ValueError("mask must be a uint8 GPU tensor of T * n_in / 8 bytes")
+    mask = mask.contiguous()
+    if outs is not None:
+        dX, dA, dB = outs
+    else:
+        dX = torch.empty_like(X) if need_dx else None
+        dA = torch.empty_like(A)
+        dB = torch.empty_like(B)
+    if ws is None:
+        ws, nb = _workspace(OP_BWD, T, w, r)
+    else:
+        nb = ws.numel()
+    st = w.struct()
+    _check(load_library().qlora_linear_bwd_dropout(_ptr(X), _ptr(dY), T, ctypes.byref(st), _ptr(A), _ptr(B), r,
+                                                   float(alpha), float(p), _ptr(mask), _ptr(U), _ptr(dX), _ptr(dA),
+                                                   _ptr(dB), _ptr(ws), nb, _stream(X.device)),
+           "qlora_linear_bwd_dropout")
     return dX, dA, dB
 
 

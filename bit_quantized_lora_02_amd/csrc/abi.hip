@@ -234,10 +234,10 @@ Plan make_plan(int op, int64_t T, int64_t N, int64_t K, int32_t r) {
   p.off_v = off;  // fwd: V = bf16(s U) padded; bwd: U padded
   off = up(off + (size_t)(T * p.rp * 2), kAlign);
   size_t part = 0;
-  if (op == QLORA_OP_FWD) {
+  if (op == QLORA_OP_FWD || op == QLORA_OP_FWD_DROPOUT) {
     p.su = plan_skinny(T, K);
     part = (size_t)p.su.n * T * p.rn * 4;
-    if (use_gemv(T, K)) {
+    if (op == QLORA_OP_FWD && use_gemv(T, K)) {  // dropout needs the adapter input's own pass
       p.gemv = true;
       nf4_gemv_plan(T, N, K, &p.gemv_rg, &p.gemv_w, &p.gemv_split, &p.gemv_main);
       part = up((size_t)p.gemv_split * T * N * 4, kAlign);
@@ -273,6 +273,27 @@ int check_lora_args(int64_t T, const qlora_nf4 *q, const void *A, const void *B,
   if (!A || !B) return fail(QLORA_EINVAL, "A and B must not be NULL");
   if (!aligned16(A) || !aligned16(B)) return fail(QLORA_EINVAL, "A and B must be 16-byte aligned");
   return QLORA_OK;
+}
+
+// Dropout probability p in [0, 1): drop threshold D = round_half_even(p 65536)
+// on 16-bit draws, scale q = fl32(1 / (1 - p)).
+int check_dropout(float p, const void *mask, int64_t T) {
+  if (!(p >= 0.f && p < 1.f)) return fail(QLORA_EINVAL, "dropout probability must be in [0, 1) (got %g)", (double)p);
+  if (T > 0 && !mask) return fail(QLORA_EINVAL, "the keep-bit mask must not be NULL");
+  if (mask && !aligned16(mask)) return fail(QLORA_EINVAL, "the keep-bit mask must be 16-byte aligned");
+  return QLORA_OK;
+}
+
+DropParams drop_params(float p, uint8_t *mask, uint64_t seed, uint64_t offset) {
+  DropParams d;
+  d.mask = mask;
+  d.thr = (uint32_t)nearbyint((double)p * 65536.0);
+  d.q = (float)(1.0 / (1.0 - (double)p));
+  d.key0 = (uint32_t)seed;
+  d.key1 = (uint32_t)(seed >> 32);
+  d.off0 = (uint32_t)offset;
+  d.off1 = (uint32_t)(offset >> 32);
+  return d;
 }
 
 int check_ws(int op, int64_t T, int64_t N, int64_t K, int32_t r, const void *ws, size_t ws_bytes, Plan *p) {
@@ -323,7 +344,8 @@ int qlora_nf4_codebook(float levels[16]) {
 
 int qlora_workspace_bytes(int op, int64_t T, int64_t n_out, int64_t n_in, int32_t r, size_t *bytes) {
   if (!bytes) return fail(QLORA_EINVAL, "bytes is NULL");
-  if (op != QLORA_OP_FWD && op != QLORA_OP_BWD) return fail(QLORA_EINVAL, "unknown op %d", op);
+  if (op != QLORA_OP_FWD && op != QLORA_OP_BWD && op != QLORA_OP_FWD_DROPOUT)
+    return fail(QLORA_EINVAL, "unknown op %d", op);
   if (T < 0 || T > kMaxDim || n_out < 8 || n_out % 8 != 0 || n_out > kMaxDim || n_in < 64 || n_in % 64 != 0 ||
       n_in > kMaxDim || r < 1 || r > QLORA_MAX_RANK)
     return fail(QLORA_EINVAL, "bad sizes T=%lld n_out=%lld n_in=%lld r=%d", (long long)T, (long long)n_out,
@@ -353,9 +375,14 @@ int qlora_dequant(const qlora_nf4 *q, qlora_bf16 *W_out, void *stream) {
   return QLORA_OK;
 }
 
-int qlora_linear_fwd(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const qlora_bf16 *A, const qlora_bf16 *B,
-                     int32_t r, float alpha, qlora_bf16 *Y, qlora_bf16 *U_out, void *ws, size_t ws_bytes,
-                     void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Forward, without dropout (drop == NULL) or with it.
+int linear_fwd(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const qlora_bf16 *A, const qlora_bf16 *B,
+               int32_t r, float alpha, const DropParams *drop, qlora_bf16 *Y, qlora_bf16 *U_out, void *ws,
+               size_t ws_bytes, void *stream) {
   int rc = check_lora_args(T, q, A, B, r, alpha);
   if (rc) return rc;
   if (T > 0 && (!X || !Y)) return fail(QLORA_EINVAL, "X and Y must not be NULL");
@@ -363,7 +390,7 @@ int qlora_linear_fwd(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const q
     return fail(QLORA_EINVAL, "X, Y and U_out must be 16-byte aligned");
   const int64_t N = q->n_out, K = q->n_in;
   Plan p;
-  if ((rc = check_ws(QLORA_OP_FWD, T, N, K, r, ws, ws_bytes, &p))) return rc;
+  if ((rc = check_ws(drop ? QLORA_OP_FWD_DROPOUT : QLORA_OP_FWD, T, N, K, r, ws, ws_bytes, &p))) return rc;
   if ((rc = check_device(nullptr))) return rc;
   if (T == 0) return QLORA_OK;
   hipStream_t s = (hipStream_t)stream;
@@ -380,7 +407,11 @@ int qlora_linear_fwd(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const q
     LAUNCH("gemv_finish", launch_gemv_finish(part, upart, p.gemv_split, T, N, B, r, sc, Y, U_out, s));
     return QLORA_OK;
   }
-  LAUNCH("lora_u", launch_skinny(false, false, p.rn, X, K, T, A, K, r, K, p.su.kchunk, p.su.n, part, s));
+  if (drop)  // U = Xd A^T, drawing the keep bits of X on the way
+    LAUNCH("lora_u_dropout", launch_skinny(false, false, p.rn, X, K, T, A, K, r, K, p.su.kchunk, p.su.n, part, s,
+                                           DROP_GENERATE, *drop));
+  else
+    LAUNCH("lora_u", launch_skinny(false, false, p.rn, X, K, T, A, K, r, K, p.su.kchunk, p.su.n, part, s));
   LAUNCH("lora_u_finalize",
          launch_finalize(part, p.su.n, T, p.rn, U_out, r, U_out ? r : 0, 1.0f, V, p.rp, p.rp, r, sc, s));
   // B is read in place when its rows are 16-byte multiples, else from a zero-padded copy
@@ -392,9 +423,10 @@ int qlora_linear_fwd(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const q
   return QLORA_OK;
 }
 
-int qlora_linear_bwd(const qlora_bf16 *X, const qlora_bf16 *dY, int64_t T, const qlora_nf4 *q, const qlora_bf16 *A,
-                     const qlora_bf16 *B, int32_t r, float alpha, const qlora_bf16 *U, qlora_bf16 *dX,
-                     qlora_bf16 *dA, qlora_bf16 *dB, void *ws, size_t ws_bytes, void *stream) {
+// Backward, without dropout (drop == NULL) or with the keep bits in drop->mask.
+int linear_bwd(const qlora_bf16 *X, const qlora_bf16 *dY, int64_t T, const qlora_nf4 *q, const qlora_bf16 *A,
+               const qlora_bf16 *B, int32_t r, float alpha, const DropParams *drop, const qlora_bf16 *U,
+               qlora_bf16 *dX, qlora_bf16 *dA, qlora_bf16 *dB, void *ws, size_t ws_bytes, void *stream) {
   int rc = check_lora_args(T, q, A, B, r, alpha);
   if (rc) return rc;
   if (!dA || !dB) return fail(QLORA_EINVAL, "dA and dB must not be NULL");
@@ -436,7 +468,11 @@ int qlora_linear_bwd(const qlora_bf16 *X, const qlora_bf16 *dY, int64_t T, const
     ldu = p.rp;
     rvu = p.rv;
   } else if (!U) {
-    LAUNCH("lora_u", launch_skinny(false, false, p.rn, X, K, T, A, K, r, K, p.su.kchunk, p.su.n, part, s));
+    if (drop)
+      LAUNCH("lora_u_dropout", launch_skinny(false, false, p.rn, X, K, T, A, K, r, K, p.su.kchunk, p.su.n, part, s,
+                                             DROP_APPLY, *drop));
+    else
+      LAUNCH("lora_u", launch_skinny(false, false, p.rn, X, K, T, A, K, r, K, p.su.kchunk, p.su.n, part, s));
     LAUNCH("lora_u_finalize",
            launch_finalize(part, p.su.n, T, p.rn, nullptr, 0, 0, 0.f, Up, p.rp, p.rp, r, 1.0f, s));
     Usrc = Up;
@@ -451,16 +487,56 @@ int qlora_linear_bwd(const qlora_bf16 *X, const qlora_bf16 *dY, int64_t T, const
   LAUNCH("lora_db", launch_skinny(true, true, p.rn, dY, N, N, Usrc, ldu, rvu, T, p.sdb.kchunk, p.sdb.n, part, s));
   // dA^T = X^T dU  -> [K, r], stored transposed as dA [r, K]
   float *part2 = (float *)(w + p.off_part2);
-  LAUNCH("lora_da", launch_skinny(true, true, p.rn, X, K, K, dUp, p.rp, p.rv, T, p.sda.kchunk, p.sda.n, part2, s));
+  if (drop)  // dA^T = Xd^T dU
+    LAUNCH("lora_da_dropout", launch_skinny(true, true, p.rn, X, K, K, dUp, p.rp, p.rv, T, p.sda.kchunk, p.sda.n,
+                                            part2, s, DROP_APPLY, *drop));
+  else
+    LAUNCH("lora_da", launch_skinny(true, true, p.rn, X, K, K, dUp, p.rp, p.rv, T, p.sda.kchunk, p.sda.n, part2, s));
   // dB = s (sum of dB's partials), dA = (sum of dA's partials)^T, one launch
   LAUNCH("lora_dadb_finalize", launch_finalize_pair(part, p.sdb.n, N, p.rn, dB, r, r, sc, false, part2, p.sda.n, K,
                                                     p.rn, dA, K, r, 1.0f, true, s));
-  // dX = dY W' + dU A
+  // dX = dY W' + dU A   (with dropout: + (keep q) o (dU A))
   if (dX)
     LAUNCH("nf4_gemm_dx",
            launch_nf4_gemm_dx(nf4_gemm_pick_tile(T, K), dY, T, N, q->codes, q->absmax_q, q->absmax_step, K, dUp, A,
-                              r, p.rp, dX, lv, s));
+                              r, p.rp, dX, lv, s, drop ? drop->mask : nullptr, drop ? drop->q : 1.f));
   return QLORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qlora_linear_fwd(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const qlora_bf16 *A, const qlora_bf16 *B,
+                     int32_t r, float alpha, qlora_bf16 *Y, qlora_bf16 *U_out, void *ws, size_t ws_bytes,
+                     void *stream) {
+  return linear_fwd(X, T, q, A, B, r, alpha, nullptr, Y, U_out, ws, ws_bytes, stream);
+}
+
+int qlora_linear_bwd(const qlora_bf16 *X, const qlora_bf16 *dY, int64_t T, const qlora_nf4 *q, const qlora_bf16 *A,
+                     const qlora_bf16 *B, int32_t r, float alpha, const qlora_bf16 *U, qlora_bf16 *dX,
+                     qlora_bf16 *dA, qlora_bf16 *dB, void *ws, size_t ws_bytes, void *stream) {
+  return linear_bwd(X, dY, T, q, A, B, r, alpha, nullptr, U, dX, dA, dB, ws, ws_bytes, stream);
+}
+
+int qlora_linear_fwd_dropout(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const qlora_bf16 *A,
+                             const qlora_bf16 *B, int32_t r, float alpha, float p, uint64_t seed, uint64_t offset,
+                             uint8_t *mask_out, qlora_bf16 *Y, qlora_bf16 *U_out, void *ws, size_t ws_bytes,
+                             void *stream) {
+  int rc = check_dropout(p, mask_out, T);
+  if (rc) return rc;
+  const DropParams d = drop_params(p, mask_out, seed, offset);
+  return linear_fwd(X, T, q, A, B, r, alpha, &d, Y, U_out, ws, ws_bytes, stream);
+}
+
+int qlora_linear_bwd_dropout(const qlora_bf16 *X, const qlora_bf16 *dY, int64_t T, const qlora_nf4 *q,
+                             const qlora_bf16 *A, const qlora_bf16 *B, int32_t r, float alpha, float p,
+                             const uint8_t *mask, const qlora_bf16 *U, qlora_bf16 *dX, qlora_bf16 *dA,
+                             qlora_bf16 *dB, void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_dropout(p, mask, T);
+  if (rc) return rc;
+  const DropParams d = drop_params(p, const_cast<uint8_t *>(mask), 0, 0);  // read only on this path
+  return linear_bwd(X, dY, T, q, A, B, r, alpha, &d, U, dX, dA, dB, ws, ws_bytes, stream);
 }
 
 int qlora_timing_enable(const char *kernel, int enable) {

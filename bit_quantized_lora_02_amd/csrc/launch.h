@@ -43,9 +43,12 @@ hipError_t launch_nf4_gemm_fwd(int tile, const bf16_t *X, int64_t T, int64_t K, 
                                const uint8_t *absmax_q, const float *step, int64_t N, const bf16_t *V,
                                const bf16_t *Bp, int64_t ldb, int64_t r, int64_t rp, bf16_t *Y, const Levels &lv,
                                hipStream_t s);
+// dX = dY W' + G o (dUp A); with `mask` (keep bits of X, byte (t K + k) / 8,
+// bit k % 8) G = keep * q, without it G = 1.
 hipError_t launch_nf4_gemm_dx(int tile, const bf16_t *dY, int64_t T, int64_t N, const uint8_t *codes,
                               const uint8_t *absmax_q, const float *step, int64_t K, const bf16_t *dUp, const bf16_t *A,
-                              int64_t r, int64_t rp, bf16_t *dX, const Levels &lv, hipStream_t s);
+                              int64_t r, int64_t rp, bf16_t *dX, const Levels &lv, hipStream_t s,
+                              const uint8_t *mask = nullptr, float q = 1.f);
 
 // Small-token forward (T <= 64, n_in % 128 == 0): the split-K GEMV over the
 // weight (binary32 partials per K range, plus the partials of U = X A^T from
@@ -59,13 +62,25 @@ hipError_t launch_nf4_gemv(const bf16_t *X, int64_t T, int64_t K, const uint8_t 
 hipError_t launch_gemv_finish(const float *part, const float *upart, int nsplit, int64_t T, int64_t N,
                               const bf16_t *B, int64_t r, float s, bf16_t *Y, bf16_t *U_out, hipStream_t st);
 
+// Dropout on the adapter input P (a dense row-major [rows, ld] activation):
+// 8-element chunk c of P (flat element index / 8) has its keep bits in byte c
+// of `mask`; kept elements become bf16(fl32(x q)), dropped ones 0.
+enum { DROP_NONE = 0, DROP_GENERATE = 1, DROP_APPLY = 2 };
+struct DropParams {
+  uint8_t *mask = nullptr;  // DROP_GENERATE writes it, DROP_APPLY reads it
+  uint32_t thr = 0;         // a 16-bit draw below thr drops its element
+  float q = 1.f;            // fl32(1 / (1 - p))
+  uint32_t key0 = 0, key1 = 0, off0 = 0, off1 = 0;  // generator key and counter words 2, 3
+};
+
 // Skinny GEMM of the LoRA branch: C[split][m][j] (j < rn) over one reduction
 // chunk; pt / qt select the storage of the long operand P and the rank-wide
-// operand Q (see lora_gemm.hip).
+// operand Q (see lora_gemm.hip); `drop` (DROP_*) applies dropout to P.
 int skinny_rn(int64_t r);
 void skinny_plan(int64_t M, int64_t Kred, int *nsplit, int64_t *kchunk);
 hipError_t launch_skinny(bool pt, bool qt, int rn, const bf16_t *P, int64_t ldp, int64_t M, const bf16_t *Q,
-                         int64_t ldq, int64_t Rv, int64_t Kred, int64_t kchunk, int nsplit, float *C, hipStream_t s);
+                         int64_t ldq, int64_t Rv, int64_t Kred, int64_t kchunk, int nsplit, float *C, hipStream_t s,
+                         int drop = DROP_NONE, const DropParams &dp = DropParams());
 hipError_t launch_finalize(const float *part, int nsplit, int64_t M, int64_t N, bf16_t *out1, int64_t ld1, int64_t n1,
                            float scale1, bf16_t *out2, int64_t ld2, int64_t n2, int64_t nvalid2, float scale2,
                            hipStream_t s, bool trans1 = false);

@@ -30,6 +30,16 @@ namespace qlora {
 // Requirements: ldp, ldq, M (when PT = 1) and the valid Q columns Rv (when
 // QT = 1) are multiples of 8; reduction extents past Kred and rows past M
 // read as zero.
+//
+// LoRA dropout on P (DM != DROP_NONE; the adapter config of "Module 08 - QLoRA
+// & Quantization" (ainiketan.in), "4. QLoRA in code", sets lora_dropout =
+// 0.05).  P is then the dense layer input, and its 8-element chunk c (flat
+// element index / 8 -- exactly one 16-byte load here) keeps element i iff the
+// 16-bit draw i of Philox4x32-10 (Salmon et al., SC 2011) at counter
+// (c, offset), key seed, is at least thr; draw i is the low (i even) or high
+// half of output word i / 2.  Kept elements become bf16(fl32(x q)), dropped
+// ones zero.  DROP_GENERATE draws the bits and writes them to mask[c] (every
+// chunk is loaded by exactly one workgroup, once); DROP_APPLY reads them.
 namespace {
 typedef float f32x4s_t __attribute__((ext_vector_type(4)));
 typedef short s4_t __attribute__((ext_vector_type(4)));
@@ -48,12 +58,50 @@ __device__ __forceinline__ u32x4_t tr_read8(const bf16_t *base, int ld, int row0
 }
 constexpr int SK = 64;    // reduction step
 constexpr int SBM = 128;  // rows of M per workgroup
+
+// Keep bits of 8-element chunk `chunk`: Philox4x32 with 10 rounds -- each round
+// takes both halves of the 64-bit products of words 0 and 2 with the round
+// multipliers, folds the high halves into words 1 and 3 with the key, and
+// advances the key by the two Weyl increments.
+__device__ __forceinline__ uint32_t keep_bits8(uint64_t chunk, const DropParams &d) {
+  uint32_t x0 = (uint32_t)chunk, x1 = (uint32_t)(chunk >> 32), x2 = d.off0, x3 = d.off1;
+  uint32_t k0 = d.key0, k1 = d.key1;
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint32_t lo0 = 0xD2511F53u * x0, hi0 = __umulhi(0xD2511F53u, x0);
+    const uint32_t lo1 = 0xCD9E8D57u * x2, hi1 = __umulhi(0xCD9E8D57u, x2);
+    x0 = hi1 ^ x1 ^ k0;
+    x2 = hi0 ^ x3 ^ k1;
+    x1 = lo1;
+    x3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  const uint32_t w[4] = {x0, x1, x2, x3};
+  uint32_t bits = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) bits |= (((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) >= d.thr ? 1u : 0u) << i;
+  return bits;
+}
+
+// Eight bf16 values (element e in half e % 2 of word e / 2): kept ones scaled
+// by q and rounded to bf16 once, dropped ones zero.
+__device__ __forceinline__ u32x4_t apply_keep(const u32x4_t &v, uint32_t bits, float q) {
+  u32x4_t o;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float lo = ((bits >> (2 * w)) & 1u) ? __fmul_rn(bf16_lo_to_f32(v[w]), q) : 0.f;
+    const float hi = ((bits >> (2 * w + 1)) & 1u) ? __fmul_rn(bf16_hi_to_f32(v[w]), q) : 0.f;
+    o[w] = pack_bf16x2(lo, hi);
+  }
+  return o;
+}
 }  // namespace
 
-template <bool PT, bool QT, int RN>
+template <bool PT, bool QT, int RN, int DM>
 __global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, int64_t ldp, int64_t M,
                                                 const bf16_t *__restrict__ Q, int64_t ldq, int64_t Rv, int64_t Kred,
-                                                int64_t kchunk, float *__restrict__ C) {
+                                                int64_t kchunk, float *__restrict__ C, DropParams dp) {
   constexpr int LDP = PT ? SBM + 16 : SK;             // LDS row length of the P tile (elements)
   constexpr int LDQ = QT ? RN + (RN >= 32 ? 16 : 0) : SK;
   constexpr int P_ROWS = PT ? SK : SBM;
@@ -76,7 +124,8 @@ __global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, in
   };
   // two register slots (steps of even and odd index): the loads run two steps ahead
   u32x4_t rpA[P_CH], rqA[Q_CH], rpB[P_CH], rqB[Q_CH];
-  auto load = [&](int s, u32x4_t(&rp_)[P_CH], u32x4_t(&rq_)[Q_CH]) {
+  uint32_t kmA[P_CH], kmB[P_CH];  // keep bits of the P chunks (dropout only)
+  auto load = [&](int s, u32x4_t(&rp_)[P_CH], u32x4_t(&rq_)[Q_CH], uint32_t(&km_)[P_CH]) {
     const int64_t k0 = kb + (int64_t)s * SK;
 #pragma unroll
     for (int i = 0; i < P_CH; ++i) {
@@ -93,6 +142,12 @@ __global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, in
         src = P + m * ldp + k;
       }
       rp_[i] = ok ? *reinterpret_cast<const u32x4_t *>(src) : u32x4_t{0u, 0u, 0u, 0u};
+      if constexpr (DM == DROP_APPLY) km_[i] = ok ? (uint32_t)dp.mask[(src - P) >> 3] : 0u;
+      if constexpr (DM == DROP_GENERATE) {
+        const int64_t chunk = (src - P) >> 3;
+        km_[i] = keep_bits8((uint64_t)chunk, dp);
+        if (ok) dp.mask[chunk] = (uint8_t)km_[i];
+      }
     }
 #pragma unroll
     for (int i = 0; i < Q_CH; ++i) {
@@ -111,12 +166,13 @@ __global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, in
       rq_[i] = ok ? *reinterpret_cast<const u32x4_t *>(src) : u32x4_t{0u, 0u, 0u, 0u};
     }
   };
-  auto store = [&](int buf, const u32x4_t(&rp_)[P_CH], const u32x4_t(&rq_)[Q_CH]) {
+  auto store = [&](int buf, const u32x4_t(&rp_)[P_CH], const u32x4_t(&rq_)[Q_CH], const uint32_t(&km_)[P_CH]) {
 #pragma unroll
     for (int i = 0; i < P_CH; ++i) {
       int row, col;
       p_off(tid + 256 * i, row, col);
-      *reinterpret_cast<u32x4_t *>(&sP[buf][row * LDP + col]) = rp_[i];
+      *reinterpret_cast<u32x4_t *>(&sP[buf][row * LDP + col]) =
+          (DM == DROP_NONE) ? rp_[i] : apply_keep(rp_[i], km_[i], dp.q);
     }
 #pragma unroll
     for (int i = 0; i < Q_CH; ++i) {
@@ -167,19 +223,19 @@ __global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, in
   };
 
   if (nsteps > 0) {
-    load(0, rpA, rqA);
-    if (nsteps > 1) load(1, rpB, rqB);
-    store(0, rpA, rqA);
+    load(0, rpA, rqA, kmA);
+    if (nsteps > 1) load(1, rpB, rqB, kmB);
+    store(0, rpA, rqA, kmA);
     __syncthreads();
     for (int s = 0; s < nsteps; s += 2) {
-      if (s + 2 < nsteps) load(s + 2, rpA, rqA);
+      if (s + 2 < nsteps) load(s + 2, rpA, rqA, kmA);
       mma(0);
-      if (s + 1 < nsteps) store(1, rpB, rqB);
+      if (s + 1 < nsteps) store(1, rpB, rqB, kmB);
       __syncthreads();
       if (s + 1 >= nsteps) break;
-      if (s + 3 < nsteps) load(s + 3, rpB, rqB);
+      if (s + 3 < nsteps) load(s + 3, rpB, rqB, kmB);
       mma(1);
-      if (s + 2 < nsteps) store(0, rpA, rqA);
+      if (s + 2 < nsteps) store(0, rpA, rqA, kmA);
       __syncthreads();
     }
   }
@@ -317,26 +373,36 @@ void skinny_plan(int64_t M, int64_t Kred, int *nsplit, int64_t *kchunk) {
   *nsplit = Kred > 0 ? (int)((Kred + *kchunk - 1) / *kchunk) : 0;
 }
 
-template <bool PT, bool QT>
+template <bool PT, bool QT, int DM>
 static hipError_t skinny_dispatch(int rn, dim3 grid, hipStream_t s, const bf16_t *P, int64_t ldp, int64_t M,
-                            const bf16_t *Q, int64_t ldq, int64_t Rv, int64_t Kred, int64_t kchunk, float *C) {
+                                  const bf16_t *Q, int64_t ldq, int64_t Rv, int64_t Kred, int64_t kchunk, float *C,
+                                  const DropParams &dp) {
   switch (rn) {
-    case 16: launch((k_skinny<PT, QT, 16>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C); break;
-    case 32: launch((k_skinny<PT, QT, 32>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C); break;
-    case 64: launch((k_skinny<PT, QT, 64>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C); break;
-    default: launch((k_skinny<PT, QT, 128>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C); break;
+    case 16: launch((k_skinny<PT, QT, 16, DM>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp); break;
+    case 32: launch((k_skinny<PT, QT, 32, DM>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp); break;
+    case 64: launch((k_skinny<PT, QT, 64, DM>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp); break;
+    default: launch((k_skinny<PT, QT, 128, DM>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp); break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_skinny(bool pt, bool qt, int rn, const bf16_t *P, int64_t ldp, int64_t M, const bf16_t *Q,
-                         int64_t ldq, int64_t Rv, int64_t Kred, int64_t kchunk, int nsplit, float *C, hipStream_t s) {
+                         int64_t ldq, int64_t Rv, int64_t Kred, int64_t kchunk, int nsplit, float *C, hipStream_t s,
+                         int drop, const DropParams &dp) {
   if (M == 0 || nsplit == 0) return hipSuccess;
   dim3 grid((unsigned)((M + SBM - 1) / SBM), (unsigned)nsplit);
-  if (!pt && !qt) return skinny_dispatch<false, false>(rn, grid, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C);
-  if (!pt && qt) return skinny_dispatch<false, true>(rn, grid, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C);
-  if (pt && !qt) return skinny_dispatch<true, false>(rn, grid, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C);
-  return skinny_dispatch<true, true>(rn, grid, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C);
+  // dropout applies to the layer input: U = Xd A^T (P = X by rows) and dA^T = Xd^T dU (P = X by columns)
+  if (drop == DROP_GENERATE && !pt && !qt)
+    return skinny_dispatch<false, false, DROP_GENERATE>(rn, grid, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp);
+  if (drop == DROP_APPLY && !pt && !qt)
+    return skinny_dispatch<false, false, DROP_APPLY>(rn, grid, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp);
+  if (drop == DROP_APPLY && pt && qt)
+    return skinny_dispatch<true, true, DROP_APPLY>(rn, grid, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp);
+  if (drop != DROP_NONE) return hipErrorInvalidValue;
+  if (!pt && !qt) return skinny_dispatch<false, false, DROP_NONE>(rn, grid, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp);
+  if (!pt && qt) return skinny_dispatch<false, true, DROP_NONE>(rn, grid, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp);
+  if (pt && !qt) return skinny_dispatch<true, false, DROP_NONE>(rn, grid, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp);
+  return skinny_dispatch<true, true, DROP_NONE>(rn, grid, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp);
 }
 
 hipError_t launch_pad_copy(const bf16_t *in, int64_t ldi, int64_t ncols, int64_t M, bf16_t *out, int64_t ldo,

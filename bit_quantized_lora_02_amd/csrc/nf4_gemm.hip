@@ -432,14 +432,39 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
 // operand, which needs 8 consecutive n for one k_out, is read transposed.
 // Weight rows past N decode to zero, so the clamped activation columns they
 // meet contribute nothing.
+//
+// With LoRA dropout on the layer input (DROP), the adapter term is multiplied
+// elementwise by keep * q (the derivative of inverted dropout): the kernel
+// then forms dUp . A first, scales each accumulator element by its keep bit
+// times q, and accumulates dY . W' on top, so no second accumulator is needed.
+// Keep bit (t, k) is bit k % 8 of mask[(t K + k) / 8].
 template <class C>
+__device__ __forceinline__ void keep_scale_acc(f32x16_t acc[C::WM][C::WN], const uint8_t *__restrict__ mask,
+                                               int64_t K, int64_t m0, int64_t rows, int64_t n0, int wm, int wn,
+                                               int lane, float q) {
+#pragma unroll
+  for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) {
+      const int64_t col0 = n0 + (wn * C::WN + j) * 32;  // multiple of 32: one 32-bit word per row
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        int64_t row = m0 + (wm * C::WM + i) * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+        row = row < rows ? row : rows - 1;  // rows past T are never stored
+        const uint32_t w = col0 < K ? *reinterpret_cast<const uint32_t *>(mask + (row * K + col0) / 8) : 0u;
+        acc[i][j][e] = ((w >> (lane & 31)) & 1u) ? __fmul_rn(acc[i][j][e], q) : 0.f;
+      }
+    }
+}
+
+template <class C, bool DROP>
 __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict__ dY, int64_t T, int64_t N,
                                                        const uint8_t *__restrict__ codes,
                                                        const uint8_t *__restrict__ absmax_q,
                                                        const float *__restrict__ step, int64_t K,
                                                        const bf16_t *__restrict__ dUp, const bf16_t *__restrict__ A,
                                                        int64_t r, int64_t rp, bf16_t *__restrict__ dX, Levels lv,
-                                                       int xb_m, int xb_n) {
+                                                       int xb_m, int xb_n, const uint8_t *__restrict__ mask, float q) {
   constexpr int LDB = C::BN + 32;  // row length (elements) of the [64][BN] B tile: 16 banks mod 64 per row
   __shared__ __attribute__((aligned(16))) bf16_t sA0[C::BM * BK];
   __shared__ __attribute__((aligned(16))) bf16_t sA1[C::BM * BK];
@@ -475,6 +500,35 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
 
   f32x16_t acc[C::WM][C::WN];
   zero_acc<C>(acc);
+
+  // LoRA term: dUp [T, rp] . A [r, K], reduction over the rank (rows j of A)
+  auto lora_steps = [&]() {
+    for (int64_t k0 = 0; k0 < rp; k0 += BK) {
+      copy_a_tile<C>(dUp, rp, m0, T, k0, rp, tid, sA[0]);
+      constexpr int LCH = BK * C::BN / 8 / C::NT;  // 16-byte chunks of A per thread
+#pragma unroll
+      for (int i = 0; i < LCH; ++i) {
+        const int c = tid + C::NT * i;
+        const int64_t j = k0 + c / (C::BN / 8), kcol = n0 + (c % (C::BN / 8)) * 8;
+        const u32x4_t v =
+            (j < r && kcol < K) ? *reinterpret_cast<const u32x4_t *>(A + j * K + kcol) : u32x4_t{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4_t *>(sB[0] + (c / (C::BN / 8)) * LDB + (c % (C::BN / 8)) * 8) = v;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        u32x4_t a[C::WM], b[C::WN];
+        read_a<C>(sA[0], wm, lane, kk, a);
+        read_b_tr<C, LDB>(sB[0], wn, lane, kk, b);
+        mma_rows<C>(0, C::WM, a, b, acc);
+      }
+      __syncthreads();
+    }
+  };
+  if constexpr (DROP) {  // adapter term first, masked, then the base product on top
+    lora_steps();
+    keep_scale_acc<C>(acc, mask, K, m0, T, n0, wm, wn, lane, q);
+  }
 
   al.issue(0, N, sA[0]);
   load_words_of(0, rc[0], rs[0]);
@@ -513,28 +567,7 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
   }
   if (s < nk) step_p(std::integral_constant<int, 0>(), s);
 
-  // LoRA term: dUp [T, rp] . A [r, K], reduction over the rank (rows j of A)
-  for (int64_t k0 = 0; k0 < rp; k0 += BK) {
-    copy_a_tile<C>(dUp, rp, m0, T, k0, rp, tid, sA[0]);
-    constexpr int LCH = BK * C::BN / 8 / C::NT;  // 16-byte chunks of A per thread
-#pragma unroll
-    for (int i = 0; i < LCH; ++i) {
-      const int c = tid + C::NT * i;
-      const int64_t j = k0 + c / (C::BN / 8), kcol = n0 + (c % (C::BN / 8)) * 8;
-      const u32x4_t v =
-          (j < r && kcol < K) ? *reinterpret_cast<const u32x4_t *>(A + j * K + kcol) : u32x4_t{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4_t *>(sB[0] + (c / (C::BN / 8)) * LDB + (c % (C::BN / 8)) * 8) = v;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      u32x4_t a[C::WM], b[C::WN];
-      read_a<C>(sA[0], wm, lane, kk, a);
-      read_b_tr<C, LDB>(sB[0], wn, lane, kk, b);
-      mma_rows<C>(0, C::WM, a, b, acc);
-    }
-    __syncthreads();
-  }
+  if constexpr (!DROP) lora_steps();
   store_out<C>(dX, K, m0, T, n0, K, wm, wn, lane, acc);
 }
 
@@ -585,12 +618,16 @@ hipError_t fwd_with(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes,
 template <class C>
 hipError_t dx_with(const bf16_t *dY, int64_t T, int64_t N, const uint8_t *codes, const uint8_t *absmax_q,
                    const float *step, int64_t K, const bf16_t *dUp, const bf16_t *A, int64_t r, int64_t rp,
-                   bf16_t *dX, const Levels &lv, hipStream_t s) {
+                   bf16_t *dX, const Levels &lv, hipStream_t s, const uint8_t *mask, float q) {
   const int64_t tm = (T + C::BM - 1) / C::BM, tn = (K + C::BN - 1) / C::BN;
   int xb_m, xb_n;
   xcd_blocking(tm, tn, 2.0 * T * N, 0.516 * N * K, &xb_m, &xb_n);
-  launch(k_nf4_gemm_dx<C>, dim3((unsigned)(tm * tn)), dim3(C::NT), 0, s, dY, T, N, codes, absmax_q, step,
-                     K, dUp, A, r, rp, dX, lv, xb_m, xb_n);
+  if (mask)
+    launch(k_nf4_gemm_dx<C, true>, dim3((unsigned)(tm * tn)), dim3(C::NT), 0, s, dY, T, N, codes, absmax_q, step,
+           K, dUp, A, r, rp, dX, lv, xb_m, xb_n, mask, q);
+  else
+    launch(k_nf4_gemm_dx<C, false>, dim3((unsigned)(tm * tn)), dim3(C::NT), 0, s, dY, T, N, codes, absmax_q, step,
+           K, dUp, A, r, rp, dX, lv, xb_m, xb_n, mask, q);
   return hipGetLastError();
 }
 }  // namespace
@@ -622,14 +659,19 @@ hipError_t launch_nf4_gemm_fwd(int tile, const bf16_t *X, int64_t T, int64_t K, 
 
 hipError_t launch_nf4_gemm_dx(int tile, const bf16_t *dY, int64_t T, int64_t N, const uint8_t *codes,
                               const uint8_t *absmax_q, const float *step, int64_t K, const bf16_t *dUp, const bf16_t *A,
-                              int64_t r, int64_t rp, bf16_t *dX, const Levels &lv, hipStream_t s) {
+                              int64_t r, int64_t rp, bf16_t *dX, const Levels &lv, hipStream_t s,
+                              const uint8_t *mask, float q) {
   if (T == 0) return hipSuccess;
   switch (tile) {
-    case NF4_TILE_256x256_W8: return dx_with<T256x256w8>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s);
-    case NF4_TILE_256x128_W8: return dx_with<T256x128w8>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s);
-    case NF4_TILE_128x256_W8: return dx_with<T128x256w8>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s);
-    case NF4_TILE_128x128_W8: return dx_with<T128x128w8>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s);
-    default: return dx_with<T128x128>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s);
+    case NF4_TILE_256x256_W8:
+      return dx_with<T256x256w8>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s, mask, q);
+    case NF4_TILE_256x128_W8:
+      return dx_with<T256x128w8>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s, mask, q);
+    case NF4_TILE_128x256_W8:
+      return dx_with<T128x256w8>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s, mask, q);
+    case NF4_TILE_128x128_W8:
+      return dx_with<T128x128w8>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s, mask, q);
+    default: return dx_with<T128x128>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s, mask, q);
   }
 }
 

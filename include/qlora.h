@@ -54,6 +54,7 @@ typedef uint16_t qlora_bf16; /* bf16 bit pattern */
 
 #define QLORA_OP_FWD 0
 #define QLORA_OP_BWD 1
+#define QLORA_OP_FWD_DROPOUT 2 /* qlora_linear_fwd_dropout; its backward uses QLORA_OP_BWD */
 
 #define QLORA_MAX_RANK 128
 
@@ -94,7 +95,7 @@ int qlora_nf4_storage(int64_t n_out, int64_t n_in, size_t *codes_bytes, size_t *
  * (katajob, "NF4": levels placed for a zero-centred normal). */
 int qlora_nf4_codebook(float levels[16]);
 
-/* Workspace bytes needed by `op` (QLORA_OP_FWD or QLORA_OP_BWD) for these
+/* Workspace bytes needed by `op` (QLORA_OP_FWD, QLORA_OP_BWD or QLORA_OP_FWD_DROPOUT) for these
  * sizes, into host *bytes (no HIP call).  The forward workspace is O(T*r + n_out*r),
  * never O(n_out*n_in): the dequantized weight is never stored. */
 int qlora_workspace_bytes(int op, int64_t T, int64_t n_out, int64_t n_in, int32_t r, size_t *bytes);
@@ -141,6 +142,49 @@ int qlora_linear_fwd(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const q
 int qlora_linear_bwd(const qlora_bf16 *X, const qlora_bf16 *dY, int64_t T, const qlora_nf4 *q, const qlora_bf16 *A,
                      const qlora_bf16 *B, int32_t r, float alpha, const qlora_bf16 *U, qlora_bf16 *dX,
                      qlora_bf16 *dA, qlora_bf16 *dB, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * LoRA dropout on the adapter input ("Module 08 - QLoRA & Quantization",
+ * ainiketan.in, "4. QLoRA in code", and the Developer level of the
+ * pranaymahendrakar page configure lora_dropout = 0.05).  Inverted dropout on
+ * the adapter branch only; the base product reads X itself:
+ *   Xd = keep o bf16(fl32(X q)),  q = fl32(1 / (1 - p))
+ *   U  = Xd . A^T
+ *   Y  = X . deq(W)^T + s . U . B^T
+ * Keep bits: X is viewed as a flat row-major array of T * n_in bf16 values;
+ * its 8-element chunk c (elements 8c .. 8c+7) is one Philox4x32-10 block
+ * (Salmon, Moraes, Dror, Shaw, SC 2011) with counter words
+ * (c mod 2^32, c div 2^32, offset mod 2^32, offset div 2^32) and key words
+ * (seed mod 2^32, seed div 2^32).  Element 8c+i takes the 16-bit draw formed by
+ * bits 16(i mod 2) .. 16(i mod 2)+15 of output word i div 2 and is kept iff the
+ * draw is >= D = round_half_even(p * 65536).  Bit i of byte c of mask_out is
+ * its keep flag.
+ * mask_out: device, [T * n_in / 8] bytes, 16-byte aligned, written completely
+ * (it is the backward's input).  0 <= p < 1 (p = 0 keeps everything).  Use
+ * `offset` to draw a fresh mask per step with one seed.  The workspace is
+ * qlora_workspace_bytes(QLORA_OP_FWD_DROPOUT, ...).  Other arguments and
+ * conventions as for qlora_linear_fwd.
+ */
+int qlora_linear_fwd_dropout(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const qlora_bf16 *A,
+                             const qlora_bf16 *B, int32_t r, float alpha, float p, uint64_t seed, uint64_t offset,
+                             uint8_t *mask_out, qlora_bf16 *Y, qlora_bf16 *U_out, void *ws, size_t ws_bytes,
+                             void *stream);
+
+/*
+ * Backward of qlora_linear_fwd_dropout (same p, the mask it wrote, and the U
+ * it saved or NULL to recompute U = Xd . A^T).  The derivative of the dropout
+ * is keep * q (straight through the rounding to bf16):
+ *   dU = s . dY . B
+ *   dA = dU^T . Xd
+ *   dB = s . dY^T . U
+ *   dX = dY . deq(W) + (keep q) o (dU . A)
+ * Workspace: qlora_workspace_bytes(QLORA_OP_BWD, ...).  Other arguments and
+ * conventions as for qlora_linear_bwd.
+ */
+int qlora_linear_bwd_dropout(const qlora_bf16 *X, const qlora_bf16 *dY, int64_t T, const qlora_nf4 *q,
+                             const qlora_bf16 *A, const qlora_bf16 *B, int32_t r, float alpha, float p,
+                             const uint8_t *mask, const qlora_bf16 *U, qlora_bf16 *dX, qlora_bf16 *dA,
+                             qlora_bf16 *dB, void *ws, size_t ws_bytes, void *stream);
 
 /* Static text for a QLORA_E* code. */
 const char *qlora_strerror(int code);

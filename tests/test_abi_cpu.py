@@ -151,6 +151,49 @@ def test_error_paths_backward(lib):
     assert _bwd(lib, nb=need - 1) == B.QLORA_EWORKSPACE
 
 
+def _fwd_drop(lib, X=FAKE, T=4, q=None, A=FAKE, Bm=FAKE, r=8, alpha=16.0, p=0.05, seed=1, offset=0, mask=FAKE,
+              Y=FAKE, U=None, ws=FAKE, nb=1 << 30):
+    q = q if q is not None else _nf4(64, 64)
+    return lib.qlora_linear_fwd_dropout(X, T, ctypes.byref(q), A, Bm, r, alpha, p, seed, offset, mask, Y, U, ws, nb,
+                                        None)
+
+
+def _bwd_drop(lib, X=FAKE, dY=FAKE, T=4, q=None, A=FAKE, Bm=FAKE, r=8, alpha=16.0, p=0.05, mask=FAKE, U=None,
+              dX=FAKE, dA=FAKE, dB=FAKE, ws=FAKE, nb=1 << 30):
+    q = q if q is not None else _nf4(64, 64)
+    return lib.qlora_linear_bwd_dropout(X, dY, T, ctypes.byref(q), A, Bm, r, alpha, p, mask, U, dX, dA, dB, ws, nb,
+                                        None)
+
+
+def test_error_paths_dropout(lib):
+    E = B.QLORA_EINVAL
+    for bad_p in (-0.1, 1.0, 1.5, float("nan")):
+        rc, msg = _err(lambda: _fwd_drop(lib, p=bad_p))
+        assert rc == E and "probability" in msg, (bad_p, msg)
+        assert _bwd_drop(lib, p=bad_p) == E
+    rc, msg = _err(lambda: _fwd_drop(lib, mask=None))
+    assert rc == E and "mask" in msg
+    assert _bwd_drop(lib, mask=None) == E
+    assert _fwd_drop(lib, mask=MIS) == E
+    assert _bwd_drop(lib, mask=MIS) == E
+    # the plain argument checks still apply
+    assert _fwd_drop(lib, X=None) == E
+    assert _bwd_drop(lib, dA=None) == E
+    need = B.workspace_bytes(B.OP_FWD_DROPOUT, 4, 64, 64, 8)
+    assert _fwd_drop(lib, nb=need - 1) == B.QLORA_EWORKSPACE
+    need = B.workspace_bytes(B.OP_BWD, 4, 64, 64, 8)
+    assert _bwd_drop(lib, nb=need - 1) == B.QLORA_EWORKSPACE
+
+
+def test_dropout_workspace_covers_the_skinny_path(lib):
+    """Few tokens take the GEMV path without dropout; with dropout the forward needs the split-K U pass."""
+    for T in (1, 16, 64, 65, 2048):
+        wd = B.workspace_bytes(B.OP_FWD_DROPOUT, T, 4096, 4096, 16)
+        assert wd > 0
+        if T > 64:
+            assert wd == B.workspace_bytes(B.OP_FWD, T, 4096, 4096, 16)
+
+
 def test_strerror(lib):
     for code in (0, -1, -2, -3, -4):
         assert lib.qlora_strerror(code)
@@ -164,6 +207,8 @@ def test_no_device_is_reported(lib):
     assert lib.qlora_quantize_nf4(FAKE, ctypes.byref(q), None) == B.QLORA_ENODEV
     assert _fwd(lib) == B.QLORA_ENODEV
     assert _bwd(lib) == B.QLORA_ENODEV
+    assert _fwd_drop(lib) == B.QLORA_ENODEV
+    assert _bwd_drop(lib) == B.QLORA_ENODEV
 
 
 def test_timing_api_host_only(lib):
