@@ -72,6 +72,9 @@ def _load():
     lib.oracle_dropout_mask.restype = None
     lib.oracle_dropout_apply.argtypes = [P, i64, P, ctypes.c_double, P, P]
     lib.oracle_dropout_apply.restype = None
+    d = ctypes.c_double
+    lib.oracle_adamw_step.argtypes = [P, P, P, P, i64, d, d, d, d, d, i64]
+    lib.oracle_adamw_step.restype = None
     _lib = lib
     return lib
 
@@ -285,3 +288,15 @@ def linear_bwd_dropout(X_bits, dY, Wdq, A, B, alpha: float, mask, p: float, rows
     """Backward of ``linear_fwd_dropout``: (dX or None, dA, dB) in binary64."""
     Xa, G = dropout_apply(X_bits, mask, p)
     return linear_bwd_xa(np.ascontiguousarray(X_bits, np.uint16), Xa, G, dY, Wdq, A, B, alpha, rows, want_dx)
+
+
+# ------------------------------------------------------------------ AdamW
+
+def adamw_step(theta: np.ndarray, g, m: np.ndarray, v: np.ndarray, lr: float, beta1: float, beta2: float,
+               eps: float, weight_decay: float, step: int):
+    """One AdamW step in binary64, in place on theta, m and v (float64 arrays); g as floats or bf16 bits."""
+    g = np.ascontiguousarray(_f64(g).reshape(-1))
+    for a in (theta, m, v):
+        assert a.dtype == np.float64 and a.flags.c_contiguous and a.size == g.size
+    _load().oracle_adamw_step(_ptr(theta), _ptr(g), _ptr(m), _ptr(v), g.size, float(lr), float(beta1), float(beta2),
+                              float(eps), float(weight_decay), int(step))

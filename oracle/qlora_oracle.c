@@ -26,6 +26,9 @@
  *  [STEPS] "qlora" glossary (chipfoundryservices), table "How QLoRA Works":
  *         quantize at load (4-bit), forward dequantizes then computes, backward
  *         in bfloat16, only the adapter is updated.
+ *  [OPT]  katajob, "What stays in full precision" (A and B keep ordinary AdamW
+ *         state) and pranaymahendrakar, Developer level, "The walkthrough" (about
+ *         8 bytes of Adam state per trainable parameter).
  *  [DROP] "Module 08 - QLoRA & Quantization" (ainiketan), "4. QLoRA in code":
  *         the adapter config sets lora_dropout = 0.05 (so does the Developer
  *         level of the pranaymahendrakar page).
@@ -440,5 +443,31 @@ void oracle_dropout_apply(const uint16_t *X, int64_t n, const uint8_t *mask, dou
     memcpy(&x, &u, 4);
     if (Xa) Xa[i] = keep ? f32_to_bf16_rne(x * q) : 0;
     if (G) G[i] = keep ? (double)q : 0.0;
+  }
+}
+
+/* ------------------------------------------------------------------ AdamW */
+
+/*
+ * [OPT] katajob, "What stays in full precision": A and B are bf16 tensors with
+ * ordinary AdamW state; pranaymahendrakar, Developer level, "The walkthrough":
+ * Adam keeps about 8 bytes per trainable parameter (two binary32 moments).
+ * AdamW is Adam with weight decay decoupled from the gradient (I. Loshchilov,
+ * F. Hutter, "Decoupled Weight Decay Regularization", ICLR 2019), here with a
+ * constant schedule multiplier.  One step t >= 1 over n parameters, all in
+ * binary64:
+ *   m     <- b1 m + (1 - b1) g
+ *   v     <- b2 v + (1 - b2) g^2
+ *   theta <- theta - lr (wd theta + (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps))
+ * (the decay term uses the parameter before the step).  theta, m, v in place.
+ */
+void oracle_adamw_step(double *theta, const double *g, double *m, double *v, int64_t n, double lr, double b1,
+                       double b2, double eps, double wd, int64_t t) {
+  const double bc1 = 1.0 - pow(b1, (double)t), bc2 = 1.0 - pow(b2, (double)t);
+  for (int64_t i = 0; i < n; ++i) {
+    m[i] = b1 * m[i] + (1.0 - b1) * g[i];
+    v[i] = b2 * v[i] + (1.0 - b2) * g[i] * g[i];
+    const double mhat = m[i] / bc1, vhat = v[i] / bc2;
+    theta[i] = theta[i] - lr * (wd * theta[i] + mhat / (sqrt(vhat) + eps));
   }
 }
