@@ -51,6 +51,8 @@ def parse():
                     help="rotating input/weight copies; default: enough for 512 MB, twice the 256 MB MALL")
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="LoRA dropout probability on the adapter input (training configs; default 0: none)")
+    ap.add_argument("--adamw", action="store_true",
+                    help="end each training step with the fused AdamW update of every A and B (timed as 'adamw')")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -281,12 +283,19 @@ def main():
                                mask=torch.empty((T, n_in // 8), dtype=torch.uint8, device=dev) if drop else None))
         layers.append(dict(name=name, n_out=n_out, n_in=n_in, A=A, B=Bm, copies=copies,
                            dA=torch.empty_like(A), dB=torch.empty_like(Bm),
+                           adam=[B.AdamState.zeros_like(A), B.AdamState.zeros_like(Bm)] if args.adamw else None,
                            ws_f=torch.empty(max(1, B.workspace_bytes(B.OP_FWD_DROPOUT if drop else B.OP_FWD, T,
                                                                      n_out, n_in, r)), dtype=torch.uint8, device=dev),
                            ws_b=torch.empty(max(1, B.workspace_bytes(B.OP_BWD, T, n_out, n_in, r)), dtype=torch.uint8,
                                             device=dev) if train else None))
 
     def step(i):
+        step_layers(i)
+        if args.adamw and train:  # one launch updates every adapter matrix of the step
+            B.adamw_step([t for L in layers for t in (L["A"], L["B"])], [t for L in layers for t in (L["dA"], L["dB"])],
+                         [s_ for L in layers for s_ in L["adam"]], lr=2e-4, step=i + 1)
+
+    def step_layers(i):
         for L in layers:
             c = L["copies"][i % len(L["copies"])]
             if drop:  # a fresh mask per step: the step index is the generator offset
@@ -305,6 +314,8 @@ def main():
     torch.cuda.synchronize()
 
     timed = ["nf4_gemm_fwd", "nf4_gemm_dx"] if train else ["nf4_gemm_fwd", "nf4_gemv"]
+    if args.adamw and train:
+        timed.append("adamw")
     for k in timed:
         B.timing_read(k)  # clear
         B.timing_enable(k, True)
@@ -329,6 +340,7 @@ def main():
         "nf4_gemm_fwd": sum(2 * T * L["n_out"] * (L["n_in"] + r) for L in layers),
         "nf4_gemm_dx": sum(2 * T * L["n_in"] * (L["n_out"] + r) for L in layers),
         "nf4_gemv": sum(2 * T * L["n_out"] * L["n_in"] for L in layers),
+        "adamw": 0,
     }
     kbytes = {  # compulsory HBM bytes of one launch: weight stream + activations in and out + LoRA operands
         "nf4_gemm_fwd": sum(weight_bytes(L["n_out"], L["n_in"]) + 2 * T * (L["n_in"] + L["n_out"]) +
@@ -337,6 +349,8 @@ def main():
                            2 * (T + L["n_in"]) * r for L in layers),
         # the small-token kernel reads the weight stream and X; its binary32 partials are not algorithmic
         "nf4_gemv": sum(weight_bytes(L["n_out"], L["n_in"]) + 2 * T * L["n_in"] for L in layers),
+        # per adapter element: bf16 param and grad read, param written; binary32 m and v read and written
+        "adamw": sum(22 * r * (L["n_in"] + L["n_out"]) for L in layers),
     }
     kernels = {}
     for k, (n, ms) in ktimes.items():
@@ -346,10 +360,10 @@ def main():
         avg_ms = ms / n if n else float("nan")
         kernels[k] = {"launches": n, "avg_ms_per_launch": avg_ms,
                       "ms_per_step": ms / args.steps,
-                      "tflops": kflops[k] / (ms / args.steps * 1e-3) / 1e12 if ms else None,
+                      "tflops": kflops[k] / (ms / args.steps * 1e-3) / 1e12 if ms and kflops[k] else None,
                       "gbps": kbytes[k] / (ms / args.steps * 1e-3) / 1e9 if ms else None,
                       "launches_per_step": per_step_launches}
-    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    dom = max((k for k in kernels if k != "adamw"), key=lambda k: kernels[k]["ms_per_step"])
     kd = kernels[dom]
     wl = args.config if args.config != "small_token" else f"small_token_{lins[0][1]}x8192_T{T}"
     if drop:
@@ -386,7 +400,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": text, "name": wl, "tokens": T, "rank": r, "alpha": alpha,
-                   "pass": "fwd+bwd" if train else "fwd", "lora_dropout": drop,
+                   "pass": ("fwd+bwd+adamw" if args.adamw else "fwd+bwd") if train else "fwd", "lora_dropout": drop,
                    "linears": [[L["name"], L["n_out"], L["n_in"]] for L in layers],
                    "parallelism": "single GPU"},
         "weight_stream_GBps": wgbps,

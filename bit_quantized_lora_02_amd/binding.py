@@ -6,7 +6,7 @@ in the library's gfx950 kernels.  There is no CPU or PyTorch fallback: if the
 library is missing or the device is not gfx950, calls raise.
 
 Names follow the C ABI: ``quantize_nf4``, ``dequant``, ``linear_fwd``,
-``linear_bwd``, ``linear_fwd_dropout``, ``linear_bwd_dropout``, plus ``QLoRALinearFn`` (a torch.autograd.Function whose backward
+``linear_bwd``, ``linear_fwd_dropout``, ``linear_bwd_dropout``, ``adamw_step``, plus ``QLoRALinearFn`` (a torch.autograd.Function whose backward
 returns gradients for X, A and B and none for the frozen NF4 weight).
 """
 from __future__ import annotations
@@ -40,6 +40,7 @@ EXPORTED = (
     "qlora_linear_bwd",
     "qlora_linear_fwd_dropout",
     "qlora_linear_bwd_dropout",
+    "qlora_adamw_step",
     "qlora_strerror",
     "qlora_last_error",
     "qlora_timing_enable",
@@ -60,6 +61,17 @@ class _NF4(ctypes.Structure):
         ("codes", ctypes.c_void_p),
         ("absmax_q", ctypes.c_void_p),
         ("absmax_step", ctypes.c_void_p),
+    ]
+
+
+class _AdamTensor(ctypes.Structure):
+    _fields_ = [
+        ("param", ctypes.c_void_p),
+        ("grad", ctypes.c_void_p),
+        ("exp_avg", ctypes.c_void_p),
+        ("exp_avg_sq", ctypes.c_void_p),
+        ("master", ctypes.c_void_p),
+        ("n", ctypes.c_int64),
     ]
 
 
@@ -88,6 +100,8 @@ def load_library() -> ctypes.CDLL:
                                       ctypes.c_uint64, P, P, P, P, sz, P], ctypes.c_int),
         "qlora_linear_bwd_dropout": ([P, P, i64, pnf4, P, P, i32, ctypes.c_float, ctypes.c_float, P, P, P, P, P, P,
                                       sz, P], ctypes.c_int),
+        "qlora_adamw_step": ([ctypes.POINTER(_AdamTensor), i32, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                              ctypes.c_double, ctypes.c_double, i64, P], ctypes.c_int),
         "qlora_strerror": ([ctypes.c_int], ctypes.c_char_p),
         "qlora_last_error": ([], ctypes.c_char_p),
         "qlora_timing_enable": ([ctypes.c_char_p, ctypes.c_int], ctypes.c_int),
@@ -296,6 +310,44 @@ def linear_bwd_dropout(X: torch.Tensor, dY: torch.Tensor, w: NF4Weight, A: torch
                                                    _ptr(dB), _ptr(ws), nb, _stream(X.device)),
            "qlora_linear_bwd_dropout")
     return dX, dA, dB
+
+
+@dataclass
+class AdamState:
+    """AdamW state of one bf16 parameter: binary32 moments and an optional binary32 master copy."""
+    exp_avg: torch.Tensor
+    exp_avg_sq: torch.Tensor
+    master: torch.Tensor | None = None
+
+    @staticmethod
+    def zeros_like(param: torch.Tensor, master: bool = False) -> "AdamState":
+        z = lambda: torch.zeros(param.shape, dtype=torch.float32, device=param.device)
+        return AdamState(z(), z(), param.float().clone() if master else None)
+
+
+def adamw_step(params, grads, states, lr: float, step: int, beta1: float = 0.9, beta2: float = 0.999,
+               eps: float = 1e-8, weight_decay: float = 0.0):
+    """One fused AdamW step, in place, over lists of bf16 params, bf16 grads and AdamState."""
+    descs = []
+    keep = []
+    for p, g, st in zip(params, grads, states, strict=True):
+        if p.dtype != torch.bfloat16 or g.dtype != torch.bfloat16 or not p.is_contiguous() or not p.is_cuda:
+            raise TypeError("params and grads must be contiguous bf16 GPU tensors")
+        g = g.contiguous()
+        keep.append(g)
+        if g.shape != p.shape or st.exp_avg.shape != p.shape or st.exp_avg_sq.shape != p.shape:
+            raise ValueError("shape mismatch in adamw_step")
+        for t in (st.exp_avg, st.exp_avg_sq) + ((st.master,) if st.master is not None else ()):
+            if t.dtype != torch.float32 or not t.is_contiguous():
+                raise TypeError("AdamW state must be contiguous float32")
+        descs.append(_AdamTensor(p.data_ptr(), g.data_ptr(), st.exp_avg.data_ptr(), st.exp_avg_sq.data_ptr(),
+                                 st.master.data_ptr() if st.master is not None else None, p.numel()))
+    if not descs:
+        return
+    arr = (_AdamTensor * len(descs))(*descs)
+    _check(load_library().qlora_adamw_step(arr, len(descs), float(lr), float(beta1), float(beta2), float(eps),
+                                           float(weight_decay), int(step), _stream(params[0].device)),
+           "qlora_adamw_step")
 
 
 class QLoRALinearFn(torch.autograd.Function):

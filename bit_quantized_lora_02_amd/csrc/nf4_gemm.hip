@@ -155,13 +155,16 @@ __device__ __forceinline__ u32x4_t scale_pack8(const float (&v)[8], float cq) {
                  pack_bf16x2(__fmul_rn(v[6], cq), __fmul_rn(v[7], cq))};
 }
 
-// A operand of substep kk (16 reduction columns) for this wave's WM tiles.
+// A operand of substep kk (16 reduction columns) for this wave's row tile i, and for all WM of them.
+template <class C>
+__device__ __forceinline__ u32x4_t read_a_one(const bf16_t *sa, int wm, int lane, int kk, int i) {
+  const int chunk = kk * 2 + (lane >> 5);
+  return *reinterpret_cast<const u32x4_t *>(sa + lds_off((wm * C::WM + i) * 32 + (lane & 31), chunk));
+}
 template <class C>
 __device__ __forceinline__ void read_a(const bf16_t *sa, int wm, int lane, int kk, u32x4_t (&a)[C::WM]) {
-  const int chunk = kk * 2 + (lane >> 5);
 #pragma unroll
-  for (int i = 0; i < C::WM; ++i)
-    a[i] = *reinterpret_cast<const u32x4_t *>(sa + lds_off((wm * C::WM + i) * 32 + (lane & 31), chunk));
+  for (int i = 0; i < C::WM; ++i) a[i] = read_a_one<C>(sa, wm, lane, kk, i);
 }
 // B operand from a [n][64] tile (forward)
 template <class C>
@@ -176,19 +179,21 @@ __device__ __forceinline__ void read_b_rows(const bf16_t *sb, int wn, int lane, 
 // by lane 4m + (i >> 2), so lane a points at row base + (a >> 2), columns
 // 4 (a & 3) .. +3, and reads of rows +0..3 and +4..7 give its 8 reduction values.
 template <class C, int LDB>
-__device__ __forceinline__ void read_b_tr(const bf16_t *sb, int wn, int lane, int kk, u32x4_t (&b)[C::WN]) {
+__device__ __forceinline__ u32x4_t read_b_tr_one(const bf16_t *sb, int wn, int lane, int kk, int j) {
   typedef short s4_t __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s4_t lds_s4;
   const int grp = lane >> 4, ai = lane & 15;
   const int row = kk * 16 + 8 * (grp >> 1) + (ai >> 2);
+  const int col = (wn * C::WN + j) * 32 + 16 * (grp & 1) + 4 * (ai & 3);
+  const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(sb + row * LDB + col));
+  const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(sb + (row + 4) * LDB + col));
+  const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+  return u32x4_t{l2.x, l2.y, h2.x, h2.y};
+}
+template <class C, int LDB>
+__device__ __forceinline__ void read_b_tr(const bf16_t *sb, int wn, int lane, int kk, u32x4_t (&b)[C::WN]) {
 #pragma unroll
-  for (int j = 0; j < C::WN; ++j) {
-    const int col = (wn * C::WN + j) * 32 + 16 * (grp & 1) + 4 * (ai & 3);
-    const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(sb + row * LDB + col));
-    const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(sb + (row + 4) * LDB + col));
-    const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
-    b[j] = u32x4_t{l2.x, l2.y, h2.x, h2.y};
-  }
+  for (int j = 0; j < C::WN; ++j) b[j] = read_b_tr_one<C, LDB>(sb, wn, lane, kk, j);
 }
 
 template <class C>
@@ -438,23 +443,20 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
 // then forms dUp . A first, scales each accumulator element by its keep bit
 // times q, and accumulates dY . W' on top, so no second accumulator is needed.
 // Keep bit (t, k) is bit k % 8 of mask[(t K + k) / 8].
+// Keep bits of the output tile, staged in LDS as BM rows of BN / 8 bytes; each
+// accumulator element then reads its row's 32-bit word for its 32-column tile.
 template <class C>
-__device__ __forceinline__ void keep_scale_acc(f32x16_t acc[C::WM][C::WN], const uint8_t *__restrict__ mask,
-                                               int64_t K, int64_t m0, int64_t rows, int64_t n0, int wm, int wn,
-                                               int lane, float q) {
+__device__ __forceinline__ void stage_keep_bits(uint8_t *s_keep, const uint8_t *__restrict__ mask, int64_t K,
+                                                int64_t m0, int64_t rows, int64_t n0, int tid) {
+  constexpr int PIECES = C::BM * C::BN / 64;  // 8-byte pieces (64 columns of one row)
 #pragma unroll
-  for (int i = 0; i < C::WM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::WN; ++j) {
-      const int64_t col0 = n0 + (wn * C::WN + j) * 32;  // multiple of 32: one 32-bit word per row
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        int64_t row = m0 + (wm * C::WM + i) * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-        row = row < rows ? row : rows - 1;  // rows past T are never stored
-        const uint32_t w = col0 < K ? *reinterpret_cast<const uint32_t *>(mask + (row * K + col0) / 8) : 0u;
-        acc[i][j][e] = ((w >> (lane & 31)) & 1u) ? __fmul_rn(acc[i][j][e], q) : 0.f;
-      }
-    }
+  for (int c = tid; c < PIECES; c += C::NT) {
+    const int row = c / (C::BN / 64), part = c % (C::BN / 64);
+    const int64_t col = n0 + 64 * part;  // n0 and K are multiples of 64: a piece is all in or all out
+    u32x2_t v = u32x2_t{0u, 0u};
+    if (m0 + row < rows && col < K) v = *reinterpret_cast<const u32x2_t *>(mask + ((m0 + row) * K + col) / 8);
+    *reinterpret_cast<u32x2_t *>(s_keep + row * (C::BN / 8) + 8 * part) = v;
+  }
 }
 
 template <class C, bool DROP>
@@ -525,11 +527,6 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
       __syncthreads();
     }
   };
-  if constexpr (DROP) {  // adapter term first, masked, then the base product on top
-    lora_steps();
-    keep_scale_acc<C>(acc, mask, K, m0, T, n0, wm, wn, lane, q);
-  }
-
   al.issue(0, N, sA[0]);
   load_words_of(0, rc[0], rs[0]);
   load_words_of(nk > 1 ? 1 : 0, rc[1], rs[1]);
@@ -567,7 +564,53 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
   }
   if (s < nk) step_p(std::integral_constant<int, 0>(), s);
 
-  if constexpr (!DROP) lora_steps();
+  if constexpr (!DROP) {
+    lora_steps();
+  } else {
+    // The adapter term times keep * q: all of dUp [BM, rp] and A [rp, BN] (rp <= 128: two 64-deep
+    // chunks at most) go to LDS with the tile's keep bits; then each 32x32 tile forms its adapter
+    // term in an accumulator of its own, scales it by its keep bits and q, and adds it.
+    __shared__ __attribute__((aligned(16))) uint8_t s_keep[C::BM * C::BN / 8];
+    stage_keep_bits<C>(s_keep, mask, K, m0, T, n0, tid);
+    const int nkc = (int)(rp / BK);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      if (c >= nkc) break;
+      copy_a_tile<C>(dUp, rp, m0, T, (int64_t)c * BK, rp, tid, sA[c]);
+      constexpr int LCH = BK * C::BN / 8 / C::NT;  // 16-byte chunks of A per thread
+#pragma unroll
+      for (int u = 0; u < LCH; ++u) {
+        const int cc = tid + C::NT * u;
+        const int64_t j = (int64_t)c * BK + cc / (C::BN / 8), kcol = n0 + (cc % (C::BN / 8)) * 8;
+        const u32x4_t v =
+            (j < r && kcol < K) ? *reinterpret_cast<const u32x4_t *>(A + j * K + kcol) : u32x4_t{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4_t *>(sB[c] + (cc / (C::BN / 8)) * LDB + (cc % (C::BN / 8)) * 8) = v;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+      for (int jt = 0; jt < C::WN; ++jt) {
+        f32x16_t t;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) t[e] = 0.f;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          if (c >= nkc) break;
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+            t = mfma_32x32x16(read_a_one<C>(sA[c], wm, lane, kk, i), read_b_tr_one<C, LDB>(sB[c], wn, lane, kk, jt), t);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = (wm * C::WM + i) * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+          const uint32_t w = *reinterpret_cast<const uint32_t *>(s_keep + row * (C::BN / 8) + 4 * (wn * C::WN + jt));
+          acc[i][jt][e] = __fadd_rn(acc[i][jt][e], ((w >> (lane & 31)) & 1u) ? __fmul_rn(t[e], q) : 0.f);
+        }
+        fence_sched();  // one tile's operands and words in flight at a time
+      }
+  }
   store_out<C>(dX, K, m0, T, n0, K, wm, wn, lane, acc);
 }
 
@@ -615,19 +658,15 @@ hipError_t fwd_with(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes,
   return hipGetLastError();
 }
 
-template <class C>
+template <class C, bool DROP>
 hipError_t dx_with(const bf16_t *dY, int64_t T, int64_t N, const uint8_t *codes, const uint8_t *absmax_q,
                    const float *step, int64_t K, const bf16_t *dUp, const bf16_t *A, int64_t r, int64_t rp,
                    bf16_t *dX, const Levels &lv, hipStream_t s, const uint8_t *mask, float q) {
   const int64_t tm = (T + C::BM - 1) / C::BM, tn = (K + C::BN - 1) / C::BN;
   int xb_m, xb_n;
   xcd_blocking(tm, tn, 2.0 * T * N, 0.516 * N * K, &xb_m, &xb_n);
-  if (mask)
-    launch(k_nf4_gemm_dx<C, true>, dim3((unsigned)(tm * tn)), dim3(C::NT), 0, s, dY, T, N, codes, absmax_q, step,
-           K, dUp, A, r, rp, dX, lv, xb_m, xb_n, mask, q);
-  else
-    launch(k_nf4_gemm_dx<C, false>, dim3((unsigned)(tm * tn)), dim3(C::NT), 0, s, dY, T, N, codes, absmax_q, step,
-           K, dUp, A, r, rp, dX, lv, xb_m, xb_n, mask, q);
+  launch(k_nf4_gemm_dx<C, DROP>, dim3((unsigned)(tm * tn)), dim3(C::NT), 0, s, dY, T, N, codes, absmax_q, step, K,
+         dUp, A, r, rp, dX, lv, xb_m, xb_n, mask, q);
   return hipGetLastError();
 }
 }  // namespace
@@ -662,16 +701,28 @@ hipError_t launch_nf4_gemm_dx(int tile, const bf16_t *dY, int64_t T, int64_t N, 
                               int64_t r, int64_t rp, bf16_t *dX, const Levels &lv, hipStream_t s,
                               const uint8_t *mask, float q) {
   if (T == 0) return hipSuccess;
+  if (mask) {  // dropout: the per-tile adapter epilogue needs registers that the 256x256 tile does not have
+    switch (tile) {
+      case NF4_TILE_256x256_W8:
+      case NF4_TILE_256x128_W8:
+        return dx_with<T256x128w8, true>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s, mask, q);
+      case NF4_TILE_128x256_W8:
+        return dx_with<T128x256w8, true>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s, mask, q);
+      case NF4_TILE_128x128_W8:
+        return dx_with<T128x128w8, true>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s, mask, q);
+      default: return dx_with<T128x128, true>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s, mask, q);
+    }
+  }
   switch (tile) {
     case NF4_TILE_256x256_W8:
-      return dx_with<T256x256w8>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s, mask, q);
+      return dx_with<T256x256w8, false>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s, mask, q);
     case NF4_TILE_256x128_W8:
-      return dx_with<T256x128w8>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s, mask, q);
+      return dx_with<T256x128w8, false>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s, mask, q);
     case NF4_TILE_128x256_W8:
-      return dx_with<T128x256w8>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s, mask, q);
+      return dx_with<T128x256w8, false>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s, mask, q);
     case NF4_TILE_128x128_W8:
-      return dx_with<T128x128w8>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s, mask, q);
-    default: return dx_with<T128x128>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s, mask, q);
+      return dx_with<T128x128w8, false>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s, mask, q);
+    default: return dx_with<T128x128, false>(dY, T, N, codes, absmax_q, step, K, dUp, A, r, rp, dX, lv, s, mask, q);
   }
 }
 

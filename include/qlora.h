@@ -186,6 +186,38 @@ int qlora_linear_bwd_dropout(const qlora_bf16 *X, const qlora_bf16 *dY, int64_t 
                              const uint8_t *mask, const qlora_bf16 *U, qlora_bf16 *dX, qlora_bf16 *dA,
                              qlora_bf16 *dB, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * One AdamW step of the adapter matrices ("What stays in full precision",
+ * katajob: A and B are bf16 with ordinary AdamW state; pranaymahendrakar,
+ * Developer level, "The walkthrough": about 8 bytes of state per trainable
+ * parameter).  Decoupled weight decay (Loshchilov and Hutter, ICLR 2019) with a
+ * constant schedule multiplier; step t >= 1:
+ *   m     = b1 m + (1 - b1) g
+ *   v     = b2 v + (1 - b2) g^2
+ *   theta = theta - lr (wd theta + (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps))
+ * in binary32 (each operation rounded once).  The hyperparameters are binary64;
+ * the host forms b1, 1 - b1, b2, 1 - b2, eps, 1 - lr wd, lr / (1 - b1^t) and
+ * sqrt(1 - b2^t) in binary64 and rounds each to binary32 once.
+ * theta is `master` when given (updated in place), else the bf16 `param`
+ * widened; `param` receives bf16_rne(theta).
+ * Every array of a tensor is device memory of n elements, 16-byte aligned, and
+ * updated in place except `grad`; tensors must not overlap.  `tensors` is a
+ * host array of `count` descriptors (any count; the library launches one kernel
+ * per 32 of them; no elements at all means no HIP call).  0 <= beta1, beta2 < 1,
+ * eps > 0, lr >= 0, weight_decay >= 0, all finite.
+ */
+typedef struct qlora_adamw_tensor {
+  qlora_bf16 *param;      /* [n] bf16 parameter                       */
+  const qlora_bf16 *grad; /* [n] bf16 gradient (e.g. dA or dB)        */
+  float *exp_avg;         /* [n] binary32 first moment m              */
+  float *exp_avg_sq;      /* [n] binary32 second moment v             */
+  float *master;          /* [n] binary32 master copy of param, or NULL */
+  int64_t n;
+} qlora_adamw_tensor;
+
+int qlora_adamw_step(const qlora_adamw_tensor *tensors, int32_t count, double lr, double beta1, double beta2,
+                     double eps, double weight_decay, int64_t step, void *stream);
+
 /* Static text for a QLORA_E* code. */
 const char *qlora_strerror(int code);
 

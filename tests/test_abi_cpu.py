@@ -194,6 +194,32 @@ def test_dropout_workspace_covers_the_skinny_path(lib):
             assert wd == B.workspace_bytes(B.OP_FWD, T, 4096, 4096, 16)
 
 
+def _adam(lib, descs, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.0, step=1, count=None):
+    arr = (B._AdamTensor * max(1, len(descs)))(*descs)
+    return lib.qlora_adamw_step(arr, len(descs) if count is None else count, lr, b1, b2, eps, wd, step, None)
+
+
+def test_error_paths_adamw(lib):
+    E = B.QLORA_EINVAL
+    ok = B._AdamTensor(0x1000, 0x2000, 0x3000, 0x4000, None, 100)
+    assert _adam(lib, [ok], step=0) == E
+    assert _adam(lib, [ok], b1=1.0) == E
+    assert _adam(lib, [ok], b2=-0.1) == E
+    assert _adam(lib, [ok], eps=0.0) == E
+    assert _adam(lib, [ok], lr=-1.0) == E
+    assert _adam(lib, [ok], wd=float("nan")) == E
+    assert _adam(lib, [ok], count=-1) == E
+    assert lib.qlora_adamw_step(None, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, None) == E
+    assert _adam(lib, [B._AdamTensor(0x1000, None, 0x3000, 0x4000, None, 100)]) == E
+    assert _adam(lib, [B._AdamTensor(0x1008, 0x2000, 0x3000, 0x4000, None, 100)]) == E
+    assert _adam(lib, [B._AdamTensor(0x1000, 0x2000, 0x3000, 0x4000, 0x5004, 100)]) == E
+    assert _adam(lib, [B._AdamTensor(0x1000, 0x2000, 0x3000, 0x4000, None, -1)]) == E
+    assert "tensor 1" in (_adam(lib, [ok, B._AdamTensor(0, 0, 0, 0, None, 5)]) == E and
+                          lib.qlora_last_error().decode())
+    # empty lists and empty tensors are fine without touching the device
+    assert _adam(lib, []) == B.QLORA_OK
+
+
 def test_strerror(lib):
     for code in (0, -1, -2, -3, -4):
         assert lib.qlora_strerror(code)
@@ -209,6 +235,7 @@ def test_no_device_is_reported(lib):
     assert _bwd(lib) == B.QLORA_ENODEV
     assert _fwd_drop(lib) == B.QLORA_ENODEV
     assert _bwd_drop(lib) == B.QLORA_ENODEV
+    assert _adam(lib, [B._AdamTensor(0x1000, 0x2000, 0x3000, 0x4000, None, 100)]) == B.QLORA_ENODEV
 
 
 def test_timing_api_host_only(lib):

@@ -140,3 +140,21 @@ def test_dropout_attention_size_sampled():
         assert_close(k, gpu_f64(g[k][idx]), ref[k])
     assert_close("dA", gpu_f64(g["dA"]), ref["dA"])
     assert_close("dB", gpu_f64(g["dB"]), ref["dB"])
+
+
+def test_dropout_large_dx_tiles_sampled():
+    """dX of 4096 x 4096 tokens x features: without dropout the 256x256 tile; with it the 256x128 tile with the
+    per-tile adapter epilogue.  Mask bit for bit, dA and dB in full, dX, Y and U on sampled rows."""
+    n_out, n_in, T, r = 1024, 4096, 4096, 16
+    print(f"dropout large tiles {n_out}x{n_in} T={T}", flush=True)
+    inp = linear_inputs(n_out, n_in, T, r, 32.0, seed=5, sigma_ab=0.1)
+    _, g = run_gpu_drop(inp, 0.1, 77, 1)
+    mask = O.dropout_mask(T, n_in, 0.1, 77, 1)
+    np.testing.assert_array_equal(g["mask"].cpu().numpy(), mask)
+    rows = np.unique(np.concatenate([[0, 255, 256, T - 1], np.random.default_rng(6).choice(T, 28, replace=False)]))
+    ref = oracle_drop(inp, 0.1, mask, rows=rows)
+    idx = torch.from_numpy(rows).to(dev())
+    for k in ("Y", "U", "dX"):
+        assert_close(k, gpu_f64(g[k][idx]), ref[k])
+    assert_close("dA", gpu_f64(g["dA"]), ref["dA"])
+    assert_close("dB", gpu_f64(g["dB"]), ref["dB"])
