@@ -75,6 +75,8 @@ def _load():
     d = ctypes.c_double
     lib.oracle_adamw_step.argtypes = [P, P, P, P, i64, d, d, d, d, d, i64]
     lib.oracle_adamw_step.restype = None
+    lib.oracle_merge.argtypes = [P, i64, i64, P, P, ctypes.c_int32, ctypes.c_float, P]
+    lib.oracle_merge.restype = None
     _lib = lib
     return lib
 
@@ -300,3 +302,16 @@ def adamw_step(theta: np.ndarray, g, m: np.ndarray, v: np.ndarray, lr: float, be
         assert a.dtype == np.float64 and a.flags.c_contiguous and a.size == g.size
     _load().oracle_adamw_step(_ptr(theta), _ptr(g), _ptr(m), _ptr(v), g.size, float(lr), float(beta1), float(beta2),
                               float(eps), float(weight_decay), int(step))
+
+
+# ------------------------------------------------------------------ merge
+
+def merge(W, A, B, alpha: float) -> np.ndarray:
+    """Merged weight W + s B A in binary64; W [N, K] as floats or bf16 bits (the reloaded or dequantized base)."""
+    W, A, B = _f64(W), _f64(A), _f64(B)
+    N, K = W.shape
+    r = A.shape[0]
+    assert A.shape == (r, K) and B.shape == (N, r)
+    out = np.zeros((N, K), np.float64)
+    _load().oracle_merge(_ptr(W), N, K, _ptr(A), _ptr(B), r, float(alpha), _ptr(out))
+    return out

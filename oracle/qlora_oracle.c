@@ -29,6 +29,8 @@
  *  [OPT]  katajob, "What stays in full precision" (A and B keep ordinary AdamW
  *         state) and pranaymahendrakar, Developer level, "The walkthrough" (about
  *         8 bytes of Adam state per trainable parameter).
+ *  [MERGE] "Module 08 - QLoRA & Quantization" (ainiketan), "7. A subtle but
+ *         important deployment note"; katajob, "What it costs" (3. Merging).
  *  [DROP] "Module 08 - QLoRA & Quantization" (ainiketan), "4. QLoRA in code":
  *         the adapter config sets lora_dropout = 0.05 (so does the Developer
  *         level of the pranaymahendrakar page).
@@ -470,4 +472,28 @@ void oracle_adamw_step(double *theta, const double *g, double *m, double *v, int
     const double mhat = m[i] / bc1, vhat = v[i] / bc2;
     theta[i] = theta[i] - lr * (wd * theta[i] + mhat / (sqrt(vhat) + eps));
   }
+}
+
+/* ------------------------------------------------------------------ merge */
+
+/*
+ * [MERGE] "Module 08 - QLoRA & Quantization" (ainiketan), "7. A subtle but
+ * important deployment note", and katajob, "What it costs" (3. Merging): for
+ * serving, the trained adapter is folded into a 16-bit base (the reloaded
+ * original, or here also the dequantized NF4 base it was trained against),
+ * and the merged model may then be quantized again.  With [LORA]'s layer
+ * h = W0 x + s B A x the merged weight is
+ *   Wm[n, k] = W[n, k] + s * sum_j B[n, j] A[j, k]         (binary64)
+ * W [N, K], A [r, K], B [N, r], Wm [N, K]; s = fl32(alpha / r).
+ */
+void oracle_merge(const double *W, int64_t N, int64_t K, const double *A, const double *B, int32_t r, float alpha,
+                  double *Wm) {
+  const double s = (double)(alpha / (float)r);
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) {
+      double acc = 0.0;
+      for (int32_t j = 0; j < r; ++j) acc += B[n * r + j] * A[(int64_t)j * K + k];
+      Wm[n * K + k] = W[n * K + k] + s * acc;
+    }
 }
