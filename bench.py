@@ -53,6 +53,8 @@ def parse():
                     help="LoRA dropout probability on the adapter input (training configs; default 0: none)")
     ap.add_argument("--adamw", action="store_true",
                     help="end each training step with the fused AdamW update of every A and B (timed as 'adamw')")
+    ap.add_argument("--merge", action="store_true",
+                    help="time the export merge W' + s B A (NF4 base, bf16 out) of every linear instead of a step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -213,6 +215,46 @@ def weight_bytes(N, K):
     return N * K // 2 + nblk + 4 * ((nblk + 255) // 256)
 
 
+def bench_merge(args, B, layers, r, alpha):
+    """Export merge of every linear: HBM bytes = NF4 weight read + bf16 merged weight written (+ A, B)."""
+    import torch
+
+    outs = [torch.empty((L["n_out"], L["n_in"]), dtype=torch.bfloat16, device=L["A"].device) for L in layers]
+
+    def run(i):
+        for L, o in zip(layers, outs):
+            c = L["copies"][i % len(L["copies"])]
+            st = c["w"].struct()
+            B._check(B.load_library().qlora_merge(B.ctypes.byref(st), None, L["n_out"], L["n_in"], B._ptr(L["A"]),
+                                                  B._ptr(L["B"]), r, float(alpha), B._ptr(o), None,
+                                                  B._stream(o.device)), "qlora_merge")
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    B.timing_read("merge")
+    B.timing_enable("merge", True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    B.timing_enable("merge", False)
+    n, ms = B.timing_read("merge")
+    nbytes = sum(weight_bytes(L["n_out"], L["n_in"]) + 2 * L["n_out"] * L["n_in"] + 2 * r * (L["n_in"] + L["n_out"])
+                 for L in layers)
+    gbps = nbytes / (ms / args.steps * 1e-3) / 1e9
+    print(json.dumps({"metric": "NF4 adapter merge for export, HBM GB/s", "value": gbps, "unit": "GB/s",
+                      "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True, "dtype": "bf16",
+                      "data": "synthetic",
+                      "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config + "_merge", "rank": r,
+                                 "linears": [[L["name"], L["n_out"], L["n_in"]] for L in layers]},
+                      "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                   "frac": gbps / PEAK_HBM_GBPS, "traffic": None, "kernel": "merge",
+                                   "avg_ms_per_launch": ms / n if n else None}}))
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -288,6 +330,10 @@ def main():
                                                                      n_out, n_in, r)), dtype=torch.uint8, device=dev),
                            ws_b=torch.empty(max(1, B.workspace_bytes(B.OP_BWD, T, n_out, n_in, r)), dtype=torch.uint8,
                                             device=dev) if train else None))
+
+    if args.merge:
+        bench_merge(args, B, layers, r, alpha)
+        return
 
     def step(i):
         step_layers(i)

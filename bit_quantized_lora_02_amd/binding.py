@@ -6,7 +6,7 @@ in the library's gfx950 kernels.  There is no CPU or PyTorch fallback: if the
 library is missing or the device is not gfx950, calls raise.
 
 Names follow the C ABI: ``quantize_nf4``, ``dequant``, ``linear_fwd``,
-``linear_bwd``, ``linear_fwd_dropout``, ``linear_bwd_dropout``, ``adamw_step``, plus ``QLoRALinearFn`` (a torch.autograd.Function whose backward
+``linear_bwd``, ``linear_fwd_dropout``, ``linear_bwd_dropout``, ``adamw_step``, ``merge``, plus ``QLoRALinearFn`` (a torch.autograd.Function whose backward
 returns gradients for X, A and B and none for the frozen NF4 weight).
 """
 from __future__ import annotations
@@ -41,6 +41,7 @@ EXPORTED = (
     "qlora_linear_fwd_dropout",
     "qlora_linear_bwd_dropout",
     "qlora_adamw_step",
+    "qlora_merge",
     "qlora_strerror",
     "qlora_last_error",
     "qlora_timing_enable",
@@ -102,6 +103,7 @@ def load_library() -> ctypes.CDLL:
                                       sz, P], ctypes.c_int),
         "qlora_adamw_step": ([ctypes.POINTER(_AdamTensor), i32, ctypes.c_double, ctypes.c_double, ctypes.c_double,
                               ctypes.c_double, ctypes.c_double, i64, P], ctypes.c_int),
+        "qlora_merge": ([pnf4, P, i64, i64, P, P, i32, ctypes.c_float, P, P, P], ctypes.c_int),
         "qlora_strerror": ([ctypes.c_int], ctypes.c_char_p),
         "qlora_last_error": ([], ctypes.c_char_p),
         "qlora_timing_enable": ([ctypes.c_char_p, ctypes.c_int], ctypes.c_int),
@@ -310,6 +312,29 @@ def linear_bwd_dropout(X: torch.Tensor, dY: torch.Tensor, w: NF4Weight, A: torch
                                                    _ptr(dB), _ptr(ws), nb, _stream(X.device)),
            "qlora_linear_bwd_dropout")
     return dX, dA, dB
+
+
+def merge(A: torch.Tensor, B: torch.Tensor, alpha: float, w: NF4Weight | None = None,
+          W_base: torch.Tensor | None = None, bf16_out: bool = True, f32_out: bool = False):
+    """Merged weight W + (alpha/r) B A for export, W = deq(w) or the bf16 base W_base (exactly one).
+
+    Returns (bf16 [n_out, n_in] or None, float32 [n_out, n_in] or None); the float32 output is what
+    ``quantize_nf4`` takes to quantize the merged weight again."""
+    if (w is None) == (W_base is None):
+        raise ValueError("give exactly one of w and W_base")
+    A, B = _bits(A), _bits(B)
+    r = A.shape[0]
+    n_out, n_in = (w.n_out, w.n_in) if w is not None else tuple(W_base.shape)
+    if A.shape != (r, n_in) or B.shape != (n_out, r):
+        raise ValueError("shape mismatch in merge")
+    dev = A.device
+    out = torch.empty((n_out, n_in), dtype=torch.bfloat16, device=dev) if bf16_out else None
+    out32 = torch.empty((n_out, n_in), dtype=torch.float32, device=dev) if f32_out else None
+    Wb = _bits(W_base) if W_base is not None else None
+    st = w.struct() if w is not None else None
+    _check(load_library().qlora_merge(ctypes.byref(st) if st is not None else None, _ptr(Wb), n_out, n_in, _ptr(A),
+                                      _ptr(B), r, float(alpha), _ptr(out), _ptr(out32), _stream(dev)), "qlora_merge")
+    return out, out32
 
 
 @dataclass

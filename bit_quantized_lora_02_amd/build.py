@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqlora.so")
-SOURCES = ["abi.hip", "quant.hip", "nf4_gemm.hip", "nf4_gemv.hip", "lora_gemm.hip", "adamw.hip"]
+SOURCES = ["abi.hip", "quant.hip", "nf4_gemm.hip", "nf4_gemv.hip", "lora_gemm.hip", "adamw.hip", "merge.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -540,6 +540,35 @@ int qlora_linear_bwd_dropout(const qlora_bf16 *X, const qlora_bf16 *dY, int64_t 
   return linear_bwd(X, dY, T, q, A, B, r, alpha, &d, U, dX, dA, dB, ws, ws_bytes, stream);
 }
 
+int qlora_merge(const qlora_nf4 *q, const qlora_bf16 *W_base, int64_t n_out, int64_t n_in, const qlora_bf16 *A,
+                const qlora_bf16 *B, int32_t r, float alpha, qlora_bf16 *W_out, float *W_out_f32, void *stream) {
+  if ((q == nullptr) == (W_base == nullptr)) return fail(QLORA_EINVAL, "give exactly one of q and W_base");
+  int rc;
+  if (q) {
+    if ((rc = check_nf4(q, false))) return rc;
+    if (q->n_out != n_out || q->n_in != n_in)
+      return fail(QLORA_EINVAL, "q is %lld x %lld, the merge asks for %lld x %lld", (long long)q->n_out,
+                  (long long)q->n_in, (long long)n_out, (long long)n_in);
+  } else if (!aligned16(W_base)) {
+    return fail(QLORA_EINVAL, "W_base must be 16-byte aligned");
+  }
+  if (n_out < 1 || n_in < 64 || n_in % 64 != 0 || n_out > kMaxDim || n_in > kMaxDim ||
+      n_out * n_in > ((int64_t)1 << 40))
+    return fail(QLORA_EINVAL, "need n_out >= 1 and n_in a positive multiple of 64 (got %lld x %lld)",
+                (long long)n_out, (long long)n_in);
+  if (r < 1 || r > QLORA_MAX_RANK) return fail(QLORA_EINVAL, "r must be in [1, %d] (got %d)", QLORA_MAX_RANK, (int)r);
+  if (!isfinite(alpha)) return fail(QLORA_EINVAL, "alpha must be finite");
+  if (!A || !B || !aligned16(A) || !aligned16(B)) return fail(QLORA_EINVAL, "A and B must be non-NULL and 16-byte aligned");
+  if (!W_out && !W_out_f32) return fail(QLORA_EINVAL, "give W_out, W_out_f32 or both");
+  if ((W_out && !aligned16(W_out)) || (W_out_f32 && !aligned16(W_out_f32)))
+    return fail(QLORA_EINVAL, "outputs must be 16-byte aligned");
+  if ((rc = check_device(nullptr))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  LAUNCH("merge", launch_merge(q ? q->codes : nullptr, q ? q->absmax_q : nullptr, q ? q->absmax_step : nullptr,
+                               W_base, n_out, n_in, A, B, r, alpha / (float)r, W_out, W_out_f32, codebook().lv, s));
+  return QLORA_OK;
+}
+
 int qlora_adamw_step(const qlora_adamw_tensor *tensors, int32_t count, double lr, double beta1, double beta2,
                      double eps, double weight_decay, int64_t step, void *stream) {
   if (count < 0 || (count > 0 && !tensors)) return fail(QLORA_EINVAL, "tensors is NULL or count < 0");

@@ -50,6 +50,11 @@ hipError_t launch_nf4_gemm_dx(int tile, const bf16_t *dY, int64_t T, int64_t N, 
                               int64_t r, int64_t rp, bf16_t *dX, const Levels &lv, hipStream_t s,
                               const uint8_t *mask = nullptr, float q = 1.f);
 
+// Merge for export: out = W + s B A (bf16 and/or binary32), W = W_base or the decoded NF4 weight.
+hipError_t launch_merge(const uint8_t *codes, const uint8_t *absmax_q, const float *step, const bf16_t *W_base,
+                        int64_t N, int64_t K, const bf16_t *A, const bf16_t *B, int r, float s, bf16_t *out,
+                        float *out_f32, const Levels &lv, hipStream_t st);
+
 // Small-token forward (T <= 64, n_in % 128 == 0): the split-K GEMV over the
 // weight (binary32 partials per K range, plus the partials of U = X A^T from
 // one extra workgroup per range), then one finishing launch that adds the

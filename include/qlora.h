@@ -187,6 +187,22 @@ int qlora_linear_bwd_dropout(const qlora_bf16 *X, const qlora_bf16 *dY, int64_t 
                              qlora_bf16 *dB, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Merge a trained adapter into a 16-bit base for export ("Module 08 - QLoRA &
+ * Quantization", ainiketan.in, "7. A subtle but important deployment note";
+ * katajob, "What it costs", 3. Merging):
+ *   Wm = W + s . B . A        [n_out, n_in],  s = fl32(alpha / r)
+ * W is either the reloaded bf16 base W_base [n_out, n_in] (device; q NULL) or
+ * the dequantized NF4 weight deq(q) (q non-NULL; W_base NULL; its shape must
+ * equal n_out x n_in).  Exactly one of them.  A [r, n_in], B [n_out, r] bf16.
+ * Arithmetic: P = B . A in binary32 (MFMA), m = fl32(w + fl32(s P)).
+ * Outputs (device, either may be NULL but not both): W_out bf16 = bf16_rne(m);
+ * W_out_f32 binary32 = m, the input qlora_quantize_nf4 takes to quantize the
+ * merged weight again.  n_in % 64 == 0, 1 <= r <= QLORA_MAX_RANK.
+ */
+int qlora_merge(const qlora_nf4 *q, const qlora_bf16 *W_base, int64_t n_out, int64_t n_in, const qlora_bf16 *A,
+                const qlora_bf16 *B, int32_t r, float alpha, qlora_bf16 *W_out, float *W_out_f32, void *stream);
+
+/*
  * One AdamW step of the adapter matrices ("What stays in full precision",
  * katajob: A and B are bf16 with ordinary AdamW state; pranaymahendrakar,
  * Developer level, "The walkthrough": about 8 bytes of state per trainable

@@ -220,6 +220,27 @@ def test_error_paths_adamw(lib):
     assert _adam(lib, []) == B.QLORA_OK
 
 
+def test_error_paths_merge(lib):
+    E = B.QLORA_EINVAL
+    q = _nf4(64, 128)
+
+    def merge(q_=q, Wb=None, n_out=64, n_in=128, A=FAKE, Bm=FAKE, r=8, alpha=16.0, W=FAKE, W32=None):
+        return lib.qlora_merge(ctypes.byref(q_) if q_ is not None else None, Wb, n_out, n_in, A, Bm, r, alpha, W, W32,
+                               None)
+
+    rc, msg = _err(lambda: merge(Wb=FAKE))
+    assert rc == E and "exactly one" in msg
+    assert merge(q_=None) == E
+    assert merge(n_out=32) == E  # shape differs from q
+    assert merge(q_=None, Wb=FAKE, n_in=100) == E
+    assert merge(q_=None, Wb=MIS) == E
+    assert merge(r=0) == E and merge(r=129) == E
+    assert merge(A=None) == E and merge(Bm=MIS) == E
+    assert merge(W=None, W32=None) == E
+    assert merge(W=MIS) == E
+    assert merge(alpha=float("nan")) == E
+
+
 def test_strerror(lib):
     for code in (0, -1, -2, -3, -4):
         assert lib.qlora_strerror(code)
@@ -236,6 +257,7 @@ def test_no_device_is_reported(lib):
     assert _fwd_drop(lib) == B.QLORA_ENODEV
     assert _bwd_drop(lib) == B.QLORA_ENODEV
     assert _adam(lib, [B._AdamTensor(0x1000, 0x2000, 0x3000, 0x4000, None, 100)]) == B.QLORA_ENODEV
+    assert lib.qlora_merge(ctypes.byref(q), None, 64, 64, FAKE, FAKE, 8, 16.0, FAKE, None, None) == B.QLORA_ENODEV
 
 
 def test_timing_api_host_only(lib):
