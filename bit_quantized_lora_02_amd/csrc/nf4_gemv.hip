@@ -10,7 +10,8 @@
 // 1. k_nf4_gemv: the reduction over n_in is split into K ranges.  A workgroup
 //    (4 waves) owns 64 RG weight rows and one K range; each wave owns RG
 //    groups of 16 rows and issues v_mfma_f32_16x16x32_bf16 with the tokens as
-//    the M dimension, so one load of the activations serves RG row groups.
+//    the M dimension, so one load of the activations serves RG row groups
+//    (MFMA rows of tokens past T repeat token T - 1 and are never stored).
 //    Each lane streams 16 bytes of codes per row group and 128-deep step (32
 //    consecutive weights of one row, one block constant) and decodes them
 //    straight into its four B operands, so the weight never touches LDS.  The
@@ -130,14 +131,14 @@ __global__ __launch_bounds__(256) void k_nf4_gemv(const bf16_t *__restrict__ X, 
   const int64_t total = my_items * nsteps;  // steps of this workgroup
   if (total == 0) return;
 
-  // activations: token 16 m + (lane & 15); tokens past T are zero and not loaded
+  // activations: token 16 m + (lane & 15); lanes of tokens past T load token T - 1 instead (MFMA
+  // output row t depends on operand row t only, and rows past T are never stored), so the loads
+  // need no branch around them
   const bf16_t *xrow[MT];
-  bool tok[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     const int64_t t = m * 16 + (lane & 15);
-    tok[m] = t < T;
-    xrow[m] = X + (tok[m] ? t : 0) * K + 32 * W * g;
+    xrow[m] = X + (t < T ? t : T - 1) * K + 32 * W * g;
   }
   // row of row group q in tile `tile`: 64 RG tile + 64 q + 16 wave + (lane & 15)
   auto row_of = [&](int64_t tile, int q) { return tile * 64 * RG + 64 * q + 16 * wave + (lane & 15); };
@@ -180,16 +181,18 @@ __global__ __launch_bounds__(256) void k_nf4_gemv(const bf16_t *__restrict__ X, 
   int64_t ci = 0;
   int cs = 0;
   auto do_step = [&](Slot &cur, Slot &refill) {
-    load_slot(refill);
     const int64_t item = blockIdx.x + ci * gmain;
     const int64_t tile = item / nsplit, split = item - tile * nsplit;
     const int64_t koff = split * kchunk + (int64_t)cs * D;
+    // this step's activations first, then the code prefetch: vector-memory counters complete in
+    // order, so waiting for activations issued after the prefetch would wait for the prefetch too
     u32x4_t a[MT][4 * W];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int j = 0; j < 4 * W; ++j)
-        a[m][j] = tok[m] ? *reinterpret_cast<const u32x4_t *>(xrow[m] + koff + 8 * j) : u32x4_t{0u, 0u, 0u, 0u};
+        a[m][j] = *reinterpret_cast<const u32x4_t *>(xrow[m] + koff + 8 * j);
+    load_slot(refill);
 #pragma unroll
     for (int q = 0; q < RG; ++q) {
 #pragma unroll
@@ -298,20 +301,24 @@ __global__ __launch_bounds__(256) void k_gemv_finish(const float *__restrict__ p
 // Plan of the small-token forward: step depth (W), RG row groups per wave,
 // the K split (nsplit equal ranges of whole steps) and the number of
 // persistent workgroups.  Chosen from a sweep on MI355X over 8192 x 8192 and
-// 28672 x 8192 weights with 1, 8 and 32 tokens: 256-deep steps up to 16
-// tokens, one row group per wave for very few tokens (more waves in flight),
-// up to ~4096 work items of at most 16 K ranges.
+// 28672 x 8192 weights with 1, 8 and 32 tokens, rotating through more than
+// 512 MB of weight copies so that the 256 MB last-level cache cannot serve
+// them: 256-deep steps up to 16 tokens; more row groups per wave for wide
+// weights and more tokens (one activation load then serves several row
+// groups); 512 persistent workgroups up to 16 tokens, 256 beyond; up to
+// ~4096 work items of at most 16 K ranges.
 void nf4_gemv_plan(int64_t T, int64_t N, int64_t K, int *rg, int *w, int *nsplit, int *gmain) {
   int ww = T <= 16 ? 2 : 1;
   while (ww > 1 && K % (128 * ww) != 0) ww /= 2;
-  const int rr = T <= 4 ? 1 : (T <= 16 ? 2 : 4);
+  const bool wide = N >= 16384;
+  const int rr = T <= 4 ? (wide ? 2 : 1) : (T <= 16 ? (wide ? 4 : 2) : 4);
   const int64_t steps = K / (128 * ww);
   const int64_t tiles = (N + 64 * rr - 1) / (64 * rr);
   int64_t ns = 1;
   for (int64_t d = 1; d <= steps && d <= 16; ++d)
     if (steps % d == 0 && tiles * d <= 4096) ns = d;
   const int64_t items = tiles * ns;
-  const int64_t gm = T <= 4 ? 1024 : 512;
+  const int64_t gm = T <= 16 ? 512 : 256;
   *rg = rr;
   *w = ww;
   *nsplit = (int)ns;
