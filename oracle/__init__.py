@@ -77,6 +77,9 @@ def _load():
     lib.oracle_adamw_step.restype = None
     lib.oracle_merge.argtypes = [P, i64, i64, P, P, ctypes.c_int32, ctypes.c_float, P]
     lib.oracle_merge.restype = None
+    lib.oracle_linear_fwd_multi.argtypes = [P, i64, P, i64, i64, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                            P, P, ctypes.c_int32, P]
+    lib.oracle_linear_fwd_multi.restype = None
     _lib = lib
     return lib
 
@@ -315,3 +318,25 @@ def merge(W, A, B, alpha: float) -> np.ndarray:
     out = np.zeros((N, K), np.float64)
     _load().oracle_merge(_ptr(W), N, K, _ptr(A), _ptr(B), r, float(alpha), _ptr(out))
     return out
+
+
+# ----------------------------------------------------------- many adapters
+
+def linear_fwd_multi(X, Wdq: np.ndarray, A_pool, B_pool, alpha: float, seg, adapters) -> np.ndarray:
+    """Forward of a batch whose token segments use different adapters of a pool (binary64 Y [T, N]).
+
+    A_pool [n_pool, r, K], B_pool [n_pool, N, r]; tokens seg[s] .. seg[s+1]-1 use adapter adapters[s]
+    (outside [0, n_pool): none)."""
+    X, A_pool, B_pool = _f64(X), _f64(A_pool), _f64(B_pool)
+    Wdq = np.ascontiguousarray(Wdq, np.uint16)
+    T, K = X.shape
+    N = Wdq.shape[0]
+    n_pool, r = A_pool.shape[0], A_pool.shape[1]
+    assert A_pool.shape == (n_pool, r, K) and B_pool.shape == (n_pool, N, r)
+    seg = np.ascontiguousarray(seg, np.int32)
+    adapters = np.ascontiguousarray(adapters, np.int32)
+    assert seg.size == adapters.size + 1
+    Y = np.zeros((T, N), np.float64)
+    _load().oracle_linear_fwd_multi(_ptr(X), T, _ptr(Wdq), N, K, _ptr(A_pool), _ptr(B_pool), n_pool, r, float(alpha),
+                                    _ptr(seg), _ptr(adapters), adapters.size, _ptr(Y))
+    return Y

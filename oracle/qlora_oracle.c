@@ -29,6 +29,9 @@
  *  [OPT]  katajob, "What stays in full precision" (A and B keep ordinary AdamW
  *         state) and pranaymahendrakar, Developer level, "The walkthrough" (about
  *         8 bytes of Adam state per trainable parameter).
+ *  [MULTI] pranaymahendrakar, Researcher level, "The variants worth knowing":
+ *         one base model in memory, many adapters, requests for different
+ *         adapters batched together.
  *  [MERGE] "Module 08 - QLoRA & Quantization" (ainiketan), "7. A subtle but
  *         important deployment note"; katajob, "What it costs" (3. Merging).
  *  [DROP] "Module 08 - QLoRA & Quantization" (ainiketan), "4. QLoRA in code":
@@ -496,4 +499,53 @@ void oracle_merge(const double *W, int64_t N, int64_t K, const double *A, const 
       for (int32_t j = 0; j < r; ++j) acc += B[n * r + j] * A[(int64_t)j * K + k];
       Wm[n * K + k] = W[n * K + k] + s * acc;
     }
+}
+
+/* ------------------------------------------------------- many adapters */
+
+/*
+ * [MULTI] pranaymahendrakar, Researcher level, "The variants worth knowing":
+ * since the update is separable, one server holds one base model and many
+ * adapters and batches requests for different adapters together.  Tokens
+ * come in segments: tokens seg[s] .. seg[s+1]-1 use adapter ad[s] of a pool
+ * (A_pool [n_pool][r][K], B_pool [n_pool][N][r]); an adapter index outside
+ * [0, n_pool) means no adapter (the base product alone).  Per token t with
+ * adapter a, [LORA]'s layer:
+ *   U[t, j] = sum_k X[t, k] A_a[j, k]
+ *   Y[t, n] = sum_k X[t, k] W'[n, k] + s * sum_j U[t, j] B_a[n, j]
+ * Y [T, N] binary64.  Tokens outside every segment also get the base alone.
+ */
+void oracle_linear_fwd_multi(const double *X, int64_t T, const uint16_t *Wdq, int64_t N, int64_t K,
+                             const double *A_pool, const double *B_pool, int32_t n_pool, int32_t r, float alpha,
+                             const int32_t *seg, const int32_t *ad, int32_t n_seg, double *Y) {
+  const double s = (double)(alpha / (float)r);
+  int32_t *tok_ad = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+  for (int64_t t = 0; t < T; ++t) tok_ad[t] = -1;
+  for (int32_t g = 0; g < n_seg; ++g)
+    for (int64_t t = seg[g]; t < seg[g + 1] && t < T; ++t)
+      if (t >= 0) tok_ad[t] = (ad[g] >= 0 && ad[g] < n_pool) ? ad[g] : -1;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t t = 0; t < T; ++t) {
+    const double *x = X + t * K;
+    const int32_t a = tok_ad[t];
+    double *u = (double *)calloc((size_t)(r > 0 ? r : 1), sizeof(double));
+    if (a >= 0)
+      for (int32_t j = 0; j < r; ++j) {
+        const double *arow = A_pool + ((int64_t)a * r + j) * K;
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) acc += x[k] * arow[k];
+        u[j] = acc;
+      }
+    for (int64_t n = 0; n < N; ++n) {
+      const uint16_t *w = Wdq + n * K;
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k) acc += x[k] * bf16_to_f64(w[k]);
+      double lora = 0.0;
+      if (a >= 0)
+        for (int32_t j = 0; j < r; ++j) lora += u[j] * B_pool[((int64_t)a * N + n) * r + j];
+      Y[t * N + n] = acc + s * lora;
+    }
+    free(u);
+  }
+  free(tok_ad);
 }
