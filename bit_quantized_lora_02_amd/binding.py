@@ -6,7 +6,7 @@ in the library's gfx950 kernels.  There is no CPU or PyTorch fallback: if the
 library is missing or the device is not gfx950, calls raise.
 
 Names follow the C ABI: ``quantize_nf4``, ``dequant``, ``linear_fwd``,
-``linear_bwd``, ``linear_fwd_dropout``, ``linear_bwd_dropout``, ``adamw_step``, ``merge``, plus ``QLoRALinearFn`` (a torch.autograd.Function whose backward
+``linear_bwd``, ``linear_fwd_dropout``, ``linear_bwd_dropout``, ``linear_fwd_multi``, ``adamw_step``, ``merge``, plus ``QLoRALinearFn`` (a torch.autograd.Function whose backward
 returns gradients for X, A and B and none for the frozen NF4 weight).
 """
 from __future__ import annotations
@@ -28,6 +28,7 @@ QLORA_EHIP = -4
 OP_FWD = 0
 OP_BWD = 1
 OP_FWD_DROPOUT = 2
+OP_FWD_MULTI = 3
 MAX_RANK = 128
 
 EXPORTED = (
@@ -40,6 +41,7 @@ EXPORTED = (
     "qlora_linear_bwd",
     "qlora_linear_fwd_dropout",
     "qlora_linear_bwd_dropout",
+    "qlora_linear_fwd_multi",
     "qlora_adamw_step",
     "qlora_merge",
     "qlora_strerror",
@@ -104,6 +106,8 @@ def load_library() -> ctypes.CDLL:
         "qlora_adamw_step": ([ctypes.POINTER(_AdamTensor), i32, ctypes.c_double, ctypes.c_double, ctypes.c_double,
                               ctypes.c_double, ctypes.c_double, i64, P], ctypes.c_int),
         "qlora_merge": ([pnf4, P, i64, i64, P, P, i32, ctypes.c_float, P, P, P], ctypes.c_int),
+        "qlora_linear_fwd_multi": ([P, i64, pnf4, P, P, i32, i32, ctypes.c_float, P, P, i32, P, P, sz, P],
+                                   ctypes.c_int),
         "qlora_strerror": ([ctypes.c_int], ctypes.c_char_p),
         "qlora_last_error": ([], ctypes.c_char_p),
         "qlora_timing_enable": ([ctypes.c_char_p, ctypes.c_int], ctypes.c_int),
@@ -312,6 +316,34 @@ def linear_bwd_dropout(X: torch.Tensor, dY: torch.Tensor, w: NF4Weight, A: torch
                                                    _ptr(dB), _ptr(ws), nb, _stream(X.device)),
            "qlora_linear_bwd_dropout")
     return dX, dA, dB
+
+
+def linear_fwd_multi(X: torch.Tensor, w: NF4Weight, A_pool: torch.Tensor, B_pool: torch.Tensor, alpha: float,
+                     seg_offsets: torch.Tensor, seg_adapter: torch.Tensor, ws: torch.Tensor | None = None,
+                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y for a batch whose token segments use different adapters of a pool (A_pool [n, r, n_in],
+    B_pool [n, n_out, r]); seg_offsets int32 [n_seg + 1], seg_adapter int32 [n_seg] on the GPU."""
+    X, A_pool, B_pool = _bits(X), _bits(A_pool), _bits(B_pool)
+    T = X.shape[0]
+    n_pool, r = A_pool.shape[0], A_pool.shape[1]
+    if A_pool.shape != (n_pool, r, w.n_in) or B_pool.shape != (n_pool, w.n_out, r) or X.shape[1] != w.n_in:
+        raise ValueError("shape mismatch in linear_fwd_multi")
+    for t in (seg_offsets, seg_adapter):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError("segment tables must be contiguous int32 GPU tensors")
+    n_seg = seg_adapter.numel()
+    if seg_offsets.numel() != n_seg + 1:
+        raise ValueError("seg_offsets needs n_seg + 1 entries")
+    Y = out if out is not None else torch.empty((T, w.n_out), dtype=torch.bfloat16, device=X.device)
+    if ws is None:
+        ws, nb = _workspace(OP_FWD_MULTI, T, w, r)
+    else:
+        nb = ws.numel()
+    st = w.struct()
+    _check(load_library().qlora_linear_fwd_multi(_ptr(X), T, ctypes.byref(st), _ptr(A_pool), _ptr(B_pool), n_pool, r,
+                                                 float(alpha), _ptr(seg_offsets), _ptr(seg_adapter), n_seg, _ptr(Y),
+                                                 _ptr(ws), nb, _stream(X.device)), "qlora_linear_fwd_multi")
+    return Y
 
 
 def merge(A: torch.Tensor, B: torch.Tensor, alpha: float, w: NF4Weight | None = None,

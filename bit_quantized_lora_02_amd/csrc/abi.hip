@@ -235,9 +235,15 @@ Plan make_plan(int op, int64_t T, int64_t N, int64_t K, int32_t r) {
   p.off_v = off;  // fwd: V = bf16(s U) padded; bwd: U padded
   off = up(off + (size_t)(T * p.rp * 2), kAlign);
   size_t part = 0;
-  if (op == QLORA_OP_FWD || op == QLORA_OP_FWD_DROPOUT) {
+  if (op == QLORA_OP_FWD || op == QLORA_OP_FWD_DROPOUT || op == QLORA_OP_FWD_MULTI) {
     p.su = plan_skinny(T, K);
     part = (size_t)p.su.n * T * p.rn * 4;
+    if (op == QLORA_OP_FWD_MULTI && use_gemv(T, K)) {  // U by segments first; its partials are dead before the GEMV's
+      p.gemv = true;
+      nf4_gemv_plan(T, N, K, &p.gemv_rg, &p.gemv_w, &p.gemv_split, &p.gemv_main);
+      const size_t gp = (size_t)p.gemv_split * T * N * 4;
+      part = part > gp ? part : gp;
+    }
     if (op == QLORA_OP_FWD && use_gemv(T, K)) {  // dropout needs the adapter input's own pass
       p.gemv = true;
       nf4_gemv_plan(T, N, K, &p.gemv_rg, &p.gemv_w, &p.gemv_split, &p.gemv_main);
@@ -345,7 +351,7 @@ int qlora_nf4_codebook(float levels[16]) {
 
 int qlora_workspace_bytes(int op, int64_t T, int64_t n_out, int64_t n_in, int32_t r, size_t *bytes) {
   if (!bytes) return fail(QLORA_EINVAL, "bytes is NULL");
-  if (op != QLORA_OP_FWD && op != QLORA_OP_BWD && op != QLORA_OP_FWD_DROPOUT)
+  if (op != QLORA_OP_FWD && op != QLORA_OP_BWD && op != QLORA_OP_FWD_DROPOUT && op != QLORA_OP_FWD_MULTI)
     return fail(QLORA_EINVAL, "unknown op %d", op);
   if (T < 0 || T > kMaxDim || n_out < 8 || n_out % 8 != 0 || n_out > kMaxDim || n_in < 64 || n_in % 64 != 0 ||
       n_in > kMaxDim || r < 1 || r > QLORA_MAX_RANK)
@@ -518,6 +524,50 @@ int qlora_linear_bwd(const qlora_bf16 *X, const qlora_bf16 *dY, int64_t T, const
                      const qlora_bf16 *B, int32_t r, float alpha, const qlora_bf16 *U, qlora_bf16 *dX,
                      qlora_bf16 *dA, qlora_bf16 *dB, void *ws, size_t ws_bytes, void *stream) {
   return linear_bwd(X, dY, T, q, A, B, r, alpha, nullptr, U, dX, dA, dB, ws, ws_bytes, stream);
+}
+
+int qlora_linear_fwd_multi(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const qlora_bf16 *A_pool,
+                           const qlora_bf16 *B_pool, int32_t n_pool, int32_t r, float alpha, const int32_t *seg_offsets,
+                           const int32_t *seg_adapter, int32_t n_seg, qlora_bf16 *Y, void *ws, size_t ws_bytes,
+                           void *stream) {
+  int rc = check_lora_args(T, q, A_pool, B_pool, r, alpha);
+  if (rc) return rc;
+  if (r % 8 != 0) return fail(QLORA_EINVAL, "r must be a multiple of 8 for adapter pools (got %d)", (int)r);
+  if (n_pool < 1) return fail(QLORA_EINVAL, "n_pool must be >= 1 (got %d)", (int)n_pool);
+  if (n_seg < 1 || n_seg > (1 << 24)) return fail(QLORA_EINVAL, "n_seg must be in [1, 2^24] (got %d)", (int)n_seg);
+  if (!seg_offsets || !seg_adapter || ((uintptr_t)seg_offsets & 3) || ((uintptr_t)seg_adapter & 3))
+    return fail(QLORA_EINVAL, "segment arrays must be non-NULL and 4-byte aligned");
+  if (T > 0 && (!X || !Y)) return fail(QLORA_EINVAL, "X and Y must not be NULL");
+  if ((X && !aligned16(X)) || (Y && !aligned16(Y))) return fail(QLORA_EINVAL, "X and Y must be 16-byte aligned");
+  const int64_t N = q->n_out, K = q->n_in;
+  Plan p;
+  if ((rc = check_ws(QLORA_OP_FWD_MULTI, T, N, K, r, ws, ws_bytes, &p))) return rc;
+  if ((rc = check_device(nullptr))) return rc;
+  if (T == 0) return QLORA_OK;
+  hipStream_t s = (hipStream_t)stream;
+  char *w = (char *)ws;
+  bf16_t *V = (bf16_t *)(w + p.off_v);
+  float *part = (float *)(w + p.off_part);
+  const float sc = alpha / (float)r;
+  const Levels &lv = codebook().lv;
+  SegTable sg;
+  sg.seg = seg_offsets;
+  sg.ad = seg_adapter;
+  sg.n_seg = n_seg;
+  sg.n_pool = n_pool;
+  // U = X A_a^T per segment, then V = bf16(s U), zero-padded to rp columns
+  LAUNCH("lora_u_multi", launch_skinny_grouped(p.rn, X, K, T, A_pool, K, (int64_t)r * K, r, K, p.su.kchunk, p.su.n,
+                                               sg, part, s));
+  LAUNCH("lora_u_finalize", launch_finalize(part, p.su.n, T, p.rn, nullptr, 0, 0, 1.0f, V, p.rp, p.rp, r, sc, s));
+  if (p.gemv) {
+    LAUNCH("nf4_gemv", launch_nf4_gemv(X, T, K, q->codes, q->absmax_q, q->absmax_step, N, p.gemv_rg, p.gemv_w,
+                                       p.gemv_split, p.gemv_main, A_pool, r, part, nullptr, lv, s, false));
+    LAUNCH("gemv_finish", launch_gemv_finish_multi(part, p.gemv_split, T, N, V, p.rp, B_pool, r, sg, Y, s));
+    return QLORA_OK;
+  }
+  LAUNCH("nf4_gemm_fwd", launch_nf4_gemm_fwd(nf4_gemm_pick_tile(T, N), X, T, K, q->codes, q->absmax_q,
+                                             q->absmax_step, N, V, B_pool, r, r, p.rp, Y, lv, s, sg));
+  return QLORA_OK;
 }
 
 int qlora_linear_fwd_dropout(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const qlora_bf16 *A,

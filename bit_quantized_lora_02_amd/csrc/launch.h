@@ -29,6 +29,17 @@ hipError_t launch_quantize_nf4(const float *W, int64_t n_out, int64_t n_in, uint
 hipError_t launch_dequant(const uint8_t *codes, const uint8_t *absmax_q, const float *absmax_step, int64_t n_out,
                           int64_t n_in, bf16_t *out, const Levels &lv, hipStream_t s);
 
+// Token segments of a batch that uses several adapters of a pool: tokens
+// seg[g] .. seg[g+1]-1 use adapter ad[g] (outside [0, n_pool): none).  Device
+// arrays; kernels clamp every entry, so a malformed table cannot make them
+// read or write out of bounds.
+struct SegTable {
+  const int32_t *seg = nullptr;  // [n_seg + 1]
+  const int32_t *ad = nullptr;   // [n_seg]
+  int n_seg = 0;
+  int n_pool = 0;
+};
+
 // Output-tile shapes of the fused NF4 GEMMs (rows x columns of the output).
 enum {
   NF4_TILE_128x128 = 0,
@@ -39,10 +50,12 @@ enum {
 };
 int nf4_gemm_pick_tile(int64_t M, int64_t N);
 
+// Y = X W'^T + V Bp^T; with a segment table (sg.seg non-null) the rows of each
+// segment use B = Bp + ad * N * r (ldb = r), and rows without an adapter none.
 hipError_t launch_nf4_gemm_fwd(int tile, const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes,
                                const uint8_t *absmax_q, const float *step, int64_t N, const bf16_t *V,
                                const bf16_t *Bp, int64_t ldb, int64_t r, int64_t rp, bf16_t *Y, const Levels &lv,
-                               hipStream_t s);
+                               hipStream_t s, const SegTable &sg = SegTable());
 // dX = dY W' + G o (dUp A); with `mask` (keep bits of X, byte (t K + k) / 8,
 // bit k % 8) G = keep * q, without it G = 1.
 hipError_t launch_nf4_gemm_dx(int tile, const bf16_t *dY, int64_t T, int64_t N, const uint8_t *codes,
@@ -61,11 +74,18 @@ hipError_t launch_merge(const uint8_t *codes, const uint8_t *absmax_q, const flo
 // partials in range order, forms V = bf16(s U), adds V B^T and rounds Y.
 constexpr int64_t kGemvMaxT = 64;
 void nf4_gemv_plan(int64_t T, int64_t N, int64_t K, int *rg, int *w, int *nsplit, int *gmain);
+// (with_u false: no U workgroups; the caller forms V itself)
 hipError_t launch_nf4_gemv(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
                            const float *step, int64_t N, int rg, int w, int nsplit, int gmain, const bf16_t *A,
-                           int64_t r, float *part, float *upart, const Levels &lv, hipStream_t s);
+                           int64_t r, float *part, float *upart, const Levels &lv, hipStream_t s,
+                           bool with_u = true);
 hipError_t launch_gemv_finish(const float *part, const float *upart, int nsplit, int64_t T, int64_t N,
                               const bf16_t *B, int64_t r, float s, bf16_t *Y, bf16_t *U_out, hipStream_t st);
+// Many adapters: Y = bf16(sum of the weight partials + V[t] B_a^T) with V [T, ldv] given and
+// B_a = B_pool + a N r for the adapter a of token t's segment (none: the partials alone).
+hipError_t launch_gemv_finish_multi(const float *part, int nsplit, int64_t T, int64_t N, const bf16_t *V,
+                                    int64_t ldv, const bf16_t *B_pool, int64_t r, const SegTable &sg, bf16_t *Y,
+                                    hipStream_t st);
 
 // Dropout on the adapter input P (a dense row-major [rows, ld] activation):
 // 8-element chunk c of P (flat element index / 8) has its keep bits in byte c
@@ -86,6 +106,11 @@ void skinny_plan(int64_t M, int64_t Kred, int *nsplit, int64_t *kchunk);
 hipError_t launch_skinny(bool pt, bool qt, int rn, const bf16_t *P, int64_t ldp, int64_t M, const bf16_t *Q,
                          int64_t ldq, int64_t Rv, int64_t Kred, int64_t kchunk, int nsplit, float *C, hipStream_t s,
                          int drop = DROP_NONE, const DropParams &dp = DropParams());
+// U of a batch with many adapters: C[split][t][j] = sum over the range of P[t, k] Q_a[j, k] with
+// Q_a = Q_pool + a q_stride for token t's adapter a (rows P [M, ldp], Q_a [r, ldq]; none: zero).
+hipError_t launch_skinny_grouped(int rn, const bf16_t *P, int64_t ldp, int64_t M, const bf16_t *Q_pool, int64_t ldq,
+                                 int64_t q_stride, int64_t Rv, int64_t Kred, int64_t kchunk, int nsplit,
+                                 const SegTable &sg, float *C, hipStream_t s);
 hipError_t launch_finalize(const float *part, int nsplit, int64_t M, int64_t N, bf16_t *out1, int64_t ld1, int64_t n1,
                            float scale1, bf16_t *out2, int64_t ld2, int64_t n2, int64_t nvalid2, float scale2,
                            hipStream_t s, bool trans1 = false);

@@ -98,10 +98,15 @@ __device__ __forceinline__ u32x4_t apply_keep(const u32x4_t &v, uint32_t bits, f
 }
 }  // namespace
 
-template <bool PT, bool QT, int RN, int DM>
+// Many adapters (GR): workgroup x takes the x-th 128-row tile of the token
+// segments in order (tiles never straddle a segment), with Q the segment's
+// adapter Q + a q_stride (none: Rv = 0, all zero); rows past the segment read
+// as zero and are not stored.
+template <bool PT, bool QT, int RN, int DM, bool GR = false>
 __global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, int64_t ldp, int64_t M,
                                                 const bf16_t *__restrict__ Q, int64_t ldq, int64_t Rv, int64_t Kred,
-                                                int64_t kchunk, float *__restrict__ C, DropParams dp) {
+                                                int64_t kchunk, float *__restrict__ C, DropParams dp,
+                                                SegTable sg, int64_t q_stride) {
   constexpr int LDP = PT ? SBM + 16 : SK;             // LDS row length of the P tile (elements)
   constexpr int LDQ = QT ? RN + (RN >= 32 ? 16 : 0) : SK;
   constexpr int P_ROWS = PT ? SK : SBM;
@@ -113,7 +118,30 @@ __global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, in
   __shared__ __attribute__((aligned(16))) bf16_t sP[2][P_ROWS * LDP];
   __shared__ __attribute__((aligned(16))) bf16_t sQ[2][Q_ROWS * LDQ];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t m0 = (int64_t)blockIdx.x * SBM;
+  int64_t m0 = (int64_t)blockIdx.x * SBM, mend = M;
+  if constexpr (GR) {
+    int64_t b = blockIdx.x, lo = 0, hi = 0;
+    int g = -1;
+    for (int h = 0; h < sg.n_seg; ++h) {
+      int64_t a0 = sg.seg[h], a1 = sg.seg[h + 1];
+      a0 = a0 < 0 ? 0 : (a0 > M ? M : a0);
+      a1 = a1 < a0 ? a0 : (a1 > M ? M : a1);
+      const int64_t nt = (a1 - a0 + SBM - 1) / SBM;
+      if (b < nt) {
+        g = h;
+        lo = a0;
+        hi = a1;
+        break;
+      }
+      b -= nt;
+    }
+    if (g < 0) return;  // past the last tile (the grid is an upper bound)
+    m0 = lo + b * SBM;
+    mend = (m0 + SBM < hi) ? m0 + SBM : hi;
+    const int a = sg.ad[g];
+    if (a >= 0 && a < sg.n_pool) Q += (int64_t)a * q_stride;
+    else Rv = 0;
+  }
   const int64_t kb = (int64_t)blockIdx.y * kchunk;
   const int64_t ke = (kb + kchunk < Kred) ? kb + kchunk : Kred;
   const int nsteps = (int)((ke - kb + SK - 1) / SK);
@@ -138,7 +166,7 @@ __global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, in
         src = P + k * ldp + m;
       } else {
         const int64_t m = m0 + (c >> 3), k = k0 + (c & 7) * 8;
-        ok = m < M && k < ke;
+        ok = m < mend && k < ke;
         src = P + m * ldp + k;
       }
       rp_[i] = ok ? *reinterpret_cast<const u32x4_t *>(src) : u32x4_t{0u, 0u, 0u, 0u};
@@ -248,7 +276,7 @@ __global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, in
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t m = m0 + wave * 32 + i * 16 + 4 * g + e;
-        if (m < M) Cs[m * RN + j * 16 + a] = acc[i][j][e];
+        if (m < mend) Cs[m * RN + j * 16 + a] = acc[i][j][e];
       }
 }
 
@@ -378,10 +406,10 @@ static hipError_t skinny_dispatch(int rn, dim3 grid, hipStream_t s, const bf16_t
                                   const bf16_t *Q, int64_t ldq, int64_t Rv, int64_t Kred, int64_t kchunk, float *C,
                                   const DropParams &dp) {
   switch (rn) {
-    case 16: launch((k_skinny<PT, QT, 16, DM>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp); break;
-    case 32: launch((k_skinny<PT, QT, 32, DM>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp); break;
-    case 64: launch((k_skinny<PT, QT, 64, DM>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp); break;
-    default: launch((k_skinny<PT, QT, 128, DM>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp); break;
+    case 16: launch((k_skinny<PT, QT, 16, DM>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp, SegTable(), (int64_t)0); break;
+    case 32: launch((k_skinny<PT, QT, 32, DM>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp, SegTable(), (int64_t)0); break;
+    case 64: launch((k_skinny<PT, QT, 64, DM>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp, SegTable(), (int64_t)0); break;
+    default: launch((k_skinny<PT, QT, 128, DM>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp, SegTable(), (int64_t)0); break;
   }
   return hipGetLastError();
 }
@@ -403,6 +431,33 @@ hipError_t launch_skinny(bool pt, bool qt, int rn, const bf16_t *P, int64_t ldp,
   if (!pt && qt) return skinny_dispatch<false, true, DROP_NONE>(rn, grid, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp);
   if (pt && !qt) return skinny_dispatch<true, false, DROP_NONE>(rn, grid, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp);
   return skinny_dispatch<true, true, DROP_NONE>(rn, grid, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp);
+}
+
+hipError_t launch_skinny_grouped(int rn, const bf16_t *P, int64_t ldp, int64_t M, const bf16_t *Q_pool, int64_t ldq,
+                                 int64_t q_stride, int64_t Rv, int64_t Kred, int64_t kchunk, int nsplit,
+                                 const SegTable &sg, float *C, hipStream_t s) {
+  if (M == 0 || nsplit == 0 || sg.n_seg == 0) return hipSuccess;
+  const dim3 grid((unsigned)((M + SBM - 1) / SBM + sg.n_seg), (unsigned)nsplit);  // tiles of all segments, at most
+  const DropParams dp;
+  switch (rn) {
+    case 16:
+      launch((k_skinny<false, false, 16, DROP_NONE, true>), grid, dim3(256), 0, s, P, ldp, M, Q_pool, ldq, Rv, Kred,
+             kchunk, C, dp, sg, q_stride);
+      break;
+    case 32:
+      launch((k_skinny<false, false, 32, DROP_NONE, true>), grid, dim3(256), 0, s, P, ldp, M, Q_pool, ldq, Rv, Kred,
+             kchunk, C, dp, sg, q_stride);
+      break;
+    case 64:
+      launch((k_skinny<false, false, 64, DROP_NONE, true>), grid, dim3(256), 0, s, P, ldp, M, Q_pool, ldq, Rv, Kred,
+             kchunk, C, dp, sg, q_stride);
+      break;
+    default:
+      launch((k_skinny<false, false, 128, DROP_NONE, true>), grid, dim3(256), 0, s, P, ldp, M, Q_pool, ldq, Rv, Kred,
+             kchunk, C, dp, sg, q_stride);
+      break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_pad_copy(const bf16_t *in, int64_t ldi, int64_t ncols, int64_t M, bf16_t *out, int64_t ldo,

@@ -207,18 +207,18 @@ __device__ __forceinline__ void mma_rows(int i0, int i1, const u32x4_t (&a)[C::W
 
 // Rows [row0, row0+BM) x columns [col0, col0+64) of a row-major bf16 matrix
 // into registers and LDS (the unpipelined LoRA steps): chunk c = tid + NT*i
-// covers row c>>3, 16-byte chunk c&7.  Rows >= rows or columns >= cols read
-// as zero (cols % 8 == 0).
+// covers row c>>3, 16-byte chunk c&7.  Rows >= rows (or < row_lo) or columns
+// >= cols read as zero (cols % 8 == 0).
 template <class C>
 __device__ __forceinline__ void copy_a_tile(const bf16_t *__restrict__ src, int64_t ld, int64_t row0, int64_t rows,
-                                            int64_t col0, int64_t cols, int tid, bf16_t *s) {
+                                            int64_t col0, int64_t cols, int tid, bf16_t *s, int64_t row_lo = 0) {
   u32x4_t r[C::A_LD];
 #pragma unroll
   for (int i = 0; i < C::A_LD; ++i) {
     const int c = tid + C::NT * i;
     const int64_t row = row0 + (c >> 3), col = col0 + (c & 7) * 8;
-    r[i] = (row < rows && col < cols) ? *reinterpret_cast<const u32x4_t *>(src + row * ld + col)
-                                      : u32x4_t{0u, 0u, 0u, 0u};
+    r[i] = (row >= row_lo && row < rows && col < cols) ? *reinterpret_cast<const u32x4_t *>(src + row * ld + col)
+                                                       : u32x4_t{0u, 0u, 0u, 0u};
   }
 #pragma unroll
   for (int i = 0; i < C::A_LD; ++i) {
@@ -324,14 +324,14 @@ __device__ __forceinline__ void pipelined_step(const bf16_t *sa, const bf16_t *s
 
 // ---------------------------------------------------------------- forward
 // Y[T, N] = X[T, K] . W'[N, K]^T + V[T, rp] . B[N, :r]^T   (B row stride ldb, columns >= r read as 0)
-template <class C>
+template <class C, bool MULTI>
 __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict__ X, int64_t T, int64_t K,
                                                         const uint8_t *__restrict__ codes,
                                                         const uint8_t *__restrict__ absmax_q,
                                                         const float *__restrict__ step, int64_t N,
                                                         const bf16_t *__restrict__ V, const bf16_t *__restrict__ Bp,
                                                         int64_t ldb, int64_t r, int64_t rp, bf16_t *__restrict__ Y,
-                                                        Levels lv, int xb_m, int xb_n) {
+                                                        Levels lv, int xb_m, int xb_n, SegTable sg) {
   __shared__ __attribute__((aligned(16))) bf16_t sA0[C::BM * BK];
   __shared__ __attribute__((aligned(16))) bf16_t sA1[C::BM * BK];
   __shared__ __attribute__((aligned(16))) bf16_t sB0[C::BN * BK];
@@ -404,26 +404,48 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
   }
   if (s < nk) step_p(std::integral_constant<int, 0>(), s);
 
-  // LoRA up-projection: V [T, rp] . Bp [N, rp]^T, one 64-deep step at a time
-  for (int64_t k0 = 0; k0 < rp; k0 += BK) {
-    copy_a_tile<C>(V, rp, m0, T, k0, rp, tid, sA[0]);
+  // LoRA up-projection: V [T, rp] . B [N, rp]^T over the rows [lo, hi), one 64-deep step at a time
+  auto lora_rows = [&](const bf16_t *__restrict__ Bsrc, int64_t lo, int64_t hi) {
+    for (int64_t k0 = 0; k0 < rp; k0 += BK) {
+      copy_a_tile<C>(V, rp, m0, hi, k0, rp, tid, sA[0], lo);
 #pragma unroll
-    for (int i = 0; i < C::L_CH; ++i) {
-      const int c = tid + C::NT * i;
-      const int64_t brw = n0 + (c >> 3), col = k0 + (c & 7) * 8;  // r % 8 == 0 or B padded to ldb
-      const u32x4_t v = (brw < N && col < r) ? *reinterpret_cast<const u32x4_t *>(Bp + brw * ldb + col)
-                                             : u32x4_t{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4_t *>(sB[0] + lds_off(c >> 3, c & 7)) = v;
-    }
-    __syncthreads();
+      for (int i = 0; i < C::L_CH; ++i) {
+        const int c = tid + C::NT * i;
+        const int64_t brw = n0 + (c >> 3), col = k0 + (c & 7) * 8;  // r % 8 == 0 or B padded to ldb
+        const u32x4_t v = (brw < N && col < r) ? *reinterpret_cast<const u32x4_t *>(Bsrc + brw * ldb + col)
+                                               : u32x4_t{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4_t *>(sB[0] + lds_off(c >> 3, c & 7)) = v;
+      }
+      __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      u32x4_t a[C::WM], b[C::WN];
-      read_a<C>(sA[0], wm, lane, kk, a);
-      read_b_rows<C>(sB[0], wn, lane, kk, b);
-      mma_rows<C>(0, C::WM, a, b, acc);
+      for (int kk = 0; kk < 4; ++kk) {
+        u32x4_t a[C::WM], b[C::WN];
+        read_a<C>(sA[0], wm, lane, kk, a);
+        read_b_rows<C>(sB[0], wn, lane, kk, b);
+        mma_rows<C>(0, C::WM, a, b, acc);
+      }
+      __syncthreads();
     }
-    __syncthreads();
+  };
+  if constexpr (!MULTI) {
+    lora_rows(Bp, 0, T);
+  } else {
+    // many adapters: one masked up-projection per token segment that meets this tile's rows
+    // (first segment ending past m0 by bisection; entries clamped to [0, T])
+    auto clampT = [&](int64_t v) { return v < 0 ? (int64_t)0 : (v > T ? T : v); };
+    int g0 = 0, g1 = sg.n_seg;
+    while (g0 < g1) {
+      const int mid = (g0 + g1) >> 1;
+      if (clampT(sg.seg[mid + 1]) <= m0) g0 = mid + 1;
+      else g1 = mid;
+    }
+    for (int g = g0; g < sg.n_seg; ++g) {
+      const int64_t lo = clampT(sg.seg[g]), hi = clampT(sg.seg[g + 1]);
+      if (lo >= m0 + C::BM) break;
+      const int a = sg.ad[g];
+      if (hi <= lo || hi <= m0 || a < 0 || a >= sg.n_pool) continue;
+      lora_rows(Bp + (int64_t)a * N * r, lo, hi);
+    }
   }
   store_out<C>(Y, N, m0, T, n0, N, wm, wn, lane, acc);
 }
@@ -649,12 +671,16 @@ void xcd_blocking(int64_t tiles_m, int64_t tiles_n, double a_bytes, double b_byt
 template <class C>
 hipError_t fwd_with(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
                     const float *step, int64_t N, const bf16_t *V, const bf16_t *Bp, int64_t ldb, int64_t r,
-                    int64_t rp, bf16_t *Y, const Levels &lv, hipStream_t s) {
+                    int64_t rp, bf16_t *Y, const Levels &lv, hipStream_t s, const SegTable &sg) {
   const int64_t tm = (T + C::BM - 1) / C::BM, tn = (N + C::BN - 1) / C::BN;
   int xb_m, xb_n;
   xcd_blocking(tm, tn, 2.0 * T * K, 0.516 * N * K, &xb_m, &xb_n);
-  launch(k_nf4_gemm_fwd<C>, dim3((unsigned)(tm * tn)), dim3(C::NT), 0, s, X, T, K, codes, absmax_q, step,
-                     N, V, Bp, ldb, r, rp, Y, lv, xb_m, xb_n);
+  if (sg.seg)
+    launch(k_nf4_gemm_fwd<C, true>, dim3((unsigned)(tm * tn)), dim3(C::NT), 0, s, X, T, K, codes, absmax_q, step, N,
+           V, Bp, ldb, r, rp, Y, lv, xb_m, xb_n, sg);
+  else
+    launch(k_nf4_gemm_fwd<C, false>, dim3((unsigned)(tm * tn)), dim3(C::NT), 0, s, X, T, K, codes, absmax_q, step, N,
+           V, Bp, ldb, r, rp, Y, lv, xb_m, xb_n, sg);
   return hipGetLastError();
 }
 
@@ -685,14 +711,18 @@ int nf4_gemm_pick_tile(int64_t M, int64_t N) {
 hipError_t launch_nf4_gemm_fwd(int tile, const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes,
                                const uint8_t *absmax_q, const float *step, int64_t N, const bf16_t *V,
                                const bf16_t *Bp, int64_t ldb, int64_t r, int64_t rp, bf16_t *Y, const Levels &lv,
-                               hipStream_t s) {
+                               hipStream_t s, const SegTable &sg) {
   if (T == 0) return hipSuccess;
   switch (tile) {
-    case NF4_TILE_256x256_W8: return fwd_with<T256x256w8>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s);
-    case NF4_TILE_256x128_W8: return fwd_with<T256x128w8>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s);
-    case NF4_TILE_128x256_W8: return fwd_with<T128x256w8>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s);
-    case NF4_TILE_128x128_W8: return fwd_with<T128x128w8>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s);
-    default: return fwd_with<T128x128>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s);
+    case NF4_TILE_256x256_W8:
+      return fwd_with<T256x256w8>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s, sg);
+    case NF4_TILE_256x128_W8:
+      return fwd_with<T256x128w8>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s, sg);
+    case NF4_TILE_128x256_W8:
+      return fwd_with<T128x256w8>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s, sg);
+    case NF4_TILE_128x128_W8:
+      return fwd_with<T128x128w8>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s, sg);
+    default: return fwd_with<T128x128>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s, sg);
   }
 }
 

@@ -298,6 +298,70 @@ __global__ __launch_bounds__(256) void k_gemv_finish(const float *__restrict__ p
   Y[t * N + n] = f32_to_bf16(y + l);
 }
 
+// Many adapters: workgroup (x, t) finds token t's segment by bisection (entries
+// clamped to [0, T]); then for its 256 outputs n
+// Y[t, n] = bf16(sum over p (in order) of part[p][t][n] + V[t, :] . B_a[n, :]),
+// V [T, ldv] bf16 (already s U), B_a = B_pool + a N r, or the partials alone
+// when the segment has no adapter (or the token no segment).
+__global__ __launch_bounds__(256) void k_gemv_finish_multi(const float *__restrict__ part, int nsplit, int64_t T,
+                                                           int64_t N, const bf16_t *__restrict__ V, int64_t ldv,
+                                                           const bf16_t *__restrict__ B_pool, int64_t r, SegTable sg,
+                                                           bf16_t *__restrict__ Y) {
+  __shared__ float s_v[QLORA_MAX_RANK];
+  const int tid = threadIdx.x;
+  const int64_t t = blockIdx.y;
+  auto clampT = [&](int64_t v) { return v < 0 ? (int64_t)0 : (v > T ? T : v); };
+  int g0 = 0, g1 = sg.n_seg;  // first segment ending past t
+  while (g0 < g1) {
+    const int mid = (g0 + g1) >> 1;
+    if (clampT(sg.seg[mid + 1]) <= t) g0 = mid + 1;
+    else g1 = mid;
+  }
+  int a = -1;
+  if (g0 < sg.n_seg && clampT(sg.seg[g0]) <= t) a = sg.ad[g0];
+  const bool has = a >= 0 && a < sg.n_pool;
+  if (tid < r) s_v[tid] = has ? bf16_lo_to_f32(V[t * ldv + tid]) : 0.f;
+  __syncthreads();
+  const int64_t n = (int64_t)blockIdx.x * 256 + tid;
+  if (n >= N) return;
+  float y = 0.f;
+  {  // all loads first, then the additions in split order
+    const float *src = part + t * N + n;
+    const int64_t stride = T * N;
+    int p = 0;
+    for (; p + 8 <= nsplit; p += 8) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = src[(int64_t)(p + q) * stride];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) y += v[q];
+    }
+    for (; p < nsplit; ++p) y += src[(int64_t)p * stride];
+  }
+  float l = 0.f;
+  if (has) {
+    const bf16_t *brow = B_pool + ((int64_t)a * N + n) * r;  // r % 8 == 0: 16-byte rows
+    for (int64_t j = 0; j < r; j += 8) {
+      const u32x4_t w = *reinterpret_cast<const u32x4_t *>(brow + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        l = fmaf(s_v[j + 2 * e], bf16_lo_to_f32(w[e]), l);
+        l = fmaf(s_v[j + 2 * e + 1], bf16_hi_to_f32(w[e]), l);
+      }
+    }
+  }
+  Y[t * N + n] = f32_to_bf16(y + l);
+}
+
+hipError_t launch_gemv_finish_multi(const float *part, int nsplit, int64_t T, int64_t N, const bf16_t *V,
+                                    int64_t ldv, const bf16_t *B_pool, int64_t r, const SegTable &sg, bf16_t *Y,
+                                    hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  dim3 grid((unsigned)((N + 255) / 256), (unsigned)T);
+  launch(k_gemv_finish_multi, grid, dim3(256), 0, st, part, nsplit, T, N, V, ldv, B_pool, r, sg, Y);
+  return hipGetLastError();
+}
+
 // Plan of the small-token forward: step depth (W), RG row groups per wave,
 // the K split (nsplit equal ranges of whole steps) and the number of
 // persistent workgroups.  Chosen from a sweep on MI355X over 8192 x 8192 and
@@ -328,31 +392,31 @@ void nf4_gemv_plan(int64_t T, int64_t N, int64_t K, int *rg, int *w, int *nsplit
 template <int MT, int RG, int W>
 static void gemv_with(hipStream_t s, const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes,
                       const uint8_t *absmax_q, const float *step, int64_t N, int nsplit, int gmain, const bf16_t *A,
-                      int64_t r, float *part, float *upart, const Levels &lv) {
-  launch(k_nf4_gemv<MT, RG, W>, dim3((unsigned)(gmain + nsplit)), dim3(256), 0, s, X, T, K, codes, absmax_q, step, N,
-         nsplit, gmain, A, r, part, upart, lv);
+                      int64_t r, float *part, float *upart, const Levels &lv, bool with_u) {
+  launch(k_nf4_gemv<MT, RG, W>, dim3((unsigned)(gmain + (with_u ? nsplit : 0))), dim3(256), 0, s, X, T, K, codes,
+         absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv);
 }
 
 template <int MT, int W>
 static void gemv_rg(int rg, hipStream_t s, const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes,
                     const uint8_t *absmax_q, const float *step, int64_t N, int nsplit, int gmain, const bf16_t *A,
-                    int64_t r, float *part, float *upart, const Levels &lv) {
-  if (rg == 4) gemv_with<MT, 4, W>(s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv);
-  else if (rg == 2) gemv_with<MT, 2, W>(s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv);
-  else gemv_with<MT, 1, W>(s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv);
+                    int64_t r, float *part, float *upart, const Levels &lv, bool with_u) {
+  if (rg == 4) gemv_with<MT, 4, W>(s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv, with_u);
+  else if (rg == 2) gemv_with<MT, 2, W>(s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv, with_u);
+  else gemv_with<MT, 1, W>(s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv, with_u);
 }
 
 hipError_t launch_nf4_gemv(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
                            const float *step, int64_t N, int rg, int w, int nsplit, int gmain, const bf16_t *A,
-                           int64_t r, float *part, float *upart, const Levels &lv, hipStream_t s) {
+                           int64_t r, float *part, float *upart, const Levels &lv, hipStream_t s, bool with_u) {
   if (T == 0) return hipSuccess;
   if (T <= 16) {
-    if (w == 2) gemv_rg<1, 2>(rg, s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv);
-    else gemv_rg<1, 1>(rg, s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv);
+    if (w == 2) gemv_rg<1, 2>(rg, s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv, with_u);
+    else gemv_rg<1, 1>(rg, s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv, with_u);
   } else if (T <= 32) {
-    gemv_rg<2, 1>(rg, s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv);
+    gemv_rg<2, 1>(rg, s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv, with_u);
   } else {
-    gemv_rg<4, 1>(rg, s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv);
+    gemv_rg<4, 1>(rg, s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv, with_u);
   }
   return hipGetLastError();
 }

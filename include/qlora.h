@@ -55,6 +55,7 @@ typedef uint16_t qlora_bf16; /* bf16 bit pattern */
 #define QLORA_OP_FWD 0
 #define QLORA_OP_BWD 1
 #define QLORA_OP_FWD_DROPOUT 2 /* qlora_linear_fwd_dropout; its backward uses QLORA_OP_BWD */
+#define QLORA_OP_FWD_MULTI 3   /* qlora_linear_fwd_multi */
 
 #define QLORA_MAX_RANK 128
 
@@ -95,7 +96,7 @@ int qlora_nf4_storage(int64_t n_out, int64_t n_in, size_t *codes_bytes, size_t *
  * (katajob, "NF4": levels placed for a zero-centred normal). */
 int qlora_nf4_codebook(float levels[16]);
 
-/* Workspace bytes needed by `op` (QLORA_OP_FWD, QLORA_OP_BWD or QLORA_OP_FWD_DROPOUT) for these
+/* Workspace bytes needed by `op` (a QLORA_OP_* value) for these
  * sizes, into host *bytes (no HIP call).  The forward workspace is O(T*r + n_out*r),
  * never O(n_out*n_in): the dequantized weight is never stored. */
 int qlora_workspace_bytes(int op, int64_t T, int64_t n_out, int64_t n_in, int32_t r, size_t *bytes);
@@ -185,6 +186,30 @@ int qlora_linear_bwd_dropout(const qlora_bf16 *X, const qlora_bf16 *dY, int64_t 
                              const qlora_bf16 *A, const qlora_bf16 *B, int32_t r, float alpha, float p,
                              const uint8_t *mask, const qlora_bf16 *U, qlora_bf16 *dX, qlora_bf16 *dA,
                              qlora_bf16 *dB, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Forward of a batch whose tokens use different adapters over one NF4 base
+ * (pranaymahendrakar, Researcher level, "The variants worth knowing": one base
+ * model in memory, many adapters, requests for different adapters batched
+ * together).  The pool holds n_pool adapters of one rank r:
+ *   A_pool [n_pool, r, n_in], B_pool [n_pool, n_out, r]   bf16, device
+ * (pad an adapter of smaller rank with zero rows of A and zero columns of B).
+ * Tokens seg_offsets[g] .. seg_offsets[g+1]-1 use adapter seg_adapter[g]; an
+ * index outside [0, n_pool) means none (the base product alone).  For token t
+ * with adapter a:  Y[t] = X[t] . deq(W)^T + s . (X[t] . A_a^T) . B_a^T.
+ * seg_offsets [n_seg + 1] and seg_adapter [n_seg]: device int32 arrays, read by
+ * the kernels (no host copy); they must describe a partition of [0, T):
+ * seg_offsets[0] = 0, non-decreasing, seg_offsets[n_seg] = T.  The kernels clamp
+ * every entry, so a malformed table gives wrong rows but no access out of
+ * bounds.  r % 8 == 0, 1 <= n_seg.  Workspace: QLORA_OP_FWD_MULTI.  Cost: the
+ * base product once; U per 128-token tile of each segment; each output tile
+ * adds one rank-deep up-projection per segment that meets its rows (few
+ * tokens, at most 64: per token in the finishing kernel).
+ */
+int qlora_linear_fwd_multi(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const qlora_bf16 *A_pool,
+                           const qlora_bf16 *B_pool, int32_t n_pool, int32_t r, float alpha, const int32_t *seg_offsets,
+                           const int32_t *seg_adapter, int32_t n_seg, qlora_bf16 *Y, void *ws, size_t ws_bytes,
+                           void *stream);
 
 /*
  * Merge a trained adapter into a 16-bit base for export ("Module 08 - QLoRA &

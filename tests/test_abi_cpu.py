@@ -241,6 +241,26 @@ def test_error_paths_merge(lib):
     assert merge(alpha=float("nan")) == E
 
 
+def test_error_paths_multi(lib):
+    E = B.QLORA_EINVAL
+    q = _nf4(64, 128)
+
+    def multi(X=FAKE, T=4, Ap=FAKE, Bp=FAKE, n_pool=3, r=8, alpha=16.0, seg=FAKE, ad=FAKE, n_seg=2, Y=FAKE, ws=FAKE,
+              nb=1 << 30):
+        return lib.qlora_linear_fwd_multi(X, T, ctypes.byref(q), Ap, Bp, n_pool, r, alpha, seg, ad, n_seg, Y, ws, nb,
+                                          None)
+
+    rc, msg = _err(lambda: multi(r=12))
+    assert rc == E and "multiple of 8" in msg
+    assert multi(n_pool=0) == E
+    assert multi(n_seg=0) == E
+    assert multi(seg=None) == E and multi(ad=None) == E
+    assert multi(seg=ctypes.c_void_p(0x10002)) == E
+    assert multi(Ap=None) == E and multi(Y=None) == E
+    need = B.workspace_bytes(B.OP_FWD_MULTI, 4, 64, 128, 8)
+    assert multi(nb=need - 1) == B.QLORA_EWORKSPACE
+
+
 def test_strerror(lib):
     for code in (0, -1, -2, -3, -4):
         assert lib.qlora_strerror(code)
