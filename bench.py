@@ -53,6 +53,9 @@ def parse():
                     help="LoRA dropout probability on the adapter input (training configs; default 0: none)")
     ap.add_argument("--adamw", action="store_true",
                     help="end each training step with the fused AdamW update of every A and B (timed as 'adamw')")
+    ap.add_argument("--adapters", type=int, default=0,
+                    help="serve the forward with this many adapters of a pool, the tokens cut into as many equal "
+                         "segments (many-adapter batching; forward only)")
     ap.add_argument("--merge", action="store_true",
                     help="time the export merge W' + s B A (NF4 base, bf16 out) of every linear instead of a step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -255,6 +258,65 @@ def bench_merge(args, B, layers, r, alpha):
                                    "avg_ms_per_launch": ms / n if n else None}}))
 
 
+def bench_multi(args, B, layers, T, r, alpha, lins):
+    """Forward of a batch cut into equal token segments, each with its own adapter of a pool."""
+    import numpy as np
+    import torch
+
+    from bit_quantized_lora_02_amd.synth import linear_inputs
+
+    S = args.adapters
+    dev = layers[0]["A"].device
+    bounds = [round(i * T / S) for i in range(S + 1)]
+    seg = torch.tensor(bounds, dtype=torch.int32, device=dev)
+    ad = torch.arange(S, dtype=torch.int32, device=dev)
+    g = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    for li, L in enumerate(layers):
+        pa, pb = [], []
+        for i in range(S):
+            inp = linear_inputs(L["n_out"], L["n_in"], 1, r, alpha, seed=500 + 31 * li + i, make_dy=False)
+            pa.append(inp.A)
+            pb.append(inp.B)
+        L["A_pool"], L["B_pool"] = g(np.stack(pa)), g(np.stack(pb))
+        L["ws_m"] = torch.empty(max(1, B.workspace_bytes(B.OP_FWD_MULTI, T, L["n_out"], L["n_in"], r)),
+                                dtype=torch.uint8, device=dev)
+
+    def step(i):
+        for L in layers:
+            c = L["copies"][i % len(L["copies"])]
+            B.linear_fwd_multi(c["X"], c["w"], L["A_pool"], L["B_pool"], alpha, seg, ad, ws=L["ws_m"], out=c["Y"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    timed = ["nf4_gemm_fwd", "nf4_gemv", "lora_u_multi"]
+    for k in timed:
+        B.timing_read(k)
+        B.timing_enable(k, True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kernels = {}
+    for k in timed:
+        B.timing_enable(k, False)
+        n, ms = B.timing_read(k)
+        if n:
+            kernels[k] = {"launches": n, "avg_ms_per_launch": ms / n, "ms_per_step": ms / args.steps}
+    fl = sum(2 * T * L["n_out"] * L["n_in"] + 2 * T * r * (L["n_in"] + L["n_out"]) for L in layers)
+    wb = sum(weight_bytes(L["n_out"], L["n_in"]) for L in layers)
+    ms_step = elapsed / args.steps * 1e3
+    print(json.dumps({"metric": "NF4 many-adapter forward TFLOP/s", "value": fl / (elapsed / args.steps) / 1e12,
+                      "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "ms_per_step": ms_step, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+                      "weight_stream_GBps": wb / (elapsed / args.steps) / 1e9,
+                      "config": {"workload": WORKLOAD_TEXT[args.config].format(n=lins[0][1], t=T) +
+                                 f", {S} adapters in {S} equal token segments", "tokens": T, "rank": r,
+                                 "adapters": S, "linears": [[L["name"], L["n_out"], L["n_in"]] for L in layers]},
+                      "kernels": kernels}))
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -333,6 +395,9 @@ def main():
 
     if args.merge:
         bench_merge(args, B, layers, r, alpha)
+        return
+    if args.adapters:
+        bench_multi(args, B, layers, T, r, alpha, lins)
         return
 
     def step(i):

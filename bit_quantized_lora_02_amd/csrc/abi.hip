@@ -238,13 +238,7 @@ Plan make_plan(int op, int64_t T, int64_t N, int64_t K, int32_t r) {
   if (op == QLORA_OP_FWD || op == QLORA_OP_FWD_DROPOUT || op == QLORA_OP_FWD_MULTI) {
     p.su = plan_skinny(T, K);
     part = (size_t)p.su.n * T * p.rn * 4;
-    if (op == QLORA_OP_FWD_MULTI && use_gemv(T, K)) {  // U by segments first; its partials are dead before the GEMV's
-      p.gemv = true;
-      nf4_gemv_plan(T, N, K, &p.gemv_rg, &p.gemv_w, &p.gemv_split, &p.gemv_main);
-      const size_t gp = (size_t)p.gemv_split * T * N * 4;
-      part = part > gp ? part : gp;
-    }
-    if (op == QLORA_OP_FWD && use_gemv(T, K)) {  // dropout needs the adapter input's own pass
+    if ((op == QLORA_OP_FWD || op == QLORA_OP_FWD_MULTI) && use_gemv(T, K)) {  // dropout: the tiled path
       p.gemv = true;
       nf4_gemv_plan(T, N, K, &p.gemv_rg, &p.gemv_w, &p.gemv_split, &p.gemv_main);
       part = up((size_t)p.gemv_split * T * N * 4, kAlign);
@@ -555,16 +549,19 @@ int qlora_linear_fwd_multi(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, c
   sg.ad = seg_adapter;
   sg.n_seg = n_seg;
   sg.n_pool = n_pool;
-  // U = X A_a^T per segment, then V = bf16(s U), zero-padded to rp columns
-  LAUNCH("lora_u_multi", launch_skinny_grouped(p.rn, X, K, T, A_pool, K, (int64_t)r * K, r, K, p.su.kchunk, p.su.n,
-                                               sg, part, s));
-  LAUNCH("lora_u_finalize", launch_finalize(part, p.su.n, T, p.rn, nullptr, 0, 0, 1.0f, V, p.rp, p.rp, r, sc, s));
-  if (p.gemv) {
+  if (p.gemv) {  // few tokens: the U partials of every segment ride along in the weight-streaming launch
+    float *upart = (float *)(w + p.off_part + p.off_upart);
     LAUNCH("nf4_gemv", launch_nf4_gemv(X, T, K, q->codes, q->absmax_q, q->absmax_step, N, p.gemv_rg, p.gemv_w,
-                                       p.gemv_split, p.gemv_main, A_pool, r, part, nullptr, lv, s, false));
-    LAUNCH("gemv_finish", launch_gemv_finish_multi(part, p.gemv_split, T, N, V, p.rp, B_pool, r, sg, Y, s));
+                                       p.gemv_split, p.gemv_main, A_pool, r, part, upart, lv, s, sg));
+    LAUNCH("gemv_finish", launch_gemv_finish_multi(part, upart, p.gemv_split, T, N, B_pool, r, sc, sg, Y, s));
     return QLORA_OK;
   }
+  // U = X A_a^T per segment, then V = bf16(s U), zero-padded to rp columns
+  int gns;
+  int64_t gkc;
+  skinny_plan_grouped(T, n_seg, K, &gns, &gkc);  // at most p.su.n ranges: fits the workspace
+  LAUNCH("lora_u_multi", launch_skinny_grouped(p.rn, X, K, T, A_pool, K, (int64_t)r * K, r, K, gkc, gns, sg, part, s));
+  LAUNCH("lora_u_finalize", launch_finalize(part, gns, T, p.rn, nullptr, 0, 0, 1.0f, V, p.rp, p.rp, r, sc, s));
   LAUNCH("nf4_gemm_fwd", launch_nf4_gemm_fwd(nf4_gemm_pick_tile(T, N), X, T, K, q->codes, q->absmax_q,
                                              q->absmax_step, N, V, B_pool, r, r, p.rp, Y, lv, s, sg));
   return QLORA_OK;

@@ -74,17 +74,18 @@ hipError_t launch_merge(const uint8_t *codes, const uint8_t *absmax_q, const flo
 // partials in range order, forms V = bf16(s U), adds V B^T and rounds Y.
 constexpr int64_t kGemvMaxT = 64;
 void nf4_gemv_plan(int64_t T, int64_t N, int64_t K, int *rg, int *w, int *nsplit, int *gmain);
-// (with_u false: no U workgroups; the caller forms V itself)
+// With a segment table (sg.n_seg > 0) the U partials come per segment and K range, with each
+// segment's adapter A + a r K (segments without an adapter leave their rows unwritten).
 hipError_t launch_nf4_gemv(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
                            const float *step, int64_t N, int rg, int w, int nsplit, int gmain, const bf16_t *A,
                            int64_t r, float *part, float *upart, const Levels &lv, hipStream_t s,
-                           bool with_u = true);
+                           const SegTable &sg = SegTable());
 hipError_t launch_gemv_finish(const float *part, const float *upart, int nsplit, int64_t T, int64_t N,
                               const bf16_t *B, int64_t r, float s, bf16_t *Y, bf16_t *U_out, hipStream_t st);
-// Many adapters: Y = bf16(sum of the weight partials + V[t] B_a^T) with V [T, ldv] given and
-// B_a = B_pool + a N r for the adapter a of token t's segment (none: the partials alone).
-hipError_t launch_gemv_finish_multi(const float *part, int nsplit, int64_t T, int64_t N, const bf16_t *V,
-                                    int64_t ldv, const bf16_t *B_pool, int64_t r, const SegTable &sg, bf16_t *Y,
+// Many adapters: Y = bf16(sum of the weight partials + bf16(s U[t]) B_a^T) with B_a = B_pool + a N r
+// for the adapter a of token t's segment (none: the partials alone).
+hipError_t launch_gemv_finish_multi(const float *part, const float *upart, int nsplit, int64_t T, int64_t N,
+                                    const bf16_t *B_pool, int64_t r, float s, const SegTable &sg, bf16_t *Y,
                                     hipStream_t st);
 
 // Dropout on the adapter input P (a dense row-major [rows, ld] activation):
@@ -103,6 +104,7 @@ struct DropParams {
 // operand Q (see lora_gemm.hip); `drop` (DROP_*) applies dropout to P.
 int skinny_rn(int64_t r);
 void skinny_plan(int64_t M, int64_t Kred, int *nsplit, int64_t *kchunk);
+void skinny_plan_grouped(int64_t M, int64_t n_seg, int64_t Kred, int *nsplit, int64_t *kchunk);
 hipError_t launch_skinny(bool pt, bool qt, int rn, const bf16_t *P, int64_t ldp, int64_t M, const bf16_t *Q,
                          int64_t ldq, int64_t Rv, int64_t Kred, int64_t kchunk, int nsplit, float *C, hipStream_t s,
                          int drop = DROP_NONE, const DropParams &dp = DropParams());

@@ -401,6 +401,24 @@ void skinny_plan(int64_t M, int64_t Kred, int *nsplit, int64_t *kchunk) {
   *nsplit = Kred > 0 ? (int)((Kred + *kchunk - 1) / *kchunk) : 0;
 }
 
+// Split of the grouped (many-adapter) U pass: the grid has up to tiles + n_seg
+// row tiles, so the split aims at ~1024 workgroups over those, and never
+// exceeds the split of the plain plan (whose partial sums the workspace holds).
+void skinny_plan_grouped(int64_t M, int64_t n_seg, int64_t Kred, int *nsplit, int64_t *kchunk) {
+  int ns_max;
+  int64_t kc_max;
+  skinny_plan(M, Kred, &ns_max, &kc_max);
+  const int64_t tiles = (M + SBM - 1) / SBM + n_seg;
+  int64_t ns = (1024 + tiles - 1) / tiles;
+  if (ns > ns_max) ns = ns_max;
+  if (ns < 1) ns = 1;
+  int64_t kc = (Kred + ns - 1) / ns;
+  kc = (kc + SK - 1) / SK * SK;
+  if (kc < kc_max) kc = kc_max;  // never more ranges than the plain plan
+  *kchunk = kc > 0 ? kc : SK;
+  *nsplit = Kred > 0 ? (int)((Kred + *kchunk - 1) / *kchunk) : 0;
+}
+
 template <bool PT, bool QT, int DM>
 static hipError_t skinny_dispatch(int rn, dim3 grid, hipStream_t s, const bf16_t *P, int64_t ldp, int64_t M,
                                   const bf16_t *Q, int64_t ldq, int64_t Rv, int64_t Kred, int64_t kchunk, float *C,

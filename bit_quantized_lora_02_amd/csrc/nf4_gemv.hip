@@ -109,16 +109,29 @@ __global__ __launch_bounds__(256) void k_nf4_gemv(const bf16_t *__restrict__ X, 
                                                   const uint8_t *__restrict__ absmax_q,
                                                   const float *__restrict__ step, int64_t N, int nsplit,
                                                   int gmain, const bf16_t *__restrict__ A, int64_t r,
-                                                  float *__restrict__ part, float *__restrict__ upart, Levels lv) {
+                                                  float *__restrict__ part, float *__restrict__ upart, Levels lv,
+                                                  SegTable sg) {
   constexpr int D = 128 * W;              // reduction depth of one step
   constexpr int NB = W >= 2 ? W / 2 : 1;  // NF4 blocks a lane touches per step
   __shared__ __attribute__((aligned(16))) float2 s_tab[256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t kchunk = K / nsplit;
   if ((int)blockIdx.x >= gmain) {
-    const int64_t kb = (int64_t)(blockIdx.x - gmain) * kchunk;
-    lora_u_partial<MT>(X, T, K, A, r, kb, kb + kchunk, upart + ((int64_t)(blockIdx.x - gmain) * 4 + wave) * T * r,
-                       wave, lane);
+    const int64_t u = (int64_t)blockIdx.x - gmain;
+    if (sg.n_seg == 0) {  // one adapter: workgroup u takes K range u for every token
+      const int64_t kb = u * kchunk;
+      lora_u_partial<MT>(X, T, K, A, r, kb, kb + kchunk, upart + (u * 4 + wave) * T * r, wave, lane);
+      return;
+    }
+    // many adapters: workgroup u takes segment u / nsplit over K range u % nsplit, with its adapter
+    const int g = (int)(u / nsplit);
+    const int64_t p = u - (int64_t)g * nsplit, kb = p * kchunk;
+    auto clampT = [&](int64_t v) { return v < 0 ? (int64_t)0 : (v > T ? T : v); };
+    const int64_t lo = clampT(sg.seg[g]), hi = clampT(sg.seg[g + 1]);
+    const int a = sg.ad[g];
+    if (hi <= lo || a < 0 || a >= sg.n_pool) return;  // no tokens, or no adapter: U is not used
+    lora_u_partial<MT>(X + lo * K, hi - lo, K, A + (int64_t)a * r * K, r, kb, kb + kchunk,
+                       upart + ((p * 4 + wave) * T + lo) * r, wave, lane);
     return;
   }
   pair_levels_to_lds(lv, s_tab, tid);
@@ -299,14 +312,16 @@ __global__ __launch_bounds__(256) void k_gemv_finish(const float *__restrict__ p
 }
 
 // Many adapters: workgroup (x, t) finds token t's segment by bisection (entries
-// clamped to [0, T]); then for its 256 outputs n
-// Y[t, n] = bf16(sum over p (in order) of part[p][t][n] + V[t, :] . B_a[n, :]),
-// V [T, ldv] bf16 (already s U), B_a = B_pool + a N r, or the partials alone
-// when the segment has no adapter (or the token no segment).
-__global__ __launch_bounds__(256) void k_gemv_finish_multi(const float *__restrict__ part, int nsplit, int64_t T,
-                                                           int64_t N, const bf16_t *__restrict__ V, int64_t ldv,
-                                                           const bf16_t *__restrict__ B_pool, int64_t r, SegTable sg,
-                                                           bf16_t *__restrict__ Y) {
+// clamped to [0, T]); U[t, :] = its nup U partials added as in k_gemv_finish,
+// V = bf16(s U); then for its 256 outputs n
+// Y[t, n] = bf16(sum over p (in order) of part[p][t][n] + V . B_a[n, :]),
+// B_a = B_pool + a N r, or the partials alone when the segment has no adapter
+// (or the token no segment).
+__global__ __launch_bounds__(256) void k_gemv_finish_multi(const float *__restrict__ part,
+                                                           const float *__restrict__ upart, int nsplit, int nup,
+                                                           int64_t T, int64_t N, const bf16_t *__restrict__ B_pool,
+                                                           int64_t r, float s, SegTable sg, bf16_t *__restrict__ Y) {
+  __shared__ float s_sub[8][QLORA_MAX_RANK];
   __shared__ float s_v[QLORA_MAX_RANK];
   const int tid = threadIdx.x;
   const int64_t t = blockIdx.y;
@@ -319,8 +334,22 @@ __global__ __launch_bounds__(256) void k_gemv_finish_multi(const float *__restri
   }
   int a = -1;
   if (g0 < sg.n_seg && clampT(sg.seg[g0]) <= t) a = sg.ad[g0];
-  const bool has = a >= 0 && a < sg.n_pool;
-  if (tid < r) s_v[tid] = has ? bf16_lo_to_f32(V[t * ldv + tid]) : 0.f;
+  const bool has = a >= 0 && a < sg.n_pool;  // uniform in the workgroup
+  if (has) {
+    for (int i = tid; i < 8 * r; i += 256) {
+      const int j = i % r, q = i / r;
+      float u = 0.f;
+      for (int p = q; p < nup; p += 8) u += upart[((int64_t)p * T + t) * r + j];
+      s_sub[q][j] = u;
+    }
+    __syncthreads();
+    if (tid < r) {
+      float u = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) u += s_sub[q][tid];
+      s_v[tid] = bf16_lo_to_f32(f32_to_bf16(s * u));
+    }
+  }
   __syncthreads();
   const int64_t n = (int64_t)blockIdx.x * 256 + tid;
   if (n >= N) return;
@@ -353,12 +382,12 @@ __global__ __launch_bounds__(256) void k_gemv_finish_multi(const float *__restri
   Y[t * N + n] = f32_to_bf16(y + l);
 }
 
-hipError_t launch_gemv_finish_multi(const float *part, int nsplit, int64_t T, int64_t N, const bf16_t *V,
-                                    int64_t ldv, const bf16_t *B_pool, int64_t r, const SegTable &sg, bf16_t *Y,
+hipError_t launch_gemv_finish_multi(const float *part, const float *upart, int nsplit, int64_t T, int64_t N,
+                                    const bf16_t *B_pool, int64_t r, float s, const SegTable &sg, bf16_t *Y,
                                     hipStream_t st) {
   if (T == 0) return hipSuccess;
   dim3 grid((unsigned)((N + 255) / 256), (unsigned)T);
-  launch(k_gemv_finish_multi, grid, dim3(256), 0, st, part, nsplit, T, N, V, ldv, B_pool, r, sg, Y);
+  launch(k_gemv_finish_multi, grid, dim3(256), 0, st, part, upart, nsplit, 4 * nsplit, T, N, B_pool, r, s, sg, Y);
   return hipGetLastError();
 }
 
@@ -392,31 +421,32 @@ void nf4_gemv_plan(int64_t T, int64_t N, int64_t K, int *rg, int *w, int *nsplit
 template <int MT, int RG, int W>
 static void gemv_with(hipStream_t s, const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes,
                       const uint8_t *absmax_q, const float *step, int64_t N, int nsplit, int gmain, const bf16_t *A,
-                      int64_t r, float *part, float *upart, const Levels &lv, bool with_u) {
-  launch(k_nf4_gemv<MT, RG, W>, dim3((unsigned)(gmain + (with_u ? nsplit : 0))), dim3(256), 0, s, X, T, K, codes,
-         absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv);
+                      int64_t r, float *part, float *upart, const Levels &lv, const SegTable &sg) {
+  const int64_t u_wgs = (int64_t)nsplit * (sg.n_seg > 0 ? sg.n_seg : 1);
+  launch(k_nf4_gemv<MT, RG, W>, dim3((unsigned)(gmain + u_wgs)), dim3(256), 0, s, X, T, K, codes, absmax_q, step, N,
+         nsplit, gmain, A, r, part, upart, lv, sg);
 }
 
 template <int MT, int W>
 static void gemv_rg(int rg, hipStream_t s, const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes,
                     const uint8_t *absmax_q, const float *step, int64_t N, int nsplit, int gmain, const bf16_t *A,
-                    int64_t r, float *part, float *upart, const Levels &lv, bool with_u) {
-  if (rg == 4) gemv_with<MT, 4, W>(s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv, with_u);
-  else if (rg == 2) gemv_with<MT, 2, W>(s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv, with_u);
-  else gemv_with<MT, 1, W>(s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv, with_u);
+                    int64_t r, float *part, float *upart, const Levels &lv, const SegTable &sg) {
+  if (rg == 4) gemv_with<MT, 4, W>(s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv, sg);
+  else if (rg == 2) gemv_with<MT, 2, W>(s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv, sg);
+  else gemv_with<MT, 1, W>(s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv, sg);
 }
 
 hipError_t launch_nf4_gemv(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
                            const float *step, int64_t N, int rg, int w, int nsplit, int gmain, const bf16_t *A,
-                           int64_t r, float *part, float *upart, const Levels &lv, hipStream_t s, bool with_u) {
+                           int64_t r, float *part, float *upart, const Levels &lv, hipStream_t s, const SegTable &sg) {
   if (T == 0) return hipSuccess;
   if (T <= 16) {
-    if (w == 2) gemv_rg<1, 2>(rg, s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv, with_u);
-    else gemv_rg<1, 1>(rg, s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv, with_u);
+    if (w == 2) gemv_rg<1, 2>(rg, s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv, sg);
+    else gemv_rg<1, 1>(rg, s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv, sg);
   } else if (T <= 32) {
-    gemv_rg<2, 1>(rg, s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv, with_u);
+    gemv_rg<2, 1>(rg, s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv, sg);
   } else {
-    gemv_rg<4, 1>(rg, s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv, with_u);
+    gemv_rg<4, 1>(rg, s, X, T, K, codes, absmax_q, step, N, nsplit, gmain, A, r, part, upart, lv, sg);
   }
   return hipGetLastError();
 }
