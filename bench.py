@@ -196,7 +196,7 @@ def cpu_baseline(inp, train: bool, target_s: float):
     ts = int(max(1, min(T, ts * target_s / max(dt, 1e-3))))
     dt = run(ts)
     reps = 1
-    while dt < 0.5 * target_s and ts == T:  # the whole batch is quicker than the target: repeat the pass
+    while dt < target_s and ts == T:  # the whole batch is quicker than the target: repeat the pass
         dt += run(ts)
         reps += 1
     fl = reps * flops_linear(ts, n_out, n_in, r, train)
