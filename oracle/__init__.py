@@ -80,6 +80,12 @@ def _load():
     lib.oracle_linear_fwd_multi.argtypes = [P, i64, P, i64, i64, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
                                             P, P, ctypes.c_int32, P]
     lib.oracle_linear_fwd_multi.restype = None
+    lib.oracle_dyn_codebook.argtypes = [ctypes.c_int, P]
+    lib.oracle_dyn_codebook.restype = None
+    lib.oracle_dyn_encode.argtypes = [ctypes.c_float, ctypes.c_int]
+    lib.oracle_dyn_encode.restype = ctypes.c_int
+    lib.oracle_adamw8_step.argtypes = [P, P, P, P, P, P, P, i64, d, d, d, d, d, i64]
+    lib.oracle_adamw8_step.restype = None
     _lib = lib
     return lib
 
@@ -340,3 +346,35 @@ def linear_fwd_multi(X, Wdq: np.ndarray, A_pool, B_pool, alpha: float, seg, adap
     _load().oracle_linear_fwd_multi(_ptr(X), T, _ptr(Wdq), N, K, _ptr(A_pool), _ptr(B_pool), n_pool, r, float(alpha),
                                     _ptr(seg), _ptr(adapters), adapters.size, _ptr(Y))
     return Y
+
+
+# -------------------------------------------------- AdamW with 8-bit state
+
+def dyn_codebook(signed: bool) -> np.ndarray:
+    """Values of the 256 bytes of the dynamic code book (signed: first moment, unsigned: second)."""
+    out = np.zeros(256, np.float32)
+    _load().oracle_dyn_codebook(1 if signed else 0, _ptr(out))
+    return out
+
+
+def dyn_encode(x: float, signed: bool) -> int:
+    """Nearest code of a normalized binary32 value, ties to the smaller magnitude."""
+    return int(_load().oracle_dyn_encode(float(np.float32(x)), 1 if signed else 0))
+
+
+def adamw8_step(param_bits: np.ndarray, grad_bits, m_code: np.ndarray, m_absmax: np.ndarray, v_code: np.ndarray,
+                v_absmax: np.ndarray, lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
+                step: int, master: np.ndarray | None = None):
+    """One AdamW step with block-wise 8-bit moments (blocks of 2048), in place on every state array."""
+    g = np.ascontiguousarray(grad_bits, np.uint16).reshape(-1)
+    n = g.size
+    for a, dt in ((param_bits, np.uint16), (m_code, np.uint8), (v_code, np.uint8)):
+        assert a.dtype == dt and a.flags.c_contiguous and a.size == n
+    nb = (n + 2047) // 2048
+    for a in (m_absmax, v_absmax):
+        assert a.dtype == np.float32 and a.flags.c_contiguous and a.size == nb
+    if master is not None:
+        assert master.dtype == np.float32 and master.flags.c_contiguous and master.size == n
+    _load().oracle_adamw8_step(_ptr(param_bits), _ptr(master), _ptr(g), _ptr(m_code), _ptr(m_absmax), _ptr(v_code),
+                               _ptr(v_absmax), n, float(lr), float(beta1), float(beta2), float(eps),
+                               float(weight_decay), int(step))

@@ -26,6 +26,8 @@
  *  [STEPS] "qlora" glossary (chipfoundryservices), table "How QLoRA Works":
  *         quantize at load (4-bit), forward dequantizes then computes, backward
  *         in bfloat16, only the adapter is updated.
+ *  [OPT8] "Module 08 - QLoRA & Quantization" (ainiketan), "4. QLoRA in code" and
+ *         "5. Other memory-saving levers": paged 8-bit AdamW state.
  *  [OPT]  katajob, "What stays in full precision" (A and B keep ordinary AdamW
  *         state) and pranaymahendrakar, Developer level, "The walkthrough" (about
  *         8 bytes of Adam state per trainable parameter).
@@ -548,4 +550,140 @@ void oracle_linear_fwd_multi(const double *X, int64_t T, const uint16_t *Wdq, in
     free(u);
   }
   free(tok_ad);
+}
+
+/* ------------------------------------------------- AdamW with 8-bit state */
+
+/*
+ * [OPT8] "Module 08 - QLoRA & Quantization" (ainiketan), "4. QLoRA in code"
+ * and "5. Other memory-saving levers": a paged 8-bit AdamW (paged_adamw_8bit)
+ * keeps the optimizer state smaller.  The 8-bit state follows the block-wise
+ * quantization of optimizer states of Dettmers, Lewis, Shleifer and
+ * Zettlemoyer ("8-bit Optimizers via Block-wise Quantization", ICLR 2022):
+ * each moment is stored as 8-bit codes plus one binary32 absmax per block of
+ * 2048 consecutive elements, the codes indexing a dynamic (exponent + linear
+ * fraction) code book.  Paging to host memory is not part of this.
+ * Readings (listed in the design notes):
+ *  - code book: in a signed byte (first moment) bit 7 is the sign; among the
+ *    other 7 bits, E = the number of leading zeros, then a set indicator bit,
+ *    then F = 6 - E fraction bits f; the magnitude is
+ *    fl32((0.1 + 0.9 ((f + 1) / 2^F)) / 10^E) (binary64, in that order), and
+ *    all-zero bits mean 0.  An unsigned byte (second moment) has no sign bit:
+ *    E counts leading zeros among 8 bits and F = 7 - E.  Magnitudes grow with
+ *    the unsigned value of the bits, so the code is the count of thresholds
+ *    below the value;
+ *  - encode: x = fl32(value / absmax) with absmax the block's largest
+ *    magnitude (all codes 0 when it is 0); nearest magnitude, ties to the
+ *    smaller (thresholds: the largest binary32 value not above each exact
+ *    midpoint); the sign bit is set for x < 0 unless the magnitude is 0;
+ *  - decode: fl32(table[code] * absmax);
+ *  - the step is the binary32 AdamW of the fused kernel, every operation
+ *    rounded once, in this order (the codes are integer decisions, taken in
+ *    the kernel's precision):
+ *      m = fl(fl(b1 m) + fl(c1 g)),  v = fl(fl(b2 v) + fl(fl(c2 g) g)),
+ *      d = fl(fl(sqrt(v) / sb) + eps),  theta = fl(fl(theta dk) - fl(ss fl(m / d)))
+ *    with b1 = fl32(beta1), c1 = fl32(1 - beta1), b2 = fl32(beta2),
+ *    c2 = fl32(1 - beta2), eps = fl32(eps), dk = fl32(1 - lr wd),
+ *    ss = fl32(lr / (1 - beta1^t)), sb = fl32(sqrt(1 - beta2^t)), each formed
+ *    in binary64 and rounded once.
+ */
+static float dyn_magnitude(int E, int F, int f) {
+  double p10 = 1.0;
+  for (int i = 0; i < E; ++i) p10 *= 10.0; /* exact: 10^E < 2^53 */
+  const double frac = (double)(f + 1) / (double)(1 << F);
+  return (float)((0.1 + 0.9 * frac) / p10);
+}
+
+/* Value of every byte: signed (first moment) or unsigned (second moment) book. */
+void oracle_dyn_codebook(int is_signed, float out[256]) {
+  const int bits = is_signed ? 7 : 8;
+  for (int b = 0; b < 256; ++b) {
+    const int p = is_signed ? (b & 127) : b;
+    float mag = 0.0f;
+    if (p != 0) {
+      int top = bits - 1;
+      while (!((p >> top) & 1)) --top; /* position of the indicator bit */
+      const int E = bits - 1 - top, F = top;
+      mag = dyn_magnitude(E, F, p - (1 << F));
+    }
+    out[b] = (is_signed && (b & 128)) ? -mag : mag;
+  }
+}
+
+/* Nearest code of a normalized value (|x| <= 1), ties to the smaller magnitude. */
+static int dyn_encode(float x, int is_signed, const float book[256]) {
+  const int n = is_signed ? 128 : 256;
+  const float a = fabsf(x);
+  int p = 0;
+  for (int i = 1; i < n; ++i) {
+    const double mid = ((double)book[i - 1] + (double)book[i]) * 0.5; /* exact */
+    if ((double)a > mid) p = i;
+  }
+  if (is_signed && x < 0.0f && p != 0) p |= 128;
+  return p;
+}
+
+int oracle_dyn_encode(float x, int is_signed) {
+  float book[256];
+  oracle_dyn_codebook(is_signed, book);
+  return dyn_encode(x, is_signed, book);
+}
+
+/*
+ * One step over n parameters: param bf16 bits (and master binary32 or NULL),
+ * grad bf16 bits, m_code/v_code [n] bytes, m_absmax/v_absmax [ceil(n / 2048)]
+ * binary32, all updated in place.
+ */
+void oracle_adamw8_step(uint16_t *param, float *master, const uint16_t *grad, uint8_t *m_code, float *m_absmax,
+                        uint8_t *v_code, float *v_absmax, int64_t n, double lr, double beta1, double beta2,
+                        double eps, double wd, int64_t t) {
+  float sbook[256], ubook[256];
+  oracle_dyn_codebook(1, sbook);
+  oracle_dyn_codebook(0, ubook);
+  const float b1 = (float)beta1, c1 = (float)(1.0 - beta1), b2 = (float)beta2, c2 = (float)(1.0 - beta2);
+  const float ef = (float)eps, dk = (float)(1.0 - lr * wd);
+  const float ss = (float)(lr / (1.0 - pow(beta1, (double)t))), sb = (float)sqrt(1.0 - pow(beta2, (double)t));
+  const int64_t nblk = (n + 2047) / 2048;
+  float *m = (float *)malloc(sizeof(float) * 2048), *v = (float *)malloc(sizeof(float) * 2048);
+  for (int64_t blk = 0; blk < nblk; ++blk) {
+    const int64_t e0 = blk * 2048, e1 = (e0 + 2048 < n) ? e0 + 2048 : n;
+    float am = 0.0f, av = 0.0f;
+    for (int64_t e = e0; e < e1; ++e) {
+      uint32_t u = (uint32_t)grad[e] << 16;
+      float g;
+      memcpy(&g, &u, 4);
+      float th;
+      if (master) th = master[e];
+      else {
+        u = (uint32_t)param[e] << 16;
+        memcpy(&th, &u, 4);
+      }
+      float mo = sbook[m_code[e]] * m_absmax[blk];
+      float vo = ubook[v_code[e]] * v_absmax[blk];
+      float mm = b1 * mo;
+      mm = mm + c1 * g;
+      float cg = c2 * g;
+      float vv = b2 * vo;
+      vv = vv + cg * g;
+      float d = sqrtf(vv) / sb;
+      d = d + ef;
+      const float q = mm / d;
+      float tn = th * dk;
+      tn = tn - ss * q;
+      if (master) master[e] = tn;
+      param[e] = f32_to_bf16_rne(tn);
+      m[e - e0] = mm;
+      v[e - e0] = vv;
+      if (fabsf(mm) > am) am = fabsf(mm);
+      if (vv > av) av = vv;
+    }
+    m_absmax[blk] = am;
+    v_absmax[blk] = av;
+    for (int64_t e = e0; e < e1; ++e) {
+      m_code[e] = (uint8_t)(am > 0.0f ? dyn_encode(m[e - e0] / am, 1, sbook) : 0);
+      v_code[e] = (uint8_t)(av > 0.0f ? dyn_encode(v[e - e0] / av, 0, ubook) : 0);
+    }
+  }
+  free(m);
+  free(v);
 }
