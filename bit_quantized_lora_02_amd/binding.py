@@ -6,7 +6,7 @@ in the library's gfx950 kernels.  There is no CPU or PyTorch fallback: if the
 library is missing or the device is not gfx950, calls raise.
 
 Names follow the C ABI: ``quantize_nf4``, ``dequant``, ``linear_fwd``,
-``linear_bwd``, ``linear_fwd_dropout``, ``linear_bwd_dropout``, ``linear_fwd_multi``, ``adamw_step``, ``merge``, plus ``QLoRALinearFn`` (a torch.autograd.Function whose backward
+``linear_bwd``, ``linear_fwd_dropout``, ``linear_bwd_dropout``, ``linear_fwd_multi``, ``adamw_step``, ``adamw8_step``, ``merge``, plus ``QLoRALinearFn`` (a torch.autograd.Function whose backward
 returns gradients for X, A and B and none for the frozen NF4 weight).
 """
 from __future__ import annotations
@@ -43,6 +43,7 @@ EXPORTED = (
     "qlora_linear_bwd_dropout",
     "qlora_linear_fwd_multi",
     "qlora_adamw_step",
+    "qlora_adamw8_step",
     "qlora_merge",
     "qlora_strerror",
     "qlora_last_error",
@@ -78,6 +79,19 @@ class _AdamTensor(ctypes.Structure):
     ]
 
 
+class _Adam8Tensor(ctypes.Structure):
+    _fields_ = [
+        ("param", ctypes.c_void_p),
+        ("grad", ctypes.c_void_p),
+        ("exp_avg_code", ctypes.c_void_p),
+        ("exp_avg_absmax", ctypes.c_void_p),
+        ("exp_avg_sq_code", ctypes.c_void_p),
+        ("exp_avg_sq_absmax", ctypes.c_void_p),
+        ("master", ctypes.c_void_p),
+        ("n", ctypes.c_int64),
+    ]
+
+
 _lib = None
 
 
@@ -108,6 +122,8 @@ def load_library() -> ctypes.CDLL:
         "qlora_merge": ([pnf4, P, i64, i64, P, P, i32, ctypes.c_float, P, P, P], ctypes.c_int),
         "qlora_linear_fwd_multi": ([P, i64, pnf4, P, P, i32, i32, ctypes.c_float, P, P, i32, P, P, sz, P],
                                    ctypes.c_int),
+        "qlora_adamw8_step": ([ctypes.POINTER(_Adam8Tensor), i32, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                               ctypes.c_double, ctypes.c_double, i64, P], ctypes.c_int),
         "qlora_strerror": ([ctypes.c_int], ctypes.c_char_p),
         "qlora_last_error": ([], ctypes.c_char_p),
         "qlora_timing_enable": ([ctypes.c_char_p, ctypes.c_int], ctypes.c_int),
@@ -405,6 +421,49 @@ def adamw_step(params, grads, states, lr: float, step: int, beta1: float = 0.9, 
     _check(load_library().qlora_adamw_step(arr, len(descs), float(lr), float(beta1), float(beta2), float(eps),
                                            float(weight_decay), int(step), _stream(params[0].device)),
            "qlora_adamw_step")
+
+
+@dataclass
+class Adam8State:
+    """8-bit AdamW state of one bf16 parameter: codes and per-2048-block absmax of each moment."""
+    exp_avg_code: torch.Tensor
+    exp_avg_absmax: torch.Tensor
+    exp_avg_sq_code: torch.Tensor
+    exp_avg_sq_absmax: torch.Tensor
+    master: torch.Tensor | None = None
+
+    @staticmethod
+    def zeros_like(param: torch.Tensor, master: bool = False) -> "Adam8State":
+        n = param.numel()
+        nb = (n + 2047) // 2048
+        dev = param.device
+        return Adam8State(torch.zeros(n, dtype=torch.uint8, device=dev), torch.zeros(nb, dtype=torch.float32, device=dev),
+                          torch.zeros(n, dtype=torch.uint8, device=dev), torch.zeros(nb, dtype=torch.float32, device=dev),
+                          param.float().clone() if master else None)
+
+
+def adamw8_step(params, grads, states, lr: float, step: int, beta1: float = 0.9, beta2: float = 0.999,
+                eps: float = 1e-8, weight_decay: float = 0.0):
+    """One fused AdamW step with block-wise 8-bit moments, in place, over lists of params, grads and Adam8State."""
+    descs, keep = [], []
+    for p, g, st in zip(params, grads, states, strict=True):
+        if p.dtype != torch.bfloat16 or g.dtype != torch.bfloat16 or not p.is_contiguous() or not p.is_cuda:
+            raise TypeError("params and grads must be contiguous bf16 GPU tensors")
+        g = g.contiguous()
+        keep.append(g)
+        n, nb = p.numel(), (p.numel() + 2047) // 2048
+        if g.numel() != n or st.exp_avg_code.numel() != n or st.exp_avg_sq_code.numel() != n or \
+                st.exp_avg_absmax.numel() != nb or st.exp_avg_sq_absmax.numel() != nb:
+            raise ValueError("shape mismatch in adamw8_step")
+        descs.append(_Adam8Tensor(p.data_ptr(), g.data_ptr(), st.exp_avg_code.data_ptr(), st.exp_avg_absmax.data_ptr(),
+                                  st.exp_avg_sq_code.data_ptr(), st.exp_avg_sq_absmax.data_ptr(),
+                                  st.master.data_ptr() if st.master is not None else None, n))
+    if not descs:
+        return
+    arr = (_Adam8Tensor * len(descs))(*descs)
+    _check(load_library().qlora_adamw8_step(arr, len(descs), float(lr), float(beta1), float(beta2), float(eps),
+                                            float(weight_decay), int(step), _stream(params[0].device)),
+           "qlora_adamw8_step")
 
 
 class QLoRALinearFn(torch.autograd.Function):

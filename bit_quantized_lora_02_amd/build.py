@@ -25,6 +25,10 @@ FLAGS = [
     "-shared",
     # packed binary32 instructions stay off (they are not needed by these kernels)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # every a * b + c written in the sources is two rounded operations (HIP's default would fuse
+    # them into one FMA, and __fmul_rn / __fadd_rn are plain * and + in this toolchain); an FMA
+    # is written as fmaf where one is meant
+    "-ffp-contract=off",
     "-Wall",
     "-Wno-unused-result",
 ]

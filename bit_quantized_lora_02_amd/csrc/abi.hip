@@ -669,6 +669,60 @@ int qlora_adamw_step(const qlora_adamw_tensor *tensors, int32_t count, double lr
   return QLORA_OK;
 }
 
+int qlora_adamw8_step(const qlora_adamw8_tensor *tensors, int32_t count, double lr, double beta1, double beta2,
+                      double eps, double weight_decay, int64_t step, void *stream) {
+  if (count < 0 || (count > 0 && !tensors)) return fail(QLORA_EINVAL, "tensors is NULL or count < 0");
+  if (!(beta1 >= 0.0 && beta1 < 1.0 && beta2 >= 0.0 && beta2 < 1.0))
+    return fail(QLORA_EINVAL, "betas must be in [0, 1) (got %g, %g)", beta1, beta2);
+  if (!(eps > 0.0) || !isfinite(eps)) return fail(QLORA_EINVAL, "eps must be positive and finite");
+  if (!(lr >= 0.0) || !isfinite(lr) || !(weight_decay >= 0.0) || !isfinite(weight_decay))
+    return fail(QLORA_EINVAL, "lr and weight_decay must be finite and >= 0");
+  if (step < 1) return fail(QLORA_EINVAL, "step must be >= 1 (got %lld)", (long long)step);
+  int64_t total = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const qlora_adamw8_tensor &t = tensors[i];
+    if (t.n < 0) return fail(QLORA_EINVAL, "tensor %d: n < 0", (int)i);
+    if (t.n == 0) continue;
+    if (!t.param || !t.grad || !t.exp_avg_code || !t.exp_avg_absmax || !t.exp_avg_sq_code || !t.exp_avg_sq_absmax)
+      return fail(QLORA_EINVAL, "tensor %d: NULL array", (int)i);
+    if (!aligned16(t.param) || !aligned16(t.grad) || !aligned16(t.exp_avg_code) || !aligned16(t.exp_avg_sq_code) ||
+        ((uintptr_t)t.exp_avg_absmax & 3) || ((uintptr_t)t.exp_avg_sq_absmax & 3) || (t.master && !aligned16(t.master)))
+      return fail(QLORA_EINVAL, "tensor %d: misaligned array", (int)i);
+    total += t.n;
+  }
+  if (total == 0) return QLORA_OK;
+  int rc;
+  if ((rc = check_device(nullptr))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  Adam8Params a;
+  a.b1 = (float)beta1;
+  a.omb1 = (float)(1.0 - beta1);
+  a.b2 = (float)beta2;
+  a.omb2 = (float)(1.0 - beta2);
+  a.eps = (float)eps;
+  a.decay = (float)(1.0 - lr * weight_decay);
+  a.step_size = (float)(lr / (1.0 - pow(beta1, (double)step)));
+  a.sqrt_bc2 = (float)sqrt(1.0 - pow(beta2, (double)step));
+  for (int32_t first = 0; first < count; first += kAdamMaxTensors) {
+    const int32_t cnt = (count - first < kAdamMaxTensors) ? count - first : kAdamMaxTensors;
+    int64_t blocks = 0;
+    for (int32_t i = 0; i < kAdamMaxTensors; ++i) {
+      Adam8Tensor &d = a.t[i];
+      if (i < cnt) {
+        const qlora_adamw8_tensor &t = tensors[first + i];
+        d = Adam8Tensor{t.param, t.grad, t.exp_avg_code, t.exp_avg_absmax, t.exp_avg_sq_code, t.exp_avg_sq_absmax,
+                        t.master, t.n, blocks};
+        blocks += (t.n + kAdam8Block - 1) / kAdam8Block;
+      } else {
+        d = Adam8Tensor{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, INT64_MAX};
+      }
+    }
+    a.count = cnt;
+    LAUNCH("adamw8", launch_adamw8(a, blocks, s));
+  }
+  return QLORA_OK;
+}
+
 int qlora_timing_enable(const char *kernel, int enable) {
   if (!kernel) return fail(QLORA_EINVAL, "kernel name is NULL");
   std::lock_guard<std::mutex> lk(g_tmu);

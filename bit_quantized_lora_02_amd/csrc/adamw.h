@@ -25,4 +25,24 @@ struct AdamParams {
 
 hipError_t launch_adamw(const AdamParams &a, int64_t blocks, hipStream_t s);
 
+// 8-bit state: one workgroup per block of 2048 elements of one tensor.
+constexpr int kAdam8Block = 2048;
+struct Adam8Tensor {
+  uint16_t *p;
+  const uint16_t *g;
+  uint8_t *mq;  // first-moment codes (signed book)
+  float *ma;    // first-moment absmax per block
+  uint8_t *vq;  // second-moment codes (unsigned book)
+  float *va;    // second-moment absmax per block
+  float *master;
+  int64_t n;
+  int64_t block0;
+};
+struct Adam8Params {
+  Adam8Tensor t[kAdamMaxTensors];
+  int count;
+  float b1, omb1, b2, omb2, eps, decay, step_size, sqrt_bc2;
+};
+hipError_t launch_adamw8(const Adam8Params &a, int64_t blocks, hipStream_t s);
+
 }  // namespace qlora

@@ -30,10 +30,12 @@ namespace qlora {
 
 namespace {
 
-__device__ __forceinline__ float adam_elem(float &m, float &v, float theta, float g, const AdamParams &a) {
+// (sqrtf is the correctly rounded square root; __fsqrt_rn would be the native one here)
+template <class P>
+__device__ __forceinline__ float adam_elem(float &m, float &v, float theta, float g, const P &a) {
   m = __fadd_rn(__fmul_rn(a.b1, m), __fmul_rn(a.omb1, g));
   v = __fadd_rn(__fmul_rn(a.b2, v), __fmul_rn(__fmul_rn(a.omb2, g), g));
-  const float denom = __fadd_rn(__fdiv_rn(__fsqrt_rn(v), a.sqrt_bc2), a.eps);
+  const float denom = __fadd_rn(__fdiv_rn(sqrtf(v), a.sqrt_bc2), a.eps);
   return __fsub_rn(__fmul_rn(theta, a.decay), __fmul_rn(a.step_size, __fdiv_rn(m, denom)));
 }
 
@@ -115,6 +117,170 @@ __global__ __launch_bounds__(256) void k_adamw(AdamParams a) {
     if (master) master[e] = t;
     p[e] = f32_to_bf16(t);
   }
+}
+
+// ------------------------------------------------------------ 8-bit state
+// "Module 08 - QLoRA & Quantization" (ainiketan.in), "4. QLoRA in code" and "5.
+// Other memory-saving levers": paged_adamw_8bit keeps the state in 8 bits.
+// Block-wise state quantization after Dettmers et al., "8-bit Optimizers via
+// Block-wise Quantization" (ICLR 2022): per block of 2048 elements, 8-bit codes
+// and one binary32 absmax for each moment.  The code book is dynamic: in a
+// signed byte (first moment) bit 7 is the sign and, among the other 7 bits, E =
+// the leading zeros, then an indicator bit, then F = 6 - E fraction bits f;
+// the magnitude is fl32((0.1 + 0.9 ((f + 1) / 2^F)) / 10^E) (binary64, in that
+// order) and all-zero bits mean 0.  An unsigned byte (second moment) counts E
+// among 8 bits, F = 7 - E.  Magnitudes grow with the bits' unsigned value, so a
+// code is the number of thresholds below |x| (threshold: the largest binary32
+// value not above the exact midpoint of two neighbours; ties go down).
+// One workgroup owns one block: it decodes the moments (fl32(book * absmax)),
+// runs the binary32 step of k_adamw, reduces the block's new absmax, and
+// encodes x = fl32(value / absmax) by bisection over the thresholds.
+__device__ __forceinline__ float dyn_mag(int p, int bits) {
+  if (p == 0) return 0.f;
+  const int top = 31 - __builtin_clz((unsigned)p);  // the indicator bit
+  const int E = bits - 1 - top, F = top, f = p - (1 << F);
+  double p10 = 1.0;
+  for (int i = 0; i < E; ++i) p10 *= 10.0;  // exact
+  // each binary64 operation rounded once (no contraction into a fused multiply-add)
+  return (float)__ddiv_rn(__dadd_rn(0.1, __dmul_rn(0.9, __ddiv_rn((double)(f + 1), (double)(1 << F)))), p10);
+}
+__device__ __forceinline__ float below_mid(float lo, float hi) {  // largest binary32 not above (lo + hi) / 2
+  const double mid = __dmul_rn(__dadd_rn((double)lo, (double)hi), 0.5);  // exact
+  float t = (float)mid;
+  if ((double)t > mid) t = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, t) - 1u);  // t > 0 here
+  return t;
+}
+// number of thresholds thr[1 .. n-1] that a (>= 0) exceeds
+__device__ __forceinline__ int dyn_count(float a, const float *thr, int n) {
+  int lo = 0, hi = n - 1;  // answer in [lo, hi]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a > thr[mid]) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256) void k_adamw8(Adam8Params a) {
+  __shared__ float s_sm[128], s_um[256], s_st[128], s_ut[256];
+  __shared__ float s_red[2][4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  s_um[tid] = dyn_mag(tid, 8);
+  if (tid < 128) s_sm[tid] = dyn_mag(tid, 7);
+  __syncthreads();
+  if (tid >= 1) s_ut[tid] = below_mid(s_um[tid - 1], s_um[tid]);
+  if (tid >= 1 && tid < 128) s_st[tid] = below_mid(s_sm[tid - 1], s_sm[tid]);
+
+  const int64_t blk = blockIdx.x;
+  uint16_t *p = nullptr;
+  const uint16_t *g = nullptr;
+  uint8_t *mq = nullptr, *vq = nullptr;
+  float *ma = nullptr, *va = nullptr, *master = nullptr;
+  int64_t n = 0, b0 = 0;
+#pragma unroll
+  for (int i = 0; i < kAdamMaxTensors; ++i) {
+    if (i < a.count && blk >= a.t[i].block0) {
+      p = a.t[i].p, g = a.t[i].g, mq = a.t[i].mq, ma = a.t[i].ma, vq = a.t[i].vq, va = a.t[i].va;
+      master = a.t[i].master, n = a.t[i].n, b0 = a.t[i].block0;
+    }
+  }
+  const int64_t lb = blk - b0;  // block of this tensor
+  const int64_t e0 = lb * kAdam8Block + (int64_t)tid * 8;
+  const int cnt = (int)((n - e0) < 0 ? 0 : ((n - e0) > 8 ? 8 : (n - e0)));
+  const float m_abs = ma[lb], v_abs = va[lb];
+  __syncthreads();  // thresholds visible
+
+  float m[8], v[8], th[8];
+  uint32_t mc[2] = {0u, 0u}, vc[2] = {0u, 0u};
+  float gr[8];
+  if (cnt == 8) {
+    const u32x2_t mw = *reinterpret_cast<const u32x2_t *>(mq + e0), vw = *reinterpret_cast<const u32x2_t *>(vq + e0);
+    mc[0] = mw.x, mc[1] = mw.y, vc[0] = vw.x, vc[1] = vw.y;
+    const u32x4_t gw = *reinterpret_cast<const u32x4_t *>(g + e0);
+    const u32x4_t pw = *reinterpret_cast<const u32x4_t *>(p + e0);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      gr[2 * w] = bf16_lo_to_f32(gw[w]), gr[2 * w + 1] = bf16_hi_to_f32(gw[w]);
+      th[2 * w] = bf16_lo_to_f32(pw[w]), th[2 * w + 1] = bf16_hi_to_f32(pw[w]);
+    }
+    if (master) {
+      const float4 t0 = *reinterpret_cast<const float4 *>(master + e0), t1 = *reinterpret_cast<const float4 *>(master + e0 + 4);
+      th[0] = t0.x, th[1] = t0.y, th[2] = t0.z, th[3] = t0.w, th[4] = t1.x, th[5] = t1.y, th[6] = t1.z, th[7] = t1.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      gr[e] = 0.f, th[e] = 0.f;
+      if (e < cnt) {
+        mc[e >> 2] |= (uint32_t)mq[e0 + e] << (8 * (e & 3));
+        vc[e >> 2] |= (uint32_t)vq[e0 + e] << (8 * (e & 3));
+        gr[e] = __builtin_bit_cast(float, (uint32_t)g[e0 + e] << 16);
+        th[e] = master ? master[e0 + e] : __builtin_bit_cast(float, (uint32_t)p[e0 + e] << 16);
+      }
+    }
+  }
+  float mx = 0.f, vx = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t cm = (mc[e >> 2] >> (8 * (e & 3))) & 0xffu, cv = (vc[e >> 2] >> (8 * (e & 3))) & 0xffu;
+    const float mag = s_sm[cm & 127u];
+    m[e] = __fmul_rn((cm & 128u) ? -mag : mag, m_abs);
+    v[e] = __fmul_rn(s_um[cv], v_abs);
+    th[e] = adam_elem(m[e], v[e], th[e], gr[e], a);
+    if (e < cnt) {
+      mx = fmaxf(mx, fabsf(m[e]));
+      vx = fmaxf(vx, v[e]);
+    }
+  }
+  // block absmax of the new moments
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, o));
+    vx = fmaxf(vx, __shfl_xor(vx, o));
+  }
+  if (lane == 0) s_red[0][wave] = mx, s_red[1][wave] = vx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
+  vx = fmaxf(fmaxf(s_red[1][0], s_red[1][1]), fmaxf(s_red[1][2], s_red[1][3]));
+  if (tid == 0) ma[lb] = mx, va[lb] = vx;
+  uint32_t om[2] = {0u, 0u}, ov[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    uint32_t cm = 0u, cv = 0u;
+    if (mx > 0.f) {
+      const float x = __fdiv_rn(m[e], mx);
+      cm = (uint32_t)dyn_count(fabsf(x), s_st, 128);
+      if (x < 0.f && cm) cm |= 128u;
+    }
+    if (vx > 0.f) cv = (uint32_t)dyn_count(__fdiv_rn(v[e], vx), s_ut, 256);
+    om[e >> 2] |= cm << (8 * (e & 3));
+    ov[e >> 2] |= cv << (8 * (e & 3));
+  }
+  if (cnt == 8) {
+    *reinterpret_cast<u32x2_t *>(mq + e0) = u32x2_t{om[0], om[1]};
+    *reinterpret_cast<u32x2_t *>(vq + e0) = u32x2_t{ov[0], ov[1]};
+    u32x4_t po;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) po[w] = pack_bf16x2(th[2 * w], th[2 * w + 1]);
+    *reinterpret_cast<u32x4_t *>(p + e0) = po;
+    if (master) {
+      *reinterpret_cast<float4 *>(master + e0) = make_float4(th[0], th[1], th[2], th[3]);
+      *reinterpret_cast<float4 *>(master + e0 + 4) = make_float4(th[4], th[5], th[6], th[7]);
+    }
+  } else {
+    for (int e = 0; e < cnt; ++e) {
+      mq[e0 + e] = (uint8_t)(om[e >> 2] >> (8 * (e & 3)));
+      vq[e0 + e] = (uint8_t)(ov[e >> 2] >> (8 * (e & 3)));
+      p[e0 + e] = f32_to_bf16(th[e]);
+      if (master) master[e0 + e] = th[e];
+    }
+  }
+}
+
+hipError_t launch_adamw8(const Adam8Params &a, int64_t blocks, hipStream_t s) {
+  if (blocks == 0) return hipSuccess;
+  launch(k_adamw8, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_adamw(const AdamParams &a, int64_t blocks, hipStream_t s) {

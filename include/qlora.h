@@ -259,6 +259,39 @@ typedef struct qlora_adamw_tensor {
 int qlora_adamw_step(const qlora_adamw_tensor *tensors, int32_t count, double lr, double beta1, double beta2,
                      double eps, double weight_decay, int64_t step, void *stream);
 
+/*
+ * The same AdamW step with block-wise 8-bit moments ("Module 08 - QLoRA &
+ * Quantization", ainiketan.in, "4. QLoRA in code" and "5. Other memory-saving
+ * levers": paged_adamw_8bit; block-wise state quantization after Dettmers et
+ * al., "8-bit Optimizers via Block-wise Quantization", ICLR 2022; paging to host
+ * memory is not done).  Each moment of a tensor of n elements is stored as n
+ * 8-bit codes plus one binary32 absmax per block of 2048 consecutive elements
+ * (ceil(n / 2048) of them).  A code is a byte of a dynamic book: for the first
+ * moment bit 7 is the sign and, among the other 7 bits, E = the number of
+ * leading zeros, then a set indicator bit, then F = 6 - E fraction bits f, the
+ * magnitude being fl32((0.1 + 0.9 ((f + 1) / 2^F)) / 10^E) (binary64 in that
+ * order; all-zero bits: 0); for the second moment all 8 bits are used the same
+ * way (F = 7 - E).  A stored moment is fl32(book[code] * absmax).  Each step:
+ * decode, the binary32 update of qlora_adamw_step, new absmax = the block's
+ * largest magnitude, code = the nearest book magnitude to fl32(value / absmax)
+ * (ties to the smaller; 0 when the absmax is 0).  Zeroed codes and absmax are
+ * the zero state.  Codes 16-byte aligned; absmax 4-byte aligned; the rest as
+ * for qlora_adamw_step.
+ */
+typedef struct qlora_adamw8_tensor {
+  qlora_bf16 *param;
+  const qlora_bf16 *grad;
+  uint8_t *exp_avg_code;     /* [n]               */
+  float *exp_avg_absmax;     /* [ceil(n / 2048)]  */
+  uint8_t *exp_avg_sq_code;  /* [n]               */
+  float *exp_avg_sq_absmax;  /* [ceil(n / 2048)]  */
+  float *master;             /* [n] or NULL       */
+  int64_t n;
+} qlora_adamw8_tensor;
+
+int qlora_adamw8_step(const qlora_adamw8_tensor *tensors, int32_t count, double lr, double beta1, double beta2,
+                      double eps, double weight_decay, int64_t step, void *stream);
+
 /* Static text for a QLORA_E* code. */
 const char *qlora_strerror(int code);
 

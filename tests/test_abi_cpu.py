@@ -261,6 +261,26 @@ def test_error_paths_multi(lib):
     assert multi(nb=need - 1) == B.QLORA_EWORKSPACE
 
 
+def test_error_paths_adamw8(lib):
+    E = B.QLORA_EINVAL
+    ok = B._Adam8Tensor(0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None, 100)
+
+    def step(descs, **kw):
+        arr = (B._Adam8Tensor * max(1, len(descs)))(*descs)
+        args = dict(lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.0, step=1)
+        args.update(kw)
+        return lib.qlora_adamw8_step(arr, len(descs), args["lr"], args["b1"], args["b2"], args["eps"], args["wd"],
+                                     args["step"], None)
+
+    assert step([ok], step=0) == E and step([ok], b1=1.0) == E and step([ok], eps=0.0) == E
+    assert step([B._Adam8Tensor(0x1000, 0x2000, None, 0x4000, 0x5000, 0x6000, None, 100)]) == E
+    assert step([B._Adam8Tensor(0x1000, 0x2000, 0x3008, 0x4000, 0x5000, 0x6000, None, 100)]) == E
+    assert step([B._Adam8Tensor(0x1000, 0x2000, 0x3000, 0x4002, 0x5000, 0x6000, None, 100)]) == E
+    assert step([]) == B.QLORA_OK
+    if not gpu_available():
+        assert step([ok]) == B.QLORA_ENODEV
+
+
 def test_strerror(lib):
     for code in (0, -1, -2, -3, -4):
         assert lib.qlora_strerror(code)
