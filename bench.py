@@ -53,6 +53,8 @@ def parse():
                     help="LoRA dropout probability on the adapter input (training configs; default 0: none)")
     ap.add_argument("--adamw", action="store_true",
                     help="end each training step with the fused AdamW update of every A and B (timed as 'adamw')")
+    ap.add_argument("--adamw8", action="store_true",
+                    help="the same with block-wise 8-bit moments (timed as 'adamw8')")
     ap.add_argument("--adapters", type=int, default=0,
                     help="serve the forward with this many adapters of a pool, the tokens cut into as many equal "
                          "segments (many-adapter batching; forward only)")
@@ -388,6 +390,7 @@ def main():
         layers.append(dict(name=name, n_out=n_out, n_in=n_in, A=A, B=Bm, copies=copies,
                            dA=torch.empty_like(A), dB=torch.empty_like(Bm),
                            adam=[B.AdamState.zeros_like(A), B.AdamState.zeros_like(Bm)] if args.adamw else None,
+                           adam8=[B.Adam8State.zeros_like(A), B.Adam8State.zeros_like(Bm)] if args.adamw8 else None,
                            ws_f=torch.empty(max(1, B.workspace_bytes(B.OP_FWD_DROPOUT if drop else B.OP_FWD, T,
                                                                      n_out, n_in, r)), dtype=torch.uint8, device=dev),
                            ws_b=torch.empty(max(1, B.workspace_bytes(B.OP_BWD, T, n_out, n_in, r)), dtype=torch.uint8,
@@ -405,6 +408,10 @@ def main():
         if args.adamw and train:  # one launch updates every adapter matrix of the step
             B.adamw_step([t for L in layers for t in (L["A"], L["B"])], [t for L in layers for t in (L["dA"], L["dB"])],
                          [s_ for L in layers for s_ in L["adam"]], lr=2e-4, step=i + 1)
+        if args.adamw8 and train:
+            B.adamw8_step([t for L in layers for t in (L["A"], L["B"])],
+                          [t for L in layers for t in (L["dA"], L["dB"])], [s_ for L in layers for s_ in L["adam8"]],
+                          lr=2e-4, step=i + 1)
 
     def step_layers(i):
         for L in layers:
@@ -427,6 +434,8 @@ def main():
     timed = ["nf4_gemm_fwd", "nf4_gemm_dx"] if train else ["nf4_gemm_fwd", "nf4_gemv"]
     if args.adamw and train:
         timed.append("adamw")
+    if args.adamw8 and train:
+        timed.append("adamw8")
     for k in timed:
         B.timing_read(k)  # clear
         B.timing_enable(k, True)
@@ -452,6 +461,7 @@ def main():
         "nf4_gemm_dx": sum(2 * T * L["n_in"] * (L["n_out"] + r) for L in layers),
         "nf4_gemv": sum(2 * T * L["n_out"] * L["n_in"] for L in layers),
         "adamw": 0,
+        "adamw8": 0,
     }
     kbytes = {  # compulsory HBM bytes of one launch: weight stream + activations in and out + LoRA operands
         "nf4_gemm_fwd": sum(weight_bytes(L["n_out"], L["n_in"]) + 2 * T * (L["n_in"] + L["n_out"]) +
@@ -462,6 +472,8 @@ def main():
         "nf4_gemv": sum(weight_bytes(L["n_out"], L["n_in"]) + 2 * T * L["n_in"] for L in layers),
         # per adapter element: bf16 param and grad read, param written; binary32 m and v read and written
         "adamw": sum(22 * r * (L["n_in"] + L["n_out"]) for L in layers),
+        # bf16 param and grad read, param written; one code of each moment read and written (+ absmax)
+        "adamw8": sum(10 * r * (L["n_in"] + L["n_out"]) for L in layers),
     }
     kernels = {}
     for k, (n, ms) in ktimes.items():
@@ -474,7 +486,7 @@ def main():
                       "tflops": kflops[k] / (ms / args.steps * 1e-3) / 1e12 if ms and kflops[k] else None,
                       "gbps": kbytes[k] / (ms / args.steps * 1e-3) / 1e9 if ms else None,
                       "launches_per_step": per_step_launches}
-    dom = max((k for k in kernels if k != "adamw"), key=lambda k: kernels[k]["ms_per_step"])
+    dom = max((k for k in kernels if k not in ("adamw", "adamw8")), key=lambda k: kernels[k]["ms_per_step"])
     kd = kernels[dom]
     wl = args.config if args.config != "small_token" else f"small_token_{lins[0][1]}x8192_T{T}"
     if drop:
@@ -511,7 +523,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": text, "name": wl, "tokens": T, "rank": r, "alpha": alpha,
-                   "pass": ("fwd+bwd+adamw" if args.adamw else "fwd+bwd") if train else "fwd", "lora_dropout": drop,
+                   "pass": ("fwd+bwd+adamw" if args.adamw else "fwd+bwd+adamw8" if args.adamw8 else "fwd+bwd")
+                   if train else "fwd", "lora_dropout": drop,
                    "linears": [[L["name"], L["n_out"], L["n_in"]] for L in layers],
                    "parallelism": "single GPU"},
         "weight_stream_GBps": wgbps,
