@@ -219,8 +219,16 @@ struct Plan {
   Split su, sdu, sdb, sda;
   bool gemv = false;  // forward through the small-token kernels
   int gemv_rg = 0, gemv_w = 0, gemv_split = 0, gemv_main = 0;
+  bool gemv_rows = false;  // one or two tokens: the row-streaming kernel (gemv_split = its U K ranges)
   size_t off_upart = 0;
 };
+
+// Row-streaming GEMV: the K ranges of its U partials (the main grid is sized at launch).
+int gemv_rows_usplit(int64_t K) {
+  for (int c = 16; c > 1; --c)
+    if (K % (c * 128) == 0) return c;
+  return 1;
+}
 
 bool use_gemv(int64_t T, int64_t K) { return T >= 1 && T <= kGemvMaxT && K % 128 == 0; }
 
@@ -238,7 +246,13 @@ Plan make_plan(int op, int64_t T, int64_t N, int64_t K, int32_t r) {
   if (op == QLORA_OP_FWD || op == QLORA_OP_FWD_DROPOUT || op == QLORA_OP_FWD_MULTI) {
     p.su = plan_skinny(T, K);
     part = (size_t)p.su.n * T * p.rn * 4;
-    if ((op == QLORA_OP_FWD || op == QLORA_OP_FWD_MULTI) && use_gemv(T, K)) {  // dropout: the tiled path
+    if (op == QLORA_OP_FWD && use_gemv(T, K) && nf4_gemv_rows_ok(T, K)) {  // one or two tokens
+      p.gemv = p.gemv_rows = true;
+      p.gemv_split = gemv_rows_usplit(K);
+      part = up((size_t)4 * T * N * 4, kAlign);  // up to four row segments
+      p.off_upart = part;
+      part += (size_t)4 * p.gemv_split * T * r * 4;
+    } else if ((op == QLORA_OP_FWD || op == QLORA_OP_FWD_MULTI) && use_gemv(T, K)) {  // dropout: the tiled path
       p.gemv = true;
       nf4_gemv_plan(T, N, K, &p.gemv_rg, &p.gemv_w, &p.gemv_split, &p.gemv_main);
       part = up((size_t)p.gemv_split * T * N * 4, kAlign);
@@ -401,6 +415,14 @@ int linear_fwd(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const qlora_b
   float *part = (float *)(w + p.off_part);
   const float sc = alpha / (float)r;
   const Levels &lv = codebook().lv;
+  if (p.gemv_rows) {  // one or two tokens: bound by the weight stream, one wave per weight row
+    float *upart = (float *)(w + p.off_part + p.off_upart);
+    int nseg = 1;
+    LAUNCH("nf4_gemv", launch_nf4_gemv_rows(X, T, K, q->codes, q->absmax_q, q->absmax_step, N, p.gemv_split, A, r,
+                                            part, upart, lv, s, &nseg));
+    LAUNCH("gemv_finish", launch_gemv_finish(part, upart, nseg, T, N, B, r, sc, Y, U_out, s, p.gemv_split));
+    return QLORA_OK;
+  }
   if (p.gemv) {  // few tokens: bound by the weight stream
     float *upart = (float *)(w + p.off_part + p.off_upart);
     LAUNCH("nf4_gemv", launch_nf4_gemv(X, T, K, q->codes, q->absmax_q, q->absmax_step, N, p.gemv_rg, p.gemv_w,

@@ -81,7 +81,15 @@ hipError_t launch_nf4_gemv(const bf16_t *X, int64_t T, int64_t K, const uint8_t 
                            int64_t r, float *part, float *upart, const Levels &lv, hipStream_t s,
                            const SegTable &sg = SegTable());
 hipError_t launch_gemv_finish(const float *part, const float *upart, int nsplit, int64_t T, int64_t N,
-                              const bf16_t *B, int64_t r, float s, bf16_t *Y, bf16_t *U_out, hipStream_t st);
+                              const bf16_t *B, int64_t r, float s, bf16_t *Y, bf16_t *U_out, hipStream_t st,
+                              int nsplit_u = 0);
+// Row-streaming GEMV for one or two tokens (K % 2048 == 0, T K <= 32768): binary32
+// partials of nseg row segments (part [nseg][T][N], nseg <= 4, returned in *nseg_out) plus the U partials
+// of nsplit_u K ranges (upart [4 nsplit_u][T][r]).
+bool nf4_gemv_rows_ok(int64_t T, int64_t K);
+hipError_t launch_nf4_gemv_rows(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
+                                const float *step, int64_t N, int nsplit_u, const bf16_t *A, int64_t r, float *part,
+                                float *upart, const Levels &lv, hipStream_t s, int *nseg_out);
 // Many adapters: Y = bf16(sum of the weight partials + bf16(s U[t]) B_a^T) with B_a = B_pool + a N r
 // for the adapter a of token t's segment (none: the partials alone).
 hipError_t launch_gemv_finish_multi(const float *part, const float *upart, int nsplit, int64_t T, int64_t N,

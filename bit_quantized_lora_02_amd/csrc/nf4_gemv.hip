@@ -29,6 +29,8 @@
 //    (A single launch with a last-arriving-workgroup reduction needs
 //    device-scope fences, which on this chip write back and invalidate the L2
 //    in every workgroup and cost far more than a second launch.)
+#include <algorithm>
+
 #include "device.h"
 #include "launch.h"
 #include "qlora.h"
@@ -54,6 +56,24 @@ __device__ __forceinline__ u32x4_t decode8_pairs(uint32_t w, float cq, const flo
     o[b] = pack_bf16x2(__fmul_rn(l.x, cq), __fmul_rn(l.y, cq));
   }
   return o;
+}
+
+// Sum over the 64 lanes of a wave with DPP moves: pairs, quads, half rows and rows of 16
+// (quad_perm, row_half_mirror, row_mirror), then row 0 into row 1 and row 2 into row 3
+// (row_bcast:15), then rows 0..1 into rows 2..3 (row_bcast:31).  The total lands in lane 63.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf,
+                                                                   false));
+}
+__device__ __forceinline__ float wave_sum_lane63(float v) {
+  v = dpp_add<0xb1>(v);   // quad_perm [1, 0, 3, 2]
+  v = dpp_add<0x4e>(v);   // quad_perm [2, 3, 0, 1]
+  v = dpp_add<0x141>(v);  // row_half_mirror
+  v = dpp_add<0x140>(v);  // row_mirror
+  v = dpp_add<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
 }
 
 // Partial U over a quarter of one K range: wave w of the workgroup takes
@@ -251,11 +271,154 @@ __global__ __launch_bounds__(256) void k_nf4_gemv(const bf16_t *__restrict__ X, 
   }
 }
 
+// ------------------------------------------------ the row-streaming GEMV
+// For one or two tokens the MFMA formulation wastes most of each 16-token operand
+// and its 16-row loads touch 16 weight rows per instruction.  Here a wave owns
+// weight rows instead: one 16-byte load per lane covers 2048 consecutive
+// weights of one row (1 KB contiguous per wave instruction, like a plain
+// stream); the tokens' activations sit in LDS for the whole launch; a lane
+// decodes its 32 weights byte by byte through the level-pair table into bf16
+// pairs fl32(level * c') and accumulates v_dot2_f32_bf16 with the matching
+// activation pairs; at the end of its piece of a row a wave reduction gives
+// the binary32 partial sum of that piece.
+//
+// Work items: each row is cut into nseg equal segments of Ks = K / nseg columns
+// (nseg = 1, 2 or 4, chosen by the host to even out the items per wave).  Main
+// workgroup g owns segment g % nseg, and its wave w the rows
+// 4 (g / nseg) + w + i 4 gmain / nseg (gmain % nseg == 0); a wave streams all its
+// items as one sequence of steps (CH chunks of 2048 columns each), loading one
+// step ahead in two fixed register slots, the first load issued before the
+// workgroup stages the activations of its segment (TT Ks bf16 in LDS).  part
+// is [nseg][T][N] binary32.  Workgroups 0 .. nsplit_u - 1 come first and form
+// the U partials of K range u as in k_nf4_gemv ([4 nsplit_u][T][r]).
+// K % (2048 CH nseg) == 0 and TT Ks <= 32768; tokens T .. TT-1 are zero.
+template <int TT, int CH>
+__global__ __launch_bounds__(256, TT == 1 ? 6 : 4) void k_nf4_gemv_rows(
+    const bf16_t *__restrict__ X, int64_t T, int64_t K, const uint8_t *__restrict__ codes,
+    const uint8_t *__restrict__ absmax_q, const float *__restrict__ step, int64_t N, int gmain, int nseg, int nsplit_u,
+    const bf16_t *__restrict__ A, int64_t r, float *__restrict__ part, float *__restrict__ upart, Levels lv) {
+  extern __shared__ __attribute__((aligned(16))) bf16_t sx[];  // [TT][Ks], sized at launch
+  __shared__ __attribute__((aligned(16))) float2 s_tab[256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if ((int)blockIdx.x < nsplit_u) {
+    const int64_t u = blockIdx.x, kchunk = K / nsplit_u, kb = u * kchunk;
+    lora_u_partial<1>(X, T, K, A, r, kb, kb + kchunk, upart + (u * 4 + wave) * T * r, wave, lane);
+    return;
+  }
+  const int g = (int)blockIdx.x - nsplit_u, seg = g % nseg;
+  const int64_t Ks = K / nseg;
+  const int64_t row0 = (int64_t)(g / nseg) * 4 + wave, rstride = (int64_t)(gmain / nseg) * 4;
+  const int sps = (int)(K / 2048) / (CH * nseg);             // steps per item
+  const int64_t items = row0 < N ? (N - row0 + rstride - 1) / rstride : 0;
+  const int64_t total = items * sps;
+  const int jseg = seg * sps * CH;  // first 2048-column chunk of this workgroup's segment
+
+  struct Slot {
+    u32x4_t c[CH];
+    RawScale sc[CH];
+  };
+  // load stream: step lg of the current item; the lane's 16 code bytes of chunk j of the row sit
+  // at lrow + 1024 j and their block constant at lblk + 32 j.  The stream stops advancing at the
+  // last step, so the prefetches past the end reload that step (never used).
+  int64_t li = 0;
+  int lg = 0;
+  const uint8_t *lrow = codes + row0 * (K / 2) + 16 * lane;
+  int64_t lblk = row0 * (K / 64) + (lane >> 1);
+  const int64_t row_bytes = rstride * (K / 2), row_blocks = rstride * (K / 64);
+  auto load_slot = [&](Slot &sl) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int j = jseg + lg * CH + c;
+      sl.c[c] = *reinterpret_cast<const u32x4_t *>(lrow + 1024 * j);
+      const int64_t b = lblk + 32 * j;
+      sl.sc[c] = RawScale{(uint32_t)absmax_q[b], step[b >> 8]};
+    }
+    if (++li < total && ++lg == sps) {
+      lg = 0;
+      lrow += row_bytes;
+      lblk += row_blocks;
+    }
+  };
+  Slot s0, s1;
+  if (total > 0) load_slot(s0);  // in flight while the activations are staged
+
+  pair_levels_to_lds(lv, s_tab, tid);
+  // activations of the TT tokens (T..TT-1: zero); 16-byte unit u of a token's row is stored at
+  // unit u ^ ((u >> 4) & 3), so that the 16 lanes of one pass of a 16-byte read (lane l reads
+  // unit 4 l + q) fall in 16 distinct bank groups
+  const bf16_t *xs = X + seg * Ks;
+  for (int64_t i = (int64_t)tid * 8; i < TT * Ks; i += 256 * 8) {
+    const int64_t t = i / Ks, k = i - t * Ks, u = k >> 3;
+    *reinterpret_cast<u32x4_t *>(sx + t * Ks + 8 * (u ^ ((u >> 4) & 3))) =
+        t < T ? *reinterpret_cast<const u32x4_t *>(xs + t * K + k) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  if (total <= 0) return;
+
+  // this lane's 16-byte activation units of chunk 0 (unit 4 lane + q, swizzled as staged)
+  const int xsw = (lane >> 2) & 3;
+  const bf16_t *xq[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) xq[q] = sx + 8 * (4 * lane + (q ^ xsw));
+  float acc[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) acc[t] = 0.f;
+  float *pseg = part + (int64_t)seg * T * N;
+  int64_t cn = row0;  // compute stream: step cg of the item on row cn
+  int cg = 0;
+  auto do_step = [&](Slot &cur, Slot &refill) {
+    load_slot(refill);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int j = jseg + cg * CH + c;
+      const float cq = scale_of(cur.sc[c]);
+      u32x4_t xv[TT][4];
+#pragma unroll
+      for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xv[t][q] = *reinterpret_cast<const u32x4_t *>(xq[q] + t * Ks + 2048 * (j - jseg));
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        const uint32_t w = cur.c[c][wd];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const float2 l = s_tab[(w >> (8 * b)) & 0xffu];
+          const bf16x2_t wp = __builtin_bit_cast(bf16x2_t, pack_bf16x2(__fmul_rn(l.x, cq), __fmul_rn(l.y, cq)));
+#pragma unroll
+          for (int t = 0; t < TT; ++t) {
+            // copied to a scalar first: this compiler lowers a bit_cast of a vector-element
+            // lvalue as a read of element 0
+            const uint32_t xw = xv[t][wd][b];
+            acc[t] = __builtin_amdgcn_fdot2_f32_bf16(wp, __builtin_bit_cast(bf16x2_t, xw), acc[t], false);
+          }
+        }
+      }
+    }
+    if (++cg == sps) {  // item done: reduce over the wave, lane 63 writes the partial
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        const float v = wave_sum_lane63(acc[t]);
+        if (lane == 63 && t < T) pseg[t * N + cn] = v;
+        acc[t] = 0.f;
+      }
+      cg = 0;
+      cn += rstride;
+    }
+  };
+  for (int64_t f = 0; f < total; f += 2) {
+    do_step(s0, s1);
+    if (f + 1 < total) do_step(s1, s0);
+  }
+}
+
 // Workgroup (x, t): U[t, :] = sum of the nup U partials upart[p][t][:] (thread
 // (j, q) adds the partials p = q, q + 8, ... in order, then the eight subtotals
 // are added in q order), V = bf16(s U) in LDS (U_out[t, :] = bf16(U) from
 // x == 0); then for its 256 outputs n:
 // Y[t, n] = bf16(sum over p (in order) of part[p][t][n] + V . B[n, :r]).
+// The weight partials and, for r = 8 NBP, the row of B are loaded before the U
+// sums, so that their latency overlaps that of the U partials.
+template <int NBP>
 __global__ __launch_bounds__(256) void k_gemv_finish(const float *__restrict__ part, const float *__restrict__ upart,
                                                      int nsplit, int nup, int64_t T, int64_t N,
                                                      const bf16_t *__restrict__ B, int64_t r, float s,
@@ -264,6 +427,25 @@ __global__ __launch_bounds__(256) void k_gemv_finish(const float *__restrict__ p
   __shared__ float s_v[QLORA_MAX_RANK];
   const int tid = threadIdx.x;
   const int64_t t = blockIdx.y;
+  const int64_t n = (int64_t)blockIdx.x * 256 + tid;
+  const bool nok = n < N;
+  float y = 0.f;
+  u32x4_t bw[NBP > 0 ? NBP : 1];
+  if (nok) {  // all loads first, then the additions in split order
+    const float *src = part + t * N + n;
+    const int64_t stride = T * N;
+    int p = 0;
+    for (; p + 8 <= nsplit; p += 8) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = src[(int64_t)(p + q) * stride];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) y += v[q];
+    }
+    for (; p < nsplit; ++p) y += src[(int64_t)p * stride];
+#pragma unroll
+    for (int c = 0; c < NBP; ++c) bw[c] = *reinterpret_cast<const u32x4_t *>(B + n * r + 8 * c);
+  }
   for (int i = tid; i < 8 * r; i += 256) {
     const int j = i % r, q = i / r;
     float u = 0.f;
@@ -279,35 +461,30 @@ __global__ __launch_bounds__(256) void k_gemv_finish(const float *__restrict__ p
     if (U_out && blockIdx.x == 0) U_out[t * r + tid] = f32_to_bf16(u);
   }
   __syncthreads();
-  const int64_t n = (int64_t)blockIdx.x * 256 + tid;
-  if (n >= N) return;
-  float y = 0.f;
-  {  // all loads first, then the additions in split order
-    const float *src = part + t * N + n;
-    const int64_t stride = T * N;
-    int p = 0;
-    for (; p + 8 <= nsplit; p += 8) {
-      float v[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = src[(int64_t)(p + q) * stride];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) y += v[q];
-    }
-    for (; p < nsplit; ++p) y += src[(int64_t)p * stride];
-  }
+  if (!nok) return;
   float l = 0.f;
-  const bf16_t *brow = B + n * r;
-  int64_t j = 0;
-  if ((r & 7) == 0)  // rows of B are 16-byte multiples: 8 ranks per load
-    for (; j < r; j += 8) {
-      const u32x4_t w = *reinterpret_cast<const u32x4_t *>(brow + j);
+  if (NBP > 0) {
+#pragma unroll
+    for (int c = 0; c < NBP; ++c)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        l = fmaf(s_v[j + 2 * e], bf16_lo_to_f32(w[e]), l);
-        l = fmaf(s_v[j + 2 * e + 1], bf16_hi_to_f32(w[e]), l);
+        l = fmaf(s_v[8 * c + 2 * e], bf16_lo_to_f32(bw[c][e]), l);
+        l = fmaf(s_v[8 * c + 2 * e + 1], bf16_hi_to_f32(bw[c][e]), l);
       }
-    }
-  for (; j < r; ++j) l = fmaf(s_v[j], bf16_lo_to_f32(brow[j]), l);
+  } else {
+    const bf16_t *brow = B + n * r;
+    int64_t j = 0;
+    if ((r & 7) == 0)  // rows of B are 16-byte multiples: 8 ranks per load
+      for (; j < r; j += 8) {
+        const u32x4_t w = *reinterpret_cast<const u32x4_t *>(brow + j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          l = fmaf(s_v[j + 2 * e], bf16_lo_to_f32(w[e]), l);
+          l = fmaf(s_v[j + 2 * e + 1], bf16_hi_to_f32(w[e]), l);
+        }
+      }
+    for (; j < r; ++j) l = fmaf(s_v[j], bf16_lo_to_f32(brow[j]), l);
+  }
   Y[t * N + n] = f32_to_bf16(y + l);
 }
 
@@ -452,10 +629,95 @@ hipError_t launch_nf4_gemv(const bf16_t *X, int64_t T, int64_t K, const uint8_t 
 }
 
 hipError_t launch_gemv_finish(const float *part, const float *upart, int nsplit, int64_t T, int64_t N,
-                              const bf16_t *B, int64_t r, float s, bf16_t *Y, bf16_t *U_out, hipStream_t st) {
+                              const bf16_t *B, int64_t r, float s, bf16_t *Y, bf16_t *U_out, hipStream_t st,
+                              int nsplit_u) {
   if (T == 0) return hipSuccess;
   dim3 grid((unsigned)((N + 255) / 256), (unsigned)T);
-  launch(k_gemv_finish, grid, dim3(256), 0, st, part, upart, nsplit, 4 * nsplit, T, N, B, r, s, Y, U_out);
+  const int nup = 4 * (nsplit_u > 0 ? nsplit_u : nsplit);
+  const int nbp = (r % 8 == 0 && r <= 32) ? (int)(r / 8) : 0;
+  if (nbp == 4) launch(k_gemv_finish<4>, grid, dim3(256), 0, st, part, upart, nsplit, nup, T, N, B, r, s, Y, U_out);
+  else if (nbp == 3) launch(k_gemv_finish<3>, grid, dim3(256), 0, st, part, upart, nsplit, nup, T, N, B, r, s, Y, U_out);
+  else if (nbp == 2) launch(k_gemv_finish<2>, grid, dim3(256), 0, st, part, upart, nsplit, nup, T, N, B, r, s, Y, U_out);
+  else if (nbp == 1) launch(k_gemv_finish<1>, grid, dim3(256), 0, st, part, upart, nsplit, nup, T, N, B, r, s, Y, U_out);
+  else launch(k_gemv_finish<0>, grid, dim3(256), 0, st, part, upart, nsplit, nup, T, N, B, r, s, Y, U_out);
+  return hipGetLastError();
+}
+
+// one or two tokens (the activations of that many take TT K bf16 of LDS, at most 64 KB); from
+// three tokens on the MFMA GEMV is faster
+static int rows_tt(int64_t T) { return T <= 1 ? 1 : 2; }
+bool nf4_gemv_rows_ok(int64_t T, int64_t K) { return T >= 1 && T <= 2 && K % 2048 == 0 && rows_tt(T) * K <= 32768; }
+
+// Workgroups of one variant resident on the device at once with `shm` bytes of dynamic LDS
+// (a few LDS sizes cached per variant).
+template <int TT, int CH>
+static int rows_resident(uint32_t shm) {
+  static thread_local uint32_t c_shm[4] = {0, 0, 0, 0};
+  static thread_local int c_res[4] = {0, 0, 0, 0};
+  for (int i = 0; i < 4; ++i)
+    if (c_res[i] > 0 && c_shm[i] == shm) return c_res[i];
+  int dev = 0, cus = 0, nb = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_nf4_gemv_rows<TT, CH>, 256, shm) != hipSuccess || nb < 1 ||
+      cus < 1)
+    return 0;
+  for (int i = 3; i > 0; --i) {
+    c_shm[i] = c_shm[i - 1];
+    c_res[i] = c_res[i - 1];
+  }
+  c_shm[0] = shm;
+  c_res[0] = nb * cus;
+  return c_res[0];
+}
+
+// Work split of the row-streaming GEMV: the number of row segments (1, 2 or 4, dividing the
+// steps of a row) whose longest wave has the fewest steps (ties: fewer segments), and the
+// main-grid workgroups (a multiple of the segments), at most what stays resident next to the
+// U workgroups with that segment's share of the activations in LDS.
+template <int TT, int CH>
+static bool rows_split(int64_t N, int64_t K, int nsplit_u, int *gmain, int *nseg) {
+  const int spr = (int)(K / 2048) / CH;
+  int64_t best = -1;
+  for (int sg = 1; sg <= 4; sg *= 2) {
+    if (spr % sg) continue;
+    const int res = rows_resident<TT, CH>((uint32_t)(TT * (K / sg) * 2));
+    if (res <= 0) return false;
+    int64_t g = std::min<int64_t>(std::max(1, res - nsplit_u), (N * sg + 3) / 4);
+    g = std::max<int64_t>(sg, g / sg * sg);
+    const int64_t nw = 4 * g;
+    const int64_t cost = ((N * sg + nw - 1) / nw) * (spr / sg);
+    if (best < 0 || cost < best) {
+      best = cost;
+      *gmain = (int)g;
+      *nseg = sg;
+    }
+  }
+  return best >= 0;
+}
+
+hipError_t launch_nf4_gemv_rows(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
+                                const float *step, int64_t N, int nsplit_u, const bf16_t *A, int64_t r, float *part,
+                                float *upart, const Levels &lv, hipStream_t s, int *nseg_out) {
+  *nseg_out = 1;
+  if (T == 0) return hipSuccess;
+  const int64_t nch = K / 2048;
+  const int ch = nch % 2 == 0 ? 2 : 1;  // two chunks per step (four cost occupancy)
+  const int tt = rows_tt(T);
+  int gmain = 1, nseg = 1;
+  bool ok;
+  if (tt == 1) ok = ch == 2 ? rows_split<1, 2>(N, K, nsplit_u, &gmain, &nseg) : rows_split<1, 1>(N, K, nsplit_u, &gmain, &nseg);
+  else ok = ch == 2 ? rows_split<2, 2>(N, K, nsplit_u, &gmain, &nseg) : rows_split<2, 1>(N, K, nsplit_u, &gmain, &nseg);
+  if (!ok) return hipErrorInvalidDeviceFunction;
+  const dim3 grid((unsigned)(gmain + nsplit_u));
+  const uint32_t shm = (uint32_t)(tt * (K / nseg) * 2);
+#define QLORA_ROWS(TT, CH_)                                                                                   \
+  launch(k_nf4_gemv_rows<TT, CH_>, grid, dim3(256), shm, s, X, T, K, codes, absmax_q, step, N, gmain, nseg, \
+         nsplit_u, A, r, part, upart, lv)
+  if (tt == 1) { if (ch == 2) QLORA_ROWS(1, 2); else QLORA_ROWS(1, 1); }
+  else { if (ch == 2) QLORA_ROWS(2, 2); else QLORA_ROWS(2, 1); }
+#undef QLORA_ROWS
+  *nseg_out = nseg;
   return hipGetLastError();
 }
 
