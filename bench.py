@@ -78,6 +78,9 @@ def log(*a):
 
 
 KERNEL_SOURCES = {"nf4_gemm_fwd": "nf4_gemm.hip", "nf4_gemm_dx": "nf4_gemm.hip", "nf4_gemv": "nf4_gemv.hip"}
+# kernel symbols behind each timed launch label (the small-token forward has two kernels)
+KERNEL_SYMBOLS = {"nf4_gemm_fwd": ("k_nf4_gemm_fwd",), "nf4_gemm_dx": ("k_nf4_gemm_dx",),
+                  "nf4_gemv": ("k_nf4_gemv", "k_nf4_gemv_rows")}
 
 
 def source_digest(kernel: str) -> str:
@@ -144,11 +147,12 @@ def write_traffic(args, workload: str, kernels):
     fetch_rows = _pmc_rows(os.path.join(d, "fetch"))
     write_rows = _pmc_rows(os.path.join(d, "write"))
     for k in kernels:
-        symbol = "k_" + k
-        fk = _per_dispatch_kib(fetch_rows, "FETCH_SIZE", lambda n: symbol + "<" in n or symbol + "(" in n)
-        wk = _per_dispatch_kib(write_rows, "WRITE_SIZE", lambda n: symbol + "<" in n or symbol + "(" in n)
+        syms = KERNEL_SYMBOLS.get(k, ("k_" + k,))
+        match = lambda n: any(sy + "<" in n or sy + "(" in n for sy in syms)
+        fk = _per_dispatch_kib(fetch_rows, "FETCH_SIZE", match)
+        wk = _per_dispatch_kib(write_rows, "WRITE_SIZE", match)
         if not fk or not wk:
-            log(f"no dispatches of {symbol} in the counter runs")
+            log(f"no dispatches of {' or '.join(syms)} in the counter runs")
             continue
         fetch_b = sum(fk) / len(fk) * 1024 * f_fac
         write_b = sum(wk) / len(wk) * 1024 * w_fac
