@@ -411,6 +411,49 @@ __global__ __launch_bounds__(256, TT == 1 ? 6 : 4) void k_nf4_gemv_rows(
   }
 }
 
+// Sums of the finishing kernels, in index order with every load issued first (a loop bound known only
+// at run time would otherwise wait for each load before the next): the 1 <= n <= 16 weight partials
+// src[0], src[stride], ..., and the U partials p = q, q + 8, ... < nup <= 64 of (t, j).  Indexes past
+// the end are clamped (the load stays in bounds) and the value replaced by +0; adding +0 to a sum
+// that starts at +0 changes nothing.
+constexpr int kFinishMaxSplit = 16, kFinishMaxUp = 64;
+__device__ __forceinline__ void load_partials(const float *__restrict__ src, int64_t stride, int n,
+                                              float (&v)[kFinishMaxSplit]) {
+#pragma unroll
+  for (int q = 0; q < kFinishMaxSplit; ++q) v[q] = src[(int64_t)(q < n ? q : n - 1) * stride];
+}
+__device__ __forceinline__ float add_partials(const float (&v)[kFinishMaxSplit], int n) {
+  float y = 0.f;
+#pragma unroll
+  for (int q = 0; q < kFinishMaxSplit; ++q) y += q < n ? v[q] : 0.f;
+  return y;
+}
+__device__ __forceinline__ float sum_partials(const float *__restrict__ src, int64_t stride, int n) {
+  float v[kFinishMaxSplit];
+  load_partials(src, stride, n, v);
+  return add_partials(v, n);
+}
+__device__ __forceinline__ void load_upart(const float *__restrict__ upart, int64_t T, int64_t t, int64_t r, int j,
+                                           int q, int nup, float (&v)[kFinishMaxUp / 8]) {
+#pragma unroll
+  for (int c = 0; c < kFinishMaxUp / 8; ++c) {
+    const int p = q + 8 * c;
+    v[c] = upart[((int64_t)(p < nup ? p : nup - 1) * T + t) * r + j];
+  }
+}
+__device__ __forceinline__ float add_upart(const float (&v)[kFinishMaxUp / 8], int q, int nup) {
+  float u = 0.f;
+#pragma unroll
+  for (int c = 0; c < kFinishMaxUp / 8; ++c) u += q + 8 * c < nup ? v[c] : 0.f;
+  return u;
+}
+__device__ __forceinline__ float sum_upart(const float *__restrict__ upart, int64_t T, int64_t t, int64_t r, int j,
+                                           int q, int nup) {
+  float v[kFinishMaxUp / 8];
+  load_upart(upart, T, t, r, j, q, nup, v);
+  return add_upart(v, q, nup);
+}
+
 // Workgroup (x, t): U[t, :] = sum of the nup U partials upart[p][t][:] (thread
 // (j, q) adds the partials p = q, q + 8, ... in order, then the eight subtotals
 // are added in q order), V = bf16(s U) in LDS (U_out[t, :] = bf16(U) from
@@ -429,28 +472,21 @@ __global__ __launch_bounds__(256) void k_gemv_finish(const float *__restrict__ p
   const int64_t t = blockIdx.y;
   const int64_t n = (int64_t)blockIdx.x * 256 + tid;
   const bool nok = n < N;
-  float y = 0.f;
+  // this thread's first U pair (j, q) = (tid % r, tid / r), its weight partials and its B row are all
+  // loaded (indexes clamped into range) before the first addition
+  const int iu = tid < 8 * r ? tid : 8 * (int)r - 1;
+  const int64_t nn = nok ? n : N - 1;
+  float uv[kFinishMaxUp / 8], pv[kFinishMaxSplit];
   u32x4_t bw[NBP > 0 ? NBP : 1];
-  if (nok) {  // all loads first, then the additions in split order
-    const float *src = part + t * N + n;
-    const int64_t stride = T * N;
-    int p = 0;
-    for (; p + 8 <= nsplit; p += 8) {
-      float v[8];
+  load_upart(upart, T, t, r, iu % r, iu / r, nup, uv);
+  load_partials(part + t * N + nn, T * N, nsplit, pv);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = src[(int64_t)(p + q) * stride];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) y += v[q];
-    }
-    for (; p < nsplit; ++p) y += src[(int64_t)p * stride];
-#pragma unroll
-    for (int c = 0; c < NBP; ++c) bw[c] = *reinterpret_cast<const u32x4_t *>(B + n * r + 8 * c);
-  }
-  for (int i = tid; i < 8 * r; i += 256) {
+  for (int c = 0; c < NBP; ++c) bw[c] = *reinterpret_cast<const u32x4_t *>(B + nn * r + 8 * c);
+  if (tid < 8 * r) s_sub[tid / r][tid % r] = add_upart(uv, iu / r, nup);
+  const float y = add_partials(pv, nsplit);
+  for (int i = tid + 256; i < 8 * r; i += 256) {
     const int j = i % r, q = i / r;
-    float u = 0.f;
-    for (int p = q; p < nup; p += 8) u += upart[((int64_t)p * T + t) * r + j];
-    s_sub[q][j] = u;
+    s_sub[q][j] = sum_upart(upart, T, t, r, j, q, nup);
   }
   __syncthreads();
   if (tid < r) {
@@ -515,9 +551,7 @@ __global__ __launch_bounds__(256) void k_gemv_finish_multi(const float *__restri
   if (has) {
     for (int i = tid; i < 8 * r; i += 256) {
       const int j = i % r, q = i / r;
-      float u = 0.f;
-      for (int p = q; p < nup; p += 8) u += upart[((int64_t)p * T + t) * r + j];
-      s_sub[q][j] = u;
+      s_sub[q][j] = sum_upart(upart, T, t, r, j, q, nup);
     }
     __syncthreads();
     if (tid < r) {
@@ -530,20 +564,7 @@ __global__ __launch_bounds__(256) void k_gemv_finish_multi(const float *__restri
   __syncthreads();
   const int64_t n = (int64_t)blockIdx.x * 256 + tid;
   if (n >= N) return;
-  float y = 0.f;
-  {  // all loads first, then the additions in split order
-    const float *src = part + t * N + n;
-    const int64_t stride = T * N;
-    int p = 0;
-    for (; p + 8 <= nsplit; p += 8) {
-      float v[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = src[(int64_t)(p + q) * stride];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) y += v[q];
-    }
-    for (; p < nsplit; ++p) y += src[(int64_t)p * stride];
-  }
+  const float y = sum_partials(part + t * N + n, T * N, nsplit);
   float l = 0.f;
   if (has) {
     const bf16_t *brow = B_pool + ((int64_t)a * N + n) * r;  // r % 8 == 0: 16-byte rows
@@ -564,6 +585,7 @@ hipError_t launch_gemv_finish_multi(const float *part, const float *upart, int n
                                     hipStream_t st) {
   if (T == 0) return hipSuccess;
   dim3 grid((unsigned)((N + 255) / 256), (unsigned)T);
+  if (nsplit > kFinishMaxSplit || 4 * nsplit > kFinishMaxUp) return hipErrorInvalidValue;
   launch(k_gemv_finish_multi, grid, dim3(256), 0, st, part, upart, nsplit, 4 * nsplit, T, N, B_pool, r, s, sg, Y);
   return hipGetLastError();
 }
@@ -634,6 +656,7 @@ hipError_t launch_gemv_finish(const float *part, const float *upart, int nsplit,
   if (T == 0) return hipSuccess;
   dim3 grid((unsigned)((N + 255) / 256), (unsigned)T);
   const int nup = 4 * (nsplit_u > 0 ? nsplit_u : nsplit);
+  if (nsplit > kFinishMaxSplit || nup > kFinishMaxUp) return hipErrorInvalidValue;
   const int nbp = (r % 8 == 0 && r <= 32) ? (int)(r / 8) : 0;
   if (nbp == 4) launch(k_gemv_finish<4>, grid, dim3(256), 0, st, part, upart, nsplit, nup, T, N, B, r, s, Y, U_out);
   else if (nbp == 3) launch(k_gemv_finish<3>, grid, dim3(256), 0, st, part, upart, nsplit, nup, T, N, B, r, s, Y, U_out);
