@@ -350,7 +350,7 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
   al.init(X, K, m0, T, wave, lane);
   // this thread decodes weights part*E .. part*E+E-1 of tile row brow
   constexpr int PARTS = BK / C::E;
-  const bool decoder = tid < C::DEC;  // wave-uniform
+  const bool decoder = C::DEC == C::NT || tid < C::DEC;  // wave-uniform; a constant when every thread decodes
   const int brow = decoder ? tid / PARTS : 0, part = tid % PARTS;
   const int64_t wrow = (n0 + brow < N) ? n0 + brow : N - 1;  // rows past N feed columns that are never stored
   const uint8_t *crow = codes + wrow * (K / 2) + part * (C::E / 2);
@@ -508,7 +508,7 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
   al.init(dY, N, m0, T, wave, lane);
   // this thread decodes columns piece*E .. piece*E+E-1 of tile row bn (weight row k0 + bn)
   constexpr int PIECES = C::BN / C::E;
-  const bool decoder = tid < C::DEC;  // wave-uniform
+  const bool decoder = tid < C::DEC;  // wave-uniform (kept a run-time value here: measured faster for dX)
   const int bn = decoder ? tid / PIECES : 0, piece = tid % PIECES;
   const int64_t kc = (n0 + piece * C::E + C::E <= K) ? n0 + piece * C::E : K - C::E;  // columns past K: never stored
   uint32_t rc[2][C::NWD];
