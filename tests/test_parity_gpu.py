@@ -329,7 +329,7 @@ def test_small_token_forward(n_out, T):
 @pytest.mark.parametrize("n_out,n_in,T,r", [(72, 2048, 1, 16), (1032, 4096, 2, 5), (520, 8192, 1, 32),
                                             (264, 16384, 2, 64), (8, 2048, 2, 8), (4104, 6144, 1, 12),
                                             (2056, 4096, 2, 24), (6152, 8192, 1, 16), (520, 8192, 3, 16),
-                                            (8, 2048, 4, 8)])
+                                            (8, 2048, 4, 8), (8, 2048, 1, 1), (16, 4096, 2, 3)])
 def test_row_streaming_forward(n_out, n_in, T, r):
     """Few tokens with n_in % 2048 == 0: the row-streaming kernel (1-2 tokens, one wave per weight row, rows cut
     into 1, 2 or 4 segments) and the MFMA kernel (3-4 tokens), checked in full."""
