@@ -186,15 +186,25 @@ __global__ __launch_bounds__(256) void k_nf4_gemv(const bf16_t *__restrict__ X, 
     u32x4_t c[RG][W];
     RawScale cq[RG][NB];
   };
-  // load stream position: item li of this workgroup, step ls
-  int64_t li = 0;
-  int ls = 0;
+  // Item i = tile * nsplit + split; a workgroup's items are gmain apart, so (tile, split) advances by
+  // (gmain / nsplit, gmain % nsplit) with a carry instead of a division per step.
+  const int64_t item_dt = gmain / nsplit;
+  const int item_ds = gmain % nsplit;
+  auto next_item = [&](int64_t &tile, int &split) {
+    tile += item_dt;
+    split += item_ds;
+    if (split >= nsplit) {
+      split -= nsplit;
+      ++tile;
+    }
+  };
+  // load stream position: item li of this workgroup (tile lt, split lsp), step ls; it stops
+  // advancing at the last step, so the prefetches past the end re-read that step (unused)
+  int64_t li = 0, lt = (int64_t)blockIdx.x / nsplit;
+  int ls = 0, lsp = (int)((int64_t)blockIdx.x % nsplit);
   auto load_slot = [&](Slot &sl) {
-    const bool past = li >= my_items;  // past the end: re-read the last step (unused)
-    const int64_t item = blockIdx.x + (past ? my_items - 1 : li) * gmain;
-    const int sidx = past ? nsteps - 1 : ls;
-    const int64_t tile = item / nsplit, split = item - tile * nsplit;
-    const int64_t koff = split * kchunk + (int64_t)sidx * D + 32 * W * g;
+    const int64_t tile = lt;
+    const int64_t koff = (int64_t)lsp * kchunk + (int64_t)ls * D + 32 * W * g;
 #pragma unroll
     for (int q = 0; q < RG; ++q) {
       int64_t n = row_of(tile, q);
@@ -205,18 +215,20 @@ __global__ __launch_bounds__(256) void k_nf4_gemv(const bf16_t *__restrict__ X, 
 #pragma unroll
       for (int b = 0; b < NB; ++b) sl.cq[q][b] = load_scale(absmax_q, step, n * (K / 64) + koff / 64 + b);
     }
-    if (++ls == nsteps) {
+    if (ls + 1 < nsteps) {
+      ++ls;
+    } else if (li + 1 < my_items) {
       ls = 0;
       ++li;
+      next_item(lt, lsp);
     }
   };
-  // compute stream position: item ci, step cs
-  int64_t ci = 0;
-  int cs = 0;
+  // compute stream position: step cs of the item at (tile ct, split csp)
+  int64_t ct = (int64_t)blockIdx.x / nsplit;
+  int cs = 0, csp = (int)((int64_t)blockIdx.x % nsplit);
   auto do_step = [&](Slot &cur, Slot &refill) {
-    const int64_t item = blockIdx.x + ci * gmain;
-    const int64_t tile = item / nsplit, split = item - tile * nsplit;
-    const int64_t koff = split * kchunk + (int64_t)cs * D;
+    const int64_t tile = ct;
+    const int64_t koff = (int64_t)csp * kchunk + (int64_t)cs * D;
     // this step's activations first, then the code prefetch: vector-memory counters complete in
     // order, so waiting for activations issued after the prefetch would wait for the prefetch too
     u32x4_t a[MT][4 * W];
@@ -241,7 +253,7 @@ __global__ __launch_bounds__(256) void k_nf4_gemv(const bf16_t *__restrict__ X, 
     }
     if (++cs == nsteps) {  // item done: store its partial sums and start the next
       // accumulator element e of lane l holds token 16 m + 4 (l >> 4) + e, row n
-      float *dst = part + split * T * N;
+      float *dst = part + (int64_t)csp * T * N;
 #pragma unroll
       for (int q = 0; q < RG; ++q) {
         const int64_t n = row_of(tile, q);
@@ -256,7 +268,7 @@ __global__ __launch_bounds__(256) void k_nf4_gemv(const bf16_t *__restrict__ X, 
         }
       }
       cs = 0;
-      ++ci;
+      next_item(ct, csp);
     }
   };
   // three fixed slots, unrolled so that no register holding a load in flight
