@@ -134,22 +134,39 @@ __global__ __launch_bounds__(256) void k_adamw(AdamParams a) {
 // value not above the exact midpoint of two neighbours; ties go down).
 // One workgroup owns one block: it decodes the moments (fl32(book * absmax)),
 // runs the binary32 step of k_adamw, reduces the block's new absmax, and
-// encodes x = fl32(value / absmax) by bisection over the thresholds.
-__device__ __forceinline__ float dyn_mag(int p, int bits) {
+// encodes x = fl32(value / absmax) by bisection over the thresholds (the books
+// and thresholds are compile-time constants, copied into LDS).
+constexpr float dyn_mag(int p, int bits) {
   if (p == 0) return 0.f;
-  const int top = 31 - __builtin_clz((unsigned)p);  // the indicator bit
+  int top = 0;  // the indicator bit
+  while ((p >> (top + 1)) != 0) ++top;
   const int E = bits - 1 - top, F = top, f = p - (1 << F);
   double p10 = 1.0;
   for (int i = 0; i < E; ++i) p10 *= 10.0;  // exact
-  // each binary64 operation rounded once (no contraction into a fused multiply-add)
-  return (float)__ddiv_rn(__dadd_rn(0.1, __dmul_rn(0.9, __ddiv_rn((double)(f + 1), (double)(1 << F)))), p10);
+  // each binary64 operation rounded once, in this order
+  return (float)((0.1 + 0.9 * ((double)(f + 1) / (double)(1 << F))) / p10);
 }
-__device__ __forceinline__ float below_mid(float lo, float hi) {  // largest binary32 not above (lo + hi) / 2
-  const double mid = __dmul_rn(__dadd_rn((double)lo, (double)hi), 0.5);  // exact
+constexpr float below_mid(float lo, float hi) {  // largest binary32 not above (lo + hi) / 2
+  const double mid = ((double)lo + (double)hi) * 0.5;  // exact
   float t = (float)mid;
   if ((double)t > mid) t = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, t) - 1u);  // t > 0 here
   return t;
 }
+// The two books and their thresholds, computed once at compile time (the constant evaluator rounds
+// every binary64 operation to nearest, as the arithmetic above states): magnitudes of the unsigned
+// (um) and signed (sm) codes, and thr[i] = below_mid(mag[i-1], mag[i]) (entry 0 unused).
+struct DynBooks {
+  float um[256], sm[128], ut[256], st[128];
+};
+constexpr DynBooks make_dyn_books() {
+  DynBooks b{};
+  for (int i = 0; i < 256; ++i) b.um[i] = dyn_mag(i, 8);
+  for (int i = 0; i < 128; ++i) b.sm[i] = dyn_mag(i, 7);
+  for (int i = 1; i < 256; ++i) b.ut[i] = below_mid(b.um[i - 1], b.um[i]);
+  for (int i = 1; i < 128; ++i) b.st[i] = below_mid(b.sm[i - 1], b.sm[i]);
+  return b;
+}
+__constant__ const DynBooks kDynBooks = make_dyn_books();
 // number of thresholds thr[1 .. n-1] that a (>= 0) exceeds
 __device__ __forceinline__ int dyn_count(float a, const float *thr, int n) {
   int lo = 0, hi = n - 1;  // answer in [lo, hi]
@@ -165,11 +182,12 @@ __global__ __launch_bounds__(256) void k_adamw8(Adam8Params a) {
   __shared__ float s_sm[128], s_um[256], s_st[128], s_ut[256];
   __shared__ float s_red[2][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  s_um[tid] = dyn_mag(tid, 8);
-  if (tid < 128) s_sm[tid] = dyn_mag(tid, 7);
-  __syncthreads();
-  if (tid >= 1) s_ut[tid] = below_mid(s_um[tid - 1], s_um[tid]);
-  if (tid >= 1 && tid < 128) s_st[tid] = below_mid(s_sm[tid - 1], s_sm[tid]);
+  s_um[tid] = kDynBooks.um[tid];
+  s_ut[tid] = kDynBooks.ut[tid];
+  if (tid < 128) {
+    s_sm[tid] = kDynBooks.sm[tid];
+    s_st[tid] = kDynBooks.st[tid];
+  }
 
   const int64_t blk = blockIdx.x;
   uint16_t *p = nullptr;
