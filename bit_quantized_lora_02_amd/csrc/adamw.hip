@@ -23,6 +23,7 @@
 // consecutive elements of one tensor, 8 per thread: one 16-byte load of the
 // parameter and of the gradient, two of each binary32 array.
 #include "adamw.h"
+#include "dyn_code.h"
 #include "device.h"
 #include "launch.h"
 
@@ -124,62 +125,19 @@ __global__ __launch_bounds__(256) void k_adamw(AdamParams a) {
 // Other memory-saving levers": paged_adamw_8bit keeps the state in 8 bits.
 // Block-wise state quantization after Dettmers et al., "8-bit Optimizers via
 // Block-wise Quantization" (ICLR 2022): per block of 2048 elements, 8-bit codes
-// and one binary32 absmax for each moment.  The code book is dynamic: in a
-// signed byte (first moment) bit 7 is the sign and, among the other 7 bits, E =
-// the leading zeros, then an indicator bit, then F = 6 - E fraction bits f;
-// the magnitude is fl32((0.1 + 0.9 ((f + 1) / 2^F)) / 10^E) (binary64, in that
-// order) and all-zero bits mean 0.  An unsigned byte (second moment) counts E
-// among 8 bits, F = 7 - E.  Magnitudes grow with the bits' unsigned value, so a
-// code is the number of thresholds below |x| (threshold: the largest binary32
-// value not above the exact midpoint of two neighbours; ties go down).
+// and one binary32 absmax for each moment, in the dynamic code books of
+// dyn_code.h (nearest code, ties to the smaller magnitude).
 // One workgroup owns one block: it decodes the moments (fl32(book * absmax)),
 // runs the binary32 step of k_adamw, reduces the block's new absmax, and
-// encodes x = fl32(value / absmax) by bisection over the thresholds (the books
-// and thresholds are compile-time constants, copied into LDS).
-constexpr float dyn_mag(int p, int bits) {
-  if (p == 0) return 0.f;
-  int top = 0;  // the indicator bit
-  while ((p >> (top + 1)) != 0) ++top;
-  const int E = bits - 1 - top, F = top, f = p - (1 << F);
-  double p10 = 1.0;
-  for (int i = 0; i < E; ++i) p10 *= 10.0;  // exact
-  // each binary64 operation rounded once, in this order
-  return (float)((0.1 + 0.9 * ((double)(f + 1) / (double)(1 << F))) / p10);
-}
-constexpr float below_mid(float lo, float hi) {  // largest binary32 not above (lo + hi) / 2
-  const double mid = ((double)lo + (double)hi) * 0.5;  // exact
-  float t = (float)mid;
-  if ((double)t > mid) t = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, t) - 1u);  // t > 0 here
-  return t;
-}
-// The two books and their thresholds, computed once at compile time (the constant evaluator rounds
-// every binary64 operation to nearest, as the arithmetic above states): magnitudes of the unsigned
-// (um) and signed (sm) codes, and thr[i] = below_mid(mag[i-1], mag[i]) (entry 0 unused).
-struct DynBooks {
-  float um[256], sm[128], ut[256], st[128];
-};
-constexpr DynBooks make_dyn_books() {
-  DynBooks b{};
-  for (int i = 0; i < 256; ++i) b.um[i] = dyn_mag(i, 8);
-  for (int i = 0; i < 128; ++i) b.sm[i] = dyn_mag(i, 7);
-  for (int i = 1; i < 256; ++i) b.ut[i] = below_mid(b.um[i - 1], b.um[i]);
-  for (int i = 1; i < 128; ++i) b.st[i] = below_mid(b.sm[i - 1], b.sm[i]);
-  return b;
-}
-__constant__ const DynBooks kDynBooks = make_dyn_books();
-// number of thresholds thr[1 .. n-1] that a (>= 0) exceeds
-__device__ __forceinline__ int dyn_count(float a, const float *thr, int n) {
-  int lo = 0, hi = n - 1;  // answer in [lo, hi]
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a > thr[mid]) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
+// encodes x = fl32(value / absmax) through the bucket index: one table read
+// and one or two threshold comparisons per code (the books, thresholds and
+// index are compile-time constants, copied into LDS).
+__constant__ const DynBooks kDynBooks = kBooks;
+__constant__ const DynIndex kDynIndex = kIndex;
 
 __global__ __launch_bounds__(256) void k_adamw8(Adam8Params a) {
-  __shared__ float s_sm[128], s_um[256], s_st[128], s_ut[256];
+  __shared__ float s_sm[128], s_um[256], s_st[128 + kCmpS], s_ut[256 + kCmpU];
+  __shared__ uint32_t s_ixu[kIxWordsU], s_ixs[kIxWordsS];
   __shared__ float s_red[2][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   s_um[tid] = kDynBooks.um[tid];
@@ -188,6 +146,10 @@ __global__ __launch_bounds__(256) void k_adamw8(Adam8Params a) {
     s_sm[tid] = kDynBooks.sm[tid];
     s_st[tid] = kDynBooks.st[tid];
   }
+  if (tid < kCmpU) s_ut[256 + tid] = kDynBooks.ut[256 + tid];
+  if (tid < kCmpS) s_st[128 + tid] = kDynBooks.st[128 + tid];
+  for (int i = tid; i < kIxWordsU; i += 256) s_ixu[i] = kDynIndex.u[i];
+  for (int i = tid; i < kIxWordsS; i += 256) s_ixs[i] = kDynIndex.s[i];
 
   const int64_t blk = blockIdx.x;
   uint16_t *p = nullptr;
@@ -206,7 +168,7 @@ __global__ __launch_bounds__(256) void k_adamw8(Adam8Params a) {
   const int64_t e0 = lb * kAdam8Block + (int64_t)tid * 8;
   const int cnt = (int)((n - e0) < 0 ? 0 : ((n - e0) > 8 ? 8 : (n - e0)));
   const float m_abs = ma[lb], v_abs = va[lb];
-  __syncthreads();  // thresholds visible
+  __syncthreads();  // books, thresholds and index visible
 
   float m[8], v[8], th[8];
   uint32_t mc[2] = {0u, 0u}, vc[2] = {0u, 0u};
@@ -267,10 +229,11 @@ __global__ __launch_bounds__(256) void k_adamw8(Adam8Params a) {
     uint32_t cm = 0u, cv = 0u;
     if (mx > 0.f) {
       const float x = __fdiv_rn(m[e], mx);
-      cm = (uint32_t)dyn_count(fabsf(x), s_st, 128);
+      cm = dyn_code<kCmpS>(fabsf(x), reinterpret_cast<const uint8_t *>(s_ixs), kIxBaseS, kIxLastS, s_st);
       if (x < 0.f && cm) cm |= 128u;
     }
-    if (vx > 0.f) cv = (uint32_t)dyn_count(__fdiv_rn(v[e], vx), s_ut, 256);
+    if (vx > 0.f)
+      cv = dyn_code<kCmpU>(__fdiv_rn(v[e], vx), reinterpret_cast<const uint8_t *>(s_ixu), kIxBaseU, kIxLastU, s_ut);
     om[e >> 2] |= cm << (8 * (e & 3));
     ov[e >> 2] |= cv << (8 * (e & 3));
   }
