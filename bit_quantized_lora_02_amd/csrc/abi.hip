@@ -249,7 +249,7 @@ Plan make_plan(int op, int64_t T, int64_t N, int64_t K, int32_t r) {
     if (op == QLORA_OP_FWD && use_gemv(T, K) && nf4_gemv_rows_ok(T, K)) {  // one or two tokens
       p.gemv = p.gemv_rows = true;
       p.gemv_split = gemv_rows_usplit(K);
-      part = up((size_t)4 * T * N * 4, kAlign);  // up to four row segments
+      part = up((size_t)nf4_gemv_rows_nseg(T, K) * T * N * 4, kAlign);  // one partial per row segment
       p.off_upart = part;
       part += (size_t)4 * p.gemv_split * T * r * 4;
     } else if ((op == QLORA_OP_FWD || op == QLORA_OP_FWD_MULTI) && use_gemv(T, K)) {  // dropout: the tiled path

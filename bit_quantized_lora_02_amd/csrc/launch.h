@@ -83,9 +83,10 @@ hipError_t launch_nf4_gemv(const bf16_t *X, int64_t T, int64_t K, const uint8_t 
 hipError_t launch_gemv_finish(const float *part, const float *upart, int nsplit, int64_t T, int64_t N,
                               const bf16_t *B, int64_t r, float s, bf16_t *Y, bf16_t *U_out, hipStream_t st,
                               int nsplit_u = 0);
-// Row-streaming GEMV for one or two tokens (K % 2048 == 0, T K <= 32768): binary32
-// partials of nseg row segments (part [nseg][T][N], nseg <= 4, returned in *nseg_out) plus the U partials
-// of nsplit_u K ranges (upart [4 nsplit_u][T][r]).
+// Row-streaming GEMV for one or two tokens (K % 2048 == 0, at most 16 row segments): binary32
+// partials of nseg row segments (part [nseg][T][N], nseg = nf4_gemv_rows_nseg(T, K), also returned in
+// *nseg_out) plus the U partials of nsplit_u K ranges (upart [4 nsplit_u][T][r]).
+int nf4_gemv_rows_nseg(int64_t T, int64_t K);  // 0: the kernel does not take (T, K)
 bool nf4_gemv_rows_ok(int64_t T, int64_t K);
 hipError_t launch_nf4_gemv_rows(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
                                 const float *step, int64_t N, int nsplit_u, const bf16_t *A, int64_t r, float *part,

@@ -286,109 +286,96 @@ __global__ __launch_bounds__(256) void k_nf4_gemv(const bf16_t *__restrict__ X, 
 // ------------------------------------------------ the row-streaming GEMV
 // For one or two tokens the MFMA formulation wastes most of each 16-token operand
 // and its 16-row loads touch 16 weight rows per instruction.  Here a wave owns
-// weight rows instead: one 16-byte load per lane covers 2048 consecutive
-// weights of one row (1 KB contiguous per wave instruction, like a plain
-// stream); the tokens' activations sit in LDS for the whole launch; a lane
-// decodes its 32 weights byte by byte through the level-pair table into bf16
-// pairs fl32(level * c') and accumulates v_dot2_f32_bf16 with the matching
-// activation pairs; at the end of its piece of a row a wave reduction gives
-// the binary32 partial sum of that piece.
+// weight rows instead.  A work item is one segment of Ks = 2048 CH columns of
+// one row (nseg = K / Ks segments per row); lane l covers columns
+// 2048 c + 32 l .. 2048 c + 32 l + 31 of chunk c of the segment, so one
+// 16-byte load per lane and chunk streams 1 KB of one row per wave
+// instruction, like a plain copy.  Since a workgroup keeps one segment for the
+// whole launch, every lane keeps its TT CH 32 activations in registers (loaded
+// once; no LDS traffic for them).  Per item a lane decodes its 32 CH weights
+// byte by byte through the level-pair table into bf16 pairs fl32(level * c')
+// and accumulates v_dot2_f32_bf16 with the matching activation pairs; a wave
+// reduction then gives the binary32 partial sum of that segment.
 //
-// Work items: each row is cut into nseg equal segments of Ks = K / nseg columns
-// (nseg = 1, 2 or 4, chosen by the host to even out the items per wave).  Main
-// workgroup g owns segment g % nseg, and its wave w the rows
-// 4 (g / nseg) + w + i 4 gmain / nseg (gmain % nseg == 0); a wave streams all its
-// items as one sequence of steps (CH chunks of 2048 columns each), loading one
-// step ahead in two fixed register slots, the first load issued before the
-// workgroup stages the activations of its segment (TT Ks bf16 in LDS).  part
-// is [nseg][T][N] binary32.  Workgroups 0 .. nsplit_u - 1 come first and form
-// the U partials of K range u as in k_nf4_gemv ([4 nsplit_u][T][r]).
-// K % (2048 CH nseg) == 0 and TT Ks <= 32768; tokens T .. TT-1 are zero.
+// Main workgroup g owns segment g % nseg, and its wave w the rows
+// 4 (g / nseg) + w + i 4 gmain / nseg (gmain % nseg == 0).  A wave loads the
+// next item while it computes the current one, in two fixed register slots
+// (the loop runs two items per iteration, so no slot is ever copied: a copy of
+// a register whose load is in flight would make the wave wait for it).  The
+// wave index is made wave-uniform, so the item bookkeeping and addresses stay
+// in scalar registers.  The block constants of an item: lane l's block in
+// chunk c is block 32 c + (l >> 1) of the segment; it is read as the aligned
+// 4-byte word holding its byte (absmax_q is 16-byte aligned), and the item's
+// 32 CH blocks share one binary32 step (32 CH divides 256 and the item's
+// first block is a multiple of 32 CH).  part is [nseg][T][N] binary32.
+// Workgroups 0 .. nsplit_u - 1 come first and form the U partials of K range
+// u as in k_nf4_gemv ([4 nsplit_u][T][r]).  Tokens T .. TT-1 are zero.
 template <int TT, int CH>
-__global__ __launch_bounds__(256, TT == 1 ? 6 : 4) void k_nf4_gemv_rows(
+__global__ __launch_bounds__(256, TT == 1 ? 8 : 6) void k_nf4_gemv_rows(
     const bf16_t *__restrict__ X, int64_t T, int64_t K, const uint8_t *__restrict__ codes,
     const uint8_t *__restrict__ absmax_q, const float *__restrict__ step, int64_t N, int gmain, int nseg, int nsplit_u,
     const bf16_t *__restrict__ A, int64_t r, float *__restrict__ part, float *__restrict__ upart, Levels lv) {
-  extern __shared__ __attribute__((aligned(16))) bf16_t sx[];  // [TT][Ks], sized at launch
   __shared__ __attribute__((aligned(16))) float2 s_tab[256];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if ((int)blockIdx.x < nsplit_u) {
     const int64_t u = blockIdx.x, kchunk = K / nsplit_u, kb = u * kchunk;
     lora_u_partial<1>(X, T, K, A, r, kb, kb + kchunk, upart + (u * 4 + wave) * T * r, wave, lane);
     return;
   }
+  constexpr int Ks = 2048 * CH;
   const int g = (int)blockIdx.x - nsplit_u, seg = g % nseg;
-  const int64_t Ks = K / nseg;
   const int64_t row0 = (int64_t)(g / nseg) * 4 + wave, rstride = (int64_t)(gmain / nseg) * 4;
-  const int sps = (int)(K / 2048) / (CH * nseg);             // steps per item
   const int64_t items = row0 < N ? (N - row0 + rstride - 1) / rstride : 0;
-  const int64_t total = items * sps;
-  const int jseg = seg * sps * CH;  // first 2048-column chunk of this workgroup's segment
 
   struct Slot {
-    u32x4_t c[CH];
-    RawScale sc[CH];
+    u32x4_t c[CH];   // the lane's 16 code bytes of each chunk
+    uint32_t q[CH];  // the aligned word holding the lane's block byte of each chunk
+    float d;         // the item's binary32 step
   };
-  // load stream: step lg of the current item; the lane's 16 code bytes of chunk j of the row sit
-  // at lrow + 1024 j and their block constant at lblk + 32 j.  The stream stops advancing at the
-  // last step, so the prefetches past the end reload that step (never used).
-  int64_t li = 0;
-  int lg = 0;
-  const uint8_t *lrow = codes + row0 * (K / 2) + 16 * lane;
-  int64_t lblk = row0 * (K / 64) + (lane >> 1);
-  const int64_t row_bytes = rstride * (K / 2), row_blocks = rstride * (K / 64);
+  const int lofs = 16 * lane, bofs = (lane >> 1) & ~3, bsh = 8 * ((lane >> 1) & 3);
+  int64_t li = 0;  // item of the load stream; it stops at the last item (later prefetches reload it, unused)
   auto load_slot = [&](Slot &sl) {
+    const int64_t row = row0 + li * rstride;
+    const uint8_t *cr = codes + row * (K / 2) + seg * (Ks / 2);
+    const int64_t b0 = row * (K / 64) + seg * (Ks / 64);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int j = jseg + lg * CH + c;
-      sl.c[c] = *reinterpret_cast<const u32x4_t *>(lrow + 1024 * j);
-      const int64_t b = lblk + 32 * j;
-      sl.sc[c] = RawScale{(uint32_t)absmax_q[b], step[b >> 8]};
+      sl.c[c] = *reinterpret_cast<const u32x4_t *>(cr + 1024 * c + lofs);
+      sl.q[c] = *reinterpret_cast<const uint32_t *>(absmax_q + b0 + 32 * c + bofs);
     }
-    if (++li < total && ++lg == sps) {
-      lg = 0;
-      lrow += row_bytes;
-      lblk += row_blocks;
-    }
+    sl.d = step[b0 >> 8];
+    if (li + 1 < items) ++li;
   };
   Slot s0, s1;
-  if (total > 0) load_slot(s0);  // in flight while the activations are staged
+  if (items > 0) load_slot(s0);  // in flight while the activations and the table are loaded
 
   pair_levels_to_lds(lv, s_tab, tid);
-  // activations of the TT tokens (T..TT-1: zero); 16-byte unit u of a token's row is stored at
-  // unit u ^ ((u >> 4) & 3), so that the 16 lanes of one pass of a 16-byte read (lane l reads
-  // unit 4 l + q) fall in 16 distinct bank groups
-  const bf16_t *xs = X + seg * Ks;
-  for (int64_t i = (int64_t)tid * 8; i < TT * Ks; i += 256 * 8) {
-    const int64_t t = i / Ks, k = i - t * Ks, u = k >> 3;
-    *reinterpret_cast<u32x4_t *>(sx + t * Ks + 8 * (u ^ ((u >> 4) & 3))) =
-        t < T ? *reinterpret_cast<const u32x4_t *>(xs + t * K + k) : u32x4_t{0u, 0u, 0u, 0u};
-  }
+  uint32_t xr[TT][CH][16];
+#pragma unroll
+  for (int t = 0; t < TT; ++t)
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const u32x4_t v = t < T ? *reinterpret_cast<const u32x4_t *>(X + t * K + seg * Ks + 2048 * c + 32 * lane + 8 * h)
+                                : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xr[t][c][4 * h + e] = v[e];
+      }
   __syncthreads();
-  if (total <= 0) return;
+  if (items <= 0) return;
 
-  // this lane's 16-byte activation units of chunk 0 (unit 4 lane + q, swizzled as staged)
-  const int xsw = (lane >> 2) & 3;
-  const bf16_t *xq[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) xq[q] = sx + 8 * (4 * lane + (q ^ xsw));
-  float acc[TT];
-#pragma unroll
-  for (int t = 0; t < TT; ++t) acc[t] = 0.f;
   float *pseg = part + (int64_t)seg * T * N;
-  int64_t cn = row0;  // compute stream: step cg of the item on row cn
-  int cg = 0;
+  int64_t cn = row0;  // row of the item being computed
   auto do_step = [&](Slot &cur, Slot &refill) {
     load_slot(refill);
+    float acc[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) acc[t] = 0.f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int j = jseg + cg * CH + c;
-      const float cq = scale_of(cur.sc[c]);
-      u32x4_t xv[TT][4];
-#pragma unroll
-      for (int t = 0; t < TT; ++t)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) xv[t][q] = *reinterpret_cast<const u32x4_t *>(xq[q] + t * Ks + 2048 * (j - jseg));
+      const float cq = __fmul_rn((float)__builtin_amdgcn_ubfe(cur.q[c], bsh, 8), cur.d);
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd) {
         const uint32_t w = cur.c[c][wd];
@@ -397,30 +384,25 @@ __global__ __launch_bounds__(256, TT == 1 ? 6 : 4) void k_nf4_gemv_rows(
           const float2 l = s_tab[(w >> (8 * b)) & 0xffu];
           const bf16x2_t wp = __builtin_bit_cast(bf16x2_t, pack_bf16x2(__fmul_rn(l.x, cq), __fmul_rn(l.y, cq)));
 #pragma unroll
-          for (int t = 0; t < TT; ++t) {
-            // copied to a scalar first: this compiler lowers a bit_cast of a vector-element
-            // lvalue as a read of element 0
-            const uint32_t xw = xv[t][wd][b];
-            acc[t] = __builtin_amdgcn_fdot2_f32_bf16(wp, __builtin_bit_cast(bf16x2_t, xw), acc[t], false);
-          }
+          for (int t = 0; t < TT; ++t)
+            acc[t] = __builtin_amdgcn_fdot2_f32_bf16(wp, __builtin_bit_cast(bf16x2_t, xr[t][c][4 * wd + b]), acc[t],
+                                                     false);
         }
       }
     }
-    if (++cg == sps) {  // item done: reduce over the wave, lane 63 writes the partial
 #pragma unroll
-      for (int t = 0; t < TT; ++t) {
-        const float v = wave_sum_lane63(acc[t]);
-        if (lane == 63 && t < T) pseg[t * N + cn] = v;
-        acc[t] = 0.f;
-      }
-      cg = 0;
-      cn += rstride;
+    for (int t = 0; t < TT; ++t) {  // reduce over the wave, lane 63 writes the partial
+      const float v = wave_sum_lane63(acc[t]);
+      if (lane == 63 && t < T) pseg[t * N + cn] = v;
     }
+    cn += rstride;
   };
-  for (int64_t f = 0; f < total; f += 2) {
+  int64_t f = 0;
+  for (; f + 1 < items; f += 2) {
     do_step(s0, s1);
-    if (f + 1 < total) do_step(s1, s0);
+    do_step(s1, s0);
   }
+  if (f < items) do_step(s0, s1);
 }
 
 // Sums of the finishing kernels, in index order with every load issued first (a loop bound known only
@@ -678,57 +660,30 @@ hipError_t launch_gemv_finish(const float *part, const float *upart, int nsplit,
   return hipGetLastError();
 }
 
-// one or two tokens (the activations of that many take TT K bf16 of LDS, at most 64 KB); from
-// three tokens on the MFMA GEMV is faster
+// one or two tokens (from three on the MFMA GEMV is faster); two 2048-column chunks per item for one
+// token when K allows, one for two tokens (their activations take 32 TT CH registers)
 static int rows_tt(int64_t T) { return T <= 1 ? 1 : 2; }
-bool nf4_gemv_rows_ok(int64_t T, int64_t K) { return T >= 1 && T <= 2 && K % 2048 == 0 && rows_tt(T) * K <= 32768; }
+static int rows_ch(int64_t T, int64_t K) { return rows_tt(T) == 1 && K % 4096 == 0 ? 2 : 1; }
+int nf4_gemv_rows_nseg(int64_t T, int64_t K) {
+  if (T < 1 || T > 2 || K <= 0 || K % 2048 != 0) return 0;
+  const int64_t ns = K / (2048 * rows_ch(T, K));
+  return ns <= kFinishMaxSplit ? (int)ns : 0;
+}
+bool nf4_gemv_rows_ok(int64_t T, int64_t K) { return nf4_gemv_rows_nseg(T, K) > 0; }
 
-// Workgroups of one variant resident on the device at once with `shm` bytes of dynamic LDS
-// (a few LDS sizes cached per variant).
+// Workgroups of one variant resident on the device at once (computed once per variant and thread).
 template <int TT, int CH>
-static int rows_resident(uint32_t shm) {
-  static thread_local uint32_t c_shm[4] = {0, 0, 0, 0};
-  static thread_local int c_res[4] = {0, 0, 0, 0};
-  for (int i = 0; i < 4; ++i)
-    if (c_res[i] > 0 && c_shm[i] == shm) return c_res[i];
+static int rows_resident() {
+  static thread_local int res = 0;
+  if (res > 0) return res;
   int dev = 0, cus = 0, nb = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_nf4_gemv_rows<TT, CH>, 256, shm) != hipSuccess || nb < 1 ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_nf4_gemv_rows<TT, CH>, 256, 0) != hipSuccess || nb < 1 ||
       cus < 1)
     return 0;
-  for (int i = 3; i > 0; --i) {
-    c_shm[i] = c_shm[i - 1];
-    c_res[i] = c_res[i - 1];
-  }
-  c_shm[0] = shm;
-  c_res[0] = nb * cus;
-  return c_res[0];
-}
-
-// Work split of the row-streaming GEMV: the number of row segments (1, 2 or 4, dividing the
-// steps of a row) whose longest wave has the fewest steps (ties: fewer segments), and the
-// main-grid workgroups (a multiple of the segments), at most what stays resident next to the
-// U workgroups with that segment's share of the activations in LDS.
-template <int TT, int CH>
-static bool rows_split(int64_t N, int64_t K, int nsplit_u, int *gmain, int *nseg) {
-  const int spr = (int)(K / 2048) / CH;
-  int64_t best = -1;
-  for (int sg = 1; sg <= 4; sg *= 2) {
-    if (spr % sg) continue;
-    const int res = rows_resident<TT, CH>((uint32_t)(TT * (K / sg) * 2));
-    if (res <= 0) return false;
-    int64_t g = std::min<int64_t>(std::max(1, res - nsplit_u), (N * sg + 3) / 4);
-    g = std::max<int64_t>(sg, g / sg * sg);
-    const int64_t nw = 4 * g;
-    const int64_t cost = ((N * sg + nw - 1) / nw) * (spr / sg);
-    if (best < 0 || cost < best) {
-      best = cost;
-      *gmain = (int)g;
-      *nseg = sg;
-    }
-  }
-  return best >= 0;
+  res = nb * cus;
+  return res;
 }
 
 hipError_t launch_nf4_gemv_rows(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
@@ -736,21 +691,21 @@ hipError_t launch_nf4_gemv_rows(const bf16_t *X, int64_t T, int64_t K, const uin
                                 float *upart, const Levels &lv, hipStream_t s, int *nseg_out) {
   *nseg_out = 1;
   if (T == 0) return hipSuccess;
-  const int64_t nch = K / 2048;
-  const int ch = nch % 2 == 0 ? 2 : 1;  // two chunks per step (four cost occupancy)
-  const int tt = rows_tt(T);
-  int gmain = 1, nseg = 1;
-  bool ok;
-  if (tt == 1) ok = ch == 2 ? rows_split<1, 2>(N, K, nsplit_u, &gmain, &nseg) : rows_split<1, 1>(N, K, nsplit_u, &gmain, &nseg);
-  else ok = ch == 2 ? rows_split<2, 2>(N, K, nsplit_u, &gmain, &nseg) : rows_split<2, 1>(N, K, nsplit_u, &gmain, &nseg);
-  if (!ok) return hipErrorInvalidDeviceFunction;
+  const int nseg = nf4_gemv_rows_nseg(T, K);
+  if (nseg <= 0) return hipErrorInvalidValue;
+  const int tt = rows_tt(T), ch = rows_ch(T, K);
+  const int res = tt == 1 ? (ch == 2 ? rows_resident<1, 2>() : rows_resident<1, 1>()) : rows_resident<2, 1>();
+  if (res <= 0) return hipErrorInvalidDeviceFunction;
+  // main workgroups: what stays resident beside the U workgroups, at most one item per wave, a multiple of nseg
+  int64_t g = std::min<int64_t>(std::max(1, res - nsplit_u), (N * nseg + 3) / 4);
+  g = std::max<int64_t>(nseg, g / nseg * nseg);
+  const int gmain = (int)g;
   const dim3 grid((unsigned)(gmain + nsplit_u));
-  const uint32_t shm = (uint32_t)(tt * (K / nseg) * 2);
-#define QLORA_ROWS(TT, CH_)                                                                                   \
-  launch(k_nf4_gemv_rows<TT, CH_>, grid, dim3(256), shm, s, X, T, K, codes, absmax_q, step, N, gmain, nseg, \
-         nsplit_u, A, r, part, upart, lv)
+#define QLORA_ROWS(TT, CH_) \
+  launch(k_nf4_gemv_rows<TT, CH_>, grid, dim3(256), 0, s, X, T, K, codes, absmax_q, step, N, gmain, nseg, nsplit_u, \
+         A, r, part, upart, lv)
   if (tt == 1) { if (ch == 2) QLORA_ROWS(1, 2); else QLORA_ROWS(1, 1); }
-  else { if (ch == 2) QLORA_ROWS(2, 2); else QLORA_ROWS(2, 1); }
+  else QLORA_ROWS(2, 1);
 #undef QLORA_ROWS
   *nseg_out = nseg;
   return hipGetLastError();

@@ -329,10 +329,12 @@ def test_small_token_forward(n_out, T):
 @pytest.mark.parametrize("n_out,n_in,T,r", [(72, 2048, 1, 16), (1032, 4096, 2, 5), (520, 8192, 1, 32),
                                             (264, 16384, 2, 64), (8, 2048, 2, 8), (4104, 6144, 1, 12),
                                             (2056, 4096, 2, 24), (6152, 8192, 1, 16), (520, 8192, 3, 16),
-                                            (8, 2048, 4, 8), (8, 2048, 1, 1), (16, 4096, 2, 3)])
+                                            (8, 2048, 4, 8), (8, 2048, 1, 1), (16, 4096, 2, 3),
+                                            (8, 65536, 1, 8), (24, 32768, 2, 4), (8, 34816, 1, 8)])
 def test_row_streaming_forward(n_out, n_in, T, r):
     """Few tokens with n_in % 2048 == 0: the row-streaming kernel (1-2 tokens, one wave per weight row, rows cut
-    into 1, 2 or 4 segments) and the MFMA kernel (3-4 tokens), checked in full."""
+    into segments of 4096 or 2048 columns, up to 16 of them: n_in 65536 with one token, 32768 with two) and the
+    MFMA kernel (3-4 tokens, or 17 segments: n_in 34816), checked in full."""
     print(f"row-streaming forward {n_out}x{n_in} T={T} r={r}", flush=True)
     inp = linear_inputs(n_out, n_in, T, r, 2.0 * r, seed=n_out + T, sigma_ab=0.05)
     w = Bd.quantize_nf4(torch.from_numpy(inp.W).to(dev()))
