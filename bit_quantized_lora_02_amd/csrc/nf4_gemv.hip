@@ -384,9 +384,10 @@ __global__ __launch_bounds__(256, TT == 1 ? 8 : 6) void k_nf4_gemv_rows(
           const float2 l = s_tab[(w >> (8 * b)) & 0xffu];
           const bf16x2_t wp = __builtin_bit_cast(bf16x2_t, pack_bf16x2(__fmul_rn(l.x, cq), __fmul_rn(l.y, cq)));
 #pragma unroll
-          for (int t = 0; t < TT; ++t)
-            acc[t] = __builtin_amdgcn_fdot2_f32_bf16(wp, __builtin_bit_cast(bf16x2_t, xr[t][c][4 * wd + b]), acc[t],
-                                                     false);
+          for (int t = 0; t < TT; ++t) {
+            const uint32_t xw = xr[t][c][4 * wd + b];
+            acc[t] = __builtin_amdgcn_fdot2_f32_bf16(wp, __builtin_bit_cast(bf16x2_t, xw), acc[t], false);
+          }
         }
       }
     }
