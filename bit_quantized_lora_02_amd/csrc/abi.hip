@@ -430,13 +430,18 @@ int linear_fwd(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const qlora_b
     LAUNCH("gemv_finish", launch_gemv_finish(part, upart, p.gemv_split, T, N, B, r, sc, Y, U_out, s));
     return QLORA_OK;
   }
-  if (drop)  // U = Xd A^T, drawing the keep bits of X on the way
+  if (drop) {  // U = Xd A^T, drawing the keep bits of X on the way
     LAUNCH("lora_u_dropout", launch_skinny(false, false, p.rn, X, K, T, A, K, r, K, p.su.kchunk, p.su.n, part, s,
                                            DROP_GENERATE, *drop));
-  else
+  } else if (lora_rows_ok(p.rn, T)) {  // many rows, narrow rank: the whole reduction per workgroup
+    LAUNCH("lora_u", launch_lora_rows(false, p.rn, X, K, T, A, K, r, K, U_out, r, U_out ? r : 0, 1.0f, V, p.rp, p.rp,
+                                      r, sc, s));
+  } else {
     LAUNCH("lora_u", launch_skinny(false, false, p.rn, X, K, T, A, K, r, K, p.su.kchunk, p.su.n, part, s));
-  LAUNCH("lora_u_finalize",
-         launch_finalize(part, p.su.n, T, p.rn, U_out, r, U_out ? r : 0, 1.0f, V, p.rp, p.rp, r, sc, s));
+  }
+  if (drop || !lora_rows_ok(p.rn, T))
+    LAUNCH("lora_u_finalize",
+           launch_finalize(part, p.su.n, T, p.rn, U_out, r, U_out ? r : 0, 1.0f, V, p.rp, p.rp, r, sc, s));
   // B is read in place when its rows are 16-byte multiples, else from a zero-padded copy
   const bool b_direct = (r % 8) == 0;
   if (!b_direct) LAUNCH("pad_b", launch_pad_copy(B, r, r, N, Bp, p.rp, s));
@@ -491,21 +496,31 @@ int linear_bwd(const qlora_bf16 *X, const qlora_bf16 *dY, int64_t T, const qlora
     ldu = p.rp;
     rvu = p.rv;
   } else if (!U) {
-    if (drop)
+    if (drop) {
       LAUNCH("lora_u_dropout", launch_skinny(false, false, p.rn, X, K, T, A, K, r, K, p.su.kchunk, p.su.n, part, s,
                                              DROP_APPLY, *drop));
-    else
+    } else if (lora_rows_ok(p.rn, T)) {
+      LAUNCH("lora_u", launch_lora_rows(false, p.rn, X, K, T, A, K, r, K, nullptr, 0, 0, 0.f, Up, p.rp, p.rp, r, 1.0f,
+                                        s));
+    } else {
       LAUNCH("lora_u", launch_skinny(false, false, p.rn, X, K, T, A, K, r, K, p.su.kchunk, p.su.n, part, s));
-    LAUNCH("lora_u_finalize",
-           launch_finalize(part, p.su.n, T, p.rn, nullptr, 0, 0, 0.f, Up, p.rp, p.rp, r, 1.0f, s));
+    }
+    if (drop || !lora_rows_ok(p.rn, T))
+      LAUNCH("lora_u_finalize",
+             launch_finalize(part, p.su.n, T, p.rn, nullptr, 0, 0, 0.f, Up, p.rp, p.rp, r, 1.0f, s));
     Usrc = Up;
     ldu = p.rp;
     rvu = p.rv;
   }
   // dU = s dY B  -> dUp [T, rp]
-  LAUNCH("lora_du", launch_skinny(false, true, p.rn, dY, N, T, Bsrc, ldb, rvb, N, p.sdu.kchunk, p.sdu.n, part, s));
-  LAUNCH("lora_du_finalize",
-         launch_finalize(part, p.sdu.n, T, p.rn, nullptr, 0, 0, 0.f, dUp, p.rp, p.rp, r, sc, s));
+  if (lora_rows_ok(p.rn, T)) {
+    LAUNCH("lora_du", launch_lora_rows(true, p.rn, dY, N, T, Bsrc, ldb, rvb, N, nullptr, 0, 0, 0.f, dUp, p.rp, p.rp, r,
+                                       sc, s));
+  } else {
+    LAUNCH("lora_du", launch_skinny(false, true, p.rn, dY, N, T, Bsrc, ldb, rvb, N, p.sdu.kchunk, p.sdu.n, part, s));
+    LAUNCH("lora_du_finalize",
+           launch_finalize(part, p.sdu.n, T, p.rn, nullptr, 0, 0, 0.f, dUp, p.rp, p.rp, r, sc, s));
+  }
   // dB = s dY^T U  -> [N, r]
   LAUNCH("lora_db", launch_skinny(true, true, p.rn, dY, N, N, Usrc, ldu, rvu, T, p.sdb.kchunk, p.sdb.n, part, s));
   // dA^T = X^T dU  -> [K, r], stored transposed as dA [r, K]

@@ -130,6 +130,12 @@ hipError_t launch_finalize_pair(const float *part_a, int nsplit_a, int64_t M_a, 
                                 int64_t ld_a, int64_t n_a, float scale_a, bool trans_a, const float *part_b,
                                 int nsplit_b, int64_t M_b, int64_t N_b, bf16_t *out_b, int64_t ld_b, int64_t n_b,
                                 float scale_b, bool trans_b, hipStream_t s);
+// The same contraction (pt = 0) with the whole reduction in each workgroup, writing the finalize
+// outputs directly (no partial sums, no second launch); lora_rows_ok(rn, M) says where it is used.
+bool lora_rows_ok(int rn, int64_t M);
+hipError_t launch_lora_rows(bool qt, int rn, const bf16_t *P, int64_t ldp, int64_t M, const bf16_t *Q, int64_t ldq,
+                            int64_t Rv, int64_t Kred, bf16_t *out1, int64_t ld1, int64_t n1, float scale1,
+                            bf16_t *out2, int64_t ld2, int64_t n2, int64_t nvalid2, float scale2, hipStream_t s);
 hipError_t launch_pad_copy(const bf16_t *in, int64_t ldi, int64_t ncols, int64_t M, bf16_t *out, int64_t ldo,
                            hipStream_t s);
 

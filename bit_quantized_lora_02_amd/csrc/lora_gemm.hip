@@ -280,6 +280,109 @@ __global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, in
       }
 }
 
+// ------------------------------------------------- whole-reduction variant
+// With many rows and 16 rank columns the split reduction above spends most of
+// its time in the second launch.  Here one 1024-thread workgroup owns ROWS = 8
+// or 16 rows of M (8 while that still gives no more workgroups than CUs: each
+// workgroup reads all of Q, so fewer rows only pay when they bring more CUs
+// into play) and the whole reduction: its 16 waves take consecutive reduction ranges
+// of kw columns (kw = Kred / 16 rounded up to 32), load their operands straight
+// from global memory in the MFMA layout (lane (a, g) = (l & 15, l >> 4) holds
+// row a, columns 8 g .. 8 g + 7 of a 32-deep step; with ROWS = 8 the lanes of
+// rows 8..15 load nothing and their MFMA rows are discarded: P needs PT = 0; Q with
+// QT = 0 likewise; with QT = 1 a wave copies its 32 x RN slice of Q into its own
+// LDS slot and reads it back transposed), eight steps at a time, and run
+// v_mfma_f32_16x16x32_bf16.  The 16 waves' binary32 results are then added in
+// wave order through LDS, and the workgroup writes the finalize outputs
+// itself: out1[m ld1 + n] = bf16(scale1 S) for n < n1, out2[m ld2 + n] =
+// n < nvalid2 ? bf16(scale2 S) : 0 for n < n2 (S = 0 for n >= RN).  Same
+// requirements as k_skinny (Kred, ldp, ldq and, for QT = 1, Rv multiples of 8).
+constexpr int kRowsRN = 16, kRowsMinM = 1024;  // where it is faster (measured: 16 rank columns, >= 1024 rows)
+template <bool QT, int RN, int ROWS>
+__global__ __launch_bounds__(1024) void k_lora_rows(const bf16_t *__restrict__ P, int64_t ldp, int64_t M,
+                                                    const bf16_t *__restrict__ Q, int64_t ldq, int64_t Rv, int64_t Kred,
+                                                    bf16_t *__restrict__ out1, int64_t ld1, int64_t n1, float scale1,
+                                                    bf16_t *__restrict__ out2, int64_t ld2, int64_t n2, int64_t nvalid2,
+                                                    float scale2) {
+  constexpr int NWV = 16, NT_ = RN / 16, D = 8;
+  constexpr int LDQ = RN + (RN >= 32 ? 16 : 0);
+  constexpr int QCH = QT ? RN / 16 : NT_;  // per lane and step: 16-byte chunks of the Q slice (QT) or operands
+  __shared__ __attribute__((aligned(16))) float sRed[NWV][16][RN];
+  __shared__ __attribute__((aligned(16))) bf16_t sQ[QT ? NWV : 1][QT ? 32 * LDQ : 8];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, a = lane & 15;
+  const int64_t m0 = (int64_t)blockIdx.x * ROWS;
+  const int64_t kw = ((Kred + NWV - 1) / NWV + 31) / 32 * 32;
+  const int64_t kb = wave * kw, ke = (kb + kw < Kred) ? kb + kw : Kred;
+  const int nst = ke > kb ? (int)((ke - kb + 31) / 32) : 0;
+  f32x4s_t acc[NT_];
+#pragma unroll
+  for (int j = 0; j < NT_; ++j) acc[j] = f32x4s_t{0.f, 0.f, 0.f, 0.f};
+  const bool prow = a < ROWS && m0 + a < M;
+  const bf16_t *pp = P + (prow ? m0 + a : 0) * ldp + 8 * g;
+  for (int s0 = 0; s0 < nst; s0 += D) {
+    u32x4_t pa[D], qr[D][QCH];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {  // every load of the D steps first (columns past ke read as zero)
+      const int64_t k0 = kb + (int64_t)(s0 + d) * 32;
+      pa[d] = (prow && k0 + 8 * g < ke) ? *reinterpret_cast<const u32x4_t *>(pp + k0) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < QCH; ++i) {
+        bool ok;
+        const bf16_t *src;
+        if constexpr (QT) {
+          const int c = lane + 64 * i, row = c / (RN / 8), col = (c % (RN / 8)) * 8;
+          ok = k0 + row < ke && col < Rv;
+          src = Q + (k0 + row) * ldq + col;
+        } else {
+          const int64_t col = i * 16 + a;
+          ok = col < Rv && k0 + 8 * g < ke;
+          src = Q + col * ldq + k0 + 8 * g;
+        }
+        qr[d][i] = ok ? *reinterpret_cast<const u32x4_t *>(src) : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      u32x4_t qb[NT_];
+      if constexpr (QT) {
+        bf16_t *sq = sQ[QT ? wave : 0];  // this wave's slot: written and read by this wave only
+#pragma unroll
+        for (int i = 0; i < QCH; ++i) {
+          const int c = lane + 64 * i, row = c / (RN / 8), col = (c % (RN / 8)) * 8;
+          *reinterpret_cast<u32x4_t *>(sq + row * LDQ + col) = qr[d][i];
+        }
+#pragma unroll
+        for (int j = 0; j < NT_; ++j) qb[j] = tr_read8(sq, LDQ, 8 * g + (a >> 2), j * 16 + 4 * (a & 3));
+      } else {
+#pragma unroll
+        for (int j = 0; j < NT_; ++j) qb[j] = qr[d][j];
+      }
+#pragma unroll
+      for (int j = 0; j < NT_; ++j) acc[j] = mfma16(pa[d], qb[j], acc[j]);
+    }
+  }
+  // element e of lane l of column tile j: row 4 (l >> 4) + e, column 16 j + (l & 15)
+#pragma unroll
+  for (int j = 0; j < NT_; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sRed[wave][4 * g + e][j * 16 + a] = acc[j][e];
+  __syncthreads();
+  const int64_t ncol = n1 > n2 ? n1 : n2;
+  for (int64_t idx = tid; idx < ROWS * ncol; idx += 1024) {
+    const int m = (int)(idx / ncol);
+    const int64_t n = idx - m * ncol;
+    if (m0 + m >= M) continue;
+    float sum = 0.f;
+    if (n < RN)
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) sum += sRed[w][m][n];
+    if (out1 && n < n1) out1[(m0 + m) * ld1 + n] = f32_to_bf16(scale1 * sum);
+    if (out2 && n < n2) out2[(m0 + m) * ld2 + n] = (n < nvalid2) ? f32_to_bf16(scale2 * sum) : (bf16_t)0;
+  }
+}
+
 // One finalize job: S = sum over splits p = 0 .. nsplit-1 (in that order) of
 // part[p][m][n] (ld = N), then
 //   out1[m*ld1 + n] (or out1[n*ld1 + m] with trans1) = bf16(scale1 * S) for n < n1,
@@ -379,6 +482,31 @@ hipError_t launch_finalize_pair(const float *part_a, int nsplit_a, int64_t M_a, 
   const FinJob b = fin_job(part_b, nsplit_b, M_b, N_b, out_b, ld_b, n_b, scale_b, nullptr, 0, 0, 0, 0.f, trans_b);
   if (a.nblocks + b.nblocks == 0) return hipSuccess;
   launch(k_finalize, dim3((unsigned)(a.nblocks + b.nblocks)), dim3(256), 0, s, a, b);
+  return hipGetLastError();
+}
+
+bool lora_rows_ok(int rn, int64_t M) { return rn == kRowsRN && M >= kRowsMinM; }
+
+hipError_t launch_lora_rows(bool qt, int rn, const bf16_t *P, int64_t ldp, int64_t M, const bf16_t *Q, int64_t ldq,
+                            int64_t Rv, int64_t Kred, bf16_t *out1, int64_t ld1, int64_t n1, float scale1,
+                            bf16_t *out2, int64_t ld2, int64_t n2, int64_t nvalid2, float scale2, hipStream_t s) {
+  if (rn != kRowsRN) return hipErrorInvalidValue;
+  if (M == 0) return hipSuccess;
+  static thread_local int cus = 0;
+  if (cus <= 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      return hipErrorInvalidDevice;
+  }
+  const bool r8 = (M + 7) / 8 <= cus;  // measured: 8 rows up to one workgroup per CU (T = 2048: 8.9 / 7.4 us
+                                       // for U / dU against 10.7 / 9.2 with 16), 16 beyond (T = 4096)
+#define QLORA_LROWS(QT_, ROWS_)                                                                                 \
+  launch((k_lora_rows<QT_, kRowsRN, ROWS_>), dim3((unsigned)((M + ROWS_ - 1) / ROWS_)), dim3(1024), 0, s, P, ldp, \
+         M, Q, ldq, Rv, Kred, out1, ld1, n1, scale1, out2, ld2, n2, nvalid2, scale2)
+  if (qt) { if (r8) QLORA_LROWS(true, 8); else QLORA_LROWS(true, 16); }
+  else { if (r8) QLORA_LROWS(false, 8); else QLORA_LROWS(false, 16); }
+#undef QLORA_LROWS
   return hipGetLastError();
 }
 

@@ -162,6 +162,30 @@ def test_fwd_bwd_full_parity(n_out, n_in, T, r, alpha):
         assert torch.equal(g[k], g2[k]), k
 
 
+WHOLE_REDUCTION = [
+    # n_out, n_in, T, r, alpha: >= 1024 tokens with r <= 16, where U and dU reduce inside one workgroup
+    # (8-row tiles while they number at most the 256 CUs, else 16-row tiles)
+    (1000, 192, 1031, 5, 10.0),   # n_in / 16 waves < 32: waves 6..15 get empty ranges; ragged 16-row tile
+    (264, 640, 1024, 16, 32.0),   # exactly 64 row tiles
+    (136, 1088, 1100, 1, 2.0),    # rank 1 (B through its zero-padded copy), reduction tail in every wave
+    (72, 128, 2056, 12, 24.0),    # more 8-row tiles than CUs: 16-row tiles, the last one ragged
+]
+
+
+@pytest.mark.parametrize("n_out,n_in,T,r,alpha", WHOLE_REDUCTION)
+def test_whole_reduction_lora_parity(n_out, n_in, T, r, alpha):
+    """U (forward and the backward's recompute) and dU through the whole-reduction kernel, checked in full."""
+    print(f"whole-reduction parity n_out={n_out} n_in={n_in} T={T} r={r}", flush=True)
+    inp = linear_inputs(n_out, n_in, T, r, alpha, seed=T + 7 * r)
+    _, g = run_gpu(inp)
+    ref = run_oracle(inp)
+    for k in ("Y", "U", "dX", "dA", "dB"):
+        assert_close(k, gpu_f64(g[k]), ref[k])
+    _, g2 = run_gpu(inp, with_u=False)
+    for k in ("dX", "dA", "dB"):
+        assert torch.equal(g[k], g2[k]), k
+
+
 def test_lora_dominated_parity():
     """Large adapters so the LoRA terms dominate every output (a dropped or
     mis-scaled LoRA term cannot hide under the base term's tolerance)."""
