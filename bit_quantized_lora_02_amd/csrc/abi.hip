@@ -19,6 +19,7 @@
 #include "adamw.h"
 #include "device.h"
 #include "launch.h"
+#include "recip_div.h"
 #include "qlora.h"
 
 using namespace qlora;
@@ -687,6 +688,8 @@ int qlora_adamw_step(const qlora_adamw_tensor *tensors, int32_t count, double lr
   a.decay = (float)(1.0 - lr * weight_decay);
   a.step_size = (float)(lr / (1.0 - pow(beta1, (double)step)));
   a.sqrt_bc2 = (float)sqrt(1.0 - pow(beta2, (double)step));
+  a.rbc2 = (float)(1.0 / (double)a.sqrt_bc2);  // correctly rounded: binary64 has more than 2 * 24 + 2 bits
+  a.fast_bc2 = a.sqrt_bc2 >= kRecipDivMinB && a.sqrt_bc2 <= kRecipDivMaxB;
   for (int32_t first = 0; first < count; first += kAdamMaxTensors) {
     const int32_t cnt = (count - first < kAdamMaxTensors) ? count - first : kAdamMaxTensors;
     int64_t blocks = 0;
@@ -740,6 +743,8 @@ int qlora_adamw8_step(const qlora_adamw8_tensor *tensors, int32_t count, double 
   a.decay = (float)(1.0 - lr * weight_decay);
   a.step_size = (float)(lr / (1.0 - pow(beta1, (double)step)));
   a.sqrt_bc2 = (float)sqrt(1.0 - pow(beta2, (double)step));
+  a.rbc2 = (float)(1.0 / (double)a.sqrt_bc2);  // correctly rounded: binary64 has more than 2 * 24 + 2 bits
+  a.fast_bc2 = a.sqrt_bc2 >= kRecipDivMinB && a.sqrt_bc2 <= kRecipDivMaxB;
   for (int32_t first = 0; first < count; first += kAdamMaxTensors) {
     const int32_t cnt = (count - first < kAdamMaxTensors) ? count - first : kAdamMaxTensors;
     int64_t blocks = 0;

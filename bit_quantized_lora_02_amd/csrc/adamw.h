@@ -21,6 +21,8 @@ struct AdamParams {
   AdamTensor t[kAdamMaxTensors];
   int count;
   float b1, omb1, b2, omb2, eps, decay, step_size, sqrt_bc2;
+  float rbc2;     // RN(1 / sqrt_bc2), for recip_div
+  int fast_bc2;   // sqrt_bc2 lies where recip_div is exact (always, for beta2 in [0, 1))
 };
 
 hipError_t launch_adamw(const AdamParams &a, int64_t blocks, hipStream_t s);
@@ -42,6 +44,8 @@ struct Adam8Params {
   Adam8Tensor t[kAdamMaxTensors];
   int count;
   float b1, omb1, b2, omb2, eps, decay, step_size, sqrt_bc2;
+  float rbc2;
+  int fast_bc2;
 };
 hipError_t launch_adamw8(const Adam8Params &a, int64_t blocks, hipStream_t s);
 

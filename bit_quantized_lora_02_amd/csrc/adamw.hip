@@ -24,6 +24,7 @@
 // parameter and of the gradient, two of each binary32 array.
 #include "adamw.h"
 #include "dyn_code.h"
+#include "recip_div.h"
 #include "device.h"
 #include "launch.h"
 
@@ -31,12 +32,16 @@ namespace qlora {
 
 namespace {
 
-// (sqrtf is the correctly rounded square root; __fsqrt_rn would be the native one here)
+// (sqrtf is the correctly rounded square root; __fsqrt_rn would be the native one here).  sqrt(v) /
+// sqrt_bc2 divides by a constant of the launch: recip_div from the host's RN(1 / sqrt_bc2) gives the
+// same correctly rounded quotient (sqrt(v) <= 2^64 unless v is infinite, which passes through).
 template <class P>
 __device__ __forceinline__ float adam_elem(float &m, float &v, float theta, float g, const P &a) {
   m = __fadd_rn(__fmul_rn(a.b1, m), __fmul_rn(a.omb1, g));
   v = __fadd_rn(__fmul_rn(a.b2, v), __fmul_rn(__fmul_rn(a.omb2, g), g));
-  const float denom = __fadd_rn(__fdiv_rn(sqrtf(v), a.sqrt_bc2), a.eps);
+  const float sv = sqrtf(v);
+  const float sq = a.fast_bc2 ? (__builtin_isinf(sv) ? sv : recip_div(sv, a.sqrt_bc2, a.rbc2)) : __fdiv_rn(sv, a.sqrt_bc2);
+  const float denom = __fadd_rn(sq, a.eps);
   return __fsub_rn(__fmul_rn(theta, a.decay), __fmul_rn(a.step_size, __fdiv_rn(m, denom)));
 }
 
@@ -224,16 +229,20 @@ __global__ __launch_bounds__(256) void k_adamw8(Adam8Params a) {
   vx = fmaxf(fmaxf(s_red[1][0], s_red[1][1]), fmaxf(s_red[1][2], s_red[1][3]));
   if (tid == 0) ma[lb] = mx, va[lb] = vx;
   uint32_t om[2] = {0u, 0u}, ov[2] = {0u, 0u};
+  // x / absmax through one reciprocal per block where recip_div is exact (|x| <= absmax <= 2^100)
+  const bool fm = mx >= kRecipDivMinB && mx <= kRecipDivMaxB, fv = vx >= kRecipDivMinB && vx <= kRecipDivMaxB;
+  const float ym = fm ? __fdiv_rn(1.f, mx) : 0.f, yv = fv ? __fdiv_rn(1.f, vx) : 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     uint32_t cm = 0u, cv = 0u;
     if (mx > 0.f) {
-      const float x = __fdiv_rn(m[e], mx);
+      const float x = fm ? recip_div(m[e], mx, ym) : __fdiv_rn(m[e], mx);
       cm = dyn_code<kCmpS>(fabsf(x), reinterpret_cast<const uint8_t *>(s_ixs), kIxBaseS, kIxLastS, s_st);
       if (x < 0.f && cm) cm |= 128u;
     }
     if (vx > 0.f)
-      cv = dyn_code<kCmpU>(__fdiv_rn(v[e], vx), reinterpret_cast<const uint8_t *>(s_ixu), kIxBaseU, kIxLastU, s_ut);
+      cv = dyn_code<kCmpU>(fv ? recip_div(v[e], vx, yv) : __fdiv_rn(v[e], vx), reinterpret_cast<const uint8_t *>(s_ixu),
+                           kIxBaseU, kIxLastU, s_ut);
     om[e >> 2] |= cm << (8 * (e & 3));
     ov[e >> 2] |= cv << (8 * (e & 3));
   }
