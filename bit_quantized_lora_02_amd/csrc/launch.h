@@ -55,7 +55,11 @@ int nf4_gemm_pick_tile(int64_t M, int64_t N);
 hipError_t launch_nf4_gemm_fwd(int tile, const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes,
                                const uint8_t *absmax_q, const float *step, int64_t N, const bf16_t *V,
                                const bf16_t *Bp, int64_t ldb, int64_t r, int64_t rp, bf16_t *Y, const Levels &lv,
-                               hipStream_t s, const SegTable &sg = SegTable());
+                               hipStream_t s, const SegTable &sg = SegTable(), int nsplit = 1,
+                               float *psum = nullptr);
+// Reduction ranges for the forward GEMM with `tile` (1: none): more than one only when its tiles cannot
+// occupy every CU; the binary32 sums then go to psum [nsplit][T][N] and launch_finalize adds them.
+int nf4_gemm_fwd_split(int tile, int64_t T, int64_t N, int64_t K);
 // dX = dY W' + G o (dUp A); with `mask` (keep bits of X, byte (t K + k) / 8,
 // bit k % 8) G = keep * q, without it G = 1.
 hipError_t launch_nf4_gemm_dx(int tile, const bf16_t *dY, int64_t T, int64_t N, const uint8_t *codes,

@@ -244,6 +244,25 @@ __device__ __forceinline__ void store_out(bf16_t *__restrict__ out, int64_t ld, 
     }
 }
 
+// The same for binary32 partial sums (split reduction): out[row ld + col] = acc.
+template <class C>
+__device__ __forceinline__ void store_out_f32(float *__restrict__ out, int64_t ld, int64_t m0, int64_t rows,
+                                              int64_t n0, int64_t cols, int wm, int wn, int lane,
+                                              const f32x16_t acc[C::WM][C::WN]) {
+#pragma unroll
+  for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) {
+      const int64_t col = n0 + (wn * C::WN + j) * 32 + (lane & 31);
+      if (col >= cols) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = m0 + (wm * C::WM + i) * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+        if (row < rows) out[row * ld + col] = acc[i][j][e];
+      }
+    }
+}
+
 // Wait for all but the last three vector-memory loads (the code words and the
 // block constant issued after the activation tile) and for all LDS operations.
 // s_waitcnt fields: vmcnt[3:0], expcnt[6:4] (7 = no wait), lgkmcnt[11:8].
@@ -324,6 +343,9 @@ __device__ __forceinline__ void pipelined_step(const bf16_t *sa, const bf16_t *s
 
 // ---------------------------------------------------------------- forward
 // Y[T, N] = X[T, K] . W'[N, K]^T + V[T, rp] . B[N, :r]^T   (B row stride ldb, columns >= r read as 0)
+// With psum != null the reduction is split into gridDim.y ranges of K / gridDim.y columns (a multiple
+// of 64): workgroup (x, y) computes tile x over range y and stores its binary32 sums in
+// psum[y][T][N]; range 0 also adds the LoRA term.  (A finalize adds the ranges in order.)
 template <class C, bool MULTI>
 __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict__ X, int64_t T, int64_t K,
                                                         const uint8_t *__restrict__ codes,
@@ -331,7 +353,8 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
                                                         const float *__restrict__ step, int64_t N,
                                                         const bf16_t *__restrict__ V, const bf16_t *__restrict__ Bp,
                                                         int64_t ldb, int64_t r, int64_t rp, bf16_t *__restrict__ Y,
-                                                        Levels lv, int xb_m, int xb_n, SegTable sg) {
+                                                        Levels lv, int xb_m, int xb_n, SegTable sg,
+                                                        float *__restrict__ psum) {
   __shared__ __attribute__((aligned(16))) bf16_t sA0[C::BM * BK];
   __shared__ __attribute__((aligned(16))) bf16_t sA1[C::BM * BK];
   __shared__ __attribute__((aligned(16))) bf16_t sB0[C::BN * BK];
@@ -345,16 +368,18 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
   const int64_t m0 = tc.m * C::BM, n0 = tc.n * C::BN;
   pair_levels_to_lds(lv, s_lv, tid);
 
-  const int nk = (int)(K / BK);
+  const int split = (int)blockIdx.y;
+  const int64_t kc = K / gridDim.y, kbase = (int64_t)split * kc;  // this workgroup's reduction range
+  const int nk = (int)(kc / BK);
   ALoads<C> al;
-  al.init(X, K, m0, T, wave, lane);
+  al.init(X + kbase, K, m0, T, wave, lane);
   // this thread decodes weights part*E .. part*E+E-1 of tile row brow
   constexpr int PARTS = BK / C::E;
   const bool decoder = C::DEC == C::NT || tid < C::DEC;  // wave-uniform; a constant when every thread decodes
   const int brow = decoder ? tid / PARTS : 0, part = tid % PARTS;
   const int64_t wrow = (n0 + brow < N) ? n0 + brow : N - 1;  // rows past N feed columns that are never stored
-  const uint8_t *crow = codes + wrow * (K / 2) + part * (C::E / 2);
-  const int64_t blk0 = wrow * (K / BK);
+  const uint8_t *crow = codes + wrow * (K / 2) + kbase / 2 + part * (C::E / 2);
+  const int64_t blk0 = wrow * (K / BK) + kbase / BK;
   uint32_t rc[2][C::NWD];
   RawScale rs[2];
   auto load_words_of = [&](int s, uint32_t(&w)[C::NWD], RawScale &sc) {
@@ -367,7 +392,7 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
   zero_acc<C>(acc);
 
   // prologue: tile 0 of A, words of steps 0 and 1, decode step 0
-  al.issue(0, K, sA[0]);
+  al.issue(0, kc, sA[0]);
   load_words_of(0, rc[0], rs[0]);
   load_words_of(nk > 1 ? 1 : 0, rc[1], rs[1]);
   __syncthreads();  // level table visible
@@ -387,7 +412,7 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
     constexpr int P = decltype(pc)::value;
     const int sa = (s + 1 < nk) ? s + 1 : nk - 1, sc = (s + 2 < nk) ? s + 2 : nk - 1;
     auto load_next = [&]() {
-      al.issue((int64_t)sa * BK, K, sA[P ^ 1]);
+      al.issue((int64_t)sa * BK, kc, sA[P ^ 1]);
       fence_sched();  // activation loads first: waiting for them leaves the words in flight
       load_words_of(sc, rc[P], rs[P]);
     };
@@ -427,7 +452,9 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
       __syncthreads();
     }
   };
-  if constexpr (!MULTI) {
+  if (split != 0) {
+    // the LoRA term belongs to range 0 only
+  } else if constexpr (!MULTI) {
     lora_rows(Bp, 0, T);
   } else {
     // many adapters: one masked up-projection per token segment that meets this tile's rows
@@ -447,7 +474,8 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
       lora_rows(Bp + (int64_t)a * N * r, lo, hi);
     }
   }
-  store_out<C>(Y, N, m0, T, n0, N, wm, wn, lane, acc);
+  if (psum) store_out_f32<C>(psum + (int64_t)split * T * N, N, m0, T, n0, N, wm, wn, lane, acc);
+  else store_out<C>(Y, N, m0, T, n0, N, wm, wn, lane, acc);
 }
 
 // --------------------------------------------------------------- backward
@@ -671,16 +699,18 @@ void xcd_blocking(int64_t tiles_m, int64_t tiles_n, double a_bytes, double b_byt
 template <class C>
 hipError_t fwd_with(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
                     const float *step, int64_t N, const bf16_t *V, const bf16_t *Bp, int64_t ldb, int64_t r,
-                    int64_t rp, bf16_t *Y, const Levels &lv, hipStream_t s, const SegTable &sg) {
+                    int64_t rp, bf16_t *Y, const Levels &lv, hipStream_t s, const SegTable &sg, int nsplit,
+                    float *psum) {
   const int64_t tm = (T + C::BM - 1) / C::BM, tn = (N + C::BN - 1) / C::BN;
   int xb_m, xb_n;
   xcd_blocking(tm, tn, 2.0 * T * K, 0.516 * N * K, &xb_m, &xb_n);
+  const dim3 grid((unsigned)(tm * tn), (unsigned)nsplit);
   if (sg.seg)
-    launch(k_nf4_gemm_fwd<C, true>, dim3((unsigned)(tm * tn)), dim3(C::NT), 0, s, X, T, K, codes, absmax_q, step, N,
-           V, Bp, ldb, r, rp, Y, lv, xb_m, xb_n, sg);
+    launch(k_nf4_gemm_fwd<C, true>, grid, dim3(C::NT), 0, s, X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y,
+           lv, xb_m, xb_n, sg, psum);
   else
-    launch(k_nf4_gemm_fwd<C, false>, dim3((unsigned)(tm * tn)), dim3(C::NT), 0, s, X, T, K, codes, absmax_q, step, N,
-           V, Bp, ldb, r, rp, Y, lv, xb_m, xb_n, sg);
+    launch(k_nf4_gemm_fwd<C, false>, grid, dim3(C::NT), 0, s, X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y,
+           lv, xb_m, xb_n, sg, psum);
   return hipGetLastError();
 }
 
@@ -697,6 +727,9 @@ hipError_t dx_with(const bf16_t *dY, int64_t T, int64_t N, const uint8_t *codes,
 }
 }  // namespace
 
+// Split reduction of the forward GEMM: at most this many ranges, each at least this many 64-deep steps.
+constexpr int kFwdMaxSplit = 16, kFwdMinSteps = 8;
+
 // Tile choice for an M x N output.  Measured on MI355X (both GEMMs, seven
 // workload shapes): the largest 8-wave tile that still yields at least one
 // workgroup per CU (256 tiles) is fastest -- 256x256, else 256x128; below that
@@ -708,22 +741,35 @@ int nf4_gemm_pick_tile(int64_t M, int64_t N) {
   return NF4_TILE_128x128_W8;
 }
 
+int nf4_gemm_fwd_split(int tile, int64_t T, int64_t N, int64_t K) {
+  int64_t bm = 128, bn = 128;
+  int per_cu = 2;  // resident workgroups per CU (the 128x128 tiles: two; the larger 8-wave tiles: one)
+  if (tile == NF4_TILE_256x256_W8) bm = 256, bn = 256, per_cu = 1;
+  else if (tile == NF4_TILE_256x128_W8) bm = 256, per_cu = 1;
+  else if (tile == NF4_TILE_128x256_W8) bn = 256, per_cu = 1;
+  const int64_t tiles = ((T + bm - 1) / bm) * ((N + bn - 1) / bn), slots = 256 * per_cu, nk = K / BK;
+  int best = 1;
+  for (int d = 2; d <= kFwdMaxSplit; ++d)
+    if (nk % d == 0 && nk / d >= kFwdMinSteps && tiles * d <= slots) best = d;
+  return best;
+}
+
 hipError_t launch_nf4_gemm_fwd(int tile, const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes,
                                const uint8_t *absmax_q, const float *step, int64_t N, const bf16_t *V,
                                const bf16_t *Bp, int64_t ldb, int64_t r, int64_t rp, bf16_t *Y, const Levels &lv,
-                               hipStream_t s, const SegTable &sg) {
+                               hipStream_t s, const SegTable &sg, int nsplit, float *psum) {
   if (T == 0) return hipSuccess;
+  if (nsplit < 1 || (nsplit > 1 && (!psum || K % ((int64_t)nsplit * BK) != 0))) return hipErrorInvalidValue;
+  if (nsplit == 1) psum = nullptr;
+#define QLORA_FWD(CFG) fwd_with<CFG>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s, sg, nsplit, psum)
   switch (tile) {
-    case NF4_TILE_256x256_W8:
-      return fwd_with<T256x256w8>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s, sg);
-    case NF4_TILE_256x128_W8:
-      return fwd_with<T256x128w8>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s, sg);
-    case NF4_TILE_128x256_W8:
-      return fwd_with<T128x256w8>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s, sg);
-    case NF4_TILE_128x128_W8:
-      return fwd_with<T128x128w8>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s, sg);
-    default: return fwd_with<T128x128>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s, sg);
+    case NF4_TILE_256x256_W8: return QLORA_FWD(T256x256w8);
+    case NF4_TILE_256x128_W8: return QLORA_FWD(T256x128w8);
+    case NF4_TILE_128x256_W8: return QLORA_FWD(T128x256w8);
+    case NF4_TILE_128x128_W8: return QLORA_FWD(T128x128w8);
+    default: return QLORA_FWD(T128x128);
   }
+#undef QLORA_FWD
 }
 
 hipError_t launch_nf4_gemm_dx(int tile, const bf16_t *dY, int64_t T, int64_t N, const uint8_t *codes,

@@ -172,6 +172,27 @@ WHOLE_REDUCTION = [
 ]
 
 
+SPLIT_FORWARD = [
+    # n_out, n_in, T, r, alpha: more than 64 tokens but too few output tiles to occupy every CU, so the
+    # forward GEMM splits its reduction into ranges (binary32 partial sums, added in order by a finalize)
+    (1024, 2048, 128, 16, 32.0),  # 8 tiles, 32 steps: 4 ranges
+    (520, 1024, 100, 128, 16.0),  # ragged tokens and rows, rank 128 (two LoRA steps in range 0): 2 ranges
+]
+
+
+@pytest.mark.parametrize("n_out,n_in,T,r,alpha", SPLIT_FORWARD)
+def test_split_forward_parity(n_out, n_in, T, r, alpha):
+    """The split-reduction forward GEMM, checked in full (and the backward of the same inputs)."""
+    print(f"split forward parity n_out={n_out} n_in={n_in} T={T} r={r}", flush=True)
+    inp = linear_inputs(n_out, n_in, T, r, alpha, seed=T + r)
+    _, g = run_gpu(inp)
+    ref = run_oracle(inp)
+    for k in ("Y", "U", "dX", "dA", "dB"):
+        assert_close(k, gpu_f64(g[k]), ref[k])
+    _, g2 = run_gpu(inp)  # the same inputs again: bitwise repeatable
+    assert torch.equal(g["Y"], g2["Y"])
+
+
 @pytest.mark.parametrize("n_out,n_in,T,r,alpha", WHOLE_REDUCTION)
 def test_whole_reduction_lora_parity(n_out, n_in, T, r, alpha):
     """U (forward and the backward's recompute) and dU through the whole-reduction kernel, checked in full."""
