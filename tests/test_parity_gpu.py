@@ -169,6 +169,7 @@ WHOLE_REDUCTION = [
     (264, 640, 1024, 16, 32.0),   # exactly 64 row tiles
     (136, 1088, 1100, 1, 2.0),    # rank 1 (B through its zero-padded copy), reduction tail in every wave
     (72, 128, 2056, 12, 24.0),    # more 8-row tiles than CUs: 16-row tiles, the last one ragged
+    (4104, 1088, 40, 16, 32.0),   # few tokens: U and dU split; n_out 4104 and n_in 1088 for dB and dA
 ]
 
 
