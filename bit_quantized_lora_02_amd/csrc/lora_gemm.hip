@@ -9,7 +9,8 @@
 // narrow one (the rank, r <= 128), so each is a skinny bf16 MFMA GEMM, split
 // along its reduction, that writes binary32 partial sums; a finalize kernel
 // then adds the splits in a fixed order (bitwise repeatable, no atomics),
-// scales, and rounds to bf16 once.
+// scales, and rounds to bf16 once.  U and dU of many tokens at a narrow rank
+// instead reduce inside one workgroup and skip the finalize (k_lora_rows).
 #include "device.h"
 #include "launch.h"
 

@@ -21,7 +21,9 @@
 //  - one barrier per step.
 // The dequantized weight therefore exists only as one 64-deep tile in LDS.
 // The LoRA term follows as a few extra reduction steps over the padded rank,
-// landing in the same binary32 accumulators.
+// landing in the same binary32 accumulators.  When the forward's output has too
+// few tiles to occupy every CU, its reduction is split into ranges whose
+// binary32 partial sums a finalize adds in order (nf4_gemm_fwd_split).
 //
 // LDS tiles of the A operand (and the forward B operand) are [row][64] bf16
 // (128-byte rows) with the 16-byte chunk index XOR-swizzled by (row / 2) % 8:

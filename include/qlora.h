@@ -97,8 +97,11 @@ int qlora_nf4_storage(int64_t n_out, int64_t n_in, size_t *codes_bytes, size_t *
 int qlora_nf4_codebook(float levels[16]);
 
 /* Workspace bytes needed by `op` (a QLORA_OP_* value) for these
- * sizes, into host *bytes (no HIP call).  The forward workspace is O(T*r + n_out*r),
- * never O(n_out*n_in): the dequantized weight is never stored. */
+ * sizes, into host *bytes (no HIP call).  The forward workspace is
+ * O(T*r + n_out*r + T*n_out) -- the last term only when few tokens or few output
+ * tiles make it split the reduction over n_in into at most 16 ranges, each
+ * writing binary32 partial sums of Y -- and never O(n_out*n_in): the dequantized
+ * weight is never stored. */
 int qlora_workspace_bytes(int op, int64_t T, int64_t n_out, int64_t n_in, int32_t r, size_t *bytes);
 
 /* Quantize a binary32 weight W [n_out, n_in] (device) into q's arrays (device,
