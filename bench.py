@@ -81,7 +81,7 @@ def log(*a):
 KERNEL_SOURCES = {"nf4_gemm_fwd": "nf4_gemm.hip", "nf4_gemm_dx": "nf4_gemm.hip", "nf4_gemv": "nf4_gemv.hip"}
 # kernel symbols behind each timed launch label (the small-token forward has two kernels)
 KERNEL_SYMBOLS = {"nf4_gemm_fwd": ("k_nf4_gemm_fwd",), "nf4_gemm_dx": ("k_nf4_gemm_dx",),
-                  "nf4_gemv": ("k_nf4_gemv", "k_nf4_gemv_rows")}
+                  "nf4_gemv": ("k_nf4_gemv", "k_nf4_gemv_rows", "k_nf4_gemv_mrows")}
 
 
 def _code_only(text: str) -> str:

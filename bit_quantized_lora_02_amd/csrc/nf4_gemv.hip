@@ -406,6 +406,96 @@ __global__ __launch_bounds__(256, TT == 1 ? 8 : 6) void k_nf4_gemv_rows(
   if (f < items) do_step(s0, s1);
 }
 
+// ------------------------------------------- the row-group GEMV (3..16 tokens)
+// The MFMA formulation of k_nf4_gemv with the row kernel's layout: a work item
+// is 16 weight rows over one segment of 512 columns (nseg = K / 512 segments,
+// one per workgroup for the whole launch).  Lane (a, g) = (l & 15, l >> 4)
+// keeps token a's activations at segment columns 128 g .. 128 g + 127 in
+// registers (64 VGPRs, loaded once; tokens T..15 are zero) and streams weight
+// row 16 i + a's codes for the same columns (64 bytes, four 16-byte loads per
+// item).  MFMA step s (v_mfma_f32_16x16x32_bf16, tokens as M) takes columns
+// 128 g + 8 s .. + 7 of every lane group g -- the same permutation of the
+// reduction for both operands, so the products are those of the layer.  The
+// decode is k_nf4_gemv's: level pairs from the LDS table, fl32(level * c'),
+// bf16 pack.  The next item loads while the current one computes (two fixed
+// slots, the loop unrolled by two).  Main workgroup g owns segment g % nseg,
+// its wave w the row groups 4 (g / nseg) + w + i 4 gmain / nseg.  part is
+// [nseg][T][N]; workgroups 0 .. nsplit_u - 1 come first and form the U partials
+// as in k_nf4_gemv_rows.
+constexpr int kMrowsSeg = 512, kMrowsMaxT = 16;
+__global__ __launch_bounds__(256, 3) void k_nf4_gemv_mrows(
+    const bf16_t *__restrict__ X, int64_t T, int64_t K, const uint8_t *__restrict__ codes,
+    const uint8_t *__restrict__ absmax_q, const float *__restrict__ step, int64_t N, int gmain, int nseg, int nsplit_u,
+    const bf16_t *__restrict__ A, int64_t r, float *__restrict__ part, float *__restrict__ upart, Levels lv) {
+  __shared__ __attribute__((aligned(16))) float2 s_tab[256];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if ((int)blockIdx.x < nsplit_u) {
+    const int64_t u = blockIdx.x, kchunk = K / nsplit_u, kb = u * kchunk;
+    lora_u_partial<1>(X, T, K, A, r, kb, kb + kchunk, upart + (u * 4 + wave) * T * r, wave, lane);
+    return;
+  }
+  const int a = lane & 15, g = lane >> 4;
+  const int gi = (int)blockIdx.x - nsplit_u, seg = gi % nseg;
+  const int64_t ngroups = (N + 15) / 16;
+  const int64_t rg0 = (int64_t)(gi / nseg) * 4 + wave, rgs = (int64_t)(gmain / nseg) * 4;
+  const int64_t items = rg0 < ngroups ? (ngroups - rg0 + rgs - 1) / rgs : 0;
+  const int64_t col0 = (int64_t)seg * kMrowsSeg + 128 * g;  // this lane group's first column
+  pair_levels_to_lds(lv, s_tab, tid);
+  u32x4_t xa[16];
+  const bool tok = a < T;
+  const bf16_t *xp = X + (tok ? a : 0) * K + col0;
+#pragma unroll
+  for (int s = 0; s < 16; ++s) xa[s] = tok ? *reinterpret_cast<const u32x4_t *>(xp + 8 * s) : u32x4_t{0u, 0u, 0u, 0u};
+  __syncthreads();
+  if (items <= 0) return;
+
+  struct Slot {
+    u32x4_t c[4];     // the lane's 64 code bytes (128 weights of one row)
+    RawScale sc[2];   // their two blocks' constants
+  };
+  int64_t li = 0;  // item of the load stream; it stops at the last item (later prefetches reload it, unused)
+  auto load_slot = [&](Slot &sl) {
+    int64_t n = (rg0 + li * rgs) * 16 + a;
+    n = n < N ? n : N - 1;  // rows past N re-read the last row; they are never stored
+    const uint8_t *cp = codes + n * (K / 2) + col0 / 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sl.c[i] = *reinterpret_cast<const u32x4_t *>(cp + 16 * i);
+    const int64_t b0 = n * (K / 64) + col0 / 64;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) sl.sc[b] = load_scale(absmax_q, step, b0 + b);
+    if (li + 1 < items) ++li;
+  };
+  float *pseg = part + (int64_t)seg * T * N;
+  int64_t crg = rg0;  // row group of the item being computed
+  auto do_step = [&](Slot &cur, Slot &refill) {
+    load_slot(refill);
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const float cq0 = scale_of(cur.sc[0]), cq1 = scale_of(cur.sc[1]);
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const uint32_t w = cur.c[s >> 2][s & 3];
+      acc = mfma_16x16x32(xa[s], decode8_pairs(w, s < 8 ? cq0 : cq1, s_tab), acc);
+    }
+    // element e of lane l: token 4 (l >> 4) + e, weight row 16 crg + (l & 15)
+    const int64_t n = crg * 16 + a;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t t = 4 * g + e;
+      if (n < N && t < T) pseg[t * N + n] = acc[e];
+    }
+    crg += rgs;
+  };
+  Slot s0, s1;
+  load_slot(s0);
+  int64_t f = 0;
+  for (; f + 1 < items; f += 2) {
+    do_step(s0, s1);
+    do_step(s1, s0);
+  }
+  if (f < items) do_step(s0, s1);
+}
+
 // Sums of the finishing kernels, in index order with every load issued first (a loop bound known only
 // at run time would otherwise wait for each load before the next): the 1 <= n <= 16 weight partials
 // src[0], src[stride], ..., and the U partials p = q, q + 8, ... < nup <= 64 of (t, j).  Indexes past
@@ -685,6 +775,38 @@ static int rows_resident() {
     return 0;
   res = nb * cus;
   return res;
+}
+
+int nf4_gemv_mrows_nseg(int64_t T, int64_t K) {
+  if (T < 3 || T > kMrowsMaxT || K <= 0 || K % kMrowsSeg != 0) return 0;
+  const int64_t ns = K / kMrowsSeg;
+  return ns <= kFinishMaxSplit ? (int)ns : 0;
+}
+
+hipError_t launch_nf4_gemv_mrows(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
+                                 const float *step, int64_t N, int nsplit_u, const bf16_t *A, int64_t r, float *part,
+                                 float *upart, const Levels &lv, hipStream_t s, int *nseg_out) {
+  *nseg_out = 1;
+  if (T == 0) return hipSuccess;
+  const int nseg = nf4_gemv_mrows_nseg(T, K);
+  if (nseg <= 0) return hipErrorInvalidValue;
+  static thread_local int res = 0;
+  if (res <= 0) {
+    int dev = 0, cus = 0, nb = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_nf4_gemv_mrows, 256, 0) != hipSuccess || nb < 1 || cus < 1)
+      return hipErrorInvalidDeviceFunction;
+    res = nb * cus;
+  }
+  // main workgroups: what stays resident beside the U workgroups, at most one item per wave, a multiple of nseg
+  int64_t g = std::min<int64_t>(std::max(1, res - nsplit_u), ((N + 15) / 16 * nseg + 3) / 4);
+  g = std::max<int64_t>(nseg, g / nseg * nseg);
+  const int gmain = (int)g;
+  launch(k_nf4_gemv_mrows, dim3((unsigned)(gmain + nsplit_u)), dim3(256), 0, s, X, T, K, codes, absmax_q, step, N,
+         gmain, nseg, nsplit_u, A, r, part, upart, lv);
+  *nseg_out = nseg;
+  return hipGetLastError();
 }
 
 hipError_t launch_nf4_gemv_rows(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,

@@ -372,6 +372,24 @@ def test_small_token_forward(n_out, T):
     assert_close("U", gpu_f64(U[idx]), Ur)
 
 
+@pytest.mark.parametrize("n_out,n_in,T,r", [(72, 512, 3, 16), (8, 1536, 16, 4), (1000, 4096, 9, 1),
+                                            (24, 8192, 16, 64), (136, 8704, 5, 8)])
+def test_row_group_forward(n_out, n_in, T, r):
+    """3..16 tokens with n_in % 512 == 0 and at most 16 segments of 512 columns: the row-group kernel
+    (16 rows per wave, activations in registers), from one segment with a ragged row group to 16 segments,
+    and n_in = 8704 (17 segments), which takes the MFMA kernel; checked in full."""
+    print(f"row-group forward {n_out}x{n_in} T={T} r={r}", flush=True)
+    inp = linear_inputs(n_out, n_in, T, r, 2.0 * r, seed=n_out + 3 * T, sigma_ab=0.05)
+    w = Bd.quantize_nf4(torch.from_numpy(inp.W).to(dev()))
+    X, A, B = (to_gpu_bf16(a) for a in (inp.X, inp.A, inp.B))
+    Y, U = Bd.linear_fwd(X, w, A, B, inp.alpha)
+    torch.cuda.synchronize()
+    oc, oq, od = O.quantize_nf4(inp.W)
+    Yr, Ur = O.linear_fwd(inp.X, O.dequant(oc, oq, od, n_out, n_in), inp.A, inp.B, inp.alpha)
+    assert_close("Y", gpu_f64(Y), Yr)
+    assert_close("U", gpu_f64(U), Ur)
+
+
 @pytest.mark.parametrize("n_out,n_in,T,r", [(72, 2048, 1, 16), (1032, 4096, 2, 5), (520, 8192, 1, 32),
                                             (264, 16384, 2, 64), (8, 2048, 2, 8), (4104, 6144, 1, 12),
                                             (2056, 4096, 2, 24), (6152, 8192, 1, 16), (520, 8192, 3, 16),
