@@ -406,33 +406,38 @@ __global__ __launch_bounds__(256, TT == 1 ? 8 : 6) void k_nf4_gemv_rows(
   if (f < items) do_step(s0, s1);
 }
 
-// ------------------------------------------- the row-group GEMV (3..16 tokens)
-// The MFMA formulation of k_nf4_gemv with the row kernel's layout: a work item
-// is 16 weight rows over one segment of 512 columns (nseg = K / 512 segments,
-// one per workgroup for the whole launch).  Lane (a, g) = (l & 15, l >> 4)
-// keeps token a's activations at segment columns 128 g .. 128 g + 127 in
-// registers (64 VGPRs, loaded once; tokens T..15 are zero) and streams weight
-// row 16 i + a's codes for the same columns (64 bytes, four 16-byte loads per
-// item).  MFMA step s (v_mfma_f32_16x16x32_bf16, tokens as M) takes columns
-// 128 g + 8 s .. + 7 of every lane group g -- the same permutation of the
-// reduction for both operands, so the products are those of the layer.  The
-// decode is k_nf4_gemv's: level pairs from the LDS table, fl32(level * c'),
-// bf16 pack.  The next item loads while the current one computes (two fixed
-// slots, the loop unrolled by two).  Main workgroup g owns segment g % nseg,
-// its wave w the row groups 4 (g / nseg) + w + i 4 gmain / nseg.  part is
-// [nseg][T][N]; workgroups 0 .. nsplit_u - 1 come first and form the U partials
-// as in k_nf4_gemv_rows.
-constexpr int kMrowsSeg = 512, kMrowsMaxT = 16;
+// ------------------------------------------- the row-group GEMV (3..32 tokens)
+// The MFMA formulation of k_nf4_gemv with the row kernel's layout, for MT
+// groups of 16 tokens (MT = 1: up to 16 tokens, MT = 2: up to 32).  A work item
+// is 16 weight rows over one segment of KS = 512 / MT columns (nseg = K / KS
+// segments, one per workgroup for the whole launch).  Lane (a, g) = (l & 15,
+// l >> 4) keeps tokens 16 m + a's activations at segment columns CL g .. CL g +
+// CL - 1 (CL = 128 / MT) in registers (64 VGPRs for either MT, loaded once;
+// tokens past T are zero) and streams weight row 16 i + a's codes for the same
+// columns (CL / 2 bytes: 64 / MT ... four or two 16-byte loads per item).
+// MFMA step s (v_mfma_f32_16x16x32_bf16, tokens as M) takes columns CL g + 8 s
+// .. + 7 of every lane group g -- the same permutation of the reduction for
+// both operands, so the products are those of the layer.  The decode is
+// k_nf4_gemv's: level pairs from the LDS table, fl32(level * c'), bf16 pack.
+// The next item loads while the current one computes (two fixed slots, the
+// loop unrolled by two).  Main workgroup g owns segment g % nseg, its wave w
+// the row groups 4 (g / nseg) + w + i 4 gmain / nseg.  part is [nseg][T][N];
+// workgroups 0 .. nsplit_u - 1 come first and form the U partials as in
+// k_nf4_gemv_rows.
+constexpr int kMrowsMaxT = 32;
+template <int MT>
 __global__ __launch_bounds__(256, 3) void k_nf4_gemv_mrows(
     const bf16_t *__restrict__ X, int64_t T, int64_t K, const uint8_t *__restrict__ codes,
     const uint8_t *__restrict__ absmax_q, const float *__restrict__ step, int64_t N, int gmain, int nseg, int nsplit_u,
     const bf16_t *__restrict__ A, int64_t r, float *__restrict__ part, float *__restrict__ upart, Levels lv) {
+  constexpr int KS = 512 / MT, CL = 128 / MT, NS = CL / 8;  // segment, lane-group columns, MFMA steps per item
+  constexpr int NW = CL / 32, NB = CL / 64;                  // 16-byte code loads and blocks per lane and item
   __shared__ __attribute__((aligned(16))) float2 s_tab[256];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if ((int)blockIdx.x < nsplit_u) {
     const int64_t u = blockIdx.x, kchunk = K / nsplit_u, kb = u * kchunk;
-    lora_u_partial<1>(X, T, K, A, r, kb, kb + kchunk, upart + (u * 4 + wave) * T * r, wave, lane);
+    lora_u_partial<MT>(X, T, K, A, r, kb, kb + kchunk, upart + (u * 4 + wave) * T * r, wave, lane);
     return;
   }
   const int a = lane & 15, g = lane >> 4;
@@ -440,19 +445,23 @@ __global__ __launch_bounds__(256, 3) void k_nf4_gemv_mrows(
   const int64_t ngroups = (N + 15) / 16;
   const int64_t rg0 = (int64_t)(gi / nseg) * 4 + wave, rgs = (int64_t)(gmain / nseg) * 4;
   const int64_t items = rg0 < ngroups ? (ngroups - rg0 + rgs - 1) / rgs : 0;
-  const int64_t col0 = (int64_t)seg * kMrowsSeg + 128 * g;  // this lane group's first column
+  const int64_t col0 = (int64_t)seg * KS + CL * g;  // this lane group's first column
   pair_levels_to_lds(lv, s_tab, tid);
-  u32x4_t xa[16];
-  const bool tok = a < T;
-  const bf16_t *xp = X + (tok ? a : 0) * K + col0;
+  u32x4_t xa[MT][NS];
 #pragma unroll
-  for (int s = 0; s < 16; ++s) xa[s] = tok ? *reinterpret_cast<const u32x4_t *>(xp + 8 * s) : u32x4_t{0u, 0u, 0u, 0u};
+  for (int m = 0; m < MT; ++m) {
+    const int64_t t = 16 * m + a;
+    const bf16_t *xp = X + (t < T ? t : 0) * K + col0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      xa[m][s] = t < T ? *reinterpret_cast<const u32x4_t *>(xp + 8 * s) : u32x4_t{0u, 0u, 0u, 0u};
+  }
   __syncthreads();
   if (items <= 0) return;
 
   struct Slot {
-    u32x4_t c[4];     // the lane's 64 code bytes (128 weights of one row)
-    RawScale sc[2];   // their two blocks' constants
+    u32x4_t c[NW];    // the lane's CL / 2 code bytes (CL weights of one row)
+    RawScale sc[NB];  // their blocks' constants
   };
   int64_t li = 0;  // item of the load stream; it stops at the last item (later prefetches reload it, unused)
   auto load_slot = [&](Slot &sl) {
@@ -460,30 +469,38 @@ __global__ __launch_bounds__(256, 3) void k_nf4_gemv_mrows(
     n = n < N ? n : N - 1;  // rows past N re-read the last row; they are never stored
     const uint8_t *cp = codes + n * (K / 2) + col0 / 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sl.c[i] = *reinterpret_cast<const u32x4_t *>(cp + 16 * i);
+    for (int i = 0; i < NW; ++i) sl.c[i] = *reinterpret_cast<const u32x4_t *>(cp + 16 * i);
     const int64_t b0 = n * (K / 64) + col0 / 64;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) sl.sc[b] = load_scale(absmax_q, step, b0 + b);
+    for (int b = 0; b < NB; ++b) sl.sc[b] = load_scale(absmax_q, step, b0 + b);
     if (li + 1 < items) ++li;
   };
   float *pseg = part + (int64_t)seg * T * N;
   int64_t crg = rg0;  // row group of the item being computed
   auto do_step = [&](Slot &cur, Slot &refill) {
     load_slot(refill);
-    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const float cq0 = scale_of(cur.sc[0]), cq1 = scale_of(cur.sc[1]);
+    f32x4_t acc[MT];
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
+    for (int m = 0; m < MT; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float cq[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) cq[b] = scale_of(cur.sc[b]);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
       const uint32_t w = cur.c[s >> 2][s & 3];
-      acc = mfma_16x16x32(xa[s], decode8_pairs(w, s < 8 ? cq0 : cq1, s_tab), acc);
+      const u32x4_t bop = decode8_pairs(w, cq[s / 8], s_tab);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[m] = mfma_16x16x32(xa[m][s], bop, acc[m]);
     }
-    // element e of lane l: token 4 (l >> 4) + e, weight row 16 crg + (l & 15)
+    // element e of lane l in token group m: token 16 m + 4 (l >> 4) + e, weight row 16 crg + (l & 15)
     const int64_t n = crg * 16 + a;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t t = 4 * g + e;
-      if (n < N && t < T) pseg[t * N + n] = acc[e];
-    }
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t t = 16 * m + 4 * g + e;
+        if (n < N && t < T) pseg[t * N + n] = acc[m][e];
+      }
     crg += rgs;
   };
   Slot s0, s1;
@@ -501,16 +518,18 @@ __global__ __launch_bounds__(256, 3) void k_nf4_gemv_mrows(
 // src[0], src[stride], ..., and the U partials p = q, q + 8, ... < nup <= 64 of (t, j).  Indexes past
 // the end are clamped (the load stays in bounds) and the value replaced by +0; adding +0 to a sum
 // that starts at +0 changes nothing.
-constexpr int kFinishMaxSplit = 16, kFinishMaxUp = 64;
-__device__ __forceinline__ void load_partials(const float *__restrict__ src, int64_t stride, int n,
-                                              float (&v)[kFinishMaxSplit]) {
+// kFinishMaxSplit partials by default; launches with up to kFinishMaxSplitWide use a wider variant.
+constexpr int kFinishMaxSplit = 16, kFinishMaxSplitWide = 32, kFinishMaxUp = 64;
+template <int PS>
+__device__ __forceinline__ void load_partials(const float *__restrict__ src, int64_t stride, int n, float (&v)[PS]) {
 #pragma unroll
-  for (int q = 0; q < kFinishMaxSplit; ++q) v[q] = src[(int64_t)(q < n ? q : n - 1) * stride];
+  for (int q = 0; q < PS; ++q) v[q] = src[(int64_t)(q < n ? q : n - 1) * stride];
 }
-__device__ __forceinline__ float add_partials(const float (&v)[kFinishMaxSplit], int n) {
+template <int PS>
+__device__ __forceinline__ float add_partials(const float (&v)[PS], int n) {
   float y = 0.f;
 #pragma unroll
-  for (int q = 0; q < kFinishMaxSplit; ++q) y += q < n ? v[q] : 0.f;
+  for (int q = 0; q < PS; ++q) y += q < n ? v[q] : 0.f;
   return y;
 }
 __device__ __forceinline__ float sum_partials(const float *__restrict__ src, int64_t stride, int n) {
@@ -546,7 +565,7 @@ __device__ __forceinline__ float sum_upart(const float *__restrict__ upart, int6
 // Y[t, n] = bf16(sum over p (in order) of part[p][t][n] + V . B[n, :r]).
 // The weight partials and, for r = 8 NBP, the row of B are loaded before the U
 // sums, so that their latency overlaps that of the U partials.
-template <int NBP>
+template <int NBP, int PS>
 __global__ __launch_bounds__(256) void k_gemv_finish(const float *__restrict__ part, const float *__restrict__ upart,
                                                      int nsplit, int nup, int64_t T, int64_t N,
                                                      const bf16_t *__restrict__ B, int64_t r, float s,
@@ -561,7 +580,7 @@ __global__ __launch_bounds__(256) void k_gemv_finish(const float *__restrict__ p
   // loaded (indexes clamped into range) before the first addition
   const int iu = tid < 8 * r ? tid : 8 * (int)r - 1;
   const int64_t nn = nok ? n : N - 1;
-  float uv[kFinishMaxUp / 8], pv[kFinishMaxSplit];
+  float uv[kFinishMaxUp / 8], pv[PS];
   u32x4_t bw[NBP > 0 ? NBP : 1];
   load_upart(upart, T, t, r, iu % r, iu / r, nup, uv);
   load_partials(part + t * N + nn, T * N, nsplit, pv);
@@ -741,13 +760,22 @@ hipError_t launch_gemv_finish(const float *part, const float *upart, int nsplit,
   if (T == 0) return hipSuccess;
   dim3 grid((unsigned)((N + 255) / 256), (unsigned)T);
   const int nup = 4 * (nsplit_u > 0 ? nsplit_u : nsplit);
-  if (nsplit > kFinishMaxSplit || nup > kFinishMaxUp) return hipErrorInvalidValue;
+  if (nsplit > kFinishMaxSplitWide || nup > kFinishMaxUp) return hipErrorInvalidValue;
   const int nbp = (r % 8 == 0 && r <= 32) ? (int)(r / 8) : 0;
-  if (nbp == 4) launch(k_gemv_finish<4>, grid, dim3(256), 0, st, part, upart, nsplit, nup, T, N, B, r, s, Y, U_out);
-  else if (nbp == 3) launch(k_gemv_finish<3>, grid, dim3(256), 0, st, part, upart, nsplit, nup, T, N, B, r, s, Y, U_out);
-  else if (nbp == 2) launch(k_gemv_finish<2>, grid, dim3(256), 0, st, part, upart, nsplit, nup, T, N, B, r, s, Y, U_out);
-  else if (nbp == 1) launch(k_gemv_finish<1>, grid, dim3(256), 0, st, part, upart, nsplit, nup, T, N, B, r, s, Y, U_out);
-  else launch(k_gemv_finish<0>, grid, dim3(256), 0, st, part, upart, nsplit, nup, T, N, B, r, s, Y, U_out);
+#define QLORA_FIN(NBP_, PS_) \
+  launch(k_gemv_finish<NBP_, PS_>, grid, dim3(256), 0, st, part, upart, nsplit, nup, T, N, B, r, s, Y, U_out)
+#define QLORA_FIN_PS(PS_)                       \
+  do {                                          \
+    if (nbp == 4) QLORA_FIN(4, PS_);            \
+    else if (nbp == 3) QLORA_FIN(3, PS_);       \
+    else if (nbp == 2) QLORA_FIN(2, PS_);       \
+    else if (nbp == 1) QLORA_FIN(1, PS_);       \
+    else QLORA_FIN(0, PS_);                     \
+  } while (0)
+  if (nsplit <= kFinishMaxSplit) QLORA_FIN_PS(kFinishMaxSplit);
+  else QLORA_FIN_PS(kFinishMaxSplitWide);
+#undef QLORA_FIN_PS
+#undef QLORA_FIN
   return hipGetLastError();
 }
 
@@ -777,10 +805,29 @@ static int rows_resident() {
   return res;
 }
 
+// 3..16 tokens: one token group, 512-column segments (at most 16); 17..32: two groups, 256-column
+// segments (at most 32, which the wide finish takes)
+static int mrows_mt(int64_t T) { return T <= 16 ? 1 : 2; }
 int nf4_gemv_mrows_nseg(int64_t T, int64_t K) {
-  if (T < 3 || T > kMrowsMaxT || K <= 0 || K % kMrowsSeg != 0) return 0;
-  const int64_t ns = K / kMrowsSeg;
-  return ns <= kFinishMaxSplit ? (int)ns : 0;
+  if (T < 3 || T > kMrowsMaxT || K <= 0) return 0;
+  const int mt = mrows_mt(T), ks = 512 / mt;
+  if (K % ks != 0) return 0;
+  const int64_t ns = K / ks;
+  return ns <= (mt == 1 ? kFinishMaxSplit : kFinishMaxSplitWide) ? (int)ns : 0;
+}
+
+template <int MT>
+static int mrows_resident() {
+  static thread_local int res = 0;
+  if (res > 0) return res;
+  int dev = 0, cus = 0, nb = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_nf4_gemv_mrows<MT>, 256, 0) != hipSuccess || nb < 1 ||
+      cus < 1)
+    return 0;
+  res = nb * cus;
+  return res;
 }
 
 hipError_t launch_nf4_gemv_mrows(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
@@ -790,21 +837,20 @@ hipError_t launch_nf4_gemv_mrows(const bf16_t *X, int64_t T, int64_t K, const ui
   if (T == 0) return hipSuccess;
   const int nseg = nf4_gemv_mrows_nseg(T, K);
   if (nseg <= 0) return hipErrorInvalidValue;
-  static thread_local int res = 0;
-  if (res <= 0) {
-    int dev = 0, cus = 0, nb = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_nf4_gemv_mrows, 256, 0) != hipSuccess || nb < 1 || cus < 1)
-      return hipErrorInvalidDeviceFunction;
-    res = nb * cus;
-  }
+  const int mt = mrows_mt(T);
+  const int res = mt == 1 ? mrows_resident<1>() : mrows_resident<2>();
+  if (res <= 0) return hipErrorInvalidDeviceFunction;
   // main workgroups: what stays resident beside the U workgroups, at most one item per wave, a multiple of nseg
   int64_t g = std::min<int64_t>(std::max(1, res - nsplit_u), ((N + 15) / 16 * nseg + 3) / 4);
   g = std::max<int64_t>(nseg, g / nseg * nseg);
   const int gmain = (int)g;
-  launch(k_nf4_gemv_mrows, dim3((unsigned)(gmain + nsplit_u)), dim3(256), 0, s, X, T, K, codes, absmax_q, step, N,
-         gmain, nseg, nsplit_u, A, r, part, upart, lv);
+  const dim3 grid((unsigned)(gmain + nsplit_u));
+  if (mt == 1)
+    launch(k_nf4_gemv_mrows<1>, grid, dim3(256), 0, s, X, T, K, codes, absmax_q, step, N, gmain, nseg, nsplit_u, A, r,
+           part, upart, lv);
+  else
+    launch(k_nf4_gemv_mrows<2>, grid, dim3(256), 0, s, X, T, K, codes, absmax_q, step, N, gmain, nseg, nsplit_u, A, r,
+           part, upart, lv);
   *nseg_out = nseg;
   return hipGetLastError();
 }
