@@ -420,12 +420,17 @@ __global__ __launch_bounds__(256, TT == 1 ? 8 : 6) void k_nf4_gemv_rows(
 // both operands, so the products are those of the layer.  The decode is
 // k_nf4_gemv's: level pairs from the LDS table, fl32(level * c'), bf16 pack.
 // The next item loads while the current one computes (two fixed slots, the
-// loop unrolled by two).  Main workgroup g owns segment g % nseg, its wave w
-// the row groups 4 (g / nseg) + w + i 4 gmain / nseg.  part is [nseg][T][N];
-// workgroups 0 .. nsplit_u - 1 come first and form the U partials as in
-// k_nf4_gemv_rows.
+// loop unrolled by two).  With RED = 1, main workgroup g owns segment
+// g % nseg, its wave w the row groups 4 (g / nseg) + w + i 4 gmain / nseg, and
+// part is [nseg][T][N].  With RED = 4 (nseg % 4 == 0) the four waves of main
+// workgroup g take the four segments 4 (g % nq) + w of one quarter (nq = nseg /
+// 4) over the same row groups g / nq + i gmain / nq; after each item they
+// exchange their sums through LDS (two buffers, one barrier per item), add
+// them in wave order and write one partial per quarter: part is [nq][T][N],
+// a quarter of the partial bytes.  Workgroups 0 .. nsplit_u - 1 come first
+// and form the U partials as in k_nf4_gemv_rows.
 constexpr int kMrowsMaxT = 32;
-template <int MT>
+template <int MT, int RED>
 __global__ __launch_bounds__(256, 3) void k_nf4_gemv_mrows(
     const bf16_t *__restrict__ X, int64_t T, int64_t K, const uint8_t *__restrict__ codes,
     const uint8_t *__restrict__ absmax_q, const float *__restrict__ step, int64_t N, int gmain, int nseg, int nsplit_u,
@@ -440,10 +445,12 @@ __global__ __launch_bounds__(256, 3) void k_nf4_gemv_mrows(
     lora_u_partial<MT>(X, T, K, A, r, kb, kb + kchunk, upart + (u * 4 + wave) * T * r, wave, lane);
     return;
   }
+  static_assert(RED == 1 || RED == 4, "one wave or the whole workgroup per partial");
   const int a = lane & 15, g = lane >> 4;
-  const int gi = (int)blockIdx.x - nsplit_u, seg = gi % nseg;
+  const int gi = (int)blockIdx.x - nsplit_u, npart = nseg / RED, seg = RED == 1 ? gi % nseg : gi % npart * 4 + wave;
   const int64_t ngroups = (N + 15) / 16;
-  const int64_t rg0 = (int64_t)(gi / nseg) * 4 + wave, rgs = (int64_t)(gmain / nseg) * 4;
+  const int64_t rg0 = RED == 1 ? (int64_t)(gi / nseg) * 4 + wave : (int64_t)(gi / npart);
+  const int64_t rgs = RED == 1 ? (int64_t)(gmain / nseg) * 4 : (int64_t)(gmain / npart);
   const int64_t items = rg0 < ngroups ? (ngroups - rg0 + rgs - 1) / rgs : 0;
   const int64_t col0 = (int64_t)seg * KS + CL * g;  // this lane group's first column
   pair_levels_to_lds(lv, s_tab, tid);
@@ -475,9 +482,11 @@ __global__ __launch_bounds__(256, 3) void k_nf4_gemv_mrows(
     for (int b = 0; b < NB; ++b) sl.sc[b] = load_scale(absmax_q, step, b0 + b);
     if (li + 1 < items) ++li;
   };
-  float *pseg = part + (int64_t)seg * T * N;
+  float *pseg = part + (int64_t)(RED == 1 ? seg : gi % npart) * T * N;
+  // RED = 4: the waves' sums of one item, [buffer][wave][token group][lane]
+  __shared__ __attribute__((aligned(16))) f32x4_t s_red[RED == 4 ? 2 : 1][RED][MT][64];
   int64_t crg = rg0;  // row group of the item being computed
-  auto do_step = [&](Slot &cur, Slot &refill) {
+  auto do_step = [&](Slot &cur, Slot &refill, int buf) {
     load_slot(refill);
     f32x4_t acc[MT];
 #pragma unroll
@@ -493,24 +502,42 @@ __global__ __launch_bounds__(256, 3) void k_nf4_gemv_mrows(
       for (int m = 0; m < MT; ++m) acc[m] = mfma_16x16x32(xa[m][s], bop, acc[m]);
     }
     // element e of lane l in token group m: token 16 m + 4 (l >> 4) + e, weight row 16 crg + (l & 15)
-    const int64_t n = crg * 16 + a;
+    if constexpr (RED == 1) {
+      const int64_t n = crg * 16 + a;
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+      for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t t = 16 * m + 4 * g + e;
-        if (n < N && t < T) pseg[t * N + n] = acc[m][e];
+        for (int e = 0; e < 4; ++e) {
+          const int64_t t = 16 * m + 4 * g + e;
+          if (n < N && t < T) pseg[t * N + n] = acc[m][e];
+        }
+    } else {
+      // wave w adds, for lanes 16 w .. 16 w + 15 of every wave, their four elements: thread l takes
+      // lane 16 w + (l >> 2), element l & 3, i.e. token 16 m + 4 w + (l & 3), row 16 crg + (l >> 2)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) s_red[buf][wave][m][lane] = acc[m];
+      __syncthreads();
+      const int64_t n = crg * 16 + (lane >> 2);
+      const float *rd = reinterpret_cast<const float *>(&s_red[buf][0][0][0]) + (16 * wave + (lane >> 2)) * 4 + (lane & 3);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        float y = rd[m * 256];
+#pragma unroll
+        for (int v = 1; v < RED; ++v) y += rd[(v * MT + m) * 256];
+        const int64_t t = 16 * m + 4 * wave + (lane & 3);
+        if (n < N && t < T) pseg[t * N + n] = y;
       }
+    }
     crg += rgs;
   };
   Slot s0, s1;
   load_slot(s0);
   int64_t f = 0;
   for (; f + 1 < items; f += 2) {
-    do_step(s0, s1);
-    do_step(s1, s0);
+    do_step(s0, s1, 0);
+    do_step(s1, s0, RED == 4 ? 1 : 0);
   }
-  if (f < items) do_step(s0, s1);
+  if (f < items) do_step(s0, s1, 0);
 }
 
 // Sums of the finishing kernels, in index order with every load issued first (a loop bound known only
@@ -808,6 +835,9 @@ static int rows_resident() {
 // 3..16 tokens: one token group, 512-column segments (at most 16); 17..32: two groups, 256-column
 // segments (at most 32, which the wide finish takes)
 static int mrows_mt(int64_t T) { return T <= 16 ? 1 : 2; }
+// four segments per partial wherever the segments come in fours (a quarter of the partial bytes for
+// one barrier per item)
+static int mrows_red(int nseg) { return nseg % 4 == 0 ? 4 : 1; }
 int nf4_gemv_mrows_nseg(int64_t T, int64_t K) {
   if (T < 3 || T > kMrowsMaxT || K <= 0) return 0;
   const int mt = mrows_mt(T), ks = 512 / mt;
@@ -816,14 +846,14 @@ int nf4_gemv_mrows_nseg(int64_t T, int64_t K) {
   return ns <= (mt == 1 ? kFinishMaxSplit : kFinishMaxSplitWide) ? (int)ns : 0;
 }
 
-template <int MT>
+template <int MT, int RED>
 static int mrows_resident() {
   static thread_local int res = 0;
   if (res > 0) return res;
   int dev = 0, cus = 0, nb = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_nf4_gemv_mrows<MT>, 256, 0) != hipSuccess || nb < 1 ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_nf4_gemv_mrows<MT, RED>, 256, 0) != hipSuccess || nb < 1 ||
       cus < 1)
     return 0;
   res = nb * cus;
@@ -837,21 +867,26 @@ hipError_t launch_nf4_gemv_mrows(const bf16_t *X, int64_t T, int64_t K, const ui
   if (T == 0) return hipSuccess;
   const int nseg = nf4_gemv_mrows_nseg(T, K);
   if (nseg <= 0) return hipErrorInvalidValue;
-  const int mt = mrows_mt(T);
-  const int res = mt == 1 ? mrows_resident<1>() : mrows_resident<2>();
+  const int mt = mrows_mt(T), red = mrows_red(nseg), npart = nseg / red;
+  const int res = mt == 1 ? (red == 1 ? mrows_resident<1, 1>() : mrows_resident<1, 4>())
+                          : (red == 1 ? mrows_resident<2, 1>() : mrows_resident<2, 4>());
   if (res <= 0) return hipErrorInvalidDeviceFunction;
-  // main workgroups: what stays resident beside the U workgroups, at most one item per wave, a multiple of nseg
-  int64_t g = std::min<int64_t>(std::max(1, res - nsplit_u), ((N + 15) / 16 * nseg + 3) / 4);
-  g = std::max<int64_t>(nseg, g / nseg * nseg);
+  // main workgroups: what stays resident beside the U workgroups, at most one item per wave, a multiple
+  // of the number of partials (with RED = 4 every workgroup's waves share their items)
+  const int64_t per_item = red == 1 ? 4 : 1;
+  int64_t g = std::min<int64_t>(std::max(1, res - nsplit_u), ((N + 15) / 16 * npart + per_item - 1) / per_item);
+  g = std::max<int64_t>(npart, g / npart * npart);
   const int gmain = (int)g;
   const dim3 grid((unsigned)(gmain + nsplit_u));
+  auto go = [&](auto kern) {
+    launch(kern, grid, dim3(256), 0, s, X, T, K, codes, absmax_q, step, N, gmain, nseg, nsplit_u, A, r, part, upart,
+           lv);
+  };
   if (mt == 1)
-    launch(k_nf4_gemv_mrows<1>, grid, dim3(256), 0, s, X, T, K, codes, absmax_q, step, N, gmain, nseg, nsplit_u, A, r,
-           part, upart, lv);
+    red == 1 ? go(k_nf4_gemv_mrows<1, 1>) : go(k_nf4_gemv_mrows<1, 4>);
   else
-    launch(k_nf4_gemv_mrows<2>, grid, dim3(256), 0, s, X, T, K, codes, absmax_q, step, N, gmain, nseg, nsplit_u, A, r,
-           part, upart, lv);
-  *nseg_out = nseg;
+    red == 1 ? go(k_nf4_gemv_mrows<2, 1>) : go(k_nf4_gemv_mrows<2, 4>);
+  *nseg_out = npart;
   return hipGetLastError();
 }
 
