@@ -258,7 +258,7 @@ Plan make_plan(int op, int64_t T, int64_t N, int64_t K, int32_t r) {
     } else if (op == QLORA_OP_FWD && use_gemv(T, K) && nf4_gemv_mrows_nseg(T, K) > 0) {  // 3..32 tokens
       p.gemv = p.gemv_mrows = true;
       p.gemv_split = gemv_rows_usplit(K);
-      part = up((size_t)nf4_gemv_mrows_nseg(T, K) * T * N * 4, kAlign);  // at most one partial per segment
+      part = up((size_t)nf4_gemv_mrows_nparts(T, K) * T * N * 4, kAlign);  // one per segment or per four
       p.off_upart = part;
       part += (size_t)4 * p.gemv_split * T * r * 4;
     } else if ((op == QLORA_OP_FWD || op == QLORA_OP_FWD_MULTI) && use_gemv(T, K)) {  // dropout: the tiled path

@@ -832,18 +832,22 @@ static int rows_resident() {
   return res;
 }
 
-// 3..16 tokens: one token group, 512-column segments (at most 16); 17..32: two groups, 256-column
-// segments (at most 32, which the wide finish takes)
+// 3..16 tokens: one token group, 512-column segments; 17..32: two groups, 256-column segments
 static int mrows_mt(int64_t T) { return T <= 16 ? 1 : 2; }
 // four segments per partial wherever the segments come in fours (a quarter of the partial bytes for
 // one barrier per item)
-static int mrows_red(int nseg) { return nseg % 4 == 0 ? 4 : 1; }
+static int mrows_red(int64_t nseg) { return nseg % 4 == 0 ? 4 : 1; }
+// at most 32 partials, which the wide finish takes: 128 segments in fours, else 32
 int nf4_gemv_mrows_nseg(int64_t T, int64_t K) {
   if (T < 3 || T > kMrowsMaxT || K <= 0) return 0;
   const int mt = mrows_mt(T), ks = 512 / mt;
   if (K % ks != 0) return 0;
   const int64_t ns = K / ks;
-  return ns <= (mt == 1 ? kFinishMaxSplit : kFinishMaxSplitWide) ? (int)ns : 0;
+  return ns / mrows_red(ns) <= kFinishMaxSplitWide ? (int)ns : 0;
+}
+int nf4_gemv_mrows_nparts(int64_t T, int64_t K) {
+  const int ns = nf4_gemv_mrows_nseg(T, K);
+  return ns / mrows_red(ns > 0 ? ns : 1);
 }
 
 template <int MT, int RED>

@@ -375,14 +375,16 @@ def test_small_token_forward(n_out, T):
 @pytest.mark.parametrize("n_out,n_in,T,r", [(72, 512, 3, 16), (8, 1536, 16, 4), (1000, 4096, 9, 1),
                                             (24, 8192, 16, 64), (136, 8704, 5, 8), (72, 512, 32, 16),
                                             (8, 8192, 24, 8), (520, 1536, 17, 4), (24, 8448, 20, 8),
-                                            (136, 1024, 19, 16), (40, 3072, 32, 8), (1000, 2048, 25, 16)])
+                                            (136, 1024, 19, 16), (40, 3072, 32, 8), (1000, 2048, 25, 16),
+                                            (24, 28672, 8, 8), (40, 16384, 20, 4), (8, 32768, 32, 8),
+                                            (8, 65536, 4, 8), (8, 66560, 4, 8), (8, 33024, 24, 4)])
 def test_row_group_forward(n_out, n_in, T, r):
     """3..32 tokens through the row-group kernel (16 rows per wave, activations in registers): one token
-    group and segments of 512 columns (at most 16) up to 16 tokens, two groups and segments of 256 (at most
-    32, which the finish takes in its wide variant) beyond -- from one segment with a ragged row group to the
-    maximum -- and the shapes past the maximum (n_in 8704 at 5 tokens, 8448 at 20), which take the MFMA
-    kernel.  Beyond 16 tokens with a segment count divisible by 4 the workgroup's four waves add their
-    segments before writing (n_in 1024, 2048, 3072 and 8192: 1, 2, 3 and 8 partials); checked in full."""
+    group and segments of 512 columns up to 16 tokens, two groups and segments of 256 beyond.  When the
+    segment count is divisible by 4 the workgroup's four waves add their segments before writing (n_in 1024,
+    2048, 3072, 8192, 28672, 32768 and 65536: 1 to 32 partials); otherwise each segment is a partial (n_in
+    512, 1536, 8704: 1, 3 and 17).  At most 32 partials reach the finish kernel; the shapes past that (8448
+    and 33024 at 20-24 tokens, 66560 at 4) take the MFMA kernel; checked in full."""
     print(f"row-group forward {n_out}x{n_in} T={T} r={r}", flush=True)
     inp = linear_inputs(n_out, n_in, T, r, 2.0 * r, seed=n_out + 3 * T, sigma_ab=0.05)
     w = Bd.quantize_nf4(torch.from_numpy(inp.W).to(dev()))
