@@ -740,6 +740,8 @@ int nf4_gemm_pick_tile(int64_t M, int64_t N) {
   auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   if (tiles(256, 256) >= 256) return NF4_TILE_256x256_W8;
   if (tiles(256, 128) >= 256) return NF4_TILE_256x128_W8;
+  // at most 128 rows over a wide output: 64x64 per wave where the 128x256 tiles still number 96 or more
+  if (M <= 128 && tiles(128, 256) >= 96) return NF4_TILE_128x256_W8;
   return NF4_TILE_128x128_W8;
 }
 

@@ -178,6 +178,10 @@ SPLIT_FORWARD = [
     # forward GEMM splits its reduction into ranges (binary32 partial sums, added in order by a finalize)
     (1024, 2048, 128, 16, 32.0),  # 8 tiles, 32 steps: 4 ranges
     (520, 1024, 100, 128, 16.0),  # ragged tokens and rows, rank 128 (two LoRA steps in range 0): 2 ranges
+    # at most 128 tokens over 96 or more 128x256 tiles take that tile: the forward here (2 ranges), the
+    # backward's dX with n_in 24576 below
+    (24576, 2048, 120, 16, 32.0),
+    (512, 24576, 100, 8, 16.0),
 ]
 
 
