@@ -221,7 +221,7 @@ struct Plan {
   bool gemv = false;  // forward through the small-token kernels
   int gemv_rg = 0, gemv_w = 0, gemv_split = 0, gemv_main = 0;
   bool gemv_rows = false;  // one or two tokens: the row-streaming kernel (gemv_split = its U K ranges)
-  bool gemv_mrows = false; // 3..32 tokens: the row-group kernel (gemv_split = its U K ranges)
+  bool gemv_mrows = false; // 3..64 tokens: the row-group kernel (gemv_split = its U K ranges)
   int fwd_split = 1;       // reduction ranges of the tiled forward GEMM (partial sums in the part region)
   size_t off_upart = 0;
 };
@@ -255,7 +255,7 @@ Plan make_plan(int op, int64_t T, int64_t N, int64_t K, int32_t r) {
       part = up((size_t)nf4_gemv_rows_nseg(T, K) * T * N * 4, kAlign);  // one partial per row segment
       p.off_upart = part;
       part += (size_t)4 * p.gemv_split * T * r * 4;
-    } else if (op == QLORA_OP_FWD && use_gemv(T, K) && nf4_gemv_mrows_nseg(T, K) > 0) {  // 3..32 tokens
+    } else if (op == QLORA_OP_FWD && use_gemv(T, K) && nf4_gemv_mrows_nseg(T, K) > 0) {  // 3..64 tokens
       p.gemv = p.gemv_mrows = true;
       p.gemv_split = gemv_rows_usplit(K);
       part = up((size_t)nf4_gemv_mrows_nparts(T, K) * T * N * 4, kAlign);  // one per segment or per four
@@ -437,7 +437,7 @@ int linear_fwd(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const qlora_b
     LAUNCH("gemv_finish", launch_gemv_finish(part, upart, nseg, T, N, B, r, sc, Y, U_out, s, p.gemv_split));
     return QLORA_OK;
   }
-  if (p.gemv_mrows) {  // 3..32 tokens: bound by the weight stream, 16 rows per wave, activations in registers
+  if (p.gemv_mrows) {  // 3..64 tokens: bound by the weight stream, 16 rows per wave, activations in registers
     float *upart = (float *)(w + p.off_part + p.off_upart);
     int nseg = 1;
     LAUNCH("nf4_gemv", launch_nf4_gemv_mrows(X, T, K, q->codes, q->absmax_q, q->absmax_step, N, p.gemv_split, A, r,

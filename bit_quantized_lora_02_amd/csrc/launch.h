@@ -91,7 +91,7 @@ hipError_t launch_gemv_finish(const float *part, const float *upart, int nsplit,
 // partials of nseg row segments (part [nseg][T][N], nseg = nf4_gemv_rows_nseg(T, K), also returned in
 // *nseg_out) plus the U partials of nsplit_u K ranges (upart [4 nsplit_u][T][r]).
 int nf4_gemv_rows_nseg(int64_t T, int64_t K);  // 0: the kernel does not take (T, K)
-// Row-group GEMV for 3..32 tokens (segments of 512 columns up to 16 tokens, of 256 beyond; at most 32
+// Row-group GEMV for 3..64 tokens (segments of 512 columns up to 16 tokens, 256 up to 32, 128 beyond; at most 32
 // partials): binary32 partials of the nseg = nf4_gemv_mrows_nseg(T, K) segments (part [nseg][T][N]), or of
 // their fours when nseg % 4 == 0 (part [nseg / 4][T][N]), plus the U partials as above; *nseg_out is the
 // number of partials written.

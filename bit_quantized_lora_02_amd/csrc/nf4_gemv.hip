@@ -406,9 +406,10 @@ __global__ __launch_bounds__(256, TT == 1 ? 8 : 6) void k_nf4_gemv_rows(
   if (f < items) do_step(s0, s1);
 }
 
-// ------------------------------------------- the row-group GEMV (3..32 tokens)
+// ------------------------------------------- the row-group GEMV (3..64 tokens)
 // The MFMA formulation of k_nf4_gemv with the row kernel's layout, for MT
-// groups of 16 tokens (MT = 1: up to 16 tokens, MT = 2: up to 32).  A work item
+// groups of 16 tokens (MT = 1: up to 16 tokens, MT = 2: up to 32, MT = 4: up
+// to 64; with MT = 4 a lane group's 32 columns lie in one block).  A work item
 // is 16 weight rows over one segment of KS = 512 / MT columns (nseg = K / KS
 // segments, one per workgroup for the whole launch).  Lane (a, g) = (l & 15,
 // l >> 4) keeps tokens 16 m + a's activations at segment columns CL g .. CL g +
@@ -429,14 +430,14 @@ __global__ __launch_bounds__(256, TT == 1 ? 8 : 6) void k_nf4_gemv_rows(
 // them in wave order and write one partial per quarter: part is [nq][T][N],
 // a quarter of the partial bytes.  Workgroups 0 .. nsplit_u - 1 come first
 // and form the U partials as in k_nf4_gemv_rows.
-constexpr int kMrowsMaxT = 32;
+constexpr int kMrowsMaxT = 64;
 template <int MT, int RED>
 __global__ __launch_bounds__(256, 3) void k_nf4_gemv_mrows(
     const bf16_t *__restrict__ X, int64_t T, int64_t K, const uint8_t *__restrict__ codes,
     const uint8_t *__restrict__ absmax_q, const float *__restrict__ step, int64_t N, int gmain, int nseg, int nsplit_u,
     const bf16_t *__restrict__ A, int64_t r, float *__restrict__ part, float *__restrict__ upart, Levels lv) {
   constexpr int KS = 512 / MT, CL = 128 / MT, NS = CL / 8;  // segment, lane-group columns, MFMA steps per item
-  constexpr int NW = CL / 32, NB = CL / 64;                  // 16-byte code loads and blocks per lane and item
+  constexpr int NW = CL / 32, NB = CL >= 64 ? CL / 64 : 1;  // 16-byte code loads and blocks per lane and item
   __shared__ __attribute__((aligned(16))) float2 s_tab[256];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -832,17 +833,20 @@ static int rows_resident() {
   return res;
 }
 
-// 3..16 tokens: one token group, 512-column segments; 17..32: two groups, 256-column segments
-static int mrows_mt(int64_t T) { return T <= 16 ? 1 : 2; }
+// 3..16 tokens: one token group, 512-column segments; 17..32: two groups, 256-column segments; 33..64:
+// four groups, 128-column segments
+static int mrows_mt(int64_t T) { return T <= 16 ? 1 : T <= 32 ? 2 : 4; }
 // four segments per partial wherever the segments come in fours (a quarter of the partial bytes for
 // one barrier per item)
 static int mrows_red(int64_t nseg) { return nseg % 4 == 0 ? 4 : 1; }
-// at most 32 partials, which the wide finish takes: 128 segments in fours, else 32
+// at most 32 partials, which the wide finish takes: 128 segments in fours, else 32 (four token groups:
+// segments in fours only)
 int nf4_gemv_mrows_nseg(int64_t T, int64_t K) {
   if (T < 3 || T > kMrowsMaxT || K <= 0) return 0;
   const int mt = mrows_mt(T), ks = 512 / mt;
   if (K % ks != 0) return 0;
   const int64_t ns = K / ks;
+  if (mt == 4 && ns % 4 != 0) return 0;  // four token groups only with the workgroup sum (registers)
   return ns / mrows_red(ns) <= kFinishMaxSplitWide ? (int)ns : 0;
 }
 int nf4_gemv_mrows_nparts(int64_t T, int64_t K) {
@@ -872,8 +876,9 @@ hipError_t launch_nf4_gemv_mrows(const bf16_t *X, int64_t T, int64_t K, const ui
   const int nseg = nf4_gemv_mrows_nseg(T, K);
   if (nseg <= 0) return hipErrorInvalidValue;
   const int mt = mrows_mt(T), red = mrows_red(nseg), npart = nseg / red;
-  const int res = mt == 1 ? (red == 1 ? mrows_resident<1, 1>() : mrows_resident<1, 4>())
-                          : (red == 1 ? mrows_resident<2, 1>() : mrows_resident<2, 4>());
+  const int res = mt == 1   ? (red == 1 ? mrows_resident<1, 1>() : mrows_resident<1, 4>())
+                  : mt == 2 ? (red == 1 ? mrows_resident<2, 1>() : mrows_resident<2, 4>())
+                            : mrows_resident<4, 4>();
   if (res <= 0) return hipErrorInvalidDeviceFunction;
   // main workgroups: what stays resident beside the U workgroups, at most one item per wave, a multiple
   // of the number of partials (with RED = 4 every workgroup's waves share their items)
@@ -888,8 +893,10 @@ hipError_t launch_nf4_gemv_mrows(const bf16_t *X, int64_t T, int64_t K, const ui
   };
   if (mt == 1)
     red == 1 ? go(k_nf4_gemv_mrows<1, 1>) : go(k_nf4_gemv_mrows<1, 4>);
-  else
+  else if (mt == 2)
     red == 1 ? go(k_nf4_gemv_mrows<2, 1>) : go(k_nf4_gemv_mrows<2, 4>);
+  else
+    go(k_nf4_gemv_mrows<4, 4>);
   *nseg_out = npart;
   return hipGetLastError();
 }

@@ -381,10 +381,14 @@ def test_small_token_forward(n_out, T):
                                             (8, 8192, 24, 8), (520, 1536, 17, 4), (24, 8448, 20, 8),
                                             (136, 1024, 19, 16), (40, 3072, 32, 8), (1000, 2048, 25, 16),
                                             (24, 28672, 8, 8), (40, 16384, 20, 4), (8, 32768, 32, 8),
-                                            (8, 65536, 4, 8), (8, 66560, 4, 8), (8, 33024, 24, 4)])
+                                            (8, 65536, 4, 8), (8, 66560, 4, 8), (8, 33024, 24, 4),
+                                            (72, 1024, 33, 16), (136, 8192, 64, 8), (40, 1152, 48, 4),
+                                            (8, 16384, 64, 4), (8, 16512, 40, 4)])
 def test_row_group_forward(n_out, n_in, T, r):
-    """3..32 tokens through the row-group kernel (16 rows per wave, activations in registers): one token
-    group and segments of 512 columns up to 16 tokens, two groups and segments of 256 beyond.  When the
+    """3..64 tokens through the row-group kernel (16 rows per wave, activations in registers): one token
+    group and segments of 512 columns up to 16 tokens, two groups and segments of 256 up to 32, four groups
+    and segments of 128 beyond, only when the segments come in fours (n_in 1024, 8192, 16384: 2, 16 and 32
+    partials; 1152 and 16512: 9 and 129 segments, the MFMA kernel).  When the
     segment count is divisible by 4 the workgroup's four waves add their segments before writing (n_in 1024,
     2048, 3072, 8192, 28672, 32768 and 65536: 1 to 32 partials); otherwise each segment is a partial (n_in
     512, 1536, 8704: 1, 3 and 17).  At most 32 partials reach the finish kernel; the shapes past that (8448
