@@ -1,20 +1,23 @@
 #!/usr/bin/env python3
 """Benchmark of the NF4 + LoRA linear on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config attn_4096]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config layer_70b]
 
-A step is one training pass of the layer over one batch: forward (U = X A^T,
-Y = X W'^T + s U B^T) and backward (dU, dB, dA, dX) through the C ABI, with
-every input already in HBM.  Quantization happens once before timing (the
-method quantizes at load time) and is reported separately as quantize_ms.
-The default workload is the attention-projection linear: NF4 W 4096 x 4096,
-T = 2048 tokens, r = 16, alpha = 32.  ``--config small_token`` times the
-forward alone, as that workload is defined.
+A step is one training pass over one batch: forward (U = X A^T,
+Y = X W'^T + s U B^T) and backward (dU, dB, dA, dX) through the C ABI for
+every linear of the workload, with every input already in HBM.  Quantization
+happens once before timing (the method quantizes at load time) and is reported
+separately as quantize_ms.  The default workload is the largest one that fits
+one GPU: one 70B-class decoder layer, seven NF4 linears (q, o 8192x8192; k, v
+1024x8192; gate, up 28672x8192; down 8192x28672), T = 4096 tokens, r = 64,
+alpha = 16.  ``--config small_token`` times the forward alone, as that
+workload is defined.
 
 Prints one JSON line: throughput in TFLOP/s of algorithmic work
 (fwd 2TNK + 2Tr(K+N), bwd 2TNK + 4Tr(K+N)), the 4-bit weight-stream GB/s, a
-roofline entry for the dominant kernel timed live with HIP events recorded
-around its launches, and the CPU oracle timed on a bounded sample.
+roofline entry for the dominant kernel timed live by events its own dispatch
+stamps (average, median, p10 and p90 per launch), a dense bf16 GEMM of the same
+shapes as context, and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -43,9 +46,10 @@ WORKLOAD_TEXT = {
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="attn_4096", choices=["attn_4096", "mlp_8b", "layer_70b", "small_token"])
+    ap.add_argument("--steps", type=int, default=0,
+                    help="timed steps (default: 100, or 500 for the microsecond-scale small_token forward)")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="layer_70b", choices=["attn_4096", "mlp_8b", "layer_70b", "small_token"])
     ap.add_argument("--tokens", type=int, default=1, help="T for --config small_token")
     ap.add_argument("--wide", action="store_true", help="28672x8192 instead of 8192x8192 for small_token")
     ap.add_argument("--copies", type=int, default=0,
@@ -61,7 +65,9 @@ def parse():
                          "segments (many-adapter batching; forward only)")
     ap.add_argument("--merge", action="store_true",
                     help="time the export merge W' + s B A (NF4 base, bf16 out) of every linear instead of a step")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-context-gemm", action="store_true",
+                    help="skip the dense bf16 torch.mm of the same shapes (context for the fused GEMMs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 256 MiB (scales rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -187,38 +193,122 @@ def linears_for(args):
     return c["linears"], c["T"], c["r"], c["alpha"], c["outliers"], True
 
 
-def cpu_baseline(inp, train: bool, target_s: float):
-    """The oracle as it is, on the first linear, for a token slice sized to ~target_s seconds."""
-    import numpy as np
+def cpu_baseline(inps, train: bool, target_s: float, slice_cap: int):
+    """The oracle as it is (binary64 C, OpenMP over the host cores) on a bounded sample of the workload.
 
+    Every linear's weight is quantized in full, as at load time.  Then every linear runs forward (and,
+    for training workloads, backward) on the first ts tokens, ts <= slice_cap, sized so that the whole
+    leg takes about target_s; each pass also dequantizes its weight once.  The contractions are linear in
+    T and the dequantization is not, so the full step's CPU time is extrapolated as
+    passes x dequantize + slice time x T / ts, and marked as extrapolated when ts < T."""
     import oracle
-    n_out, n_in = inp.W.shape
-    r = inp.A.shape[0]
-    T = inp.X.shape[0]
-    oc, oq, od = oracle.quantize_nf4(inp.W)
-    Wd = oracle.dequant(oc, oq, od, n_out, n_in)
+    T = inps[0].X.shape[0]
+    alpha = inps[0].alpha
+    r = inps[0].A.shape[0]
+    t_q = t_d = 0.0
+    wds = []
+    for inp in inps:
+        n_out, n_in = inp.W.shape
+        t0 = time.perf_counter()
+        oc, oq, od = oracle.quantize_nf4(inp.W)
+        t1 = time.perf_counter()
+        wds.append(oracle.dequant(oc, oq, od, n_out, n_in))
+        t_q += t1 - t0
+        t_d += time.perf_counter() - t1
+    passes = 2 if train else 1
 
     def run(ts):
-        X = inp.X[:ts]
         t0 = time.perf_counter()
-        oracle.linear_fwd(X, Wd, inp.A, inp.B, inp.alpha)
-        if train:
-            oracle.linear_bwd(X, inp.dY[:ts], Wd, inp.A, inp.B, inp.alpha)
+        for inp, Wd in zip(inps, wds):
+            oracle.linear_fwd(inp.X[:ts], Wd, inp.A, inp.B, alpha)
+            if train:
+                oracle.linear_bwd(inp.X[:ts], inp.dY[:ts], Wd, inp.A, inp.B, alpha)
         return time.perf_counter() - t0
 
-    ts = min(T, 8)
+    cap = max(1, min(T, slice_cap))
+    ts = min(cap, 4)
     dt = run(ts)
-    ts = int(max(1, min(T, ts * target_s / max(dt, 1e-3))))
+    budget = max(2.0, target_s - t_q - t_d)
+    ts = int(max(1, min(cap, ts * budget / max(dt, 1e-3))))
     dt = run(ts)
     reps = 1
-    while dt < target_s and ts == T:  # the whole batch is quicker than the target: repeat the pass
+    while dt < budget and ts == T:  # the whole batch is quicker than the target: repeat the pass
         dt += run(ts)
         reps += 1
-    fl = reps * flops_linear(ts, n_out, n_in, r, train)
+    slice_s = dt / reps
+    step_s = passes * t_d + slice_s * T / ts
+    fl_step = sum(flops_linear(T, inp.W.shape[0], inp.W.shape[1], r, train) for inp in inps)
     kind = "fwd+bwd" if train else "fwd"
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{reps} x {kind} of the {n_out}x{n_in} linear on the first {ts} of {T} tokens "
-                      f"({dt:.1f} s, binary64 C oracle, OpenMP)", "seconds": dt, "tokens": ts, "passes": reps}
+    return {"value": fl_step / step_s / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"quantize of all {len(inps)} weights in full ({t_q:.1f} s); {kind} of every linear on the "
+                      f"first {ts} of {T} tokens ({reps} x {slice_s:.1f} s) plus one dequantization per pass "
+                      f"({t_d:.1f} s per pass); binary64 C oracle, OpenMP"
+                      + (f"; the full step's {step_s:.1f} s is extrapolated linearly in T" if ts < T else ""),
+            "extrapolated": ts < T, "step_seconds": step_s, "quantize_seconds": t_q, "slice_tokens": ts,
+            "slice_seconds": slice_s, "passes": reps}
+
+
+def pct(xs, q):
+    """q-th percentile (0..100) of a list, linear interpolation."""
+    import numpy as np
+    return float(np.percentile(np.asarray(xs, np.float64), q)) if xs else None
+
+
+def launch_stats(times, per_step):
+    """Per-launch times of one kernel (ms, launch order) split by their place in the step (one launch per
+    linear per step): median, p10, p90 and average of each place."""
+    out = []
+    for i in range(per_step):
+        xs = times[i::per_step]
+        out.append({"launches": len(xs), "median_ms": pct(xs, 50), "p10_ms": pct(xs, 10), "p90_ms": pct(xs, 90),
+                    "avg_ms": sum(xs) / len(xs) if xs else None})
+    return out
+
+
+def context_gemm(B, layers, T, train, steps, warmup):
+    """Dense bf16 torch.mm (hipBLASLt) on the same shapes with each linear's dequantized weight stored as
+    a dense bf16 matrix: X [T, K] . W'^T (forward) and dY [T, N] . W' (dX); no decode, no LoRA term.
+    Both operands are contiguous row-major.  Context for the fused GEMMs only."""
+    import torch
+    dev = layers[0]["A"].device
+    jobs = []
+    for L in layers:
+        W = B.dequant(L["copies"][0]["w"])
+        Ws = [W, W.clone()]
+        WTs = [w.t().contiguous() for w in Ws]
+        c0 = L["copies"][0]
+        Y = torch.empty((T, L["n_out"]), dtype=torch.bfloat16, device=dev)
+        jobs.append(("fwd", L, c0["X"], WTs, Y, 2 * T * L["n_out"] * L["n_in"]))
+        if train:
+            dX = torch.empty((T, L["n_in"]), dtype=torch.bfloat16, device=dev)
+            jobs.append(("dx", L, c0["dY"], Ws, dX, 2 * T * L["n_out"] * L["n_in"]))
+    ev = {i: [] for i in range(len(jobs))}
+    for it in range(warmup + steps):
+        for i, (kind, L, A_, Bs, out, _) in enumerate(jobs):
+            if it >= warmup:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                torch.mm(A_, Bs[it % 2], out=out)
+                e1.record()
+                ev[i].append((e0, e1))
+            else:
+                torch.mm(A_, Bs[it % 2], out=out)
+    torch.cuda.synchronize()
+    res = {"what": "torch.mm bf16 (hipBLASLt) on the same shapes, dense bf16 weight (no decode, no LoRA term), "
+                   "median per launch over the timed steps", "per_linear": []}
+    tot = {"fwd": [0.0, 0.0], "dx": [0.0, 0.0]}
+    for i, (kind, L, *_, fl) in enumerate(jobs):
+        ms = [a.elapsed_time(b) for a, b in ev[i]]
+        med = pct(ms, 50)
+        tot[kind][0] += fl
+        tot[kind][1] += med
+        res["per_linear"].append({"linear": L["name"], "pass": kind, "median_ms": med, "p10_ms": pct(ms, 10),
+                                  "p90_ms": pct(ms, 90), "tflops": fl / (med * 1e-3) / 1e12})
+    for kind, (fl, ms) in tot.items():
+        if ms:
+            res[kind + "_tflops"] = fl / (ms * 1e-3) / 1e12
+            res[kind + "_frac_peak"] = res[kind + "_tflops"] / PEAK_BF16_TFLOPS
+    return res
 
 
 def flops_linear(T, N, K, r, train):
@@ -332,6 +422,22 @@ def bench_multi(args, B, layers, T, r, alpha, lins):
                       "kernels": kernels}))
 
 
+def gpu_clocks():
+    """Current GPU clocks as rocm-smi reports them (None where it is missing or fails)."""
+    import shutil
+    import subprocess
+    exe = shutil.which("rocm-smi") or ("/opt/rocm/bin/rocm-smi" if os.path.exists("/opt/rocm/bin/rocm-smi") else None)
+    if not exe:
+        return None
+    try:
+        out = subprocess.run([exe, "--showclocks", "--json"], capture_output=True, text=True, timeout=20).stdout
+        d = json.loads(out)
+        card = next(iter(d.values()))
+        return {k: v for k, v in card.items() if "clock" in k.lower() or k.lower().endswith("clk")} or card
+    except Exception as e:  # a missing tool or a format change must not end the bench
+        return {"error": str(e)[:200]}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -367,6 +473,8 @@ def main():
         return
 
     lins, T, r, alpha, outliers, train = linears_for(args)
+    if args.steps <= 0:
+        args.steps = 100 if train or T > 64 else 500
     drop = args.dropout
     if drop and (not train or not 0.0 < drop < 1.0):
         print("--dropout needs a training config and 0 < p < 1", file=sys.stderr)
@@ -375,12 +483,11 @@ def main():
         per_copy = sum(weight_bytes(n, k) + 2 * T * (n + k) * (2 if train else 1) for _, n, k in lins)
         args.copies = int(min(32, max(2, -(-(512 << 20) // per_copy))))
     layers = []
-    first_inp = None
+    inps = []
     t_quant = 0.0
     for li, (name, n_out, n_in) in enumerate(lins):
         inp = linear_inputs(n_out, n_in, T, r, alpha, seed=li, outlier_frac=outliers, make_dy=train)
-        if first_inp is None:
-            first_inp = inp
+        inps.append(inp)
         Wg = torch.from_numpy(inp.W).to(dev)
         g = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
         torch.cuda.synchronize()
@@ -460,7 +567,8 @@ def main():
     elapsed = time.perf_counter() - t0
     for k in timed:
         B.timing_enable(k, False)
-    ktimes = {k: B.timing_read(k) for k in timed}
+    each = {k: B.timing_read_each(k, cap=1 << 20) for k in timed}
+    ktimes = {k: (len(v), sum(v)) for k, v in each.items()}
 
     ms_step = elapsed / args.steps * 1e3
     fl_step = sum(flops_linear(T, L["n_out"], L["n_in"], r, train) for L in layers)
@@ -499,6 +607,13 @@ def main():
                       "tflops": kflops[k] / (ms / args.steps * 1e-3) / 1e12 if ms and kflops[k] else None,
                       "gbps": kbytes[k] / (ms / args.steps * 1e-3) / 1e9 if ms else None,
                       "launches_per_step": per_step_launches}
+        if per_step_launches == len(layers):  # one launch per linear per step: statistics per linear
+            st = launch_stats(each[k], len(layers))
+            med_step = sum(x["median_ms"] for x in st)
+            kernels[k]["per_linear"] = [dict(linear=L["name"], **x) for L, x in zip(layers, st)]
+            kernels[k]["median_ms_per_step"] = med_step
+            kernels[k]["tflops_median"] = kflops[k] / (med_step * 1e-3) / 1e12 if kflops[k] else None
+            kernels[k]["gbps_median"] = kbytes[k] / (med_step * 1e-3) / 1e9
     dom = max((k for k in kernels if k not in ("adamw", "adamw8")), key=lambda k: kernels[k]["ms_per_step"])
     kd = kernels[dom]
     wl = args.config if args.config != "small_token" else f"small_token_{lins[0][1]}x8192_T{T}"
@@ -509,15 +624,28 @@ def main():
         roof = {"bound": "mfma", "achieved": kd["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": kd["tflops"] / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": dom,
                 "avg_ms_per_launch": kd["avg_ms_per_launch"]}
+        if "tflops_median" in kd:
+            roof["achieved_median"] = kd["tflops_median"]
+            roof["frac_median"] = kd["tflops_median"] / PEAK_BF16_TFLOPS
     else:
         roof = {"bound": "hbm", "achieved": kd["gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": kd["gbps"] / PEAK_HBM_GBPS, "traffic": traffic, "kernel": dom,
                 "avg_ms_per_launch": kd["avg_ms_per_launch"]}
+        if "gbps_median" in kd:
+            roof["achieved_median"] = kd["gbps_median"]
+            roof["frac_median"] = kd["gbps_median"] / PEAK_HBM_GBPS
+    roof["algorithmic_per_step"] = kflops[dom] if roof["bound"] == "mfma" else kbytes[dom]
+
+    ctx = None
+    if not args.no_context_gemm and (train or T > 64):
+        log("timing the dense bf16 context GEMMs ...")
+        ctx = context_gemm(B, layers, T, train, min(args.steps, 100), 10)
 
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        cpu = cpu_baseline(first_inp, train, args.cpu_seconds)
+        cpu = cpu_baseline(inps, train, args.cpu_seconds,
+                           128 if args.config in ("mlp_8b", "layer_70b") else T)
 
     text = WORKLOAD_TEXT[args.config].format(n=lins[0][1], t=T)
     if drop:
@@ -546,6 +674,8 @@ def main():
         "rotating_copies": args.copies,
         "roofline": roof,
         "kernels": kernels,
+        "context_gemm": ctx,
+        "clocks": gpu_clocks(),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

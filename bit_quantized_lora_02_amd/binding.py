@@ -49,6 +49,7 @@ EXPORTED = (
     "qlora_last_error",
     "qlora_timing_enable",
     "qlora_timing_read",
+    "qlora_timing_read_each",
 )
 
 
@@ -128,6 +129,8 @@ def load_library() -> ctypes.CDLL:
         "qlora_last_error": ([], ctypes.c_char_p),
         "qlora_timing_enable": ([ctypes.c_char_p, ctypes.c_int], ctypes.c_int),
         "qlora_timing_read": ([ctypes.c_char_p, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
+        "qlora_timing_read_each": ([ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), i64, ctypes.POINTER(i64)],
+                                   ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -491,3 +494,12 @@ def timing_read(kernel: str) -> tuple[int, float]:
     n, ms = ctypes.c_int64(), ctypes.c_double()
     _check(load_library().qlora_timing_read(kernel.encode(), ctypes.byref(n), ctypes.byref(ms)), "qlora_timing_read")
     return n.value, ms.value
+
+
+def timing_read_each(kernel: str, cap: int = 1 << 16) -> list:
+    """Milliseconds of each recorded launch of `kernel`, in launch order (clears the record)."""
+    buf = (ctypes.c_double * cap)()
+    n = ctypes.c_int64()
+    _check(load_library().qlora_timing_read_each(kernel.encode(), buf, cap, ctypes.byref(n)),
+           "qlora_timing_read_each")
+    return list(buf[:min(cap, n.value)])

@@ -21,6 +21,7 @@
 #include "launch.h"
 #include "recip_div.h"
 #include "qlora.h"
+#include "qlora_timing.h"
 
 using namespace qlora;
 
@@ -128,6 +129,7 @@ bool debug_sync() {
 // --------------------------------------------------------------- timing
 std::mutex g_tmu;
 std::vector<std::string> g_timed;  // kernel names being timed; "*" = all
+std::atomic<int> g_ntimed{0};      // g_timed.size(): with none enabled a launch takes no lock
 std::map<std::string, std::vector<std::pair<hipEvent_t, hipEvent_t>>> g_events;
 
 bool is_timed(const char *kname) {
@@ -141,6 +143,7 @@ struct Timed {
   hipEvent_t a = nullptr, b = nullptr;
   std::string name;
   Timed(const char *kname) {
+    if (g_ntimed.load(std::memory_order_acquire) == 0) return;
     std::lock_guard<std::mutex> lk(g_tmu);
     if (!is_timed(kname)) return;
     if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
@@ -795,6 +798,7 @@ int qlora_timing_enable(const char *kernel, int enable) {
   std::lock_guard<std::mutex> lk(g_tmu);
   if (!strcmp(kernel, "*") && !enable) {
     g_timed.clear();
+    g_ntimed.store(0, std::memory_order_release);
     return QLORA_OK;
   }
   for (auto it = g_timed.begin(); it != g_timed.end(); ++it)
@@ -803,11 +807,13 @@ int qlora_timing_enable(const char *kernel, int enable) {
       break;
     }
   if (enable) g_timed.push_back(kernel);
+  g_ntimed.store((int)g_timed.size(), std::memory_order_release);
   return QLORA_OK;
 }
 
-int qlora_timing_read(const char *kernel, int64_t *launches, double *total_ms) {
-  if (!kernel || !launches || !total_ms) return fail(QLORA_EINVAL, "NULL argument");
+// Waits for and releases the recorded events of `kernel`; per-launch milliseconds in launch order go
+// to ms[0 .. cap) (ms may be NULL when cap is 0), their sum to *total_ms.
+static int timing_collect(const char *kernel, double *ms_each, int64_t cap, int64_t *launches, double *total_ms) {
   std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
   {
     std::lock_guard<std::mutex> lk(g_tmu);
@@ -819,19 +825,31 @@ int qlora_timing_read(const char *kernel, int64_t *launches, double *total_ms) {
   }
   double tot = 0.0;
   int rc = QLORA_OK;
-  for (auto &pr : ev) {
+  for (size_t i = 0; i < ev.size(); ++i) {
     float ms = 0.f;
-    if (hipEventSynchronize(pr.second) != hipSuccess || hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess) {
+    if (hipEventSynchronize(ev[i].second) != hipSuccess ||
+        hipEventElapsedTime(&ms, ev[i].first, ev[i].second) != hipSuccess) {
       (void)hipGetLastError();
       rc = fail(QLORA_EHIP, "reading timing events failed");
     }
     tot += ms;
-    (void)hipEventDestroy(pr.first);
-    (void)hipEventDestroy(pr.second);
+    if ((int64_t)i < cap) ms_each[i] = ms;
+    (void)hipEventDestroy(ev[i].first);
+    (void)hipEventDestroy(ev[i].second);
   }
   *launches = (int64_t)ev.size();
-  *total_ms = tot;
+  if (total_ms) *total_ms = tot;
   return rc;
+}
+
+int qlora_timing_read(const char *kernel, int64_t *launches, double *total_ms) {
+  if (!kernel || !launches || !total_ms) return fail(QLORA_EINVAL, "NULL argument");
+  return timing_collect(kernel, nullptr, 0, launches, total_ms);
+}
+
+int qlora_timing_read_each(const char *kernel, double *ms, int64_t cap, int64_t *launches) {
+  if (!kernel || !launches || (cap > 0 && !ms) || cap < 0) return fail(QLORA_EINVAL, "NULL argument or cap < 0");
+  return timing_collect(kernel, ms, cap, launches, nullptr);
 }
 
 }  // extern "C"

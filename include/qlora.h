@@ -301,19 +301,6 @@ const char *qlora_strerror(int code);
 /* Detail of the last failing call on this host thread ("" if none). */
 const char *qlora_last_error(void);
 
-/*
- * Kernel timing for measurement (host).  While enabled, the library records a
- * pair of HIP events on the launch stream around every launch of the kernel
- * named `kernel` ("nf4_gemm_fwd", "nf4_gemm_dx", ..., or "*" for all kernels).
- * Several names can be enabled at once; disabling "*" disables every name.
- * qlora_timing_read() waits for the recorded events, then returns the number
- * of timed launches of `kernel` and their summed milliseconds, and clears the
- * record.  Disabled by default; enabling it adds two event records per timed
- * launch and nothing else.
- */
-int qlora_timing_enable(const char *kernel, int enable);
-int qlora_timing_read(const char *kernel, int64_t *launches, double *total_ms);
-
 #ifdef __cplusplus
 }
 #endif

@@ -86,6 +86,8 @@ def _load():
     lib.oracle_dyn_encode.restype = ctypes.c_int
     lib.oracle_adamw8_step.argtypes = [P, P, P, P, P, P, P, i64, d, d, d, d, d, i64]
     lib.oracle_adamw8_step.restype = None
+    lib.oracle_adamw8_step_f64.argtypes = [P, P, P, P, P, P, i64, d, d, d, d, d, i64, P, P, P, P, P, P, P]
+    lib.oracle_adamw8_step_f64.restype = None
     _lib = lib
     return lib
 
@@ -378,3 +380,28 @@ def adamw8_step(param_bits: np.ndarray, grad_bits, m_code: np.ndarray, m_absmax:
     _load().oracle_adamw8_step(_ptr(param_bits), _ptr(master), _ptr(g), _ptr(m_code), _ptr(m_absmax), _ptr(v_code),
                                _ptr(v_absmax), n, float(lr), float(beta1), float(beta2), float(eps),
                                float(weight_decay), int(step))
+
+
+def adamw8_step_f64(theta, grad_bits, m_code, m_absmax, v_code, v_absmax, lr: float, beta1: float, beta2: float,
+                    eps: float, weight_decay: float, step: int) -> dict:
+    """One 8-bit AdamW step in binary64 from the given state (nothing is modified).
+
+    theta: the parameter before the step as floats (the binary32 master copy, or the bf16 parameter
+    widened); the state arrays as stored.  Returns theta, the moments m, v before encoding (binary64),
+    their codes mc, vc and the binary64 block absmax ma, va."""
+    g = np.ascontiguousarray(grad_bits, np.uint16).reshape(-1)
+    n = g.size
+    th = np.ascontiguousarray(np.asarray(theta, np.float64).reshape(-1))
+    mc = np.ascontiguousarray(m_code, np.uint8).reshape(-1)
+    vc = np.ascontiguousarray(v_code, np.uint8).reshape(-1)
+    ma = np.ascontiguousarray(m_absmax, np.float32).reshape(-1)
+    va = np.ascontiguousarray(v_absmax, np.float32).reshape(-1)
+    nb = (n + 2047) // 2048
+    assert th.size == n and mc.size == n and vc.size == n and ma.size == nb and va.size == nb
+    out = dict(theta=np.zeros(n), m=np.zeros(n), v=np.zeros(n), mc=np.zeros(n, np.uint8), ma=np.zeros(nb),
+               vc=np.zeros(n, np.uint8), va=np.zeros(nb))
+    _load().oracle_adamw8_step_f64(_ptr(th), _ptr(g), _ptr(mc), _ptr(ma), _ptr(vc), _ptr(va), n, float(lr),
+                                   float(beta1), float(beta2), float(eps), float(weight_decay), int(step),
+                                   _ptr(out["theta"]), _ptr(out["m"]), _ptr(out["v"]), _ptr(out["mc"]),
+                                   _ptr(out["ma"]), _ptr(out["vc"]), _ptr(out["va"]))
+    return out

@@ -578,8 +578,9 @@ void oracle_linear_fwd_multi(const double *X, int64_t T, const uint16_t *Wdq, in
  *    midpoint); the sign bit is set for x < 0 unless the magnitude is 0;
  *  - decode: fl32(table[code] * absmax);
  *  - the step is the binary32 AdamW of the fused kernel, every operation
- *    rounded once, in this order (the codes are integer decisions, taken in
- *    the kernel's precision):
+ *    rounded once, in this order.  This function fixes that declared order
+ *    (a regression pin: the kernel must keep it bit for bit); the reference
+ *    that judges a step's values is the binary64 [OPT8-64] below:
  *      m = fl(fl(b1 m) + fl(c1 g)),  v = fl(fl(b2 v) + fl(fl(c2 g) g)),
  *      d = fl(fl(sqrt(v) / sb) + eps),  theta = fl(fl(theta dk) - fl(ss fl(m / d)))
  *    with b1 = fl32(beta1), c1 = fl32(1 - beta1), b2 = fl32(beta2),
@@ -686,4 +687,65 @@ void oracle_adamw8_step(uint16_t *param, float *master, const uint16_t *grad, ui
   }
   free(m);
   free(v);
+}
+
+/*
+ * [OPT8-64] The same 8-bit step judged without the kernel's binary32 order:
+ * every operation is exact or binary64, so no rounding of binary32 arithmetic
+ * is shared with a GPU step.
+ *  - decode: a book magnitude (binary32) times a block absmax (binary32) is
+ *    exact in binary64 (48 significant bits);
+ *  - step: the binary64 AdamW of oracle_adamw_step on the decoded moments;
+ *  - encode: per block of 2048, absmax = max |m| (max v), x = m / absmax in
+ *    binary64, and the code is the number of exact midpoints of adjacent book
+ *    magnitudes strictly below |x| (ties to the smaller magnitude), with the
+ *    sign bit for x < 0 unless the magnitude is 0 (first moment only).
+ * Inputs: theta (binary64: the master copy or the bf16 parameter), grad bf16
+ * bits, the state before the step.  Outputs: theta_out, the moments before
+ * encoding (m_out, v_out), their codes and the binary64 block absmax.
+ */
+static int dyn_encode_f64(double x, int is_signed, const float book[256]) {
+  const int n = is_signed ? 128 : 256;
+  const double a = fabs(x);
+  int p = 0;
+  for (int i = 1; i < n; ++i)
+    if (a > ((double)book[i - 1] + (double)book[i]) * 0.5) p = i; /* midpoints are exact in binary64 */
+  if (is_signed && x < 0.0 && p != 0) p |= 128;
+  return p;
+}
+
+void oracle_adamw8_step_f64(const double *theta, const uint16_t *grad, const uint8_t *m_code,
+                            const float *m_absmax, const uint8_t *v_code, const float *v_absmax, int64_t n, double lr,
+                            double beta1, double beta2, double eps, double wd, int64_t t, double *theta_out,
+                            double *m_out, double *v_out, uint8_t *m_code_out, double *m_absmax_out,
+                            uint8_t *v_code_out, double *v_absmax_out) {
+  float sbook[256], ubook[256];
+  oracle_dyn_codebook(1, sbook);
+  oracle_dyn_codebook(0, ubook);
+  double *g = (double *)malloc(sizeof(double) * (n > 0 ? n : 1));
+  for (int64_t e = 0; e < n; ++e) {
+    const uint32_t u = (uint32_t)grad[e] << 16;
+    float gf;
+    memcpy(&gf, &u, 4);
+    g[e] = (double)gf;
+    theta_out[e] = theta[e];
+    m_out[e] = (double)sbook[m_code[e]] * (double)m_absmax[e / 2048];
+    v_out[e] = (double)ubook[v_code[e]] * (double)v_absmax[e / 2048];
+  }
+  oracle_adamw_step(theta_out, g, m_out, v_out, n, lr, beta1, beta2, eps, wd, t);
+  free(g);
+  for (int64_t e0 = 0; e0 < n; e0 += 2048) {
+    const int64_t e1 = (e0 + 2048 < n) ? e0 + 2048 : n;
+    double am = 0.0, av = 0.0;
+    for (int64_t e = e0; e < e1; ++e) {
+      if (fabs(m_out[e]) > am) am = fabs(m_out[e]);
+      if (v_out[e] > av) av = v_out[e];
+    }
+    m_absmax_out[e0 / 2048] = am;
+    v_absmax_out[e0 / 2048] = av;
+    for (int64_t e = e0; e < e1; ++e) {
+      m_code_out[e] = (uint8_t)(am > 0.0 ? dyn_encode_f64(m_out[e] / am, 1, sbook) : 0);
+      v_code_out[e] = (uint8_t)(av > 0.0 ? dyn_encode_f64(v_out[e] / av, 0, ubook) : 0);
+    }
+  }
 }

@@ -1,10 +1,11 @@
 """Host-side tests of the C ABI (no GPU needed).
 
-They load libqlora.so, check that it exports every function include/qlora.h
+They load libqlora.so, check that it exports every function include/*.h
 declares, exercise the host-only entry points, and drive every argument-error
 path, all of which return before the library's first HIP call.
 """
 import ctypes
+import glob
 import os
 import re
 
@@ -15,7 +16,7 @@ from bit_quantized_lora_02_amd import binding as B
 from conftest import gpu_available
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "qlora.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 @pytest.fixture(scope="module")
@@ -27,7 +28,7 @@ def lib():
 
 
 def _declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
 
@@ -306,3 +307,7 @@ def test_timing_api_host_only(lib):
     B.timing_enable("nf4_gemm_fwd", True)
     B.timing_enable("nf4_gemm_fwd", False)
     assert lib.qlora_timing_enable(None, 1) == B.QLORA_EINVAL
+    assert B.timing_read_each("nf4_gemm_fwd") == []
+    n = ctypes.c_int64()
+    assert lib.qlora_timing_read_each(b"nf4_gemm_fwd", None, 4, ctypes.byref(n)) == B.QLORA_EINVAL
+    assert lib.qlora_timing_read_each(b"nf4_gemm_fwd", None, 0, None) == B.QLORA_EINVAL

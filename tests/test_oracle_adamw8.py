@@ -122,3 +122,119 @@ def test_zero_gradient_keeps_zero_state_and_decays(oracle):
     assert np.all(mc == 0) and np.all(vc == 0) and np.all(ma == 0) and np.all(va == 0)
     dk = np.float32(1.0 - 0.5 * 0.1)
     np.testing.assert_array_equal(master, (oracle.bf16_bits_to_f64(p_bits) * np.float64(dk)).astype(np.float32))
+
+
+# ------------------------------------------- the binary64 8-bit step (oracle.adamw8_step_f64)
+
+def _random_state(rng, n, signed_scale=1e-3, v_scale=1e-6):
+    nb = (n + 2047) // 2048
+    mc = rng.integers(0, 256, n).astype(np.uint8)
+    vc = rng.integers(0, 256, n).astype(np.uint8)
+    ma = (rng.uniform(0.5, 2.0, nb) * signed_scale).astype(np.float32)
+    va = (rng.uniform(0.5, 2.0, nb) * v_scale).astype(np.float32)
+    return mc, ma, vc, va
+
+
+def test_f64_step_is_torch_adamw_on_the_decoded_state(oracle):
+    """Decode is exact (book value times absmax, checked with rationals), and the step on the decoded
+    moments is torch.optim.AdamW in float64 (an implementation of its own) from that state at step t."""
+    import torch
+    from fractions import Fraction
+
+    from adamw8_check import decode
+    from bit_quantized_lora_02_amd.synth import to_bf16_bits
+    rng = np.random.default_rng(11)
+    n, t = 4500, 5
+    lr, b1, b2, eps, wd = 1e-3, 0.9, 0.999, 1e-8, 0.01
+    mc, ma, vc, va = _random_state(rng, n)
+    theta = rng.standard_normal(n) * 0.02
+    g_bits = to_bf16_bits(rng.standard_normal(n).astype(np.float32) * np.float32(1e-3))
+    sbook, ubook = oracle.dyn_codebook(True), oracle.dyn_codebook(False)
+    mo, vo = decode(sbook, mc, ma), decode(ubook, vc, va)
+    for e in rng.integers(0, n, 50):  # binary64 products of two binary32 values are exact
+        assert Fraction(float(mo[e])) == Fraction(float(sbook[mc[e]])) * Fraction(float(ma[e // 2048]))
+        assert Fraction(float(vo[e])) == Fraction(float(ubook[vc[e]])) * Fraction(float(va[e // 2048]))
+    ref = oracle.adamw8_step_f64(theta, g_bits, mc, ma, vc, va, lr, b1, b2, eps, wd, t)
+    p = torch.nn.Parameter(torch.tensor(theta, dtype=torch.float64))
+    opt = torch.optim.AdamW([p], lr=lr, betas=(b1, b2), eps=eps, weight_decay=wd, foreach=False)
+    opt.state[p] = {"step": torch.tensor(float(t - 1), dtype=torch.float64),
+                    "exp_avg": torch.tensor(mo, dtype=torch.float64),
+                    "exp_avg_sq": torch.tensor(vo, dtype=torch.float64)}
+    p.grad = torch.tensor(oracle.bf16_bits_to_f64(g_bits), dtype=torch.float64)
+    opt.step()
+    st = opt.state[p]
+    np.testing.assert_allclose(ref["theta"], p.detach().numpy(), rtol=1e-13, atol=1e-17)
+    np.testing.assert_allclose(ref["m"], st["exp_avg"].numpy(), rtol=1e-13, atol=1e-30)
+    np.testing.assert_allclose(ref["v"], st["exp_avg_sq"].numpy(), rtol=1e-13, atol=1e-30)
+
+
+def test_f64_encode_is_exact_nearest_with_block_absmax(oracle):
+    from fractions import Fraction
+
+    from bit_quantized_lora_02_amd.synth import to_bf16_bits
+    rng = np.random.default_rng(12)
+    n = 4100  # two full blocks and a ragged one
+    mc, ma, vc, va = _random_state(rng, n)
+    theta = rng.standard_normal(n) * 0.02
+    g_bits = to_bf16_bits(rng.standard_normal(n).astype(np.float32) * np.float32(10.0 ** rng.uniform(-5, -2)))
+    ref = oracle.adamw8_step_f64(theta, g_bits, mc, ma, vc, va, 2e-4, 0.9, 0.999, 1e-8, 0.0, 3)
+    sbook, ubook = oracle.dyn_codebook(True), oracle.dyn_codebook(False)
+    smags = [Fraction(float(v)) for v in sbook[:128]]
+    umags = [Fraction(float(v)) for v in ubook]
+    for blk in range(3):
+        sl = slice(blk * 2048, min(n, (blk + 1) * 2048))
+        assert ref["ma"][blk] == np.abs(ref["m"][sl]).max() and ref["va"][blk] == ref["v"][sl].max()
+    sample = list(rng.integers(0, n, 150)) + [int(np.argmax(np.abs(ref["m"][:2048]))), int(np.argmax(ref["v"][:2048]))]
+    for e in sample:
+        blk = e // 2048
+        xm = Fraction(float(ref["m"][e])) / Fraction(float(ref["ma"][blk]))
+        best = min(range(128), key=lambda i: (abs(abs(xm) - smags[i]), i))
+        assert ref["mc"][e] == best | (128 if xm < 0 and best else 0), e
+        xv = Fraction(float(ref["v"][e])) / Fraction(float(ref["va"][blk]))
+        assert ref["vc"][e] == min(range(256), key=lambda i: (abs(xv - umags[i]), i)), e
+
+
+def _kernel_order_steps(oracle, n, steps, seed, master, lr=1e-3, wd=0.01, mutate=None):
+    """Run the binary32 (kernel-order) oracle for `steps` steps and judge each against the binary64 step
+    from the same state.  `mutate(t)` returns the arguments the binary32 step is called with instead
+    (lr, b1, b2, eps, wd, t): a planted mistake."""
+    from adamw8_check import check_step, decode
+    from bit_quantized_lora_02_amd.synth import to_bf16_bits
+    rng = np.random.default_rng(seed)
+    p_bits = to_bf16_bits(rng.standard_normal(n).astype(np.float32) * np.float32(0.02))
+    mc, ma, vc, va = _state(n)
+    ms = oracle.bf16_bits_to_f64(p_bits).astype(np.float32) if master else None
+    sbook, ubook = oracle.dyn_codebook(True), oracle.dyn_codebook(False)
+    flips = 0
+    for t in range(1, steps + 1):
+        g = rng.standard_normal(n).astype(np.float32) * np.float32(10.0 ** rng.uniform(-5, -1))
+        g[rng.random(n) < 0.05] = 0.0
+        g_bits = to_bf16_bits(g)
+        theta_in = ms.astype(np.float64) if master else oracle.bf16_bits_to_f64(p_bits)
+        mo, vo = decode(sbook, mc, ma), decode(ubook, vc, va)
+        ref = oracle.adamw8_step_f64(theta_in, g_bits, mc, ma, vc, va, lr, 0.9, 0.999, 1e-8, wd, t)
+        args = (lr, 0.9, 0.999, 1e-8, wd, t) if mutate is None else mutate(t)
+        oracle.adamw8_step(p_bits, g_bits, mc, ma, vc, va, *args, master=ms)
+        got = dict(mc=mc, vc=vc, ma=ma, va=va, p=p_bits, master=ms)
+        flips += check_step(got, ref, theta_in, g_bits, mo, vo, sbook, ubook, lr, 0.9, 0.999, 1e-8, wd, t,
+                            oracle.bf16_bits_to_f64)
+    return flips
+
+
+@pytest.mark.parametrize("master", [False, True])
+def test_kernel_order_oracle_within_binary64_bounds(oracle, master):
+    """The declared binary32 order (the kernel's, kept bit for bit by the regression pin) stays within the
+    rounding bounds of the binary64 step over six steps, two full blocks and a ragged one."""
+    flips = _kernel_order_steps(oracle, 5000, 6, 21, master)
+    assert flips < 5000 * 6 * 2 * 1e-3  # flips only at values within binary32 rounding of a midpoint
+
+
+@pytest.mark.parametrize("mistake", ["bias_correction_t_plus_1", "no_weight_decay", "beta2_0.99", "lr_x1.001"])
+def test_binary64_bounds_reject_planted_mistakes(oracle, mistake):
+    """Mistakes planted in the binary32 step (on the CPU) fail the judgement a GPU step gets."""
+    mut = {"bias_correction_t_plus_1": lambda t: (1e-3, 0.9, 0.999, 1e-8, 0.01, t + 1),
+           "no_weight_decay": lambda t: (1e-3, 0.9, 0.999, 1e-8, 0.0, t),
+           "beta2_0.99": lambda t: (1e-3, 0.9, 0.99, 1e-8, 0.01, t),
+           "lr_x1.001": lambda t: (1.001e-3, 0.9, 0.999, 1e-8, 0.01, t)}[mistake]
+    with pytest.raises(AssertionError):
+        _kernel_order_steps(oracle, 5000, 4, 22, True, mutate=mut)
