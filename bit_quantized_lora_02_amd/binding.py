@@ -158,9 +158,52 @@ def _bits(t: torch.Tensor) -> torch.Tensor:
     """bf16 tensor -> contiguous view used for the uint16 ABI arguments."""
     if t.dtype != torch.bfloat16:
         raise TypeError(f"expected a bfloat16 tensor, got {t.dtype}")
-    if not t.is_cuda:
-        raise TypeError("expected a GPU tensor")
     return t.contiguous()
+
+
+def _on_gpu(t: torch.Tensor) -> None:
+    """Operands live on a GPU (checked after their shapes, so shape errors name themselves first)."""
+    if not t.is_cuda:
+        raise TypeError("expected GPU tensors")
+
+
+def _want(t: torch.Tensor, shape: tuple, dtype: torch.dtype, device: torch.device, name: str) -> torch.Tensor:
+    """A caller-supplied buffer the library writes (or reads) by address: it must have exactly this shape
+    and dtype, be contiguous and sit on `device` (the C ABI sees only the pointer)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
+def _inputs(X: torch.Tensor, *others: torch.Tensor) -> None:
+    """X is a 2-D bf16 GPU tensor and every other operand sits on its device."""
+    if X.dim() != 2:
+        raise ValueError(f"X must be 2-D [T, n_in], got {tuple(X.shape)}")
+    for t in others:
+        if t is not None and t.device != X.device:
+            raise ValueError(f"operands on different devices: {t.device} and {X.device}")
+
+
+def _ws_bytes(ws: torch.Tensor, device: torch.device) -> int:
+    """Size in bytes of a caller-supplied workspace (a contiguous GPU tensor on `device`)."""
+    if not isinstance(ws, torch.Tensor) or not ws.is_contiguous() or ws.device != device:
+        raise ValueError("the workspace must be a contiguous tensor on the operands' device")
+    return ws.numel() * ws.element_size()
+
+
+def _check_weight(w: "NF4Weight", device: torch.device) -> None:
+    cb, qb, sb = storage_bytes(w.n_out, w.n_in)
+    for t, n, dt, name in ((w.codes, cb, torch.uint8, "codes"), (w.absmax_q, qb, torch.uint8, "absmax_q"),
+                           (w.absmax_step, sb // 4, torch.float32, "absmax_step")):
+        _want(t, (n,), dt, device, f"NF4 weight {name}")
 
 
 def storage_bytes(n_out: int, n_in: int) -> tuple[int, int, int]:
@@ -219,6 +262,7 @@ def quantize_nf4(W: torch.Tensor) -> NF4Weight:
 
 def dequant(w: NF4Weight) -> torch.Tensor:
     """bf16 [n_out, n_in] expansion of an NF4 weight (tests and export only)."""
+    _check_weight(w, w.device)
     out = torch.empty((w.n_out, w.n_in), dtype=torch.bfloat16, device=w.device)
     st = w.struct()
     _check(load_library().qlora_dequant(ctypes.byref(st), _ptr(out), _stream(w.device)), "qlora_dequant")
@@ -239,20 +283,37 @@ def linear_fwd(X: torch.Tensor, w: NF4Weight, A: torch.Tensor, B: torch.Tensor, 
 
     ``out``/``u_out`` are optional preallocated [T, n_out] / [T, r] bf16 buffers."""
     X, A, B = _bits(X), _bits(A), _bits(B)
+    _inputs(X, A, B)
+    _check_weight(w, X.device)
     T, r = X.shape[0], A.shape[0]
     if X.shape[1] != w.n_in or A.shape != (r, w.n_in) or B.shape != (w.n_out, r):
         raise ValueError(f"shape mismatch: X {tuple(X.shape)}, A {tuple(A.shape)}, B {tuple(B.shape)}, "
                          f"W [{w.n_out}, {w.n_in}]")
-    Y = out if out is not None else torch.empty((T, w.n_out), dtype=torch.bfloat16, device=X.device)
-    U = u_out if u_out is not None else (torch.empty((T, r), dtype=torch.bfloat16, device=X.device) if save_u else None)
+    bf = torch.bfloat16
+    Y = _want(out, (T, w.n_out), bf, X.device, "out") if out is not None else torch.empty((T, w.n_out), dtype=bf,
+                                                                                            device=X.device)
+    U = (_want(u_out, (T, r), bf, X.device, "u_out") if u_out is not None
+         else (torch.empty((T, r), dtype=bf, device=X.device) if save_u else None))
     if ws is None:
         ws, nb = _workspace(OP_FWD, T, w, r)
     else:
-        nb = ws.numel()
+        nb = _ws_bytes(ws, X.device)
+    _on_gpu(X)
     st = w.struct()
     _check(load_library().qlora_linear_fwd(_ptr(X), T, ctypes.byref(st), _ptr(A), _ptr(B), r, float(alpha), _ptr(Y),
                                            _ptr(U), _ptr(ws), nb, _stream(X.device)), "qlora_linear_fwd")
     return Y, U
+
+
+def _grad_outs(outs, X, A, B, need_dx):
+    """(dX or None, dA, dB): the caller's buffers, checked against X, A and B, or new ones."""
+    if outs is None:
+        return (torch.empty_like(X) if need_dx else None), torch.empty_like(A), torch.empty_like(B)
+    dX, dA, dB = outs
+    bf = torch.bfloat16
+    if dX is not None:
+        _want(dX, tuple(X.shape), bf, X.device, "dX")
+    return dX, _want(dA, tuple(A.shape), bf, X.device, "dA"), _want(dB, tuple(B.shape), bf, X.device, "dB")
 
 
 def linear_bwd(X: torch.Tensor, dY: torch.Tensor, w: NF4Weight, A: torch.Tensor, B: torch.Tensor, alpha: float,
@@ -262,19 +323,20 @@ def linear_bwd(X: torch.Tensor, dY: torch.Tensor, w: NF4Weight, A: torch.Tensor,
     X, dY, A, B = _bits(X), _bits(dY), _bits(A), _bits(B)
     if U is not None:
         U = _bits(U)
+    _inputs(X, dY, A, B, U)
+    _check_weight(w, X.device)
     T, r = X.shape[0], A.shape[0]
-    if dY.shape != (T, w.n_out) or A.shape != (r, w.n_in) or B.shape != (w.n_out, r):
-        raise ValueError("shape mismatch in linear_bwd")
-    if outs is not None:
-        dX, dA, dB = outs
-    else:
-        dX = torch.empty_like(X) if need_dx else None
-        dA = torch.empty_like(A)
-        dB = torch.empty_like(B)
+    if (X.shape[1] != w.n_in or dY.shape != (T, w.n_out) or A.shape != (r, w.n_in) or B.shape != (w.n_out, r)
+            or (U is not None and U.shape != (T, r))):
+        raise ValueError(f"shape mismatch in linear_bwd: X {tuple(X.shape)}, dY {tuple(dY.shape)}, "
+                         f"A {tuple(A.shape)}, B {tuple(B.shape)}, U {None if U is None else tuple(U.shape)}, "
+                         f"W [{w.n_out}, {w.n_in}]")
+    dX, dA, dB = _grad_outs(outs, X, A, B, need_dx)
     if ws is None:
         ws, nb = _workspace(OP_BWD, T, w, r)
     else:
-        nb = ws.numel()
+        nb = _ws_bytes(ws, X.device)
+    _on_gpu(X)
     st = w.struct()
     _check(load_library().qlora_linear_bwd(_ptr(X), _ptr(dY), T, ctypes.byref(st), _ptr(A), _ptr(B), r, float(alpha),
                                            _ptr(U), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws), nb, _stream(X.device)),
@@ -288,16 +350,23 @@ def linear_fwd_dropout(X: torch.Tensor, w: NF4Weight, A: torch.Tensor, B: torch.
                        mask_out: torch.Tensor | None = None):
     """Forward with LoRA dropout on the adapter input; returns (Y, U or None, keep-bit mask uint8 [T, n_in/8])."""
     X, A, B = _bits(X), _bits(A), _bits(B)
+    _inputs(X, A, B)
+    _check_weight(w, X.device)
     T, r = X.shape[0], A.shape[0]
     if X.shape[1] != w.n_in or A.shape != (r, w.n_in) or B.shape != (w.n_out, r):
         raise ValueError("shape mismatch in linear_fwd_dropout")
-    Y = out if out is not None else torch.empty((T, w.n_out), dtype=torch.bfloat16, device=X.device)
-    U = u_out if u_out is not None else (torch.empty((T, r), dtype=torch.bfloat16, device=X.device) if save_u else None)
-    mask = mask_out if mask_out is not None else torch.empty((T, w.n_in // 8), dtype=torch.uint8, device=X.device)
+    bf, dev = torch.bfloat16, X.device
+    Y = _want(out, (T, w.n_out), bf, dev, "out") if out is not None else torch.empty((T, w.n_out), dtype=bf,
+                                                                                       device=dev)
+    U = (_want(u_out, (T, r), bf, dev, "u_out") if u_out is not None
+         else (torch.empty((T, r), dtype=bf, device=dev) if save_u else None))
+    mask = (_want(mask_out, (T, w.n_in // 8), torch.uint8, dev, "mask_out") if mask_out is not None
+            else torch.empty((T, w.n_in // 8), dtype=torch.uint8, device=dev))
     if ws is None:
         ws, nb = _workspace(OP_FWD_DROPOUT, T, w, r)
     else:
-        nb = ws.numel()
+        nb = _ws_bytes(ws, dev)
+    _on_gpu(X)
     st = w.struct()
     _check(load_library().qlora_linear_fwd_dropout(_ptr(X), T, ctypes.byref(st), _ptr(A), _ptr(B), r, float(alpha),
                                                    float(p), int(seed) & (2**64 - 1), int(offset) & (2**64 - 1),
@@ -313,22 +382,21 @@ def linear_bwd_dropout(X: torch.Tensor, dY: torch.Tensor, w: NF4Weight, A: torch
     X, dY, A, B = _bits(X), _bits(dY), _bits(A), _bits(B)
     if U is not None:
         U = _bits(U)
+    _inputs(X, dY, A, B, U, mask)
+    _check_weight(w, X.device)
     T, r = X.shape[0], A.shape[0]
-    if dY.shape != (T, w.n_out) or A.shape != (r, w.n_in) or B.shape != (w.n_out, r):
+    if (X.shape[1] != w.n_in or dY.shape != (T, w.n_out) or A.shape != (r, w.n_in) or B.shape != (w.n_out, r)
+            or (U is not None and U.shape != (T, r))):
         raise ValueError("shape mismatch in linear_bwd_dropout")
     if mask.dtype != torch.uint8 or not mask.is_cuda or mask.numel() != T * w.n_in // 8:
         raise ValueError("mask must be a uint8 GPU tensor of T * n_in / 8 bytes")
     mask = mask.contiguous()
-    if outs is not None:
-        dX, dA, dB = outs
-    else:
-        dX = torch.empty_like(X) if need_dx else None
-        dA = torch.empty_like(A)
-        dB = torch.empty_like(B)
+    dX, dA, dB = _grad_outs(outs, X, A, B, need_dx)
     if ws is None:
         ws, nb = _workspace(OP_BWD, T, w, r)
     else:
-        nb = ws.numel()
+        nb = _ws_bytes(ws, X.device)
+    _on_gpu(X)
     st = w.struct()
     _check(load_library().qlora_linear_bwd_dropout(_ptr(X), _ptr(dY), T, ctypes.byref(st), _ptr(A), _ptr(B), r,
                                                    float(alpha), float(p), _ptr(mask), _ptr(U), _ptr(dX), _ptr(dA),
@@ -343,6 +411,8 @@ def linear_fwd_multi(X: torch.Tensor, w: NF4Weight, A_pool: torch.Tensor, B_pool
     """Y for a batch whose token segments use different adapters of a pool (A_pool [n, r, n_in],
     B_pool [n, n_out, r]); seg_offsets int32 [n_seg + 1], seg_adapter int32 [n_seg] on the GPU."""
     X, A_pool, B_pool = _bits(X), _bits(A_pool), _bits(B_pool)
+    _inputs(X, A_pool, B_pool, seg_offsets, seg_adapter)
+    _check_weight(w, X.device)
     T = X.shape[0]
     n_pool, r = A_pool.shape[0], A_pool.shape[1]
     if A_pool.shape != (n_pool, r, w.n_in) or B_pool.shape != (n_pool, w.n_out, r) or X.shape[1] != w.n_in:
@@ -353,11 +423,13 @@ def linear_fwd_multi(X: torch.Tensor, w: NF4Weight, A_pool: torch.Tensor, B_pool
     n_seg = seg_adapter.numel()
     if seg_offsets.numel() != n_seg + 1:
         raise ValueError("seg_offsets needs n_seg + 1 entries")
-    Y = out if out is not None else torch.empty((T, w.n_out), dtype=torch.bfloat16, device=X.device)
+    Y = (_want(out, (T, w.n_out), torch.bfloat16, X.device, "out") if out is not None
+         else torch.empty((T, w.n_out), dtype=torch.bfloat16, device=X.device))
     if ws is None:
         ws, nb = _workspace(OP_FWD_MULTI, T, w, r)
     else:
-        nb = ws.numel()
+        nb = _ws_bytes(ws, X.device)
+    _on_gpu(X)
     st = w.struct()
     _check(load_library().qlora_linear_fwd_multi(_ptr(X), T, ctypes.byref(st), _ptr(A_pool), _ptr(B_pool), n_pool, r,
                                                  float(alpha), _ptr(seg_offsets), _ptr(seg_adapter), n_seg, _ptr(Y),
@@ -375,12 +447,19 @@ def merge(A: torch.Tensor, B: torch.Tensor, alpha: float, w: NF4Weight | None = 
         raise ValueError("give exactly one of w and W_base")
     A, B = _bits(A), _bits(B)
     r = A.shape[0]
+    if w is not None:
+        _check_weight(w, A.device)
+    elif W_base.dim() != 2 or W_base.device != A.device:
+        raise ValueError("W_base must be a 2-D tensor on the adapters' device")
+    if B.device != A.device:
+        raise ValueError("A and B on different devices")
     n_out, n_in = (w.n_out, w.n_in) if w is not None else tuple(W_base.shape)
     if A.shape != (r, n_in) or B.shape != (n_out, r):
         raise ValueError("shape mismatch in merge")
     dev = A.device
     out = torch.empty((n_out, n_in), dtype=torch.bfloat16, device=dev) if bf16_out else None
     out32 = torch.empty((n_out, n_in), dtype=torch.float32, device=dev) if f32_out else None
+    _on_gpu(A)
     Wb = _bits(W_base) if W_base is not None else None
     st = w.struct() if w is not None else None
     _check(load_library().qlora_merge(ctypes.byref(st) if st is not None else None, _ptr(Wb), n_out, n_in, _ptr(A),

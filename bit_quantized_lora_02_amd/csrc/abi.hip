@@ -30,6 +30,11 @@ LaunchEvents &qlora::launch_events() {
   return ev;
 }
 
+bool &qlora::launch_refused() {
+  static thread_local bool refused = false;
+  return refused;
+}
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -163,6 +168,10 @@ struct Timed {
 };
 
 int launched(hipError_t e, const char *what, hipStream_t s) {
+  if (launch_refused()) {
+    launch_refused() = false;
+    return fail(QLORA_EINVAL, "%s: a grid dimension would reach 2^32 work-items", what);
+  }
   if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return fail(QLORA_EHIP, "%s: %s", what, hipGetErrorString(e));
   return QLORA_OK;
@@ -182,6 +191,18 @@ int launched(hipError_t e, const char *what, hipStream_t s) {
 // ------------------------------------------------------------- validation
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 constexpr int64_t kMaxDim = (int64_t)1 << 22;
+// Largest weight (n_out n_in) and activation (T n_out, T n_in) element counts: every launch then stays
+// below 2^32 work-items per grid dimension (the dequantization runs one work-item per 8 weights, the
+// ordered finalize of a split reduction one per output element).
+constexpr int64_t kMaxWeights = (int64_t)1 << 34;
+constexpr int64_t kMaxActs = ((int64_t)1 << 32) - 256;
+
+int check_acts(int64_t T, int64_t n_out, int64_t n_in) {
+  if (T * n_out > kMaxActs || T * n_in > kMaxActs)
+    return fail(QLORA_EINVAL, "T x n_out and T x n_in must stay below 2^32 (got T=%lld, %lld x %lld)", (long long)T,
+                (long long)n_out, (long long)n_in);
+  return QLORA_OK;
+}
 
 int check_nf4(const qlora_nf4 *q, bool for_gemm) {
   if (!q) return fail(QLORA_EINVAL, "q is NULL");
@@ -191,8 +212,9 @@ int check_nf4(const qlora_nf4 *q, bool for_gemm) {
   if (q->n_out < 1 || q->n_in < 64 || q->n_in % 64 != 0)
     return fail(QLORA_EINVAL, "need n_out >= 1 and n_in a positive multiple of 64 (got %lld x %lld)",
                 (long long)q->n_out, (long long)q->n_in);
-  if (q->n_out > kMaxDim || q->n_in > kMaxDim || q->n_out * q->n_in > ((int64_t)1 << 40))
-    return fail(QLORA_EINVAL, "weight too large (%lld x %lld)", (long long)q->n_out, (long long)q->n_in);
+  if (q->n_out > kMaxDim || q->n_in > kMaxDim || q->n_out * q->n_in > kMaxWeights)
+    return fail(QLORA_EINVAL, "weight too large (%lld x %lld; at most 2^22 per side and 2^34 weights)",
+                (long long)q->n_out, (long long)q->n_in);
   if (for_gemm && q->n_out % 8 != 0) return fail(QLORA_EINVAL, "n_out must be a multiple of 8 (got %lld)", (long long)q->n_out);
   return QLORA_OK;
 }
@@ -300,6 +322,7 @@ int check_lora_args(int64_t T, const qlora_nf4 *q, const void *A, const void *B,
   int rc = check_nf4(q, true);
   if (rc) return rc;
   if (T < 0 || T > kMaxDim) return fail(QLORA_EINVAL, "T must be in [0, 2^22] (got %lld)", (long long)T);
+  if ((rc = check_acts(T, q->n_out, q->n_in))) return rc;
   if (r < 1 || r > QLORA_MAX_RANK) return fail(QLORA_EINVAL, "r must be in [1, %d] (got %d)", QLORA_MAX_RANK, (int)r);
   if (!isfinite(alpha)) return fail(QLORA_EINVAL, "alpha must be finite");
   if (!A || !B) return fail(QLORA_EINVAL, "A and B must not be NULL");
@@ -358,9 +381,10 @@ const char *qlora_last_error(void) { return g_err; }
 int qlora_nf4_storage(int64_t n_out, int64_t n_in, size_t *codes_bytes, size_t *absmax_q_bytes,
                       size_t *absmax_step_bytes) {
   if (!codes_bytes || !absmax_q_bytes || !absmax_step_bytes) return fail(QLORA_EINVAL, "NULL output pointer");
-  if (n_out < 1 || n_in < 64 || n_in % 64 != 0 || n_out > kMaxDim || n_in > kMaxDim)
-    return fail(QLORA_EINVAL, "need n_out >= 1 and n_in a positive multiple of 64 (got %lld x %lld)",
-                (long long)n_out, (long long)n_in);
+  if (n_out < 1 || n_in < 64 || n_in % 64 != 0 || n_out > kMaxDim || n_in > kMaxDim || n_out * n_in > kMaxWeights)
+    return fail(QLORA_EINVAL,
+                "need n_out >= 1, n_in a positive multiple of 64, each at most 2^22 and at most 2^34 weights "
+                "(got %lld x %lld)", (long long)n_out, (long long)n_in);
   const int64_t n = n_out * n_in, nblk = n / 64;
   *codes_bytes = (size_t)(n / 2);
   *absmax_q_bytes = (size_t)nblk;
@@ -382,6 +406,7 @@ int qlora_workspace_bytes(int op, int64_t T, int64_t n_out, int64_t n_in, int32_
       n_in > kMaxDim || r < 1 || r > QLORA_MAX_RANK)
     return fail(QLORA_EINVAL, "bad sizes T=%lld n_out=%lld n_in=%lld r=%d", (long long)T, (long long)n_out,
                 (long long)n_in, (int)r);
+  if (int rc = check_acts(T, n_out, n_in)) return rc;
   *bytes = make_plan(op, T, n_out, n_in, r).total;
   return QLORA_OK;
 }
@@ -665,8 +690,7 @@ int qlora_merge(const qlora_nf4 *q, const qlora_bf16 *W_base, int64_t n_out, int
   } else if (!aligned16(W_base)) {
     return fail(QLORA_EINVAL, "W_base must be 16-byte aligned");
   }
-  if (n_out < 1 || n_in < 64 || n_in % 64 != 0 || n_out > kMaxDim || n_in > kMaxDim ||
-      n_out * n_in > ((int64_t)1 << 40))
+  if (n_out < 1 || n_in < 64 || n_in % 64 != 0 || n_out > kMaxDim || n_in > kMaxDim || n_out * n_in > kMaxWeights)
     return fail(QLORA_EINVAL, "need n_out >= 1 and n_in a positive multiple of 64 (got %lld x %lld)",
                 (long long)n_out, (long long)n_in);
   if (r < 1 || r > QLORA_MAX_RANK) return fail(QLORA_EINVAL, "r must be in [1, %d] (got %d)", QLORA_MAX_RANK, (int)r);

@@ -13,9 +13,18 @@ struct LaunchEvents {
   hipEvent_t start = nullptr, stop = nullptr;
 };
 LaunchEvents &launch_events();  // per host thread
+// Set (per host thread) when a launch was refused because a grid dimension would reach 2^32
+// work-items; the C ABI reads and clears it after each launch.  The argument checks keep every
+// launch below that, so this is a guard, not a path.
+bool &launch_refused();
 
 template <typename F, typename... Args>
 inline void launch(F kernel, dim3 grid, dim3 block, uint32_t shm, hipStream_t s, Args... args) {
+  const uint64_t lim = (uint64_t)1 << 32;
+  if ((uint64_t)grid.x * block.x >= lim || (uint64_t)grid.y * block.y >= lim || (uint64_t)grid.z * block.z >= lim) {
+    launch_refused() = true;
+    return;
+  }
   const LaunchEvents &ev = launch_events();
   hipExtLaunchKernelGGL(kernel, grid, block, shm, s, ev.start, ev.stop, 0u, args...);
 }

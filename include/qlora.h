@@ -71,8 +71,11 @@ typedef uint16_t qlora_bf16; /* bf16 bit pattern */
  * Decoding: w' = bf16_rne(fl32(level[code] * fl32(absmax_q[b] * absmax_step[b / 256]))).
  * Requirements: n_in % 64 == 0 (a block never straddles a row) and n_out >= 1;
  * qlora_linear_fwd/bwd also need n_out % 8 == 0 (16-byte rows of dY and Y).
- * Both sizes are at most 2^22.  The struct itself is host memory; the three arrays are device
- * memory owned by the caller.  qlora_linear_fwd/bwd never write them.
+ * Both sizes are at most 2^22 and n_out * n_in at most 2^34; the layer calls
+ * also need T <= 2^22 and T * n_out, T * n_in below 2^32 (so that no launch
+ * reaches 2^32 work-items in a grid dimension; larger sizes give QLORA_EINVAL).
+ * The struct itself is host memory; the three arrays are device memory owned
+ * by the caller.  qlora_linear_fwd/bwd never write them.
  */
 typedef struct qlora_nf4 {
   int64_t n_out;
@@ -112,8 +115,13 @@ int qlora_workspace_bytes(int op, int64_t T, int64_t n_out, int64_t n_in, int32_
  * exact binary32 c_b (katajob, "NF4" and "Double quantization"). */
 int qlora_quantize_nf4(const float *W, const qlora_nf4 *q, void *stream);
 
-/* Expand q to bf16 W_out [n_out, n_in] (device).  For tests and export only:
- * the forward and backward never materialize the dequantized weight. */
+/* Expand q to bf16 W_out [n_out, n_in] (device): w' = bf16_rne(fl32(level[code]
+ * * c'_b)) for every weight, the expansion of each block to the compute dtype
+ * that the method performs inside the matmul (katajob, "NF4: 4-bit NormalFloat";
+ * ainiketan, Module 08, section 3: dequantized on the fly).  W_out is caller-
+ * owned, 16-byte aligned, n_out * n_in bf16.  For tests and export only: the
+ * forward and backward never materialize the dequantized weight.  Errors:
+ * QLORA_EINVAL (NULL or misaligned pointer, shape), QLORA_ENODEV, QLORA_EHIP. */
 int qlora_dequant(const qlora_nf4 *q, qlora_bf16 *W_out, void *stream);
 
 /*

@@ -90,6 +90,25 @@ def test_error_paths_storage_and_workspace(lib):
     assert B.codebook()  # still fine afterwards
 
 
+def test_size_limits_keep_launches_below_2_32_work_items(lib):
+    """At most 2^34 weights (the dequantization runs n / 8 work-items) and T x n_out, T x n_in below 2^32
+    (the ordered finalize of a split reduction runs one work-item per output element)."""
+    c = ctypes.c_size_t()
+    big = 1 << 22
+    assert lib.qlora_nf4_storage(1 << 12, 1 << 22, ctypes.byref(c), ctypes.byref(c), ctypes.byref(c)) == B.QLORA_OK
+    assert lib.qlora_nf4_storage(big, big, ctypes.byref(c), ctypes.byref(c), ctypes.byref(c)) == B.QLORA_EINVAL
+    assert lib.qlora_nf4_storage((1 << 12) + 8, 1 << 22, ctypes.byref(c), ctypes.byref(c),
+                                 ctypes.byref(c)) == B.QLORA_EINVAL
+    assert lib.qlora_workspace_bytes(B.OP_FWD, 1 << 10, 1 << 21, 64, 8, ctypes.byref(c)) == B.QLORA_OK
+    assert lib.qlora_workspace_bytes(B.OP_FWD, 1 << 11, 1 << 21, 64, 8, ctypes.byref(c)) == B.QLORA_EINVAL
+    assert lib.qlora_workspace_bytes(B.OP_BWD, 1 << 11, 64, 1 << 21, 8, ctypes.byref(c)) == B.QLORA_EINVAL
+    q = _nf4(1 << 21, 64)
+    FAKE = ctypes.c_void_p(0x1000)
+    rc, msg = _err(lib.qlora_linear_fwd, FAKE, 1 << 11, ctypes.byref(q), FAKE, FAKE, 8, 16.0, FAKE, None, FAKE,
+                   1 << 40, None)
+    assert rc == B.QLORA_EINVAL and "2^32" in msg
+
+
 def test_error_paths_quantize_dequant(lib):
     q = _nf4(64, 64)
     rc, msg = _err(lib.qlora_quantize_nf4, None, ctypes.byref(q), None)
