@@ -38,6 +38,7 @@ EXPORTED = (
     "qlora_quantize_nf4",
     "qlora_dequant",
     "qlora_linear_fwd",
+    "qlora_linear_fwd_noalloc",
     "qlora_linear_bwd",
     "qlora_linear_fwd_dropout",
     "qlora_linear_bwd_dropout",
@@ -113,6 +114,7 @@ def load_library() -> ctypes.CDLL:
         "qlora_quantize_nf4": ([P, pnf4, P], ctypes.c_int),
         "qlora_dequant": ([pnf4, P, P], ctypes.c_int),
         "qlora_linear_fwd": ([P, i64, pnf4, P, P, i32, ctypes.c_float, P, P, P, sz, P], ctypes.c_int),
+        "qlora_linear_fwd_noalloc": ([P, i64, pnf4, P, P, i32, ctypes.c_float, P, P, P], ctypes.c_int),
         "qlora_linear_bwd": ([P, P, i64, pnf4, P, P, i32, ctypes.c_float, P, P, P, P, P, sz, P], ctypes.c_int),
         "qlora_linear_fwd_dropout": ([P, i64, pnf4, P, P, i32, ctypes.c_float, ctypes.c_float, ctypes.c_uint64,
                                       ctypes.c_uint64, P, P, P, P, sz, P], ctypes.c_int),

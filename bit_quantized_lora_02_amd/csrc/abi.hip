@@ -131,6 +131,32 @@ bool debug_sync() {
   return v == 1;
 }
 
+// -------------------------------------------------- allocation-free forward
+// The workspace of qlora_linear_fwd_noalloc: one array per GPU, alive until the process ends.  In
+// host code `scratch` is only a host-side stand-in for the array; its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and only that address is
+// handed to kernels.
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64] = {};
+
+int scratch_address(int dev, void **out) {
+  if (dev < 0 || dev >= 64) return fail(QLORA_ENODEV, "device index %d out of range for the static workspace", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return fail(QLORA_EHIP, "hipGetSymbolAddress of the static workspace failed: %s", hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return QLORA_OK;
+}
+
 // --------------------------------------------------------------- timing
 std::mutex g_tmu;
 std::vector<std::string> g_timed;  // kernel names being timed; "*" = all
@@ -601,6 +627,22 @@ int qlora_linear_fwd(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const q
                      int32_t r, float alpha, qlora_bf16 *Y, qlora_bf16 *U_out, void *ws, size_t ws_bytes,
                      void *stream) {
   return linear_fwd(X, T, q, A, B, r, alpha, nullptr, Y, U_out, ws, ws_bytes, stream);
+}
+
+int qlora_linear_fwd_noalloc(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const qlora_bf16 *A,
+                             const qlora_bf16 *B, int32_t r, float alpha, qlora_bf16 *Y, qlora_bf16 *U_out,
+                             void *stream) {
+  int rc = check_lora_args(T, q, A, B, r, alpha);
+  if (rc) return rc;
+  const size_t need = make_plan(QLORA_OP_FWD, T, q->n_out, q->n_in, r).total;
+  if (need > kScratchBytes)
+    return fail(QLORA_EWORKSPACE, "this forward needs %zu workspace bytes; the static workspace holds %zu", need,
+                kScratchBytes);
+  int dev = 0;
+  if ((rc = check_device(&dev))) return rc;
+  void *ws = nullptr;
+  if ((rc = scratch_address(dev, &ws))) return rc;
+  return linear_fwd(X, T, q, A, B, r, alpha, nullptr, Y, U_out, ws, kScratchBytes, stream);
 }
 
 int qlora_linear_bwd(const qlora_bf16 *X, const qlora_bf16 *dY, int64_t T, const qlora_nf4 *q, const qlora_bf16 *A,

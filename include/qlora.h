@@ -139,6 +139,24 @@ int qlora_linear_fwd(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const q
                      void *stream);
 
 /*
+ * The same forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * identical arguments and results, without ws / ws_bytes.  Its workspace is a
+ * static device array of 128 MiB per GPU, reserved when the library's code is
+ * loaded on that GPU and held until the process ends; the call itself makes no
+ * allocation.  Every forward of this build's workloads fits (the largest, 64
+ * tokens against a 28672 x 8192 weight, needs 116 MiB); a shape whose forward
+ * needs more returns QLORA_EWORKSPACE before any HIP call.  All calls on one
+ * GPU share the array: calls that overlap in time on that GPU (other streams,
+ * other host threads) race and must be ordered by the caller.  Nothing in the
+ * array needs to start at zero.  Errors as for qlora_linear_fwd, plus QLORA_EHIP
+ * if the array's device address cannot be obtained.
+ */
+int qlora_linear_fwd_noalloc(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const qlora_bf16 *A,
+                             const qlora_bf16 *B, int32_t r, float alpha, qlora_bf16 *Y, qlora_bf16 *U_out,
+                             void *stream);
+
+/*
  * Backward of the forward above with respect to X, A and B; W gets no gradient
  * (katajob, "What stays in full precision"; glossary, step 4):
  *   dU = s . dY . B                 [T, r]

@@ -1,0 +1,78 @@
+"""The allocation-free forward (static per-GPU workspace) against the forward with a caller workspace.
+
+Both run the same kernels with the same plan, so Y and U must be bit-identical.  Two calls in a
+row share the static array: the second, smaller one must not see the first one's contents.  Calls
+go straight through the C ABI with preallocated outputs.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from bit_quantized_lora_02_amd import binding as B
+from bit_quantized_lora_02_amd.synth import linear_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(n_out, n_in, T, r, seed):
+    dev = torch.device("cuda:0")
+    inp = linear_inputs(n_out, n_in, T, r, 2.0 * r, seed=seed, make_dy=False)
+    g = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    w = B.quantize_nf4(torch.from_numpy(inp.W).to(dev))
+    return w, g(inp.X), g(inp.A), g(inp.B), inp.alpha
+
+
+def _fwd_ws(lib, w, X, A, Bm, alpha):
+    T, r = X.shape[0], A.shape[0]
+    Y = torch.full((T, w.n_out), 7.0, dtype=torch.bfloat16, device=X.device)
+    U = torch.full((T, r), 7.0, dtype=torch.bfloat16, device=X.device)
+    nb = B.workspace_bytes(B.OP_FWD, T, w.n_out, w.n_in, r)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=X.device)
+    st = w.struct()
+    rc = lib.qlora_linear_fwd(B._ptr(X), T, ctypes.byref(st), B._ptr(A), B._ptr(Bm), r, float(alpha), B._ptr(Y),
+                              B._ptr(U), B._ptr(ws), nb, B._stream(X.device))
+    assert rc == B.QLORA_OK, lib.qlora_last_error()
+    return Y, U
+
+
+def _fwd_static(lib, w, X, A, Bm, alpha):
+    T, r = X.shape[0], A.shape[0]
+    Y = torch.full((T, w.n_out), -3.0, dtype=torch.bfloat16, device=X.device)
+    U = torch.full((T, r), -3.0, dtype=torch.bfloat16, device=X.device)
+    st = w.struct()
+    rc = lib.qlora_linear_fwd_noalloc(B._ptr(X), T, ctypes.byref(st), B._ptr(A), B._ptr(Bm), r, float(alpha),
+                                      B._ptr(Y), B._ptr(U), B._stream(X.device))
+    assert rc == B.QLORA_OK, lib.qlora_last_error()
+    return Y, U
+
+
+def _same(a, b):
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("first,second", [
+    ((4096, 4096, 2048, 16), (1024, 512, 40, 8)),       # tiled forward, then the row-group GEMV
+    ((28672, 8192, 64, 16), (8192, 8192, 1, 16)),       # the largest workspace, then the one-token GEMV
+    ((8192, 8192, 128, 64), (256, 256, 16, 8)),         # split reduction, then a small tiled forward
+])
+def test_noalloc_matches_forward_with_workspace(first, second):
+    lib = B.load_library()
+    for shape, seed in ((first, 1), (second, 2)):
+        print(f"noalloc forward {shape}", flush=True)
+        w, X, A, Bm, alpha = _case(*shape, seed)
+        y0, u0 = _fwd_ws(lib, w, X, A, Bm, alpha)
+        y1, u1 = _fwd_static(lib, w, X, A, Bm, alpha)
+        torch.cuda.synchronize()
+        _same(y0, y1)
+        _same(u0, u1)
+
+
+def test_noalloc_rejects_a_forward_larger_than_its_workspace():
+    lib = B.load_library()
+    q = B._NF4(1 << 17, 8192, 0x1000, 0x1000, 0x1000)
+    P = ctypes.c_void_p(0x1000)
+    rc = lib.qlora_linear_fwd_noalloc(P, 64, ctypes.byref(q), P, P, 16, 32.0, P, None, None)
+    assert rc == B.QLORA_EWORKSPACE
+    assert b"static workspace" in lib.qlora_last_error()
