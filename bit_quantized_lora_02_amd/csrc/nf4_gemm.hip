@@ -666,6 +666,170 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
   store_out<C>(dX, K, m0, T, n0, K, wm, wn, lane, acc);
 }
 
+// ------------------------------------------- forward, weights decoded in registers
+// Y[T, N] = X[T, K] . W'[N, K]^T + V[T, rp] . B[N, :r]^T for outputs of at least 256 tiles of 256 x 256.
+// One workgroup of four waves (one per SIMD) per CU.  Wave w owns all 256 rows of the tile and its
+// columns 64 w .. 64 w + 63 (8 x 2 tiles of 32 x 32, binary32 accumulators in AGPRs), so the weight
+// operand of every column is needed by one wave only: each lane loads and decodes its own codes straight
+// into MFMA B-operand registers, and the weights never pass through LDS.  The activation tile (256 rows
+// x 64) is copied global -> LDS by the load unit, three buffers deep, and read by all four waves.
+// Reduction order: in 64-deep step s the lanes of half h (lanes 32 h .. 32 h + 31) hold the columns
+// 64 s + 32 h + 8 kk .. +7 in substep kk, for both operands, so a lane's codes of one weight row and
+// step are 16 consecutive bytes (32 weights of one block, one 16-byte load).  Each lane decodes its
+// 8-nibble words through the level-pair table in LDS (one 8-byte read per code byte), multiplies by the
+// block constant and packs to bf16 -- w' = bf16_rne(fl32(level * c')), the same values as everywhere.
+namespace {
+struct RdCfg {
+  static constexpr int NW = 4, NT = 256, BM = 256, BN = 256, WM = 8, WN = 2;
+  static constexpr int A_LD = BM * 8 / NT;  // direct 16-byte activation loads per thread and step
+};
+
+// decode one code word (8 nibbles, element e in bits 4e..4e+3) into 8 bf16 (k order)
+__device__ __forceinline__ u32x4_t decode_word(uint32_t w, const float2 *s_lv, float cq) {
+  float v[8];
+  lookup8(w, s_lv, v);
+  return scale_pack8(v, cq);
+}
+}  // namespace
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_nf4_gemm_fwd_rd(
+    const bf16_t *__restrict__ X, int64_t T, int64_t K, const uint8_t *__restrict__ codes,
+    const uint8_t *__restrict__ absmax_q, const float *__restrict__ step, int64_t N, const bf16_t *__restrict__ V,
+    const bf16_t *__restrict__ Bp, int64_t ldb, int64_t r, int64_t rp, bf16_t *__restrict__ Y, Levels lv, int xb_m,
+    int xb_n) {
+  using C = RdCfg;
+  __shared__ __attribute__((aligned(16))) bf16_t sA0[C::BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t sA1[C::BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t sA2[C::BM * BK];
+  __shared__ float2 s_lv[256];
+  bf16_t *const sA[3] = {sA0, sA1, sA2};
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, rr = lane & 31;
+  const TileCoord tc = tile_of((N + C::BN - 1) / C::BN, xb_m, xb_n);
+  const int64_t m0 = tc.m * C::BM, n0 = tc.n * C::BN;
+  pair_levels_to_lds(lv, s_lv, tid);
+
+  const int nk = (int)(K / BK);
+  ALoads<C> al;
+  al.init(X, K, m0, T, wave, lane);
+  // this lane's two weight rows (columns of Y); rows past N re-read row N - 1 (never stored)
+  const uint8_t *crow[C::WN];
+  const uint8_t *qrow[C::WN];
+  const float *drow[C::WN];
+  int64_t qb[C::WN];
+#pragma unroll
+  for (int j = 0; j < C::WN; ++j) {
+    const int64_t n = n0 + 64 * wave + 32 * j + rr;
+    const int64_t nn = n < N ? n : N - 1;
+    crow[j] = codes + nn * (K / 2) + 16 * h;
+    qb[j] = nn * (K / BK);
+    qrow[j] = absmax_q + qb[j];
+    drow[j] = step;
+  }
+  // LDS read offset (elements) of this lane's A operand in substep kk: row 32 i + rr is at + 2048 i
+  const int sw = (rr >> 1) & 7;
+  int aoff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) aoff[kk] = rr * BK + (((4 * h + kk) ^ sw) << 3);
+
+  // register slots of the codes and raw block constants of three consecutive steps
+  u32x4_t wd[3][C::WN];
+  RawScale rs[3][C::WN];
+  auto load_step = [&](int s, u32x4_t(&w)[C::WN], RawScale(&sc)[C::WN]) {
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) w[j] = *reinterpret_cast<const u32x4_t *>(crow[j] + (int64_t)s * (BK / 2));
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) {
+      const int64_t b = qb[j] + s;
+      sc[j] = RawScale{(uint32_t)qrow[j][s], drow[j][b >> 8]};
+    }
+  };
+
+  f32x16_t acc[C::WM][C::WN];
+  zero_acc<C>(acc);
+
+  // prologue: activation tiles 0 and 1, codes of steps 0 and 1
+  al.issue(0, K, sA[0]);
+  al.issue(nk > 1 ? BK : 0, K, sA[1]);
+  load_step(0, wd[0], rs[0]);
+  load_step(nk > 1 ? 1 : 0, wd[1], rs[1]);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  auto step_p = [&](auto pc, int s) {
+    constexpr int P = decltype(pc)::value;  // s % 3: LDS buffer and register slot of step s
+    constexpr int P2 = (P + 2) % 3;
+    const int s2 = (s + 2 < nk) ? s + 2 : nk - 1;
+    al.issue((int64_t)s2 * BK, K, sA[P2]);
+    load_step(s2, wd[P2], rs[P2]);
+    fence_sched();
+    const bf16_t *sa = sA[P];
+    float cq[C::WN];
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) cq[j] = scale_of(rs[P][j]);
+    u32x4_t a[2][C::WM], b[2][C::WN];
+#pragma unroll
+    for (int i = 0; i < C::WM; ++i) a[0][i] = *reinterpret_cast<const u32x4_t *>(sa + aoff[0] + 2048 * i);
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) b[0][j] = decode_word(wd[P][j].x, s_lv, cq[j]);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int cur = kk & 1;
+      if (kk < 3) {
+#pragma unroll
+        for (int i = 0; i < C::WM; ++i)
+          a[cur ^ 1][i] = *reinterpret_cast<const u32x4_t *>(sa + aoff[kk + 1] + 2048 * i);
+#pragma unroll
+        for (int j = 0; j < C::WN; ++j) b[cur ^ 1][j] = decode_word(wd[P][j][kk + 1], s_lv, cq[j]);
+      }
+#pragma unroll
+      for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::WN; ++j) acc[i][j] = mfma_32x32x16(a[cur][i], b[cur][j], acc[i][j]);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);  // every load of this step and the ones before it, and all LDS reads
+    __syncthreads();
+  };
+  int s = 0;
+  for (; s + 2 < nk; s += 3) {
+    step_p(std::integral_constant<int, 0>(), s);
+    step_p(std::integral_constant<int, 1>(), s + 1);
+    step_p(std::integral_constant<int, 2>(), s + 2);
+  }
+  if (s < nk) step_p(std::integral_constant<int, 0>(), s);
+  if (s + 1 < nk) step_p(std::integral_constant<int, 1>(), s + 1);
+
+  // LoRA up-projection V [T, rp] . B [N, rp]^T: the V tile through LDS, B rows straight into registers
+  for (int64_t k0 = 0; k0 < rp; k0 += BK) {
+    __syncthreads();
+    copy_a_tile<C>(V, rp, m0, T, k0, rp, tid, sA[0]);
+    __syncthreads();
+    u32x4_t bl[4][C::WN];
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) {
+      const int64_t n = n0 + 64 * wave + 32 * j + rr;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int64_t col = k0 + 32 * h + 8 * kk;
+        bl[kk][j] = (n < N && col < r) ? *reinterpret_cast<const u32x4_t *>(Bp + n * ldb + col)
+                                       : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4_t a[C::WM];
+#pragma unroll
+      for (int i = 0; i < C::WM; ++i) a[i] = *reinterpret_cast<const u32x4_t *>(sA[0] + aoff[kk] + 2048 * i);
+#pragma unroll
+      for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::WN; ++j) acc[i][j] = mfma_32x32x16(a[i], bl[kk][j], acc[i][j]);
+    }
+  }
+  // wave w's columns: store_out's layout with WAVES_N = 4 (column block wn = w), WAVES_M = 1
+  store_out<C>(Y, N, m0, T, n0, N, 0, wave, lane, acc);
+}
+
 // ---------------------------------------------------------------- dispatch
 namespace {
 using T128x128 = TileCfg<2, 2, 2, 2>;    // 4 waves, 64x64 per wave, two workgroups per CU
@@ -765,6 +929,16 @@ hipError_t launch_nf4_gemm_fwd(int tile, const bf16_t *X, int64_t T, int64_t K, 
   if (T == 0) return hipSuccess;
   if (nsplit < 1 || (nsplit > 1 && (!psum || K % ((int64_t)nsplit * BK) != 0))) return hipErrorInvalidValue;
   if (nsplit == 1) psum = nullptr;
+#ifndef QLORA_NO_RD
+  if (tile == NF4_TILE_256x256_W8 && nsplit == 1 && !sg.seg) {  // enough 256 x 256 tiles for every CU
+    const int64_t tm = (T + RdCfg::BM - 1) / RdCfg::BM, tn = (N + RdCfg::BN - 1) / RdCfg::BN;
+    int xb_m, xb_n;
+    xcd_blocking(tm, tn, 2.0 * T * K, 0.516 * N * K, &xb_m, &xb_n);
+    launch(k_nf4_gemm_fwd_rd, dim3((unsigned)(tm * tn)), dim3(RdCfg::NT), 0, s, X, T, K, codes, absmax_q, step, N, V,
+           Bp, ldb, r, rp, Y, lv, xb_m, xb_n);
+    return hipGetLastError();
+  }
+#endif
 #define QLORA_FWD(CFG) fwd_with<CFG>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s, sg, nsplit, psum)
   switch (tile) {
     case NF4_TILE_256x256_W8: return QLORA_FWD(T256x256w8);

@@ -162,6 +162,30 @@ def test_fwd_bwd_full_parity(n_out, n_in, T, r, alpha):
         assert torch.equal(g[k], g2[k]), k
 
 
+REGISTER_DECODE = [
+    # n_out, n_in, T, r, alpha: at least 256 output tiles of 256 x 256, where the forward decodes the weights
+    # in registers (four waves per workgroup); short reductions keep the whole oracle cheap
+    (4104, 64, 4000, 5, 10.0),     # one step; ragged rows and columns; odd rank through the padded B
+    (4096, 128, 4096, 128, 256.0),  # two steps; rank 128: two LoRA steps
+    (4160, 192, 3900, 16, 32.0),   # three steps (one turn of the three-buffer loop); ragged rows
+    (4104, 256, 4001, 64, 16.0),   # four steps: the loop plus one tail step
+    (4096, 320, 4096, 8, 16.0),    # five steps: the loop plus two tail steps
+]
+
+
+@pytest.mark.parametrize("n_out,n_in,T,r,alpha", REGISTER_DECODE)
+def test_register_decode_forward_parity(n_out, n_in, T, r, alpha):
+    """The forward for training-sized outputs, checked in full against the oracle (and its backward)."""
+    print(f"register-decode forward parity n_out={n_out} n_in={n_in} T={T} r={r}", flush=True)
+    inp = linear_inputs(n_out, n_in, T, r, alpha, seed=T + n_in)
+    _, g = run_gpu(inp)
+    ref = run_oracle(inp)
+    for k in ("Y", "U", "dX", "dA", "dB"):
+        assert_close(k, gpu_f64(g[k]), ref[k])
+    _, g2 = run_gpu(inp)  # bitwise repeatable
+    assert torch.equal(g["Y"], g2["Y"])
+
+
 WHOLE_REDUCTION = [
     # n_out, n_in, T, r, alpha: >= 1024 tokens with r <= 16, where U and dU reduce inside one workgroup
     # (8-row tiles while they number at most the 256 CUs, else 16-row tiles)
