@@ -165,11 +165,12 @@ def test_fwd_bwd_full_parity(n_out, n_in, T, r, alpha):
 REGISTER_DECODE = [
     # n_out, n_in, T, r, alpha: at least 256 output tiles of 256 x 256, where the forward decodes the weights
     # in registers (four waves per workgroup); short reductions keep the whole oracle cheap
-    (4104, 64, 4000, 5, 10.0),     # one step; ragged rows and columns; odd rank through the padded B
-    (4096, 128, 4096, 128, 256.0),  # two steps; rank 128: two LoRA steps
-    (4160, 192, 3900, 16, 32.0),   # three steps (one turn of the three-buffer loop); ragged rows
-    (4104, 256, 4001, 64, 16.0),   # four steps: the loop plus one tail step
-    (4096, 320, 4096, 8, 16.0),    # five steps: the loop plus two tail steps
+    (4104, 128, 4000, 5, 10.0),     # one 128-column super-step; ragged rows and columns; odd rank (padded B)
+    (4096, 256, 4096, 128, 256.0),  # two super-steps (one turn of the double-buffered loop); rank 128
+    (4160, 384, 3900, 16, 32.0),    # three: the loop and its tail; ragged rows
+    (4104, 512, 4001, 64, 16.0),    # four
+    (4096, 640, 4096, 8, 16.0),     # five
+    (4096, 320, 4096, 16, 32.0),    # K % 128 != 0: the eight-wave kernel takes it
 ]
 
 
