@@ -666,239 +666,6 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
   store_out<C>(dX, K, m0, T, n0, K, wm, wn, lane, acc);
 }
 
-// ------------------------------------------- forward, weights decoded in registers
-// Y[T, N] = X[T, K] . W'[N, K]^T + V[T, rp] . B[N, :r]^T for outputs of at least 256 tiles of 256 x 256,
-// K % 128 == 0.
-// One workgroup of four waves (one per SIMD) per CU.  Wave w owns all 256 rows of the tile and its
-// columns 64 w .. 64 w + 63 (8 x 2 tiles of 32 x 32, binary32 accumulators in AGPRs), so the weight
-// operand of every column is needed by one wave only: each lane loads and decodes its own codes straight
-// into MFMA B-operand registers, and the weights never pass through LDS.  The activation tile (256 rows
-// x 128) is copied global -> LDS by the load unit, double-buffered, and read by all four waves; one
-// barrier per 128 columns of the reduction (two NF4 blocks, eight 16-deep substeps).
-// Reduction order: in NF4 block b the lanes of half h (lanes 32 h .. 32 h + 31) hold the columns
-// 64 b + 32 h + 8 kk .. +7 in substep kk, for both operands, so a lane's codes of one weight row and
-// block are 16 consecutive bytes (32 weights, one 16-byte load).  Each lane decodes its 8-nibble words
-// through the level-pair table in LDS (one 8-byte read per code byte), multiplies by the block constant
-// and packs to bf16 -- w' = bf16_rne(fl32(level * c')), the same values as everywhere.
-// With one wave per SIMD nothing hides a wait of that wave, so substep u is a three-stage pipeline
-// whose LDS results are always one substep old: it issues the activation reads of substep u + 1 and
-// the table reads of substep u + 2, finishes the decode of substep u + 1 from table reads issued one
-// substep earlier, and runs the 16 MFMAs of substep u, one MFMA per piece of the other work, in an
-// order pinned with scheduling barriers; its only wait is at its start.  The barrier of super-step S
-// sits at the start of its last substep: after it, the buffer of S is free for the loads of S + 2 and
-// the tile of S + 1 is complete, so that substep already reads the first operands of S + 1.
-// LDS rows of the activation tile are 256 bytes; 16-byte chunk c of row m sits at slot c ^ (m % 16).
-namespace {
-struct RdCfg {
-  static constexpr int NW = 4, NT = 256, BM = 256, BN = 256, WM = 8, WN = 2;
-  static constexpr int SK = 128;                 // reduction columns per barrier (two NF4 blocks)
-  static constexpr int A_LD = BM * SK / 8 / NT;  // direct 16-byte activation loads per thread (16)
-  static constexpr int NB = SK / BK;             // NF4 blocks per super-step
-  static constexpr int NU = 4 * NB;              // 16-deep substeps per super-step
-};
-__device__ __forceinline__ int rd_slot(int row, int chunk) { return row * RdCfg::SK + ((chunk ^ (row & 15)) << 3); }
-}  // namespace
-
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_nf4_gemm_fwd_rd(
-    const bf16_t *__restrict__ X, int64_t T, int64_t K, const uint8_t *__restrict__ codes,
-    const uint8_t *__restrict__ absmax_q, const float *__restrict__ step, int64_t N, const bf16_t *__restrict__ V,
-    const bf16_t *__restrict__ Bp, int64_t ldb, int64_t r, int64_t rp, bf16_t *__restrict__ Y, Levels lv, int xb_m,
-    int xb_n) {
-  using C = RdCfg;
-  __shared__ __attribute__((aligned(16))) bf16_t sA0[C::BM * C::SK];
-  __shared__ __attribute__((aligned(16))) bf16_t sA1[C::BM * C::SK];
-  __shared__ float2 s_lv[256];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = lane >> 5, rr = lane & 31;
-  const TileCoord tc = tile_of((N + C::BN - 1) / C::BN, xb_m, xb_n);
-  const int64_t m0 = tc.m * C::BM, n0 = tc.n * C::BN;
-  pair_levels_to_lds(lv, s_lv, tid);
-
-  const int ns = (int)(K / C::SK);  // super-steps
-  // activation loads: instruction i of wave w fills rows 4 g .. 4 g + 3 (g = 4 i + w) of the tile, lane l
-  // row 4 g + l / 16 at slot l % 16, i.e. logical chunk (l % 16) ^ (row % 16); rows past T re-read row
-  // T - 1 (their outputs are never stored).  Byte offsets from X + m0 K fit 32 bits (256 K 2 < 2^32).
-  uint32_t xoff[C::A_LD];
-#pragma unroll
-  for (int i = 0; i < C::A_LD; ++i) {
-    const int row = 4 * (4 * i + wave) + (lane >> 4);
-    const int64_t rrow = (m0 + row < T) ? row : T - 1 - m0;
-    xoff[i] = (uint32_t)(rrow * K * 2 + 16 * ((lane & 15) ^ (row & 15)));
-  }
-  const char *xbase = reinterpret_cast<const char *>(X + m0 * K);
-  auto issue_a_one = [&](int S, bf16_t *sa, int i) {
-    const char *src = xbase + 2 * (int64_t)S * C::SK + xoff[i];
-    __builtin_amdgcn_global_load_lds((const void *)src,
-                                     (__attribute__((address_space(3))) void *)(sa + (4 * i + wave) * 4 * C::SK), 16,
-                                     0, 0);
-  };
-  // this lane's two weight rows (columns of Y); rows past N re-read row N - 1 (never stored)
-  uint32_t coff[C::WN], qoff[C::WN];
-  int64_t qidx0[C::WN];
-#pragma unroll
-  for (int j = 0; j < C::WN; ++j) {
-    const int64_t n = 64 * wave + 32 * j + rr;
-    const int64_t nn = (n0 + n < N) ? n : N - 1 - n0;
-    coff[j] = (uint32_t)(nn * (K / 2) + 16 * h);
-    qoff[j] = (uint32_t)(nn * (K / BK));
-    qidx0[j] = (n0 + nn) * (K / BK);
-  }
-  const uint8_t *cbase = codes + n0 * (K / 2);
-  const uint8_t *qbase = absmax_q + n0 * (K / BK);
-  u32x4_t wd[2][C::NB][C::WN];  // codes of super-steps S (slot S % 2) and S + 1
-  RawScale rs[2][C::NB][C::WN];
-  auto load_codes = [&](int S, u32x4_t(&w)[C::NB][C::WN], RawScale(&sc)[C::NB][C::WN]) {
-#pragma unroll
-    for (int b = 0; b < C::NB; ++b) {
-      const int64_t blk = C::NB * (int64_t)S + b;
-#pragma unroll
-      for (int j = 0; j < C::WN; ++j)
-        w[b][j] = *reinterpret_cast<const u32x4_t *>(cbase + blk * (BK / 2) + coff[j]);
-#pragma unroll
-      for (int j = 0; j < C::WN; ++j) sc[b][j] = RawScale{(uint32_t)qbase[blk + qoff[j]], step[(qidx0[j] + blk) >> 8]};
-    }
-  };
-  int aoff[C::NU];  // LDS offset of this lane's A operand (row rr) in substep u; row 32 i + rr at + 32 SK i
-#pragma unroll
-  for (int u = 0; u < C::NU; ++u) aoff[u] = rd_slot(rr, 8 * (u >> 2) + 4 * h + (u & 3));
-
-  f32x16_t acc[C::WM][C::WN];
-  zero_acc<C>(acc);
-
-  // pipeline registers (two sets, alternating by substep): A operands, decoded B operands, level pairs
-  u32x4_t a[2][C::WM], bo[2][C::WN];
-  float2 pr[2][C::WN][4];
-  float cq[2][C::WN];  // block constants of the words whose pairs are in pr[.]
-
-  // word (code word) of substep u of a super-step in slot p, and the lookup of its byte k
-  auto word_of = [&](int p, int u, int j) -> uint32_t { return wd[p][u >> 2][j][u & 3]; };
-  auto gather = [&](uint32_t w, int k) -> float2 { return s_lv[(w >> (8 * k)) & 0xffu]; };
-  auto finish = [&](const float2 &l, float c) -> uint32_t { return pack_bf16x2(__fmul_rn(l.x, c), __fmul_rn(l.y, c)); };
-
-  // prologue: tiles and codes of super-steps 0 and 1; operands of substep 0 and the pairs of substep 1
-#pragma unroll
-  for (int i = 0; i < C::A_LD; ++i) issue_a_one(0, sA0, i);
-#pragma unroll
-  for (int i = 0; i < C::A_LD; ++i) issue_a_one(ns > 1 ? 1 : 0, sA1, i);
-  load_codes(0, wd[0], rs[0]);
-  load_codes(ns > 1 ? 1 : 0, wd[1], rs[1]);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < C::WM; ++i) a[0][i] = *reinterpret_cast<const u32x4_t *>(sA0 + aoff[0] + 32 * C::SK * i);
-#pragma unroll
-  for (int j = 0; j < C::WN; ++j) {
-    const float c0 = scale_of(rs[0][0][j]);
-    const uint32_t w0 = word_of(0, 0, j), w1 = word_of(0, 1, j);
-    bo[0][j] = u32x4_t{finish(gather(w0, 0), c0), finish(gather(w0, 1), c0), finish(gather(w0, 2), c0),
-                       finish(gather(w0, 3), c0)};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) pr[1][j][k] = gather(w1, k);
-    cq[1][j] = c0;  // substeps 0..3 are block 0
-  }
-
-  // substep u of super-step S (P = S % 2): see the comment above
-  auto substep = [&](auto pc, auto uc, int S) {
-    constexpr int P = decltype(pc)::value, U = decltype(uc)::value;
-    constexpr int CUR = U & 1, NXT = CUR ^ 1;
-    // substep u + 1 / u + 2 of this super-step, or the first ones of the next (slot P ^ 1, buffer P ^ 1)
-    constexpr int U1 = (U + 1) % C::NU, P1 = (U + 1 < C::NU) ? P : (P ^ 1);
-    constexpr int U2 = (U + 2) % C::NU, P2 = (U + 2 < C::NU) ? P : (P ^ 1);
-    const bf16_t *sa1 = P1 ? sA1 : sA0;
-    if constexpr (U >= C::NU - 2) {
-      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): next super-step's tile and codes are here
-    } else {
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the LDS reads of the previous substep
-    }
-    if constexpr (U == C::NU - 1) {
-      __syncthreads();  // every wave is past its reads of buffer P and its loads of buffer P ^ 1
-      const int S2 = (S + 2 < ns) ? S + 2 : ns - 1;
-#pragma unroll
-      for (int i = 0; i < C::A_LD; ++i) issue_a_one(S2, P ? sA1 : sA0, i);
-      load_codes(S2, wd[P], rs[P]);
-    }
-    fence_sched();
-    float cq2[C::WN];
-#pragma unroll
-    for (int j = 0; j < C::WN; ++j) cq2[j] = scale_of(rs[P2][U2 >> 2][j]);
-    uint32_t w2[C::WN];
-#pragma unroll
-    for (int j = 0; j < C::WN; ++j) w2[j] = word_of(P2, U2, j);
-#pragma unroll
-    for (int t = 0; t < C::WM * C::WN; ++t) {
-      acc[t >> 1][t & 1] = mfma_32x32x16(a[CUR][t >> 1], bo[CUR][t & 1], acc[t >> 1][t & 1]);
-      if (t < C::WM) {
-        a[NXT][t] = *reinterpret_cast<const u32x4_t *>(sa1 + aoff[U1] + 32 * C::SK * t);
-        const int j = t >> 2, k = t & 3;
-        bo[NXT][j][k] = finish(pr[NXT][j][k], cq[NXT][j]);
-      } else {
-        const int j = (t - C::WM) >> 2, k = (t - C::WM) & 3;
-        pr[CUR][j][k] = gather(w2[j], k);
-      }
-      fence_sched();
-    }
-#pragma unroll
-    for (int j = 0; j < C::WN; ++j) cq[CUR][j] = cq2[j];
-  };
-  auto super_p = [&](auto pc, int S) {
-#define QLORA_RD_U(u) substep(pc, std::integral_constant<int, u>(), S);
-    QLORA_RD_U(0) QLORA_RD_U(1) QLORA_RD_U(2) QLORA_RD_U(3) QLORA_RD_U(4) QLORA_RD_U(5) QLORA_RD_U(6) QLORA_RD_U(7)
-#undef QLORA_RD_U
-  };
-  static_assert(C::NU == 8, "the substep list above has eight entries");
-  int S = 0;
-  for (; S + 1 < ns; S += 2) {
-    super_p(std::integral_constant<int, 0>(), S);
-    super_p(std::integral_constant<int, 1>(), S + 1);
-  }
-  if (S < ns) super_p(std::integral_constant<int, 0>(), S);
-
-  // LoRA up-projection V [T, rp] . B [N, rp]^T (rp <= 128: one pass): the V tile through LDS, B rows
-  // straight into registers
-  {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < C::BM * C::SK / 8 / C::NT; ++i) {
-      const int c = tid + C::NT * i;
-      const int row = c >> 4, ch = c & 15;
-      const int64_t col = 8 * ch;
-      const u32x4_t v = (m0 + row < T && col < rp) ? *reinterpret_cast<const u32x4_t *>(V + (m0 + row) * rp + col)
-                                                  : u32x4_t{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4_t *>(sA0 + rd_slot(row, ch)) = v;
-    }
-    __syncthreads();
-    const int nb = (int)((rp + BK - 1) / BK);
-    for (int b = 0; b < nb; ++b) {
-      u32x4_t bl[4][C::WN];
-#pragma unroll
-      for (int j = 0; j < C::WN; ++j) {
-        const int64_t n = n0 + 64 * wave + 32 * j + rr;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int64_t col = 64 * b + 32 * h + 8 * kk;
-          bl[kk][j] = (n < N && col < r) ? *reinterpret_cast<const u32x4_t *>(Bp + n * ldb + col)
-                                         : u32x4_t{0u, 0u, 0u, 0u};
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        u32x4_t al[C::WM];
-        const int off = rd_slot(rr, 8 * b + 4 * h + kk);
-#pragma unroll
-        for (int i = 0; i < C::WM; ++i) al[i] = *reinterpret_cast<const u32x4_t *>(sA0 + off + 32 * C::SK * i);
-#pragma unroll
-        for (int i = 0; i < C::WM; ++i)
-#pragma unroll
-          for (int j = 0; j < C::WN; ++j) acc[i][j] = mfma_32x32x16(al[i], bl[kk][j], acc[i][j]);
-      }
-    }
-  }
-  // wave w's columns: store_out's layout with WAVES_N = 4 (column block wn = w), WAVES_M = 1
-  store_out<C>(Y, N, m0, T, n0, N, 0, wave, lane, acc);
-}
-
 // ---------------------------------------------------------------- dispatch
 namespace {
 using T128x128 = TileCfg<2, 2, 2, 2>;    // 4 waves, 64x64 per wave, two workgroups per CU
@@ -998,16 +765,6 @@ hipError_t launch_nf4_gemm_fwd(int tile, const bf16_t *X, int64_t T, int64_t K, 
   if (T == 0) return hipSuccess;
   if (nsplit < 1 || (nsplit > 1 && (!psum || K % ((int64_t)nsplit * BK) != 0))) return hipErrorInvalidValue;
   if (nsplit == 1) psum = nullptr;
-#ifndef QLORA_NO_RD
-  if (tile == NF4_TILE_256x256_W8 && nsplit == 1 && !sg.seg && K % RdCfg::SK == 0) {  // every CU busy
-    const int64_t tm = (T + RdCfg::BM - 1) / RdCfg::BM, tn = (N + RdCfg::BN - 1) / RdCfg::BN;
-    int xb_m, xb_n;
-    xcd_blocking(tm, tn, 2.0 * T * K, 0.516 * N * K, &xb_m, &xb_n);
-    launch(k_nf4_gemm_fwd_rd, dim3((unsigned)(tm * tn)), dim3(RdCfg::NT), 0, s, X, T, K, codes, absmax_q, step, N, V,
-           Bp, ldb, r, rp, Y, lv, xb_m, xb_n);
-    return hipGetLastError();
-  }
-#endif
 #define QLORA_FWD(CFG) fwd_with<CFG>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s, sg, nsplit, psum)
   switch (tile) {
     case NF4_TILE_256x256_W8: return QLORA_FWD(T256x256w8);
