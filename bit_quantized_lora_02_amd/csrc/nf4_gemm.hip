@@ -666,145 +666,6 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
   store_out<C>(dX, K, m0, T, n0, K, wm, wn, lane, acc);
 }
 
-// ------------------------------------------------ forward, two wave groups in alternation
-// The same product and operands as k_nf4_gemm_fwd for the eight-wave 256 x 256 tile, scheduled so that
-// on every SIMD one of its two waves multiplies while the other works on memory.  Waves 0-3 (rows
-// 0-127 of the tile) and waves 4-7 (rows 128-255) form two groups; group 1 starts one barrier interval
-// late.  A wave alternates a memory phase M(h) -- the LDS reads of the operands of half-step h (32
-// reduction columns) into registers, its share of decoding the next 64-deep step's weights into the
-// other LDS buffer, and (first half) the direct activation loads of the next step -- with a compute
-// phase C(h) of 16 MFMAs on those registers, a workgroup barrier after each phase.  In any interval
-// one group computes and the other works on memory, so each SIMD's matrix unit is fed by an MFMA-only
-// instruction stream.  Buffer lifetimes: step s is read in M(2s), M(2s+1) (intervals 4s .. 4s+3) and
-// step s+1 is written in the same intervals into the other buffer, whose reads for step s-1 ended at
-// interval 4s-1.
-template <class C>
-__global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd_pp(const bf16_t *__restrict__ X, int64_t T, int64_t K,
-                                                           const uint8_t *__restrict__ codes,
-                                                           const uint8_t *__restrict__ absmax_q,
-                                                           const float *__restrict__ step, int64_t N,
-                                                           const bf16_t *__restrict__ V, const bf16_t *__restrict__ Bp,
-                                                           int64_t ldb, int64_t r, int64_t rp, bf16_t *__restrict__ Y,
-                                                           Levels lv, int xb_m, int xb_n) {
-  static_assert(C::NW == 8 && C::WAVES_M == 2 && C::DEC == C::NT && C::NWD == 4, "tile for the alternating schedule");
-  __shared__ __attribute__((aligned(16))) bf16_t sA0[C::BM * BK];
-  __shared__ __attribute__((aligned(16))) bf16_t sA1[C::BM * BK];
-  __shared__ __attribute__((aligned(16))) bf16_t sB0[C::BN * BK];
-  __shared__ __attribute__((aligned(16))) bf16_t sB1[C::BN * BK];
-  __shared__ float2 s_lv[256];
-  bf16_t *const sA[2] = {sA0, sA1};
-  bf16_t *const sB[2] = {sB0, sB1};
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-  const TileCoord tc = tile_of((N + C::BN - 1) / C::BN, xb_m, xb_n);
-  const int64_t m0 = tc.m * C::BM, n0 = tc.n * C::BN;
-  pair_levels_to_lds(lv, s_lv, tid);
-
-  const int nk = (int)(K / BK);
-  ALoads<C> al;
-  al.init(X, K, m0, T, wave, lane);
-  constexpr int PARTS = BK / C::E;
-  const int brow = tid / PARTS, part = tid % PARTS;
-  const int64_t wrow = (n0 + brow < N) ? n0 + brow : N - 1;
-  const uint8_t *crow = codes + wrow * (K / 2) + part * (C::E / 2);
-  const int64_t blk0 = wrow * (K / BK);
-  uint32_t rc[2][C::NWD];
-  RawScale rs[2];
-  auto load_words_of = [&](int s, uint32_t(&w)[C::NWD], RawScale &sc) {
-    load_words<C::NWD>(crow + (int64_t)s * (BK / 2), w);
-    sc = load_scale(absmax_q, step, blk0 + s);
-  };
-  auto decode_word = [&](int slot, int w, bf16_t *sb) {
-    float v[8];
-    lookup8(rc[slot][w], s_lv, v);
-    *reinterpret_cast<u32x4_t *>(sb + lds_off(brow, part * C::NWD + w)) = scale_pack8(v, scale_of(rs[slot]));
-  };
-  auto barrier = [&]() {
-    fence_sched();
-    __builtin_amdgcn_s_barrier();
-    fence_sched();
-  };
-
-  f32x16_t acc[C::WM][C::WN];
-  zero_acc<C>(acc);
-
-  // prologue: activation tile 0, codes of steps 0 and 1, weights of step 0 decoded
-  al.issue(0, K, sA[0]);
-  fence_sched();
-  load_words_of(0, rc[0], rs[0]);
-  load_words_of(nk > 1 ? 1 : 0, rc[1], rs[1]);
-  __syncthreads();  // level table visible
-#pragma unroll
-  for (int w = 0; w < C::NWD; ++w) decode_word(0, w, sB[0]);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (wm == 1) barrier();  // group 1 runs one interval behind group 0
-
-  u32x4_t a[2][C::WM], b[2][C::WN];
-  auto step_p = [&](auto pc, int s) {
-    constexpr int P = decltype(pc)::value, Q = P ^ 1;  // buffers of step s and of step s + 1
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      // ---- memory phase M(2 s + q)
-      if (q == 0) {
-        // the code loads of the previous step (the last ones outstanding) have landed long ago; waiting
-        // for them here keeps the compiler from a conservative full wait after this step's loads
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-        al.issue((int64_t)((s + 1 < nk) ? s + 1 : nk - 1) * BK, K, sA[Q]);
-        fence_sched();  // the activation loads first: the wait below leaves the code loads in flight
-        load_words_of((s + 2 < nk) ? s + 2 : nk - 1, rc[P], rs[P]);
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        read_a<C>(sA[P], wm, lane, 2 * q + kk, a[kk]);
-        read_b_rows<C>(sB[P], wn, lane, 2 * q + kk, b[kk]);
-      }
-      decode_word(Q, 2 * q, sB[Q]);
-      decode_word(Q, 2 * q + 1, sB[Q]);
-      if (q == 1) __builtin_amdgcn_s_waitcnt(0x0073);  // vmcnt(3): this step's activation loads have landed
-      __builtin_amdgcn_s_waitcnt(0xc07f);               // lgkmcnt(0): operand reads and decoded stores done
-      barrier();
-      // ---- compute phase C(2 s + q)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) mma_rows<C>(0, C::WM, a[kk], b[kk], acc);
-      const bool last = (s == nk - 1) && q == 1;
-      if (!(last && wm == 1)) barrier();  // group 1 ends one barrier early: both groups count the same
-    }
-  };
-  int s = 0;
-  for (; s + 1 < nk; s += 2) {
-    step_p(std::integral_constant<int, 0>(), s);
-    step_p(std::integral_constant<int, 1>(), s + 1);
-  }
-  if (s < nk) step_p(std::integral_constant<int, 0>(), s);
-
-  // LoRA up-projection: V [T, rp] . B [N, rp]^T, one 64-deep step at a time (both groups together)
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int64_t k0 = 0; k0 < rp; k0 += BK) {
-    copy_a_tile<C>(V, rp, m0, T, k0, rp, tid, sA[0]);
-#pragma unroll
-    for (int i = 0; i < C::L_CH; ++i) {
-      const int c = tid + C::NT * i;
-      const int64_t brw = n0 + (c >> 3), col = k0 + (c & 7) * 8;  // r % 8 == 0 or B padded to ldb
-      const u32x4_t v = (brw < N && col < r) ? *reinterpret_cast<const u32x4_t *>(Bp + brw * ldb + col)
-                                             : u32x4_t{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4_t *>(sB[0] + lds_off(c >> 3, c & 7)) = v;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      u32x4_t al_[C::WM], bl_[C::WN];
-      read_a<C>(sA[0], wm, lane, kk, al_);
-      read_b_rows<C>(sB[0], wn, lane, kk, bl_);
-      mma_rows<C>(0, C::WM, al_, bl_, acc);
-    }
-    __syncthreads();
-  }
-  store_out<C>(Y, N, m0, T, n0, N, wm, wn, lane, acc);
-}
-
 // ---------------------------------------------------------------- dispatch
 namespace {
 using T128x128 = TileCfg<2, 2, 2, 2>;    // 4 waves, 64x64 per wave, two workgroups per CU
@@ -904,16 +765,6 @@ hipError_t launch_nf4_gemm_fwd(int tile, const bf16_t *X, int64_t T, int64_t K, 
   if (T == 0) return hipSuccess;
   if (nsplit < 1 || (nsplit > 1 && (!psum || K % ((int64_t)nsplit * BK) != 0))) return hipErrorInvalidValue;
   if (nsplit == 1) psum = nullptr;
-#ifndef QLORA_NO_PP
-  if (tile == NF4_TILE_256x256_W8 && nsplit == 1 && !sg.seg) {
-    const int64_t tm = (T + 255) / 256, tn = (N + 255) / 256;
-    int xb_m, xb_n;
-    xcd_blocking(tm, tn, 2.0 * T * K, 0.516 * N * K, &xb_m, &xb_n);
-    launch(k_nf4_gemm_fwd_pp<T256x256w8>, dim3((unsigned)(tm * tn)), dim3(T256x256w8::NT), 0, s, X, T, K, codes,
-           absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, xb_m, xb_n);
-    return hipGetLastError();
-  }
-#endif
 #define QLORA_FWD(CFG) fwd_with<CFG>(X, T, K, codes, absmax_q, step, N, V, Bp, ldb, r, rp, Y, lv, s, sg, nsplit, psum)
   switch (tile) {
     case NF4_TILE_256x256_W8: return QLORA_FWD(T256x256w8);
