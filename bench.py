@@ -226,7 +226,7 @@ def cpu_baseline(inps, train: bool, target_s: float, slice_cap: int):
         return time.perf_counter() - t0
 
     cap = max(1, min(T, slice_cap))
-    ts = min(cap, 4)
+    ts = min(cap, 16)
     dt = run(ts)
     budget = max(2.0, target_s - t_q - t_d)
     ts = int(max(1, min(cap, ts * budget / max(dt, 1e-3))))

@@ -176,6 +176,13 @@ __device__ __forceinline__ void read_b_rows(const bf16_t *sb, int wn, int lane, 
   for (int j = 0; j < C::WN; ++j)
     b[j] = *reinterpret_cast<const u32x4_t *>(sb + lds_off((wn * C::WN + j) * 32 + (lane & 31), chunk));
 }
+// 16-byte chunk c of row `row` of the dX weight tile sits at chunk slot c ^ 2 ((c >> 4) & 1) ^ (row & 1):
+// a 16-lane phase of the decoded-tile stores (two rows, eight 32-column pieces) then covers 16 distinct
+// 16-byte bank groups, and the slots only move within aligned groups of four chunks, so the transposing
+// reads stay conflict-free.
+__device__ __forceinline__ int dx_off(int row, int chunk, int ldb) {
+  return row * ldb + ((chunk ^ (((chunk >> 4) & 1) << 1) ^ (row & 1)) << 3);
+}
 // B operand from a natural [k][LDB] tile with two transposing reads per tile:
 // in each 16-lane group, lane i gets element (i & 3) of the 8 bytes addressed
 // by lane 4m + (i >> 2), so lane a points at row base + (a >> 2), columns
@@ -187,8 +194,9 @@ __device__ __forceinline__ u32x4_t read_b_tr_one(const bf16_t *sb, int wn, int l
   const int grp = lane >> 4, ai = lane & 15;
   const int row = kk * 16 + 8 * (grp >> 1) + (ai >> 2);
   const int col = (wn * C::WN + j) * 32 + 16 * (grp & 1) + 4 * (ai & 3);
-  const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(sb + row * LDB + col));
-  const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(sb + (row + 4) * LDB + col));
+  const int off = dx_off(row, col >> 3, LDB) + (col & 7);
+  const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(sb + off));
+  const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(sb + off + 4 * LDB));
   const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
   return u32x4_t{l2.x, l2.y, h2.x, h2.y};
 }
@@ -566,7 +574,7 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
         const int64_t j = k0 + c / (C::BN / 8), kcol = n0 + (c % (C::BN / 8)) * 8;
         const u32x4_t v =
             (j < r && kcol < K) ? *reinterpret_cast<const u32x4_t *>(A + j * K + kcol) : u32x4_t{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4_t *>(sB[0] + (c / (C::BN / 8)) * LDB + (c % (C::BN / 8)) * 8) = v;
+        *reinterpret_cast<u32x4_t *>(sB[0] + dx_off(c / (C::BN / 8), c % (C::BN / 8), LDB)) = v;
       }
       __syncthreads();
 #pragma unroll
@@ -589,7 +597,7 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
       for (int w = 0; w < C::NWD; ++w) {
         float v[8];
         lookup8(rc[0][w], s_lv, v);
-        *reinterpret_cast<u32x4_t *>(sB[0] + bn * LDB + piece * C::E + 8 * w) = scale_pack8(v, cq);
+        *reinterpret_cast<u32x4_t *>(sB[0] + dx_off(bn, piece * (C::E / 8) + w, LDB)) = scale_pack8(v, cq);
       }
   }
   __builtin_amdgcn_s_waitcnt(0);  // the direct loads of tile 0 have landed
@@ -604,7 +612,7 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
       load_words_of(sc, rc[P], rs[P]);
     };
     auto store_word = [&](int w, const u32x4_t &o) {
-      *reinterpret_cast<u32x4_t *>(sB[P ^ 1] + bn * LDB + piece * C::E + 8 * w) = o;
+      *reinterpret_cast<u32x4_t *>(sB[P ^ 1] + dx_off(bn, piece * (C::E / 8) + w, LDB)) = o;
     };
     pipelined_step<C>(sA[P], sB[P], wm, wn, lane, rc[P ^ 1], rs[P ^ 1], s_lv, acc, read_b, load_next,
                       store_word, decoder);
@@ -636,7 +644,7 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
         const int64_t j = (int64_t)c * BK + cc / (C::BN / 8), kcol = n0 + (cc % (C::BN / 8)) * 8;
         const u32x4_t v =
             (j < r && kcol < K) ? *reinterpret_cast<const u32x4_t *>(A + j * K + kcol) : u32x4_t{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4_t *>(sB[c] + (cc / (C::BN / 8)) * LDB + (cc % (C::BN / 8)) * 8) = v;
+        *reinterpret_cast<u32x4_t *>(sB[c] + dx_off(cc / (C::BN / 8), cc % (C::BN / 8), LDB)) = v;
       }
     }
     __syncthreads();
