@@ -601,16 +601,17 @@ int linear_bwd(const qlora_bf16 *X, const qlora_bf16 *dY, int64_t T, const qlora
   }
   // dB = s dY^T U  -> [N, r]
   LAUNCH("lora_db", launch_skinny(true, true, p.rn, dY, N, N, Usrc, ldu, rvu, T, p.sdb.kchunk, p.sdb.n, part, s));
-  // dA^T = X^T dU  -> [K, r], stored transposed as dA [r, K]
+  // dA^T = X^T dU  -> [K, r], its partial sums stored by rank as [split][rn][K]
   float *part2 = (float *)(w + p.off_part2);
   if (drop)  // dA^T = Xd^T dU
     LAUNCH("lora_da_dropout", launch_skinny(true, true, p.rn, X, K, K, dUp, p.rp, p.rv, T, p.sda.kchunk, p.sda.n,
-                                            part2, s, DROP_APPLY, *drop));
+                                            part2, s, DROP_APPLY, *drop, true));
   else
-    LAUNCH("lora_da", launch_skinny(true, true, p.rn, X, K, K, dUp, p.rp, p.rv, T, p.sda.kchunk, p.sda.n, part2, s));
-  // dB = s (sum of dB's partials), dA = (sum of dA's partials)^T, one launch
-  LAUNCH("lora_dadb_finalize", launch_finalize_pair(part, p.sdb.n, N, p.rn, dB, r, r, sc, false, part2, p.sda.n, K,
-                                                    p.rn, dA, K, r, 1.0f, true, s));
+    LAUNCH("lora_da", launch_skinny(true, true, p.rn, X, K, K, dUp, p.rp, p.rv, T, p.sda.kchunk, p.sda.n, part2, s,
+                                    DROP_NONE, DropParams(), true));
+  // dB = s (sum of dB's partials) [N, r], dA = (sum of dA's partials) [r, K] (rows r of rn), one launch
+  LAUNCH("lora_dadb_finalize", launch_finalize_pair(part, p.sdb.n, N, p.rn, dB, r, r, sc, part2, p.sda.n, r, K,
+                                                    (int64_t)p.rn * K, dA, K, K, 1.0f, s));
   // dX = dY W' + dU A   (with dropout: + (keep q) o (dU A))
   if (dX)
     LAUNCH("nf4_gemm_dx",

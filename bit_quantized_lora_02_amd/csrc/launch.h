@@ -138,7 +138,7 @@ void skinny_plan(int64_t M, int64_t Kred, int *nsplit, int64_t *kchunk);
 void skinny_plan_grouped(int64_t M, int64_t n_seg, int64_t Kred, int *nsplit, int64_t *kchunk);
 hipError_t launch_skinny(bool pt, bool qt, int rn, const bf16_t *P, int64_t ldp, int64_t M, const bf16_t *Q,
                          int64_t ldq, int64_t Rv, int64_t Kred, int64_t kchunk, int nsplit, float *C, hipStream_t s,
-                         int drop = DROP_NONE, const DropParams &dp = DropParams());
+                         int drop = DROP_NONE, const DropParams &dp = DropParams(), bool ct = false);
 // U of a batch with many adapters: C[split][t][j] = sum over the range of P[t, k] Q_a[j, k] with
 // Q_a = Q_pool + a q_stride for token t's adapter a (rows P [M, ldp], Q_a [r, ldq]; none: zero).
 hipError_t launch_skinny_grouped(int rn, const bf16_t *P, int64_t ldp, int64_t M, const bf16_t *Q_pool, int64_t ldq,
@@ -146,12 +146,12 @@ hipError_t launch_skinny_grouped(int rn, const bf16_t *P, int64_t ldp, int64_t M
                                  const SegTable &sg, float *C, hipStream_t s);
 hipError_t launch_finalize(const float *part, int nsplit, int64_t M, int64_t N, bf16_t *out1, int64_t ld1, int64_t n1,
                            float scale1, bf16_t *out2, int64_t ld2, int64_t n2, int64_t nvalid2, float scale2,
-                           hipStream_t s, bool trans1 = false);
-// Two finalize jobs with one output each, in one launch.
+                           hipStream_t s);
+// Two finalize jobs with one output each, in one launch; job b's splits are sstride_b apart (0: M_b N_b).
 hipError_t launch_finalize_pair(const float *part_a, int nsplit_a, int64_t M_a, int64_t N_a, bf16_t *out_a,
-                                int64_t ld_a, int64_t n_a, float scale_a, bool trans_a, const float *part_b,
-                                int nsplit_b, int64_t M_b, int64_t N_b, bf16_t *out_b, int64_t ld_b, int64_t n_b,
-                                float scale_b, bool trans_b, hipStream_t s);
+                                int64_t ld_a, int64_t n_a, float scale_a, const float *part_b, int nsplit_b,
+                                int64_t M_b, int64_t N_b, int64_t sstride_b, bf16_t *out_b, int64_t ld_b, int64_t n_b,
+                                float scale_b, hipStream_t s);
 // The same contraction (pt = 0) with the whole reduction in each workgroup, writing the finalize
 // outputs directly (no partial sums, no second launch); lora_rows_ok(rn, M) says where it is used.
 bool lora_rows_ok(int rn, int64_t M);

@@ -103,7 +103,9 @@ __device__ __forceinline__ u32x4_t apply_keep(const u32x4_t &v, uint32_t bits, f
 // segments in order (tiles never straddle a segment), with Q the segment's
 // adapter Q + a q_stride (none: Rv = 0, all zero); rows past the segment read
 // as zero and are not stored.
-template <bool PT, bool QT, int RN, int DM, bool GR = false>
+// With CT the partial sums are stored by rank column instead: C[split][j][m] (M % 4 == 0), so that a
+// finalize reading them for an output [r][M] (dA) loads and stores along m.
+template <bool PT, bool QT, int RN, int DM, bool GR = false, bool CT = false>
 __global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, int64_t ldp, int64_t M,
                                                 const bf16_t *__restrict__ Q, int64_t ldq, int64_t Rv, int64_t Kred,
                                                 int64_t kchunk, float *__restrict__ C, DropParams dp,
@@ -273,12 +275,16 @@ __global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, in
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < NT_; ++j)
+    for (int j = 0; j < NT_; ++j) {
+      const int64_t mb = m0 + wave * 32 + i * 16 + 4 * g;
+      if constexpr (CT) {  // the lane's four rows are consecutive: one 16-byte store (M % 4 == 0: all or none)
+        if (mb < mend) *reinterpret_cast<f32x4s_t *>(Cs + (int64_t)(j * 16 + a) * M + mb) = acc[i][j];
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t m = m0 + wave * 32 + i * 16 + 4 * g + e;
-        if (m < mend) Cs[m * RN + j * 16 + a] = acc[i][j][e];
+        for (int e = 0; e < 4; ++e)
+          if (mb + e < mend) Cs[(mb + e) * RN + j * 16 + a] = acc[i][j][e];
       }
+    }
 }
 
 // ------------------------------------------------- whole-reduction variant
@@ -385,13 +391,13 @@ __global__ __launch_bounds__(1024) void k_lora_rows(const bf16_t *__restrict__ P
 }
 
 // One finalize job: S = sum over splits p = 0 .. nsplit-1 (in that order) of
-// part[p][m][n] (ld = N), then
-//   out1[m*ld1 + n] (or out1[n*ld1 + m] with trans1) = bf16(scale1 * S) for n < n1,
+// part[p sstride + m N + n], then
+//   out1[m*ld1 + n] = bf16(scale1 * S) for n < n1,
 //   out2[m*ld2 + n] = n < nvalid2 ? bf16(scale2 * S) : 0 for n < n2.
 struct FinJob {
   const float *part;
-  int nsplit, trans1;
-  int64_t M, N;
+  int nsplit;
+  int64_t M, N, sstride;
   bf16_t *out1;
   int64_t ld1, n1;
   float scale1, scale2;
@@ -403,13 +409,12 @@ struct FinJob {
 __device__ __forceinline__ void finalize_one(const FinJob &j, int64_t i) {
   const int64_t ncol = (j.n1 > j.n2) ? j.n1 : j.n2;
   if (i >= j.M * ncol) return;
-  // transposed first output: consecutive threads take consecutive m so its stores coalesce
-  const int64_t m = j.trans1 ? i % j.M : i / ncol, n = j.trans1 ? i / j.M : i - m * ncol;
+  const int64_t m = i / ncol, n = i - m * ncol;
   float sum = 0.f;
   if (n < j.N) {
     // all loads first, then the additions in split order
     const float *src = j.part + m * j.N + n;
-    const int64_t stride = j.M * j.N;
+    const int64_t stride = j.sstride;
     int p = 0;
     for (; p + 8 <= j.nsplit; p += 8) {
       float v[8];
@@ -420,7 +425,7 @@ __device__ __forceinline__ void finalize_one(const FinJob &j, int64_t i) {
     }
     for (; p < j.nsplit; ++p) sum += src[(int64_t)p * stride];
   }
-  if (j.out1 && n < j.n1) j.out1[j.trans1 ? n * j.ld1 + m : m * j.ld1 + n] = f32_to_bf16(j.scale1 * sum);
+  if (j.out1 && n < j.n1) j.out1[m * j.ld1 + n] = f32_to_bf16(j.scale1 * sum);
   if (j.out2 && n < j.n2) j.out2[m * j.ld2 + n] = (n < j.nvalid2) ? f32_to_bf16(j.scale2 * sum) : (bf16_t)0;
 }
 
@@ -442,13 +447,13 @@ __global__ __launch_bounds__(256) void k_pad_copy(const bf16_t *__restrict__ in,
 
 namespace {
 FinJob fin_job(const float *part, int nsplit, int64_t M, int64_t N, bf16_t *out1, int64_t ld1, int64_t n1,
-               float scale1, bf16_t *out2, int64_t ld2, int64_t n2, int64_t nvalid2, float scale2, bool trans1) {
+               float scale1, bf16_t *out2, int64_t ld2, int64_t n2, int64_t nvalid2, float scale2, int64_t sstride) {
   FinJob j;
   j.part = part;
   j.nsplit = nsplit;
-  j.trans1 = trans1 ? 1 : 0;
   j.M = M;
   j.N = N;
+  j.sstride = sstride > 0 ? sstride : M * N;
   j.out1 = out1;
   j.ld1 = ld1;
   j.n1 = n1;
@@ -466,8 +471,8 @@ FinJob fin_job(const float *part, int nsplit, int64_t M, int64_t N, bf16_t *out1
 
 hipError_t launch_finalize(const float *part, int nsplit, int64_t M, int64_t N, bf16_t *out1, int64_t ld1, int64_t n1,
                            float scale1, bf16_t *out2, int64_t ld2, int64_t n2, int64_t nvalid2, float scale2,
-                           hipStream_t s, bool trans1) {
-  const FinJob a = fin_job(part, nsplit, M, N, out1, ld1, n1, scale1, out2, ld2, n2, nvalid2, scale2, trans1);
+                           hipStream_t s) {
+  const FinJob a = fin_job(part, nsplit, M, N, out1, ld1, n1, scale1, out2, ld2, n2, nvalid2, scale2, 0);
   if (a.nblocks == 0) return hipSuccess;
   FinJob none = a;
   none.nblocks = 0;
@@ -476,11 +481,11 @@ hipError_t launch_finalize(const float *part, int nsplit, int64_t M, int64_t N, 
 }
 
 hipError_t launch_finalize_pair(const float *part_a, int nsplit_a, int64_t M_a, int64_t N_a, bf16_t *out_a,
-                                int64_t ld_a, int64_t n_a, float scale_a, bool trans_a, const float *part_b,
-                                int nsplit_b, int64_t M_b, int64_t N_b, bf16_t *out_b, int64_t ld_b, int64_t n_b,
-                                float scale_b, bool trans_b, hipStream_t s) {
-  const FinJob a = fin_job(part_a, nsplit_a, M_a, N_a, out_a, ld_a, n_a, scale_a, nullptr, 0, 0, 0, 0.f, trans_a);
-  const FinJob b = fin_job(part_b, nsplit_b, M_b, N_b, out_b, ld_b, n_b, scale_b, nullptr, 0, 0, 0, 0.f, trans_b);
+                                int64_t ld_a, int64_t n_a, float scale_a, const float *part_b, int nsplit_b,
+                                int64_t M_b, int64_t N_b, int64_t sstride_b, bf16_t *out_b, int64_t ld_b, int64_t n_b,
+                                float scale_b, hipStream_t s) {
+  const FinJob a = fin_job(part_a, nsplit_a, M_a, N_a, out_a, ld_a, n_a, scale_a, nullptr, 0, 0, 0, 0.f, 0);
+  const FinJob b = fin_job(part_b, nsplit_b, M_b, N_b, out_b, ld_b, n_b, scale_b, nullptr, 0, 0, 0, 0.f, sstride_b);
   if (a.nblocks + b.nblocks == 0) return hipSuccess;
   launch(k_finalize, dim3((unsigned)(a.nblocks + b.nblocks)), dim3(256), 0, s, a, b);
   return hipGetLastError();
@@ -548,24 +553,30 @@ void skinny_plan_grouped(int64_t M, int64_t n_seg, int64_t Kred, int *nsplit, in
   *nsplit = Kred > 0 ? (int)((Kred + *kchunk - 1) / *kchunk) : 0;
 }
 
-template <bool PT, bool QT, int DM>
+template <bool PT, bool QT, int DM, bool CT = false>
 static hipError_t skinny_dispatch(int rn, dim3 grid, hipStream_t s, const bf16_t *P, int64_t ldp, int64_t M,
                                   const bf16_t *Q, int64_t ldq, int64_t Rv, int64_t Kred, int64_t kchunk, float *C,
                                   const DropParams &dp) {
+  const SegTable none;
   switch (rn) {
-    case 16: launch((k_skinny<PT, QT, 16, DM>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp, SegTable(), (int64_t)0); break;
-    case 32: launch((k_skinny<PT, QT, 32, DM>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp, SegTable(), (int64_t)0); break;
-    case 64: launch((k_skinny<PT, QT, 64, DM>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp, SegTable(), (int64_t)0); break;
-    default: launch((k_skinny<PT, QT, 128, DM>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp, SegTable(), (int64_t)0); break;
+    case 16: launch((k_skinny<PT, QT, 16, DM, false, CT>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp, none, (int64_t)0); break;
+    case 32: launch((k_skinny<PT, QT, 32, DM, false, CT>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp, none, (int64_t)0); break;
+    case 64: launch((k_skinny<PT, QT, 64, DM, false, CT>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp, none, (int64_t)0); break;
+    default: launch((k_skinny<PT, QT, 128, DM, false, CT>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp, none, (int64_t)0); break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_skinny(bool pt, bool qt, int rn, const bf16_t *P, int64_t ldp, int64_t M, const bf16_t *Q,
                          int64_t ldq, int64_t Rv, int64_t Kred, int64_t kchunk, int nsplit, float *C, hipStream_t s,
-                         int drop, const DropParams &dp) {
+                         int drop, const DropParams &dp, bool ct) {
   if (M == 0 || nsplit == 0) return hipSuccess;
   dim3 grid((unsigned)((M + SBM - 1) / SBM), (unsigned)nsplit);
+  if (ct && !(pt && qt)) return hipErrorInvalidValue;  // stored by rank column only for dA^T = X^T dU
+  if (ct && drop == DROP_APPLY)
+    return skinny_dispatch<true, true, DROP_APPLY, true>(rn, grid, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp);
+  if (ct && drop == DROP_NONE)
+    return skinny_dispatch<true, true, DROP_NONE, true>(rn, grid, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp);
   // dropout applies to the layer input: U = Xd A^T (P = X by rows) and dA^T = Xd^T dU (P = X by columns)
   if (drop == DROP_GENERATE && !pt && !qt)
     return skinny_dispatch<false, false, DROP_GENERATE>(rn, grid, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp);
