@@ -369,7 +369,9 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_fwd(const bf16_t *__restrict
   __shared__ __attribute__((aligned(16))) bf16_t sA1[C::BM * BK];
   __shared__ __attribute__((aligned(16))) bf16_t sB0[C::BN * BK];
   __shared__ __attribute__((aligned(16))) bf16_t sB1[C::BN * BK];
-  __shared__ float2 s_lv[256];  // level pairs by code byte
+  // level pairs by code byte; the alignment places the table at LDS address 0, so that a lookup address
+  // is the code byte times 8 (one shift with a byte select; no base to add)
+  __shared__ __attribute__((aligned(1024))) float2 s_lv[256];
   bf16_t *const sA[2] = {sA0, sA1};
   bf16_t *const sB[2] = {sB0, sB1};
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -532,7 +534,9 @@ __global__ __launch_bounds__(C::NT) void k_nf4_gemm_dx(const bf16_t *__restrict_
   __shared__ __attribute__((aligned(16))) bf16_t sA1[C::BM * BK];
   __shared__ __attribute__((aligned(16))) bf16_t sB0[BK * LDB];
   __shared__ __attribute__((aligned(16))) bf16_t sB1[BK * LDB];
-  __shared__ float2 s_lv[256];  // level pairs by code byte
+  // level pairs by code byte; the alignment places the table at LDS address 0, so that a lookup address
+  // is the code byte times 8 (one shift with a byte select; no base to add)
+  __shared__ __attribute__((aligned(1024))) float2 s_lv[256];
   bf16_t *const sA[2] = {sA0, sA1};
   bf16_t *const sB[2] = {sB0, sB1};
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
