@@ -58,6 +58,36 @@ __device__ __forceinline__ u32x4_t decode8_pairs(uint32_t w, float cq, const flo
   return o;
 }
 
+// The level-pair table in 32 interleaved copies (64 KB): entry e of copy c sits at byte
+// 256 e + 8 c, i.e. in bank pair c of the 64 four-byte banks.  Lane l reads copy l % 32, so
+// the 32 lanes of one half-wave -- the lanes an 8-byte LDS read serves together -- touch 32
+// distinct bank pairs whatever their code bytes (one copy gives a random byte mix about
+// 3.5-way bank conflicts).  Thread i of the nt >= 1024 threads writes copies 8 (i & 3) ..
+// 8 (i & 3) + 7 of entry i / 4.
+constexpr int kTabCopies = 32;
+__device__ __forceinline__ void pair_levels_rep32(const Levels &lv, float2 *tab, int tid) {
+  if (tid < 1024) {
+    const int e = tid >> 2, c0 = 8 * (tid & 3);
+    float lo = 0.f, hi = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      lo = ((e & 15) == i) ? lv.v[i] : lo;
+      hi = ((e >> 4) == i) ? lv.v[i] : hi;
+    }
+    const u32x4_t v = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi),
+                       __builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+#pragma unroll
+    for (int c = 0; c < 8; c += 2) *reinterpret_cast<u32x4_t *>(tab + e * kTabCopies + c0 + c) = v;
+  }
+}
+// Levels of the two nibbles of byte b of w from the replicated table; c8 = 8 (lane % 32).  The
+// byte offset 256 byte + c8 is one byte permute: [c8, byte b of w, 0, 0].
+template <int B>
+__device__ __forceinline__ float2 pair_rep32(const float2 *tab, uint32_t w, uint32_t c8) {
+  const uint32_t off = __builtin_amdgcn_perm(w, c8, 0x0C0C0000u | ((4u + B) << 8));
+  return *reinterpret_cast<const float2 *>(reinterpret_cast<const char *>(tab) + off);
+}
+
 // Sum over the 64 lanes of a wave with DPP moves: pairs, quads, half rows and rows of 16
 // (quad_perm, row_half_mirror, row_mirror), then row 0 into row 1 and row 2 into row 3
 // (row_bcast:15), then rows 0..1 into rows 2..3 (row_bcast:31).  The total lands in lane 63.
@@ -291,16 +321,20 @@ __global__ __launch_bounds__(256) void k_nf4_gemv(const bf16_t *__restrict__ X, 
 // 2048 c + 32 l .. 2048 c + 32 l + 31 of chunk c of the segment, so one
 // 16-byte load per lane and chunk streams 1 KB of one row per wave
 // instruction, like a plain copy.  Since a workgroup keeps one segment for the
-// whole launch, every lane keeps its TT CH 32 activations in registers (loaded
-// once; no LDS traffic for them).  Per item a lane decodes its 32 CH weights
+// whole launch, every lane keeps its TT CH 32 activations in registers, loaded
+// once: the workgroup copies the segment's activations into LDS and each wave
+// takes its lanes' share from there (one global read per workgroup instead of
+// one per wave; measured 2-4% faster).  Per item a lane decodes its 32 CH weights
 // byte by byte through the level-pair table into bf16 pairs fl32(level * c')
 // and accumulates v_dot2_f32_bf16 with the matching activation pairs; a wave
 // reduction then gives the binary32 partial sum of that segment.
 //
-// Main workgroup g owns segment g % nseg, and its wave w the rows
-// 4 (g / nseg) + w + i 4 gmain / nseg (gmain % nseg == 0).  A wave loads the
-// next item while it computes the current one, in two fixed register slots
-// (the loop runs two items per iteration, so no slot is ever copied: a copy of
+// Main workgroup g (NWV waves) owns segment g % nseg, and its wave w the rows
+// NWV (g / nseg) + w + i NWV gmain / nseg (gmain % nseg == 0).  With sixteen
+// waves the level pairs come from the replicated table above (bank-conflict
+// free, 64 KB, so two workgroups per CU); with four, from one copy.  A wave
+// keeps SLOTS - 1 items in flight while it computes one, in fixed register
+// slots (the loop is unrolled by SLOTS, so no slot is ever copied: a copy of
 // a register whose load is in flight would make the wave wait for it).  The
 // wave index is made wave-uniform, so the item bookkeeping and addresses stay
 // in scalar registers.  The block constants of an item: lane l's block in
@@ -309,23 +343,27 @@ __global__ __launch_bounds__(256) void k_nf4_gemv(const bf16_t *__restrict__ X, 
 // 32 CH blocks share one binary32 step (32 CH divides 256 and the item's
 // first block is a multiple of 32 CH).  part is [nseg][T][N] binary32.
 // Workgroups 0 .. nsplit_u - 1 come first and form the U partials of K range
-// u as in k_nf4_gemv ([4 nsplit_u][T][r]).  Tokens T .. TT-1 are zero.
-template <int TT, int CH>
-__global__ __launch_bounds__(256, TT == 1 ? 8 : 6) void k_nf4_gemv_rows(
+// u as in k_nf4_gemv ([4 nsplit_u][T][r]; their waves past the fourth have nothing to do).  Tokens
+// T .. TT-1 are zero.
+template <int TT, int CH, int SLOTS, int NWV, int MINW>
+__global__ __launch_bounds__(64 * NWV, MINW) void k_nf4_gemv_rows(
     const bf16_t *__restrict__ X, int64_t T, int64_t K, const uint8_t *__restrict__ codes,
     const uint8_t *__restrict__ absmax_q, const float *__restrict__ step, int64_t N, int gmain, int nseg, int nsplit_u,
     const bf16_t *__restrict__ A, int64_t r, float *__restrict__ part, float *__restrict__ upart, Levels lv) {
-  __shared__ __attribute__((aligned(16))) float2 s_tab[256];
+  constexpr bool REP = NWV == 16;  // sixteen waves share the replicated table
+  constexpr int Ks = 2048 * CH;
+  __shared__ __attribute__((aligned(16))) float2 s_tab[REP ? 256 * kTabCopies : 256];
+  __shared__ __attribute__((aligned(16))) uint32_t s_x[TT][Ks / 2];  // the segment's activations
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if ((int)blockIdx.x < nsplit_u) {
+    if (wave >= 4) return;
     const int64_t u = blockIdx.x, kchunk = K / nsplit_u, kb = u * kchunk;
     lora_u_partial<1>(X, T, K, A, r, kb, kb + kchunk, upart + (u * 4 + wave) * T * r, wave, lane);
     return;
   }
-  constexpr int Ks = 2048 * CH;
   const int g = (int)blockIdx.x - nsplit_u, seg = g % nseg;
-  const int64_t row0 = (int64_t)(g / nseg) * 4 + wave, rstride = (int64_t)(gmain / nseg) * 4;
+  const int64_t row0 = (int64_t)(g / nseg) * NWV + wave, rstride = (int64_t)(gmain / nseg) * NWV;
   const int64_t items = row0 < N ? (N - row0 + rstride - 1) / rstride : 0;
 
   struct Slot {
@@ -347,10 +385,22 @@ __global__ __launch_bounds__(256, TT == 1 ? 8 : 6) void k_nf4_gemv_rows(
     sl.d = step[b0 >> 8];
     if (li + 1 < items) ++li;
   };
-  Slot s0, s1;
-  if (items > 0) load_slot(s0);  // in flight while the activations and the table are loaded
+  Slot sl[SLOTS];
+#pragma unroll
+  for (int j = 0; j + 1 < SLOTS; ++j)  // in flight while the activations and the table are loaded
+    if (items > 0) load_slot(sl[j]);
 
-  pair_levels_to_lds(lv, s_tab, tid);
+  if constexpr (REP) pair_levels_rep32(lv, s_tab, tid);
+  else pair_levels_to_lds(lv, s_tab, tid);
+  const uint32_t c8 = 8u * (lane & 31);
+  // the workgroup reads the segment's activations once (every wave of it needs all of them), through LDS
+  for (int i = tid; i < TT * Ks / 8; i += 64 * NWV) {
+    const int t = i / (Ks / 8), c = i % (Ks / 8);
+    *reinterpret_cast<u32x4_t *>(&s_x[t][4 * c]) =
+        t < T ? *reinterpret_cast<const u32x4_t *>(X + t * K + seg * Ks + 8 * c) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  if (items <= 0) return;
   uint32_t xr[TT][CH][16];
 #pragma unroll
   for (int t = 0; t < TT; ++t)
@@ -358,13 +408,10 @@ __global__ __launch_bounds__(256, TT == 1 ? 8 : 6) void k_nf4_gemv_rows(
     for (int c = 0; c < CH; ++c)
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        const u32x4_t v = t < T ? *reinterpret_cast<const u32x4_t *>(X + t * K + seg * Ks + 2048 * c + 32 * lane + 8 * h)
-                                : u32x4_t{0u, 0u, 0u, 0u};
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(&s_x[t][1024 * c + 16 * lane + 4 * h]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) xr[t][c][4 * h + e] = v[e];
       }
-  __syncthreads();
-  if (items <= 0) return;
 
   float *pseg = part + (int64_t)seg * T * N;
   int64_t cn = row0;  // row of the item being computed
@@ -379,9 +426,17 @@ __global__ __launch_bounds__(256, TT == 1 ? 8 : 6) void k_nf4_gemv_rows(
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd) {
         const uint32_t w = cur.c[c][wd];
+        float2 lp[4];
+        if constexpr (REP) {
+          lp[0] = pair_rep32<0>(s_tab, w, c8), lp[1] = pair_rep32<1>(s_tab, w, c8);
+          lp[2] = pair_rep32<2>(s_tab, w, c8), lp[3] = pair_rep32<3>(s_tab, w, c8);
+        } else {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) lp[b] = s_tab[(w >> (8 * b)) & 0xffu];
+        }
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          const float2 l = s_tab[(w >> (8 * b)) & 0xffu];
+          const float2 l = lp[b];
           const bf16x2_t wp = __builtin_bit_cast(bf16x2_t, pack_bf16x2(__fmul_rn(l.x, cq), __fmul_rn(l.y, cq)));
 #pragma unroll
           for (int t = 0; t < TT; ++t) {
@@ -398,12 +453,16 @@ __global__ __launch_bounds__(256, TT == 1 ? 8 : 6) void k_nf4_gemv_rows(
     }
     cn += rstride;
   };
+  // step j computes slot j % SLOTS and refills slot (j + SLOTS - 1) % SLOTS; unrolled by SLOTS so that
+  // every slot index is a constant
   int64_t f = 0;
-  for (; f + 1 < items; f += 2) {
-    do_step(s0, s1);
-    do_step(s1, s0);
+  for (; f + SLOTS <= items; f += SLOTS) {
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) do_step(sl[j], sl[(j + SLOTS - 1) % SLOTS]);
   }
-  if (f < items) do_step(s0, s1);
+#pragma unroll
+  for (int j = 0; j + 1 < SLOTS; ++j)
+    if (f + j < items) do_step(sl[j], sl[(j + SLOTS - 1) % SLOTS]);
 }
 
 // ------------------------------------------- the row-group GEMV (3..64 tokens)
@@ -807,31 +866,33 @@ hipError_t launch_gemv_finish(const float *part, const float *upart, int nsplit,
   return hipGetLastError();
 }
 
-// one or two tokens (from three on the MFMA GEMV is faster); two 2048-column chunks per item for one
-// token when K allows, one for two tokens (their activations take 32 TT CH registers)
-static int rows_tt(int64_t T) { return T <= 1 ? 1 : 2; }
-static int rows_ch(int64_t T, int64_t K) { return rows_tt(T) == 1 && K % 4096 == 0 ? 2 : 1; }
-int nf4_gemv_rows_nseg(int64_t T, int64_t K) {
-  if (T < 1 || T > 2 || K <= 0 || K % 2048 != 0) return 0;
-  const int64_t ns = K / (2048 * rows_ch(T, K));
-  return ns <= kFinishMaxSplit ? (int)ns : 0;
-}
-bool nf4_gemv_rows_ok(int64_t T, int64_t K) { return nf4_gemv_rows_nseg(T, K) > 0; }
-
-// Workgroups of one variant resident on the device at once (computed once per variant and thread).
-template <int TT, int CH>
-static int rows_resident() {
-  static thread_local int res = 0;
-  if (res > 0) return res;
+// Workgroups of a kernel resident on the device at once.
+template <class Kern>
+static int resident(Kern kern, int threads) {
   int dev = 0, cus = 0, nb = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_nf4_gemv_rows<TT, CH>, 256, 0) != hipSuccess || nb < 1 ||
-      cus < 1)
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, threads, 0) != hipSuccess || nb < 1 || cus < 1)
     return 0;
-  res = nb * cus;
-  return res;
+  return nb * cus;
 }
+
+// One or two tokens (from three on the MFMA GEMV is faster): tokens held (TT), 2048-column chunks per
+// item (CH), register slots (SLOTS: items in flight = SLOTS - 1 beside the one computed) and waves per
+// workgroup (NWV; sixteen read the replicated level-pair table).
+struct RowsPlan {
+  int tt, ch, slots, nwv;
+};
+static RowsPlan rows_plan(int64_t T, int64_t K) {
+  if (T <= 1) return RowsPlan{1, K % 4096 == 0 ? 2 : 1, 2, 16};
+  return RowsPlan{2, 1, 2, 4};  // 72 VGPRs: six waves per SIMD with 4-wave workgroups, four with 16-wave ones
+}
+int nf4_gemv_rows_nseg(int64_t T, int64_t K) {
+  if (T < 1 || T > 2 || K <= 0 || K % 2048 != 0) return 0;
+  const int64_t ns = K / (2048 * rows_plan(T, K).ch);
+  return ns <= kFinishMaxSplit ? (int)ns : 0;
+}
+bool nf4_gemv_rows_ok(int64_t T, int64_t K) { return nf4_gemv_rows_nseg(T, K) > 0; }
 
 // 3..16 tokens: one token group, 512-column segments; 17..32: two groups, 256-column segments; 33..64:
 // four groups, 128-column segments
@@ -857,14 +918,7 @@ int nf4_gemv_mrows_nparts(int64_t T, int64_t K) {
 template <int MT, int RED>
 static int mrows_resident() {
   static thread_local int res = 0;
-  if (res > 0) return res;
-  int dev = 0, cus = 0, nb = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_nf4_gemv_mrows<MT, RED>, 256, 0) != hipSuccess || nb < 1 ||
-      cus < 1)
-    return 0;
-  res = nb * cus;
+  if (res <= 0) res = resident(k_nf4_gemv_mrows<MT, RED>, 256);
   return res;
 }
 
@@ -901,6 +955,22 @@ hipError_t launch_nf4_gemv_mrows(const bf16_t *X, int64_t T, int64_t K, const ui
   return hipGetLastError();
 }
 
+template <int TT, int CH, int SLOTS, int NWV, int MINW>
+static hipError_t rows_go(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
+                          const float *step, int64_t N, int nseg, int nsplit_u, const bf16_t *A, int64_t r, float *part,
+                          float *upart, const Levels &lv, hipStream_t s) {
+  static thread_local int res = 0;  // workgroups resident at once, per variant and thread
+  if (res <= 0) res = resident(k_nf4_gemv_rows<TT, CH, SLOTS, NWV, MINW>, 64 * NWV);
+  if (res <= 0) return hipErrorInvalidDeviceFunction;
+  // main workgroups: what stays resident beside the U workgroups, at most one item per wave, a multiple of nseg
+  int64_t g = std::min<int64_t>(std::max(1, res - nsplit_u), (N * nseg + NWV - 1) / NWV);
+  g = std::max<int64_t>(nseg, g / nseg * nseg);
+  const int gmain = (int)g;
+  launch(k_nf4_gemv_rows<TT, CH, SLOTS, NWV, MINW>, dim3((unsigned)(gmain + nsplit_u)), dim3(64 * NWV), 0, s, X, T,
+         K, codes, absmax_q, step, N, gmain, nseg, nsplit_u, A, r, part, upart, lv);
+  return hipGetLastError();
+}
+
 hipError_t launch_nf4_gemv_rows(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
                                 const float *step, int64_t N, int nsplit_u, const bf16_t *A, int64_t r, float *part,
                                 float *upart, const Levels &lv, hipStream_t s, int *nseg_out) {
@@ -908,22 +978,16 @@ hipError_t launch_nf4_gemv_rows(const bf16_t *X, int64_t T, int64_t K, const uin
   if (T == 0) return hipSuccess;
   const int nseg = nf4_gemv_rows_nseg(T, K);
   if (nseg <= 0) return hipErrorInvalidValue;
-  const int tt = rows_tt(T), ch = rows_ch(T, K);
-  const int res = tt == 1 ? (ch == 2 ? rows_resident<1, 2>() : rows_resident<1, 1>()) : rows_resident<2, 1>();
-  if (res <= 0) return hipErrorInvalidDeviceFunction;
-  // main workgroups: what stays resident beside the U workgroups, at most one item per wave, a multiple of nseg
-  int64_t g = std::min<int64_t>(std::max(1, res - nsplit_u), (N * nseg + 3) / 4);
-  g = std::max<int64_t>(nseg, g / nseg * nseg);
-  const int gmain = (int)g;
-  const dim3 grid((unsigned)(gmain + nsplit_u));
-#define QLORA_ROWS(TT, CH_) \
-  launch(k_nf4_gemv_rows<TT, CH_>, grid, dim3(256), 0, s, X, T, K, codes, absmax_q, step, N, gmain, nseg, nsplit_u, \
-         A, r, part, upart, lv)
-  if (tt == 1) { if (ch == 2) QLORA_ROWS(1, 2); else QLORA_ROWS(1, 1); }
-  else QLORA_ROWS(2, 1);
-#undef QLORA_ROWS
+  const RowsPlan p = rows_plan(T, K);
+  hipError_t e;
+  if (p.tt == 1 && p.ch == 2)
+    e = rows_go<1, 2, 2, 16, 8>(X, T, K, codes, absmax_q, step, N, nseg, nsplit_u, A, r, part, upart, lv, s);
+  else if (p.tt == 1)
+    e = rows_go<1, 1, 2, 16, 8>(X, T, K, codes, absmax_q, step, N, nseg, nsplit_u, A, r, part, upart, lv, s);
+  else
+    e = rows_go<2, 1, 2, 4, 6>(X, T, K, codes, absmax_q, step, N, nseg, nsplit_u, A, r, part, upart, lv, s);
   *nseg_out = nseg;
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace qlora
