@@ -12,6 +12,7 @@ returns gradients for X, A and B and none for the frozen NF4 weight).
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from dataclasses import dataclass
 
@@ -152,7 +153,13 @@ def _ptr(t: torch.Tensor | None):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(device: torch.device):
+    """The current HIP stream of `device` (the raw handle; building a torch Stream object costs ~2 us)."""
+    if _raw_stream is not None and device.index is not None:
+        return ctypes.c_void_p(_raw_stream(device.index))
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
@@ -208,6 +215,7 @@ def _check_weight(w: "NF4Weight", device: torch.device) -> None:
         _want(t, (n,), dt, device, f"NF4 weight {name}")
 
 
+@functools.lru_cache(maxsize=256)
 def storage_bytes(n_out: int, n_in: int) -> tuple[int, int, int]:
     c, q, s = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
     _check(load_library().qlora_nf4_storage(n_out, n_in, ctypes.byref(c), ctypes.byref(q), ctypes.byref(s)),

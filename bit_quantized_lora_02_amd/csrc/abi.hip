@@ -161,7 +161,28 @@ int scratch_address(int dev, void **out) {
 std::mutex g_tmu;
 std::vector<std::string> g_timed;  // kernel names being timed; "*" = all
 std::atomic<int> g_ntimed{0};      // g_timed.size(): with none enabled a launch takes no lock
-std::map<std::string, std::vector<std::pair<hipEvent_t, hipEvent_t>>> g_events;
+struct EventPair {
+  hipEvent_t a, b;
+  int dev;
+};
+std::map<std::string, std::vector<EventPair>> g_events;
+// Events read back are kept for reuse, per device.
+std::map<int, std::vector<hipEvent_t>> g_event_pool;
+
+hipEvent_t pooled_event(int dev) {  // caller holds g_tmu
+  auto &pool = g_event_pool[dev];
+  if (!pool.empty()) {
+    hipEvent_t e = pool.back();
+    pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return e;
+}
 
 bool is_timed(const char *kname) {
   for (const auto &n : g_timed)
@@ -172,14 +193,21 @@ bool is_timed(const char *kname) {
 // A timed launch gets a pair of events stamped by its own dispatch packet.
 struct Timed {
   hipEvent_t a = nullptr, b = nullptr;
+  int dev = 0;
   std::string name;
   Timed(const char *kname) {
     if (g_ntimed.load(std::memory_order_acquire) == 0) return;
     std::lock_guard<std::mutex> lk(g_tmu);
     if (!is_timed(kname)) return;
-    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+    if (hipGetDevice(&dev) != hipSuccess) {
       (void)hipGetLastError();
-      a = b = nullptr;
+      return;
+    }
+    a = pooled_event(dev);
+    b = a ? pooled_event(dev) : nullptr;
+    if (!b) {
+      if (a) g_event_pool[dev].push_back(a);
+      a = nullptr;
       return;
     }
     name = kname;
@@ -189,7 +217,7 @@ struct Timed {
     if (!a) return;
     launch_events() = LaunchEvents{};
     std::lock_guard<std::mutex> lk(g_tmu);
-    g_events[name].push_back({a, b});
+    g_events[name].push_back({a, b, dev});
   }
 };
 
@@ -881,7 +909,7 @@ int qlora_timing_enable(const char *kernel, int enable) {
 // Waits for and releases the recorded events of `kernel`; per-launch milliseconds in launch order go
 // to ms[0 .. cap) (ms may be NULL when cap is 0), their sum to *total_ms.
 static int timing_collect(const char *kernel, double *ms_each, int64_t cap, int64_t *launches, double *total_ms) {
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
+  std::vector<EventPair> ev;
   {
     std::lock_guard<std::mutex> lk(g_tmu);
     auto it = g_events.find(kernel);
@@ -894,15 +922,19 @@ static int timing_collect(const char *kernel, double *ms_each, int64_t cap, int6
   int rc = QLORA_OK;
   for (size_t i = 0; i < ev.size(); ++i) {
     float ms = 0.f;
-    if (hipEventSynchronize(ev[i].second) != hipSuccess ||
-        hipEventElapsedTime(&ms, ev[i].first, ev[i].second) != hipSuccess) {
+    if (hipEventSynchronize(ev[i].b) != hipSuccess || hipEventElapsedTime(&ms, ev[i].a, ev[i].b) != hipSuccess) {
       (void)hipGetLastError();
       rc = fail(QLORA_EHIP, "reading timing events failed");
     }
     tot += ms;
     if ((int64_t)i < cap) ms_each[i] = ms;
-    (void)hipEventDestroy(ev[i].first);
-    (void)hipEventDestroy(ev[i].second);
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    for (const EventPair &e : ev) {
+      g_event_pool[e.dev].push_back(e.a);
+      g_event_pool[e.dev].push_back(e.b);
+    }
   }
   *launches = (int64_t)ev.size();
   if (total_ms) *total_ms = tot;
