@@ -519,12 +519,14 @@ hipError_t launch_lora_rows(bool qt, int rn, const bf16_t *P, int64_t ldp, int64
 // Rank columns held by a skinny-GEMM workgroup for rank r.
 int skinny_rn(int64_t r) { return r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : 128; }
 
-// Split of the reduction for a skinny GEMM with M output rows: aim at ~1024
-// workgroups (four per CU, so that enough loads are in flight) with at least
-// two 64-deep steps each.
+// Split of the reduction for a skinny GEMM with M output rows: aim at ~256
+// workgroups (one per CU) with at least two 64-deep steps each.  Every range
+// writes M x RN binary32 partial sums that the finalize reads back, so fewer
+// ranges cut that traffic; measured against ~1024 workgroups (70B-class layer
+// at r = 64: 14.30 -> 14.14 ms per step; 8B MLP 3.300 -> 3.230 ms).
 void skinny_plan(int64_t M, int64_t Kred, int *nsplit, int64_t *kchunk) {
   const int64_t tiles = (M + SBM - 1) / SBM;
-  int64_t ns = (1024 + tiles - 1) / tiles;
+  int64_t ns = (256 + tiles - 1) / tiles;
   const int64_t by_depth = Kred / 128 > 0 ? Kred / 128 : 1;
   if (ns > by_depth) ns = by_depth;
   if (ns > 32) ns = 32;  // bounds the binary32 partials (workspace) at 32 T r
@@ -536,8 +538,9 @@ void skinny_plan(int64_t M, int64_t Kred, int *nsplit, int64_t *kchunk) {
 }
 
 // Split of the grouped (many-adapter) U pass: the grid has up to tiles + n_seg
-// row tiles, so the split aims at ~1024 workgroups over those, and never
-// exceeds the split of the plain plan (whose partial sums the workspace holds).
+// row tiles, most of them partly filled, so the split aims at ~1024 workgroups
+// over those, and never exceeds the split of the plain plan (whose partial sums
+// the workspace holds).
 void skinny_plan_grouped(int64_t M, int64_t n_seg, int64_t Kred, int *nsplit, int64_t *kchunk) {
   int ns_max;
   int64_t kc_max;
