@@ -482,16 +482,21 @@ __global__ __launch_bounds__(64 * NWV, MINW) void k_nf4_gemv_rows(
 // The next item loads while the current one computes (two fixed slots, the
 // loop unrolled by two).  With RED = 1, main workgroup g owns segment
 // g % nseg, its wave w the row groups 4 (g / nseg) + w + i 4 gmain / nseg, and
-// part is [nseg][T][N].  With RED = 4 (nseg % 4 == 0) the four waves of main
-// workgroup g take the four segments 4 (g % nq) + w of one quarter (nq = nseg /
-// 4) over the same row groups g / nq + i gmain / nq; after each item they
-// exchange their sums through LDS (two buffers, one barrier per item), add
-// them in wave order and write one partial per quarter: part is [nq][T][N],
-// a quarter of the partial bytes.  Workgroups 0 .. nsplit_u - 1 come first
-// and form the U partials as in k_nf4_gemv_rows.
+// part is [nseg][T][N].  With RED = 4 or 8 (nseg % RED == 0) the RED waves of
+// main workgroup g take the RED segments RED (g % nq) + w of one part (nq =
+// nseg / RED) over the same row groups g / nq + i gmain / nq; after each item
+// they exchange their sums through LDS (two buffers, one barrier per item),
+// waves 0..3 add them in wave order and write one partial per part: part is
+// [nq][T][N], 1 / RED of the partial bytes.  Workgroups 0 .. nsplit_u - 1
+// come first and form the U partials as in k_nf4_gemv_rows (with RED = 8 their
+// waves 4..7 have nothing to do).
 constexpr int kMrowsMaxT = 64;
+// Waves per SIMD the registers must allow: four where the kernel fits 128 VGPRs without spilling (two or
+// four token groups with the workgroup sum), else three.
 template <int MT, int RED>
-__global__ __launch_bounds__(256, 3) void k_nf4_gemv_mrows(
+constexpr int mrows_minw() { return (MT == 4 || (MT == 2 && RED > 1)) ? 4 : 3; }
+template <int MT, int RED>
+__global__ __launch_bounds__(64 * (RED == 8 ? 8 : 4), (mrows_minw<MT, RED>())) void k_nf4_gemv_mrows(
     const bf16_t *__restrict__ X, int64_t T, int64_t K, const uint8_t *__restrict__ codes,
     const uint8_t *__restrict__ absmax_q, const float *__restrict__ step, int64_t N, int gmain, int nseg, int nsplit_u,
     const bf16_t *__restrict__ A, int64_t r, float *__restrict__ part, float *__restrict__ upart, Levels lv) {
@@ -501,13 +506,14 @@ __global__ __launch_bounds__(256, 3) void k_nf4_gemv_mrows(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if ((int)blockIdx.x < nsplit_u) {
+    if (wave >= 4) return;
     const int64_t u = blockIdx.x, kchunk = K / nsplit_u, kb = u * kchunk;
     lora_u_partial<MT>(X, T, K, A, r, kb, kb + kchunk, upart + (u * 4 + wave) * T * r, wave, lane);
     return;
   }
-  static_assert(RED == 1 || RED == 4, "one wave or the whole workgroup per partial");
+  static_assert(RED == 1 || RED == 4 || RED == 8, "one wave or the whole workgroup per partial");
   const int a = lane & 15, g = lane >> 4;
-  const int gi = (int)blockIdx.x - nsplit_u, npart = nseg / RED, seg = RED == 1 ? gi % nseg : gi % npart * 4 + wave;
+  const int gi = (int)blockIdx.x - nsplit_u, npart = nseg / RED, seg = RED == 1 ? gi % nseg : gi % npart * RED + wave;
   const int64_t ngroups = (N + 15) / 16;
   const int64_t rg0 = RED == 1 ? (int64_t)(gi / nseg) * 4 + wave : (int64_t)(gi / npart);
   const int64_t rgs = RED == 1 ? (int64_t)(gmain / nseg) * 4 : (int64_t)(gmain / npart);
@@ -543,8 +549,8 @@ __global__ __launch_bounds__(256, 3) void k_nf4_gemv_mrows(
     if (li + 1 < items) ++li;
   };
   float *pseg = part + (int64_t)(RED == 1 ? seg : gi % npart) * T * N;
-  // RED = 4: the waves' sums of one item, [buffer][wave][token group][lane]
-  __shared__ __attribute__((aligned(16))) f32x4_t s_red[RED == 4 ? 2 : 1][RED][MT][64];
+  // RED > 1: the waves' sums of one item, [buffer][wave][token group][lane]
+  __shared__ __attribute__((aligned(16))) f32x4_t s_red[RED > 1 ? 2 : 1][RED][MT][64];
   int64_t crg = rg0;  // row group of the item being computed
   auto do_step = [&](Slot &cur, Slot &refill, int buf) {
     load_slot(refill);
@@ -572,11 +578,16 @@ __global__ __launch_bounds__(256, 3) void k_nf4_gemv_mrows(
           if (n < N && t < T) pseg[t * N + n] = acc[m][e];
         }
     } else {
-      // wave w adds, for lanes 16 w .. 16 w + 15 of every wave, their four elements: thread l takes
-      // lane 16 w + (l >> 2), element l & 3, i.e. token 16 m + 4 w + (l & 3), row 16 crg + (l >> 2)
+      // wave w < 4 adds, for lanes 16 w .. 16 w + 15 of every wave, their four elements: thread l takes
+      // lane 16 w + (l >> 2), element l & 3, i.e. token 16 m + 4 w + (l & 3), row 16 crg + (l >> 2); with
+      // RED = 8 waves 4..7 only contribute their sums
 #pragma unroll
       for (int m = 0; m < MT; ++m) s_red[buf][wave][m][lane] = acc[m];
       __syncthreads();
+      if (RED == 8 && wave >= 4) {
+        crg += rgs;
+        return;
+      }
       const int64_t n = crg * 16 + (lane >> 2);
       const float *rd = reinterpret_cast<const float *>(&s_red[buf][0][0][0]) + (16 * wave + (lane >> 2)) * 4 + (lane & 3);
 #pragma unroll
@@ -595,7 +606,7 @@ __global__ __launch_bounds__(256, 3) void k_nf4_gemv_mrows(
   int64_t f = 0;
   for (; f + 1 < items; f += 2) {
     do_step(s0, s1, 0);
-    do_step(s1, s0, RED == 4 ? 1 : 0);
+    do_step(s1, s0, RED > 1 ? 1 : 0);
   }
   if (f < items) do_step(s0, s1, 0);
 }
@@ -898,8 +909,9 @@ bool nf4_gemv_rows_ok(int64_t T, int64_t K) { return nf4_gemv_rows_nseg(T, K) > 
 // four groups, 128-column segments
 static int mrows_mt(int64_t T) { return T <= 16 ? 1 : T <= 32 ? 2 : 4; }
 // four segments per partial wherever the segments come in fours (a quarter of the partial bytes for
-// one barrier per item)
-static int mrows_red(int64_t nseg) { return nseg % 4 == 0 ? 4 : 1; }
+// one barrier per item); for two or four token groups (128 VGPRs or fewer: four waves per SIMD either
+// way) eight, in workgroups of eight waves, wherever they come in eights
+static int mrows_red(int mt, int64_t nseg) { return mt > 1 && nseg % 8 == 0 ? 8 : nseg % 4 == 0 ? 4 : 1; }
 // at most 32 partials, which the wide finish takes: 128 segments in fours, else 32 (four token groups:
 // segments in fours only)
 int nf4_gemv_mrows_nseg(int64_t T, int64_t K) {
@@ -908,17 +920,17 @@ int nf4_gemv_mrows_nseg(int64_t T, int64_t K) {
   if (K % ks != 0) return 0;
   const int64_t ns = K / ks;
   if (mt == 4 && ns % 4 != 0) return 0;  // four token groups only with the workgroup sum (registers)
-  return ns / mrows_red(ns) <= kFinishMaxSplitWide ? (int)ns : 0;
+  return ns / mrows_red(mt, ns) <= kFinishMaxSplitWide ? (int)ns : 0;
 }
 int nf4_gemv_mrows_nparts(int64_t T, int64_t K) {
   const int ns = nf4_gemv_mrows_nseg(T, K);
-  return ns / mrows_red(ns > 0 ? ns : 1);
+  return ns / mrows_red(mrows_mt(T), ns > 0 ? ns : 1);
 }
 
 template <int MT, int RED>
 static int mrows_resident() {
   static thread_local int res = 0;
-  if (res <= 0) res = resident(k_nf4_gemv_mrows<MT, RED>, 256);
+  if (res <= 0) res = resident(k_nf4_gemv_mrows<MT, RED>, 64 * (RED == 8 ? 8 : 4));
   return res;
 }
 
@@ -929,28 +941,29 @@ hipError_t launch_nf4_gemv_mrows(const bf16_t *X, int64_t T, int64_t K, const ui
   if (T == 0) return hipSuccess;
   const int nseg = nf4_gemv_mrows_nseg(T, K);
   if (nseg <= 0) return hipErrorInvalidValue;
-  const int mt = mrows_mt(T), red = mrows_red(nseg), npart = nseg / red;
+  const int mt = mrows_mt(T), red = mrows_red(mt, nseg), npart = nseg / red;
   const int res = mt == 1   ? (red == 1 ? mrows_resident<1, 1>() : mrows_resident<1, 4>())
-                  : mt == 2 ? (red == 1 ? mrows_resident<2, 1>() : mrows_resident<2, 4>())
-                            : mrows_resident<4, 4>();
+                  : mt == 2 ? (red == 1 ? mrows_resident<2, 1>()
+                                        : red == 4 ? mrows_resident<2, 4>() : mrows_resident<2, 8>())
+                            : (red == 4 ? mrows_resident<4, 4>() : mrows_resident<4, 8>());
   if (res <= 0) return hipErrorInvalidDeviceFunction;
   // main workgroups: what stays resident beside the U workgroups, at most one item per wave, a multiple
-  // of the number of partials (with RED = 4 every workgroup's waves share their items)
+  // of the number of partials (with RED > 1 every workgroup's waves share their items)
   const int64_t per_item = red == 1 ? 4 : 1;
   int64_t g = std::min<int64_t>(std::max(1, res - nsplit_u), ((N + 15) / 16 * npart + per_item - 1) / per_item);
   g = std::max<int64_t>(npart, g / npart * npart);
   const int gmain = (int)g;
   const dim3 grid((unsigned)(gmain + nsplit_u));
   auto go = [&](auto kern) {
-    launch(kern, grid, dim3(256), 0, s, X, T, K, codes, absmax_q, step, N, gmain, nseg, nsplit_u, A, r, part, upart,
-           lv);
+    launch(kern, grid, dim3(red == 8 ? 512 : 256), 0, s, X, T, K, codes, absmax_q, step, N, gmain, nseg, nsplit_u,
+           A, r, part, upart, lv);
   };
   if (mt == 1)
     red == 1 ? go(k_nf4_gemv_mrows<1, 1>) : go(k_nf4_gemv_mrows<1, 4>);
   else if (mt == 2)
-    red == 1 ? go(k_nf4_gemv_mrows<2, 1>) : go(k_nf4_gemv_mrows<2, 4>);
+    red == 1 ? go(k_nf4_gemv_mrows<2, 1>) : red == 4 ? go(k_nf4_gemv_mrows<2, 4>) : go(k_nf4_gemv_mrows<2, 8>);
   else
-    go(k_nf4_gemv_mrows<4, 4>);
+    red == 4 ? go(k_nf4_gemv_mrows<4, 4>) : go(k_nf4_gemv_mrows<4, 8>);
   *nseg_out = npart;
   return hipGetLastError();
 }

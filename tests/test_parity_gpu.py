@@ -408,16 +408,19 @@ def test_small_token_forward(n_out, T):
                                             (24, 28672, 8, 8), (40, 16384, 20, 4), (8, 32768, 32, 8),
                                             (8, 65536, 4, 8), (8, 66560, 4, 8), (8, 33024, 24, 4),
                                             (72, 1024, 33, 16), (136, 8192, 64, 8), (40, 1152, 48, 4),
-                                            (8, 16384, 64, 4), (8, 16512, 40, 4)])
+                                            (8, 16384, 64, 4), (8, 16512, 40, 4), (40, 1536, 40, 8),
+                                            (8, 32768, 36, 4)])
 def test_row_group_forward(n_out, n_in, T, r):
     """3..64 tokens through the row-group kernel (16 rows per wave, activations in registers): one token
     group and segments of 512 columns up to 16 tokens, two groups and segments of 256 up to 32, four groups
-    and segments of 128 beyond, only when the segments come in fours (n_in 1024, 8192, 16384: 2, 16 and 32
-    partials; 1152 and 16512: 9 and 129 segments, the MFMA kernel).  When the
-    segment count is divisible by 4 the workgroup's four waves add their segments before writing (n_in 1024,
-    2048, 3072, 8192, 28672, 32768 and 65536: 1 to 32 partials); otherwise each segment is a partial (n_in
-    512, 1536, 8704: 1, 3 and 17).  At most 32 partials reach the finish kernel; the shapes past that (8448
-    and 33024 at 20-24 tokens, 66560 at 4) take the MFMA kernel; checked in full."""
+    and segments of 128 beyond, only when the segments come in fours (1152 and 16512: 9 and 129 segments,
+    the MFMA kernel).  With two or four token groups and a segment count divisible by 8 the eight waves of a
+    workgroup add their segments before writing (n_in 1024, 8192, 16384 and 32768 at 33-64 tokens: 1, 8,
+    16 and 32 partials; 2048, 8192, 16384 and 32768 at 17-32); otherwise, with a count divisible by 4, the
+    four waves of a workgroup do (n_in 1536 at 40 tokens, 1024 and 3072 at 17-32, 4096 .. 65536 up to 16
+    tokens: 1 to 32 partials); otherwise each segment is a partial (n_in 512, 1536, 8704: 1 to 17).  At most 32
+    partials reach the finish kernel; the shapes past that (8448 and 33024 at 20-24 tokens, 66560 at 4)
+    take the MFMA kernel; checked in full."""
     print(f"row-group forward {n_out}x{n_in} T={T} r={r}", flush=True)
     inp = linear_inputs(n_out, n_in, T, r, 2.0 * r, seed=n_out + 3 * T, sigma_ab=0.05)
     w = Bd.quantize_nf4(torch.from_numpy(inp.W).to(dev()))
