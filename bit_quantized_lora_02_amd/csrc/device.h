@@ -66,6 +66,19 @@ __device__ __forceinline__ void pair_levels_to_lds(const Levels &lv, float2 *tab
   }
 }
 
+// 8 codes of one 32-bit word -> 4 packed bf16 pairs of fl32(level * cq), from
+// the level-pair table (entry b = levels of the low and high nibble of byte b;
+// the address is the byte times 8, one v_lshlrev_b32 with a byte select).
+__device__ __forceinline__ u32x4_t decode8_pairs(uint32_t w, float cq, const float2 *tab) {
+  u32x4_t o;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const float2 l = tab[(w >> (8 * b)) & 0xffu];
+    o[b] = pack_bf16x2(__fmul_rn(l.x, cq), __fmul_rn(l.y, cq));
+  }
+  return o;
+}
+
 // Block constant of NF4 block b: fl32(q_b * d_{b/256}).
 __device__ __forceinline__ float block_scale(const uint8_t *__restrict__ absmax_q, const float *__restrict__ step,
                                              int64_t b) {

@@ -29,6 +29,17 @@ inline void launch(F kernel, dim3 grid, dim3 block, uint32_t shm, hipStream_t s,
   hipExtLaunchKernelGGL(kernel, grid, block, shm, s, ev.start, ev.stop, 0u, args...);
 }
 
+// Workgroups of a kernel resident on the device at once.
+template <class Kern>
+inline int resident(Kern kern, int threads) {
+  int dev = 0, cus = 0, nb = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, threads, 0) != hipSuccess || nb < 1 || cus < 1)
+    return 0;
+  return nb * cus;
+}
+
 typedef uint16_t bf16_t;
 struct Levels;
 struct Thresholds;

@@ -45,19 +45,6 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(const u32x4_t &a, const u32x4_t
                                                  0, 0, 0);
 }
 
-// 8 codes of one 32-bit word -> 4 packed bf16 pairs of fl32(level * cq), from
-// the level-pair table (entry b = levels of the low and high nibble of byte b;
-// the address is the byte times 8, one v_lshlrev_b32 with a byte select).
-__device__ __forceinline__ u32x4_t decode8_pairs(uint32_t w, float cq, const float2 *tab) {
-  u32x4_t o;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const float2 l = tab[(w >> (8 * b)) & 0xffu];
-    o[b] = pack_bf16x2(__fmul_rn(l.x, cq), __fmul_rn(l.y, cq));
-  }
-  return o;
-}
-
 // The level-pair table in 32 interleaved copies (64 KB): entry e of copy c sits at byte
 // 256 e + 8 c, i.e. in bank pair c of the 64 four-byte banks.  Lane l reads copy l % 32, so
 // the 32 lanes of one half-wave -- the lanes an 8-byte LDS read serves together -- touch 32
@@ -875,17 +862,6 @@ hipError_t launch_gemv_finish(const float *part, const float *upart, int nsplit,
 #undef QLORA_FIN_PS
 #undef QLORA_FIN
   return hipGetLastError();
-}
-
-// Workgroups of a kernel resident on the device at once.
-template <class Kern>
-static int resident(Kern kern, int threads) {
-  int dev = 0, cus = 0, nb = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, threads, 0) != hipSuccess || nb < 1 || cus < 1)
-    return 0;
-  return nb * cus;
 }
 
 // One or two tokens (from three on the MFMA GEMV is faster): tokens held (TT), 2048-column chunks per

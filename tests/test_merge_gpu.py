@@ -33,8 +33,12 @@ def check_f32(got, ref, rtol=1e-6, floor=1e-6):
 
 
 @pytest.mark.parametrize("n_out,n_in,r,alpha", [(264, 320, 5, 10.0), (1032, 4160, 16, 32.0), (72, 1152, 128, 256.0),
-                                                (8, 64, 1, 2.0), (4096, 4096, 16, 32.0), (200, 512, 64, 16.0)])
+                                                (8, 64, 1, 2.0), (4096, 4096, 16, 32.0), (200, 512, 64, 16.0),
+                                                (2056, 8192, 24, 48.0), (33, 448, 7, 14.0)])
 def test_merge_nf4_base(n_out, n_in, r, alpha):
+    """Tiles of 32 rows x 256 columns, 64 per wave: n_in 320, 448 and 4160 end in a partly filled tile, n_out
+    264, 2056 and 33 in a partial row band; r = 5 and 7 take B element by element, the others in 16-byte rows;
+    ranks up to 16, 32, 64 and 128 each compile their own kernel."""
     print(f"merge nf4 {n_out}x{n_in} r={r}", flush=True)
     inp = linear_inputs(n_out, n_in, 1, r, alpha, seed=n_out + r, sigma_ab=0.05, make_dy=False)
     w = Bd.quantize_nf4(torch.from_numpy(inp.W).to(dev()))
@@ -51,9 +55,10 @@ def test_merge_nf4_base(n_out, n_in, r, alpha):
     assert np.abs(ref - O.bf16_bits_to_f64(O.dequant(oc, oq, od, n_out, n_in))).max() > 1e-3
 
 
-def test_merge_bf16_base_and_requantize():
+@pytest.mark.parametrize("n_out,n_in,r,alpha", [(520, 1024, 16, 32.0), (33, 448, 7, 14.0)])
+def test_merge_bf16_base_and_requantize(n_out, n_in, r, alpha):
     """The pages' recipe: merge into the reloaded 16-bit base, then quantize the merged weight again."""
-    n_out, n_in, r, alpha = 520, 1024, 16, 32.0
+    print(f"merge bf16 {n_out}x{n_in} r={r}", flush=True)
     inp = linear_inputs(n_out, n_in, 1, r, alpha, seed=9, sigma_ab=0.05, make_dy=False)
     base_bits = to_bf16_bits(inp.W)
     A, B = to_gpu_bf16(inp.A), to_gpu_bf16(inp.B)
