@@ -87,7 +87,8 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-KERNEL_SOURCES = {"nf4_gemm_fwd": "nf4_gemm.hip", "nf4_gemm_dx": "nf4_gemm.hip", "nf4_gemv": "nf4_gemv.hip"}
+KERNEL_SOURCES = {"nf4_gemm_fwd": "nf4_gemm.hip", "nf4_gemm_dx": "nf4_gemm.hip", "nf4_gemv": "nf4_gemv.hip",
+                  "merge": "merge.hip"}
 # kernel symbols behind each timed launch label (the small-token forward has two kernels)
 KERNEL_SYMBOLS = {"nf4_gemm_fwd": ("k_nf4_gemm_fwd",), "nf4_gemm_dx": ("k_nf4_gemm_dx",),
                   "nf4_gemv": ("k_nf4_gemv", "k_nf4_gemv_rows", "k_nf4_gemv_mrows")}
@@ -355,6 +356,7 @@ def bench_merge(args, B, layers, r, alpha):
     nbytes = sum(weight_bytes(L["n_out"], L["n_in"]) + 2 * L["n_out"] * L["n_in"] + 2 * r * (L["n_in"] + L["n_out"])
                  for L in layers)
     gbps = nbytes / (ms / args.steps * 1e-3) / 1e9
+    traffic = traffic_from_profiles("merge", args.config + "_merge")
     print(json.dumps({"metric": "NF4 adapter merge for export, HBM GB/s", "value": gbps, "unit": "GB/s",
                       "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                       "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True, "dtype": "bf16",
@@ -362,7 +364,9 @@ def bench_merge(args, B, layers, r, alpha):
                       "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config + "_merge", "rank": r,
                                  "linears": [[L["name"], L["n_out"], L["n_in"]] for L in layers]},
                       "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                                   "frac": gbps / PEAK_HBM_GBPS, "traffic": None, "kernel": "merge",
+                                   "frac": gbps / PEAK_HBM_GBPS,
+                                   "traffic": traffic, "algorithmic_bytes_per_launch": nbytes / len(layers),
+                                   "kernel": "merge",
                                    "avg_ms_per_launch": ms / n if n else None}}))
 
 
@@ -454,7 +458,9 @@ def main():
     if args.traffic_from:  # post-processing of counter runs: no GPU needed
         lins, T, r, alpha, outliers, train = linears_for(args)
         wl = args.config if args.config != "small_token" else f"small_token_{lins[0][1]}x8192_T{T}"
-        ks = [args.traffic_kernel] if args.traffic_kernel else (
+        if args.merge:
+            wl += "_merge"
+        ks = [args.traffic_kernel] if args.traffic_kernel else ["merge"] if args.merge else (
             ["nf4_gemm_fwd", "nf4_gemm_dx"] if train else ["nf4_gemm_fwd", "nf4_gemv"])
         write_traffic(args, wl, ks)
         return
