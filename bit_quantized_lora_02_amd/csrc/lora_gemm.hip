@@ -59,6 +59,12 @@ __device__ __forceinline__ u32x4_t tr_read8(const bf16_t *base, int ld, int row0
 }
 constexpr int SK = 64;    // reduction step
 constexpr int SBM = 128;  // rows of M per workgroup
+// k-groups of four waves per workgroup, each streaming its own part of the k range (two waves per SIMD
+// instead of one); rank 128 keeps one, as two would leave it 256 registers and spill
+template <int RN>
+constexpr int skg() {
+  return RN <= 64 ? 2 : 1;
+}
 
 // Keep bits of 8-element chunk `chunk`: Philox4x32 with 10 rounds -- each round
 // takes both halves of the 64-bit products of words 0 and 2 with the round
@@ -106,7 +112,7 @@ __device__ __forceinline__ u32x4_t apply_keep(const u32x4_t &v, uint32_t bits, f
 // With CT the partial sums are stored by rank column instead: C[split][j][m] (M % 4 == 0), so that a
 // finalize reading them for an output [r][M] (dA) loads and stores along m.
 template <bool PT, bool QT, int RN, int DM, bool GR = false, bool CT = false>
-__global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, int64_t ldp, int64_t M,
+__global__ __launch_bounds__(256 * skg<RN>()) void k_skinny(const bf16_t *__restrict__ P, int64_t ldp, int64_t M,
                                                 const bf16_t *__restrict__ Q, int64_t ldq, int64_t Rv, int64_t Kred,
                                                 int64_t kchunk, float *__restrict__ C, DropParams dp,
                                                 SegTable sg, int64_t q_stride) {
@@ -117,10 +123,17 @@ __global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, in
   constexpr int P_CH = SBM * SK / 8 / 256;            // 16-byte chunks of P per thread (4)
   constexpr int Q_CHUNKS = RN * SK / 8;               // 16-byte chunks of the Q tile
   constexpr int Q_CH = (Q_CHUNKS + 255) / 256;
-  constexpr int NT_ = RN / 16;
-  __shared__ __attribute__((aligned(16))) bf16_t sP[2][P_ROWS * LDP];
-  __shared__ __attribute__((aligned(16))) bf16_t sQ[2][Q_ROWS * LDQ];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NT_ = RN / 16, SKG = skg<RN>();
+  // per k-group: two P and two Q buffers; after the loop group 1's region takes its accumulators
+  constexpr int P_ELEMS = P_ROWS * LDP, Q_ELEMS = Q_ROWS * LDQ, G_ELEMS = 2 * (P_ELEMS + Q_ELEMS);
+  static_assert(256 * 8 * NT_ * 4 <= G_ELEMS * 2, "group 1's buffers hold its accumulators");
+  static_assert(P_ELEMS % 8 == 0 && Q_ELEMS % 8 == 0, "16-byte aligned buffers");
+  __shared__ __attribute__((aligned(16))) bf16_t smem[SKG * G_ELEMS];
+  const int kg = threadIdx.x >> 8;  // k-group
+  const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6;
+  bf16_t *const sPg = smem + kg * G_ELEMS, *const sQg = sPg + 2 * P_ELEMS;
+  auto sP = [&](int buf) { return sPg + buf * P_ELEMS; };
+  auto sQ = [&](int buf) { return sQg + buf * Q_ELEMS; };
   int64_t m0 = (int64_t)blockIdx.x * SBM, mend = M;
   if constexpr (GR) {
     int64_t b = blockIdx.x, lo = 0, hi = 0;
@@ -145,9 +158,14 @@ __global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, in
     if (a >= 0 && a < sg.n_pool) Q += (int64_t)a * q_stride;
     else Rv = 0;
   }
-  const int64_t kb = (int64_t)blockIdx.y * kchunk;
-  const int64_t ke = (kb + kchunk < Kred) ? kb + kchunk : Kred;
-  const int nsteps = (int)((ke - kb + SK - 1) / SK);
+  // the workgroup's k range [kb0, ke0) in steps of SK; k-group g takes steps g n .. g n + n - 1 of it
+  // (n = ceil(steps / SKG)), and both groups run n iterations (a group's steps past ke0 load zeros), so that
+  // they meet the same barriers
+  const int64_t kb0 = (int64_t)blockIdx.y * kchunk;
+  const int64_t ke0 = (kb0 + kchunk < Kred) ? kb0 + kchunk : Kred;
+  const int nsteps = (int)((ke0 - kb0 + SK - 1) / SK + SKG - 1) / SKG;
+  const int64_t kb = kb0 + (int64_t)kg * nsteps * SK;
+  const int64_t ke = ke0;
 
   auto p_off = [&](int c, int &row, int &col) {  // chunk c of the P tile -> LDS (row, col)
     if (PT) { row = c >> 4; col = (c & 15) * 8; }
@@ -202,7 +220,7 @@ __global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, in
     for (int i = 0; i < P_CH; ++i) {
       int row, col;
       p_off(tid + 256 * i, row, col);
-      *reinterpret_cast<u32x4_t *>(&sP[buf][row * LDP + col]) =
+      *reinterpret_cast<u32x4_t *>(&sP(buf)[row * LDP + col]) =
           (DM == DROP_NONE) ? rp_[i] : apply_keep(rp_[i], km_[i], dp.q);
     }
 #pragma unroll
@@ -212,7 +230,7 @@ __global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, in
       int row, col;
       if (QT) { row = c / (RN / 8); col = (c % (RN / 8)) * 8; }
       else { row = c >> 3; col = (((c & 7) ^ (row & 7)) << 3); }
-      *reinterpret_cast<u32x4_t *>(&sQ[buf][row * LDQ + col]) = rq_[i];
+      *reinterpret_cast<u32x4_t *>(&sQ(buf)[row * LDQ + col]) = rq_[i];
     }
   };
 
@@ -231,19 +249,19 @@ __global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, in
       for (int i = 0; i < 2; ++i) {
         const int mrow = wave * 32 + i * 16;
         if (PT) {
-          pa[i] = tr_read8(sP[buf], LDP, kk * 32 + 8 * g + (a >> 2), mrow + 4 * (a & 3));
+          pa[i] = tr_read8(sP(buf), LDP, kk * 32 + 8 * g + (a >> 2), mrow + 4 * (a & 3));
         } else {
           const int row = mrow + a, chunk = kk * 4 + g;
-          pa[i] = *reinterpret_cast<const u32x4_t *>(&sP[buf][row * LDP + ((chunk ^ (row & 7)) << 3)]);
+          pa[i] = *reinterpret_cast<const u32x4_t *>(&sP(buf)[row * LDP + ((chunk ^ (row & 7)) << 3)]);
         }
       }
 #pragma unroll
       for (int j = 0; j < NT_; ++j) {
         if (QT) {
-          qb[j] = tr_read8(sQ[buf], LDQ, kk * 32 + 8 * g + (a >> 2), j * 16 + 4 * (a & 3));
+          qb[j] = tr_read8(sQ(buf), LDQ, kk * 32 + 8 * g + (a >> 2), j * 16 + 4 * (a & 3));
         } else {
           const int row = j * 16 + a, chunk = kk * 4 + g;
-          qb[j] = *reinterpret_cast<const u32x4_t *>(&sQ[buf][row * LDQ + ((chunk ^ (row & 7)) << 3)]);
+          qb[j] = *reinterpret_cast<const u32x4_t *>(&sQ(buf)[row * LDQ + ((chunk ^ (row & 7)) << 3)]);
         }
       }
 #pragma unroll
@@ -269,6 +287,26 @@ __global__ __launch_bounds__(256) void k_skinny(const bf16_t *__restrict__ P, in
       if (s + 2 < nsteps) store(0, rpA, rqA, kmA);
       __syncthreads();
     }
+  }
+  // group 1 hands its sums to group 0 through its own buffers (free after the loop's last barrier), and
+  // group 0 adds them to its own: one fixed order
+  if constexpr (SKG == 2) {
+    f32x4s_t *xs = reinterpret_cast<f32x4s_t *>(smem + G_ELEMS);
+    if (kg == 1)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < NT_; ++j) xs[(i * NT_ + j) * 256 + tid] = acc[i][j];
+    __syncthreads();
+    if (kg == 1) return;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < NT_; ++j) {
+        const f32x4s_t o = xs[(i * NT_ + j) * 256 + tid];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][e] = __fadd_rn(acc[i][j][e], o[e]);
+      }
   }
   // element i of lane l of tile (mt, nt): row 16 mt + 4 (l >> 4) + i, column 16 nt + (l & 15)
   float *Cs = C + (int64_t)blockIdx.y * M * RN;
@@ -562,10 +600,10 @@ static hipError_t skinny_dispatch(int rn, dim3 grid, hipStream_t s, const bf16_t
                                   const DropParams &dp) {
   const SegTable none;
   switch (rn) {
-    case 16: launch((k_skinny<PT, QT, 16, DM, false, CT>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp, none, (int64_t)0); break;
-    case 32: launch((k_skinny<PT, QT, 32, DM, false, CT>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp, none, (int64_t)0); break;
-    case 64: launch((k_skinny<PT, QT, 64, DM, false, CT>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp, none, (int64_t)0); break;
-    default: launch((k_skinny<PT, QT, 128, DM, false, CT>), grid, dim3(256), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp, none, (int64_t)0); break;
+    case 16: launch((k_skinny<PT, QT, 16, DM, false, CT>), grid, dim3(256 * skg<16>()), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp, none, (int64_t)0); break;
+    case 32: launch((k_skinny<PT, QT, 32, DM, false, CT>), grid, dim3(256 * skg<32>()), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp, none, (int64_t)0); break;
+    case 64: launch((k_skinny<PT, QT, 64, DM, false, CT>), grid, dim3(256 * skg<64>()), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp, none, (int64_t)0); break;
+    default: launch((k_skinny<PT, QT, 128, DM, false, CT>), grid, dim3(256 * skg<128>()), 0, s, P, ldp, M, Q, ldq, Rv, Kred, kchunk, C, dp, none, (int64_t)0); break;
   }
   return hipGetLastError();
 }
@@ -602,19 +640,19 @@ hipError_t launch_skinny_grouped(int rn, const bf16_t *P, int64_t ldp, int64_t M
   const DropParams dp;
   switch (rn) {
     case 16:
-      launch((k_skinny<false, false, 16, DROP_NONE, true>), grid, dim3(256), 0, s, P, ldp, M, Q_pool, ldq, Rv, Kred,
+      launch((k_skinny<false, false, 16, DROP_NONE, true>), grid, dim3(256 * skg<16>()), 0, s, P, ldp, M, Q_pool, ldq, Rv, Kred,
              kchunk, C, dp, sg, q_stride);
       break;
     case 32:
-      launch((k_skinny<false, false, 32, DROP_NONE, true>), grid, dim3(256), 0, s, P, ldp, M, Q_pool, ldq, Rv, Kred,
+      launch((k_skinny<false, false, 32, DROP_NONE, true>), grid, dim3(256 * skg<32>()), 0, s, P, ldp, M, Q_pool, ldq, Rv, Kred,
              kchunk, C, dp, sg, q_stride);
       break;
     case 64:
-      launch((k_skinny<false, false, 64, DROP_NONE, true>), grid, dim3(256), 0, s, P, ldp, M, Q_pool, ldq, Rv, Kred,
+      launch((k_skinny<false, false, 64, DROP_NONE, true>), grid, dim3(256 * skg<64>()), 0, s, P, ldp, M, Q_pool, ldq, Rv, Kred,
              kchunk, C, dp, sg, q_stride);
       break;
     default:
-      launch((k_skinny<false, false, 128, DROP_NONE, true>), grid, dim3(256), 0, s, P, ldp, M, Q_pool, ldq, Rv, Kred,
+      launch((k_skinny<false, false, 128, DROP_NONE, true>), grid, dim3(256 * skg<128>()), 0, s, P, ldp, M, Q_pool, ldq, Rv, Kred,
              kchunk, C, dp, sg, q_stride);
       break;
   }
