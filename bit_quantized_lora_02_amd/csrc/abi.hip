@@ -348,7 +348,7 @@ Plan make_plan(int op, int64_t T, int64_t N, int64_t K, int32_t r) {
       part += (size_t)4 * p.gemv_split * T * r * 4;
     }
     if (!p.gemv) {  // the tiled GEMM; its partial sums follow U's, which are consumed first
-      p.fwd_split = nf4_gemm_fwd_split(nf4_gemm_pick_tile(T, N), T, N, K);
+      p.fwd_split = nf4_gemm_fwd_split(nf4_gemm_pick_tile_fwd(T, N, K), T, N, K);
       const size_t gp = p.fwd_split > 1 ? (size_t)p.fwd_split * T * N * 4 : 0;
       part = gp > part ? gp : part;
     }
@@ -549,7 +549,7 @@ int linear_fwd(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const qlora_b
   // B is read in place when its rows are 16-byte multiples, else from a zero-padded copy
   const bool b_direct = (r % 8) == 0;
   if (!b_direct) LAUNCH("pad_b", launch_pad_copy(B, r, r, N, Bp, p.rp, s));
-  LAUNCH("nf4_gemm_fwd", launch_nf4_gemm_fwd(nf4_gemm_pick_tile(T, N), X, T, K, q->codes, q->absmax_q,
+  LAUNCH("nf4_gemm_fwd", launch_nf4_gemm_fwd(nf4_gemm_pick_tile_fwd(T, N, K), X, T, K, q->codes, q->absmax_q,
                                              q->absmax_step, N, V, b_direct ? B : Bp, b_direct ? r : p.rp, r, p.rp,
                                              Y, lv, s, SegTable(), p.fwd_split, part));
   if (p.fwd_split > 1)  // few output tiles: the reduction ran in ranges; add them in order
@@ -722,7 +722,7 @@ int qlora_linear_fwd_multi(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, c
   skinny_plan_grouped(T, n_seg, K, &gns, &gkc);  // at most p.su.n ranges: fits the workspace
   LAUNCH("lora_u_multi", launch_skinny_grouped(p.rn, X, K, T, A_pool, K, (int64_t)r * K, r, K, gkc, gns, sg, part, s));
   LAUNCH("lora_u_finalize", launch_finalize(part, gns, T, p.rn, nullptr, 0, 0, 1.0f, V, p.rp, p.rp, r, sc, s));
-  LAUNCH("nf4_gemm_fwd", launch_nf4_gemm_fwd(nf4_gemm_pick_tile(T, N), X, T, K, q->codes, q->absmax_q,
+  LAUNCH("nf4_gemm_fwd", launch_nf4_gemm_fwd(nf4_gemm_pick_tile_fwd(T, N, K), X, T, K, q->codes, q->absmax_q,
                                              q->absmax_step, N, V, B_pool, r, r, p.rp, Y, lv, s, sg, p.fwd_split, part));
   if (p.fwd_split > 1)
     LAUNCH("gemm_fwd_reduce", launch_finalize(part, p.fwd_split, T, N, Y, N, N, 1.0f, nullptr, 0, 0, 0, 0.f, s));

@@ -770,6 +770,16 @@ int nf4_gemm_fwd_split(int tile, int64_t T, int64_t N, int64_t K) {
   return best;
 }
 
+// The forward's tile: as nf4_gemm_pick_tile, except that a narrow output of a training batch (at least
+// 1024 tokens; e.g. 4096 x 1024 for a grouped-query k or v projection), which would take 128x128 tiles,
+// takes the 256x256 tile with its reduction split into ranges when those fill every CU.
+int nf4_gemm_pick_tile_fwd(int64_t M, int64_t N, int64_t K) {
+  const int t = nf4_gemm_pick_tile(M, N);
+  if (t != NF4_TILE_128x128_W8 || M < 1024 || N < 256) return t;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  return tiles * nf4_gemm_fwd_split(NF4_TILE_256x256_W8, M, N, K) >= 256 ? NF4_TILE_256x256_W8 : t;
+}
+
 hipError_t launch_nf4_gemm_fwd(int tile, const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes,
                                const uint8_t *absmax_q, const float *step, int64_t N, const bf16_t *V,
                                const bf16_t *Bp, int64_t ldb, int64_t r, int64_t rp, bf16_t *Y, const Levels &lv,

@@ -367,9 +367,12 @@ def test_full_size_sampled(cfg, name, n_out, n_in, T, r, alpha, outliers):
     assert abs(la - lb) <= 1e-2 * max(abs(la), abs(lb))
 
 
-@pytest.mark.parametrize("n_out,n_in,T,r", [(4104, 4096, 4133, 16), (1032, 2048, 8200, 40)])
+@pytest.mark.parametrize("n_out,n_in,T,r", [(4104, 4096, 4133, 16), (1032, 2048, 8200, 40), (1024, 8192, 1024, 16),
+                                            (2000, 8192, 2000, 8)])
 def test_large_ragged_sampled(n_out, n_in, T, r):
-    """Shapes large enough for the 256-row tiles, with partial tiles in T and n_out."""
+    """Shapes large enough for the 256-row tiles, with partial tiles in T and n_out.  The last two are narrow
+    outputs of many tokens, whose forward takes 256x256 tiles with the reduction split in 16 and 4 ranges
+    (the second ragged in T and n_out)."""
     print(f"large ragged {n_out}x{n_in} T={T} r={r}", flush=True)
     inp = linear_inputs(n_out, n_in, T, r, 2.0 * r, seed=3)
     _, g = run_gpu(inp)
