@@ -442,6 +442,7 @@ struct FinJob {
   bf16_t *out2;
   int64_t ld2, n2, nvalid2;
   int64_t nblocks;  // 256-thread blocks of this job
+  int vec;          // 1: four consecutive columns per thread (16-byte loads; see fin_job)
 };
 
 __device__ __forceinline__ void finalize_one(const FinJob &j, int64_t i) {
@@ -467,11 +468,56 @@ __device__ __forceinline__ void finalize_one(const FinJob &j, int64_t i) {
   if (j.out2 && n < j.n2) j.out2[m * j.ld2 + n] = (n < j.nvalid2) ? f32_to_bf16(j.scale2 * sum) : (bf16_t)0;
 }
 
+// Four consecutive columns n .. n + 3 of one row (n % 4 == 0): the same sums in the same order as
+// finalize_one, with 16-byte loads of the partials and 8-byte stores.  Index math in 32 bits (the host
+// takes this form only when M ncol < 2^31).
+__device__ __forceinline__ void finalize_vec(const FinJob &j, int64_t i4) {
+  const uint32_t ncol4 = (uint32_t)(((j.n1 > j.n2) ? j.n1 : j.n2) / 4);
+  if (i4 >= (int64_t)j.M * ncol4) return;
+  const uint32_t m = (uint32_t)i4 / ncol4, n = ((uint32_t)i4 - m * ncol4) * 4;
+  float sum[4] = {0.f, 0.f, 0.f, 0.f};
+  if (n < j.N) {
+    const float *src = j.part + (int64_t)m * j.N + n;
+    const int64_t stride = j.sstride;
+    int p = 0;
+    for (; p + 4 <= j.nsplit; p += 4) {
+      f32x4s_t v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const f32x4s_t *>(src + (int64_t)(p + q) * stride);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sum[e] += v[q][e];
+    }
+    for (; p < j.nsplit; ++p) {
+      const f32x4s_t v = *reinterpret_cast<const f32x4s_t *>(src + (int64_t)p * stride);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sum[e] += v[e];
+    }
+  }
+  if (j.out1 && n < j.n1) {
+    bf16_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16(j.scale1 * sum[e]);
+    *reinterpret_cast<u32x2_t *>(j.out1 + (int64_t)m * j.ld1 + n) =
+        u32x2_t{(uint32_t)o[0] | (uint32_t)o[1] << 16, (uint32_t)o[2] | (uint32_t)o[3] << 16};
+  }
+  if (j.out2 && n < j.n2) {
+    bf16_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (n + e < j.nvalid2) ? f32_to_bf16(j.scale2 * sum[e]) : (bf16_t)0;
+    *reinterpret_cast<u32x2_t *>(j.out2 + (int64_t)m * j.ld2 + n) =
+        u32x2_t{(uint32_t)o[0] | (uint32_t)o[1] << 16, (uint32_t)o[2] | (uint32_t)o[3] << 16};
+  }
+}
+
 // Blocks [0, a.nblocks) run job a, the rest job b (two independent outputs in one launch).
 __global__ __launch_bounds__(256) void k_finalize(FinJob a, FinJob b) {
   const int64_t blk = blockIdx.x;
-  if (blk < a.nblocks) finalize_one(a, blk * 256 + threadIdx.x);
-  else finalize_one(b, (blk - a.nblocks) * 256 + threadIdx.x);
+  const FinJob &j = blk < a.nblocks ? a : b;
+  const int64_t i = (blk < a.nblocks ? blk : blk - a.nblocks) * 256 + threadIdx.x;
+  if (j.vec) finalize_vec(j, i);
+  else finalize_one(j, i);
 }
 
 // out[m*ldo + n] = n < ncols ? in[m*ldi + n] : 0, for n < ldo (zero-padded copy).
@@ -502,7 +548,13 @@ FinJob fin_job(const float *part, int nsplit, int64_t M, int64_t N, bf16_t *out1
   j.nvalid2 = nvalid2;
   j.scale2 = scale2;
   const int64_t ncol = (n1 > n2) ? n1 : n2;
-  j.nblocks = (M * ncol + 255) / 256;
+  // four columns per thread when every group of four lies within [0, N), [0, n1) or [0, n2) or outside
+  // them, and the partials and outputs are aligned for 16- and 8-byte accesses
+  auto al = [](const void *ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; };
+  j.vec = ncol % 4 == 0 && N % 4 == 0 && j.sstride % 4 == 0 && n1 % 4 == 0 && n2 % 4 == 0 && al(part, 16) &&
+          (!out1 || (ld1 % 4 == 0 && al(out1, 8))) && (!out2 || (ld2 % 4 == 0 && al(out2, 8))) &&
+          M * ncol < ((int64_t)1 << 31);
+  j.nblocks = j.vec ? (M * (ncol / 4) + 255) / 256 : (M * ncol + 255) / 256;
   return j;
 }
 }  // namespace
