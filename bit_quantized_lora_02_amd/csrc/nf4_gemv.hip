@@ -45,34 +45,42 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(const u32x4_t &a, const u32x4_t
                                                  0, 0, 0);
 }
 
-// The level-pair table in 32 interleaved copies (64 KB): entry e of copy c sits at byte
-// 256 e + 8 c, i.e. in bank pair c of the 64 four-byte banks.  Lane l reads copy l % 32, so
-// the 32 lanes of one half-wave -- the lanes an 8-byte LDS read serves together -- touch 32
-// distinct bank pairs whatever their code bytes (one copy gives a random byte mix about
-// 3.5-way bank conflicts).  Thread i of the nt >= 1024 threads writes copies 8 (i & 3) ..
-// 8 (i & 3) + 7 of entry i / 4.
-constexpr int kTabCopies = 32;
-__device__ __forceinline__ void pair_levels_rep32(const Levels &lv, float2 *tab, int tid) {
+// The bf16 level-pair table of the row-streaming GEMV: entry e (a code byte) is one word
+// holding bf16(level[e & 15]) in its low half and bf16(level[e >> 4]) in its high half, the
+// order of the two weights of the byte.  For sixteen-wave workgroups it is kept in 64
+// interleaved copies (64 KB): entry e of copy c sits at byte 256 e + 4 c, i.e. in bank c of
+// the 64 four-byte banks, and lane l reads copy l, so a 4-byte LDS read of the wave touches
+// 64 distinct banks whatever its code bytes.  Thread i of the nt >= 1024 threads writes
+// copies 16 (i & 3) .. 16 (i & 3) + 15 of entry i / 4; with fewer threads, one copy
+// (entries 0..255 at bytes 0..1023).
+constexpr int kTabCopies = 64;
+__device__ __forceinline__ uint32_t bf16_level_pair(const Levels &lv, int e) {
+  float lo = 0.f, hi = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    lo = ((e & 15) == i) ? lv.v[i] : lo;
+    hi = ((e >> 4) == i) ? lv.v[i] : hi;
+  }
+  return pack_bf16x2(lo, hi);
+}
+__device__ __forceinline__ void bf16_pairs_rep64(const Levels &lv, uint32_t *tab, int tid) {
   if (tid < 1024) {
-    const int e = tid >> 2, c0 = 8 * (tid & 3);
-    float lo = 0.f, hi = 0.f;
+    const int e = tid >> 2, c0 = 16 * (tid & 3);
+    const uint32_t p = bf16_level_pair(lv, e);
+    const u32x4_t v = {p, p, p, p};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      lo = ((e & 15) == i) ? lv.v[i] : lo;
-      hi = ((e >> 4) == i) ? lv.v[i] : hi;
-    }
-    const u32x4_t v = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi),
-                       __builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-#pragma unroll
-    for (int c = 0; c < 8; c += 2) *reinterpret_cast<u32x4_t *>(tab + e * kTabCopies + c0 + c) = v;
+    for (int c = 0; c < 16; c += 4) *reinterpret_cast<u32x4_t *>(tab + e * kTabCopies + c0 + c) = v;
   }
 }
-// Levels of the two nibbles of byte b of w from the replicated table; c8 = 8 (lane % 32).  The
-// byte offset 256 byte + c8 is one byte permute: [c8, byte b of w, 0, 0].
+__device__ __forceinline__ void bf16_pairs_one(const Levels &lv, uint32_t *tab, int tid) {
+  if (tid < 256) tab[tid] = bf16_level_pair(lv, tid);
+}
+// bf16 levels of the two nibbles of byte b of w from the replicated table; c4 = 4 lane.  The
+// byte offset 256 byte + c4 is one byte permute: [c4, byte b of w, 0, 0].
 template <int B>
-__device__ __forceinline__ float2 pair_rep32(const float2 *tab, uint32_t w, uint32_t c8) {
-  const uint32_t off = __builtin_amdgcn_perm(w, c8, 0x0C0C0000u | ((4u + B) << 8));
-  return *reinterpret_cast<const float2 *>(reinterpret_cast<const char *>(tab) + off);
+__device__ __forceinline__ uint32_t bf16_pair_rep64(const uint32_t *tab, uint32_t w, uint32_t c4) {
+  const uint32_t off = __builtin_amdgcn_perm(w, c4, 0x0C0C0000u | ((4u + B) << 8));
+  return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(tab) + off);
 }
 
 // Sum over the 64 lanes of a wave with DPP moves: pairs, quads, half rows and rows of 16
@@ -311,15 +319,22 @@ __global__ __launch_bounds__(256) void k_nf4_gemv(const bf16_t *__restrict__ X, 
 // whole launch, every lane keeps its TT CH 32 activations in registers, loaded
 // once: the workgroup copies the segment's activations into LDS and each wave
 // takes its lanes' share from there (one global read per workgroup instead of
-// one per wave; measured 2-4% faster).  Per item a lane decodes its 32 CH weights
-// byte by byte through the level-pair table into bf16 pairs fl32(level * c')
-// and accumulates v_dot2_f32_bf16 with the matching activation pairs; a wave
-// reduction then gives the binary32 partial sum of that segment.
+// one per wave; measured 2-4% faster).
+//
+// A lane's 32 weights of a chunk lie in one block, so the block constant
+// factors out of their dot product: per chunk the lane looks up each code
+// byte's two levels as a bf16 pair, accumulates v_dot2_f32_bf16 with the
+// matching activation pairs, and adds c' times that sum to its binary32
+// total (the block expanded to bf16 levels, scaled in binary32 after the
+// block's products; the same sum reassociated, with the rounding on the
+// level instead of on the product level * c').  Per code byte that is one
+// byte permute (the table address), one 4-byte LDS read and one dot product.
+// A wave reduction then gives the binary32 partial sum of the segment.
 //
 // Main workgroup g (NWV waves) owns segment g % nseg, and its wave w the rows
 // NWV (g / nseg) + w + i NWV gmain / nseg (gmain % nseg == 0).  With sixteen
-// waves the level pairs come from the replicated table above (bank-conflict
-// free, 64 KB, so two workgroups per CU); with four, from one copy.  A wave
+// waves the level pairs come from the 64-copy table (bank-conflict free,
+// 64 KB, so two workgroups per CU); with four, from one copy.  A wave
 // keeps SLOTS - 1 items in flight while it computes one, in fixed register
 // slots (the loop is unrolled by SLOTS, so no slot is ever copied: a copy of
 // a register whose load is in flight would make the wave wait for it).  The
@@ -329,9 +344,12 @@ __global__ __launch_bounds__(256) void k_nf4_gemv(const bf16_t *__restrict__ X, 
 // 4-byte word holding its byte (absmax_q is 16-byte aligned), and the item's
 // 32 CH blocks share one binary32 step (32 CH divides 256 and the item's
 // first block is a multiple of 32 CH).  part is [nseg][T][N] binary32.
-// Workgroups 0 .. nsplit_u - 1 come first and form the U partials of K range
-// u as in k_nf4_gemv ([4 nsplit_u][T][r]; their waves past the fourth have nothing to do).  Tokens
-// T .. TT-1 are zero.
+// Workgroups gmain .. gmain + nsplit_u - 1 come last and form the U partials
+// of K range u as in k_nf4_gemv ([4 nsplit_u][T][r]; their waves past the fourth have nothing
+// to do): the main workgroups then fill every slot at once and, when the items divide evenly,
+// every wave streams the same number of them (with the U workgroups first, 512 slots leave
+// 496 for the main ones, and at 8192 x 8192 512 of their 7936 waves take a third item).
+// Tokens T .. TT-1 are zero.
 template <int TT, int CH, int SLOTS, int NWV, int MINW>
 __global__ __launch_bounds__(64 * NWV, MINW) void k_nf4_gemv_rows(
     const bf16_t *__restrict__ X, int64_t T, int64_t K, const uint8_t *__restrict__ codes,
@@ -339,17 +357,17 @@ __global__ __launch_bounds__(64 * NWV, MINW) void k_nf4_gemv_rows(
     const bf16_t *__restrict__ A, int64_t r, float *__restrict__ part, float *__restrict__ upart, Levels lv) {
   constexpr bool REP = NWV == 16;  // sixteen waves share the replicated table
   constexpr int Ks = 2048 * CH;
-  __shared__ __attribute__((aligned(16))) float2 s_tab[REP ? 256 * kTabCopies : 256];
+  __shared__ __attribute__((aligned(16))) uint32_t s_tab[REP ? 256 * kTabCopies : 256];
   __shared__ __attribute__((aligned(16))) uint32_t s_x[TT][Ks / 2];  // the segment's activations
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if ((int)blockIdx.x < nsplit_u) {
+  if ((int)blockIdx.x >= gmain) {
     if (wave >= 4) return;
-    const int64_t u = blockIdx.x, kchunk = K / nsplit_u, kb = u * kchunk;
+    const int64_t u = blockIdx.x - gmain, kchunk = K / nsplit_u, kb = u * kchunk;
     lora_u_partial<1>(X, T, K, A, r, kb, kb + kchunk, upart + (u * 4 + wave) * T * r, wave, lane);
     return;
   }
-  const int g = (int)blockIdx.x - nsplit_u, seg = g % nseg;
+  const int g = (int)blockIdx.x, seg = g % nseg;
   const int64_t row0 = (int64_t)(g / nseg) * NWV + wave, rstride = (int64_t)(gmain / nseg) * NWV;
   const int64_t items = row0 < N ? (N - row0 + rstride - 1) / rstride : 0;
 
@@ -377,9 +395,9 @@ __global__ __launch_bounds__(64 * NWV, MINW) void k_nf4_gemv_rows(
   for (int j = 0; j + 1 < SLOTS; ++j)  // in flight while the activations and the table are loaded
     if (items > 0) load_slot(sl[j]);
 
-  if constexpr (REP) pair_levels_rep32(lv, s_tab, tid);
-  else pair_levels_to_lds(lv, s_tab, tid);
-  const uint32_t c8 = 8u * (lane & 31);
+  if constexpr (REP) bf16_pairs_rep64(lv, s_tab, tid);
+  else bf16_pairs_one(lv, s_tab, tid);
+  const uint32_t c4 = 4u * lane;
   // the workgroup reads the segment's activations once (every wave of it needs all of them), through LDS
   for (int i = tid; i < TT * Ks / 8; i += 64 * NWV) {
     const int t = i / (Ks / 8), c = i % (Ks / 8);
@@ -410,28 +428,33 @@ __global__ __launch_bounds__(64 * NWV, MINW) void k_nf4_gemv_rows(
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const float cq = __fmul_rn((float)__builtin_amdgcn_ubfe(cur.q[c], bsh, 8), cur.d);
+      float pb[TT];  // the block's dot products
+#pragma unroll
+      for (int t = 0; t < TT; ++t) pb[t] = 0.f;
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd) {
         const uint32_t w = cur.c[c][wd];
-        float2 lp[4];
+        uint32_t lp[4];
         if constexpr (REP) {
-          lp[0] = pair_rep32<0>(s_tab, w, c8), lp[1] = pair_rep32<1>(s_tab, w, c8);
-          lp[2] = pair_rep32<2>(s_tab, w, c8), lp[3] = pair_rep32<3>(s_tab, w, c8);
+          lp[0] = bf16_pair_rep64<0>(s_tab, w, c4), lp[1] = bf16_pair_rep64<1>(s_tab, w, c4);
+          lp[2] = bf16_pair_rep64<2>(s_tab, w, c4), lp[3] = bf16_pair_rep64<3>(s_tab, w, c4);
         } else {
 #pragma unroll
           for (int b = 0; b < 4; ++b) lp[b] = s_tab[(w >> (8 * b)) & 0xffu];
         }
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          const float2 l = lp[b];
-          const bf16x2_t wp = __builtin_bit_cast(bf16x2_t, pack_bf16x2(__fmul_rn(l.x, cq), __fmul_rn(l.y, cq)));
+          const uint32_t lb = lp[b];
+          const bf16x2_t wp = __builtin_bit_cast(bf16x2_t, lb);
 #pragma unroll
           for (int t = 0; t < TT; ++t) {
             const uint32_t xw = xr[t][c][4 * wd + b];
-            acc[t] = __builtin_amdgcn_fdot2_f32_bf16(wp, __builtin_bit_cast(bf16x2_t, xw), acc[t], false);
+            pb[t] = __builtin_amdgcn_fdot2_f32_bf16(wp, __builtin_bit_cast(bf16x2_t, xw), pb[t], false);
           }
         }
       }
+#pragma unroll
+      for (int t = 0; t < TT; ++t) acc[t] = fmaf(cq, pb[t], acc[t]);
     }
 #pragma unroll
     for (int t = 0; t < TT; ++t) {  // reduce over the wave, lane 63 writes the partial
@@ -951,8 +974,9 @@ static hipError_t rows_go(const bf16_t *X, int64_t T, int64_t K, const uint8_t *
   static thread_local int res = 0;  // workgroups resident at once, per variant and thread
   if (res <= 0) res = resident(k_nf4_gemv_rows<TT, CH, SLOTS, NWV, MINW>, 64 * NWV);
   if (res <= 0) return hipErrorInvalidDeviceFunction;
-  // main workgroups: what stays resident beside the U workgroups, at most one item per wave, a multiple of nseg
-  int64_t g = std::min<int64_t>(std::max(1, res - nsplit_u), (N * nseg + NWV - 1) / NWV);
+  // main workgroups: what is resident at once (the U workgroups follow them), at most one item per wave, a
+  // multiple of nseg
+  int64_t g = std::min<int64_t>(res, (N * nseg + NWV - 1) / NWV);
   g = std::max<int64_t>(nseg, g / nseg * nseg);
   const int gmain = (int)g;
   launch(k_nf4_gemv_rows<TT, CH, SLOTS, NWV, MINW>, dim3((unsigned)(gmain + nsplit_u)), dim3(64 * NWV), 0, s, X, T,
