@@ -29,6 +29,11 @@
 //    (A single launch with a last-arriving-workgroup reduction needs
 //    device-scope fences, which on this chip write back and invalidate the L2
 //    in every workgroup and cost far more than a second launch.)
+// Variants of the first launch with the same partial-sum contract, chosen by
+// token count and shape: k_nf4_gemv_rows (one or two tokens, a wave per
+// weight row), k_nf4_gemv_m32 (3..32 tokens, 32x32 MFMAs with the block
+// constant applied per block), k_nf4_gemv_mrows (up to 64 tokens, 16x16 MFMAs
+// on exactly dequantized weights).
 #include <algorithm>
 
 #include "device.h"
@@ -621,6 +626,163 @@ __global__ __launch_bounds__(64 * (RED == 8 ? 8 : 4), (mrows_minw<MT, RED>())) v
   if (f < items) do_step(s0, s1, 0);
 }
 
+// ------------------------------- the 32-token row-group GEMV (3..32 tokens)
+// v_mfma_f32_32x32x16_bf16 with the tokens as M (activations: operand A) and
+// 32 weight rows as N (decoded codes: operand B).  The reduction index of
+// MFMA step (b, s) is mapped onto the columns 64 b + 32 h + 8 s + e of the
+// segment (h = lane / 32 the k-half a lane feeds, e < 8), so that the 16
+// columns of one MFMA lie in block b of every row and lane (n, h) = (l % 32,
+// l / 32) feeds them from one 16-byte load: half h of block b of weight row
+// n, words s = 0..3.  The block constant then factors out as in the row
+// kernel: the four MFMAs of a block start from zero, their bf16 levels come
+// straight from the level-pair table (one byte permute and one 4-byte LDS
+// read per code byte, no arithmetic), and each of the lane's accumulators
+// adds c' times the block's result with one fmaf (the lane's accumulators all
+// belong to its row n).  Accumulator element j of lane l is token
+// 8 (j / 4) + 4 (l / 32) + j % 4, so only the first 4 TG elements (TG
+// 8-token groups, T <= 8 TG) are scaled, exchanged and stored.  Two blocks
+// are multiplied at a time with their MFMA chains alternating, so that each
+// MFMA's successor does not wait for its result.
+//
+// A segment is KS = 256 columns (four blocks); every lane keeps its token's
+// activations of the segment in 64 VGPRs for the whole launch (tokens past T
+// are zero).  The eight waves of main workgroup g take the eight segments
+// 8 (g % npart) + w (npart = nseg / 8) over the same item sequence: row group
+// g / npart + i gmain / npart (32 rows, rows past N re-read the last row and
+// are never stored), each item one 4 KB stream per wave (four 16-byte loads
+// per lane), SLOTS - 1 items in flight.  After an item the waves pass their
+// accumulators through LDS (two buffers, one barrier per item) and every
+// thread adds the eight segments' values of its outputs in wave order, so
+// each part p of 2048 columns writes one partial: part is [npart][T][N].
+// Workgroups gmain .. gmain + nsplit_u - 1 follow and form the U partials
+// ([4 nsplit_u][T][r]; waves past the fourth have nothing to do).
+constexpr int kM32Seg = 256, kM32Red = 8;
+template <int TG>
+__global__ __launch_bounds__(64 * kM32Red, 1) void k_nf4_gemv_m32(
+    const bf16_t *__restrict__ X, int64_t T, int64_t K, const uint8_t *__restrict__ codes,
+    const uint8_t *__restrict__ absmax_q, const float *__restrict__ step, int64_t N, int gmain, int nseg, int nsplit_u,
+    const bf16_t *__restrict__ A, int64_t r, float *__restrict__ part, float *__restrict__ upart, Levels lv) {
+  constexpr int NE = 4 * TG;  // accumulator elements holding tokens
+  constexpr int SLOTS = 3;
+  // the alignment places the table at LDS address 0, so that a lookup address is the byte permute alone
+  __shared__ __attribute__((aligned(1024))) uint32_t s_tab[256 * kTabCopies];
+  __shared__ __attribute__((aligned(16))) float s_red[2][kM32Red][NE][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if ((int)blockIdx.x >= gmain) {
+    if (wave >= 4) return;
+    const int64_t u = blockIdx.x - gmain, kchunk = K / nsplit_u, kb = u * kchunk;
+    lora_u_partial<2>(X, T, K, A, r, kb, kb + kchunk, upart + (u * 4 + wave) * T * r, wave, lane);
+    return;
+  }
+  const int n = lane & 31, h = lane >> 5;
+  const int npart = nseg / kM32Red, pi = (int)blockIdx.x % npart, seg = pi * kM32Red + wave;
+  const int64_t ngroups = (N + 31) / 32;
+  const int64_t rg0 = (int64_t)blockIdx.x / npart, rgs = (int64_t)gmain / npart;
+  const int64_t items = rg0 < ngroups ? (ngroups - rg0 + rgs - 1) / rgs : 0;
+  const int64_t col0 = (int64_t)seg * kM32Seg;  // the segment's first column
+
+  struct Slot {
+    u32x4_t c[4];  // half h of each of the four blocks of the lane's row
+    uint32_t q;    // the four blocks' 8-bit constants
+    float d;       // their binary32 step
+  };
+  int64_t li = 0;  // item of the load stream; it stops at the last item (later prefetches reload it, unused)
+  // row addresses: a wave-uniform 64-bit base of the row group plus a 32-bit lane offset (n K / 2 < 2^27)
+  const uint8_t *const cbase = codes + col0 / 2 + 16 * h;
+  const uint8_t *const qbase = absmax_q + col0 / 64;
+  auto load_slot = [&](Slot &sl) {
+    const int64_t r0 = (rg0 + li * rgs) * 32;                     // wave-uniform
+    const int nr = (int)(r0 + n < N ? n : N - 1 - r0);             // row r0 + nr, clamped to the last row
+    const uint8_t *cp = cbase + r0 * (K / 2) + (uint32_t)nr * (uint32_t)(K / 2);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) sl.c[b] = *reinterpret_cast<const u32x4_t *>(cp + 32 * b);
+    // block index of the row's first block here: a multiple of 4, so one aligned word and one group of 256
+    const int64_t b0 = r0 * (K / 64) + (int64_t)nr * (K / 64) + col0 / 64;
+    sl.q = *reinterpret_cast<const uint32_t *>(qbase + r0 * (K / 64) + (uint32_t)nr * (uint32_t)(K / 64));
+    sl.d = step[b0 >> 8];
+    if (li + 1 < items) ++li;
+  };
+  Slot sl[SLOTS];
+#pragma unroll
+  for (int j = 0; j + 1 < SLOTS; ++j)  // in flight while the activations and the table are loaded
+    if (items > 0) load_slot(sl[j]);
+
+  bf16_pairs_rep64(lv, s_tab, tid);
+  bf16_pairs_rep64(lv, s_tab, tid + 512);
+  const uint32_t c4 = 4u * lane;
+  u32x4_t xa[4][4];  // [block][MFMA step]: token n, columns 64 b + 32 h + 8 s .. + 7
+  {
+    const bool tok = n < T;
+    const bf16_t *xp = X + (tok ? n : 0) * K + col0 + 32 * h;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        xa[b][st] = tok ? *reinterpret_cast<const u32x4_t *>(xp + 64 * b + 8 * st) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  if (items <= 0) return;
+
+  float *pout = part + (int64_t)pi * T * N;
+  int64_t crg = rg0;  // row group of the item being computed
+  int buf = 0;  // LDS exchange buffer of the item being computed (alternates)
+  auto do_step = [&](Slot &cur, Slot &refill) {
+    load_slot(refill);
+    float acc[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int bp = 0; bp < 4; bp += 2) {  // two blocks at a time: their MFMA chains alternate
+      f32x16_t t[2] = {{}, {}};
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint32_t w = cur.c[bp + i][st];
+          const u32x4_t bop = {bf16_pair_rep64<0>(s_tab, w, c4), bf16_pair_rep64<1>(s_tab, w, c4),
+                               bf16_pair_rep64<2>(s_tab, w, c4), bf16_pair_rep64<3>(s_tab, w, c4)};
+          t[i] = mfma_32x32x16(xa[bp + i][st], bop, t[i]);
+        }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float cq = __fmul_rn((float)__builtin_amdgcn_ubfe(cur.q, 8 * (bp + i), 8), cur.d);
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[e] = fmaf(cq, t[i][e], acc[e]);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // two blocks' lookups and MFMA results live at a time
+    }
+    // exchange: thread i of the workgroup adds the eight waves' element e of lane l for
+    // (e, l) = (i / 64 + 8 k, i % 64), k = 0 .. NE / 8 - 1 (NE = 4 TG, so TG = 1 leaves half the threads idle)
+#pragma unroll
+    for (int e = 0; e < NE; ++e) s_red[buf][wave][e][lane] = acc[e];
+    __syncthreads();
+#pragma unroll
+    for (int e0 = 0; e0 < NE; e0 += kM32Red) {
+      const int e = e0 + wave;
+      if (e < NE) {
+        float y = s_red[buf][0][e][lane];
+#pragma unroll
+        for (int v = 1; v < kM32Red; ++v) y += s_red[buf][v][e][lane];
+        const int64_t t = 8 * (e >> 2) + 4 * h + (e & 3), row = crg * 32 + n;
+        if (t < T && row < N) pout[t * N + row] = y;
+      }
+    }
+    crg += rgs;
+    buf ^= 1;
+  };
+  // item j computes slot j % SLOTS and refills slot (j + SLOTS - 1) % SLOTS; unrolled by SLOTS so that
+  // every slot index is a constant
+  int64_t f = 0;
+  for (; f + SLOTS <= items; f += SLOTS) {
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) do_step(sl[j], sl[(j + SLOTS - 1) % SLOTS]);
+  }
+#pragma unroll
+  for (int j = 0; j + 1 < SLOTS; ++j)
+    if (f + j < items) do_step(sl[j], sl[(j + SLOTS - 1) % SLOTS]);
+}
+
 // Sums of the finishing kernels, in index order with every load issued first (a loop bound known only
 // at run time would otherwise wait for each load before the next): the 1 <= n <= 16 weight partials
 // src[0], src[stride], ..., and the U partials p = q, q + 8, ... < nup <= 64 of (t, j).  Indexes past
@@ -913,7 +1075,12 @@ static int mrows_mt(int64_t T) { return T <= 16 ? 1 : T <= 32 ? 2 : 4; }
 static int mrows_red(int mt, int64_t nseg) { return mt > 1 && nseg % 8 == 0 ? 8 : nseg % 4 == 0 ? 4 : 1; }
 // at most 32 partials, which the wide finish takes: 128 segments in fours, else 32 (four token groups:
 // segments in fours only)
+// 3..32 tokens with n_in % 2048 == 0 (at most 32 parts of 2048 columns): the 32-token kernel
+static bool m32_ok(int64_t T, int64_t K) {
+  return T >= 3 && T <= 32 && K > 0 && K % (kM32Seg * kM32Red) == 0 && K / (kM32Seg * kM32Red) <= kFinishMaxSplitWide;
+}
 int nf4_gemv_mrows_nseg(int64_t T, int64_t K) {
+  if (m32_ok(T, K)) return (int)(K / kM32Seg);
   if (T < 3 || T > kMrowsMaxT || K <= 0) return 0;
   const int mt = mrows_mt(T), ks = 512 / mt;
   if (K % ks != 0) return 0;
@@ -922,8 +1089,39 @@ int nf4_gemv_mrows_nseg(int64_t T, int64_t K) {
   return ns / mrows_red(mt, ns) <= kFinishMaxSplitWide ? (int)ns : 0;
 }
 int nf4_gemv_mrows_nparts(int64_t T, int64_t K) {
+  if (m32_ok(T, K)) return (int)(K / (kM32Seg * kM32Red));
   const int ns = nf4_gemv_mrows_nseg(T, K);
   return ns / mrows_red(mrows_mt(T), ns > 0 ? ns : 1);
+}
+
+template <int TG>
+static hipError_t m32_go(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,
+                         const float *step, int64_t N, int nseg, int nsplit_u, const bf16_t *A, int64_t r, float *part,
+                         float *upart, const Levels &lv, hipStream_t s, int *nseg_out) {
+  static thread_local int res = 0;  // workgroups resident at once, per variant and thread
+  if (res <= 0) res = resident(k_nf4_gemv_m32<TG>, 64 * kM32Red);
+  if (res <= 0) return hipErrorInvalidDeviceFunction;
+  const int npart = nseg / kM32Red;
+  // main workgroups: what is resident at once (the U workgroups follow them), at most one item each, a
+  // multiple of npart
+  int64_t g = std::min<int64_t>(res, (N + 31) / 32 * npart);
+  g = std::max<int64_t>(npart, g / npart * npart);
+  const int gmain = (int)g;
+  launch(k_nf4_gemv_m32<TG>, dim3((unsigned)(gmain + nsplit_u)), dim3(64 * kM32Red), 0, s, X, T, K, codes, absmax_q,
+         step, N, gmain, nseg, nsplit_u, A, r, part, upart, lv);
+  *nseg_out = npart;
+  return hipGetLastError();
+}
+static hipError_t launch_nf4_gemv_m32(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes,
+                                      const uint8_t *absmax_q, const float *step, int64_t N, int nseg, int nsplit_u,
+                                      const bf16_t *A, int64_t r, float *part, float *upart, const Levels &lv,
+                                      hipStream_t s, int *nseg_out) {
+  switch ((T + 7) / 8) {
+    case 1: return m32_go<1>(X, T, K, codes, absmax_q, step, N, nseg, nsplit_u, A, r, part, upart, lv, s, nseg_out);
+    case 2: return m32_go<2>(X, T, K, codes, absmax_q, step, N, nseg, nsplit_u, A, r, part, upart, lv, s, nseg_out);
+    case 3: return m32_go<3>(X, T, K, codes, absmax_q, step, N, nseg, nsplit_u, A, r, part, upart, lv, s, nseg_out);
+    default: return m32_go<4>(X, T, K, codes, absmax_q, step, N, nseg, nsplit_u, A, r, part, upart, lv, s, nseg_out);
+  }
 }
 
 template <int MT, int RED>
@@ -940,6 +1138,8 @@ hipError_t launch_nf4_gemv_mrows(const bf16_t *X, int64_t T, int64_t K, const ui
   if (T == 0) return hipSuccess;
   const int nseg = nf4_gemv_mrows_nseg(T, K);
   if (nseg <= 0) return hipErrorInvalidValue;
+  if (m32_ok(T, K)) return launch_nf4_gemv_m32(X, T, K, codes, absmax_q, step, N, nseg, nsplit_u, A, r, part, upart, lv,
+                                               s, nseg_out);
   const int mt = mrows_mt(T), red = mrows_red(mt, nseg), npart = nseg / red;
   const int res = mt == 1   ? (red == 1 ? mrows_resident<1, 1>() : mrows_resident<1, 4>())
                   : mt == 2 ? (red == 1 ? mrows_resident<2, 1>()

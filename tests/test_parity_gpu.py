@@ -436,6 +436,28 @@ def test_row_group_forward(n_out, n_in, T, r):
     assert_close("U", gpu_f64(U), Ur)
 
 
+@pytest.mark.parametrize("n_out,n_in,T,r", [(72, 2048, 3, 16), (1000, 8192, 32, 16), (2056, 8192, 32, 16),
+                                            (200, 28672, 17, 64), (4104, 2048, 8, 16), (8, 65536, 32, 8),
+                                            (520, 4096, 12, 128), (24, 6144, 24, 4), (1032, 2048, 9, 1),
+                                            (40, 14336, 31, 16)])
+def test_32_token_row_group_forward(n_out, n_in, T, r):
+    """3..32 tokens with n_in % 2048 == 0: the 32-token row-group kernel (32x32x16 MFMAs, tokens as M, the
+    block constant applied to each block's MFMA result, eight 256-column segments per workgroup added through
+    LDS, one partial per 2048 columns: 1 to 32 partials), including ragged row groups (n_out 1000, 200, 520,
+    24, 40, 8), several items per workgroup (2056 and 4104 rows), the last token of each 8-token group
+    (T 8, 24, 32) and one past it (9, 17), rank 128 and rank 1; checked in full."""
+    print(f"32-token row-group forward {n_out}x{n_in} T={T} r={r}", flush=True)
+    inp = linear_inputs(n_out, n_in, T, r, 2.0 * r, seed=n_out + 5 * T, sigma_ab=0.05)
+    w = Bd.quantize_nf4(torch.from_numpy(inp.W).to(dev()))
+    X, A, B = (to_gpu_bf16(a) for a in (inp.X, inp.A, inp.B))
+    Y, U = Bd.linear_fwd(X, w, A, B, inp.alpha)
+    torch.cuda.synchronize()
+    oc, oq, od = O.quantize_nf4(inp.W)
+    Yr, Ur = O.linear_fwd(inp.X, O.dequant(oc, oq, od, n_out, n_in), inp.A, inp.B, inp.alpha)
+    assert_close("Y", gpu_f64(Y), Yr)
+    assert_close("U", gpu_f64(U), Ur)
+
+
 @pytest.mark.parametrize("n_out,n_in,T,r", [(72, 2048, 1, 16), (1032, 4096, 2, 5), (520, 8192, 1, 32),
                                             (264, 16384, 2, 64), (8, 2048, 2, 8), (4104, 6144, 1, 12),
                                             (2056, 4096, 2, 24), (6152, 8192, 1, 16), (520, 8192, 3, 16),
