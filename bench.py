@@ -91,7 +91,7 @@ KERNEL_SOURCES = {"nf4_gemm_fwd": "nf4_gemm.hip", "nf4_gemm_dx": "nf4_gemm.hip",
                   "merge": "merge.hip"}
 # kernel symbols behind each timed launch label (the small-token forward has two kernels)
 KERNEL_SYMBOLS = {"nf4_gemm_fwd": ("k_nf4_gemm_fwd",), "nf4_gemm_dx": ("k_nf4_gemm_dx",),
-                  "nf4_gemv": ("k_nf4_gemv", "k_nf4_gemv_rows", "k_nf4_gemv_mrows")}
+                  "nf4_gemv": ("k_nf4_gemv", "k_nf4_gemv_rows", "k_nf4_gemv_mrows", "k_nf4_gemv_m32")}
 
 
 def _code_only(text: str) -> str:

@@ -113,10 +113,11 @@ hipError_t launch_gemv_finish(const float *part, const float *upart, int nsplit,
 // partials of nseg row segments (part [nseg][T][N], nseg = nf4_gemv_rows_nseg(T, K), also returned in
 // *nseg_out) plus the U partials of nsplit_u K ranges (upart [4 nsplit_u][T][r]).
 int nf4_gemv_rows_nseg(int64_t T, int64_t K);  // 0: the kernel does not take (T, K)
-// Row-group GEMV for 3..64 tokens (segments of 512 columns up to 16 tokens, 256 up to 32, 128 beyond; at most 32
-// partials): binary32 partials of the nseg = nf4_gemv_mrows_nseg(T, K) segments (part [nseg][T][N]), or of
-// their fours when nseg % 4 == 0 (part [nseg / 4][T][N]), plus the U partials as above; *nseg_out is the
-// number of partials written.
+// Row-group GEMV for 3..64 tokens.  With 3..32 tokens and K % 2048 == 0 (at most 32 partials) the 32-token
+// kernel: 256-column segments, one partial per eight (part [K / 2048][T][N]).  Otherwise segments of 512
+// columns up to 16 tokens, 256 up to 32, 128 beyond (at most 32 partials): binary32 partials of the
+// nseg = nf4_gemv_mrows_nseg(T, K) segments (part [nseg][T][N]), or of their fours or eights.  Plus the U
+// partials as above; *nseg_out is the number of partials written.
 int nf4_gemv_mrows_nseg(int64_t T, int64_t K);    // 0: the kernel does not take (T, K)
 int nf4_gemv_mrows_nparts(int64_t T, int64_t K);  // partials it writes (0 as above)
 hipError_t launch_nf4_gemv_mrows(const bf16_t *X, int64_t T, int64_t K, const uint8_t *codes, const uint8_t *absmax_q,

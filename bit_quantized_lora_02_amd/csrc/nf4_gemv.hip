@@ -31,7 +31,7 @@
 //    in every workgroup and cost far more than a second launch.)
 // Variants of the first launch with the same partial-sum contract, chosen by
 // token count and shape: k_nf4_gemv_rows (one or two tokens, a wave per
-// weight row), k_nf4_gemv_m32 (3..32 tokens, 32x32 MFMAs with the block
+// weight row), k_nf4_gemv_m32 (3..64 tokens, 32x32 MFMAs with the block
 // constant applied per block), k_nf4_gemv_mrows (up to 64 tokens, 16x16 MFMAs
 // on exactly dequantized weights).
 #include <algorithm>
@@ -626,53 +626,64 @@ __global__ __launch_bounds__(64 * (RED == 8 ? 8 : 4), (mrows_minw<MT, RED>())) v
   if (f < items) do_step(s0, s1, 0);
 }
 
-// ------------------------------- the 32-token row-group GEMV (3..32 tokens)
-// v_mfma_f32_32x32x16_bf16 with the tokens as M (activations: operand A) and
-// 32 weight rows as N (decoded codes: operand B).  The reduction index of
-// MFMA step (b, s) is mapped onto the columns 64 b + 32 h + 8 s + e of the
-// segment (h = lane / 32 the k-half a lane feeds, e < 8), so that the 16
-// columns of one MFMA lie in block b of every row and lane (n, h) = (l % 32,
-// l / 32) feeds them from one 16-byte load: half h of block b of weight row
-// n, words s = 0..3.  The block constant then factors out as in the row
-// kernel: the four MFMAs of a block start from zero, their bf16 levels come
-// straight from the level-pair table (one byte permute and one 4-byte LDS
-// read per code byte, no arithmetic), and each of the lane's accumulators
-// adds c' times the block's result with one fmaf (the lane's accumulators all
-// belong to its row n).  Accumulator element j of lane l is token
-// 8 (j / 4) + 4 (l / 32) + j % 4, so only the first 4 TG elements (TG
-// 8-token groups, T <= 8 TG) are scaled, exchanged and stored.  Two blocks
-// are multiplied at a time with their MFMA chains alternating, so that each
-// MFMA's successor does not wait for its result.
+// ------------------------------- the 32-token row-group GEMV (3..64 tokens)
+// v_mfma_f32_32x32x16_bf16 with the tokens as M (activations: operand A, MT
+// groups of 32 tokens) and 32 weight rows as N (decoded codes: operand B).
+// The reduction index of MFMA step (b, s) is mapped onto the columns
+// 64 b + 32 h + 8 s + e of the segment (h = lane / 32 the k-half a lane
+// feeds, e < 8), so that the 16 columns of one MFMA lie in block b of every
+// row and lane (n, h) = (l % 32, l / 32) feeds them from one 16-byte load:
+// half h of block b of weight row n, words s = 0..3.  The block constant then
+// factors out as in the row kernel: the four MFMAs of a block (per token
+// group) start from zero, their bf16 levels come straight from the
+// level-pair table (one byte permute and one 4-byte LDS read per code byte,
+// no arithmetic, shared by the token groups), and each of the lane's
+// accumulators adds c' times the block's result with one fmaf (the lane's
+// accumulators all belong to its row n).  Accumulator element j of lane l in
+// token group m is token 32 m + 8 (j / 4) + 4 (l / 32) + j % 4, so only the
+// elements that hold tokens (TG 8-token groups, T <= 8 TG) are scaled,
+// exchanged and stored.  With one token group two blocks are multiplied at a
+// time, with two the groups' chains alternate, so that each MFMA's successor
+// does not wait for its result.
 //
-// A segment is KS = 256 columns (four blocks); every lane keeps its token's
-// activations of the segment in 64 VGPRs for the whole launch (tokens past T
-// are zero).  The eight waves of main workgroup g take the eight segments
-// 8 (g % npart) + w (npart = nseg / 8) over the same item sequence: row group
-// g / npart + i gmain / npart (32 rows, rows past N re-read the last row and
-// are never stored), each item one 4 KB stream per wave (four 16-byte loads
-// per lane), SLOTS - 1 items in flight.  After an item the waves pass their
-// accumulators through LDS (two buffers, one barrier per item) and every
-// thread adds the eight segments' values of its outputs in wave order, so
-// each part p of 2048 columns writes one partial: part is [npart][T][N].
-// Workgroups gmain .. gmain + nsplit_u - 1 follow and form the U partials
-// ([4 nsplit_u][T][r]; waves past the fourth have nothing to do).
-constexpr int kM32Seg = 256, kM32Red = 8;
+// A segment is KS = 256 / MT columns (4 / MT blocks); every lane keeps its
+// tokens' activations of the segment in 64 VGPRs for the whole launch
+// (tokens past T are zero).  One workgroup per CU (two waves per SIMD).  The eight waves of main workgroup g take the
+// eight segments 8 (g % npart) + w (npart = nseg / 8) over the same item
+// sequence: row group g / npart + i gmain / npart (32 rows, rows past N
+// re-read the last row and are never stored), each item one KS / 64 KB stream
+// per wave, SLOTS - 1 items in flight.  After an item the waves pass their
+// accumulators through LDS (two buffers and one barrier per item for 256-column
+// segments; one buffer and two barriers otherwise) and every thread adds the
+// eight segments' values of its outputs in wave order, so each part of 8 KS
+// columns writes one partial: part is [npart][T][N].  Workgroups gmain ..
+// gmain + nsplit_u - 1 follow and form the U partials ([4 nsplit_u][T][r];
+// waves past the fourth have nothing to do).
+constexpr int kM32Red = 8;
+// segment columns: 256 for one token group, 128 for two (64 VGPRs of activations either way)
+constexpr int m32_seg(int64_t T) { return T > 32 ? 128 : 256; }
 template <int TG>
-__global__ __launch_bounds__(64 * kM32Red, 1) void k_nf4_gemv_m32(
+__global__ __launch_bounds__(64 * kM32Red, 2) void k_nf4_gemv_m32(
     const bf16_t *__restrict__ X, int64_t T, int64_t K, const uint8_t *__restrict__ codes,
     const uint8_t *__restrict__ absmax_q, const float *__restrict__ step, int64_t N, int gmain, int nseg, int nsplit_u,
     const bf16_t *__restrict__ A, int64_t r, float *__restrict__ part, float *__restrict__ upart, Levels lv) {
-  constexpr int NE = 4 * TG;  // accumulator elements holding tokens
+  static_assert(TG >= 1 && TG <= 8, "up to 64 tokens");
+  constexpr int MT = TG > 4 ? 2 : 1;                 // 32-token groups
+  constexpr int KS = m32_seg(8 * TG), NB = KS / 64;   // segment columns, blocks per item
+  constexpr int NE0 = TG >= 4 ? 16 : 4 * TG;          // elements of group 0 holding tokens
+  constexpr int NE = NE0 + (MT == 2 ? 4 * (TG - 4) : 0);
+  constexpr int IL = MT == 1 ? 2 : 1;                 // blocks multiplied at a time
+  constexpr int NBUF = KS == 256 ? 2 : 1;             // exchange buffers (one: two workgroups fit a CU)
   constexpr int SLOTS = 3;
   // the alignment places the table at LDS address 0, so that a lookup address is the byte permute alone
   __shared__ __attribute__((aligned(1024))) uint32_t s_tab[256 * kTabCopies];
-  __shared__ __attribute__((aligned(16))) float s_red[2][kM32Red][NE][64];
+  __shared__ __attribute__((aligned(16))) float s_red[NBUF][kM32Red][NE][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if ((int)blockIdx.x >= gmain) {
     if (wave >= 4) return;
     const int64_t u = blockIdx.x - gmain, kchunk = K / nsplit_u, kb = u * kchunk;
-    lora_u_partial<2>(X, T, K, A, r, kb, kb + kchunk, upart + (u * 4 + wave) * T * r, wave, lane);
+    lora_u_partial<2 * MT>(X, T, K, A, r, kb, kb + kchunk, upart + (u * 4 + wave) * T * r, wave, lane);
     return;
   }
   const int n = lane & 31, h = lane >> 5;
@@ -680,27 +691,29 @@ __global__ __launch_bounds__(64 * kM32Red, 1) void k_nf4_gemv_m32(
   const int64_t ngroups = (N + 31) / 32;
   const int64_t rg0 = (int64_t)blockIdx.x / npart, rgs = (int64_t)gmain / npart;
   const int64_t items = rg0 < ngroups ? (ngroups - rg0 + rgs - 1) / rgs : 0;
-  const int64_t col0 = (int64_t)seg * kM32Seg;  // the segment's first column
+  const int64_t col0 = (int64_t)seg * KS;  // the segment's first column
 
   struct Slot {
-    u32x4_t c[4];  // half h of each of the four blocks of the lane's row
-    uint32_t q;    // the four blocks' 8-bit constants
-    float d;       // their binary32 step
+    u32x4_t c[NB];  // half h of each block of the lane's row
+    uint32_t q;     // the aligned word holding the blocks' 8-bit constants
+    float d;        // their binary32 step
   };
   int64_t li = 0;  // item of the load stream; it stops at the last item (later prefetches reload it, unused)
   // row addresses: a wave-uniform 64-bit base of the row group plus a 32-bit lane offset (n K / 2 < 2^27)
   const uint8_t *const cbase = codes + col0 / 2 + 16 * h;
-  const uint8_t *const qbase = absmax_q + col0 / 64;
+  // the row's first block here is a multiple of NB: its constants lie in the aligned word at qofs (byte
+  // qsh / 8 onwards), and its NB blocks in one group of 256
+  const int64_t qofs = (col0 / 64) & ~(int64_t)3;
+  const int qsh = 8 * (int)((col0 / 64) & 3);
   auto load_slot = [&](Slot &sl) {
-    const int64_t r0 = (rg0 + li * rgs) * 32;                     // wave-uniform
-    const int nr = (int)(r0 + n < N ? n : N - 1 - r0);             // row r0 + nr, clamped to the last row
+    const int64_t r0 = (rg0 + li * rgs) * 32;          // wave-uniform
+    const int nr = (int)(r0 + n < N ? n : N - 1 - r0);  // row r0 + nr, clamped to the last row
     const uint8_t *cp = cbase + r0 * (K / 2) + (uint32_t)nr * (uint32_t)(K / 2);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) sl.c[b] = *reinterpret_cast<const u32x4_t *>(cp + 32 * b);
-    // block index of the row's first block here: a multiple of 4, so one aligned word and one group of 256
-    const int64_t b0 = r0 * (K / 64) + (int64_t)nr * (K / 64) + col0 / 64;
-    sl.q = *reinterpret_cast<const uint32_t *>(qbase + r0 * (K / 64) + (uint32_t)nr * (uint32_t)(K / 64));
-    sl.d = step[b0 >> 8];
+    for (int b = 0; b < NB; ++b) sl.c[b] = *reinterpret_cast<const u32x4_t *>(cp + 32 * b);
+    const int64_t rb = r0 * (K / 64) + (int64_t)nr * (K / 64);  // the row's first block
+    sl.q = *reinterpret_cast<const uint32_t *>(absmax_q + rb + qofs);
+    sl.d = step[(rb + col0 / 64) >> 8];
     if (li + 1 < items) ++li;
   };
   Slot sl[SLOTS];
@@ -711,49 +724,51 @@ __global__ __launch_bounds__(64 * kM32Red, 1) void k_nf4_gemv_m32(
   bf16_pairs_rep64(lv, s_tab, tid);
   bf16_pairs_rep64(lv, s_tab, tid + 512);
   const uint32_t c4 = 4u * lane;
-  u32x4_t xa[4][4];  // [block][MFMA step]: token n, columns 64 b + 32 h + 8 s .. + 7
-  {
-    const bool tok = n < T;
-    const bf16_t *xp = X + (tok ? n : 0) * K + col0 + 32 * h;
+  u32x4_t xa[MT][NB][4];  // [token group][block][MFMA step]: token 32 m + n, columns 64 b + 32 h + 8 s .. + 7
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+  for (int m = 0; m < MT; ++m) {
+    const int64_t t = 32 * m + n;
+    const bf16_t *xp = X + (t < T ? t : 0) * K + col0 + 32 * h;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int st = 0; st < 4; ++st)
-        xa[b][st] = tok ? *reinterpret_cast<const u32x4_t *>(xp + 64 * b + 8 * st) : u32x4_t{0u, 0u, 0u, 0u};
+        xa[m][b][st] = t < T ? *reinterpret_cast<const u32x4_t *>(xp + 64 * b + 8 * st) : u32x4_t{0u, 0u, 0u, 0u};
   }
   __syncthreads();
   if (items <= 0) return;
 
   float *pout = part + (int64_t)pi * T * N;
   int64_t crg = rg0;  // row group of the item being computed
-  int buf = 0;  // LDS exchange buffer of the item being computed (alternates)
+  int buf = 0;        // LDS exchange buffer of the item being computed
   auto do_step = [&](Slot &cur, Slot &refill) {
     load_slot(refill);
-    float acc[NE];
+    float acc[NE];  // group 0's elements, then group 1's
 #pragma unroll
     for (int e = 0; e < NE; ++e) acc[e] = 0.f;
 #pragma unroll
-    for (int bp = 0; bp < 4; bp += 2) {  // two blocks at a time: their MFMA chains alternate
-      f32x16_t t[2] = {{}, {}};
+    for (int bp = 0; bp < NB; bp += IL) {
+      f32x16_t t[IL][MT] = {};
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < IL; ++i) {
           const uint32_t w = cur.c[bp + i][st];
           const u32x4_t bop = {bf16_pair_rep64<0>(s_tab, w, c4), bf16_pair_rep64<1>(s_tab, w, c4),
                                bf16_pair_rep64<2>(s_tab, w, c4), bf16_pair_rep64<3>(s_tab, w, c4)};
-          t[i] = mfma_32x32x16(xa[bp + i][st], bop, t[i]);
+#pragma unroll
+          for (int m = 0; m < MT; ++m) t[i][m] = mfma_32x32x16(xa[m][bp + i][st], bop, t[i][m]);
         }
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const float cq = __fmul_rn((float)__builtin_amdgcn_ubfe(cur.q, 8 * (bp + i), 8), cur.d);
+      for (int i = 0; i < IL; ++i) {
+        const float cq = __fmul_rn((float)__builtin_amdgcn_ubfe(cur.q, qsh + 8 * (bp + i), 8), cur.d);
 #pragma unroll
-        for (int e = 0; e < NE; ++e) acc[e] = fmaf(cq, t[i][e], acc[e]);
+        for (int e = 0; e < NE; ++e) acc[e] = fmaf(cq, t[i][e < NE0 ? 0 : 1][e < NE0 ? e : e - NE0], acc[e]);
       }
-      __builtin_amdgcn_sched_barrier(0);  // two blocks' lookups and MFMA results live at a time
+      __builtin_amdgcn_sched_barrier(0);  // IL blocks' lookups and MFMA results live at a time
     }
-    // exchange: thread i of the workgroup adds the eight waves' element e of lane l for
-    // (e, l) = (i / 64 + 8 k, i % 64), k = 0 .. NE / 8 - 1 (NE = 4 TG, so TG = 1 leaves half the threads idle)
+    // exchange: thread (w, l) of the workgroup adds the eight waves' flat element w + 8 k of lane l
+    if constexpr (NBUF == 1) __syncthreads();  // every wave has read the previous item's sums
 #pragma unroll
     for (int e = 0; e < NE; ++e) s_red[buf][wave][e][lane] = acc[e];
     __syncthreads();
@@ -764,12 +779,13 @@ __global__ __launch_bounds__(64 * kM32Red, 1) void k_nf4_gemv_m32(
         float y = s_red[buf][0][e][lane];
 #pragma unroll
         for (int v = 1; v < kM32Red; ++v) y += s_red[buf][v][e][lane];
-        const int64_t t = 8 * (e >> 2) + 4 * h + (e & 3), row = crg * 32 + n;
+        const int m = e < NE0 ? 0 : 1, j = e < NE0 ? e : e - NE0;
+        const int64_t t = 32 * m + 8 * (j >> 2) + 4 * h + (j & 3), row = crg * 32 + n;
         if (t < T && row < N) pout[t * N + row] = y;
       }
     }
     crg += rgs;
-    buf ^= 1;
+    if constexpr (NBUF == 2) buf ^= 1;
   };
   // item j computes slot j % SLOTS and refills slot (j + SLOTS - 1) % SLOTS; unrolled by SLOTS so that
   // every slot index is a constant
@@ -1075,12 +1091,14 @@ static int mrows_mt(int64_t T) { return T <= 16 ? 1 : T <= 32 ? 2 : 4; }
 static int mrows_red(int mt, int64_t nseg) { return mt > 1 && nseg % 8 == 0 ? 8 : nseg % 4 == 0 ? 4 : 1; }
 // at most 32 partials, which the wide finish takes: 128 segments in fours, else 32 (four token groups:
 // segments in fours only)
-// 3..32 tokens with n_in % 2048 == 0 (at most 32 parts of 2048 columns): the 32-token kernel
+// 3..64 tokens with n_in a multiple of eight segments (2048 columns up to 32 tokens, 1024 beyond) and at
+// most 32 such parts: the 32-token kernel
 static bool m32_ok(int64_t T, int64_t K) {
-  return T >= 3 && T <= 32 && K > 0 && K % (kM32Seg * kM32Red) == 0 && K / (kM32Seg * kM32Red) <= kFinishMaxSplitWide;
+  const int64_t part = m32_seg(T) * kM32Red;
+  return T >= 3 && T <= 64 && K > 0 && K % part == 0 && K / part <= kFinishMaxSplitWide;
 }
 int nf4_gemv_mrows_nseg(int64_t T, int64_t K) {
-  if (m32_ok(T, K)) return (int)(K / kM32Seg);
+  if (m32_ok(T, K)) return (int)(K / m32_seg(T));
   if (T < 3 || T > kMrowsMaxT || K <= 0) return 0;
   const int mt = mrows_mt(T), ks = 512 / mt;
   if (K % ks != 0) return 0;
@@ -1089,7 +1107,7 @@ int nf4_gemv_mrows_nseg(int64_t T, int64_t K) {
   return ns / mrows_red(mt, ns) <= kFinishMaxSplitWide ? (int)ns : 0;
 }
 int nf4_gemv_mrows_nparts(int64_t T, int64_t K) {
-  if (m32_ok(T, K)) return (int)(K / (kM32Seg * kM32Red));
+  if (m32_ok(T, K)) return (int)(K / (m32_seg(T) * kM32Red));
   const int ns = nf4_gemv_mrows_nseg(T, K);
   return ns / mrows_red(mrows_mt(T), ns > 0 ? ns : 1);
 }
@@ -1116,12 +1134,18 @@ static hipError_t launch_nf4_gemv_m32(const bf16_t *X, int64_t T, int64_t K, con
                                       const uint8_t *absmax_q, const float *step, int64_t N, int nseg, int nsplit_u,
                                       const bf16_t *A, int64_t r, float *part, float *upart, const Levels &lv,
                                       hipStream_t s, int *nseg_out) {
+#define QLORA_M32(TG_) m32_go<TG_>(X, T, K, codes, absmax_q, step, N, nseg, nsplit_u, A, r, part, upart, lv, s, nseg_out)
   switch ((T + 7) / 8) {
-    case 1: return m32_go<1>(X, T, K, codes, absmax_q, step, N, nseg, nsplit_u, A, r, part, upart, lv, s, nseg_out);
-    case 2: return m32_go<2>(X, T, K, codes, absmax_q, step, N, nseg, nsplit_u, A, r, part, upart, lv, s, nseg_out);
-    case 3: return m32_go<3>(X, T, K, codes, absmax_q, step, N, nseg, nsplit_u, A, r, part, upart, lv, s, nseg_out);
-    default: return m32_go<4>(X, T, K, codes, absmax_q, step, N, nseg, nsplit_u, A, r, part, upart, lv, s, nseg_out);
+    case 1: return QLORA_M32(1);
+    case 2: return QLORA_M32(2);
+    case 3: return QLORA_M32(3);
+    case 4: return QLORA_M32(4);
+    case 5: return QLORA_M32(5);
+    case 6: return QLORA_M32(6);
+    case 7: return QLORA_M32(7);
+    default: return QLORA_M32(8);
   }
+#undef QLORA_M32
 }
 
 template <int MT, int RED>

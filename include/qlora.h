@@ -133,10 +133,11 @@ int qlora_dequant(const qlora_nf4 *q, qlora_bf16 *W_out, void *stream);
  * T >= 0 (T = 0 does nothing), 1 <= r <= QLORA_MAX_RANK.
  * ws: device workspace of at least qlora_workspace_bytes(QLORA_OP_FWD, ...).
  * Accumulation is binary32; Y is rounded to bf16 once.  For 1 to 32 tokens
- * with n_in % 2048 == 0 the block constant multiplies each block's binary32
- * dot product with the bf16-rounded levels instead of each weight (the same
- * sum reassociated; the result is within the stated tolerance of the
- * dequantized product, not bit-identical to the tiled path's).
+ * with n_in % 2048 == 0, and 33 to 64 with n_in % 1024 == 0, the block
+ * constant multiplies each block's binary32 dot product with the bf16-rounded
+ * levels instead of each weight (the same sum reassociated; the result is
+ * within the stated tolerance of the dequantized product, not bit-identical to
+ * the tiled path's).
  */
 int qlora_linear_fwd(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const qlora_bf16 *A, const qlora_bf16 *B,
                      int32_t r, float alpha, qlora_bf16 *Y, qlora_bf16 *U_out, void *ws, size_t ws_bytes,

@@ -439,13 +439,15 @@ def test_row_group_forward(n_out, n_in, T, r):
 @pytest.mark.parametrize("n_out,n_in,T,r", [(72, 2048, 3, 16), (1000, 8192, 32, 16), (2056, 8192, 32, 16),
                                             (200, 28672, 17, 64), (4104, 2048, 8, 16), (8, 65536, 32, 8),
                                             (520, 4096, 12, 128), (24, 6144, 24, 4), (1032, 2048, 9, 1),
-                                            (40, 14336, 31, 16)])
+                                            (40, 14336, 31, 16), (1000, 8192, 64, 16), (200, 28672, 33, 64),
+                                            (2056, 4096, 40, 16), (24, 1024, 57, 128), (8, 32768, 48, 8)])
 def test_32_token_row_group_forward(n_out, n_in, T, r):
-    """3..32 tokens with n_in % 2048 == 0: the 32-token row-group kernel (32x32x16 MFMAs, tokens as M, the
-    block constant applied to each block's MFMA result, eight 256-column segments per workgroup added through
-    LDS, one partial per 2048 columns: 1 to 32 partials), including ragged row groups (n_out 1000, 200, 520,
-    24, 40, 8), several items per workgroup (2056 and 4104 rows), the last token of each 8-token group
-    (T 8, 24, 32) and one past it (9, 17), rank 128 and rank 1; checked in full."""
+    """3..64 tokens with n_in a multiple of 2048 (up to 32 tokens) or 1024 (33-64): the 32-token row-group
+    kernel (32x32x16 MFMAs, tokens as M in one or two groups of 32, the block constant applied to each block's
+    MFMA result, eight segments of 256 or 128 columns per workgroup added through LDS: 1 to 32 partials),
+    including ragged row groups (n_out 1000, 200, 520, 24, 40, 8), several items per workgroup (2056 and 4104
+    rows), the last token of each 8-token group (T 8, 24, 32, 40, 48, 64) and one past it (9, 17, 33, 57),
+    rank 128 and rank 1; checked in full."""
     print(f"32-token row-group forward {n_out}x{n_in} T={T} r={r}", flush=True)
     inp = linear_inputs(n_out, n_in, T, r, 2.0 * r, seed=n_out + 5 * T, sigma_ab=0.05)
     w = Bd.quantize_nf4(torch.from_numpy(inp.W).to(dev()))
