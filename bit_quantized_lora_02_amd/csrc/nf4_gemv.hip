@@ -381,7 +381,10 @@ __global__ __launch_bounds__(64 * NWV, MINW) void k_nf4_gemv_rows(
     uint32_t q[CH];  // the aligned word holding the lane's block byte of each chunk
     float d;         // the item's binary32 step
   };
-  const int lofs = 16 * lane, bofs = (lane >> 1) & ~3, bsh = 8 * ((lane >> 1) & 3);
+  // lane offsets: codes 16 lane, block-constant word (lane >> 1) & ~3; the constant's bit offset
+  // 8 ((lane >> 1) & 3) equals (4 lane) & 24 and is formed from the table offset c4 = 4 lane where it is
+  // used, which keeps one VGPR fewer live across the loop (64 VGPRs, eight waves per SIMD, no spill)
+  const int lofs = 16 * lane, bofs = (lane >> 1) & ~3;
   int64_t li = 0;  // item of the load stream; it stops at the last item (later prefetches reload it, unused)
   auto load_slot = [&](Slot &sl) {
     const int64_t row = row0 + li * rstride;
@@ -432,7 +435,7 @@ __global__ __launch_bounds__(64 * NWV, MINW) void k_nf4_gemv_rows(
     for (int t = 0; t < TT; ++t) acc[t] = 0.f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const float cq = __fmul_rn((float)__builtin_amdgcn_ubfe(cur.q[c], bsh, 8), cur.d);
+      const float cq = __fmul_rn((float)__builtin_amdgcn_ubfe(cur.q[c], c4 & 24u, 8), cur.d);
       float pb[TT];  // the block's dot products
 #pragma unroll
       for (int t = 0; t < TT; ++t) pb[t] = 0.f;
@@ -469,15 +472,13 @@ __global__ __launch_bounds__(64 * NWV, MINW) void k_nf4_gemv_rows(
     cn += rstride;
   };
   // step j computes slot j % SLOTS and refills slot (j + SLOTS - 1) % SLOTS; unrolled by SLOTS so that
-  // every slot index is a constant
-  int64_t f = 0;
-  for (; f + SLOTS <= items; f += SLOTS) {
+  // every slot index is a constant, the last round cut short by wave-uniform guards (no separate tail
+  // copy of the body, whose registers would have to live across the loop)
+  for (int64_t f = 0; f < items; f += SLOTS) {
 #pragma unroll
-    for (int j = 0; j < SLOTS; ++j) do_step(sl[j], sl[(j + SLOTS - 1) % SLOTS]);
+    for (int j = 0; j < SLOTS; ++j)
+      if (f + j < items) do_step(sl[j], sl[(j + SLOTS - 1) % SLOTS]);
   }
-#pragma unroll
-  for (int j = 0; j + 1 < SLOTS; ++j)
-    if (f + j < items) do_step(sl[j], sl[(j + SLOTS - 1) % SLOTS]);
 }
 
 // ------------------------------------------- the row-group GEMV (3..64 tokens)
