@@ -149,8 +149,9 @@ int qlora_linear_fwd(const qlora_bf16 *X, int64_t T, const qlora_nf4 *q, const q
  * identical arguments and results, without ws / ws_bytes.  Its workspace is a
  * static device array of 128 MiB per GPU, reserved when the library's code is
  * loaded on that GPU and held until the process ends; the call itself makes no
- * allocation.  Every forward of this build's workloads fits (the largest, 64
- * tokens against a 28672 x 8192 weight, needs 116 MiB); a shape whose forward
+ * allocation.  Every forward of this build's workloads fits (the largest, 4096
+ * tokens against a 1024 x 8192 weight with its reduction split in four ranges,
+ * needs 65 MiB; 64 tokens against 28672 x 8192 need 61 MiB); a shape whose forward
  * needs more returns QLORA_EWORKSPACE before any HIP call.  All calls on one
  * GPU share the array: calls that overlap in time on that GPU (other streams,
  * other host threads) race and must be ordered by the caller.  Nothing in the
