@@ -414,7 +414,10 @@ def test_small_token_forward(n_out, T):
                                             (8, 16384, 64, 4), (8, 16512, 40, 4), (40, 1536, 40, 8),
                                             (8, 32768, 36, 4)])
 def test_row_group_forward(n_out, n_in, T, r):
-    """3..64 tokens through the row-group kernel (16 rows per wave, activations in registers): one token
+    """3..64 tokens through the row-group kernels.  Where n_in is a multiple of 2048 (up to 32 tokens) or 1024
+    (33-64) with at most 32 parts, the 32-token kernel takes the shape (4096, 8192, 2048, 28672, 16384, 32768
+    up to 32 tokens; 1024, 8192, 16384, 32768 beyond); the rest keep the 16-row kernel (16 rows per wave,
+    activations in registers, exactly dequantized weights), described next: one token
     group and segments of 512 columns up to 16 tokens, two groups and segments of 256 up to 32, four groups
     and segments of 128 beyond, only when the segments come in fours (1152 and 16512: 9 and 129 segments,
     the MFMA kernel).  With two or four token groups and a segment count divisible by 8 the eight waves of a
