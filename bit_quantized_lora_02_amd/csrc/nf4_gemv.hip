@@ -55,9 +55,11 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(const u32x4_t &a, const u32x4_t
 // order of the two weights of the byte.  For sixteen-wave workgroups it is kept in 64
 // interleaved copies (64 KB): entry e of copy c sits at byte 256 e + 4 c, i.e. in bank c of
 // the 64 four-byte banks, and lane l reads copy l, so a 4-byte LDS read of the wave touches
-// 64 distinct banks whatever its code bytes.  Thread i of the nt >= 1024 threads writes
-// copies 16 (i & 3) .. 16 (i & 3) + 15 of entry i / 4; with fewer threads, one copy
-// (entries 0..255 at bytes 0..1023).
+// 64 distinct banks whatever its code bytes.  Built by 1024 threads t, each storing copies
+// 4 (t & 15) .. + 3 of the entries (t >> 4) + 64 i, i < 4: the 16 lanes of each phase of a
+// 16-byte store then fill the 64 banks once (with 16 entries per phase the stores were 16-way
+// bank conflicts, about 1.6 us of a one-token launch at 8192 x 8192).  With fewer threads, one
+// copy (entries 0..255 at bytes 0..1023).
 constexpr int kTabCopies = 64;
 __device__ __forceinline__ uint32_t bf16_level_pair(const Levels &lv, int e) {
   float lo = 0.f, hi = 0.f;
@@ -68,13 +70,26 @@ __device__ __forceinline__ uint32_t bf16_level_pair(const Levels &lv, int e) {
   }
   return pack_bf16x2(lo, hi);
 }
-__device__ __forceinline__ void bf16_pairs_rep64(const Levels &lv, uint32_t *tab, int tid) {
-  if (tid < 1024) {
-    const int e = tid >> 2, c0 = 16 * (tid & 3);
-    const uint32_t p = bf16_level_pair(lv, e);
-    const u32x4_t v = {p, p, p, p};
+// The five levels a thread needs come from one register holding level[lane & 15] in every lane, read
+// across lanes (ds_bpermute), instead of a chain of selects per level.  Every lane of the wave must
+// call it (the cross-lane reads); t >= 1024 writes nothing.
+__device__ __forceinline__ void bf16_pairs_rep64(const Levels &lv, uint32_t *tab, int t) {
+  const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  float mine = 0.f;  // level[lane & 15]
 #pragma unroll
-    for (int c = 0; c < 16; c += 4) *reinterpret_cast<u32x4_t *>(tab + e * kTabCopies + c0 + c) = v;
+  for (int v = 0; v < 16; ++v) mine = ((lane & 15) == v) ? lv.v[v] : mine;
+  const int e0 = (t >> 4) & 63, c0 = 4 * (t & 15);  // entries e0 + 64 i share the low nibble e0 & 15
+  const int mi = __builtin_bit_cast(int, mine);
+  const float lo = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (e0 & 15), mi));
+  float hi[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hi[i] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * ((e0 >> 4) + 4 * i), mi));
+  if (t < 1024) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t p = pack_bf16x2(lo, hi[i]);
+      *reinterpret_cast<u32x4_t *>(tab + (e0 + 64 * i) * kTabCopies + c0) = u32x4_t{p, p, p, p};
+    }
   }
 }
 __device__ __forceinline__ void bf16_pairs_one(const Levels &lv, uint32_t *tab, int tid) {
