@@ -63,6 +63,22 @@ def test_workspace_never_scales_with_weight(lib):
     assert big < deq_bytes // 100
 
 
+def test_few_token_workspace_holds_the_partials_and_fits_the_static_array(lib):
+    """The few-token forward writes one binary32 partial of Y per part of the reduction: 2048 columns up to
+    32 tokens, 1024 from 33 to 64 with the 32-token kernel (n_in 8192: 4 and 8 parts), 4096 for one token
+    (2 parts); its workspace must hold them, and every configured forward must fit the allocation-free
+    entry point's 128 MiB array."""
+    for T, parts in ((1, 2), (8, 4), (32, 4), (33, 8), (64, 8)):
+        for n_out in (8192, 28672):
+            ws = B.workspace_bytes(B.OP_FWD, T, n_out, 8192, 16)
+            assert ws >= parts * T * n_out * 4, (T, n_out)
+            assert ws < (parts + 2) * T * n_out * 4 + (8 << 20), (T, n_out)  # partials dominate
+    shapes = [(n, k, t, r) for n, k in ((8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672))
+              for t, r in ((4096, 64),)] + [(4096, 4096, 2048, 16), (14336, 4096, 4096, 64), (4096, 14336, 4096, 64)]
+    shapes += [(n, 8192, t, 16) for n in (8192, 28672) for t in (1, 8, 32, 64, 128)]
+    assert max(B.workspace_bytes(B.OP_FWD, t, n, k, r) for n, k, t, r in shapes) <= 128 << 20
+
+
 def _nf4(n_out, n_in, p=0x1000):
     return B._NF4(n_out, n_in, p, p, p)
 
