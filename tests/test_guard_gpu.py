@@ -64,8 +64,10 @@ CASES = [
     (520, 192, 300, 5),      # tiled, ragged, odd rank (padded B)
     (1024, 2048, 128, 16),   # tiled with a split reduction (binary32 partials in the workspace)
     (520, 2048, 1, 16),      # one token: row-streaming kernel
-    (1000, 4096, 9, 1),      # 3..16 tokens: row-group kernel
-    (1032, 1024, 40, 12),    # 33..64 tokens: row-group kernel, four token groups
+    (1000, 4096, 9, 1),      # 3..32 tokens, n_in % 2048 == 0: 32-token kernel, one token group
+    (1032, 1024, 40, 12),    # 33..64 tokens, n_in % 1024 == 0: 32-token kernel, two token groups
+    (520, 1536, 17, 4),      # n_in % 1024 != 0: 16-row kernel, two token groups, one partial per segment
+    (40, 1536, 40, 8),       # n_in % 1024 != 0: 16-row kernel, four token groups, four segments per partial
     (72, 384, 20, 4),        # split-K small-token kernel
     (4104, 256, 4001, 64),   # training-sized tile counts (256 x 256 tiles), ragged
 ]
