@@ -303,6 +303,21 @@ def test_repeatable_and_weight_frozen():
     assert torch.equal(before[2], w.absmax_step)
 
 
+@pytest.mark.parametrize("n_out,n_in,T", [(1032, 4096, 1), (1000, 4096, 8), (1032, 2048, 40), (520, 1536, 17)])
+def test_few_token_forward_is_bitwise_repeatable(n_out, n_in, T):
+    """The few-token kernels add their split partial sums in a fixed order (no atomics): the same call on the
+    same inputs gives the same bits, whatever the workspace held before (row kernel, 32-token kernel with one
+    and two token groups, 16-row kernel)."""
+    print(f"few-token repeatability {n_out}x{n_in} T={T}", flush=True)
+    inp = linear_inputs(n_out, n_in, T, 16, 32.0, seed=n_out + T)
+    w = Bd.quantize_nf4(torch.from_numpy(inp.W).to(dev()))
+    X, A, B = (to_gpu_bf16(a) for a in (inp.X, inp.A, inp.B))
+    Y1, U1 = Bd.linear_fwd(X, w, A, B, inp.alpha)
+    Y2, U2 = Bd.linear_fwd(X, w, A, B, inp.alpha)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2) and torch.equal(U1, U2)
+
+
 def test_autograd_function():
     inp = linear_inputs(136, 192, 40, 8, 16.0, seed=12)
     w = Bd.quantize_nf4(torch.from_numpy(inp.W).to(dev()))
