@@ -53,9 +53,11 @@ def _same(a, b):
 
 
 @pytest.mark.parametrize("first,second", [
-    ((4096, 4096, 2048, 16), (1024, 512, 40, 8)),       # tiled forward, then the row-group GEMV
-    ((28672, 8192, 64, 16), (8192, 8192, 1, 16)),       # the largest workspace, then the one-token GEMV
+    ((4096, 4096, 2048, 16), (1024, 512, 40, 8)),       # tiled forward, then the 16-row GEMV
+    ((28672, 8192, 64, 16), (8192, 8192, 1, 16)),       # 32-token GEMV (two token groups), then the one-token GEMV
     ((8192, 8192, 128, 64), (256, 256, 16, 8)),         # split reduction, then a small tiled forward
+    ((1024, 8192, 4096, 64), (8192, 8192, 8, 16)),      # the largest workspace (k/v forward, 4 ranges), then the
+                                                        # 32-token GEMV (one token group)
 ])
 def test_noalloc_matches_forward_with_workspace(first, second):
     lib = B.load_library()
